@@ -1,0 +1,282 @@
+"""fp64 CPU oracle of the multi-pass EAGLE-3 TTT draft attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import or call this module.  The GPU library
+never uses it, and this module uses nothing from the GPU library.
+
+What is computed (one call = one TTT pass p, 1-based):
+
+* Pass p's query at row i attends to two key sets (NeMo-RL issue "DFlash/DSpark
+  and EAGLE-3 TTT draft co-training for speculative decoding (Megatron
+  backend)", section "What I'm working on", item 1; NeMo-RL PR #3725,
+  self-review comment: multi-pass staircase visibility):
+    - the trunk: pass-1 keys/values at rows j <= i of the same sequence (causal);
+    - the branch: the keys/values that passes q = 2..p produced at the same row i.
+  Both sets are expressed here as ONE explicit boolean mask row over the
+  concatenated keys [K(1)_0..L-1 ; K(2)_0..L-1 ; ... ; K(p)_0..L-1] of the
+  sequence, and a single softmax is taken over the allowed entries.  That is
+  the exact value the two-part trunk+branch method with its joint
+  log-sum-exp merge reaches (issue above, item 1: exact joint-LSE merge).
+
+* Rotary embedding, rotate-half pairing (PR #3725 self-review: rotate-half
+  oracle), applied to queries and keys, never to values, with
+  theta_k = base^(-2k/D) in fp64 and the pair (k, k + D/2).
+  Positions (issue above, item 1: inference-aligned per-pass RoPE offsets;
+  reading: a pass-p draft token sits p-1 positions after its row):
+    query of pass p at row i      -> position i + p - 1
+    trunk key (pass 1) at row j   -> position j
+    branch key of pass q at row i -> position i + q - 1
+  base == 0 disables the rotation.
+
+* Layouts: padded BSHD ([B, S, H, D], every row of every batch is valid) and
+  packed THD ([T, H, D] with cu_seqlens; rows of one sequence never see another
+  sequence, positions restart at 0 per sequence) (issue above, item 4: THD
+  varlen layout).  GQA: query head h uses key/value head h // (Hq / Hkv).
+
+* LSE is the natural-log sum of exp of the scaled scores.  Per-row LSE layout:
+  [B, Hq, S] (BSHD) or [Hq, T] (THD).
+
+* Backward (standard softmax-attention chain rule, with the merged LSE):
+    Delta_i = <dO_i, O_i>
+    dS_a    = P_a * (<dO_i, v_a> - Delta_i)
+    dq_i    = scale * R(pos_q)^T sum_a dS_a R(pos_a) k_a
+    dk_a    = scale * R(pos_a)^T sum_{rows i, heads h of the group} dS_a R(pos_q) q_i
+    dv_a    = sum_{rows i, heads h of the group} P_a dO_i
+  Gradients are returned per tensor (dK(q), dV(q) for q = 1..p); nothing is
+  accumulated across calls.
+
+Everything is fp64; inputs are upcast from whatever float type they hold.
+No blocking, fusion or reordering beyond evaluating rows in independent
+groups.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+__all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_position",
+           "ttt_mask_row", "sequences", "fwd", "bwd", "fwd_rows", "bwd_rows", "Slice"]
+
+
+# ----------------------------------------------------------------------------- RoPE
+def inv_freq(D: int, base: float) -> np.ndarray:
+    """theta_k = base^(-2k/D), k = 0..D/2-1, in fp64."""
+    k = np.arange(D // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * k / D)
+
+
+def rotate_half(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """R(pos) x with rotate-half pairing: for k < D/2,
+    y_k = x_k cos(pos*theta_k) - x_{k+D/2} sin(pos*theta_k),
+    y_{k+D/2} = x_{k+D/2} cos(pos*theta_k) + x_k sin(pos*theta_k).
+    x: [..., D]; pos broadcasts against x[..., 0]."""
+    x = np.asarray(x, dtype=np.float64)
+    if base == 0:
+        return x.copy()
+    D = x.shape[-1]
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq(D, base)
+    c, s = np.cos(ang), np.sin(ang)
+    x1, x2 = x[..., : D // 2], x[..., D // 2:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def unrotate_half(g: np.ndarray, pos, base: float) -> np.ndarray:
+    """R(pos)^T g, the transpose (= inverse) rotation."""
+    return rotate_half(g, -np.asarray(pos, dtype=np.float64), base)
+
+
+def query_position(i, p: int):
+    return np.asarray(i) + (p - 1)
+
+
+def key_position(q: int, j):
+    """Position of the key that pass q produced at row j (q = 1 is the trunk)."""
+    return np.asarray(j) + (q - 1)
+
+
+# ----------------------------------------------------------------------------- mask
+def ttt_mask_row(i: int, p: int, L: int) -> np.ndarray:
+    """Explicit visibility of row i at pass p over the concatenated keys of a
+    length-L sequence, [K(1)_0..L-1 ; K(2)_0..L-1 ; ... ; K(p)_0..L-1]."""
+    m = np.zeros(p * L, dtype=bool)
+    m[: i + 1] = True                      # trunk: pass-1 keys j <= i
+    for q in range(2, p + 1):              # branch: passes 2..p at the same row
+        m[(q - 1) * L + i] = True
+    return m
+
+
+# ----------------------------------------------------------------------------- layouts
+class Slice:
+    """One sequence of the batch: batch index b (BSHD) and token range [start, start+L)."""
+
+    def __init__(self, b: int, start: int, L: int):
+        self.b, self.start, self.L = b, start, L
+
+    def take(self, x: np.ndarray, layout: str) -> np.ndarray:
+        """[L, H, D] fp64 view of this sequence from a BSHD or THD tensor."""
+        if layout == "bshd":
+            return np.asarray(x[self.b], dtype=np.float64)
+        return np.asarray(x[self.start: self.start + self.L], dtype=np.float64)
+
+
+def sequences(layout: str, shape: Sequence[int], cu_seqlens=None) -> list:
+    if layout == "bshd":
+        B, S = shape[0], shape[1]
+        return [Slice(b, 0, S) for b in range(B)]
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    return [Slice(0, int(cu[s]), int(cu[s + 1] - cu[s])) for s in range(len(cu) - 1)]
+
+
+def _lse_index(layout: str, sl: Slice, h: int, i):
+    if layout == "bshd":
+        return (sl.b, h, i)
+    return (h, sl.start + np.asarray(i))
+
+
+def _row_index(layout: str, sl: Slice, i):
+    if layout == "bshd":
+        return (sl.b, i)
+    return (sl.start + np.asarray(i),)
+
+
+# ----------------------------------------------------------------------------- core
+class _GroupKeys:
+    """Rotated concatenated keys and values of one (sequence, KV head) slice."""
+
+    def __init__(self, sl: Slice, g: int, ks, vs, p: int, layout: str, base: float):
+        L = sl.L
+        rows = np.arange(L)
+        kt, vt = [], []
+        for q in range(1, p + 1):
+            kt.append(rotate_half(sl.take(ks[q - 1], layout)[:, g, :], key_position(q, rows), base))
+            vt.append(sl.take(vs[q - 1], layout)[:, g, :])
+        self.keys = np.concatenate(kt, axis=0)     # [p*L, D] rotated
+        self.vals = np.concatenate(vt, axis=0)     # [p*L, D]
+        self.pos = np.concatenate([key_position(q, rows) for q in range(1, p + 1)])
+
+
+def _row_block_fwd(gk: _GroupKeys, q_rot: np.ndarray, rows: np.ndarray, p: int, L: int, scale: float):
+    """Scores, probabilities, LSE and O for a block of query rows (one head)."""
+    mask = np.stack([ttt_mask_row(int(i), p, L) for i in rows])          # [n, p*L]
+    s = scale * (q_rot @ gk.keys.T)
+    s = np.where(mask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    lse = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
+    P = np.exp(s - lse[:, None])
+    O = P @ gk.vals
+    return P, lse, O
+
+
+def _blocks(rows: np.ndarray, n: int):
+    for a in range(0, len(rows), n):
+        yield rows[a: a + n]
+
+
+def _block_rows(L: int, p: int) -> int:
+    # keep a block's [n, p*L] fp64 score matrix near 64 MB
+    return max(1, min(256, (8 << 20) // max(1, p * L)))
+
+
+def fwd_rows(q, ks, vs, p: int, sl: Slice, h: int, rows, *, layout: str, Hq: int, Hkv: int,
+             scale: float, base: float):
+    """O [n, D] and LSE [n] for rows `rows` of sequence `sl`, query head h, at pass p."""
+    rows = np.asarray(rows, dtype=np.int64)
+    g = h // (Hq // Hkv)
+    gk = _GroupKeys(sl, g, ks, vs, p, layout, base)
+    qs = sl.take(q, layout)[:, h, :]
+    O = np.empty((len(rows), qs.shape[-1]))
+    lse = np.empty(len(rows))
+    a = 0
+    for blk in _blocks(rows, _block_rows(sl.L, p)):
+        qr = rotate_half(qs[blk], query_position(blk, p), base)
+        _, l_, o_ = _row_block_fwd(gk, qr, blk, p, sl.L, scale)
+        O[a: a + len(blk)] = o_
+        lse[a: a + len(blk)] = l_
+        a += len(blk)
+    return O, lse
+
+
+def fwd(q, ks, vs, p: int, *, layout: str = "bshd", cu_seqlens=None, scale: Optional[float] = None,
+        base: float = 0.0):
+    """Full forward of pass p.  q: [B,S,Hq,D] or [T,Hq,D]; ks, vs: p tensors of
+    [B,S,Hkv,D] or [T,Hkv,D] (index 0 = trunk).  Returns (O fp64 like q, LSE fp64)."""
+    assert len(ks) >= p and len(vs) >= p and p >= 1
+    Hq, D = q.shape[-2], q.shape[-1]
+    Hkv = ks[0].shape[-2]
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    O = np.zeros(q.shape, dtype=np.float64)
+    if layout == "bshd":
+        lse = np.zeros((q.shape[0], Hq, q.shape[1]))
+    else:
+        lse = np.zeros((Hq, q.shape[0]))
+    for sl in sequences(layout, q.shape, cu_seqlens):
+        rows = np.arange(sl.L)
+        for h in range(Hq):
+            o_, l_ = fwd_rows(q, ks, vs, p, sl, h, rows, layout=layout, Hq=Hq, Hkv=Hkv,
+                              scale=scale, base=base)
+            O[_row_index(layout, sl, rows) + (h,)] = o_
+            lse[_lse_index(layout, sl, h, rows)] = l_
+    return O, lse
+
+
+def bwd_rows(q, ks, vs, dout, p: int, sl: Slice, g: int, rows, *, layout: str, Hq: int,
+             Hkv: int, scale: float, base: float):
+    """Backward contributions of query rows `rows` (all r heads of KV group g).
+
+    Returns (dq [r, n, D] for those rows, dk [p*L, D], dv [p*L, D]) where dk, dv
+    hold only the contributions of the given rows, over the concatenated keys.
+    A key's gradient is complete when `rows` holds every row that sees it
+    (trunk key j: all rows i >= j; branch key (q, i): row i)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    r = Hq // Hkv
+    gk = _GroupKeys(sl, g, ks, vs, p, layout, base)
+    D = gk.keys.shape[-1]
+    dq = np.zeros((r, len(rows), D))
+    dk_rot = np.zeros_like(gk.keys)
+    dv = np.zeros_like(gk.vals)
+    for hh in range(r):
+        h = g * r + hh
+        qs = sl.take(q, layout)[:, h, :]
+        dos = sl.take(dout, layout)[:, h, :]
+        a = 0
+        for blk in _blocks(rows, _block_rows(sl.L, p)):
+            qr = rotate_half(qs[blk], query_position(blk, p), base)
+            P, lse, O = _row_block_fwd(gk, qr, blk, p, sl.L, scale)
+            do = dos[blk]
+            delta = (do * O).sum(axis=1)
+            dP = do @ gk.vals.T
+            dS = P * (dP - delta[:, None])
+            dq_rot = scale * (dS @ gk.keys)
+            dq[hh, a: a + len(blk)] = unrotate_half(dq_rot, query_position(blk, p), base)
+            dk_rot += scale * (dS.T @ qr)
+            dv += P.T @ do
+            a += len(blk)
+    dk = unrotate_half(dk_rot, gk.pos, base)
+    return dq, dk, dv
+
+
+def bwd(q, ks, vs, dout, p: int, *, layout: str = "bshd", cu_seqlens=None,
+        scale: Optional[float] = None, base: float = 0.0):
+    """Full backward of pass p.  Returns (dQ like q, [dK(1..p)], [dV(1..p)]) in fp64."""
+    Hq, D = q.shape[-2], q.shape[-1]
+    Hkv = ks[0].shape[-2]
+    r = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    dQ = np.zeros(q.shape)
+    dK = [np.zeros(ks[0].shape) for _ in range(p)]
+    dV = [np.zeros(vs[0].shape) for _ in range(p)]
+    for sl in sequences(layout, q.shape, cu_seqlens):
+        rows = np.arange(sl.L)
+        for g in range(Hkv):
+            dq, dk, dv = bwd_rows(q, ks, vs, dout, p, sl, g, rows, layout=layout, Hq=Hq,
+                                  Hkv=Hkv, scale=scale, base=base)
+            for hh in range(r):
+                dQ[_row_index(layout, sl, rows) + (g * r + hh,)] = dq[hh]
+            for qq in range(p):
+                dK[qq][_row_index(layout, sl, rows) + (g,)] = dk[qq * sl.L:(qq + 1) * sl.L]
+                dV[qq][_row_index(layout, sl, rows) + (g,)] = dv[qq * sl.L:(qq + 1) * sl.L]
+    return dQ, dK, dV

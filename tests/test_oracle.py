@@ -1,0 +1,417 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each check derives the expected value independently: torch's fp64
+scaled_dot_product_attention (a library routine) on keys rotated through the
+complex-number form of rotate-half, closed forms, RoPE group identities, fp64
+autograd of an independently written brute force, central finite
+differences, and layout equivalences.  The last test plants mistakes in the
+oracle (on the CPU) and checks that the pins catch each of them.
+"""
+import contextlib
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import ttt_oracle as O
+
+F64 = torch.float64
+
+
+# ----------------------------------------------------------------------------- independent helpers
+def rope_complex(x: torch.Tensor, pos: torch.Tensor, base: float) -> torch.Tensor:
+    """Rotate-half RoPE written as complex multiplication: (x1 + i x2) * e^{i pos theta_k}."""
+    if base == 0:
+        return x.clone()
+    D = x.shape[-1]
+    theta = torch.tensor([math.pow(base, -2.0 * k / D) for k in range(D // 2)], dtype=F64)
+    ang = pos.to(F64)[..., None] * theta
+    z = torch.complex(x[..., : D // 2], x[..., D // 2:]) * torch.polar(torch.ones_like(ang), ang)
+    return torch.cat([z.real, z.imag], dim=-1)
+
+
+def dense_reference(q, ks, vs, p, scale, base, requires_grad=False):
+    """One sequence, BSHD with B=1 squeezed: q [S,Hq,D], ks/vs list of [S,Hkv,D] (torch fp64).
+
+    Builds the concatenated keys [K1; K2; ...; Kp] rotated at their positions and
+    the explicit boolean mask from tril/eye blocks, then calls torch's SDPA."""
+    S, Hq, D = q.shape
+    Hkv = ks[0].shape[1]
+    r = Hq // Hkv
+    i = torch.arange(S)
+    qr = rope_complex(q, (i + p - 1)[:, None].expand(S, Hq), base)
+    krs = [rope_complex(ks[0], i[:, None].expand(S, Hkv), base)]
+    for t in range(1, p):
+        krs.append(rope_complex(ks[t], (i + t)[:, None].expand(S, Hkv), base))
+    kc = torch.cat(krs, 0)                     # [pS, Hkv, D]
+    vc = torch.cat(list(vs[:p]), 0)
+    mask = torch.cat([torch.tril(torch.ones(S, S, dtype=torch.bool))] +
+                     [torch.eye(S, dtype=torch.bool)] * (p - 1), dim=1)   # [S, pS]
+    qh = qr.permute(1, 0, 2)                                        # [Hq, S, D]
+    kh = kc.permute(1, 0, 2).repeat_interleave(r, 0)
+    vh = vc.permute(1, 0, 2).repeat_interleave(r, 0)
+    o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask, scale=scale)
+    s = (qh @ kh.transpose(-1, -2)) * scale
+    lse = torch.logsumexp(s.masked_fill(~mask, -math.inf), dim=-1)  # [Hq, S]
+    return o.permute(1, 0, 2), lse
+
+
+def rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def make(S=13, Hq=4, Hkv=2, D=8, p=3, seed=0, B=None):
+    shp_q = (S, Hq, D) if B is None else (B, S, Hq, D)
+    shp_k = (S, Hkv, D) if B is None else (B, S, Hkv, D)
+    q = rand(shp_q, seed)
+    ks = [rand(shp_k, seed + 10 + t) for t in range(p)]
+    vs = [rand(shp_k, seed + 20 + t) for t in range(p)]
+    do = rand(shp_q, seed + 30)
+    return q, ks, vs, do
+
+
+# ----------------------------------------------------------------------------- pin checks (also run on planted mistakes)
+def check_rope_complex_form():
+    x = rand((5, 16), 1)
+    pos = np.array([0, 1, 7, 100, 4097])
+    for base in (1e4, 1e6):
+        a = O.rotate_half(x, pos, base)
+        b = rope_complex(torch.tensor(x), torch.tensor(pos), base).numpy()
+        assert np.max(np.abs(a - b)) < 1e-12
+
+
+def check_rope_single_pair():
+    D, base = 16, 1e4
+    for k in (0, 3, 7):
+        e = np.zeros(D); e[k] = 1.0
+        for m, n in ((5, 2), (40, 3), (9, 9)):
+            s = O.rotate_half(e, m, base) @ O.rotate_half(e, n, base)
+            assert abs(s - math.cos((m - n) * math.pow(base, -2.0 * k / D))) < 1e-12
+
+
+def check_rope_group():
+    x, y = rand((6, 32), 2), rand((6, 32), 3)
+    base = 1e6
+    m, n = np.array([0, 3, 50, 9, 1000, 31]), np.array([1, 1, 2, 40, 999, 0])
+    assert np.max(np.abs(O.rotate_half(x, 0, base) - x)) == 0
+    assert np.max(np.abs(O.unrotate_half(O.rotate_half(x, m, base), m, base) - x)) < 1e-12
+    assert np.max(np.abs(O.rotate_half(O.rotate_half(x, m, base), n, base) - O.rotate_half(x, m + n, base))) < 1e-12
+    for c in (1, 17, 32768):
+        a = (O.rotate_half(x, m + c, base) * O.rotate_half(y, n + c, base)).sum(-1)
+        b = (O.rotate_half(x, m, base) * O.rotate_half(y, n, base)).sum(-1)
+        assert np.max(np.abs(a - b)) < 1e-12
+
+
+def check_zero_query_closed_form(layout="bshd"):
+    """Q = 0: every visible score is 0, so LSE_i = ln(i + p) and O_i is the mean of
+    the visible value rows: V1[0..i] and Vq[i] for q = 2..p."""
+    Hq, Hkv, D = 4, 2, 8
+    lens = [7, 1, 12, 5]
+    for p in (1, 2, 4):
+        if layout == "bshd":
+            B, S = 2, 9
+            q = np.zeros((B, S, Hq, D))
+            ks = [rand((B, S, Hkv, D), 40 + t) for t in range(p)]
+            vs = [rand((B, S, Hkv, D), 50 + t) for t in range(p)]
+            o, lse = O.fwd(q, ks, vs, p, layout="bshd", base=1e4)
+            for b in range(B):
+                for i in range(S):
+                    for h in range(Hq):
+                        g = h // (Hq // Hkv)
+                        vis = [vs[0][b, j, g] for j in range(i + 1)] + [vs[t][b, i, g] for t in range(1, p)]
+                        assert abs(lse[b, h, i] - math.log(i + p)) < 1e-12
+                        assert np.max(np.abs(o[b, i, h] - np.mean(vis, axis=0))) < 1e-12
+        else:
+            cu = np.concatenate([[0], np.cumsum(lens)])
+            T = int(cu[-1])
+            q = np.zeros((T, Hq, D))
+            ks = [rand((T, Hkv, D), 60 + t) for t in range(p)]
+            vs = [rand((T, Hkv, D), 70 + t) for t in range(p)]
+            o, lse = O.fwd(q, ks, vs, p, layout="thd", cu_seqlens=cu, base=1e6)
+            for s in range(len(lens)):
+                for i in range(lens[s]):
+                    t0 = cu[s] + i
+                    for h in range(Hq):
+                        g = h // (Hq // Hkv)
+                        vis = [vs[0][cu[s] + j, g] for j in range(i + 1)] + [vs[t][t0, g] for t in range(1, p)]
+                        assert abs(lse[h, t0] - math.log(i + p)) < 1e-12
+                        assert np.max(np.abs(o[t0, h] - np.mean(vis, axis=0))) < 1e-12
+
+
+def check_sdpa_brute_force():
+    """Any p, RoPE on or off: oracle == torch SDPA over concatenated keys with an explicit mask."""
+    for p, base, (Hq, Hkv) in ((1, 1e4, (2, 1)), (2, 1e6, (4, 2)), (3, 1e4, (4, 4)), (5, 1e6, (6, 2)), (4, 0.0, (2, 2))):
+        q, ks, vs, _ = make(S=11, Hq=Hq, Hkv=Hkv, D=8, p=p, seed=p)
+        scale = 0.3
+        o, lse = O.fwd(q, ks, vs, p, layout="thd", cu_seqlens=[0, 11], scale=scale, base=base)
+        ro, rl = dense_reference(torch.tensor(q), [torch.tensor(k) for k in ks], [torch.tensor(v) for v in vs],
+                                 p, scale, base)
+        assert np.max(np.abs(o - ro.numpy())) < 1e-12
+        assert np.max(np.abs(lse - rl.numpy())) < 1e-12
+
+
+def check_p1_is_causal_sdpa():
+    q, ks, vs, _ = make(S=17, Hq=4, Hkv=2, D=16, p=1, seed=5)
+    base = 1e6
+    o, lse = O.fwd(q, ks, vs, 1, layout="thd", cu_seqlens=[0, 17], base=base)
+    i = torch.arange(17)
+    qr = rope_complex(torch.tensor(q), i[:, None].expand(17, 4), base).permute(1, 0, 2)
+    kr = rope_complex(torch.tensor(ks[0]), i[:, None].expand(17, 2), base).permute(1, 0, 2).repeat_interleave(2, 0)
+    vh = torch.tensor(vs[0]).permute(1, 0, 2).repeat_interleave(2, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qr, kr, vh, is_causal=True)
+    assert np.max(np.abs(o - ref.permute(1, 0, 2).numpy())) < 1e-12
+
+
+def check_merge_invariant():
+    """Trunk-only causal softmax and branch-only softmax, merged by logaddexp, equal the oracle."""
+    S, Hq, Hkv, D, p, base = 10, 2, 1, 8, 4, 1e4
+    q, ks, vs, _ = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=7)
+    scale = 1 / math.sqrt(D)
+    o, lse = O.fwd(q, ks, vs, p, layout="thd", cu_seqlens=[0, S], scale=scale, base=base)
+    i = torch.arange(S)
+    qt = torch.tensor(q)
+    for h in range(Hq):
+        qr = rope_complex(qt[:, h], i + p - 1, base)                       # [S, D]
+        kt = rope_complex(torch.tensor(ks[0][:, 0]), i, base)
+        st = (qr @ kt.T * scale).masked_fill(~torch.tril(torch.ones(S, S, dtype=torch.bool)), -math.inf)
+        lt = torch.logsumexp(st, -1)
+        ot = torch.softmax(st, -1) @ torch.tensor(vs[0][:, 0])
+        sb = torch.stack([(qr * rope_complex(torch.tensor(ks[t][:, 0]), i + t, base)).sum(-1) * scale
+                          for t in range(1, p)], -1)                        # [S, p-1]
+        lb = torch.logsumexp(sb, -1)
+        ob = (torch.softmax(sb, -1)[..., None] * torch.stack([torch.tensor(vs[t][:, 0]) for t in range(1, p)], 1)).sum(1)
+        l = torch.logaddexp(lt, lb)
+        om = torch.exp(lt - l)[:, None] * ot + torch.exp(lb - l)[:, None] * ob
+        assert np.max(np.abs(lse[h] - l.numpy())) < 1e-12
+        assert np.max(np.abs(o[:, h] - om.numpy())) < 1e-12
+
+
+def check_branch_relative_position():
+    """Branch score of pass q at pass p depends on p - q only: shifting every row's
+    position leaves it unchanged (rows i and i' with equal data give equal scores)."""
+    D, base, p = 16, 1e6, 5
+    S = 6
+    q1 = rand((1, 1, D), 80)
+    k1 = [rand((1, 1, D), 81 + t) for t in range(p)]
+    q = np.repeat(q1, S, axis=0); ks = [np.repeat(k, S, axis=0) for k in k1]; vs = [np.ones((S, 1, D)) * t for t in range(p)]
+    ks[0] = np.zeros((S, 1, D))  # zero trunk keys: every trunk score is 0
+    lse_rows = []
+    o, lse = O.fwd(q, ks, vs, p, layout="thd", cu_seqlens=[0, S], base=base)
+    # remove the trunk's (i+1) zero-score terms: exp(lse) - (i + 1) = sum of branch exps
+    for i in range(S):
+        lse_rows.append(math.log(math.exp(lse[0, i]) - (i + 1)))
+    assert max(lse_rows) - min(lse_rows) < 1e-12
+
+
+def check_grad_autograd():
+    for p, (Hq, Hkv), base in ((1, (2, 1), 1e4), (3, (4, 2), 1e6), (4, (2, 2), 0.0)):
+        S, D = 9, 8
+        q, ks, vs, do = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=11 + p)
+        scale = 0.4
+        dq, dk, dv = O.bwd(q, ks, vs, do, p, layout="thd", cu_seqlens=[0, S], scale=scale, base=base)
+        qt = torch.tensor(q, requires_grad=True)
+        kt = [torch.tensor(k, requires_grad=True) for k in ks]
+        vt = [torch.tensor(v, requires_grad=True) for v in vs]
+        ro, _ = dense_reference(qt, kt, vt, p, scale, base)
+        (ro * torch.tensor(do)).sum().backward()
+        assert np.max(np.abs(dq - qt.grad.numpy())) < 1e-10
+        for t in range(p):
+            assert np.max(np.abs(dk[t] - kt[t].grad.numpy())) < 1e-10
+            assert np.max(np.abs(dv[t] - vt[t].grad.numpy())) < 1e-10
+
+
+def check_grad_finite_difference():
+    S, Hq, Hkv, D, p, base = 6, 2, 1, 4, 3, 1e4
+    q, ks, vs, do = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=21)
+    kw = dict(layout="thd", cu_seqlens=[0, S], scale=0.5, base=base)
+    dq, dk, dv = O.bwd(q, ks, vs, do, p, **kw)
+
+    def loss(q_, ks_, vs_):
+        o, _ = O.fwd(q_, ks_, vs_, p, **kw)
+        return float((o * do).sum())
+
+    h = 1e-6
+    rng = np.random.default_rng(0)
+    for _ in range(6):
+        idx = tuple(int(rng.integers(n)) for n in q.shape)
+        qp, qm = q.copy(), q.copy(); qp[idx] += h; qm[idx] -= h
+        fd = (loss(qp, ks, vs) - loss(qm, ks, vs)) / (2 * h)
+        assert abs(fd - dq[idx]) <= 1e-7 * max(1.0, abs(fd))
+        t = int(rng.integers(p))
+        idx = tuple(int(rng.integers(n)) for n in ks[0].shape)
+        for arr, grad in ((ks, dk), (vs, dv)):
+            ap = [a.copy() for a in arr]; am = [a.copy() for a in arr]
+            ap[t][idx] += h; am[t][idx] -= h
+            if arr is ks:
+                fd = (loss(q, ap, vs) - loss(q, am, vs)) / (2 * h)
+            else:
+                fd = (loss(q, ks, ap) - loss(q, ks, am)) / (2 * h)
+            assert abs(fd - grad[t][idx]) <= 1e-7 * max(1.0, abs(fd))
+
+
+def check_thd_equals_bshd():
+    B, S, Hq, Hkv, D, p, base = 3, 7, 4, 2, 8, 3, 1e6
+    q, ks, vs, do = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=31, B=B)
+    o1, l1 = O.fwd(q, ks, vs, p, layout="bshd", base=base)
+    cu = [0, 7, 14, 21]
+    flat = lambda x: x.reshape(B * S, *x.shape[2:])
+    o2, l2 = O.fwd(flat(q), [flat(k) for k in ks], [flat(v) for v in vs], p, layout="thd", cu_seqlens=cu, base=base)
+    assert np.max(np.abs(flat(o1) - o2)) == 0
+    assert np.max(np.abs(l1.transpose(1, 0, 2).reshape(Hq, B * S) - l2)) == 0
+    g1 = O.bwd(q, ks, vs, do, p, layout="bshd", base=base)
+    g2 = O.bwd(flat(q), [flat(k) for k in ks], [flat(v) for v in vs], flat(do), p, layout="thd", cu_seqlens=cu, base=base)
+    assert np.max(np.abs(flat(g1[0]) - g2[0])) == 0
+    for t in range(p):
+        assert np.max(np.abs(flat(g1[1][t]) - g2[1][t])) == 0
+        assert np.max(np.abs(flat(g1[2][t]) - g2[2][t])) == 0
+
+
+def check_thd_isolation():
+    lens = [5, 8, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, Hq, Hkv, D, p = int(cu[-1]), 2, 1, 8, 3
+    q, ks, vs, do = make(S=T, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=41)
+    o1, l1 = O.fwd(q, ks, vs, p, layout="thd", cu_seqlens=cu, base=1e4)
+    q2, ks2, vs2 = q.copy(), [k.copy() for k in ks], [v.copy() for v in vs]
+    sl = slice(cu[1], cu[2])
+    q2[sl] += 1.0; ks2[0][sl] -= 2.0; ks2[2][sl] *= 3.0; vs2[0][sl] += 5.0; vs2[1][sl] -= 1.0
+    o2, l2 = O.fwd(q2, ks2, vs2, p, layout="thd", cu_seqlens=cu, base=1e4)
+    keep = np.r_[cu[0]:cu[1], cu[2]:cu[3]]
+    assert np.array_equal(o1[keep], o2[keep]) and np.array_equal(l1[:, keep], l2[:, keep])
+    assert not np.allclose(o1[sl], o2[sl])
+
+
+def check_gqa_is_repeated_kv():
+    S, Hq, Hkv, D, p = 8, 6, 2, 8, 3
+    q, ks, vs, do = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=51)
+    kw = dict(layout="thd", cu_seqlens=[0, S], base=1e6)
+    o1, l1 = O.fwd(q, ks, vs, p, **kw)
+    rep = lambda x: np.repeat(x, Hq // Hkv, axis=1)
+    o2, l2 = O.fwd(q, [rep(k) for k in ks], [rep(v) for v in vs], p, **kw)
+    assert np.max(np.abs(o1 - o2)) < 1e-14 and np.max(np.abs(l1 - l2)) < 1e-14
+    g1 = O.bwd(q, ks, vs, do, p, **kw)
+    g2 = O.bwd(q, [rep(k) for k in ks], [rep(v) for v in vs], do, p, **kw)
+    assert np.max(np.abs(g1[0] - g2[0])) < 1e-13
+    for t in range(p):
+        sumg = lambda x: x.reshape(S, Hkv, Hq // Hkv, D).sum(2)
+        assert np.max(np.abs(g1[1][t] - sumg(g2[1][t]))) < 1e-13
+        assert np.max(np.abs(g1[2][t] - sumg(g2[2][t]))) < 1e-13
+
+
+def check_sampled_rows_match_full():
+    """bwd_rows over a row subset gives exact key gradients for keys all of whose rows are included."""
+    S, Hq, Hkv, D, p, base = 12, 4, 2, 8, 3, 1e6
+    q, ks, vs, do = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=61)
+    kw = dict(layout="thd", Hq=Hq, Hkv=Hkv, scale=1 / math.sqrt(D), base=base)
+    dQ, dK, dV = O.bwd(q, ks, vs, do, p, layout="thd", cu_seqlens=[0, S], base=base)
+    sl = O.Slice(0, 0, S)
+    rows = np.arange(8, S)
+    dq, dk, dv = O.bwd_rows(q, ks, vs, do, p, sl, 1, rows, **kw)
+    assert np.max(np.abs(dq[0] - dQ[8:, 2])) < 1e-13
+    assert np.max(np.abs(dk[8:S] - dK[0][8:, 1])) < 1e-13           # trunk keys j >= 8
+    assert np.max(np.abs(dv[S + 8: 2 * S] - dV[1][8:, 1])) < 1e-13  # branch keys of pass 2 at rows >= 8
+    o, l = O.fwd_rows(q, ks, vs, p, sl, 3, [0, 5, 11], layout="thd", Hq=Hq, Hkv=Hkv, scale=1 / math.sqrt(D), base=base)
+    of, lf = O.fwd(q, ks, vs, p, layout="thd", cu_seqlens=[0, S], base=base)
+    assert np.max(np.abs(o - of[[0, 5, 11], 3])) < 1e-14 and np.max(np.abs(l - lf[3, [0, 5, 11]])) < 1e-14
+
+
+PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check_zero_query_closed_form,
+        lambda: check_zero_query_closed_form("thd"), check_sdpa_brute_force, check_p1_is_causal_sdpa,
+        check_merge_invariant, check_branch_relative_position, check_grad_autograd,
+        check_grad_finite_difference, check_thd_equals_bshd, check_thd_isolation, check_gqa_is_repeated_kv,
+        check_sampled_rows_match_full]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
+def test_pin(pin):
+    pin()
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+@contextlib.contextmanager
+def planted(name, fn):
+    old = getattr(O, name)
+    setattr(O, name, fn)
+    try:
+        yield
+    finally:
+        setattr(O, name, old)
+
+
+def _orig(name):
+    return getattr(O, name)
+
+
+def _mask_no_branch(i, p, L):
+    m = np.zeros(p * L, dtype=bool); m[: i + 1] = True; return m
+
+
+def _mask_strict_causal(i, p, L):
+    m = _orig_mask(i, p, L); m[i] = i == 0; return m
+
+
+def _mask_branch_next_row(i, p, L):
+    m = np.zeros(p * L, dtype=bool); m[: i + 1] = True
+    for q in range(2, p + 1):
+        m[(q - 1) * L + min(i + 1, L - 1)] = True
+    return m
+
+
+_orig_mask = O.ttt_mask_row
+_orig_rot = O.rotate_half
+_orig_qpos = O.query_position
+_orig_kpos = O.key_position
+_orig_inv = O.inv_freq
+_orig_blk = O._row_block_fwd
+
+
+def _rot_sign(x, pos, base):
+    return _orig_rot(x, -np.asarray(pos, dtype=np.float64), base)
+
+
+def _rot_pairing(x, pos, base):
+    # adjacent-pair (interleaved) rotation instead of rotate-half
+    x = np.asarray(x, dtype=np.float64)
+    if base == 0:
+        return x.copy()
+    D = x.shape[-1]
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * _orig_inv(D, base)
+    c, s = np.cos(ang), np.sin(ang)
+    y = x.copy()
+    y[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    y[..., 1::2] = x[..., 1::2] * c + x[..., 0::2] * s
+    return y
+
+
+def _blk_transposed_v(gk, q_rot, rows, p, L, scale):
+    P, lse, O_ = _orig_blk(gk, q_rot, rows, p, L, scale)
+    return P, lse, O_ * 1.0 + (P @ gk.vals[:, ::-1] - O_) * 1.0
+
+
+MISTAKES = [
+    ("ttt_mask_row", _mask_no_branch),
+    ("ttt_mask_row", _mask_strict_causal),
+    ("ttt_mask_row", _mask_branch_next_row),
+    ("rotate_half", _rot_sign),
+    ("rotate_half", _rot_pairing),
+    ("query_position", lambda i, p: np.asarray(i) + p),
+    ("query_position", lambda i, p: np.asarray(i)),
+    ("key_position", lambda q, j: np.asarray(j)),
+    ("key_position", lambda q, j: np.asarray(j) + q),
+    ("inv_freq", lambda D, base: np.power(np.float64(base), -1.0 * np.arange(D // 2) / D)),
+    ("_row_block_fwd", _blk_transposed_v),
+]
+
+
+@pytest.mark.parametrize("name,fn", MISTAKES, ids=[f"{n}-{i}" for i, (n, _) in enumerate(MISTAKES)])
+def test_planted_mistake_is_caught(name, fn):
+    caught = 0
+    with planted(name, fn):
+        for pin in PINS:
+            try:
+                pin()
+            except (AssertionError, ValueError, IndexError):
+                caught += 1
+    assert caught >= 1, f"no pin catches a planted mistake in {name}"
