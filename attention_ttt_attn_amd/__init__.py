@@ -1,0 +1,224 @@
+"""Python binding of libtttattn (multi-pass EAGLE-3 TTT draft attention, MI355X).
+
+Thin ctypes marshalling over the C ABI in include/tttattn.h: torch is used only
+to own device memory and to name the current HIP stream.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback path, and
+importing the functions fails loudly when the built library is missing.
+
+    o, lse = fwd(q, ks, vs, p, rope_base=1e6)
+    dq, dks, dvs = bwd(q, ks, vs, o, lse, dout, p, rope_base=1e6)
+
+`ks`/`vs` are the pass 1..p key/value tensors (index 0 = pass 1 = trunk).  BSHD
+tensors are [B, S, H, D]; pass `cu_seqlens` (int32 on the device) for THD
+tensors [T, H, D].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = ["fwd", "bwd", "workspace_bytes", "TTTAttnError", "library", "library_path", "Desc",
+           "LAYOUT_BSHD", "LAYOUT_THD", "DTYPE_BF16", "DTYPE_FP32", "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libtttattn.so")
+
+LAYOUT_BSHD, LAYOUT_THD = 0, 1
+DTYPE_BF16, DTYPE_FP32 = 0, 1
+STATUS = {0: "TTT_OK", 1: "TTT_ERR_NULL_ARG", 2: "TTT_ERR_BAD_SHAPE", 3: "TTT_ERR_UNSUPPORTED",
+          4: "TTT_ERR_MISALIGNED", 5: "TTT_ERR_WORKSPACE", 6: "TTT_ERR_HIP", 7: "TTT_ERR_ABI"}
+MAX_PASSES = 16
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("layout", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("o_dtype", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("check_cu_seqlens", ctypes.c_int32),
+        ("cu_seqlens", ctypes.c_void_p),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("pass_index", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("rope_base", ctypes.c_float),
+        ("q_stride", ctypes.c_int64 * 3),
+        ("kv_stride", ctypes.c_int64 * 3),
+        ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class TTTAttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libtttattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"libtttattn.so not found at {library_path}; build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(library_path)
+        vp, sz = ctypes.c_void_p, ctypes.c_size_t
+        lib.ttt_attn_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.c_int]
+        lib.ttt_attn_workspace_bytes.restype = sz
+        lib.ttt_attn_fwd.argtypes = [ctypes.POINTER(Desc), vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp,
+                                     sz, vp]
+        lib.ttt_attn_fwd.restype = ctypes.c_int
+        lib.ttt_attn_bwd.argtypes = [ctypes.POINTER(Desc), vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp,
+                                     ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
+        lib.ttt_attn_bwd.restype = ctypes.c_int
+        lib.ttt_attn_status_string.argtypes = [ctypes.c_int]
+        lib.ttt_attn_status_string.restype = ctypes.c_char_p
+        lib.ttt_attn_last_error.argtypes = []
+        lib.ttt_attn_last_error.restype = ctypes.c_char_p
+        lib.ttt_attn_abi_version.argtypes = []
+        lib.ttt_attn_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise TTTAttnError(status, library().ttt_attn_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _strides3(t, thd: bool):
+    s = t.stride()
+    if s[-1] != 1:
+        raise ValueError("the head_dim axis must be contiguous")
+    return (0, s[0], s[1]) if thd else (s[0], s[1], s[2])
+
+
+def make_desc(q, ks, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0, rope_base: float = 0.0,
+              o_dtype: Optional[int] = None, o_like=None, check_cu_seqlens: bool = False) -> Desc:
+    thd = cu_seqlens is not None
+    d = Desc()
+    d.struct_size = ctypes.sizeof(Desc)
+    d.layout = LAYOUT_THD if thd else LAYOUT_BSHD
+    d.dtype = _dtype_code(q)
+    d.o_dtype = d.dtype if o_dtype is None else o_dtype
+    if thd:
+        d.batch, d.seqlen = 1, q.shape[0]
+        d.num_seqs = cu_seqlens.numel() - 1
+        d.cu_seqlens = cu_seqlens.data_ptr()
+    else:
+        d.batch, d.seqlen = q.shape[0], q.shape[1]
+    d.check_cu_seqlens = int(bool(check_cu_seqlens))
+    d.num_q_heads, d.head_dim = q.shape[-2], q.shape[-1]
+    d.num_kv_heads = ks[0].shape[-2]
+    d.pass_index = p
+    d.softmax_scale = softmax_scale
+    d.rope_base = rope_base
+    d.q_stride[:] = _strides3(q, thd)
+    d.kv_stride[:] = _strides3(ks[0], thd)
+    d.o_stride[:] = _strides3(o_like if o_like is not None else q, thd)
+    return d
+
+
+def workspace_bytes(desc: Desc, for_bwd: bool) -> int:
+    return int(library().ttt_attn_workspace_bytes(ctypes.byref(desc), int(bool(for_bwd))))
+
+
+def _ptrs(ts):
+    arr = (ctypes.c_void_p * MAX_PASSES)()
+    for i, t in enumerate(ts):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes: int, device, ws):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    return ws
+
+
+def _ws_ptr(ws):
+    if ws is None:
+        return None, 0
+    addr = ws.data_ptr()
+    aligned = (addr + 255) & ~255
+    return ctypes.c_void_p(aligned), ws.numel() - (aligned - addr)
+
+
+def fwd(q, ks: Sequence, vs: Sequence, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0,
+        rope_base: float = 0.0, o_fp32: bool = False, out=None, lse=None, workspace=None, stream=None,
+        check_cu_seqlens: bool = False):
+    """Forward of TTT pass p.  Returns (o, lse); lse is fp32 [B,Hq,S] or [Hq,T]."""
+    torch = _torch()
+    thd = cu_seqlens is not None
+    o_dtype = DTYPE_FP32 if (o_fp32 or q.dtype == torch.float32) else _dtype_code(q)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if o_dtype == DTYPE_FP32 else q.dtype, device=q.device)
+    if lse is None:
+        shape = (q.shape[-2], q.shape[0]) if thd else (q.shape[0], q.shape[2], q.shape[1])
+        lse = torch.empty(shape, dtype=torch.float32, device=q.device)
+    d = make_desc(q, ks, p, cu_seqlens=cu_seqlens, softmax_scale=softmax_scale, rope_base=rope_base,
+                  o_dtype=o_dtype, o_like=out, check_cu_seqlens=check_cu_seqlens)
+    nbytes = workspace_bytes(d, False)
+    ws = _workspace(nbytes, q.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    _check(library().ttt_attn_fwd(ctypes.byref(d), q.data_ptr(), _ptrs(ks[:p]), _ptrs(vs[:p]), out.data_ptr(),
+                                  lse.data_ptr(), wp, wn, _stream(stream)))
+    return out, lse
+
+
+def bwd(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0,
+        rope_base: float = 0.0, dq=None, dks=None, dvs=None, workspace=None, stream=None,
+        check_cu_seqlens: bool = False):
+    """Backward of TTT pass p.  Returns (dq, [dk_1..dk_p], [dv_1..dv_p])."""
+    torch = _torch()
+    o_dtype = _dtype_code(o)
+    d = make_desc(q, ks, p, cu_seqlens=cu_seqlens, softmax_scale=softmax_scale, rope_base=rope_base,
+                  o_dtype=o_dtype, o_like=o, check_cu_seqlens=check_cu_seqlens)
+    if dout.stride() != o.stride():
+        raise ValueError("dout must have the strides of o")
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dks is None:
+        dks = [torch.empty_like(ks[0]) for _ in range(p)]
+    if dvs is None:
+        dvs = [torch.empty_like(vs[0]) for _ in range(p)]
+    nbytes = workspace_bytes(d, True)
+    ws = _workspace(nbytes, q.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    _check(library().ttt_attn_bwd(ctypes.byref(d), q.data_ptr(), _ptrs(ks[:p]), _ptrs(vs[:p]), o.data_ptr(),
+                                  lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), _ptrs(dks[:p]), _ptrs(dvs[:p]),
+                                  wp, wn, _stream(stream)))
+    return dq, dks, dvs

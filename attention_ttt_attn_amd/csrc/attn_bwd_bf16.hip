@@ -1,0 +1,532 @@
+// bf16 backward of the multi-pass TTT attention: probabilities are recomputed
+// from the forward's merged LSE (NeMo-RL issue "DFlash/DSpark and EAGLE-3 TTT
+// draft co-training ...", "What I'm working on", item 1: exact joint-LSE merge
+// -- the merged LSE normalises trunk and branch probabilities alike).
+//
+//   Delta_i = <dO_i, O_i>,  P_a = exp(s_a - LSE_i),  dS_a = P_a (<dO_i, v_a> - Delta_i)
+//   dq~_i  = sigma sum_a dS_a k~_a            (trunk keys and branch keys)
+//   dk~_a  = sigma sum_{i,h} dS_a q~_i,  dv_a = sum_{i,h} P_a dO_i
+//   dq = R(i+p-1)^T dq~,  dk^(1)_j = R(j)^T dk~,  dk^(q)_i = R(i+q-1)^T dk~
+//
+// Three kernels:
+// * dq_bf16_kernel (query-outer, MFMA): per 128 query rows of one head, loops
+//   over the causal key tiles and accumulates dQ~^T = K~^T dS^T; the epilogue
+//   adds the branch terms of passes 2..p (row-local, xor-shuffle reductions),
+//   un-rotates and writes dQ.  No atomics: deterministic.
+// * dkdv_bf16_kernel (key-outer, MFMA): per 128 trunk keys of one KV head,
+//   loops over the r query heads of the group and the query rows i >= j;
+//   dK~^T and dV^T stay in VGPRs; un-rotated in the epilogue.
+// * branch_bwd_bf16_kernel (HBM-bound, no MFMA): dK^(q), dV^(q) for q = 2..p at
+//   every row, summed over the group's heads with xor-shuffle dot products.
+// MFMA operand layouts follow the forward: transposed products so that one
+// product's accumulator is the next one's B operand (A rows read permuted).
+#include "kernels.hpp"
+
+namespace ttt {
+
+namespace bwd {
+
+constexpr int D = 128;
+constexpr int KPAD = D + 8;
+constexpr int BN = 64;        // dQ kernel: keys per tile
+constexpr int BM = kBwdBQ;    // dQ kernel: query rows per workgroup
+constexpr int BKV = kBwdBKV;  // dK/dV kernel: keys per workgroup
+constexpr int BQ = 64;        // dK/dV kernel: query rows per step
+constexpr int TPAD = 64 + 8;  // transposed LDS rows of 64 tokens
+constexpr int OPAD = D + 4;
+
+__device__ __forceinline__ int perm_row(int a) { return (a & ~0xC) | ((a & 4) << 1) | ((a & 8) >> 1); }
+
+// ============================================================================= dQ
+struct DqSmem {
+  union {
+    struct {
+      _Float16 k[BN][KPAD];   // K~ rows (A of S^T)
+      uint16_t v[BN][KPAD];   // V rows  (A of dP^T)
+      _Float16 kt[D][TPAD];   // K~^T    (A of dQ^T)
+    } loop;
+    float acc[BM][OPAD];
+  };
+};
+
+__global__ void __launch_bounds__(256, 2)
+    dq_bf16_kernel(Prob P, const uint16_t* __restrict__ q, PassPtrs kv, const float* __restrict__ lse,
+                   const uint16_t* __restrict__ dout, const _Float16* __restrict__ kt,
+                   const _Float16* __restrict__ ktt, const _Float16* __restrict__ qt, const float* __restrict__ delta,
+                   const int4* __restrict__ tiles, const float* __restrict__ cosT, const float* __restrict__ sinT,
+                   uint16_t* __restrict__ dq) {
+  __shared__ __attribute__((aligned(16))) DqSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int r = P.r;
+  const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
+  const int logical = ((kk / r) * 8 + xcd) * r + (kk % r);
+  const int hr = logical % r, rest = logical / r;
+  const int g = rest % P.Hkv, tix = rest / P.Hkv;
+  int b, t, start, L, slot0;
+  if (P.layout == 0) {
+    const int nqt = (P.stok + BM - 1) / BM;
+    if (tix >= P.B * nqt) return;
+    t = nqt - 1 - tix / P.B;
+    b = tix % P.B;
+    start = 0;
+    L = P.stok;
+    slot0 = 0;
+  } else {
+    if (tix >= tiles[0].x) return;
+    const int4 e = tiles[1 + tix];
+    t = e.x, start = e.y, L = e.z, slot0 = e.w, b = 0;
+  }
+  const int h = g * r + hr;
+  const int row0 = t * BM;
+  const int my_row = row0 + wv * 32 + l32;
+  const bool row_ok = my_row < L;
+
+  // B operands of this lane's query: Q~ (fp16, pre-rotated) and dO (bf16)
+  f16x8 qf[8];
+  bf16x8 dof[8];
+  {
+    const _Float16* qrow = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row) * D;
+    const uint16_t* grow = dout + b * P.os_b + (int64_t)(start + my_row) * P.os_t + h * P.os_h;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int d0 = c * 16 + hf * 8;
+      qf[c] = *(const f16x8*)(qrow + d0);
+      u32x4 gv = row_ok ? *(const u32x4*)(grow + d0) : u32x4{0, 0, 0, 0};
+      dof[c] = __builtin_bit_cast(bf16x8, gv);
+    }
+  }
+  const float lse2 = row_ok ? lse[b * P.lse_b + h * P.lse_h + start + my_row] * kLog2e : 0.f;
+  const float dl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row];
+  const float sl2 = P.scale_log2;
+
+  const int qend = min(row0 + BM, L);
+  const int nkt = (qend + BN - 1) / BN;
+  const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
+  const _Float16* ktbase = ktt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
+  const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * P.ks_b + (int64_t)start * P.ks_t + g * P.ks_h;
+  const int krow = tid >> 4, kch = tid & 15;
+  const int trow = tid >> 3, tch = tid & 7;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[d4][v] = 0.f;
+  const int prow = perm_row(l32);
+  const int wave_row0 = row0 + wv * 32;
+
+  for (int kt_ = 0; kt_ < nkt; ++kt_) {
+    {
+      const int key0 = kt_ * BN;
+      __syncthreads();  // previous tile's LDS reads are done
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int kr = key0 + krow + 16 * it;
+        *(u32x4*)&sm.loop.k[krow + 16 * it][kch * 8] = *(const u32x4*)(kbase + (int64_t)kr * D + kch * 8);
+        *(u32x4*)&sm.loop.v[krow + 16 * it][kch * 8] =
+            kr < L ? *(const u32x4*)(vbase + (int64_t)kr * P.ks_t + kch * 8) : u32x4{0, 0, 0, 0};
+        *(u32x4*)&sm.loop.kt[trow + 32 * it][tch * 8] =
+            *(const u32x4*)(ktbase + (int64_t)(trow + 32 * it) * P.spad + key0 + tch * 8);
+      }
+      __syncthreads();
+    }
+    const int key0 = kt_ * BN;
+    if (key0 > wave_row0 + 31) continue;  // whole tile above this wave's rows
+
+    f32x16 s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kb][v] = dp[kb][v] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f16x8 a = *(const f16x8*)&sm.loop.k[kb * 32 + prow][c * 16 + hf * 8];
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], s[kb], 0, 0, 0);
+        const bf16x8 a2 = *(const bf16x8*)&sm.loop.v[kb * 32 + prow][c * 16 + hf * 8];
+        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, dof[c], dp[kb], 0, 0, 0);
+      }
+    }
+    const bool need_mask = key0 + BN - 1 > wave_row0;
+    f16x8 dsb[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float pr = fast_exp2(s[kb][v] * sl2 - lse2);
+        if (need_mask) {
+          const int key = key0 + kb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
+          if (key > my_row) pr = 0.f;
+        }
+        if (!row_ok) pr = 0.f;
+        dsb[kb * 2 + (v >> 3)][v & 7] = (_Float16)(pr * (dp[kb][v] - dl));
+      }
+#pragma unroll
+    for (int c2 = 0; c2 < 4; ++c2)
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4) {
+        const f16x8 a = *(const f16x8*)&sm.loop.kt[d4 * 32 + l32][c2 * 16 + hf * 8];
+        acc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, dsb[c2], acc[d4], 0, 0, 0);
+      }
+  }
+  __syncthreads();
+  {
+    const int lr = wv * 32 + l32;
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = acc[d4][v4 * 4 + e] * P.scale;
+        *(f32x4*)&sm.acc[lr][d4 * 32 + v4 * 8 + hf * 4] = w;
+      }
+  }
+  __syncthreads();
+
+  // row-major epilogue: branch terms, un-rotation, store
+  const int c8 = tid & 7;
+  const int dlo = c8 * 8, dhi = 64 + c8 * 8;
+  for (int rp = 0; rp < BM; rp += 32) {
+    const int lr = rp + (tid >> 3);
+    const int i = row0 + lr;
+    if (i >= L) continue;
+    float a[16];
+    {
+      const f32x4* x = (const f32x4*)&sm.acc[lr][dlo];
+      const f32x4* y = (const f32x4*)&sm.acc[lr][dhi];
+      f32x4 x0 = x[0], x1 = x[1], y0 = y[0], y1 = y[1];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = x0[e], a[4 + e] = x1[e], a[8 + e] = y0[e], a[12 + e] = y1[e];
+    }
+    const int pos = i + P.p - 1;
+    const float* cq = cosT + (int64_t)pos * 64 + dlo;
+    const float* sq = sinT + (int64_t)pos * 64 + dlo;
+    if (P.p > 1) {
+      float qr[16], go[16];
+      {
+        const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + i) * P.qs_t + h * P.qs_h;
+        const uint16_t* grow = dout + b * P.os_b + (int64_t)(start + i) * P.os_t + h * P.os_h;
+        float x1[8], x2[8];
+        unpack_bf8(*(const u32x4*)(qrow + dlo), x1);
+        unpack_bf8(*(const u32x4*)(qrow + dhi), x2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          qr[e] = x1[e] * cq[e] - x2[e] * sq[e];
+          qr[8 + e] = x2[e] * cq[e] + x1[e] * sq[e];
+        }
+        unpack_bf8(*(const u32x4*)(grow + dlo), go);
+        unpack_bf8(*(const u32x4*)(grow + dhi), go + 8);
+      }
+      const float lse_i = lse[b * P.lse_b + h * P.lse_h + start + i];
+      const float dl_i = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + i];
+      const int64_t koff = b * P.ks_b + (int64_t)(start + i) * P.ks_t + g * P.ks_h;
+      for (int qq = 2; qq <= P.p; ++qq) {
+        const uint16_t* krow_ = (const uint16_t*)kv.k[qq - 1] + koff;
+        const uint16_t* vrow_ = (const uint16_t*)kv.v[qq - 1] + koff;
+        float x1[8], x2[8], v1[8], v2[8];
+        unpack_bf8(*(const u32x4*)(krow_ + dlo), x1);
+        unpack_bf8(*(const u32x4*)(krow_ + dhi), x2);
+        unpack_bf8(*(const u32x4*)(vrow_ + dlo), v1);
+        unpack_bf8(*(const u32x4*)(vrow_ + dhi), v2);
+        const int pk = i + qq - 1;
+        const float* ck = cosT + (int64_t)pk * 64 + dlo;
+        const float* sk = sinT + (int64_t)pk * 64 + dlo;
+        float kr[16];
+        float ps = 0.f, pd = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          kr[e] = x1[e] * ck[e] - x2[e] * sk[e];
+          kr[8 + e] = x2[e] * ck[e] + x1[e] * sk[e];
+          ps += qr[e] * kr[e] + qr[8 + e] * kr[8 + e];
+          pd += go[e] * v1[e] + go[8 + e] * v2[e];
+        }
+#pragma unroll
+        for (int m = 1; m < 8; m <<= 1) {
+          ps += __shfl_xor(ps, m, 64);
+          pd += __shfl_xor(pd, m, 64);
+        }
+        const float pr = __expf(ps * P.scale - lse_i);
+        const float dsv = pr * (pd - dl_i) * P.scale;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) a[e] += dsv * kr[e];
+      }
+    }
+    float res[16];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      res[e] = a[e] * cq[e] + a[8 + e] * sq[e];
+      res[8 + e] = a[8 + e] * cq[e] - a[e] * sq[e];
+    }
+    uint16_t* orow = dq + b * P.qs_b + (int64_t)(start + i) * P.qs_t + h * P.qs_h;
+    *(u32x4*)(orow + dlo) = pack_bf8(res);
+    *(u32x4*)(orow + dhi) = pack_bf8(res + 8);
+  }
+}
+
+// ============================================================================= dK/dV (trunk)
+struct KvSmem {
+  _Float16 q[BQ][KPAD];    // Q~ rows   (A of S)
+  uint16_t g[BQ][KPAD];    // dO rows   (A of dP)
+  _Float16 qt[D][TPAD];    // Q~^T      (A of dK^T)
+  uint16_t gt[D][TPAD];    // dO^T      (A of dV^T)
+  float lse2[BQ];
+  float dl[BQ];
+};
+
+__global__ void __launch_bounds__(256, 1)
+    dkdv_bf16_kernel(Prob P, PassPtrs kv, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
+                     const _Float16* __restrict__ kt, const _Float16* __restrict__ qt,
+                     const _Float16* __restrict__ qtt, const uint16_t* __restrict__ dot,
+                     const float* __restrict__ delta, const int4* __restrict__ tiles, const float* __restrict__ cosT,
+                     const float* __restrict__ sinT, PassGradPtrs gr) {
+  __shared__ __attribute__((aligned(16))) KvSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int g = blockIdx.x % P.Hkv, tix = blockIdx.x / P.Hkv;
+  int b, t, start, L, slot0;
+  if (P.layout == 0) {
+    const int nkt = (P.stok + BKV - 1) / BKV;
+    if (tix >= P.B * nkt) return;
+    t = tix / P.B;
+    b = tix % P.B;
+    start = 0;
+    L = P.stok;
+    slot0 = 0;
+  } else {
+    if (tix >= tiles[0].x) return;
+    const int4 e = tiles[1 + tix];
+    t = e.x, start = e.y, L = e.z, slot0 = e.w, b = 0;
+  }
+  const int kv0 = t * BKV;
+  const int my_key = kv0 + wv * 32 + l32;
+  const bool key_ok = my_key < L;
+
+  f16x8 kf[8];
+  bf16x8 vf[8];
+  {
+    const _Float16* krow = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0 + my_key) * D;
+    const uint16_t* vrow = (const uint16_t*)kv.v[0] + b * P.ks_b + (int64_t)(start + my_key) * P.ks_t + g * P.ks_h;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int d0 = c * 16 + hf * 8;
+      kf[c] = *(const f16x8*)(krow + d0);
+      u32x4 x = key_ok ? *(const u32x4*)(vrow + d0) : u32x4{0, 0, 0, 0};
+      vf[c] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int d4 = 0; d4 < 4; ++d4)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) dk[d4][v] = dv[d4][v] = 0.f;
+  const int prow = perm_row(l32);
+  const float sl2 = P.scale_log2;
+  const int wave_key0 = kv0 + wv * 32;
+  const int qrow_t = tid >> 4, qch = tid & 15;  // row-major staging: rows qrow_t + 16*it
+  const int trow = tid >> 3, tch = tid & 7;     // transposed staging: d rows trow + 32*it
+
+  for (int hh = 0; hh < P.r; ++hh) {
+    const int h = g * P.r + hh;
+    const _Float16* qb = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0) * D;
+    const _Float16* qtb = qtt + (int64_t)(b * P.Hq + h) * D * P.spad + slot0;
+    const uint16_t* gtb = dot + (int64_t)(b * P.Hq + h) * D * P.spad + slot0;
+    const uint16_t* gb = dout + b * P.os_b + (int64_t)start * P.os_t + h * P.os_h;
+    const float* lb = lse + b * P.lse_b + h * P.lse_h + start;
+    const float* db = delta + (int64_t)(b * P.Hq + h) * P.spad + slot0;
+    for (int q0 = kv0; q0 < L; q0 += BQ) {
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int rr = q0 + qrow_t + 16 * it;
+        *(u32x4*)&sm.q[qrow_t + 16 * it][qch * 8] = *(const u32x4*)(qb + (int64_t)rr * D + qch * 8);
+        *(u32x4*)&sm.g[qrow_t + 16 * it][qch * 8] =
+            rr < L ? *(const u32x4*)(gb + (int64_t)rr * P.os_t + qch * 8) : u32x4{0, 0, 0, 0};
+        const int dd = trow + 32 * it;
+        *(u32x4*)&sm.qt[dd][tch * 8] = *(const u32x4*)(qtb + (int64_t)dd * P.spad + q0 + tch * 8);
+        *(u32x4*)&sm.gt[dd][tch * 8] = *(const u32x4*)(gtb + (int64_t)dd * P.spad + q0 + tch * 8);
+      }
+      if (tid < BQ) {
+        const int rr = q0 + tid;
+        sm.lse2[tid] = rr < L ? lb[rr] * kLog2e : INFINITY;
+        sm.dl[tid] = db[rr];
+      }
+      __syncthreads();
+      if (q0 + BQ - 1 < wave_key0) continue;  // every row of this step precedes this wave's keys
+
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        if (q0 + rb * 32 + 31 < wave_key0) continue;  // these 32 rows precede every key of this wave
+        bf16x8 pb[2];
+        f16x8 dsb[2];
+        f32x16 s, dp;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const f16x8 a = *(const f16x8*)&sm.q[rb * 32 + prow][c * 16 + hf * 8];
+          s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf[c], s, 0, 0, 0);
+          const bf16x8 a2 = *(const bf16x8*)&sm.g[rb * 32 + prow][c * 16 + hf * 8];
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, vf[c], dp, 0, 0, 0);
+        }
+        const bool need_mask = q0 + rb * 32 < wave_key0 + 31;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int m = rb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
+          float pr = fast_exp2(s[v] * sl2 - sm.lse2[m]);
+          if (need_mask && q0 + m < my_key) pr = 0.f;
+          const float dsv = pr * (dp[v] - sm.dl[m]);
+          pb[v >> 3][v & 7] = (__bf16)pr;
+          dsb[v >> 3][v & 7] = (_Float16)dsv;
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int d4 = 0; d4 < 4; ++d4) {
+            const int col = (rb * 2 + c2) * 16 + hf * 8;
+            const bf16x8 a = *(const bf16x8*)&sm.gt[d4 * 32 + l32][col];
+            dv[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c2], dv[d4], 0, 0, 0);
+            const f16x8 a2 = *(const f16x8*)&sm.qt[d4 * 32 + l32][col];
+            dk[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2, dsb[c2], dk[d4], 0, 0, 0);
+          }
+      }
+    }
+  }
+  if (!key_ok) return;
+  // epilogue: dK = sigma R(j)^T dK~, dV; lane owns key my_key, d = 32*d4 + 8*v4 + 4*hf + e
+  const int64_t off = b * P.ks_b + (int64_t)(start + my_key) * P.ks_t + g * P.ks_h;
+  uint16_t* dkrow = (uint16_t*)gr.dk[0] + off;
+  uint16_t* dvrow = (uint16_t*)gr.dv[0] + off;
+  const float* cp = cosT + (int64_t)my_key * 64;
+  const float* sp = sinT + (int64_t)my_key * 64;
+#pragma unroll
+  for (int d4 = 0; d4 < 2; ++d4)
+#pragma unroll
+    for (int v4 = 0; v4 < 4; ++v4) {
+      const int d = d4 * 32 + v4 * 8 + hf * 4;
+      float lo[4], hi[4], vlo[4], vhi[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = dk[d4][v4 * 4 + e] * P.scale, y = dk[d4 + 2][v4 * 4 + e] * P.scale;
+        const float c = cp[d + e], s = sp[d + e];
+        lo[e] = x * c + y * s;
+        hi[e] = y * c - x * s;
+        vlo[e] = dv[d4][v4 * 4 + e];
+        vhi[e] = dv[d4 + 2][v4 * 4 + e];
+      }
+      *(u32x2*)(dkrow + d) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
+      *(u32x2*)(dkrow + d + 64) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
+      *(u32x2*)(dvrow + d) = u32x2{pack_bf2(vlo[0], vlo[1]), pack_bf2(vlo[2], vlo[3])};
+      *(u32x2*)(dvrow + d + 64) = u32x2{pack_bf2(vhi[0], vhi[1]), pack_bf2(vhi[2], vhi[3])};
+    }
+}
+
+// ============================================================================= branch dK/dV
+// Grid (ceil(stok/16), Hkv, B), 256 threads: 16 rows per block, 16 lanes per
+// row, each lane 4 rotate-half pairs (d and d + 64).
+__global__ void __launch_bounds__(256)
+    branch_bwd_bf16_kernel(Prob P, const uint16_t* __restrict__ q, PassPtrs kv, const float* __restrict__ lse,
+                           const uint16_t* __restrict__ dout, const float* __restrict__ delta,
+                           const float* __restrict__ cosT, const float* __restrict__ sinT, PassGradPtrs gr) {
+  const int tid = threadIdx.x, c16 = tid & 15;
+  const int tok = blockIdx.x * 16 + (tid >> 4);
+  const int g = blockIdx.y, b = blockIdx.z;
+  int s, start, L;
+  if (tok >= P.stok || !token_seq(P, tok, s, start, L)) return;
+  const int i = tok - start, slot = seq_slot0(P, s) + i;
+  const int dlo = c16 * 4, dhi = 64 + c16 * 4;
+  const int pq = i + P.p - 1;
+  const f32x4 cqa = *(const f32x4*)(cosT + (int64_t)pq * 64 + dlo);
+  const f32x4 sqa = *(const f32x4*)(sinT + (int64_t)pq * 64 + dlo);
+  const int64_t koff = b * P.ks_b + (int64_t)tok * P.ks_t + g * P.ks_h;
+  for (int qq = 2; qq <= P.p; ++qq) {
+    const uint16_t* krow = (const uint16_t*)kv.k[qq - 1] + koff;
+    const uint16_t* vrow = (const uint16_t*)kv.v[qq - 1] + koff;
+    const u32x2 ka = *(const u32x2*)(krow + dlo), kb2 = *(const u32x2*)(krow + dhi);
+    const u32x2 va = *(const u32x2*)(vrow + dlo), vb2 = *(const u32x2*)(vrow + dhi);
+    const int pk = i + qq - 1;
+    const f32x4 ck = *(const f32x4*)(cosT + (int64_t)pk * 64 + dlo);
+    const f32x4 sk = *(const f32x4*)(sinT + (int64_t)pk * 64 + dlo);
+    float kr[8], vv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t wa = ka[e >> 1], wb = kb2[e >> 1];
+      const float x1 = __uint_as_float((e & 1) ? (wa & 0xffff0000u) : (wa << 16));
+      const float x2 = __uint_as_float((e & 1) ? (wb & 0xffff0000u) : (wb << 16));
+      kr[e] = x1 * ck[e] - x2 * sk[e];
+      kr[4 + e] = x2 * ck[e] + x1 * sk[e];
+      const uint32_t ua = va[e >> 1], ub = vb2[e >> 1];
+      vv[e] = __uint_as_float((e & 1) ? (ua & 0xffff0000u) : (ua << 16));
+      vv[4 + e] = __uint_as_float((e & 1) ? (ub & 0xffff0000u) : (ub << 16));
+    }
+    float dk[8] = {}, dv[8] = {};
+    for (int hh = 0; hh < P.r; ++hh) {
+      const int h = g * P.r + hh;
+      const uint16_t* qrow = q + b * P.qs_b + (int64_t)tok * P.qs_t + h * P.qs_h;
+      const uint16_t* grow = dout + b * P.os_b + (int64_t)tok * P.os_t + h * P.os_h;
+      const u32x2 qa = *(const u32x2*)(qrow + dlo), qb2 = *(const u32x2*)(qrow + dhi);
+      const u32x2 ga = *(const u32x2*)(grow + dlo), gb2 = *(const u32x2*)(grow + dhi);
+      float qr[8], go[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t wa = qa[e >> 1], wb = qb2[e >> 1];
+        const float x1 = __uint_as_float((e & 1) ? (wa & 0xffff0000u) : (wa << 16));
+        const float x2 = __uint_as_float((e & 1) ? (wb & 0xffff0000u) : (wb << 16));
+        qr[e] = x1 * cqa[e] - x2 * sqa[e];
+        qr[4 + e] = x2 * cqa[e] + x1 * sqa[e];
+        const uint32_t ua = ga[e >> 1], ub = gb2[e >> 1];
+        go[e] = __uint_as_float((e & 1) ? (ua & 0xffff0000u) : (ua << 16));
+        go[4 + e] = __uint_as_float((e & 1) ? (ub & 0xffff0000u) : (ub << 16));
+      }
+      float ps = 0.f, pd = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ps += qr[e] * kr[e], pd += go[e] * vv[e];
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) {
+        ps += __shfl_xor(ps, m, 64);
+        pd += __shfl_xor(pd, m, 64);
+      }
+      const float pr = __expf(ps * P.scale - lse[b * P.lse_b + h * P.lse_h + tok]);
+      const float dsv = pr * (pd - delta[(int64_t)(b * P.Hq + h) * P.spad + slot]) * P.scale;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dk[e] += dsv * qr[e], dv[e] += pr * go[e];
+    }
+    float lo[4], hi[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = dk[e] * ck[e] + dk[4 + e] * sk[e];
+      hi[e] = dk[4 + e] * ck[e] - dk[e] * sk[e];
+    }
+    uint16_t* dkrow = (uint16_t*)gr.dk[qq - 1] + koff;
+    uint16_t* dvrow = (uint16_t*)gr.dv[qq - 1] + koff;
+    *(u32x2*)(dkrow + dlo) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
+    *(u32x2*)(dkrow + dhi) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
+    *(u32x2*)(dvrow + dlo) = u32x2{pack_bf2(dv[0], dv[1]), pack_bf2(dv[2], dv[3])};
+    *(u32x2*)(dvrow + dhi) = u32x2{pack_bf2(dv[4], dv[5]), pack_bf2(dv[6], dv[7])};
+  }
+}
+
+}  // namespace bwd
+
+void launch_bwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
+                     const _Float16* kt, const _Float16* ktt, const _Float16* qt, const _Float16* qtt,
+                     const uint16_t* dot, const float* delta, const int4* tiles_q, const int4* tiles_kv,
+                     const float* cosT, const float* sinT, uint16_t* dq, const PassGradPtrs& g, hipStream_t st) {
+  // dK/dV of the trunk
+  int nkv = P.layout == 0 ? P.B * ((P.stok + bwd::BKV - 1) / bwd::BKV) : (P.stok + bwd::BKV - 1) / bwd::BKV + P.nseq;
+  bwd::dkdv_bf16_kernel<<<(unsigned)((int64_t)nkv * P.Hkv), 256, 0, st>>>(P, kv, lse, dout, kt, qt, qtt, dot, delta,
+                                                                          tiles_kv, cosT, sinT, g);
+  // dQ (trunk + branch terms)
+  int nq = P.layout == 0 ? P.B * ((P.stok + bwd::BM - 1) / bwd::BM) : (P.stok + bwd::BM - 1) / bwd::BM + P.nseq;
+  const int64_t items = (int64_t)nq * P.Hq, unit = 8 * (int64_t)P.r;
+  const int64_t grid = (items + unit - 1) / unit * unit;
+  bwd::dq_bf16_kernel<<<(unsigned)grid, 256, 0, st>>>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT,
+                                                      dq);
+  // dK/dV of the branch keys (passes 2..p)
+  if (P.p > 1) {
+    dim3 gb((P.stok + 15) / 16, P.Hkv, P.B);
+    bwd::branch_bwd_bf16_kernel<<<gb, 256, 0, st>>>(P, q, kv, lse, dout, delta, cosT, sinT, g);
+  }
+}
+
+}  // namespace ttt

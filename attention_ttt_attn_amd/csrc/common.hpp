@@ -1,0 +1,162 @@
+// Shared device/host definitions of libtttattn (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+typedef _Float16 f16;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Kernel-side view of one call.  Every "sequence" s is a batch row (BSHD) or a
+// packed sequence (THD); its tokens are tok = start + i, i = 0..L-1, inside
+// batch b.  Workspace tensors hold one row per "slot": BSHD slot = token;
+// THD sequence s owns slots [slot_base[s], slot_base[s+1]), a multiple of 64
+// long, so every 64-row workspace tile lies inside one sequence, starts
+// 16-byte aligned and is zero past the sequence end.
+struct Prob {
+  int layout;          // 0 BSHD, 1 THD
+  int B;               // batches (1 for THD)
+  int stok;            // tokens per batch: S (BSHD) or T (THD)
+  int spad;            // workspace slots per (batch, head): multiple of 64, >= 64 past the last used slot
+  int nseq;            // sequences: B (BSHD) or num_seqs (THD)
+  const int* cu;       // THD cu_seqlens (device)
+  const int* slot_base;  // THD: [nseq + 1] first slot of every sequence (device workspace)
+  int Hq, Hkv, D, p, r;
+  int npos;            // rows of the RoPE table: positions 0 .. npos-1
+  float scale;         // softmax scale sigma
+  float scale_log2;    // sigma * log2(e)
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t os_b, os_t, os_h;
+  int64_t lse_b, lse_h;  // LSE element (b, h, tok) = b*lse_b + h*lse_h + tok
+};
+
+// Passes' key/value pointers (up to 16), passed by value to kernels.
+struct PassPtrs {
+  const void* k[16];
+  const void* v[16];
+};
+struct PassGradPtrs {
+  void* dk[16];
+  void* dv[16];
+};
+
+// Sequence s of the call: batch, first token and length.  THD bounds are
+// clamped into [0, stok) and to the sequence's slot range.
+__device__ __forceinline__ void seq_info(const Prob& P, int s, int& b, int& start, int& L) {
+  if (P.layout == 0) {
+    b = s;
+    start = 0;
+    L = P.stok;
+  } else {
+    b = 0;
+    int a = P.cu[s], e = P.cu[s + 1];
+    a = a < 0 ? 0 : (a > P.stok ? P.stok : a);
+    e = e < a ? a : (e > P.stok ? P.stok : e);
+    start = a;
+    L = e - a;
+    int room = P.slot_base[s + 1] - P.slot_base[s];
+    if (L > room) L = room;
+  }
+}
+
+__device__ __forceinline__ int seq_slot0(const Prob& P, int s) { return P.layout == 0 ? 0 : P.slot_base[s]; }
+
+// Sequence holding token `tok` (THD: binary search over cu_seqlens).
+__device__ __forceinline__ bool token_seq(const Prob& P, int tok, int& s, int& start, int& L) {
+  if (P.layout == 0) {
+    s = 0;
+    start = 0;
+    L = P.stok;
+    return tok < P.stok;
+  }
+  int lo = 0, hi = P.nseq;  // last s with cu[s] <= tok
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (P.cu[mid] <= tok) lo = mid; else hi = mid;
+  }
+  s = lo;
+  int b_;
+  seq_info(P, s, b_, start, L);
+  return tok >= start && tok < start + L;
+}
+
+// Sequence owning workspace slot `slot`; tok is its token when the slot holds one.
+__device__ __forceinline__ bool slot_token(const Prob& P, int slot, int& tok, int& row) {
+  if (P.layout == 0) {
+    tok = row = slot;
+    return slot < P.stok;
+  }
+  int lo = 0, hi = P.nseq;  // last s with slot_base[s] <= slot
+  if (slot >= P.slot_base[P.nseq]) return false;
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (P.slot_base[mid] <= slot) lo = mid; else hi = mid;
+  }
+  int b_, start, L;
+  seq_info(P, lo, b_, start, L);
+  row = slot - P.slot_base[lo];
+  tok = start + row;
+  return row < L;
+}
+
+__device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float a, float b) {
+  return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
+}
+
+__device__ __forceinline__ uint32_t pack_h2(float a, float b) {
+  _Float16 x = (_Float16)a, y = (_Float16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+__device__ __forceinline__ void unpack_bf8(const u32x4& w, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ u32x4 pack_bf8(const float* f) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf2(f[2 * i], f[2 * i + 1]);
+  return w;
+}
+
+__device__ __forceinline__ u32x4 pack_h8(const float* f) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_h2(f[2 * i], f[2 * i + 1]);
+  return w;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Workspace layout shared by host launchers.
+struct WsPlan {
+  size_t table, slots, tiles_q, tiles_kv, kt, vt, ktt, qt, qtt, dot, delta, total;
+};
+
+}  // namespace ttt

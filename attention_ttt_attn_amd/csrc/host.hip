@@ -1,0 +1,383 @@
+// C-ABI entry points of libtttattn: argument validation, workspace plan and
+// launch order.  Nothing is launched unless every check passes.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/tttattn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Plan {
+  ttt::Prob P;
+  ttt::WsPlan ws;
+  bool bf16;
+  bool o_f32;
+  int max_tiles_q, max_tiles_kv;
+};
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validates the descriptor and fills the kernel view and workspace plan.
+int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl) {
+  if (!d) return fail(TTT_ERR_NULL_ARG, "descriptor is NULL");
+  if (d->struct_size != sizeof(ttt_attn_desc))
+    return fail(TTT_ERR_ABI, "struct_size %u != %zu (ABI version %d)", d->struct_size, sizeof(ttt_attn_desc),
+                TTT_ATTN_ABI_VERSION);
+  if (d->layout != TTT_LAYOUT_BSHD && d->layout != TTT_LAYOUT_THD)
+    return fail(TTT_ERR_BAD_SHAPE, "layout %d is neither BSHD (0) nor THD (1)", d->layout);
+  if (d->dtype != TTT_DTYPE_BF16 && d->dtype != TTT_DTYPE_FP32)
+    return fail(TTT_ERR_UNSUPPORTED, "dtype %d is neither BF16 (0) nor FP32 (1)", d->dtype);
+  if (d->o_dtype != d->dtype && !(d->dtype == TTT_DTYPE_BF16 && d->o_dtype == TTT_DTYPE_FP32))
+    return fail(TTT_ERR_UNSUPPORTED, "o_dtype %d with dtype %d: O is dtype, or FP32 with BF16 inputs", d->o_dtype,
+                d->dtype);
+  const int Hq = d->num_q_heads, Hkv = d->num_kv_heads, D = d->head_dim, p = d->pass_index;
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv != 0)
+    return fail(TTT_ERR_BAD_SHAPE, "num_q_heads %d must be a positive multiple of num_kv_heads %d", Hq, Hkv);
+  if (D <= 0 || (D & 1)) return fail(TTT_ERR_BAD_SHAPE, "head_dim %d must be positive and even", D);
+  const bool bf16 = d->dtype == TTT_DTYPE_BF16;
+  if (bf16 ? (D != 128) : (D != 32 && D != 64 && D != 128))
+    return fail(TTT_ERR_UNSUPPORTED, "head_dim %d not built for %s (fp32: 32/64/128, bf16: 128)", D,
+                bf16 ? "bf16" : "fp32");
+  if (p < 1 || p > TTT_MAX_PASSES)
+    return fail(TTT_ERR_BAD_SHAPE, "pass_index %d outside 1..%d", p, TTT_MAX_PASSES);
+  if (!isfinite(d->softmax_scale)) return fail(TTT_ERR_BAD_SHAPE, "softmax_scale is not finite");
+  if (!isfinite(d->rope_base) || d->rope_base < 0.f || (d->rope_base > 0.f && d->rope_base <= 1.f))
+    return fail(TTT_ERR_BAD_SHAPE, "rope_base %g must be 0 (no RoPE) or > 1", (double)d->rope_base);
+  int B, stok, nseq;
+  if (d->layout == TTT_LAYOUT_BSHD) {
+    if (d->batch < 1 || d->seqlen < 0) return fail(TTT_ERR_BAD_SHAPE, "batch %d / seqlen %d", d->batch, d->seqlen);
+    B = d->batch;
+    stok = d->seqlen;
+    nseq = B;
+  } else {
+    if (d->seqlen < 0 || d->num_seqs < 1)
+      return fail(TTT_ERR_BAD_SHAPE, "THD needs total tokens >= 0 (got %d) and num_seqs >= 1 (got %d)", d->seqlen,
+                  d->num_seqs);
+    if (!d->cu_seqlens) return fail(TTT_ERR_NULL_ARG, "THD layout needs cu_seqlens");
+    B = 1;
+    stok = d->seqlen;
+    nseq = d->num_seqs;
+  }
+  if ((int64_t)stok + 128 + 64 * (int64_t)nseq > (int64_t)1 << 30)
+    return fail(TTT_ERR_BAD_SHAPE, "too many tokens (%d) or sequences (%d)", stok, nseq);
+
+  ttt::Prob& P = pl.P;
+  memset(&P, 0, sizeof P);
+  P.layout = d->layout;
+  P.B = B;
+  P.stok = stok;
+  // workspace slots: BSHD one per token; THD each sequence rounded up to 64
+  P.spad = ((stok + 63) / 64) * 64 + 64 + (d->layout == TTT_LAYOUT_THD ? 64 * nseq : 0);
+  P.nseq = nseq;
+  P.cu = d->cu_seqlens;
+  P.Hq = Hq;
+  P.Hkv = Hkv;
+  P.D = D;
+  P.p = p;
+  P.r = Hq / Hkv;
+  P.npos = stok + p - 1;
+  P.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)D);
+  P.scale_log2 = P.scale * ttt::kLog2e;
+  const bool thd = d->layout == TTT_LAYOUT_THD;
+  auto strides = [&](const int64_t* s, int H, int64_t* out, const char* name, int elem_align) -> int {
+    if (s[0] == 0 && s[1] == 0 && s[2] == 0) {
+      out[0] = thd ? 0 : (int64_t)stok * H * D;
+      out[1] = (int64_t)H * D;
+      out[2] = D;
+      return 0;
+    }
+    for (int i = 0; i < 3; ++i) {
+      if (s[i] < 0) return fail(TTT_ERR_BAD_SHAPE, "%s stride[%d] = %lld is negative", name, i, (long long)s[i]);
+      if (s[i] % elem_align) return fail(TTT_ERR_MISALIGNED, "%s stride[%d] = %lld not a multiple of %d elements",
+                                         name, i, (long long)s[i], elem_align);
+    }
+    out[0] = thd ? 0 : s[0];
+    out[1] = s[1];
+    out[2] = s[2];
+    return 0;
+  };
+  int64_t tmp[3];
+  const int ea = bf16 ? 8 : 4;
+  if (int e = strides(d->q_stride, Hq, tmp, "q", ea)) return e;
+  P.qs_b = tmp[0], P.qs_t = tmp[1], P.qs_h = tmp[2];
+  if (int e = strides(d->kv_stride, Hkv, tmp, "kv", ea)) return e;
+  P.ks_b = tmp[0], P.ks_t = tmp[1], P.ks_h = tmp[2];
+  const bool o_f32 = d->o_dtype == TTT_DTYPE_FP32;
+  if (int e = strides(d->o_stride, Hq, tmp, "o", (o_f32 && bf16) ? 8 : ea)) return e;
+  P.os_b = tmp[0], P.os_t = tmp[1], P.os_h = tmp[2];
+  if (thd) {
+    P.lse_b = 0;
+    P.lse_h = stok;
+  } else {
+    P.lse_b = (int64_t)Hq * stok;
+    P.lse_h = stok;
+  }
+  pl.bf16 = bf16;
+  pl.o_f32 = o_f32;
+
+  // workspace plan
+  ttt::WsPlan& w = pl.ws;
+  memset(&w, 0, sizeof w);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  const size_t nkv = (size_t)B * Hkv * P.spad * D, nq = (size_t)B * Hq * P.spad * D;
+  pl.max_tiles_q = thd ? (stok + ttt::kFwdBM - 1) / ttt::kFwdBM + nseq + 1 : 0;
+  pl.max_tiles_kv = thd ? (stok + ttt::kBwdBKV - 1) / ttt::kBwdBKV + nseq + 1 : 0;
+  w.table = take((size_t)2 * P.npos * (D / 2) * sizeof(float));
+  if (thd) w.slots = take((size_t)(nseq + 1) * sizeof(int));
+  if (bf16) {
+    if (thd) w.tiles_q = take((size_t)(pl.max_tiles_q + 1) * 16);
+    w.kt = take(nkv * 2);
+    if (!for_bwd) {
+      w.vt = take(nkv * 2);
+    } else {
+      if (thd) w.tiles_kv = take((size_t)(pl.max_tiles_kv + 1) * 16);
+      w.ktt = take(nkv * 2);
+      w.qt = take(nq * 2);
+      w.qtt = take(nq * 2);
+      w.dot = take(nq * 2);
+      w.delta = take((size_t)B * Hq * P.spad * 4);
+    }
+  } else {
+    w.kt = take(nkv * 4);
+    if (for_bwd) {
+      w.qt = take(nq * 4);
+      w.delta = take((size_t)B * Hq * P.spad * 4);
+    }
+  }
+  w.total = off;
+  return TTT_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+  if (!p) return fail(TTT_ERR_NULL_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(TTT_ERR_MISALIGNED, "%s (%p) is not 16-byte aligned", name, p);
+  return 0;
+}
+
+int check_ws(const Plan& pl, const void* ws, size_t ws_bytes) {
+  if (pl.ws.total == 0) return 0;
+  if (!ws) return fail(TTT_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", pl.ws.total);
+  if ((uintptr_t)ws & 255u) return fail(TTT_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
+  if (ws_bytes < pl.ws.total)
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu needed", ws_bytes, pl.ws.total);
+  return 0;
+}
+
+int check_cu(const ttt_attn_desc* d, hipStream_t st) {
+  if (d->layout != TTT_LAYOUT_THD || !d->check_cu_seqlens) return 0;
+  std::vector<int32_t> cu(d->num_seqs + 1);
+  hipError_t e = hipMemcpyAsync(cu.data(), d->cu_seqlens, cu.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "reading cu_seqlens: %s", hipGetErrorString(e));
+  if (cu[0] != 0) return fail(TTT_ERR_BAD_SHAPE, "cu_seqlens[0] = %d, expected 0", cu[0]);
+  for (int s = 0; s < d->num_seqs; ++s)
+    if (cu[s + 1] < cu[s]) return fail(TTT_ERR_BAD_SHAPE, "cu_seqlens decreases at %d (%d > %d)", s, cu[s], cu[s + 1]);
+  if (cu[d->num_seqs] != d->seqlen)
+    return fail(TTT_ERR_BAD_SHAPE, "cu_seqlens[%d] = %d, expected total tokens %d", d->num_seqs, cu[d->num_seqs],
+                d->seqlen);
+  return 0;
+}
+
+int hip_check(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return 0;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ttt_attn_abi_version(void) { return TTT_ATTN_ABI_VERSION; }
+
+const char* ttt_attn_status_string(int status) {
+  switch (status) {
+    case TTT_OK: return "ok";
+    case TTT_ERR_NULL_ARG: return "null argument";
+    case TTT_ERR_BAD_SHAPE: return "bad shape";
+    case TTT_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TTT_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case TTT_ERR_WORKSPACE: return "workspace missing or too small";
+    case TTT_ERR_HIP: return "HIP runtime error";
+    case TTT_ERR_ABI: return "descriptor ABI mismatch";
+    default: return "unknown status";
+  }
+}
+
+const char* ttt_attn_last_error(void) { return g_last_error.c_str(); }
+
+size_t ttt_attn_workspace_bytes(const ttt_attn_desc* d, int for_bwd) {
+  Plan pl;
+  if (make_plan(d, for_bwd, pl) != TTT_OK) return 0;
+  return pl.ws.total;
+}
+
+int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, void* o,
+                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Plan pl;
+  if (int e = make_plan(d, 0, pl)) return e;
+  ttt::Prob& P = pl.P;
+  if (!k || !v) return fail(TTT_ERR_NULL_ARG, "k or v pointer array is NULL");
+  if (int e = check_ptr(q, "q")) return e;
+  if (int e = check_ptr(o, "o")) return e;
+  if (!lse) return fail(TTT_ERR_NULL_ARG, "lse is NULL");
+  if ((uintptr_t)lse & 3u) return fail(TTT_ERR_MISALIGNED, "lse is not 4-byte aligned");
+  ttt::PassPtrs kv;
+  memset(&kv, 0, sizeof kv);
+  for (int i = 0; i < P.p; ++i) {
+    char nm[16];
+    snprintf(nm, sizeof nm, "k[%d]", i);
+    if (int e = check_ptr(k[i], nm)) return e;
+    snprintf(nm, sizeof nm, "v[%d]", i);
+    if (int e = check_ptr(v[i], nm)) return e;
+    kv.k[i] = k[i];
+    kv.v[i] = v[i];
+  }
+  if (int e = check_ws(pl, ws, ws_bytes)) return e;
+  hipStream_t st = (hipStream_t)stream;
+  if (int e = check_cu(d, st)) return e;
+  if (P.stok == 0) return TTT_OK;
+  (void)hipGetLastError();
+
+  float* cosT = at<float>(ws, pl.ws.table);
+  float* sinT = cosT + (size_t)P.npos * (P.D / 2);
+  const bool thd = P.layout == TTT_LAYOUT_THD;
+  int* slots = thd ? at<int>(ws, pl.ws.slots) : nullptr;
+  P.slot_base = slots;
+  ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st);
+  if (!pl.bf16) {
+    if (thd) ttt::launch_tile_sched(P, 64, 1, nullptr, 0, slots, st);
+    float* kt = at<float>(ws, pl.ws.kt);
+    ttt::launch_prep_rot_f32(P, (const float*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT, sinT, kt, st);
+    ttt::launch_fwd_f32(P, (const float*)q, kv, kt, cosT, sinT, (float*)o, lse, st);
+  } else {
+    const int4* tiles = nullptr;
+    if (thd) {
+      int4* t = at<int4>(ws, pl.ws.tiles_q);
+      ttt::launch_tile_sched(P, ttt::kFwdBM, 1, t, pl.max_tiles_q, slots, st);
+      tiles = t;
+    }
+    _Float16* kt = at<_Float16>(ws, pl.ws.kt);
+    uint16_t* vt = at<uint16_t>(ws, pl.ws.vt);
+    ttt::launch_prep_rot_h(P, (const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT, sinT, kt, nullptr, st);
+    ttt::launch_prep_transpose_bf(P, (const uint16_t*)v[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, vt, st);
+    ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st);
+  }
+  return hip_check("ttt_attn_fwd launch");
+}
+
+int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, const void* o,
+                 const float* lse, const void* dout, void* dq, void* const* dk, void* const* dv, void* ws,
+                 size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Plan pl;
+  if (int e = make_plan(d, 1, pl)) return e;
+  ttt::Prob& P = pl.P;
+  if (!k || !v || !dk || !dv) return fail(TTT_ERR_NULL_ARG, "a k/v/dk/dv pointer array is NULL");
+  if (int e = check_ptr(q, "q")) return e;
+  if (int e = check_ptr(o, "o")) return e;
+  if (int e = check_ptr(dout, "dout")) return e;
+  if (int e = check_ptr(dq, "dq")) return e;
+  if (!lse) return fail(TTT_ERR_NULL_ARG, "lse is NULL");
+  if ((uintptr_t)lse & 3u) return fail(TTT_ERR_MISALIGNED, "lse is not 4-byte aligned");
+  ttt::PassPtrs kv;
+  ttt::PassGradPtrs g;
+  memset(&kv, 0, sizeof kv);
+  memset(&g, 0, sizeof g);
+  for (int i = 0; i < P.p; ++i) {
+    char nm[16];
+    snprintf(nm, sizeof nm, "k[%d]", i);
+    if (int e = check_ptr(k[i], nm)) return e;
+    snprintf(nm, sizeof nm, "v[%d]", i);
+    if (int e = check_ptr(v[i], nm)) return e;
+    snprintf(nm, sizeof nm, "dk[%d]", i);
+    if (int e = check_ptr(dk[i], nm)) return e;
+    snprintf(nm, sizeof nm, "dv[%d]", i);
+    if (int e = check_ptr(dv[i], nm)) return e;
+    kv.k[i] = k[i];
+    kv.v[i] = v[i];
+    g.dk[i] = dk[i];
+    g.dv[i] = dv[i];
+  }
+  if (int e = check_ws(pl, ws, ws_bytes)) return e;
+  hipStream_t st = (hipStream_t)stream;
+  if (int e = check_cu(d, st)) return e;
+  if (P.stok == 0) return TTT_OK;
+  (void)hipGetLastError();
+
+  float* cosT = at<float>(ws, pl.ws.table);
+  float* sinT = cosT + (size_t)P.npos * (P.D / 2);
+  float* delta = at<float>(ws, pl.ws.delta);
+  const bool thd = P.layout == TTT_LAYOUT_THD;
+  int* slots = thd ? at<int>(ws, pl.ws.slots) : nullptr;
+  P.slot_base = slots;
+  ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st);
+  const int4 *tq = nullptr, *tkv = nullptr;
+  if (thd) {
+    if (pl.bf16) {
+      int4* a = at<int4>(ws, pl.ws.tiles_q);
+      int4* b = at<int4>(ws, pl.ws.tiles_kv);
+      ttt::launch_tile_sched(P, ttt::kBwdBQ, 1, a, pl.max_tiles_q, slots, st);
+      ttt::launch_tile_sched(P, ttt::kBwdBKV, 0, b, pl.max_tiles_kv, nullptr, st);
+      tq = a;
+      tkv = b;
+    } else {
+      ttt::launch_tile_sched(P, 64, 1, nullptr, 0, slots, st);
+    }
+  }
+  ttt::launch_delta(P, o, pl.o_f32, dout, !pl.bf16, delta, st);
+  if (!pl.bf16) {
+    float* kt = at<float>(ws, pl.ws.kt);
+    float* qt = at<float>(ws, pl.ws.qt);
+    ttt::launch_prep_rot_f32(P, (const float*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT, sinT, kt, st);
+    ttt::launch_prep_rot_f32(P, (const float*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, cosT, sinT, qt, st);
+    ttt::launch_bwd_f32(P, (const float*)q, kv, lse, (const float*)dout, kt, qt, delta, cosT, sinT, (float*)dq, g,
+                        st);
+  } else {
+    _Float16* kt = at<_Float16>(ws, pl.ws.kt);
+    _Float16* ktt = at<_Float16>(ws, pl.ws.ktt);
+    _Float16* qt = at<_Float16>(ws, pl.ws.qt);
+    _Float16* qtt = at<_Float16>(ws, pl.ws.qtt);
+    uint16_t* dot = at<uint16_t>(ws, pl.ws.dot);
+    ttt::launch_prep_rot_h(P, (const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT, sinT, kt, ktt, st);
+    ttt::launch_prep_rot_h(P, (const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, cosT, sinT, qt, qtt, st);
+    ttt::launch_prep_transpose_bf(P, (const uint16_t*)dout, P.os_b, P.os_t, P.os_h, P.Hq, dot, st);
+    ttt::launch_bwd_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, kt, ktt, qt, qtt, dot, delta, tq,
+                         tkv, cosT, sinT, (uint16_t*)dq, g, st);
+  }
+  return hip_check("ttt_attn_bwd launch");
+}
+
+}  // extern "C"

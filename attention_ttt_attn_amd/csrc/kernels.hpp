@@ -1,0 +1,39 @@
+// Launcher declarations of libtttattn's kernels (host side).
+#pragma once
+
+#include "common.hpp"
+
+namespace ttt {
+
+void launch_rope_table(const Prob& P, float* cosT, float* sinT, double base, hipStream_t st);
+void launch_prep_rot_f32(const Prob& P, const float* x, int64_t sb, int64_t st_, int64_t sh, int H, int pos_off,
+                         const float* cosT, const float* sinT, float* out_row, hipStream_t st);
+void launch_prep_rot_h(const Prob& P, const uint16_t* x, int64_t sb, int64_t st_, int64_t sh, int H, int pos_off,
+                       const float* cosT, const float* sinT, _Float16* out_row, _Float16* out_col, hipStream_t st);
+void launch_prep_transpose_bf(const Prob& P, const uint16_t* x, int64_t sb, int64_t st_, int64_t sh, int H,
+                              uint16_t* out_col, hipStream_t st);
+void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, float* delta,
+                  hipStream_t st);
+void launch_tile_sched(const Prob& P, int tile, int descending, int4* out, int max_entries, int* slot_base,
+                       hipStream_t st);
+
+// fp32 path (VALU)
+void launch_fwd_f32(const Prob& P, const float* q, const PassPtrs& kv, const float* kt, const float* cosT,
+                    const float* sinT, float* o, float* lse, hipStream_t st);
+void launch_bwd_f32(const Prob& P, const float* q, const PassPtrs& kv, const float* lse, const float* dout,
+                    const float* kt, const float* qt, const float* delta, const float* cosT, const float* sinT,
+                    float* dq, const PassGradPtrs& g, hipStream_t st);
+
+// bf16 path (MFMA trunk + shuffle-reduction branch)
+constexpr int kFwdBM = 128;   // query rows per forward workgroup
+constexpr int kBwdBQ = 128;   // query rows per dQ workgroup
+constexpr int kBwdBKV = 128;  // key rows per dK/dV workgroup
+void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const uint16_t* vt,
+                     const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
+                     hipStream_t st);
+void launch_bwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
+                     const _Float16* kt, const _Float16* ktt, const _Float16* qt, const _Float16* qtt,
+                     const uint16_t* dot, const float* delta, const int4* tiles_q, const int4* tiles_kv,
+                     const float* cosT, const float* sinT, uint16_t* dq, const PassGradPtrs& g, hipStream_t st);
+
+}  // namespace ttt

@@ -1,0 +1,284 @@
+// Prologue kernels: RoPE table, rotate/transposed staging copies, Delta, and
+// the varlen tile scheduler.  All are HBM-bound single passes.
+#include "kernels.hpp"
+
+namespace ttt {
+
+// cos/sin of pos * theta_k, theta_k = base^(-2k/D), evaluated in fp64 and stored
+// as fp32 [npos][D/2].  base == 0 fills the identity rotation (cos 1, sin 0).
+// Rotate-half RoPE: NeoX pairing of k and k + D/2 (NeMo-RL PR #3725,
+// self-review comment: rotate-half oracle).
+__global__ void rope_table_kernel(float* __restrict__ cosT, float* __restrict__ sinT, int npos, int half,
+                                  double base) {
+  int64_t n = (int64_t)npos * half;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    int pos = (int)(e / half), k = (int)(e % half);
+    if (base == 0.0) {
+      cosT[e] = 1.f;
+      sinT[e] = 0.f;
+    } else {
+      double th = pow(base, -2.0 * (double)k / (double)(2 * half));
+      double a = (double)pos * th;
+      cosT[e] = (float)cos(a);
+      sinT[e] = (float)sin(a);
+    }
+  }
+}
+
+template <typename T> __device__ __forceinline__ float ld(const T* p);
+template <> __device__ __forceinline__ float ld<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld<uint16_t>(const uint16_t* p) { return bf2f(*p); }
+
+template <typename T> __device__ __forceinline__ void st(T* p, float x);
+template <> __device__ __forceinline__ void st<float>(float* p, float x) { *p = x; }
+template <> __device__ __forceinline__ void st<_Float16>(_Float16* p, float x) { *p = (_Float16)x; }
+template <> __device__ __forceinline__ void st<uint16_t>(uint16_t* p, float x) { *p = f2bf(x); }
+
+// Staging copy of one tensor X [b][tok][h][D] (element strides sb, st_, sh):
+//   out_row [(b*H + h)][spad][D]  rotated at position (row + pos_off) when ROT
+//   out_col [(b*H + h)][D][spad]  the same values transposed
+// indexed by workspace slot; slots that hold no token are written as 0.
+// Grid (spad/64, H, B), 256 threads; tile = 64 slots of one (b, h).
+template <int D, typename InT, bool ROT, typename RowT, typename ColT>
+__global__ void __launch_bounds__(256) prep_rows_kernel(Prob P, const InT* __restrict__ x, int64_t sb, int64_t st_,
+                                                        int64_t sh, int H, int pos_off,
+                                                        const float* __restrict__ cosT,
+                                                        const float* __restrict__ sinT, RowT* __restrict__ out_row,
+                                                        ColT* __restrict__ out_col) {
+  constexpr int HALF = D / 2;
+  constexpr int TPR = HALF / 4;              // threads per token row, each 4 pairs (k, k + D/2)
+  constexpr int ROWS = 256 / TPR;            // token rows per pass
+  __shared__ float tile[64][D + 1];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tok0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
+  const int c = tid % TPR, rr = tid / TPR;
+  const int64_t slab = (int64_t)(b * H + h) * P.spad;
+  for (int r0 = 0; r0 < 64; r0 += ROWS) {
+    int lr = r0 + rr, slot = tok0 + lr;
+    float a[4], bb[4];
+    int tok, row;
+    bool valid = slot_token(P, slot, tok, row);
+    if (valid) {
+      const InT* src = x + (int64_t)b * sb + (int64_t)tok * st_ + (int64_t)h * sh;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[e] = ld<InT>(src + 4 * c + e);
+        bb[e] = ld<InT>(src + HALF + 4 * c + e);
+      }
+      if (ROT) {
+        int pos = row + pos_off;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float cs = cosT[(int64_t)pos * HALF + 4 * c + e], sn = sinT[(int64_t)pos * HALF + 4 * c + e];
+          float y1 = a[e] * cs - bb[e] * sn, y2 = bb[e] * cs + a[e] * sn;
+          a[e] = y1;
+          bb[e] = y2;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = bb[e] = 0.f;
+    }
+    if (out_row) {
+      RowT* dst = out_row + (slab + slot) * D;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        st<RowT>(dst + 4 * c + e, a[e]);
+        st<RowT>(dst + HALF + 4 * c + e, bb[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[lr][4 * c + e] = a[e];
+      tile[lr][HALF + 4 * c + e] = bb[e];
+    }
+  }
+  if (!out_col) return;
+  __syncthreads();
+  // transposed write: each thread owns (d, 8 consecutive tokens)
+  for (int w = tid; w < D * 8; w += 256) {
+    int d = w / 8, t8 = (w % 8) * 8;
+    ColT* dst = out_col + ((int64_t)(b * H + h) * D + d) * P.spad + tok0 + t8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st<ColT>(dst + e, tile[t8 + e][d]);
+  }
+}
+
+// Delta[(b*Hq + h)][slot] = <dO row, O row> in fp32 (0 in slots without a token).
+// Grid (spad/64, Hq, B), 256 threads, D/8 threads per row.
+template <int D, typename OT, typename GT>
+__global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict__ o, const GT* __restrict__ dout,
+                                                    float* __restrict__ delta) {
+  constexpr int TPR = D / 8;
+  constexpr int ROWS = 256 / TPR;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, c = tid % TPR;
+  for (int r0 = 0; r0 < 64; r0 += ROWS) {
+    int slot = blockIdx.x * 64 + r0 + tid / TPR;
+    int tok, row;
+    bool valid = slot_token(P, slot, tok, row);
+    float acc = 0.f;
+    if (valid) {
+      int64_t off = (int64_t)b * P.os_b + (int64_t)tok * P.os_t + (int64_t)h * P.os_h + 8 * c;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += ld<OT>(o + off + e) * ld<GT>(dout + off + e);
+    }
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    if (c == 0) delta[(int64_t)(b * P.Hq + h) * P.spad + slot] = acc;
+  }
+}
+
+// Varlen tile scheduler (THD).  First lays out the workspace slots: sequence
+// s gets slot_base[s] .. slot_base[s+1], its length rounded up to 64 (clamped
+// so the total stays inside the workspace).  Then, when `out` is given, splits
+// every sequence into tiles of `tile` rows and lists them heavy-first:
+// descending tile index for the query-outer kernels (a query tile's causal
+// work grows with its index), ascending for the key-outer kernel (a key tile's
+// work shrinks with its index).  Entry = {tile index, first token, length,
+// first slot}; out[0].x = count.  One workgroup; deterministic order.
+__global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int descending, int4* __restrict__ out,
+                                                          int max_entries, int* __restrict__ slot_base) {
+  __shared__ int s_maxt;
+  __shared__ int s_base;
+  __shared__ int s_scan[1024];
+  const int tid = threadIdx.x;
+  const int slot_cap = P.spad - 64;
+  auto raw_len = [&](int s, int& a) {
+    a = P.cu[s];
+    int e = P.cu[s + 1];
+    a = a < 0 ? 0 : (a > P.stok ? P.stok : a);
+    e = e < a ? a : (e > P.stok ? P.stok : e);
+    return e - a;
+  };
+  auto block_scan = [&](int v) {  // inclusive scan of v over the block
+    s_scan[tid] = v;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      int x = tid >= o ? s_scan[tid - o] : 0;
+      __syncthreads();
+      s_scan[tid] += x;
+      __syncthreads();
+    }
+    return s_scan[tid];
+  };
+  if (tid == 0) s_base = 0, s_maxt = 0;
+  __syncthreads();
+  if (slot_base) {
+    for (int s0 = 0; s0 < P.nseq; s0 += 1024) {
+      int s = s0 + tid, a, w = 0;
+      if (s < P.nseq) w = (raw_len(s, a) + 63) & ~63;
+      int inc = block_scan(w);
+      if (s < P.nseq) {
+        int lo = s_base + inc - w;
+        slot_base[s] = lo < slot_cap ? lo : slot_cap;
+      }
+      __syncthreads();
+      if (tid == 1023) s_base += s_scan[1023];
+      __syncthreads();
+    }
+    if (tid == 0) slot_base[P.nseq] = s_base < slot_cap ? s_base : slot_cap;
+    __threadfence_block();
+    __syncthreads();
+    if (tid == 0) s_base = 0;
+    __syncthreads();
+  }
+  if (!out) return;
+  Prob Q = P;
+  Q.slot_base = slot_base ? slot_base : P.slot_base;
+  for (int s = tid; s < P.nseq; s += 1024) {
+    int b, st0, L;
+    seq_info(Q, s, b, st0, L);
+    atomicMax(&s_maxt, (L + tile - 1) / tile);
+  }
+  __syncthreads();
+  const int maxt = s_maxt;
+  for (int it = 0; it < maxt; ++it) {
+    int t = descending ? maxt - 1 - it : it;
+    for (int s0 = 0; s0 < P.nseq; s0 += 1024) {
+      int s = s0 + tid;
+      int b, st0 = 0, L = 0, flag = 0;
+      if (s < P.nseq) {
+        seq_info(Q, s, b, st0, L);
+        flag = t * tile < L;
+      }
+      int inc = block_scan(flag);
+      int idx = s_base + inc - flag;
+      if (flag && idx < max_entries) out[1 + idx] = make_int4(t, st0, L, Q.slot_base[s]);
+      __syncthreads();
+      if (tid == 1023) s_base += s_scan[1023];
+      __syncthreads();
+    }
+  }
+  if (tid == 0) out[0] = make_int4(s_base < max_entries ? s_base : max_entries, 0, 0, 0);
+}
+
+// ----------------------------------------------------------------------------- launchers
+void launch_rope_table(const Prob& P, float* cosT, float* sinT, double base, hipStream_t st) {
+  int64_t n = (int64_t)P.npos * (P.D / 2);
+  int blocks = (int)((n + 255) / 256);
+  if (blocks > 65535) blocks = 65535;
+  rope_table_kernel<<<blocks, 256, 0, st>>>(cosT, sinT, P.npos, P.D / 2, base);
+}
+
+template <int D, typename InT, bool ROT, typename RowT, typename ColT>
+static void prep_rows_d(const Prob& P, const void* x, int64_t sb, int64_t st_, int64_t sh, int H, int pos_off,
+                        const float* cosT, const float* sinT, void* out_row, void* out_col, hipStream_t st) {
+  dim3 grid(P.spad / 64, H, P.B);
+  prep_rows_kernel<D, InT, ROT, RowT, ColT><<<grid, 256, 0, st>>>(P, (const InT*)x, sb, st_, sh, H, pos_off, cosT,
+                                                                  sinT, (RowT*)out_row, (ColT*)out_col);
+}
+
+template <typename InT, bool ROT, typename RowT, typename ColT>
+static void prep_rows_any(const Prob& P, const void* x, int64_t sb, int64_t st_, int64_t sh, int H, int pos_off,
+                          const float* cosT, const float* sinT, void* out_row, void* out_col, hipStream_t st) {
+  if (P.D == 32)
+    prep_rows_d<32, InT, ROT, RowT, ColT>(P, x, sb, st_, sh, H, pos_off, cosT, sinT, out_row, out_col, st);
+  else if (P.D == 64)
+    prep_rows_d<64, InT, ROT, RowT, ColT>(P, x, sb, st_, sh, H, pos_off, cosT, sinT, out_row, out_col, st);
+  else
+    prep_rows_d<128, InT, ROT, RowT, ColT>(P, x, sb, st_, sh, H, pos_off, cosT, sinT, out_row, out_col, st);
+}
+
+void launch_prep_rot_f32(const Prob& P, const float* x, int64_t sb, int64_t st_, int64_t sh, int H, int pos_off,
+                         const float* cosT, const float* sinT, float* out_row, hipStream_t st) {
+  prep_rows_any<float, true, float, float>(P, x, sb, st_, sh, H, pos_off, cosT, sinT, out_row, nullptr, st);
+}
+
+void launch_prep_rot_h(const Prob& P, const uint16_t* x, int64_t sb, int64_t st_, int64_t sh, int H, int pos_off,
+                       const float* cosT, const float* sinT, _Float16* out_row, _Float16* out_col, hipStream_t st) {
+  prep_rows_any<uint16_t, true, _Float16, _Float16>(P, x, sb, st_, sh, H, pos_off, cosT, sinT, out_row, out_col, st);
+}
+
+void launch_prep_transpose_bf(const Prob& P, const uint16_t* x, int64_t sb, int64_t st_, int64_t sh, int H,
+                              uint16_t* out_col, hipStream_t st) {
+  prep_rows_any<uint16_t, false, uint16_t, uint16_t>(P, x, sb, st_, sh, H, 0, nullptr, nullptr, nullptr, out_col,
+                                                     st);
+}
+
+void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, float* delta,
+                  hipStream_t st) {
+  dim3 grid(P.spad / 64, P.Hq, P.B);
+#define TTT_DELTA(DD)                                                                              \
+  if (P.D == DD) {                                                                                 \
+    if (o_f32 && g_f32)                                                                            \
+      delta_kernel<DD, float, float><<<grid, 256, 0, st>>>(P, (const float*)o, (const float*)dout, delta); \
+    else if (o_f32)                                                                                \
+      delta_kernel<DD, float, uint16_t><<<grid, 256, 0, st>>>(P, (const float*)o, (const uint16_t*)dout, delta); \
+    else                                                                                           \
+      delta_kernel<DD, uint16_t, uint16_t><<<grid, 256, 0, st>>>(P, (const uint16_t*)o, (const uint16_t*)dout, delta); \
+    return;                                                                                        \
+  }
+  TTT_DELTA(32)
+  TTT_DELTA(64)
+  TTT_DELTA(128)
+#undef TTT_DELTA
+}
+
+void launch_tile_sched(const Prob& P, int tile, int descending, int4* out, int max_entries, int* slot_base,
+                       hipStream_t st) {
+  tile_sched_kernel<<<1, 1024, 0, st>>>(P, tile, descending, out, max_entries, slot_base);
+}
+
+}  // namespace ttt

@@ -1,0 +1,138 @@
+/*
+ * libtttattn: multi-pass EAGLE-3 test-time-training (TTT) draft attention for
+ * AMD Instinct MI355X (gfx950).  C ABI; plain pointers and sizes only.
+ *
+ * What one call computes (one TTT pass p, 1-based).  Sources: NeMo-RL issue
+ * "DFlash/DSpark and EAGLE-3 TTT draft co-training for speculative decoding
+ * (Megatron backend)", section "What I'm working on", item 1 (sequential draft
+ * passes, two-part trunk+branch flash attention, exact joint-LSE merge,
+ * inference-aligned per-pass RoPE offsets) and item 4 (THD varlen layout);
+ * NeMo-RL PR #3725 (bounded multi-pass EAGLE-3 TTT provider), Summary (no dense
+ * pass logits or sequence-square masks; rotary support validated up front)
+ * and the self-review comment (staircase visibility, rotate-half RoPE, the
+ * attention core owns no parameters).
+ *
+ *   Query row i of pass p (position i+p-1) attends to
+ *     trunk : pass-1 keys/values at rows j <= i of its own sequence (position j)
+ *     branch: the keys/values that passes q = 2..p produced at row i
+ *             (position i+q-1)
+ *   Keys and queries get rotate-half RoPE (pair k with k+D/2,
+ *   theta_k = base^(-2k/D)); values are not rotated.  The trunk and branch
+ *   partial softmaxes are joined by an exact log-sum-exp merge, so
+ *     O_i   = sum over visible keys a of softmax(scale * <R q_i, R k_a>) v_a
+ *     LSE_i = ln sum over visible keys a of exp(scale * <R q_i, R k_a>)
+ *   GQA: query head h reads key/value head h / (Hq / Hkv).
+ *
+ * Tensors (element strides; the head_dim axis must be contiguous):
+ *   q, o, dout, dq : BSHD [B, S, Hq, D] or THD [T, Hq, D]
+ *   k[q], v[q], dk[q], dv[q] (q = 0..p-1, index 0 = pass 1 = trunk):
+ *                    BSHD [B, S, Hkv, D] or THD [T, Hkv, D]
+ *   lse (fp32, contiguous): BSHD [B, Hq, S], THD [Hq, T]
+ * q/dq use q_stride, o/dout use o_stride, every k/v/dk/dv uses kv_stride.
+ * A zero stride triple selects the contiguous default.
+ *
+ * Ownership and state: the caller owns every buffer, including the
+ * workspace.  The library allocates no device memory and keeps no state
+ * between calls; calls are asynchronous on `stream` (a hipStream_t; NULL is
+ * the default stream) and re-entrant.  Outputs are overwritten, never
+ * accumulated: gradients of a key/value tensor used by several passes are
+ * summed by the caller.  Two calls that share a workspace must be ordered on
+ * one stream.
+ *
+ * Errors: every argument is checked on the host before anything is launched;
+ * a non-zero status means nothing was enqueued.  ttt_attn_last_error() gives
+ * the detail (thread-local).  Faults inside kernels surface at the caller's
+ * next synchronisation.  No C++ exception crosses this interface.
+ */
+#ifndef TTTATTN_H
+#define TTTATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_ATTN_ABI_VERSION 1
+
+enum ttt_attn_layout { TTT_LAYOUT_BSHD = 0, TTT_LAYOUT_THD = 1 };
+enum ttt_attn_dtype { TTT_DTYPE_BF16 = 0, TTT_DTYPE_FP32 = 1 };
+
+enum ttt_attn_status {
+  TTT_OK = 0,
+  TTT_ERR_NULL_ARG = 1,       /* a required pointer is NULL                         */
+  TTT_ERR_BAD_SHAPE = 2,      /* sizes or strides inconsistent or out of range      */
+  TTT_ERR_UNSUPPORTED = 3,    /* head_dim / dtype combination not built             */
+  TTT_ERR_MISALIGNED = 4,     /* base pointer or stride not 16-byte aligned         */
+  TTT_ERR_WORKSPACE = 5,      /* workspace NULL, too small or not 256-byte aligned  */
+  TTT_ERR_HIP = 6,            /* a HIP runtime call failed                          */
+  TTT_ERR_ABI = 7             /* descriptor struct_size does not match this library */
+};
+
+#define TTT_MAX_PASSES 16
+
+typedef struct ttt_attn_desc {
+  uint32_t struct_size;       /* = sizeof(ttt_attn_desc)                                   */
+  int32_t layout;             /* ttt_attn_layout                                           */
+  int32_t dtype;              /* dtype of q, k, v, dout, dq, dk, dv                        */
+  int32_t o_dtype;            /* dtype of o: = dtype, or FP32 with bf16 inputs             */
+  int32_t batch;              /* B (BSHD); ignored for THD                                 */
+  int32_t seqlen;             /* S (BSHD) or total tokens T (THD)                          */
+  int32_t num_seqs;           /* THD: number of packed sequences                           */
+  int32_t check_cu_seqlens;   /* THD: non-zero = copy cu_seqlens to the host and validate
+                                 (synchronises the stream); zero = trust them, the kernels
+                                 then clamp every sequence to [0, T)                       */
+  const int32_t* cu_seqlens;  /* THD: device int32 [num_seqs + 1], cu[0] = 0, cu[n] = T,
+                                 non-decreasing                                            */
+  int32_t num_q_heads;        /* Hq                                                        */
+  int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0                                        */
+  int32_t head_dim;           /* D: 32, 64 or 128 (fp32); 64 or 128 (bf16)                 */
+  int32_t pass_index;         /* p, 1 .. TTT_MAX_PASSES                                    */
+  float softmax_scale;        /* <= 0 selects 1/sqrt(D)                                    */
+  float rope_base;            /* RoPE base; 0 disables the rotation                        */
+  int64_t q_stride[3];        /* batch, token, head strides of q / dq (elements)           */
+  int64_t kv_stride[3];       /* ... of every k, v, dk, dv                                 */
+  int64_t o_stride[3];        /* ... of o / dout                                           */
+} ttt_attn_desc;
+
+/* Bytes of caller-provided device workspace a forward (for_bwd = 0) or
+ * backward (for_bwd = 1) call with this descriptor needs.  Returns 0 and sets
+ * the last error if the descriptor is invalid (a valid call may also need 0). */
+size_t ttt_attn_workspace_bytes(const ttt_attn_desc* d, int for_bwd);
+
+/* Forward of pass p.
+ *   q            : device, pass-p queries (pre-RoPE)
+ *   k, v         : HOST arrays of p device pointers, pass 1 .. p keys/values (pre-RoPE)
+ *   o            : device output, o_dtype
+ *   lse          : device output, fp32 natural-log LSE of the merged softmax
+ *   ws, ws_bytes : device workspace of at least ttt_attn_workspace_bytes(d, 0)
+ * Returns a ttt_attn_status. */
+int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v,
+                 void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of pass p, recomputing probabilities from the forward's LSE.
+ *   o, lse       : the forward's outputs for the same inputs
+ *   dout         : gradient of o (dtype, o_stride)
+ *   dq           : device output, gradient of q
+ *   dk, dv       : HOST arrays of p device pointers, gradients of k[0..p-1], v[0..p-1]
+ *   ws, ws_bytes : device workspace of at least ttt_attn_workspace_bytes(d, 1)
+ * LSE is an auxiliary output: no gradient flows into it.  Returns a ttt_attn_status. */
+int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v,
+                 const void* o, const float* lse, const void* dout, void* dq, void* const* dk,
+                 void* const* dv, void* ws, size_t ws_bytes, void* stream);
+
+/* Static text of a status code. */
+const char* ttt_attn_status_string(int status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* ttt_attn_last_error(void);
+
+/* TTT_ATTN_ABI_VERSION of the loaded library. */
+int ttt_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTTATTN_H */
