@@ -18,7 +18,7 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
-__all__ = ["fwd", "bwd", "workspace_bytes", "TTTAttnError", "library", "library_path", "Desc",
+__all__ = ["fwd", "bwd", "workspace_bytes", "set_trace_hook", "TTTAttnError", "library", "library_path", "Desc",
            "LAYOUT_BSHD", "LAYOUT_THD", "DTYPE_BF16", "DTYPE_FP32", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +54,24 @@ class Desc(ctypes.Structure):
     ]
 
 
+# void (*)(void* user, const char* kernel, int phase, void* stream)
+TRACE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int, ctypes.c_void_p)
+_trace_ref = None
+
+
+def set_trace_hook(fn) -> None:
+    """Install fn(kernel_name: str, phase: int, stream_handle: int) around every
+    kernel launch of later calls on this thread (phase 0 before, 1 after);
+    None removes it."""
+    global _trace_ref
+    if fn is None:
+        _trace_ref = None
+        library().ttt_attn_set_trace_hook(TRACE_FN(), None)
+        return
+    _trace_ref = TRACE_FN(lambda user, name, phase, stream: fn(name.decode(), phase, stream))
+    library().ttt_attn_set_trace_hook(_trace_ref, None)
+
+
 class TTTAttnError(RuntimeError):
     def __init__(self, status: int, detail: str):
         super().__init__(f"{STATUS.get(status, status)}: {detail}")
@@ -87,6 +105,8 @@ def library() -> ctypes.CDLL:
         lib.ttt_attn_last_error.restype = ctypes.c_char_p
         lib.ttt_attn_abi_version.argtypes = []
         lib.ttt_attn_abi_version.restype = ctypes.c_int
+        lib.ttt_attn_set_trace_hook.argtypes = [TRACE_FN, ctypes.c_void_p]
+        lib.ttt_attn_set_trace_hook.restype = None
         _lib = lib
     return _lib
 

@@ -20,6 +20,8 @@
 //   every row, summed over the group's heads with xor-shuffle dot products.
 // MFMA operand layouts follow the forward: transposed products so that one
 // product's accumulator is the next one's B operand (A rows read permuted).
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace ttt {
@@ -31,8 +33,9 @@ constexpr int KPAD = D + 8;
 constexpr int BN = 64;        // dQ kernel: keys per tile
 constexpr int BM = kBwdBQ;    // dQ kernel: query rows per workgroup
 constexpr int BKV = kBwdBKV;  // dK/dV kernel: keys per workgroup
-constexpr int BQ = 64;        // dK/dV kernel: query rows per step
-constexpr int TPAD = 64 + 8;  // transposed LDS rows of 64 tokens
+constexpr int BQ = 32;        // dK/dV kernel: query rows per step
+constexpr int TPAD = 64 + 8;  // transposed LDS rows of 64 tokens (dQ kernel)
+constexpr int TPADQ = BQ + 8; // transposed LDS rows of BQ tokens (dK/dV kernel)
 constexpr int OPAD = D + 4;
 
 __device__ __forceinline__ int perm_row(int a) { return (a & ~0xC) | ((a & 4) << 1) | ((a & 8) >> 1); }
@@ -96,7 +99,8 @@ __global__ void __launch_bounds__(256, 2)
       dof[c] = __builtin_bit_cast(bf16x8, gv);
     }
   }
-  const float lse2 = row_ok ? lse[b * P.lse_b + h * P.lse_h + start + my_row] * kLog2e : 0.f;
+  // rows past the sequence end get LSE = +inf: every probability is then 0
+  const float lse2 = row_ok ? lse[b * P.lse_b + h * P.lse_h + start + my_row] * kLog2e : INFINITY;
   const float dl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row];
   const float sl2 = P.scale_log2;
 
@@ -134,33 +138,34 @@ __global__ void __launch_bounds__(256, 2)
     const int key0 = kt_ * BN;
     if (key0 > wave_row0 + 31) continue;  // whole tile above this wave's rows
 
-    f32x16 s[2], dp[2];
+    f16x8 dsb[4];
+    const bool diag = key0 + BN - 1 > wave_row0;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s, dp;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[kb][v] = dp[kb][v] = 0.f;
+      for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const f16x8 a = *(const f16x8*)&sm.loop.k[kb * 32 + prow][c * 16 + hf * 8];
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], s[kb], 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], s, 0, 0, 0);
         const bf16x8 a2 = *(const bf16x8*)&sm.loop.v[kb * 32 + prow][c * 16 + hf * 8];
-        dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, dof[c], dp[kb], 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, dof[c], dp, 0, 0, 0);
       }
-    }
-    const bool need_mask = key0 + BN - 1 > wave_row0;
-    f16x8 dsb[4];
+      auto probs = [&](auto masked) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float pr = fast_exp2(s[kb][v] * sl2 - lse2);
-        if (need_mask) {
-          const int key = key0 + kb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
-          if (key > my_row) pr = 0.f;
+        for (int v = 0; v < 16; ++v) {
+          float pr = fast_exp2(__builtin_fmaf(s[v], sl2, -lse2));
+          if constexpr (decltype(masked)::value) {
+            const int key = key0 + kb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
+            if (key > my_row) pr = 0.f;
+          }
+          dsb[kb * 2 + (v >> 3)][v & 7] = (_Float16)(pr * (dp[v] - dl));
         }
-        if (!row_ok) pr = 0.f;
-        dsb[kb * 2 + (v >> 3)][v & 7] = (_Float16)(pr * (dp[kb][v] - dl));
-      }
+      };
+      if (diag) probs(std::true_type{});
+      else probs(std::false_type{});
+    }
 #pragma unroll
     for (int c2 = 0; c2 < 4; ++c2)
 #pragma unroll
@@ -268,9 +273,9 @@ __global__ void __launch_bounds__(256, 2)
 struct KvSmem {
   _Float16 q[BQ][KPAD];    // Q~ rows   (A of S)
   uint16_t g[BQ][KPAD];    // dO rows   (A of dP)
-  _Float16 qt[D][TPAD];    // Q~^T      (A of dK^T)
-  uint16_t gt[D][TPAD];    // dO^T      (A of dV^T)
-  float lse2[BQ];
+  _Float16 qt[D][TPADQ];   // Q~^T      (A of dK^T)
+  uint16_t gt[D][TPADQ];   // dO^T      (A of dV^T)
+  float lse2[BQ];  // LSE * log2(e); +inf past the sequence end
   float dl[BQ];
 };
 
@@ -280,7 +285,7 @@ __global__ void __launch_bounds__(256, 1)
                      const _Float16* __restrict__ qtt, const uint16_t* __restrict__ dot,
                      const float* __restrict__ delta, const int4* __restrict__ tiles, const float* __restrict__ cosT,
                      const float* __restrict__ sinT, PassGradPtrs gr) {
-  __shared__ __attribute__((aligned(16))) KvSmem sm;
+  __shared__ __attribute__((aligned(16))) KvSmem sm[2];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int g = blockIdx.x % P.Hkv, tix = blockIdx.x / P.Hkv;
@@ -324,39 +329,65 @@ __global__ void __launch_bounds__(256, 1)
   const float sl2 = P.scale_log2;
   const int wave_key0 = kv0 + wv * 32;
   const int qrow_t = tid >> 4, qch = tid & 15;  // row-major staging: rows qrow_t + 16*it
-  const int trow = tid >> 3, tch = tid & 7;     // transposed staging: d rows trow + 32*it
+  const int trow = tid >> 2, tch = tid & 3;     // transposed staging: d rows trow + 64*it
 
-  for (int hh = 0; hh < P.r; ++hh) {
+  // Steps = (head of the group, 64-row query block at or after this key tile);
+  // the next step's rows are fetched into registers while this step computes,
+  // then stored into the other LDS buffer: one barrier per step.
+  const int nq = (L - kv0 + BQ - 1) / BQ;
+  const int nsteps = P.r * nq;
+  u32x4 pq[2], pg[2], pqt[2], pgt[2];
+  float plse = 0.f, pdl = 0.f;
+  auto gload = [&](int st) {
+    const int hh = st / nq, q0 = kv0 + (st % nq) * BQ;
     const int h = g * P.r + hh;
     const _Float16* qb = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0) * D;
     const _Float16* qtb = qtt + (int64_t)(b * P.Hq + h) * D * P.spad + slot0;
     const uint16_t* gtb = dot + (int64_t)(b * P.Hq + h) * D * P.spad + slot0;
     const uint16_t* gb = dout + b * P.os_b + (int64_t)start * P.os_t + h * P.os_h;
-    const float* lb = lse + b * P.lse_b + h * P.lse_h + start;
-    const float* db = delta + (int64_t)(b * P.Hq + h) * P.spad + slot0;
-    for (int q0 = kv0; q0 < L; q0 += BQ) {
-      __syncthreads();
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int rr = q0 + qrow_t + 16 * it;
-        *(u32x4*)&sm.q[qrow_t + 16 * it][qch * 8] = *(const u32x4*)(qb + (int64_t)rr * D + qch * 8);
-        *(u32x4*)&sm.g[qrow_t + 16 * it][qch * 8] =
-            rr < L ? *(const u32x4*)(gb + (int64_t)rr * P.os_t + qch * 8) : u32x4{0, 0, 0, 0};
-        const int dd = trow + 32 * it;
-        *(u32x4*)&sm.qt[dd][tch * 8] = *(const u32x4*)(qtb + (int64_t)dd * P.spad + q0 + tch * 8);
-        *(u32x4*)&sm.gt[dd][tch * 8] = *(const u32x4*)(gtb + (int64_t)dd * P.spad + q0 + tch * 8);
-      }
-      if (tid < BQ) {
-        const int rr = q0 + tid;
-        sm.lse2[tid] = rr < L ? lb[rr] * kLog2e : INFINITY;
-        sm.dl[tid] = db[rr];
-      }
-      __syncthreads();
-      if (q0 + BQ - 1 < wave_key0) continue;  // every row of this step precedes this wave's keys
+    for (int it = 0; it < 2; ++it) {
+      const int rr = q0 + qrow_t + 16 * it;
+      pq[it] = *(const u32x4*)(qb + (int64_t)rr * D + qch * 8);
+      pg[it] = rr < L ? *(const u32x4*)(gb + (int64_t)rr * P.os_t + qch * 8) : u32x4{0, 0, 0, 0};
+      const int dd = trow + 64 * it;
+      pqt[it] = *(const u32x4*)(qtb + (int64_t)dd * P.spad + q0 + tch * 8);
+      pgt[it] = *(const u32x4*)(gtb + (int64_t)dd * P.spad + q0 + tch * 8);
+    }
+    if (tid < BQ) {
+      const int rr = q0 + tid;
+      plse = rr < L ? lse[b * P.lse_b + h * P.lse_h + start + rr] * kLog2e : INFINITY;
+      pdl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + rr];
+    }
+  };
+  auto sstore = [&](int buf) {
+    KvSmem& S = sm[buf];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      *(u32x4*)&S.q[qrow_t + 16 * it][qch * 8] = pq[it];
+      *(u32x4*)&S.g[qrow_t + 16 * it][qch * 8] = pg[it];
+      *(u32x4*)&S.qt[trow + 64 * it][tch * 8] = pqt[it];
+      *(u32x4*)&S.gt[trow + 64 * it][tch * 8] = pgt[it];
+    }
+    if (tid < BQ) {
+      S.lse2[tid] = plse;
+      S.dl[tid] = pdl;
+    }
+  };
 
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        if (q0 + rb * 32 + 31 < wave_key0) continue;  // these 32 rows precede every key of this wave
+  if (nsteps > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nsteps) gload(st + 1);
+    const KvSmem& S = sm[buf];
+    const int q0 = kv0 + (st % nq) * BQ;
+    if (q0 + BQ - 1 >= wave_key0) {  // else every row of this step precedes this wave's keys
+      {
+        constexpr int rb = 0;
         bf16x8 pb[2];
         f16x8 dsb[2];
         f32x16 s, dp;
@@ -364,33 +395,52 @@ __global__ void __launch_bounds__(256, 1)
         for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          const f16x8 a = *(const f16x8*)&sm.q[rb * 32 + prow][c * 16 + hf * 8];
+          const f16x8 a = *(const f16x8*)&S.q[rb * 32 + prow][c * 16 + hf * 8];
           s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf[c], s, 0, 0, 0);
-          const bf16x8 a2 = *(const bf16x8*)&sm.g[rb * 32 + prow][c * 16 + hf * 8];
+          const bf16x8 a2 = *(const bf16x8*)&S.g[rb * 32 + prow][c * 16 + hf * 8];
           dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, vf[c], dp, 0, 0, 0);
         }
-        const bool need_mask = q0 + rb * 32 < wave_key0 + 31;
+        // this lane's 16 query rows: m = rb*32 + 16*(v/8) + 8*hf + v%8
+        float l2v[16], dlv[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int m = rb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
-          float pr = fast_exp2(s[v] * sl2 - sm.lse2[m]);
-          if (need_mask && q0 + m < my_key) pr = 0.f;
-          const float dsv = pr * (dp[v] - sm.dl[m]);
-          pb[v >> 3][v & 7] = (__bf16)pr;
-          dsb[v >> 3][v & 7] = (_Float16)dsv;
+        for (int half = 0; half < 2; ++half) {
+          const int m0 = rb * 32 + half * 16 + hf * 8;
+          const f32x4 a0 = *(const f32x4*)&S.lse2[m0], a1 = *(const f32x4*)&S.lse2[m0 + 4];
+          const f32x4 b0 = *(const f32x4*)&S.dl[m0], b1 = *(const f32x4*)&S.dl[m0 + 4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            l2v[half * 8 + e] = a0[e], l2v[half * 8 + 4 + e] = a1[e];
+            dlv[half * 8 + e] = b0[e], dlv[half * 8 + 4 + e] = b1[e];
+          }
         }
+        auto probs = [&](auto masked) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            float pr = fast_exp2(__builtin_fmaf(s[v], sl2, -l2v[v]));
+            if constexpr (decltype(masked)::value) {
+              const int m = rb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
+              if (q0 + m < my_key) pr = 0.f;
+            }
+            pb[v >> 3][v & 7] = (__bf16)pr;
+            dsb[v >> 3][v & 7] = (_Float16)(pr * (dp[v] - dlv[v]));
+          }
+        };
+        if (q0 + rb * 32 < wave_key0 + 31) probs(std::true_type{});
+        else probs(std::false_type{});
 #pragma unroll
         for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
           for (int d4 = 0; d4 < 4; ++d4) {
-            const int col = (rb * 2 + c2) * 16 + hf * 8;
-            const bf16x8 a = *(const bf16x8*)&sm.gt[d4 * 32 + l32][col];
+            const int col = c2 * 16 + hf * 8;
+            const bf16x8 a = *(const bf16x8*)&S.gt[d4 * 32 + l32][col];
             dv[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c2], dv[d4], 0, 0, 0);
-            const f16x8 a2 = *(const f16x8*)&sm.qt[d4 * 32 + l32][col];
+            const f16x8 a2 = *(const f16x8*)&S.qt[d4 * 32 + l32][col];
             dk[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2, dsb[c2], dk[d4], 0, 0, 0);
           }
       }
     }
+    if (st + 1 < nsteps) sstore(buf ^ 1);
+    __syncthreads();
   }
   if (!key_ok) return;
   // epilogue: dK = sigma R(j)^T dK~, dV; lane owns key my_key, d = 32*d4 + 8*v4 + 4*hf + e
@@ -508,25 +558,31 @@ __global__ void __launch_bounds__(256)
 
 }  // namespace bwd
 
-void launch_bwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
-                     const _Float16* kt, const _Float16* ktt, const _Float16* qt, const _Float16* qtt,
-                     const uint16_t* dot, const float* delta, const int4* tiles_q, const int4* tiles_kv,
-                     const float* cosT, const float* sinT, uint16_t* dq, const PassGradPtrs& g, hipStream_t st) {
-  // dK/dV of the trunk
-  int nkv = P.layout == 0 ? P.B * ((P.stok + bwd::BKV - 1) / bwd::BKV) : (P.stok + bwd::BKV - 1) / bwd::BKV + P.nseq;
+void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const uint16_t* dout, const _Float16* kt,
+                      const _Float16* qt, const _Float16* qtt, const uint16_t* dot, const float* delta,
+                      const int4* tiles_kv, const float* cosT, const float* sinT, const PassGradPtrs& g,
+                      hipStream_t st) {
+  const int nkv =
+      P.layout == 0 ? P.B * ((P.stok + bwd::BKV - 1) / bwd::BKV) : (P.stok + bwd::BKV - 1) / bwd::BKV + P.nseq;
   bwd::dkdv_bf16_kernel<<<(unsigned)((int64_t)nkv * P.Hkv), 256, 0, st>>>(P, kv, lse, dout, kt, qt, qtt, dot, delta,
                                                                           tiles_kv, cosT, sinT, g);
-  // dQ (trunk + branch terms)
-  int nq = P.layout == 0 ? P.B * ((P.stok + bwd::BM - 1) / bwd::BM) : (P.stok + bwd::BM - 1) / bwd::BM + P.nseq;
+}
+
+void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
+                    const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
+                    const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st) {
+  const int nq = P.layout == 0 ? P.B * ((P.stok + bwd::BM - 1) / bwd::BM) : (P.stok + bwd::BM - 1) / bwd::BM + P.nseq;
   const int64_t items = (int64_t)nq * P.Hq, unit = 8 * (int64_t)P.r;
   const int64_t grid = (items + unit - 1) / unit * unit;
   bwd::dq_bf16_kernel<<<(unsigned)grid, 256, 0, st>>>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT,
                                                       dq);
-  // dK/dV of the branch keys (passes 2..p)
-  if (P.p > 1) {
-    dim3 gb((P.stok + 15) / 16, P.Hkv, P.B);
-    bwd::branch_bwd_bf16_kernel<<<gb, 256, 0, st>>>(P, q, kv, lse, dout, delta, cosT, sinT, g);
-  }
+}
+
+void launch_branch_bwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse,
+                            const uint16_t* dout, const float* delta, const float* cosT, const float* sinT,
+                            const PassGradPtrs& g, hipStream_t st) {
+  dim3 gb((P.stok + 15) / 16, P.Hkv, P.B);
+  bwd::branch_bwd_bf16_kernel<<<gb, 256, 0, st>>>(P, q, kv, lse, dout, delta, cosT, sinT, g);
 }
 
 }  // namespace ttt

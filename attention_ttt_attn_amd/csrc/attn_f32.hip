@@ -344,16 +344,22 @@ template <int D>
 static void bwd_f32_d(const Prob& P, const PassPtrs& kv, const float* lse, const float* dout, const float* kt,
                       const float* qt, const float* delta, const float* cosT, const float* sinT, float* dq,
                       const PassGradPtrs& g, hipStream_t st) {
+  trace("dq_f32", 0, st);
   dq_f32_kernel<D><<<dim3(P.stok, P.Hq, P.B), 64, 0, st>>>(P, kv, lse, dout, kt, qt, delta, cosT, sinT, dq);
+  trace("dq_f32", 1, st);
+  trace("dkdv_f32", 0, st);
   dkdv_f32_kernel<D><<<dim3(P.stok, P.Hkv, P.B), 64, 0, st>>>(P, kv, lse, dout, kt, qt, delta, cosT, sinT, g);
-  if (P.p > 1)
+  trace("dkdv_f32", 1, st);
+  if (P.p > 1) {
+    trace("branch_bwd_f32", 0, st);
     branch_bwd_f32_kernel<D><<<dim3(P.stok, P.Hkv, P.B), 64, 0, st>>>(P, kv, lse, dout, qt, delta, cosT, sinT, g);
+    trace("branch_bwd_f32", 1, st);
+  }
 }
 
-void launch_bwd_f32(const Prob& P, const float* q, const PassPtrs& kv, const float* lse, const float* dout,
-                    const float* kt, const float* qt, const float* delta, const float* cosT, const float* sinT,
-                    float* dq, const PassGradPtrs& g, hipStream_t st) {
-  (void)q;
+void launch_bwd_f32(const Prob& P, const PassPtrs& kv, const float* lse, const float* dout, const float* kt,
+                    const float* qt, const float* delta, const float* cosT, const float* sinT, float* dq,
+                    const PassGradPtrs& g, hipStream_t st) {
   if (P.D == 32) bwd_f32_d<32>(P, kv, lse, dout, kt, qt, delta, cosT, sinT, dq, g, st);
   else if (P.D == 64) bwd_f32_d<64>(P, kv, lse, dout, kt, qt, delta, cosT, sinT, dq, g, st);
   else bwd_f32_d<128>(P, kv, lse, dout, kt, qt, delta, cosT, sinT, dq, g, st);

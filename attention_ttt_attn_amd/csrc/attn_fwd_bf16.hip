@@ -36,6 +36,8 @@
 // * Grid: heavy-first (descending query tile), and the r = Hq/Hkv heads that
 //   share a KV head are placed on the same XCD back to back so that their
 //   K/V tiles are served from that XCD's L2.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace ttt {
@@ -167,15 +169,19 @@ __global__ void __launch_bounds__(256, 2)
   for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
     for (int v = 0; v < 16; ++v) oacc[d4][v] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, l_run = 0.f, scale_o = 1.f;
   const int prow = perm_row(l32);
   const float sl2 = P.scale_log2;
   const int wave_row0 = row0 + wv * 32;
 
-  for (int kt_ = 0; kt_ < nkt; ++kt_) {
-    const int buf = kt_ & 1;
-    if (kt_ + 1 < nkt) gload(kt_ + 1);
+  // Tiles whose every key precedes every row of this wave need no mask.
+  const int n_free = wave_row0 + 1 >= BN ? (wave_row0 + 1) / BN : 0;
 
+  // One key tile: S^T = K~ Q~^T, online softmax (log2 domain), O^T += V^T P^T.
+  // The running max is lazy: it only moves when a score exceeds it by more than
+  // 2^8, so P <= 256 and the O rescale is skipped wave-wide otherwise (exact:
+  // O and l always share the max they were accumulated with).
+  auto tile = [&](const int buf, const int key0, auto masked) {
     f32x16 sacc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -187,40 +193,46 @@ __global__ void __launch_bounds__(256, 2)
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], sacc[kb], 0, 0, 0);
       }
     }
-
-    const int key0 = kt_ * BN;
-    const bool need_mask = key0 + BN - 1 > wave_row0;
+    if constexpr (decltype(masked)::value) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + kb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
+          if (key > my_row) sacc[kb][v] = -INFINITY;
+        }
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float sv = sacc[kb][v] * sl2;
-        if (need_mask) {
-          const int key = key0 + kb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
-          if (key > my_row) sv = -INFINITY;
-        }
-        sacc[kb][v] = sv;
-        mx = fmaxf(mx, sv);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    if (mx > m_run + 8.f) {  // only then move the running max
+      const float alpha = fast_exp2(m_run - mx);
+      l_run *= alpha;
+      m_run = mx;
+      scale_o = scale_o * alpha;
+    }
+    const float neg_m = -m_run;
     float lsum = 0.f;
     bf16x8 pb[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float pv = fast_exp2(sacc[kb][v] - m_new);
+        const float pv = fast_exp2(__builtin_fmaf(sacc[kb][v], sl2, neg_m));
         lsum += pv;
         pb[kb * 2 + (v >> 3)][v & 7] = (__bf16)pv;
       }
-    l_run = l_run * alpha + lsum;
+    l_run += lsum;
+    if (__builtin_amdgcn_ballot_w64(scale_o != 1.f)) {
 #pragma unroll
-    for (int d4 = 0; d4 < 4; ++d4)
+      for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) oacc[d4][v] *= alpha;
+        for (int v = 0; v < 16; ++v) oacc[d4][v] *= scale_o;
+      scale_o = 1.f;
+    }
 #pragma unroll
     for (int c2 = 0; c2 < 4; ++c2)
 #pragma unroll
@@ -228,7 +240,13 @@ __global__ void __launch_bounds__(256, 2)
         const bf16x8 a = *(const bf16x8*)&sm.loop.v[buf][d4 * 32 + l32][c2 * 16 + hf * 8];
         oacc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c2], oacc[d4], 0, 0, 0);
       }
-    m_run = m_new;
+  };
+
+  for (int kt_ = 0; kt_ < nkt; ++kt_) {
+    const int buf = kt_ & 1;
+    if (kt_ + 1 < nkt) gload(kt_ + 1);
+    if (kt_ < n_free) tile(buf, kt_ * BN, std::false_type{});
+    else tile(buf, kt_ * BN, std::true_type{});
     if (kt_ + 1 < nkt) sstore(buf ^ 1);
     __syncthreads();
   }

@@ -14,6 +14,8 @@
 namespace {
 
 thread_local std::string g_last_error;
+thread_local ttt_attn_trace_fn g_trace_fn = nullptr;
+thread_local void* g_trace_user = nullptr;
 
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int code, const char* fmt, ...) {
@@ -217,7 +219,26 @@ T* at(void* ws, size_t off) {
 
 }  // namespace
 
+namespace ttt {
+void trace(const char* name, int phase, hipStream_t st) {
+  if (g_trace_fn) g_trace_fn(g_trace_user, name, phase, (void*)st);
+}
+}  // namespace ttt
+
+// Runs one launcher between the two trace callbacks.
+#define TTT_TRACED(name, call) \
+  do {                         \
+    ttt::trace(name, 0, st);   \
+    call;                      \
+    ttt::trace(name, 1, st);   \
+  } while (0)
+
 extern "C" {
+
+void ttt_attn_set_trace_hook(ttt_attn_trace_fn fn, void* user) {
+  g_trace_fn = fn;
+  g_trace_user = user;
+}
 
 int ttt_attn_abi_version(void) { return TTT_ATTN_ABI_VERSION; }
 
@@ -276,24 +297,28 @@ int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
   const bool thd = P.layout == TTT_LAYOUT_THD;
   int* slots = thd ? at<int>(ws, pl.ws.slots) : nullptr;
   P.slot_base = slots;
-  ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st);
+  TTT_TRACED("rope_table", ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st));
   if (!pl.bf16) {
-    if (thd) ttt::launch_tile_sched(P, 64, 1, nullptr, 0, slots, st);
+    if (thd) TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, 64, 1, nullptr, 0, slots, st));
     float* kt = at<float>(ws, pl.ws.kt);
-    ttt::launch_prep_rot_f32(P, (const float*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT, sinT, kt, st);
-    ttt::launch_fwd_f32(P, (const float*)q, kv, kt, cosT, sinT, (float*)o, lse, st);
+    TTT_TRACED("prep_k_f32",
+               ttt::launch_prep_rot_f32(P, (const float*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT, sinT, kt, st));
+    TTT_TRACED("fwd_f32", ttt::launch_fwd_f32(P, (const float*)q, kv, kt, cosT, sinT, (float*)o, lse, st));
   } else {
     const int4* tiles = nullptr;
     if (thd) {
       int4* t = at<int4>(ws, pl.ws.tiles_q);
-      ttt::launch_tile_sched(P, ttt::kFwdBM, 1, t, pl.max_tiles_q, slots, st);
+      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kFwdBM, 1, t, pl.max_tiles_q, slots, st));
       tiles = t;
     }
     _Float16* kt = at<_Float16>(ws, pl.ws.kt);
     uint16_t* vt = at<uint16_t>(ws, pl.ws.vt);
-    ttt::launch_prep_rot_h(P, (const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT, sinT, kt, nullptr, st);
-    ttt::launch_prep_transpose_bf(P, (const uint16_t*)v[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, vt, st);
-    ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st);
+    TTT_TRACED("prep_k", ttt::launch_prep_rot_h(P, (const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT,
+                                                sinT, kt, nullptr, st));
+    TTT_TRACED("prep_vt",
+               ttt::launch_prep_transpose_bf(P, (const uint16_t*)v[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, vt, st));
+    TTT_TRACED("trunk_fwd",
+               ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st));
   }
   return hip_check("ttt_attn_fwd launch");
 }
@@ -343,39 +368,48 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
   const bool thd = P.layout == TTT_LAYOUT_THD;
   int* slots = thd ? at<int>(ws, pl.ws.slots) : nullptr;
   P.slot_base = slots;
-  ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st);
+  TTT_TRACED("rope_table", ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st));
   const int4 *tq = nullptr, *tkv = nullptr;
   if (thd) {
     if (pl.bf16) {
       int4* a = at<int4>(ws, pl.ws.tiles_q);
       int4* b = at<int4>(ws, pl.ws.tiles_kv);
-      ttt::launch_tile_sched(P, ttt::kBwdBQ, 1, a, pl.max_tiles_q, slots, st);
-      ttt::launch_tile_sched(P, ttt::kBwdBKV, 0, b, pl.max_tiles_kv, nullptr, st);
+      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kBwdBQ, 1, a, pl.max_tiles_q, slots, st));
+      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kBwdBKV, 0, b, pl.max_tiles_kv, nullptr, st));
       tq = a;
       tkv = b;
     } else {
-      ttt::launch_tile_sched(P, 64, 1, nullptr, 0, slots, st);
+      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, 64, 1, nullptr, 0, slots, st));
     }
   }
-  ttt::launch_delta(P, o, pl.o_f32, dout, !pl.bf16, delta, st);
+  TTT_TRACED("bwd_delta", ttt::launch_delta(P, o, pl.o_f32, dout, !pl.bf16, delta, st));
   if (!pl.bf16) {
     float* kt = at<float>(ws, pl.ws.kt);
     float* qt = at<float>(ws, pl.ws.qt);
-    ttt::launch_prep_rot_f32(P, (const float*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT, sinT, kt, st);
-    ttt::launch_prep_rot_f32(P, (const float*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, cosT, sinT, qt, st);
-    ttt::launch_bwd_f32(P, (const float*)q, kv, lse, (const float*)dout, kt, qt, delta, cosT, sinT, (float*)dq, g,
-                        st);
+    TTT_TRACED("prep_k_f32",
+               ttt::launch_prep_rot_f32(P, (const float*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT, sinT, kt, st));
+    TTT_TRACED("prep_q_f32", ttt::launch_prep_rot_f32(P, (const float*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, cosT,
+                                                      sinT, qt, st));
+    ttt::launch_bwd_f32(P, kv, lse, (const float*)dout, kt, qt, delta, cosT, sinT, (float*)dq, g, st);
   } else {
     _Float16* kt = at<_Float16>(ws, pl.ws.kt);
     _Float16* ktt = at<_Float16>(ws, pl.ws.ktt);
     _Float16* qt = at<_Float16>(ws, pl.ws.qt);
     _Float16* qtt = at<_Float16>(ws, pl.ws.qtt);
     uint16_t* dot = at<uint16_t>(ws, pl.ws.dot);
-    ttt::launch_prep_rot_h(P, (const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT, sinT, kt, ktt, st);
-    ttt::launch_prep_rot_h(P, (const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, cosT, sinT, qt, qtt, st);
-    ttt::launch_prep_transpose_bf(P, (const uint16_t*)dout, P.os_b, P.os_t, P.os_h, P.Hq, dot, st);
-    ttt::launch_bwd_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, kt, ktt, qt, qtt, dot, delta, tq,
-                         tkv, cosT, sinT, (uint16_t*)dq, g, st);
+    TTT_TRACED("prep_k", ttt::launch_prep_rot_h(P, (const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT,
+                                                sinT, kt, ktt, st));
+    TTT_TRACED("prep_q", ttt::launch_prep_rot_h(P, (const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, cosT,
+                                                sinT, qt, qtt, st));
+    TTT_TRACED("prep_dot",
+               ttt::launch_prep_transpose_bf(P, (const uint16_t*)dout, P.os_b, P.os_t, P.os_h, P.Hq, dot, st));
+    TTT_TRACED("trunk_dkdv", ttt::launch_dkdv_bf16(P, kv, lse, (const uint16_t*)dout, kt, qt, qtt, dot, delta, tkv,
+                                                   cosT, sinT, g, st));
+    TTT_TRACED("trunk_dq", ttt::launch_dq_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, kt, ktt, qt,
+                                               delta, tq, cosT, sinT, (uint16_t*)dq, st));
+    if (P.p > 1)
+      TTT_TRACED("branch_bwd", ttt::launch_branch_bwd_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout,
+                                                           delta, cosT, sinT, g, st));
   }
   return hip_check("ttt_attn_bwd launch");
 }

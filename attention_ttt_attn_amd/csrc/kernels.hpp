@@ -20,9 +20,9 @@ void launch_tile_sched(const Prob& P, int tile, int descending, int4* out, int m
 // fp32 path (VALU)
 void launch_fwd_f32(const Prob& P, const float* q, const PassPtrs& kv, const float* kt, const float* cosT,
                     const float* sinT, float* o, float* lse, hipStream_t st);
-void launch_bwd_f32(const Prob& P, const float* q, const PassPtrs& kv, const float* lse, const float* dout,
-                    const float* kt, const float* qt, const float* delta, const float* cosT, const float* sinT,
-                    float* dq, const PassGradPtrs& g, hipStream_t st);
+void launch_bwd_f32(const Prob& P, const PassPtrs& kv, const float* lse, const float* dout, const float* kt,
+                    const float* qt, const float* delta, const float* cosT, const float* sinT, float* dq,
+                    const PassGradPtrs& g, hipStream_t st);
 
 // bf16 path (MFMA trunk + shuffle-reduction branch)
 constexpr int kFwdBM = 128;   // query rows per forward workgroup
@@ -31,9 +31,18 @@ constexpr int kBwdBKV = 128;  // key rows per dK/dV workgroup
 void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const uint16_t* vt,
                      const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
                      hipStream_t st);
-void launch_bwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
-                     const _Float16* kt, const _Float16* ktt, const _Float16* qt, const _Float16* qtt,
-                     const uint16_t* dot, const float* delta, const int4* tiles_q, const int4* tiles_kv,
-                     const float* cosT, const float* sinT, uint16_t* dq, const PassGradPtrs& g, hipStream_t st);
+void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const uint16_t* dout, const _Float16* kt,
+                      const _Float16* qt, const _Float16* qtt, const uint16_t* dot, const float* delta,
+                      const int4* tiles_kv, const float* cosT, const float* sinT, const PassGradPtrs& g,
+                      hipStream_t st);
+void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
+                    const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
+                    const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st);
+void launch_branch_bwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse,
+                            const uint16_t* dout, const float* delta, const float* cosT, const float* sinT,
+                            const PassGradPtrs& g, hipStream_t st);
+
+// launch trace hook (host.hip)
+void trace(const char* name, int phase, hipStream_t st);
 
 }  // namespace ttt

@@ -1,0 +1,303 @@
+"""Benchmark of libtttattn on one MI355X: the full multi-pass TTT attention unroll.
+
+One step = the whole hot path over one batch of synthetic inputs: the forward of
+passes p = 1..K, then the backward of passes p = K..1 (every kernel of the
+library's bf16 path runs each step).  Inputs are resident in HBM before the
+timed region.  Prints ONE JSON line (see the keys below).
+
+  python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload b4_s4k]
+
+Throughput counts causal useful FLOPs only: per pass, forward
+4*D*Hq*(trunk visible pairs + branch pairs) and backward 2.5x that.  Per-kernel
+durations come from HIP events recorded around each launch (through the
+library's launch trace hook) over the timed region; each kernel's roofline
+uses its own algorithmic work per launch.  The fp64 CPU oracle is timed on a
+bounded sample of the same workload on the host (rank 0) as a baseline only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_BF16 = 2.5e15     # MI355X dense bf16/fp16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12           # MI355X HBM3E, bytes/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="b4_s4k")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel event timing")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- work accounting
+def trunk_pairs(w) -> int:
+    """Causal (query, key) pairs of the trunk per head per pass: sum over sequences of L(L+1)/2."""
+    return sum(L * (L + 1) // 2 for L in w.lengths())
+
+
+def useful_flops(w, p: int) -> tuple[float, float]:
+    """(forward, backward) causal useful FLOPs of pass p."""
+    fwd = 4.0 * w.D * w.Hq * (trunk_pairs(w) + (p - 1) * w.tokens)
+    return fwd, 2.5 * fwd
+
+
+def kernel_work(w, name: str, p: int):
+    """(amount, unit) of algorithmic work of one launch of kernel `name` at pass p."""
+    tp = trunk_pairs(w)
+    T = w.tokens
+    row_q, row_kv = w.Hq * w.D * 2, w.Hkv * w.D * 2     # bf16 bytes per token
+    if name == "trunk_fwd":            # S = QK^T and O = PV over the visible trunk pairs
+        return 4.0 * w.D * w.Hq * tp, "flop"
+    if name == "trunk_dkdv":           # S, dP, dV, dK
+        return 8.0 * w.D * w.Hq * tp, "flop"
+    if name == "trunk_dq":             # S, dP, dQ
+        return 6.0 * w.D * w.Hq * tp, "flop"
+    if name == "branch_bwd":           # read Q, dO, LSE, Delta, (p-1) K, V; write (p-1) dK, dV
+        return float(T * (2 * row_q + w.Hq * 8) + (p - 1) * T * row_kv * 4), "byte"
+    if name == "prep_k":               # read K (bf16), write rotated fp16 copy (+ transposed in bwd)
+        return float(T * row_kv * 2), "byte"
+    if name == "prep_vt":
+        return float(T * row_kv * 2), "byte"
+    if name == "prep_q":               # read Q, write rotated fp16 rows + transposed
+        return float(T * row_q * 3), "byte"
+    if name == "prep_dot":
+        return float(T * row_q * 2), "byte"
+    if name == "bwd_delta":
+        return float(T * row_q * 2 + T * w.Hq * 4), "byte"
+    return 0.0, "byte"
+
+
+# ----------------------------------------------------------------------------- traffic from committed counters
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_ttt_attn_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, fn), "rb") as f:
+                h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/<kernel>_<workload>_traffic.md, or None
+    when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"source digest:\s*`?([0-9a-f]+)", text)
+    m_b = re.search(r"HBM bytes per launch:\s*([0-9.eE+]+)", text)
+    if not m_src or not m_b or m_src.group(1) != source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+# ----------------------------------------------------------------------------- CPU oracle baseline
+def cpu_baseline(w, seconds: float):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import ttt_synth as syn
+    from oracle import ttt_oracle as O
+
+    p = w.K
+    L = w.S if w.layout == "bshd" else w.lengths()[0]
+    shp_q = (1, L, w.Hq, w.D)
+    shp_kv = (1, L, w.Hkv, w.D)
+    q = syn.draw(w, syn.KIND_Q, p, shp_q)
+    ks = [syn.draw(w, syn.KIND_K, t, shp_kv) for t in range(1, p + 1)]
+    vs = [syn.draw(w, syn.KIND_V, t, shp_kv) for t in range(1, p + 1)]
+    do = syn.draw(w, syn.KIND_DO, p, shp_q)
+    sl = O.Slice(0, 0, L)
+    rng = np.random.default_rng(5)
+    order = rng.permutation(L)
+    r = w.Hq // w.Hkv
+    done = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    while done < L and time.perf_counter() - t0 < seconds:
+        rows = np.sort(order[done: done + 64])
+        O.fwd_group_rows(q, ks, vs, p, sl, 0, {h: rows for h in range(r)}, layout="bshd", Hq=w.Hq, Hkv=w.Hkv,
+                         scale=w.scale, base=w.rope_base)
+        O.bwd_rows(q, ks, vs, do, p, sl, 0, rows, layout="bshd", Hq=w.Hq, Hkv=w.Hkv, scale=w.scale,
+                   base=w.rope_base)
+        flops += 3.5 * 4.0 * w.D * r * float(np.sum(rows + p))
+        done += len(rows)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} query rows x {r} heads of one KV group at pass {p} of {w.name} (sequence length {L}), "
+                      f"forward + backward, {dt:.1f} s"}
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} (WORLD_SIZE {world}) is not supported; "
+              "the per-pass attention shards over (batch x KV-head group) with no exchange, so N GPUs "
+              "would each run this benchmark on their own share.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_ttt_attn_amd as tk
+    import ttt_synth as syn
+
+    tk.library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = syn.workload(args.workload)
+    K = w.K
+    cu = torch.from_numpy(syn.cu_seqlens_of(w.lengths())).to(dev) if w.layout == "thd" else None
+
+    q = {p: syn.draw_device(w, syn.KIND_Q, p, dev) for p in range(1, K + 1)}
+    ks = [syn.draw_device(w, syn.KIND_K, t, dev) for t in range(1, K + 1)]
+    vs = [syn.draw_device(w, syn.KIND_V, t, dev) for t in range(1, K + 1)]
+    do = {p: syn.draw_device(w, syn.KIND_DO, p, dev) for p in range(1, K + 1)}
+    o = {p: torch.empty_like(q[p]) for p in q}
+    lse_shape = (w.Hq, w.S) if w.layout == "thd" else (w.B, w.Hq, w.S)
+    lse = {p: torch.empty(lse_shape, dtype=torch.float32, device=dev) for p in q}
+    dq = {p: torch.empty_like(q[p]) for p in q}
+    dk = {p: [torch.empty_like(ks[0]) for _ in range(p)] for p in q}
+    dv = {p: [torch.empty_like(vs[0]) for _ in range(p)] for p in q}
+    d_f = tk.make_desc(q[K], ks, K, cu_seqlens=cu, rope_base=w.rope_base)
+    ws_bytes = max(tk.workspace_bytes(d_f, False), tk.workspace_bytes(d_f, True))
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+    kw = dict(cu_seqlens=cu, rope_base=w.rope_base, workspace=ws)
+
+    def step():
+        for p in range(1, K + 1):
+            tk.fwd(q[p], ks, vs, p, out=o[p], lse=lse[p], **kw)
+        for p in range(K, 0, -1):
+            tk.bwd(q[p], ks, vs, o[p], lse[p], do[p], p, dq=dq[p], dks=dk[p], dvs=dv[p], **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-kernel HIP events recorded on the launch stream
+    events = []
+    cur_pass = [0]
+
+    def hook(name, phase, stream):
+        if phase == 0:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(torch.cuda.current_stream())
+            events.append([name, cur_pass[0], ev, None])
+        else:
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(torch.cuda.current_stream())
+            events[-1][3] = ev
+
+    if not args.no_kernel_times:
+        tk.set_trace_hook(hook)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        for p in range(1, K + 1):
+            cur_pass[0] = p
+            tk.fwd(q[p], ks, vs, p, out=o[p], lse=lse[p], **kw)
+        for p in range(K, 0, -1):
+            cur_pass[0] = p
+            tk.bwd(q[p], ks, vs, o[p], lse[p], do[p], p, dq=dq[p], dks=dk[p], dvs=dv[p], **kw)
+    end.record()
+    torch.cuda.synchronize()
+    tk.set_trace_hook(None)
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+
+    flops_step = sum(sum(useful_flops(w, p)) for p in range(1, K + 1))
+    fwd_flops_step = sum(useful_flops(w, p)[0] for p in range(1, K + 1))
+    value = flops_step / (ms_step * 1e-3) / 1e12
+
+    # per-kernel statistics
+    kstats = {}
+    for name, p, e0, e1 in events:
+        dt = e0.elapsed_time(e1)
+        work, unit = kernel_work(w, name, p)
+        s = kstats.setdefault(name, {"launches": 0, "ms": 0.0, "work": 0.0, "unit": unit})
+        s["launches"] += 1
+        s["ms"] += dt
+        s["work"] += work
+    by_pass = {}
+    for name, p, e0, e1 in events:
+        if name == "trunk_fwd":
+            by_pass.setdefault(p, []).append(e0.elapsed_time(e1))
+    kernels = {}
+    for name, s in sorted(kstats.items(), key=lambda kv: -kv[1]["ms"]):
+        avg_ms = s["ms"] / s["launches"]
+        rate = s["work"] / (s["ms"] * 1e-3) if s["ms"] > 0 else 0.0
+        ent = {"avg_us": round(avg_ms * 1e3, 2), "ms_per_step": round(s["ms"] / args.steps, 4),
+               "launches_per_step": s["launches"] // args.steps}
+        if s["unit"] == "flop":
+            ent["tflops"] = round(rate / 1e12, 1)
+            ent["frac_of_peak"] = round(rate / PEAK_MFMA_BF16, 4)
+        elif s["work"] > 0:
+            ent["gbps"] = round(rate / 1e9, 1)
+            ent["frac_of_peak"] = round(rate / PEAK_HBM, 4)
+        kernels[name] = ent
+    if by_pass:
+        kernels["trunk_fwd"]["avg_us_by_pass"] = {str(p): round(1e3 * sum(v) / len(v), 2)
+                                                  for p, v in sorted(by_pass.items())}
+
+    roofline = None
+    if kstats:
+        dom = max(kstats, key=lambda n: kstats[n]["ms"])
+        s = kstats[dom]
+        per_launch = s["work"] / s["launches"]
+        avg_s = s["ms"] / s["launches"] * 1e-3
+        achieved = per_launch / avg_s
+        mfma = s["unit"] == "flop"
+        roofline = {"kernel": dom, "bound": "mfma" if mfma else "hbm",
+                    "achieved": round(achieved / (1e12 if mfma else 1e9), 2),
+                    "peak": 2500.0 if mfma else 8000.0, "unit": "TFLOP/s" if mfma else "GB/s",
+                    "frac": round(achieved / (PEAK_MFMA_BF16 if mfma else PEAK_HBM), 4),
+                    "traffic": committed_traffic(dom, w.name),
+                    "work_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    # sanity: the outputs are finite
+    assert all(torch.isfinite(o[p]).all().item() and torch.isfinite(dq[p]).all().item() for p in q)
+
+    out = {
+        "metric": "TTT attn fwd+bwd TFLOP/s (causal useful FLOPs) and % of MI355X bf16 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "frac_of_peak": round(value * 1e12 / PEAK_MFMA_BF16, 4),
+        "config": {"workload": w.name, "layout": w.layout, "batch": w.B, "seq_len": w.S, "q_heads": w.Hq,
+                   "kv_heads": w.Hkv, "head_dim": w.D, "passes": K, "rope_base": w.rope_base,
+                   "step": f"fwd p=1..{K} then bwd p={K}..1", "useful_tflop_per_step": round(flops_step / 1e12, 4),
+                   "fwd_useful_tflop_per_step": round(fwd_flops_step / 1e12, 4),
+                   "mfma_operands": "fp16 Q~K~^T and dS, bf16 P.V, dO.V, P^T.dO; fp32 accumulate",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -87,7 +87,7 @@ typedef struct ttt_attn_desc {
                                  non-decreasing                                            */
   int32_t num_q_heads;        /* Hq                                                        */
   int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0                                        */
-  int32_t head_dim;           /* D: 32, 64 or 128 (fp32); 64 or 128 (bf16)                 */
+  int32_t head_dim;           /* D: 32, 64 or 128 (fp32); 128 (bf16)                       */
   int32_t pass_index;         /* p, 1 .. TTT_MAX_PASSES                                    */
   float softmax_scale;        /* <= 0 selects 1/sqrt(D)                                    */
   float rope_base;            /* RoPE base; 0 disables the rotation                        */
@@ -130,6 +130,15 @@ const char* ttt_attn_last_error(void);
 
 /* TTT_ATTN_ABI_VERSION of the loaded library. */
 int ttt_attn_abi_version(void);
+
+/* Launch trace hook, a profiling aid outside the method.  When set (per host
+ * thread), every kernel that a later ttt_attn_fwd / ttt_attn_bwd call on this
+ * thread enqueues is bracketed by fn(user, name, 0, stream) just before and
+ * fn(user, name, 1, stream) just after its launch, on the calling thread, so a
+ * caller can record HIP events around single kernels.  `name` is a static
+ * string.  fn = NULL removes the hook.  Never fails. */
+typedef void (*ttt_attn_trace_fn)(void* user, const char* kernel, int phase, void* stream);
+void ttt_attn_set_trace_hook(ttt_attn_trace_fn fn, void* user);
 
 #ifdef __cplusplus
 }

@@ -57,7 +57,7 @@ from typing import Iterable, Optional, Sequence
 import numpy as np
 
 __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_position",
-           "ttt_mask_row", "sequences", "fwd", "bwd", "fwd_rows", "bwd_rows", "Slice"]
+           "ttt_mask_row", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows", "Slice"]
 
 
 # ----------------------------------------------------------------------------- RoPE
@@ -114,11 +114,11 @@ class Slice:
     def __init__(self, b: int, start: int, L: int):
         self.b, self.start, self.L = b, start, L
 
-    def take(self, x: np.ndarray, layout: str) -> np.ndarray:
-        """[L, H, D] fp64 view of this sequence from a BSHD or THD tensor."""
+    def take(self, x: np.ndarray, layout: str, head: int) -> np.ndarray:
+        """[L, D] fp64 copy of head `head` of this sequence from a BSHD or THD tensor."""
         if layout == "bshd":
-            return np.asarray(x[self.b], dtype=np.float64)
-        return np.asarray(x[self.start: self.start + self.L], dtype=np.float64)
+            return np.asarray(x[self.b, :, head], dtype=np.float64)
+        return np.asarray(x[self.start: self.start + self.L, head], dtype=np.float64)
 
 
 def sequences(layout: str, shape: Sequence[int], cu_seqlens=None) -> list:
@@ -150,23 +150,39 @@ class _GroupKeys:
         rows = np.arange(L)
         kt, vt = [], []
         for q in range(1, p + 1):
-            kt.append(rotate_half(sl.take(ks[q - 1], layout)[:, g, :], key_position(q, rows), base))
-            vt.append(sl.take(vs[q - 1], layout)[:, g, :])
+            kt.append(rotate_half(sl.take(ks[q - 1], layout, g), key_position(q, rows), base))
+            vt.append(sl.take(vs[q - 1], layout, g))
         self.keys = np.concatenate(kt, axis=0)     # [p*L, D] rotated
         self.vals = np.concatenate(vt, axis=0)     # [p*L, D]
         self.pos = np.concatenate([key_position(q, rows) for q in range(1, p + 1)])
 
 
+def _candidate_columns(rows: np.ndarray, p: int, L: int) -> np.ndarray:
+    """Concatenated-key columns that any row of the block can see: the trunk prefix
+    up to the block's last row and every pass's key at the block's rows."""
+    cols = [np.arange(int(rows.max()) + 1)]
+    for q in range(2, p + 1):
+        cols.append((q - 1) * L + rows)
+    return np.unique(np.concatenate(cols))
+
+
 def _row_block_fwd(gk: _GroupKeys, q_rot: np.ndarray, rows: np.ndarray, p: int, L: int, scale: float):
-    """Scores, probabilities, LSE and O for a block of query rows (one head)."""
-    mask = np.stack([ttt_mask_row(int(i), p, L) for i in rows])          # [n, p*L]
-    s = scale * (q_rot @ gk.keys.T)
+    """Scores, probabilities, LSE and O for a block of query rows (one head).
+
+    The explicit mask rows are evaluated on the block's candidate columns; the
+    assertion checks that no allowed key lies outside them, so the softmax over
+    the candidates equals the softmax over all p*L concatenated keys."""
+    cols = _candidate_columns(rows, p, L)
+    full = np.stack([ttt_mask_row(int(i), p, L) for i in rows])          # [n, p*L]
+    mask = full[:, cols]
+    assert np.array_equal(mask.sum(axis=1), full.sum(axis=1))
+    s = scale * (q_rot @ gk.keys[cols].T)
     s = np.where(mask, s, -np.inf)
     m = s.max(axis=1, keepdims=True)
     lse = (m + np.log(np.exp(s - m).sum(axis=1, keepdims=True)))[:, 0]
     P = np.exp(s - lse[:, None])
-    O = P @ gk.vals
-    return P, lse, O
+    O = P @ gk.vals[cols]
+    return P, lse, O, cols
 
 
 def _blocks(rows: np.ndarray, n: int):
@@ -175,27 +191,39 @@ def _blocks(rows: np.ndarray, n: int):
 
 
 def _block_rows(L: int, p: int) -> int:
-    # keep a block's [n, p*L] fp64 score matrix near 64 MB
-    return max(1, min(256, (8 << 20) // max(1, p * L)))
+    # keep a block's [n, p*L] mask near 16 MB
+    return max(1, min(256, (16 << 20) // max(1, p * L)))
+
+
+def fwd_group_rows(q, ks, vs, p: int, sl: Slice, g: int, rows_by_head, *, layout: str, Hq: int, Hkv: int,
+                   scale: float, base: float):
+    """{h: (O [n, D], LSE [n])} for the requested rows of the query heads h of KV
+    group g in sequence `sl`, at pass p (the group's rotated keys are built once)."""
+    gk = _GroupKeys(sl, g, ks, vs, p, layout, base)
+    out = {}
+    for h, rows in rows_by_head.items():
+        assert h // (Hq // Hkv) == g
+        rows = np.asarray(rows, dtype=np.int64)
+        qs = sl.take(q, layout, h)
+        O = np.empty((len(rows), qs.shape[-1]))
+        lse = np.empty(len(rows))
+        a = 0
+        for blk in _blocks(rows, _block_rows(sl.L, p)):
+            qr = rotate_half(qs[blk], query_position(blk, p), base)
+            _, l_, o_, _ = _row_block_fwd(gk, qr, blk, p, sl.L, scale)
+            O[a: a + len(blk)] = o_
+            lse[a: a + len(blk)] = l_
+            a += len(blk)
+        out[h] = (O, lse)
+    return out
 
 
 def fwd_rows(q, ks, vs, p: int, sl: Slice, h: int, rows, *, layout: str, Hq: int, Hkv: int,
              scale: float, base: float):
     """O [n, D] and LSE [n] for rows `rows` of sequence `sl`, query head h, at pass p."""
-    rows = np.asarray(rows, dtype=np.int64)
     g = h // (Hq // Hkv)
-    gk = _GroupKeys(sl, g, ks, vs, p, layout, base)
-    qs = sl.take(q, layout)[:, h, :]
-    O = np.empty((len(rows), qs.shape[-1]))
-    lse = np.empty(len(rows))
-    a = 0
-    for blk in _blocks(rows, _block_rows(sl.L, p)):
-        qr = rotate_half(qs[blk], query_position(blk, p), base)
-        _, l_, o_ = _row_block_fwd(gk, qr, blk, p, sl.L, scale)
-        O[a: a + len(blk)] = o_
-        lse[a: a + len(blk)] = l_
-        a += len(blk)
-    return O, lse
+    return fwd_group_rows(q, ks, vs, p, sl, g, {h: rows}, layout=layout, Hq=Hq, Hkv=Hkv, scale=scale,
+                          base=base)[h]
 
 
 def fwd(q, ks, vs, p: int, *, layout: str = "bshd", cu_seqlens=None, scale: Optional[float] = None,
@@ -212,18 +240,20 @@ def fwd(q, ks, vs, p: int, *, layout: str = "bshd", cu_seqlens=None, scale: Opti
         lse = np.zeros((q.shape[0], Hq, q.shape[1]))
     else:
         lse = np.zeros((Hq, q.shape[0]))
+    r = Hq // Hkv
     for sl in sequences(layout, q.shape, cu_seqlens):
         rows = np.arange(sl.L)
-        for h in range(Hq):
-            o_, l_ = fwd_rows(q, ks, vs, p, sl, h, rows, layout=layout, Hq=Hq, Hkv=Hkv,
-                              scale=scale, base=base)
-            O[_row_index(layout, sl, rows) + (h,)] = o_
-            lse[_lse_index(layout, sl, h, rows)] = l_
+        for g in range(Hkv):
+            res = fwd_group_rows(q, ks, vs, p, sl, g, {h: rows for h in range(g * r, (g + 1) * r)},
+                                 layout=layout, Hq=Hq, Hkv=Hkv, scale=scale, base=base)
+            for h, (o_, l_) in res.items():
+                O[_row_index(layout, sl, rows) + (h,)] = o_
+                lse[_lse_index(layout, sl, h, rows)] = l_
     return O, lse
 
 
 def bwd_rows(q, ks, vs, dout, p: int, sl: Slice, g: int, rows, *, layout: str, Hq: int,
-             Hkv: int, scale: float, base: float):
+             Hkv: int, scale: float, base: float, need_kv: bool = True):
     """Backward contributions of query rows `rows` (all r heads of KV group g).
 
     Returns (dq [r, n, D] for those rows, dk [p*L, D], dv [p*L, D]) where dk, dv
@@ -237,24 +267,30 @@ def bwd_rows(q, ks, vs, dout, p: int, sl: Slice, g: int, rows, *, layout: str, H
     dq = np.zeros((r, len(rows), D))
     dk_rot = np.zeros_like(gk.keys)
     dv = np.zeros_like(gk.vals)
+    touched = np.zeros(len(gk.keys), dtype=bool)
     for hh in range(r):
         h = g * r + hh
-        qs = sl.take(q, layout)[:, h, :]
-        dos = sl.take(dout, layout)[:, h, :]
+        qs = sl.take(q, layout, h)
+        dos = sl.take(dout, layout, h)
         a = 0
         for blk in _blocks(rows, _block_rows(sl.L, p)):
             qr = rotate_half(qs[blk], query_position(blk, p), base)
-            P, lse, O = _row_block_fwd(gk, qr, blk, p, sl.L, scale)
+            P, lse, O, cols = _row_block_fwd(gk, qr, blk, p, sl.L, scale)
+            keys, vals = gk.keys[cols], gk.vals[cols]
             do = dos[blk]
             delta = (do * O).sum(axis=1)
-            dP = do @ gk.vals.T
+            dP = do @ vals.T
             dS = P * (dP - delta[:, None])
-            dq_rot = scale * (dS @ gk.keys)
+            dq_rot = scale * (dS @ keys)
             dq[hh, a: a + len(blk)] = unrotate_half(dq_rot, query_position(blk, p), base)
-            dk_rot += scale * (dS.T @ qr)
-            dv += P.T @ do
+            if need_kv:
+                dk_rot[cols] += scale * (dS.T @ qr)
+                dv[cols] += P.T @ do
+                touched[cols] = True
             a += len(blk)
-    dk = unrotate_half(dk_rot, gk.pos, base)
+    dk = np.zeros_like(dk_rot)             # keys no row reached keep a zero gradient
+    idx = np.flatnonzero(touched)
+    dk[idx] = unrotate_half(dk_rot[idx], gk.pos[idx], base)
     return dq, dk, dv
 
 

@@ -386,8 +386,8 @@ def _rot_pairing(x, pos, base):
 
 
 def _blk_transposed_v(gk, q_rot, rows, p, L, scale):
-    P, lse, O_ = _orig_blk(gk, q_rot, rows, p, L, scale)
-    return P, lse, O_ * 1.0 + (P @ gk.vals[:, ::-1] - O_) * 1.0
+    P, lse, O_, cols = _orig_blk(gk, q_rot, rows, p, L, scale)
+    return P, lse, P @ gk.vals[cols][:, ::-1], cols
 
 
 MISTAKES = [

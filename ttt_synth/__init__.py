@@ -27,7 +27,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "workload", "thd_lengths", "cu_seqlens_of",
-           "draw", "round_bf16", "bf16_bits", "KIND_Q", "KIND_K", "KIND_V", "KIND_DO"]
+           "draw", "draw_device", "round_bf16", "bf16_bits", "KIND_Q", "KIND_K", "KIND_V", "KIND_DO"]
 
 KIND_Q, KIND_K, KIND_V, KIND_DO = 0, 1, 2, 3
 
@@ -129,6 +129,19 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     """Upper 16 bits of float32 values that are already bfloat16-representable."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     return (u >> 16).astype(np.uint16)
+
+
+def draw_device(w: Workload, kind: int, pass_index: int, device, shape: Optional[tuple] = None):
+    """N(0,1) torch tensor drawn on `device` from a seeded torch generator, in the
+    workload's dtype (bf16: fp32 draws rounded to nearest even).  A different
+    stream from `draw`; used where the host copy is not needed (benchmarks)."""
+    import torch
+    if shape is None:
+        shape = w.q_shape() if kind in (KIND_Q, KIND_DO) else w.kv_shape()
+    gen = torch.Generator(device=device)
+    gen.manual_seed((w.index * 1000003 + kind * 1009 + pass_index) & 0x7FFFFFFF)
+    x = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return x.to(torch.bfloat16) if w.dtype == "bf16" else x
 
 
 def draw(w: Workload, kind: int, pass_index: int, shape: Optional[tuple] = None) -> np.ndarray:
