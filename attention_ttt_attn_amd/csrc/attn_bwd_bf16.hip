@@ -35,7 +35,6 @@ constexpr int BM = kBwdBQ;    // dQ kernel: query rows per workgroup
 constexpr int BKV = kBwdBKV;  // dK/dV kernel: keys per workgroup
 constexpr int BQ = 32;        // dK/dV kernel: query rows per step
 constexpr int TPAD = 64 + 8;  // transposed LDS rows of 64 tokens (dQ kernel)
-constexpr int TPADQ = BQ + 8; // transposed LDS rows of BQ tokens (dK/dV kernel)
 constexpr int OPAD = D + 4;
 
 __device__ __forceinline__ int perm_row(int a) { return (a & ~0xC) | ((a & 4) << 1) | ((a & 8) >> 1); }
@@ -270,14 +269,25 @@ __global__ void __launch_bounds__(256, 2)
 }
 
 // ============================================================================= dK/dV (trunk)
+// Per 32-query step the workgroup stages Q~ rows, dO rows, Q~^T and dO^T
+// (8 KB each) HBM -> LDS with global_load_lds_dwordx4, double-buffered and
+// XOR-swizzled (16-byte chunk c of row r at slot c ^ (r & 15) for the 256-byte
+// rows, c ^ ((d >> 2) & 3) for the 64-byte transposed rows) so that the MFMA
+// operand reads are conflict-free.  LSE and Delta of the next step go through
+// two VGPRs.
 struct KvSmem {
-  _Float16 q[BQ][KPAD];    // Q~ rows   (A of S)
-  uint16_t g[BQ][KPAD];    // dO rows   (A of dP)
-  _Float16 qt[D][TPADQ];   // Q~^T      (A of dK^T)
-  uint16_t gt[D][TPADQ];   // dO^T      (A of dV^T)
-  float lse2[BQ];  // LSE * log2(e); +inf past the sequence end
-  float dl[BQ];
+  _Float16 q[2][BQ * D];   // Q~ rows   (A of S)
+  uint16_t g[2][BQ * D];   // dO rows   (A of dP)
+  _Float16 qt[2][D * BQ];  // Q~^T      (A of dK^T)
+  uint16_t gt[2][D * BQ];  // dO^T      (A of dV^T)
+  float lse2[2][BQ];       // LSE * log2(e); +inf past the sequence end
+  float dl[2][BQ];
 };
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)l, 16, 0, 0);
+}
 
 __global__ void __launch_bounds__(256, 1)
     dkdv_bf16_kernel(Prob P, PassPtrs kv, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
@@ -285,7 +295,7 @@ __global__ void __launch_bounds__(256, 1)
                      const _Float16* __restrict__ qtt, const uint16_t* __restrict__ dot,
                      const float* __restrict__ delta, const int4* __restrict__ tiles, const float* __restrict__ cosT,
                      const float* __restrict__ sinT, PassGradPtrs gr) {
-  __shared__ __attribute__((aligned(16))) KvSmem sm[2];
+  __shared__ __attribute__((aligned(16))) KvSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int g = blockIdx.x % P.Hkv, tix = blockIdx.x / P.Hkv;
@@ -328,119 +338,132 @@ __global__ void __launch_bounds__(256, 1)
   const int prow = perm_row(l32);
   const float sl2 = P.scale_log2;
   const int wave_key0 = kv0 + wv * 32;
-  const int qrow_t = tid >> 4, qch = tid & 15;  // row-major staging: rows qrow_t + 16*it
-  const int trow = tid >> 2, tch = tid & 3;     // transposed staging: d rows trow + 64*it
 
-  // Steps = (head of the group, 64-row query block at or after this key tile);
-  // the next step's rows are fetched into registers while this step computes,
-  // then stored into the other LDS buffer: one barrier per step.
+  // Steps = (head of the group, 32-row query block at or after this key tile).
   const int nq = (L - kv0 + BQ - 1) / BQ;
   const int nsteps = P.r * nq;
-  u32x4 pq[2], pg[2], pqt[2], pgt[2];
+  // DMA lane roles (wave w issues instructions j = 2w, 2w+1 of each tile):
+  // rows: r = 4j + lane/16, slot lane%16; transposed: d = 16j + lane/4, slot lane%4.
+  uint32_t roff[2], toff[2];
+  int rrow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int j = 2 * wv + i;
+    const int r = 4 * j + (lane >> 4);
+    rrow[i] = r;
+    roff[i] = (uint32_t)(((lane & 15) ^ (r & 15)) * 8);
+    const int d = 16 * j + (lane >> 2);
+    toff[i] = (uint32_t)(d * P.spad + ((lane & 3) ^ ((d >> 2) & 3)) * 8);
+  }
   float plse = 0.f, pdl = 0.f;
-  auto gload = [&](int st) {
+  bool pvalid = false;
+  auto issue = [&](int st, int buf) {
     const int hh = st / nq, q0 = kv0 + (st % nq) * BQ;
     const int h = g * P.r + hh;
-    const _Float16* qb = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0) * D;
-    const _Float16* qtb = qtt + (int64_t)(b * P.Hq + h) * D * P.spad + slot0;
-    const uint16_t* gtb = dot + (int64_t)(b * P.Hq + h) * D * P.spad + slot0;
+    const _Float16* qb = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0 + q0) * D;
+    const _Float16* qtb = qtt + (int64_t)(b * P.Hq + h) * D * P.spad + slot0 + q0;
+    const uint16_t* gtb = dot + (int64_t)(b * P.Hq + h) * D * P.spad + slot0 + q0;
     const uint16_t* gb = dout + b * P.os_b + (int64_t)start * P.os_t + h * P.os_h;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int rr = q0 + qrow_t + 16 * it;
-      pq[it] = *(const u32x4*)(qb + (int64_t)rr * D + qch * 8);
-      pg[it] = rr < L ? *(const u32x4*)(gb + (int64_t)rr * P.os_t + qch * 8) : u32x4{0, 0, 0, 0};
-      const int dd = trow + 64 * it;
-      pqt[it] = *(const u32x4*)(qtb + (int64_t)dd * P.spad + q0 + tch * 8);
-      pgt[it] = *(const u32x4*)(gtb + (int64_t)dd * P.spad + q0 + tch * 8);
+    for (int i = 0; i < 2; ++i) {
+      const int j = 2 * wv + i;
+      const int r = rrow[i];
+      const int rg = min(q0 + r, L - 1);  // rows past the end repeat the last row (their P is 0)
+      lds_dma16(qb + r * D + roff[i], &sm.q[buf][4 * j * D]);
+      lds_dma16(gb + (int64_t)rg * P.os_t + roff[i], &sm.g[buf][4 * j * D]);
+      lds_dma16(qtb + toff[i], &sm.qt[buf][16 * j * BQ]);
+      lds_dma16(gtb + toff[i], &sm.gt[buf][16 * j * BQ]);
     }
+    // raw loads only: any use here would make the compiler wait for the DMA above
     if (tid < BQ) {
-      const int rr = q0 + tid;
-      plse = rr < L ? lse[b * P.lse_b + h * P.lse_h + start + rr] * kLog2e : INFINITY;
-      pdl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + rr];
+      const int rr = min(q0 + tid, L - 1);
+      plse = lse[b * P.lse_b + h * P.lse_h + start + rr];
+      pdl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + min(q0 + tid, L)];
+      pvalid = q0 + tid < L;
     }
   };
-  auto sstore = [&](int buf) {
-    KvSmem& S = sm[buf];
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      *(u32x4*)&S.q[qrow_t + 16 * it][qch * 8] = pq[it];
-      *(u32x4*)&S.g[qrow_t + 16 * it][qch * 8] = pg[it];
-      *(u32x4*)&S.qt[trow + 64 * it][tch * 8] = pqt[it];
-      *(u32x4*)&S.gt[trow + 64 * it][tch * 8] = pgt[it];
-    }
+  auto settle = [&](int buf) {  // after issue() and the compute: publish the step's data
     if (tid < BQ) {
-      S.lse2[tid] = plse;
-      S.dl[tid] = pdl;
+      sm.lse2[buf][tid] = pvalid ? plse * kLog2e : INFINITY;
+      sm.dl[buf][tid] = pdl;
     }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
-  if (nsteps > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
+  if (nsteps > 0) issue(0, 0);
+  settle(0);
   for (int st = 0; st < nsteps; ++st) {
     const int buf = st & 1;
-    if (st + 1 < nsteps) gload(st + 1);
-    const KvSmem& S = sm[buf];
+    if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
     const int q0 = kv0 + (st % nq) * BQ;
     if (q0 + BQ - 1 >= wave_key0) {  // else every row of this step precedes this wave's keys
-      {
-        constexpr int rb = 0;
-        bf16x8 pb[2];
-        f16x8 dsb[2];
-        f32x16 s, dp;
+      const _Float16* ql = sm.q[buf];
+      const uint16_t* gl = sm.g[buf];
+      f32x16 s, dp;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
+      for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const f16x8 a = *(const f16x8*)&S.q[rb * 32 + prow][c * 16 + hf * 8];
-          s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, kf[c], s, 0, 0, 0);
-          const bf16x8 a2 = *(const bf16x8*)&S.g[rb * 32 + prow][c * 16 + hf * 8];
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, vf[c], dp, 0, 0, 0);
+      for (int c0 = 0; c0 < 8; c0 += 4) {
+        f16x8 a[4];
+        bf16x8 a2[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int off = prow * D + (((2 * (c0 + c) + hf) ^ (prow & 15)) * 8);
+          a[c] = *(const f16x8*)&ql[off];
+          a2[c] = *(const bf16x8*)&gl[off];
         }
-        // this lane's 16 query rows: m = rb*32 + 16*(v/8) + 8*hf + v%8
-        float l2v[16], dlv[16];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], kf[c0 + c], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[c], vf[c0 + c], dp, 0, 0, 0);
+        }
+      }
+      bf16x8 pb[2];
+      f16x8 dsb[2];
+      auto probs = [&](auto masked) {
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const int m0 = rb * 32 + half * 16 + hf * 8;
-          const f32x4 a0 = *(const f32x4*)&S.lse2[m0], a1 = *(const f32x4*)&S.lse2[m0 + 4];
-          const f32x4 b0 = *(const f32x4*)&S.dl[m0], b1 = *(const f32x4*)&S.dl[m0 + 4];
+          const int m0 = half * 16 + hf * 8;  // this lane's rows m = 16*(v/8) + 8*hf + v%8
+          const f32x4 l0 = *(const f32x4*)&sm.lse2[buf][m0], l1 = *(const f32x4*)&sm.lse2[buf][m0 + 4];
+          const f32x4 d0 = *(const f32x4*)&sm.dl[buf][m0], d1 = *(const f32x4*)&sm.dl[buf][m0 + 4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            l2v[half * 8 + e] = a0[e], l2v[half * 8 + 4 + e] = a1[e];
-            dlv[half * 8 + e] = b0[e], dlv[half * 8 + 4 + e] = b1[e];
+          for (int e = 0; e < 8; ++e) {
+            const int v = half * 8 + e;
+            const float lv = e < 4 ? l0[e] : l1[e - 4];
+            const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+            float pr = fast_exp2(__builtin_fmaf(s[v], sl2, -lv));
+            if constexpr (decltype(masked)::value) {
+              if (q0 + m0 + e < my_key) pr = 0.f;
+            }
+            pb[half][e] = (__bf16)pr;
+            dsb[half][e] = (_Float16)(pr * (dp[v] - dv_));
           }
         }
-        auto probs = [&](auto masked) {
+      };
+      if (q0 < wave_key0 + 31) probs(std::true_type{});
+      else probs(std::false_type{});
+      const _Float16* qtl = sm.qt[buf];
+      const uint16_t* gtl = sm.gt[buf];
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            float pr = fast_exp2(__builtin_fmaf(s[v], sl2, -l2v[v]));
-            if constexpr (decltype(masked)::value) {
-              const int m = rb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
-              if (q0 + m < my_key) pr = 0.f;
-            }
-            pb[v >> 3][v & 7] = (__bf16)pr;
-            dsb[v >> 3][v & 7] = (_Float16)(pr * (dp[v] - dlv[v]));
-          }
-        };
-        if (q0 + rb * 32 < wave_key0 + 31) probs(std::true_type{});
-        else probs(std::false_type{});
+      for (int c2 = 0; c2 < 2; ++c2) {
+        bf16x8 a[4];
+        f16x8 a2[4];
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
+        for (int d4 = 0; d4 < 4; ++d4) {
+          const int d = d4 * 32 + l32;
+          const int off = d * BQ + (((2 * c2 + hf) ^ ((d >> 2) & 3)) * 8);
+          a[d4] = *(const bf16x8*)&gtl[off];
+          a2[d4] = *(const f16x8*)&qtl[off];
+        }
 #pragma unroll
-          for (int d4 = 0; d4 < 4; ++d4) {
-            const int col = c2 * 16 + hf * 8;
-            const bf16x8 a = *(const bf16x8*)&S.gt[d4 * 32 + l32][col];
-            dv[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[c2], dv[d4], 0, 0, 0);
-            const f16x8 a2 = *(const f16x8*)&S.qt[d4 * 32 + l32][col];
-            dk[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2, dsb[c2], dk[d4], 0, 0, 0);
-          }
+        for (int d4 = 0; d4 < 4; ++d4) {
+          dv[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4], pb[c2], dv[d4], 0, 0, 0);
+          dk[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2[d4], dsb[c2], dk[d4], 0, 0, 0);
+        }
       }
     }
-    if (st + 1 < nsteps) sstore(buf ^ 1);
-    __syncthreads();
+    settle(buf ^ 1);
   }
   if (!key_ok) return;
   // epilogue: dK = sigma R(j)^T dK~, dV; lane owns key my_key, d = 32*d4 + 8*v4 + 4*hf + e
@@ -458,9 +481,9 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const float x = dk[d4][v4 * 4 + e] * P.scale, y = dk[d4 + 2][v4 * 4 + e] * P.scale;
-        const float c = cp[d + e], s = sp[d + e];
-        lo[e] = x * c + y * s;
-        hi[e] = y * c - x * s;
+        const float c = cp[d + e], s_ = sp[d + e];
+        lo[e] = x * c + y * s_;
+        hi[e] = y * c - x * s_;
         vlo[e] = dv[d4][v4 * 4 + e];
         vhi[e] = dv[d4 + 2][v4 * 4 + e];
       }

@@ -148,7 +148,7 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl) {
     return at;
   };
   const size_t nkv = (size_t)B * Hkv * P.spad * D, nq = (size_t)B * Hq * P.spad * D;
-  pl.max_tiles_q = thd ? (stok + ttt::kFwdBM - 1) / ttt::kFwdBM + nseq + 1 : 0;
+  pl.max_tiles_q = thd ? (stok + ttt::kFwdMinRows - 1) / ttt::kFwdMinRows + nseq + 1 : 0;
   pl.max_tiles_kv = thd ? (stok + ttt::kBwdBKV - 1) / ttt::kBwdBKV + nseq + 1 : 0;
   w.table = take((size_t)2 * P.npos * (D / 2) * sizeof(float));
   if (thd) w.slots = take((size_t)(nseq + 1) * sizeof(int));
@@ -308,7 +308,8 @@ int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
     const int4* tiles = nullptr;
     if (thd) {
       int4* t = at<int4>(ws, pl.ws.tiles_q);
-      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kFwdBM, 1, t, pl.max_tiles_q, slots, st));
+      TTT_TRACED("tile_sched",
+                 ttt::launch_tile_sched(P, ttt::fwd_tile_rows(P.r), 1, t, pl.max_tiles_q, slots, st));
       tiles = t;
     }
     _Float16* kt = at<_Float16>(ws, pl.ws.kt);
