@@ -211,6 +211,8 @@ def fwd(q, ks: Sequence, vs: Sequence, p: int, *, cu_seqlens=None, softmax_scale
         lse = torch.empty(shape, dtype=torch.float32, device=q.device)
     d = make_desc(q, ks, p, cu_seqlens=cu_seqlens, softmax_scale=softmax_scale, rope_base=rope_base,
                   o_dtype=o_dtype, o_like=out, check_cu_seqlens=check_cu_seqlens)
+    if any(t.stride() != ks[0].stride() for t in list(ks[:p]) + list(vs[:p])):
+        raise ValueError("every k and v must share one set of strides")
     nbytes = workspace_bytes(d, False)
     ws = _workspace(nbytes, q.device, workspace)
     wp, wn = _ws_ptr(ws)
@@ -229,12 +231,18 @@ def bwd(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, cu_seqlens=None,
                   o_dtype=o_dtype, o_like=o, check_cu_seqlens=check_cu_seqlens)
     if dout.stride() != o.stride():
         raise ValueError("dout must have the strides of o")
+    like = lambda t: torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
     if dq is None:
-        dq = torch.empty_like(q)
+        dq = like(q)
     if dks is None:
-        dks = [torch.empty_like(ks[0]) for _ in range(p)]
+        dks = [like(ks[0]) for _ in range(p)]
     if dvs is None:
-        dvs = [torch.empty_like(vs[0]) for _ in range(p)]
+        dvs = [like(vs[0]) for _ in range(p)]
+    # gradients are written with the strides of their primal
+    if dq.stride() != q.stride() or any(t.stride() != ks[0].stride() for t in list(dks[:p]) + list(dvs[:p])):
+        raise ValueError("dq must have the strides of q, dk/dv those of k")
+    if any(t.stride() != ks[0].stride() for t in list(ks[:p]) + list(vs[:p])):
+        raise ValueError("every k and v must share one set of strides")
     nbytes = workspace_bytes(d, True)
     ws = _workspace(nbytes, q.device, workspace)
     wp, wn = _ws_ptr(ws)

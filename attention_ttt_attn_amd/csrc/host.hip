@@ -270,6 +270,7 @@ int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
   Plan pl;
   if (int e = make_plan(d, 0, pl)) return e;
   ttt::Prob& P = pl.P;
+  if (P.stok == 0) return TTT_OK;  // nothing to compute; pointers of empty tensors may be NULL
   if (!k || !v) return fail(TTT_ERR_NULL_ARG, "k or v pointer array is NULL");
   if (int e = check_ptr(q, "q")) return e;
   if (int e = check_ptr(o, "o")) return e;
@@ -289,7 +290,6 @@ int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
   if (int e = check_ws(pl, ws, ws_bytes)) return e;
   hipStream_t st = (hipStream_t)stream;
   if (int e = check_cu(d, st)) return e;
-  if (P.stok == 0) return TTT_OK;
   (void)hipGetLastError();
 
   float* cosT = at<float>(ws, pl.ws.table);
@@ -331,6 +331,7 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
   Plan pl;
   if (int e = make_plan(d, 1, pl)) return e;
   ttt::Prob& P = pl.P;
+  if (P.stok == 0) return TTT_OK;  // nothing to compute; pointers of empty tensors may be NULL
   if (!k || !v || !dk || !dv) return fail(TTT_ERR_NULL_ARG, "a k/v/dk/dv pointer array is NULL");
   if (int e = check_ptr(q, "q")) return e;
   if (int e = check_ptr(o, "o")) return e;
@@ -360,7 +361,6 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
   if (int e = check_ws(pl, ws, ws_bytes)) return e;
   hipStream_t st = (hipStream_t)stream;
   if (int e = check_cu(d, st)) return e;
-  if (P.stok == 0) return TTT_OK;
   (void)hipGetLastError();
 
   float* cosT = at<float>(ws, pl.ws.table);

@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, copy a 256 MiB buffer 3 times (a plain copy kernel of known size "
+                         "that scales the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -274,6 +277,13 @@ def main():
                     "frac": round(achieved / (PEAK_MFMA_BF16 if mfma else PEAK_HBM), 4),
                     "traffic": committed_traffic(dom, w.name),
                     "work_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
 
     # sanity: the outputs are finite
     assert all(torch.isfinite(o[p]).all().item() and torch.isfinite(dq[p]).all().item() for p in q)

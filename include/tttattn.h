@@ -39,6 +39,9 @@
  * summed by the caller.  Two calls that share a workspace must be ordered on
  * one stream.
  *
+ * Empty problems (zero tokens) return TTT_OK at once, after the descriptor is
+ * checked; their tensor pointers are not examined.
+ *
  * Errors: every argument is checked on the host before anything is launched;
  * a non-zero status means nothing was enqueued.  ttt_attn_last_error() gives
  * the detail (thread-local).  Faults inside kernels surface at the caller's
