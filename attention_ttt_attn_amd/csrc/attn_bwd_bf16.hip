@@ -270,24 +270,36 @@ __global__ void __launch_bounds__(256, 2)
 
 // ============================================================================= dK/dV (trunk)
 // Per 32-query step the workgroup stages Q~ rows, dO rows, Q~^T and dO^T
-// (8 KB each) HBM -> LDS with global_load_lds_dwordx4, double-buffered and
-// XOR-swizzled (16-byte chunk c of row r at slot c ^ (r & 15) for the 256-byte
-// rows, c ^ ((d >> 2) & 3) for the 64-byte transposed rows) so that the MFMA
-// operand reads are conflict-free.  LSE and Delta of the next step go through
-// two VGPRs.
-struct KvSmem {
-  _Float16 q[2][BQ * D];   // Q~ rows   (A of S)
-  uint16_t g[2][BQ * D];   // dO rows   (A of dP)
-  _Float16 qt[2][D * BQ];  // Q~^T      (A of dK^T)
-  uint16_t gt[2][D * BQ];  // dO^T      (A of dV^T)
-  float lse2[2][BQ];       // LSE * log2(e); +inf past the sequence end
-  float dl[2][BQ];
+// (8 KB each) plus the rows' LSE and Delta HBM -> LDS with direct loads
+// (global_load_lds), XOR-swizzled (16-byte chunk c of row r at slot
+// c ^ (r & 15) for the 256-byte rows, c ^ ((d >> 2) & 3) for the 64-byte
+// transposed rows) so that the MFMA operand reads are conflict-free.
+// Software pipeline (one wave per SIMD): iteration i issues the loads of step
+// i+3 into a 4-deep ring of LDS buffers, runs the S/dP products of step i+1,
+// the softmax of step i (whose S/dP came from iteration i-1) and step i's
+// dV/dK products, so the matrix pipe has independent work while the vector
+// ALUs run the softmax.  Every wave issues the same 9 loads per step, so one
+// vmcnt threshold releases exactly the step two ahead.
+constexpr int NBUF = 4;
+struct KvBuf {
+  _Float16 q[BQ * D];   // Q~ rows   (A of S)
+  uint16_t g[BQ * D];   // dO rows   (A of dP)
+  _Float16 qt[D * BQ];  // Q~^T      (A of dK^T)
+  uint16_t gt[D * BQ];  // dO^T      (A of dV^T)
+  float lse[BQ];        // natural-log LSE of the rows
+  float dl[BQ];         // Delta of the rows
 };
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
                                    (void __attribute__((address_space(3)))*)l, 16, 0, 0);
 }
+__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)l, 4, 0, 0);
+}
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left open (gfx9 encoding).
+#define TTT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
 __global__ void __launch_bounds__(256, 1)
     dkdv_bf16_kernel(Prob P, PassPtrs kv, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
@@ -295,20 +307,28 @@ __global__ void __launch_bounds__(256, 1)
                      const _Float16* __restrict__ qtt, const uint16_t* __restrict__ dot,
                      const float* __restrict__ delta, const int4* __restrict__ tiles, const float* __restrict__ cosT,
                      const float* __restrict__ sinT, PassGradPtrs gr) {
-  __shared__ __attribute__((aligned(16))) KvSmem sm;
+  __shared__ __attribute__((aligned(16))) KvBuf sm[NBUF];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int g = blockIdx.x % P.Hkv, tix = blockIdx.x / P.Hkv;
-  int b, t, start, L, slot0;
+  // Order: key tiles heavy-first (ascending tile index), and every (batch, KV
+  // group) pair pinned to one XCD (blockIdx % 8), so the tiles of a pair that
+  // run together share that XCD's L2 for the query rows they all stream.
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  int b, t, start, L, slot0, g;
   if (P.layout == 0) {
     const int nkt = (P.stok + BKV - 1) / BKV;
-    if (tix >= P.B * nkt) return;
-    t = tix / P.B;
-    b = tix % P.B;
+    const int ppx = (P.B * P.Hkv + 7) / 8;  // pairs per XCD
+    t = slot / ppx;
+    const int pair = (slot % ppx) * 8 + xcd;
+    if (t >= nkt || pair >= P.B * P.Hkv) return;
+    b = pair / P.Hkv;
+    g = pair % P.Hkv;
     start = 0;
     L = P.stok;
     slot0 = 0;
   } else {
+    g = blockIdx.x % P.Hkv;
+    const int tix = blockIdx.x / P.Hkv;
     if (tix >= tiles[0].x) return;
     const int4 e = tiles[1 + tix];
     t = e.x, start = e.y, L = e.z, slot0 = e.w, b = 0;
@@ -339,10 +359,11 @@ __global__ void __launch_bounds__(256, 1)
   const float sl2 = P.scale_log2;
   const int wave_key0 = kv0 + wv * 32;
 
-  // Steps = (head of the group, 32-row query block at or after this key tile).
+  // Steps: row block nq-1-st/r (from the sequence end downwards) of head st%r.
   const int nq = (L - kv0 + BQ - 1) / BQ;
   const int nsteps = P.r * nq;
-  // DMA lane roles (wave w issues instructions j = 2w, 2w+1 of each tile):
+  auto step_q0 = [&](int st) { return kv0 + (nq - 1 - st / P.r) * BQ; };
+  // DMA lane roles (wave w issues instructions j = 2w, 2w+1 of each 8 KB tile):
   // rows: r = 4j + lane/16, slot lane%16; transposed: d = 16j + lane/4, slot lane%4.
   uint32_t roff[2], toff[2];
   int rrow[2];
@@ -355,10 +376,11 @@ __global__ void __launch_bounds__(256, 1)
     const int d = 16 * j + (lane >> 2);
     toff[i] = (uint32_t)(d * P.spad + ((lane & 3) ^ ((d >> 2) & 3)) * 8);
   }
-  float plse = 0.f, pdl = 0.f;
-  bool pvalid = false;
-  auto issue = [&](int st, int buf) {
-    const int hh = st / nq, q0 = kv0 + (st % nq) * BQ;
+  // LSE / Delta: waves 0,1 load LSE rows 16w..16w+15, waves 2,3 Delta rows 16(w-2)..
+  const int mrow = (wv & 1) * 16 + (lane & 15);
+  auto issue = [&](int st) {
+    KvBuf& B = sm[st % NBUF];
+    const int hh = st % P.r, q0 = step_q0(st);
     const int h = g * P.r + hh;
     const _Float16* qb = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0 + q0) * D;
     const _Float16* qtb = qtt + (int64_t)(b * P.Hq + h) * D * P.spad + slot0 + q0;
@@ -367,103 +389,113 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = 2 * wv + i;
-      const int r = rrow[i];
-      const int rg = min(q0 + r, L - 1);  // rows past the end repeat the last row (their P is 0)
-      lds_dma16(qb + r * D + roff[i], &sm.q[buf][4 * j * D]);
-      lds_dma16(gb + (int64_t)rg * P.os_t + roff[i], &sm.g[buf][4 * j * D]);
-      lds_dma16(qtb + toff[i], &sm.qt[buf][16 * j * BQ]);
-      lds_dma16(gtb + toff[i], &sm.gt[buf][16 * j * BQ]);
+      const int rg = min(q0 + rrow[i], L - 1);  // rows past the end repeat the last row (masked below)
+      lds_dma16(qb + rrow[i] * D + roff[i], &B.q[4 * j * D]);
+      lds_dma16(gb + (int64_t)rg * P.os_t + roff[i], &B.g[4 * j * D]);
+      lds_dma16(qtb + toff[i], &B.qt[16 * j * BQ]);
+      lds_dma16(gtb + toff[i], &B.gt[16 * j * BQ]);
     }
-    // raw loads only: any use here would make the compiler wait for the DMA above
-    if (tid < BQ) {
-      const int rr = min(q0 + tid, L - 1);
-      plse = lse[b * P.lse_b + h * P.lse_h + start + rr];
-      pdl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + min(q0 + tid, L)];
-      pvalid = q0 + tid < L;
+    if (lane < 16) {
+      const int rr = q0 + mrow;
+      if (wv < 2) lds_dma4(lse + b * P.lse_b + h * P.lse_h + start + min(rr, L - 1), &B.lse[(wv & 1) * 16]);
+      else lds_dma4(delta + (int64_t)(b * P.Hq + h) * P.spad + slot0 + min(rr, L), &B.dl[(wv & 1) * 16]);
     }
-  };
-  auto settle = [&](int buf) {  // after issue() and the compute: publish the step's data
-    if (tid < BQ) {
-      sm.lse2[buf][tid] = pvalid ? plse * kLog2e : INFINITY;
-      sm.dl[buf][tid] = pdl;
-    }
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
   };
 
-  if (nsteps > 0) issue(0, 0);
-  settle(0);
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nsteps) issue(st + 1, buf ^ 1);
-    const int q0 = kv0 + (st % nq) * BQ;
-    if (q0 + BQ - 1 >= wave_key0) {  // else every row of this step precedes this wave's keys
-      const _Float16* ql = sm.q[buf];
-      const uint16_t* gl = sm.g[buf];
-      f32x16 s, dp;
+  // S = Q~ K~^T and dP = dO V^T for step st (this wave's 32 keys x 32 rows).
+  auto products = [&](int st, f32x16& s, f32x16& dp) {
+    const KvBuf& B = sm[st % NBUF];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
+    for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
 #pragma unroll
-      for (int c0 = 0; c0 < 8; c0 += 4) {
-        f16x8 a[4];
-        bf16x8 a2[4];
+    for (int c0 = 0; c0 < 8; c0 += 4) {
+      f16x8 a[4];
+      bf16x8 a2[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int off = prow * D + (((2 * (c0 + c) + hf) ^ (prow & 15)) * 8);
-          a[c] = *(const f16x8*)&ql[off];
-          a2[c] = *(const bf16x8*)&gl[off];
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], kf[c0 + c], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[c], vf[c0 + c], dp, 0, 0, 0);
-        }
+      for (int c = 0; c < 4; ++c) {
+        const int off = prow * D + (((2 * (c0 + c) + hf) ^ (prow & 15)) * 8);
+        a[c] = *(const f16x8*)&B.q[off];
+        a2[c] = *(const bf16x8*)&B.g[off];
       }
-      bf16x8 pb[2];
-      f16x8 dsb[2];
-      auto probs = [&](auto masked) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int m0 = half * 16 + hf * 8;  // this lane's rows m = 16*(v/8) + 8*hf + v%8
-          const f32x4 l0 = *(const f32x4*)&sm.lse2[buf][m0], l1 = *(const f32x4*)&sm.lse2[buf][m0 + 4];
-          const f32x4 d0 = *(const f32x4*)&sm.dl[buf][m0], d1 = *(const f32x4*)&sm.dl[buf][m0 + 4];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int v = half * 8 + e;
-            const float lv = e < 4 ? l0[e] : l1[e - 4];
-            const float dv_ = e < 4 ? d0[e] : d1[e - 4];
-            float pr = fast_exp2(__builtin_fmaf(s[v], sl2, -lv));
-            if constexpr (decltype(masked)::value) {
-              if (q0 + m0 + e < my_key) pr = 0.f;
-            }
-            pb[half][e] = (__bf16)pr;
-            dsb[half][e] = (_Float16)(pr * (dp[v] - dv_));
-          }
-        }
-      };
-      if (q0 < wave_key0 + 31) probs(std::true_type{});
-      else probs(std::false_type{});
-      const _Float16* qtl = sm.qt[buf];
-      const uint16_t* gtl = sm.gt[buf];
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        bf16x8 a[4];
-        f16x8 a2[4];
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4) {
-          const int d = d4 * 32 + l32;
-          const int off = d * BQ + (((2 * c2 + hf) ^ ((d >> 2) & 3)) * 8);
-          a[d4] = *(const bf16x8*)&gtl[off];
-          a2[d4] = *(const f16x8*)&qtl[off];
-        }
-#pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4) {
-          dv[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4], pb[c2], dv[d4], 0, 0, 0);
-          dk[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2[d4], dsb[c2], dk[d4], 0, 0, 0);
-        }
+      for (int c = 0; c < 4; ++c) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], kf[c0 + c], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[c], vf[c0 + c], dp, 0, 0, 0);
       }
     }
-    settle(buf ^ 1);
+  };
+  // prologue: steps 0..2 in flight, steps 0 and 1 landed
+#pragma unroll
+  for (int st = 0; st < 3; ++st)
+    if (st < nsteps) issue(st);
+  if (nsteps >= 3) TTT_WAIT_VMCNT(9);  // leaves only step 2's loads outstanding
+  else TTT_WAIT_VMCNT(0);
+  __syncthreads();
+  f32x16 s_c, dp_c;
+  products(0, s_c, dp_c);
+
+  // Rows past the sequence end need no mask: their Q~^T and dO^T columns and
+  // their Delta are zero in the workspace, so they add nothing to dK or dV.
+  // The causal mask (rows before this lane's key) is one compare per score.
+  for (int st = 0; st < nsteps; ++st) {
+    if (st + 3 < nsteps) issue(st + 3);
+    const KvBuf& Bc = sm[st % NBUF];
+    const int q0 = step_q0(st);
+    // S/dP products of step st+1 (stale data past the last step is computed and
+    // ignored) interleaved with the softmax of step st (S, dP from the previous
+    // iteration): the matrix pipe runs while the vector ALUs do the softmax.
+    f32x16 s_n, dp_n;
+    products(st + 1, s_n, dp_n);
+    bf16x8 pb[2];
+    f16x8 dsb[2];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int m0 = half * 16 + hf * 8;  // this lane's rows m = 16*(v/8) + 8*hf + v%8
+      const int thr = my_key - (q0 + m0);
+      const f32x4 l0 = *(const f32x4*)&Bc.lse[m0], l1 = *(const f32x4*)&Bc.lse[m0 + 4];
+      const f32x4 d0 = *(const f32x4*)&Bc.dl[m0], d1 = *(const f32x4*)&Bc.dl[m0 + 4];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int v = half * 8 + e;
+        const float lv = (e < 4 ? l0[e] : l1[e - 4]) * kLog2e;
+        const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+        float pr = fast_exp2(__builtin_fmaf(s_c[v], sl2, -lv));
+        pr = e >= thr ? pr : 0.f;
+        pb[half][e] = (__bf16)pr;
+        dsb[half][e] = (_Float16)(pr * (dp_c[v] - dv_));
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // 4 LDS reads ahead
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
+    }
+    s_c = s_n;
+    dp_c = dp_n;
+    // dV += dO^T P, dK~ += Q~^T dS for step st
+#pragma unroll
+    for (int c2 = 0; c2 < 2; ++c2) {
+      bf16x8 a[4];
+      f16x8 a2[4];
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4) {
+        const int d = d4 * 32 + l32;
+        const int off = d * BQ + (((2 * c2 + hf) ^ ((d >> 2) & 3)) * 8);
+        a[d4] = *(const bf16x8*)&Bc.gt[off];
+        a2[d4] = *(const f16x8*)&Bc.qt[off];
+      }
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4) {
+        dv[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4], pb[c2], dv[d4], 0, 0, 0);
+        dk[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2[d4], dsb[c2], dk[d4], 0, 0, 0);
+      }
+    }
+    // step st+2 must have landed before the next iteration reads it
+    if (st + 3 < nsteps) TTT_WAIT_VMCNT(9);
+    else TTT_WAIT_VMCNT(0);
+    __syncthreads();
   }
   if (!key_ok) return;
   // epilogue: dK = sigma R(j)^T dK~, dV; lane owns key my_key, d = 32*d4 + 8*v4 + 4*hf + e
@@ -585,10 +617,11 @@ void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const
                       const _Float16* qt, const _Float16* qtt, const uint16_t* dot, const float* delta,
                       const int4* tiles_kv, const float* cosT, const float* sinT, const PassGradPtrs& g,
                       hipStream_t st) {
-  const int nkv =
-      P.layout == 0 ? P.B * ((P.stok + bwd::BKV - 1) / bwd::BKV) : (P.stok + bwd::BKV - 1) / bwd::BKV + P.nseq;
-  bwd::dkdv_bf16_kernel<<<(unsigned)((int64_t)nkv * P.Hkv), 256, 0, st>>>(P, kv, lse, dout, kt, qt, qtt, dot, delta,
-                                                                          tiles_kv, cosT, sinT, g);
+  const int64_t grid = P.layout == 0
+                           ? (int64_t)8 * ((P.B * P.Hkv + 7) / 8) * ((P.stok + bwd::BKV - 1) / bwd::BKV)
+                           : (int64_t)P.Hkv * ((P.stok + bwd::BKV - 1) / bwd::BKV + P.nseq);
+  bwd::dkdv_bf16_kernel<<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, qtt, dot, delta, tiles_kv, cosT,
+                                                        sinT, g);
 }
 
 void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,

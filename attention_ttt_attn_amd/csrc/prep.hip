@@ -136,8 +136,10 @@ __global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict
 // every sequence into tiles of `tile` rows and lists them heavy-first:
 // descending tile index for the query-outer kernels (a query tile's causal
 // work grows with its index), ascending for the key-outer kernel (a key tile's
-// work shrinks with its index).  Entry = {tile index, first token, length,
-// first slot}; out[0].x = count.  One workgroup; deterministic order.
+// work shrinks with its index), or sequence-major with ascending tiles
+// (descending == 2: the key-outer kernel's XCD-local order).  Entry = {tile
+// index, first token, length, first slot}; out[0].x = count.  One workgroup;
+// deterministic order.
 __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int descending, int4* __restrict__ out,
                                                           int max_entries, int* __restrict__ slot_base) {
   __shared__ int s_maxt;
@@ -187,6 +189,25 @@ __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int 
   if (!out) return;
   Prob Q = P;
   Q.slot_base = slot_base ? slot_base : P.slot_base;
+  if (descending == 2) {  // sequence-major, tiles ascending within a sequence
+    for (int s0 = 0; s0 < P.nseq; s0 += 1024) {
+      const int s = s0 + tid;
+      int b, st0 = 0, L = 0, nt = 0;
+      if (s < P.nseq) {
+        seq_info(Q, s, b, st0, L);
+        nt = (L + tile - 1) / tile;
+      }
+      const int inc = block_scan(nt);
+      const int base = s_base + inc - nt;
+      for (int t = 0; t < nt; ++t)
+        if (base + t < max_entries) out[1 + base + t] = make_int4(t, st0, L, Q.slot_base[s]);
+      __syncthreads();
+      if (tid == 1023) s_base += s_scan[1023];
+      __syncthreads();
+    }
+    if (tid == 0) out[0] = make_int4(s_base < max_entries ? s_base : max_entries, 0, 0, 0);
+    return;
+  }
   for (int s = tid; s < P.nseq; s += 1024) {
     int b, st0, L;
     seq_info(Q, s, b, st0, L);
