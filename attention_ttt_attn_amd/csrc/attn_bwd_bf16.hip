@@ -9,10 +9,11 @@
 //   dq = R(i+p-1)^T dq~,  dk^(1)_j = R(j)^T dk~,  dk^(q)_i = R(i+q-1)^T dk~
 //
 // Three kernels:
-// * dq_bf16_kernel (query-outer, MFMA): per 128 query rows of one head, loops
-//   over the causal key tiles and accumulates dQ~^T = K~^T dS^T; the epilogue
-//   adds the branch terms of passes 2..p (row-local, xor-shuffle reductions),
-//   un-rotates and writes dQ.  No atomics: deterministic.
+// * dq_bf16_kernel (query-outer, MFMA): per 32 query rows of the heads of one
+//   KV group, loops over the causal key tiles and accumulates
+//   dQ~^T = K~^T dS^T; the epilogue adds the branch terms of passes 2..p
+//   (row-local, xor-shuffle reductions), un-rotates and writes dQ.  No
+//   atomics: deterministic.
 // * dkdv_bf16_kernel (key-outer, MFMA): per 128 trunk keys of one KV head,
 //   loops over the r query heads of the group and the query rows i >= j;
 //   dK~^T and dV^T stay in VGPRs; un-rotated in the epilogue.
@@ -29,60 +30,117 @@ namespace ttt {
 namespace bwd {
 
 constexpr int D = 128;
-constexpr int KPAD = D + 8;
-constexpr int BN = 64;        // dQ kernel: keys per tile
-constexpr int BM = kBwdBQ;    // dQ kernel: query rows per workgroup
 constexpr int BKV = kBwdBKV;  // dK/dV kernel: keys per workgroup
 constexpr int BQ = 32;        // dK/dV kernel: query rows per step
-constexpr int TPAD = 64 + 8;  // transposed LDS rows of 64 tokens (dQ kernel)
 constexpr int OPAD = D + 4;
 
 __device__ __forceinline__ int perm_row(int a) { return (a & ~0xC) | ((a & 4) << 1) | ((a & 8) >> 1); }
 
 // ============================================================================= dQ
+// A workgroup is 4 wave64s: the R' query heads of one KV group that it covers
+// (R' = 4 for GQA 4:1) times 32*4/R' rows; each wave owns 32 query rows of one
+// head, so with R' = 4 all four waves share one causal extent.  Key tiles of
+// 32 keys -- K~ rows (A of S^T), V rows (A of dP^T) and K~^T (A of dQ^T) --
+// move HBM -> LDS with direct loads (global_load_lds), XOR-swizzled, double
+// buffered: the next tile's loads run under this tile's products; one barrier
+// per tile.  Two workgroups per CU keep the matrix pipe busy while the other
+// one's vector ALUs form dS.
+constexpr int QBN = 32;  // keys per dQ tile
+struct DqBuf {
+  _Float16 k[QBN * D];   // K~ rows: row r at r*D, 16-byte chunk c at slot c ^ (r & 15)
+  uint16_t v[QBN * D];   // V rows, same layout
+  _Float16 kt[D * QBN];  // K~^T: d-row at d*QBN, chunk c at slot c ^ ((d >> 2) & 3)
+};
 struct DqSmem {
   union {
-    struct {
-      _Float16 k[BN][KPAD];   // K~ rows (A of S^T)
-      uint16_t v[BN][KPAD];   // V rows  (A of dP^T)
-      _Float16 kt[D][TPAD];   // K~^T    (A of dQ^T)
-    } loop;
-    float acc[BM][OPAD];
+    DqBuf buf[2];
+    float acc[128][OPAD];  // dQ~ rows (wave, row) for the row-major epilogue
   };
 };
 
+__host__ __device__ constexpr int dq_rows(int heads_per_wg) { return 32 * 4 / heads_per_wg; }
+static int dq_heads_per_wg(int r) { return r % 4 == 0 ? 4 : (r % 2 == 0 ? 2 : 1); }
+
+template <int RH>
 __global__ void __launch_bounds__(256, 2)
     dq_bf16_kernel(Prob P, const uint16_t* __restrict__ q, PassPtrs kv, const float* __restrict__ lse,
                    const uint16_t* __restrict__ dout, const _Float16* __restrict__ kt,
                    const _Float16* __restrict__ ktt, const _Float16* __restrict__ qt, const float* __restrict__ delta,
                    const int4* __restrict__ tiles, const float* __restrict__ cosT, const float* __restrict__ sinT,
                    uint16_t* __restrict__ dq) {
+  constexpr int RT = dq_rows(RH);  // rows per work item
   __shared__ __attribute__((aligned(16))) DqSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
-  const int r = P.r;
-  const int xcd = blockIdx.x & 7, kk = blockIdx.x >> 3;
-  const int logical = ((kk / r) * 8 + xcd) * r + (kk % r);
-  const int hr = logical % r, rest = logical / r;
-  const int g = rest % P.Hkv, tix = rest / P.Hkv;
-  int b, t, start, L, slot0;
+
+  // ---- work item.  BSHD: row tiles heavy-first, every (batch, KV head, head
+  // sub-group) unit pinned to one XCD (blockIdx % 8) so that the row tiles
+  // running together there share its L2 for the keys they stream.  THD: the
+  // scheduler's list (heavy-first), KV head = blockIdx % Hkv.
+  const int nsub = P.r / RH;
+  int b, t, start, L, slot0, g, sub;
   if (P.layout == 0) {
-    const int nqt = (P.stok + BM - 1) / BM;
-    if (tix >= P.B * nqt) return;
-    t = nqt - 1 - tix / P.B;
-    b = tix % P.B;
+    const int units = P.B * P.Hkv * nsub;
+    const int ntl = (P.stok + RT - 1) / RT;
+    const int upx = (units + 7) / 8;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int tix = slot / upx, unit = (slot % upx) * 8 + xcd;
+    if (tix >= ntl || unit >= units) return;
+    t = ntl - 1 - tix;
+    sub = unit % nsub;
+    const int pair = unit / nsub;
+    g = pair % P.Hkv;
+    b = pair / P.Hkv;
     start = 0;
     L = P.stok;
     slot0 = 0;
   } else {
+    const int per = P.Hkv * nsub;
+    const int unit = blockIdx.x % per, tix = blockIdx.x / per;
     if (tix >= tiles[0].x) return;
     const int4 e = tiles[1 + tix];
     t = e.x, start = e.y, L = e.z, slot0 = e.w, b = 0;
+    g = unit / nsub;
+    sub = unit % nsub;
   }
-  const int h = g * r + hr;
-  const int row0 = t * BM;
-  const int my_row = row0 + wv * 32 + l32;
+  const int hw = wv % RH, rbk = wv / RH;
+  const int h = g * P.r + sub * RH + hw;
+  const int row0 = t * RT;
+  const int wave_row0 = row0 + rbk * 32;
+  const int my_row = wave_row0 + l32;
   const bool row_ok = my_row < L;
+  const int qend = min(row0 + RT, L);
+  const int nkt = (qend + QBN - 1) / QBN;  // >= 1: row0 < L
+
+  // DMA lane roles, 6 loads per wave per tile (load n = 2w + i):
+  // K~ and V rows 4n + lane/16, slot lane%16; K~^T d-rows 16n + lane/4, slot lane%4.
+  const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
+  const _Float16* ktbase = ktt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
+  const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * P.ks_b + (int64_t)start * P.ks_t + g * P.ks_h;
+  uint32_t roff[2], toff[2];
+  int rrow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int n = 2 * wv + i;
+    const int r = 4 * n + (lane >> 4);
+    rrow[i] = r;
+    roff[i] = (uint32_t)(((lane & 15) ^ (r & 15)) * 8);
+    const int d = 16 * n + (lane >> 2);
+    toff[i] = (uint32_t)(d * P.spad + ((lane & 3) ^ ((d >> 2) & 3)) * 8);
+  }
+  auto dma = [&](int j) __attribute__((always_inline)) {
+    DqBuf& B_ = sm.buf[j & 1];
+    const int key0 = j * QBN;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int n = 2 * wv + i;
+      const int rg = min(key0 + rrow[i], L - 1);  // V rows past the end repeat the last row (masked)
+      lds_dma16(kbase + (int64_t)(key0 + rrow[i]) * D + roff[i], &B_.k[4 * n * D]);
+      lds_dma16(vbase + (int64_t)rg * P.ks_t + roff[i], &B_.v[4 * n * D]);
+      lds_dma16(ktbase + key0 + toff[i], &B_.kt[16 * n * QBN]);
+    }
+  };
+  dma(0);
 
   // B operands of this lane's query: Q~ (fp16, pre-rotated) and dO (bf16)
   f16x8 qf[8];
@@ -102,14 +160,8 @@ __global__ void __launch_bounds__(256, 2)
   const float lse2 = row_ok ? lse[b * P.lse_b + h * P.lse_h + start + my_row] * kLog2e : INFINITY;
   const float dl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row];
   const float sl2 = P.scale_log2;
-
-  const int qend = min(row0 + BM, L);
-  const int nkt = (qend + BN - 1) / BN;
-  const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
-  const _Float16* ktbase = ktt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
-  const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * P.ks_b + (int64_t)start * P.ks_t + g * P.ks_h;
-  const int krow = tid >> 4, kch = tid & 15;
-  const int trow = tid >> 3, tch = tid & 7;
+  TTT_WAIT_VMCNT(0);
+  __syncthreads();
 
   f32x16 acc[4];
 #pragma unroll
@@ -117,63 +169,59 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[d4][v] = 0.f;
   const int prow = perm_row(l32);
-  const int wave_row0 = row0 + wv * 32;
+  // Tiles whose every key precedes every row of this wave need no mask.
+  const int n_free = (wave_row0 + 1) / QBN;
 
-  for (int kt_ = 0; kt_ < nkt; ++kt_) {
-    {
-      const int key0 = kt_ * BN;
-      __syncthreads();  // previous tile's LDS reads are done
+  // S^T = K~ Q~^T, dP^T = V dO^T, dS = P (dP - Delta), dQ~^T += K~^T dS^T.
+  auto tile = [&](const int j, auto masked) __attribute__((always_inline)) {
+    const DqBuf& B_ = sm.buf[j & 1];
+    f32x16 s, dp;
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int kr = key0 + krow + 16 * it;
-        *(u32x4*)&sm.loop.k[krow + 16 * it][kch * 8] = *(const u32x4*)(kbase + (int64_t)kr * D + kch * 8);
-        *(u32x4*)&sm.loop.v[krow + 16 * it][kch * 8] =
-            kr < L ? *(const u32x4*)(vbase + (int64_t)kr * P.ks_t + kch * 8) : u32x4{0, 0, 0, 0};
-        *(u32x4*)&sm.loop.kt[trow + 32 * it][tch * 8] =
-            *(const u32x4*)(ktbase + (int64_t)(trow + 32 * it) * P.spad + key0 + tch * 8);
+    for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
+#pragma unroll
+    for (int c0 = 0; c0 < 8; c0 += 4) {
+      f16x8 a[4];
+      bf16x8 a2[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int off = prow * D + (((2 * (c0 + c) + hf) ^ (prow & 15)) * 8);
+        a[c] = *(const f16x8*)&B_.k[off];
+        a2[c] = *(const bf16x8*)&B_.v[off];
       }
-      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], qf[c0 + c], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[c], dof[c0 + c], dp, 0, 0, 0);
+      }
     }
-    const int key0 = kt_ * BN;
-    if (key0 > wave_row0 + 31) continue;  // whole tile above this wave's rows
-
-    f16x8 dsb[4];
-    const bool diag = key0 + BN - 1 > wave_row0;
+    // key of (v, hf) = j*QBN + 16*(v/8) + 8*hf + v%8
+    f16x8 dsb[2];
+    const int thr = my_row - (j * QBN + 8 * hf);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s, dp;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const f16x8 a = *(const f16x8*)&sm.loop.k[kb * 32 + prow][c * 16 + hf * 8];
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[c], s, 0, 0, 0);
-        const bf16x8 a2 = *(const bf16x8*)&sm.loop.v[kb * 32 + prow][c * 16 + hf * 8];
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, dof[c], dp, 0, 0, 0);
-      }
-      auto probs = [&](auto masked) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          float pr = fast_exp2(__builtin_fmaf(s[v], sl2, -lse2));
-          if constexpr (decltype(masked)::value) {
-            const int key = key0 + kb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
-            if (key > my_row) pr = 0.f;
-          }
-          dsb[kb * 2 + (v >> 3)][v & 7] = (_Float16)(pr * (dp[v] - dl));
-        }
-      };
-      if (diag) probs(std::true_type{});
-      else probs(std::false_type{});
+    for (int v = 0; v < 16; ++v) {
+      float pr = fast_exp2(__builtin_fmaf(s[v], sl2, -lse2));
+      if constexpr (decltype(masked)::value) pr = (v >> 3) * 16 + (v & 7) > thr ? 0.f : pr;
+      dsb[v >> 3][v & 7] = (_Float16)(pr * (dp[v] - dl));
     }
 #pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2)
+    for (int c2 = 0; c2 < 2; ++c2) {
+      f16x8 a[4];
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4) {
-        const f16x8 a = *(const f16x8*)&sm.loop.kt[d4 * 32 + l32][c2 * 16 + hf * 8];
-        acc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, dsb[c2], acc[d4], 0, 0, 0);
+        const int d = d4 * 32 + l32;
+        a[d4] = *(const f16x8*)&B_.kt[d * QBN + (((2 * c2 + hf) ^ ((d >> 2) & 3)) * 8)];
       }
+#pragma unroll
+      for (int d4 = 0; d4 < 4; ++d4) acc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[d4], dsb[c2], acc[d4], 0, 0, 0);
+    }
+  };
+  for (int j = 0; j < nkt; ++j) {
+    if (j + 1 < nkt) dma(j + 1);
+    if (j < n_free) tile(j, std::false_type{});
+    else tile(j, std::true_type{});
+    TTT_WAIT_VMCNT(0);  // tile j+1 has landed
+    __syncthreads();    // and every wave is done with tile j
   }
-  __syncthreads();
   {
     const int lr = wv * 32 + l32;
 #pragma unroll
@@ -188,12 +236,15 @@ __global__ void __launch_bounds__(256, 2)
   }
   __syncthreads();
 
-  // row-major epilogue: branch terms, un-rotation, store
+  // row-major epilogue: branch terms, un-rotation, store.  LDS row lr holds
+  // wave lr/32's row lr%32.
   const int c8 = tid & 7;
   const int dlo = c8 * 8, dhi = 64 + c8 * 8;
-  for (int rp = 0; rp < BM; rp += 32) {
+  for (int rp = 0; rp < 128; rp += 32) {
     const int lr = rp + (tid >> 3);
-    const int i = row0 + lr;
+    const int w_ = lr >> 5;
+    const int hh = g * P.r + sub * RH + w_ % RH;
+    const int i = row0 + (w_ / RH) * 32 + (lr & 31);
     if (i >= L) continue;
     float a[16];
     {
@@ -209,8 +260,8 @@ __global__ void __launch_bounds__(256, 2)
     if (P.p > 1) {
       float qr[16], go[16];
       {
-        const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + i) * P.qs_t + h * P.qs_h;
-        const uint16_t* grow = dout + b * P.os_b + (int64_t)(start + i) * P.os_t + h * P.os_h;
+        const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + i) * P.qs_t + hh * P.qs_h;
+        const uint16_t* grow = dout + b * P.os_b + (int64_t)(start + i) * P.os_t + hh * P.os_h;
         float x1[8], x2[8];
         unpack_bf8(*(const u32x4*)(qrow + dlo), x1);
         unpack_bf8(*(const u32x4*)(qrow + dhi), x2);
@@ -222,8 +273,8 @@ __global__ void __launch_bounds__(256, 2)
         unpack_bf8(*(const u32x4*)(grow + dlo), go);
         unpack_bf8(*(const u32x4*)(grow + dhi), go + 8);
       }
-      const float lse_i = lse[b * P.lse_b + h * P.lse_h + start + i];
-      const float dl_i = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + i];
+      const float lse_i = lse[b * P.lse_b + hh * P.lse_h + start + i];
+      const float dl_i = delta[(int64_t)(b * P.Hq + hh) * P.spad + slot0 + i];
       const int64_t koff = b * P.ks_b + (int64_t)(start + i) * P.ks_t + g * P.ks_h;
       for (int qq = 2; qq <= P.p; ++qq) {
         const uint16_t* krow_ = (const uint16_t*)kv.k[qq - 1] + koff;
@@ -262,7 +313,7 @@ __global__ void __launch_bounds__(256, 2)
       res[e] = a[e] * cq[e] + a[8 + e] * sq[e];
       res[8 + e] = a[8 + e] * cq[e] - a[e] * sq[e];
     }
-    uint16_t* orow = dq + b * P.qs_b + (int64_t)(start + i) * P.qs_t + h * P.qs_h;
+    uint16_t* orow = dq + b * P.qs_b + (int64_t)(start + i) * P.qs_t + hh * P.qs_h;
     *(u32x4*)(orow + dlo) = pack_bf8(res);
     *(u32x4*)(orow + dhi) = pack_bf8(res + 8);
   }
@@ -290,16 +341,6 @@ struct KvBuf {
   float dl[BQ];         // Delta of the rows
 };
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)l, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)l, 4, 0, 0);
-}
-// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left open (gfx9 encoding).
-#define TTT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
 __global__ void __launch_bounds__(256, 1)
     dkdv_bf16_kernel(Prob P, PassPtrs kv, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
@@ -357,7 +398,6 @@ __global__ void __launch_bounds__(256, 1)
     for (int v = 0; v < 16; ++v) dk[d4][v] = dv[d4][v] = 0.f;
   const int prow = perm_row(l32);
   const float sl2 = P.scale_log2;
-  const int wave_key0 = kv0 + wv * 32;
 
   // Steps: row block nq-1-st/r (from the sequence end downwards) of head st%r.
   const int nq = (L - kv0 + BQ - 1) / BQ;
@@ -624,14 +664,33 @@ void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const
                                                         sinT, g);
 }
 
+template <int RH>
+static void launch_dq_rh(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
+                         const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
+                         const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st) {
+  constexpr int RT = bwd::dq_rows(RH);
+  const int nsub = P.r / RH;
+  int64_t grid;
+  if (P.layout == 0) {
+    const int64_t units = (int64_t)P.B * P.Hkv * nsub;
+    grid = 8 * ((units + 7) / 8) * ((P.stok + RT - 1) / RT);
+  } else {
+    grid = (int64_t)((P.stok + RT - 1) / RT + P.nseq) * P.Hkv * nsub;
+  }
+  bwd::dq_bf16_kernel<RH><<<(unsigned)grid, 256, 0, st>>>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT,
+                                                          sinT, dq);
+}
+
+int dq_tile_rows(int r) { return bwd::dq_rows(bwd::dq_heads_per_wg(r)); }
+
 void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
                     const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
                     const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st) {
-  const int nq = P.layout == 0 ? P.B * ((P.stok + bwd::BM - 1) / bwd::BM) : (P.stok + bwd::BM - 1) / bwd::BM + P.nseq;
-  const int64_t items = (int64_t)nq * P.Hq, unit = 8 * (int64_t)P.r;
-  const int64_t grid = (items + unit - 1) / unit * unit;
-  bwd::dq_bf16_kernel<<<(unsigned)grid, 256, 0, st>>>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT,
-                                                      dq);
+  switch (bwd::dq_heads_per_wg(P.r)) {
+    case 4: launch_dq_rh<4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, st); break;
+    case 2: launch_dq_rh<2>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, st); break;
+    default: launch_dq_rh<1>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, st); break;
+  }
 }
 
 void launch_branch_bwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse,

@@ -68,11 +68,6 @@ struct Smem {
 
 __device__ __forceinline__ int perm_row(int a) { return (a & ~0xC) | ((a & 4) << 1) | ((a & 8) >> 1); }
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)l, 16, 0, 0);
-}
-
 // Rows of one work item, per R' (heads per workgroup).
 __host__ __device__ constexpr int tile_rows(int heads_per_wg) { return 32 * 4 / heads_per_wg; }
 

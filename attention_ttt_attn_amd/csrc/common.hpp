@@ -154,6 +154,30 @@ __device__ __forceinline__ u32x4 pack_h8(const float* f) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// HBM -> LDS without VGPR staging (global_load_lds): lane l's 16 (or 4) bytes
+// land at l * 16 (or l * 4) bytes past the wave-uniform LDS address.
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)l, 4, 0, 0);
+}
+// s_waitcnt vmcnt(n) with expcnt/lgkmcnt left open (gfx9 encoding).
+#define TTT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+
+// Max and sum over the two 32-lane halves of a wave (v_permlane32_swap: the
+// two results hold the low and the high half's value in every lane).
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Workspace layout shared by host launchers.
 struct WsPlan {
   size_t table, slots, tiles_q, tiles_kv, kt, vt, ktt, qt, qtt, dot, delta, total;

@@ -375,7 +375,7 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
     if (pl.bf16) {
       int4* a = at<int4>(ws, pl.ws.tiles_q);
       int4* b = at<int4>(ws, pl.ws.tiles_kv);
-      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kBwdBQ, 1, a, pl.max_tiles_q, slots, st));
+      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::dq_tile_rows(P.r), 1, a, pl.max_tiles_q, slots, st));
       TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kBwdBKV, 0, b, pl.max_tiles_kv, nullptr, st));
       tq = a;
       tkv = b;

@@ -27,7 +27,7 @@ void launch_bwd_f32(const Prob& P, const PassPtrs& kv, const float* lse, const f
 // bf16 path (MFMA trunk + shuffle-reduction branch)
 int fwd_tile_rows(int r);     // query rows per forward work item for GQA ratio r (32, 64 or 128)
 constexpr int kFwdMinRows = 32;
-constexpr int kBwdBQ = 128;   // query rows per dQ workgroup
+int dq_tile_rows(int r);      // query rows per dQ work item for GQA ratio r (32, 64 or 128)
 constexpr int kBwdBKV = 128;  // key rows per dK/dV workgroup
 void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const uint16_t* vt,
                      const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
