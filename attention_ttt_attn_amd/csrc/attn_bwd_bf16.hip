@@ -320,23 +320,22 @@ __global__ void __launch_bounds__(256, 2)
 }
 
 // ============================================================================= dK/dV (trunk)
-// Per 32-query step the workgroup stages Q~ rows, dO rows, Q~^T and dO^T
-// (8 KB each) plus the rows' LSE and Delta HBM -> LDS with direct loads
-// (global_load_lds), XOR-swizzled (16-byte chunk c of row r at slot
-// c ^ (r & 15) for the 256-byte rows, c ^ ((d >> 2) & 3) for the 64-byte
-// transposed rows) so that the MFMA operand reads are conflict-free.
+// Per 32-query step the workgroup stages Q~ rows and dO rows (8 KB each) plus
+// the rows' LSE and Delta HBM -> LDS with direct loads (global_load_lds),
+// XOR-swizzled (16-byte chunk c of row r at slot c ^ (r & 15)) so that the
+// MFMA operand reads are conflict-free.  The transposed operands of
+// dV^T += dO^T P and dK~^T += Q~^T dS are column reads of the same tiles
+// (ds_read_b64_tr_b16), so no transposed copy is streamed.
 // Software pipeline (one wave per SIMD): iteration i issues the loads of step
 // i+3 into a 4-deep ring of LDS buffers, runs the S/dP products of step i+1,
 // the softmax of step i (whose S/dP came from iteration i-1) and step i's
 // dV/dK products, so the matrix pipe has independent work while the vector
-// ALUs run the softmax.  Every wave issues the same 9 loads per step, so one
+// ALUs run the softmax.  Every wave issues the same 5 loads per step, so one
 // vmcnt threshold releases exactly the step two ahead.
 constexpr int NBUF = 4;
 struct KvBuf {
-  _Float16 q[BQ * D];   // Q~ rows   (A of S)
-  uint16_t g[BQ * D];   // dO rows   (A of dP)
-  _Float16 qt[D * BQ];  // Q~^T      (A of dK^T)
-  uint16_t gt[D * BQ];  // dO^T      (A of dV^T)
+  _Float16 q[BQ * D];   // Q~ rows   (A of S; columns: A of dK^T)
+  uint16_t g[BQ * D];   // dO rows   (A of dP; columns: A of dV^T)
   float lse[BQ];        // natural-log LSE of the rows
   float dl[BQ];         // Delta of the rows
 };
@@ -345,7 +344,6 @@ struct KvBuf {
 __global__ void __launch_bounds__(256, 1)
     dkdv_bf16_kernel(Prob P, PassPtrs kv, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
                      const _Float16* __restrict__ kt, const _Float16* __restrict__ qt,
-                     const _Float16* __restrict__ qtt, const uint16_t* __restrict__ dot,
                      const float* __restrict__ delta, const int4* __restrict__ tiles, const float* __restrict__ cosT,
                      const float* __restrict__ sinT, PassGradPtrs gr) {
   __shared__ __attribute__((aligned(16))) KvBuf sm[NBUF];
@@ -404,8 +402,8 @@ __global__ void __launch_bounds__(256, 1)
   const int nsteps = P.r * nq;
   auto step_q0 = [&](int st) { return kv0 + (nq - 1 - st / P.r) * BQ; };
   // DMA lane roles (wave w issues instructions j = 2w, 2w+1 of each 8 KB tile):
-  // rows: r = 4j + lane/16, slot lane%16; transposed: d = 16j + lane/4, slot lane%4.
-  uint32_t roff[2], toff[2];
+  // rows r = 4j + lane/16, slot lane%16.
+  uint32_t roff[2];
   int rrow[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -413,9 +411,10 @@ __global__ void __launch_bounds__(256, 1)
     const int r = 4 * j + (lane >> 4);
     rrow[i] = r;
     roff[i] = (uint32_t)(((lane & 15) ^ (r & 15)) * 8);
-    const int d = 16 * j + (lane >> 2);
-    toff[i] = (uint32_t)(d * P.spad + ((lane & 3) ^ ((d >> 2) & 3)) * 8);
   }
+  // dO rows past the sequence end are read from an all-zero workspace row (the
+  // last slot of the first Q~ slab never holds a token), so they add nothing.
+  const uint16_t* zrow = (const uint16_t*)(qt + (int64_t)(P.spad - 1) * D);
   // LSE / Delta: waves 0,1 load LSE rows 16w..16w+15, waves 2,3 Delta rows 16(w-2)..
   const int mrow = (wv & 1) * 16 + (lane & 15);
   auto issue = [&](int st) {
@@ -423,17 +422,14 @@ __global__ void __launch_bounds__(256, 1)
     const int hh = st % P.r, q0 = step_q0(st);
     const int h = g * P.r + hh;
     const _Float16* qb = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0 + q0) * D;
-    const _Float16* qtb = qtt + (int64_t)(b * P.Hq + h) * D * P.spad + slot0 + q0;
-    const uint16_t* gtb = dot + (int64_t)(b * P.Hq + h) * D * P.spad + slot0 + q0;
     const uint16_t* gb = dout + b * P.os_b + (int64_t)start * P.os_t + h * P.os_h;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = 2 * wv + i;
-      const int rg = min(q0 + rrow[i], L - 1);  // rows past the end repeat the last row (masked below)
+      const int rg = q0 + rrow[i];
+      const uint16_t* gsrc = rg < L ? gb + (int64_t)rg * P.os_t : zrow;
       lds_dma16(qb + rrow[i] * D + roff[i], &B.q[4 * j * D]);
-      lds_dma16(gb + (int64_t)rg * P.os_t + roff[i], &B.g[4 * j * D]);
-      lds_dma16(qtb + toff[i], &B.qt[16 * j * BQ]);
-      lds_dma16(gtb + toff[i], &B.gt[16 * j * BQ]);
+      lds_dma16(gsrc + roff[i], &B.g[4 * j * D]);
     }
     if (lane < 16) {
       const int rr = q0 + mrow;
@@ -468,14 +464,14 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
   for (int st = 0; st < 3; ++st)
     if (st < nsteps) issue(st);
-  if (nsteps >= 3) TTT_WAIT_VMCNT(9);  // leaves only step 2's loads outstanding
+  if (nsteps >= 3) TTT_WAIT_VMCNT(5);  // leaves only step 2's loads outstanding
   else TTT_WAIT_VMCNT(0);
   __syncthreads();
   f32x16 s_c, dp_c;
   products(0, s_c, dp_c);
 
-  // Rows past the sequence end need no mask: their Q~^T and dO^T columns and
-  // their Delta are zero in the workspace, so they add nothing to dK or dV.
+  // Rows past the sequence end need no mask: their Q~ and dO rows and their
+  // Delta are zero, so they add nothing to dK or dV.
   // The causal mask (rows before this lane's key) is one compare per score.
   for (int st = 0; st < nsteps; ++st) {
     if (st + 3 < nsteps) issue(st + 3);
@@ -505,26 +501,27 @@ __global__ void __launch_bounds__(256, 1)
         dsb[half][e] = (_Float16)(pr * (dp_c[v] - dv_));
       }
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);    // 4 LDS reads ahead
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // 5 VALU
-    }
     s_c = s_n;
     dp_c = dp_n;
-    // dV += dO^T P, dK~ += Q~^T dS for step st
+    // dV += dO^T P, dK~ += Q~^T dS for step st: A operands are columns of the
+    // dO and Q~ tiles (lane d = 32*d4 + l32, rows 16*c2 + 8*hf + 0..7).
 #pragma unroll
     for (int c2 = 0; c2 < 2; ++c2) {
       bf16x8 a[4];
       f16x8 a2[4];
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4) {
-        const int d = d4 * 32 + l32;
-        const int off = d * BQ + (((2 * c2 + hf) ^ ((d >> 2) & 3)) * 8);
-        a[d4] = *(const bf16x8*)&Bc.gt[off];
-        a2[d4] = *(const f16x8*)&Bc.qt[off];
+        s16x4 x[2], y[2];
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+          const int r = c2 * 16 + hf * 8 + part * 4 + ((lane & 15) >> 2);
+          const int col = d4 * 32 + (lane & 16) + 4 * (lane & 3);
+          const int off = r * D + ((((col >> 3) ^ (r & 15))) << 3) + (col & 7);
+          x[part] = lds_read_tr16(&Bc.g[off]);
+          y[part] = lds_read_tr16(&Bc.q[off]);
+        }
+        a[d4] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x[0], x[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        a2[d4] = __builtin_bit_cast(f16x8, __builtin_shufflevector(y[0], y[1], 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4) {
@@ -533,7 +530,7 @@ __global__ void __launch_bounds__(256, 1)
       }
     }
     // step st+2 must have landed before the next iteration reads it
-    if (st + 3 < nsteps) TTT_WAIT_VMCNT(9);
+    if (st + 3 < nsteps) TTT_WAIT_VMCNT(5);
     else TTT_WAIT_VMCNT(0);
     __syncthreads();
   }
@@ -654,14 +651,12 @@ __global__ void __launch_bounds__(256)
 }  // namespace bwd
 
 void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const uint16_t* dout, const _Float16* kt,
-                      const _Float16* qt, const _Float16* qtt, const uint16_t* dot, const float* delta,
-                      const int4* tiles_kv, const float* cosT, const float* sinT, const PassGradPtrs& g,
-                      hipStream_t st) {
+                      const _Float16* qt, const float* delta, const int4* tiles_kv, const float* cosT,
+                      const float* sinT, const PassGradPtrs& g, hipStream_t st) {
   const int64_t grid = P.layout == 0
                            ? (int64_t)8 * ((P.B * P.Hkv + 7) / 8) * ((P.stok + bwd::BKV - 1) / bwd::BKV)
                            : (int64_t)P.Hkv * ((P.stok + bwd::BKV - 1) / bwd::BKV + P.nseq);
-  bwd::dkdv_bf16_kernel<<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, qtt, dot, delta, tiles_kv, cosT,
-                                                        sinT, g);
+  bwd::dkdv_bf16_kernel<<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);
 }
 
 template <int RH>

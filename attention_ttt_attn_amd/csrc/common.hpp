@@ -167,6 +167,16 @@ __device__ __forceinline__ void lds_dma4(const void* g, void* l) {
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left open (gfx9 encoding).
 #define TTT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within every 16-lane group,
+// lane 4e + a supplies the address of 4 consecutive 16-bit elements; lane
+// 4a + b receives element b of the chunks of lanes a, a+4, a+8, a+12.  So if
+// lane s points at row r0 + s/4, column c0 + 4*(s%4) of a row-major tile,
+// lane s receives column c0 + s, rows r0..r0+3: a column read.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+}
+
 // Max and sum over the two 32-lane halves of a wave (v_permlane32_swap: the
 // two results hold the low and the high half's value in every lane).
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -180,7 +190,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 // Workspace layout shared by host launchers.
 struct WsPlan {
-  size_t table, slots, tiles_q, tiles_kv, kt, vt, ktt, qt, qtt, dot, delta, total;
+  size_t table, slots, tiles_q, tiles_kv, kt, vt, ktt, qt, delta, total;
 };
 
 }  // namespace ttt

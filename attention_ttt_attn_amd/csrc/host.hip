@@ -161,8 +161,6 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl) {
       if (thd) w.tiles_kv = take((size_t)(pl.max_tiles_kv + 1) * 16);
       w.ktt = take(nkv * 2);
       w.qt = take(nq * 2);
-      w.qtt = take(nq * 2);
-      w.dot = take(nq * 2);
       w.delta = take((size_t)B * Hq * P.spad * 4);
     }
   } else {
@@ -396,16 +394,12 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
     _Float16* kt = at<_Float16>(ws, pl.ws.kt);
     _Float16* ktt = at<_Float16>(ws, pl.ws.ktt);
     _Float16* qt = at<_Float16>(ws, pl.ws.qt);
-    _Float16* qtt = at<_Float16>(ws, pl.ws.qtt);
-    uint16_t* dot = at<uint16_t>(ws, pl.ws.dot);
     TTT_TRACED("prep_k", ttt::launch_prep_rot_h(P, (const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT,
                                                 sinT, kt, ktt, st));
     TTT_TRACED("prep_q", ttt::launch_prep_rot_h(P, (const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, cosT,
-                                                sinT, qt, qtt, st));
-    TTT_TRACED("prep_dot",
-               ttt::launch_prep_transpose_bf(P, (const uint16_t*)dout, P.os_b, P.os_t, P.os_h, P.Hq, dot, st));
-    TTT_TRACED("trunk_dkdv", ttt::launch_dkdv_bf16(P, kv, lse, (const uint16_t*)dout, kt, qt, qtt, dot, delta, tkv,
-                                                   cosT, sinT, g, st));
+                                                sinT, qt, nullptr, st));
+    TTT_TRACED("trunk_dkdv", ttt::launch_dkdv_bf16(P, kv, lse, (const uint16_t*)dout, kt, qt, delta, tkv, cosT,
+                                                   sinT, g, st));
     TTT_TRACED("trunk_dq", ttt::launch_dq_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, kt, ktt, qt,
                                                delta, tq, cosT, sinT, (uint16_t*)dq, st));
     if (P.p > 1)

@@ -33,9 +33,8 @@ void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const
                      const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
                      hipStream_t st);
 void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const uint16_t* dout, const _Float16* kt,
-                      const _Float16* qt, const _Float16* qtt, const uint16_t* dot, const float* delta,
-                      const int4* tiles_kv, const float* cosT, const float* sinT, const PassGradPtrs& g,
-                      hipStream_t st);
+                      const _Float16* qt, const float* delta, const int4* tiles_kv, const float* cosT,
+                      const float* sinT, const PassGradPtrs& g, hipStream_t st);
 void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
                     const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
                     const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st);
