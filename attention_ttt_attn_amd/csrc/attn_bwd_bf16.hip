@@ -128,8 +128,8 @@ __global__ void __launch_bounds__(256, 2)
     const int d = 16 * n + (lane >> 2);
     toff[i] = (uint32_t)(d * P.spad + ((lane & 3) ^ ((d >> 2) & 3)) * 8);
   }
-  auto dma = [&](int j) __attribute__((always_inline)) {
-    DqBuf& B_ = sm.buf[j & 1];
+  auto dma = [&](DqBuf* __restrict__ dst, int j) __attribute__((always_inline)) {
+    DqBuf& B_ = *dst;
     const int key0 = j * QBN;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256, 2)
       lds_dma16(ktbase + key0 + toff[i], &B_.kt[16 * n * QBN]);
     }
   };
-  dma(0);
+  dma(&sm.buf[0], 0);
 
   // B operands of this lane's query: Q~ (fp16, pre-rotated) and dO (bf16)
   f16x8 qf[8];
@@ -161,6 +161,7 @@ __global__ void __launch_bounds__(256, 2)
   const float dl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row];
   const float sl2 = P.scale_log2;
   TTT_WAIT_VMCNT(0);
+  asm volatile("" ::"v"(lse2), "v"(dl));  // their loads complete here, not inside the loop
   __syncthreads();
 
   f32x16 acc[4];
@@ -173,8 +174,8 @@ __global__ void __launch_bounds__(256, 2)
   const int n_free = (wave_row0 + 1) / QBN;
 
   // S^T = K~ Q~^T, dP^T = V dO^T, dS = P (dP - Delta), dQ~^T += K~^T dS^T.
-  auto tile = [&](const int j, auto masked) __attribute__((always_inline)) {
-    const DqBuf& B_ = sm.buf[j & 1];
+  auto tile = [&](const DqBuf* __restrict__ src, const int j, auto masked) __attribute__((always_inline)) {
+    const DqBuf& B_ = *src;
     f32x16 s, dp;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
@@ -216,9 +217,14 @@ __global__ void __launch_bounds__(256, 2)
     }
   };
   for (int j = 0; j < nkt; ++j) {
-    if (j + 1 < nkt) dma(j + 1);
-    if (j < n_free) tile(j, std::false_type{});
-    else tile(j, std::true_type{});
+    // distinct restrict pointers: the loads into the other buffer cannot alias
+    // this tile's LDS reads, so the compiler puts no wait on them
+    auto step = [&](const DqBuf* __restrict__ cur, DqBuf* __restrict__ nxt) __attribute__((always_inline)) {
+      if (j + 1 < nkt) dma(nxt, j + 1);
+      if (j < n_free) tile(cur, j, std::false_type{});
+      else tile(cur, j, std::true_type{});
+    };
+    step(&sm.buf[j & 1], &sm.buf[(j + 1) & 1]);
     TTT_WAIT_VMCNT(0);  // tile j+1 has landed
     __syncthreads();    // and every wave is done with tile j
   }
@@ -417,8 +423,8 @@ __global__ void __launch_bounds__(256, 1)
   const uint16_t* zrow = (const uint16_t*)(qt + (int64_t)(P.spad - 1) * D);
   // LSE / Delta: waves 0,1 load LSE rows 16w..16w+15, waves 2,3 Delta rows 16(w-2)..
   const int mrow = (wv & 1) * 16 + (lane & 15);
-  auto issue = [&](int st) {
-    KvBuf& B = sm[st % NBUF];
+  auto issue = [&](KvBuf* __restrict__ Bd, int st) __attribute__((always_inline)) {
+    KvBuf& B = *Bd;
     const int hh = st % P.r, q0 = step_q0(st);
     const int h = g * P.r + hh;
     const _Float16* qb = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0 + q0) * D;
@@ -439,8 +445,8 @@ __global__ void __launch_bounds__(256, 1)
   };
 
   // S = Q~ K~^T and dP = dO V^T for step st (this wave's 32 keys x 32 rows).
-  auto products = [&](int st, f32x16& s, f32x16& dp) {
-    const KvBuf& B = sm[st % NBUF];
+  auto products = [&](const KvBuf* __restrict__ Bp, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
+    const KvBuf& B = *Bp;
 #pragma unroll
     for (int v = 0; v < 16; ++v) s[v] = dp[v] = 0.f;
 #pragma unroll
@@ -463,25 +469,30 @@ __global__ void __launch_bounds__(256, 1)
   // prologue: steps 0..2 in flight, steps 0 and 1 landed
 #pragma unroll
   for (int st = 0; st < 3; ++st)
-    if (st < nsteps) issue(st);
+    if (st < nsteps) issue(&sm[st], st);
   if (nsteps >= 3) TTT_WAIT_VMCNT(5);  // leaves only step 2's loads outstanding
   else TTT_WAIT_VMCNT(0);
   __syncthreads();
   f32x16 s_c, dp_c;
-  products(0, s_c, dp_c);
+  products(&sm[0], s_c, dp_c);
 
   // Rows past the sequence end need no mask: their Q~ and dO rows and their
   // Delta are zero, so they add nothing to dK or dV.
   // The causal mask (rows before this lane's key) is one compare per score.
+  // The three ring buffers an iteration touches go through distinct restrict
+  // pointers: the compiler then knows the loads into the step-(st+3) buffer
+  // cannot alias this iteration's LDS reads and puts no wait on them.
   for (int st = 0; st < nsteps; ++st) {
-    if (st + 3 < nsteps) issue(st + 3);
-    const KvBuf& Bc = sm[st % NBUF];
+   auto step = [&](const KvBuf* __restrict__ Bcp, const KvBuf* __restrict__ Bnp, KvBuf* __restrict__ Bdp)
+                   __attribute__((always_inline)) {
+    if (st + 3 < nsteps) issue(Bdp, st + 3);
+    const KvBuf& Bc = *Bcp;
     const int q0 = step_q0(st);
     // S/dP products of step st+1 (stale data past the last step is computed and
     // ignored) interleaved with the softmax of step st (S, dP from the previous
     // iteration): the matrix pipe runs while the vector ALUs do the softmax.
     f32x16 s_n, dp_n;
-    products(st + 1, s_n, dp_n);
+    products(Bnp, s_n, dp_n);
     bf16x8 pb[2];
     f16x8 dsb[2];
 #pragma unroll
@@ -529,6 +540,8 @@ __global__ void __launch_bounds__(256, 1)
         dk[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a2[d4], dsb[c2], dk[d4], 0, 0, 0);
       }
     }
+   };
+    step(&sm[st % NBUF], &sm[(st + 1) % NBUF], &sm[(st + 3) % NBUF]);
     // step st+2 must have landed before the next iteration reads it
     if (st + 3 < nsteps) TTT_WAIT_VMCNT(5);
     else TTT_WAIT_VMCNT(0);
