@@ -51,13 +51,17 @@ constexpr int BN = 64;  // keys per tile
 constexpr int OPAD = D + 4;
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef __bf16 b2 __attribute__((ext_vector_type(2)));
 
+constexpr int NBUF = 2;          // tiles in the LDS ring (loads run NBUF-1 tiles ahead)
+constexpr int CH = BN / 8;         // 16-byte chunks per V^T d-row
+struct Tile {
+  _Float16 k[BN * D];  // K~ tile: row r at r*D, 16-byte chunk c at slot c ^ (r & 15)
+  uint16_t v[D * BN];  // V^T tile: d-row at d*BN, chunk c at slot c ^ ((d >> 1) & (CH - 1))
+};
 struct Smem {
   union {
-    struct {
-      _Float16 k[2][BN * D];   // K~ tile: row r at r*D, 16-byte chunk c at slot c ^ (r & 15)
-      uint16_t v[2][D * BN];   // V^T tile: d-row at d*BN, chunk c at slot c ^ ((d >> 1) & 7)
-    } loop;
+    Tile ring[NBUF];
     struct {
       _Float16 k[128][D + 8];  // branch keys R(i+q-1) k^(q), fp16, per row of the tile
       uint16_t v[128][D + 8];  // branch values, bf16
@@ -147,28 +151,44 @@ __global__ void __launch_bounds__(256, 2)
   const int nkt = (qend + BN - 1) / BN;
   const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
   const uint16_t* vbase = vt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
-  // DMA lane roles.  K~: wave w fills rows 16w + 4i + lane/16 (i = 0..3), slot lane%16.
-  // V^T: wave w fills d-rows 32w + 8i + lane/8, slot lane%8.  Per-lane 32-bit
+  // DMA lane roles, loads n = w*KL + i.  K~: 1 KB = rows 4n + lane/16, slot
+  // lane%16.  V^T: 1 KB = d-rows RPL*n + lane/CH, slot lane%CH.  Per-lane 32-bit
   // offsets, tile bases are wave-uniform.
-  uint32_t koff[4], voff[4];
+  constexpr int KL = BN / 16;        // K~ loads per wave per tile
+  constexpr int RPL = 64 / CH;       // V^T d-rows per load
+  constexpr int VL = D / RPL / 4;    // V^T loads per wave per tile
+  constexpr int TL = KL + VL;        // loads per wave per tile
+  uint32_t koff[KL], voff[VL];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * wv + 4 * i + (lane >> 4);
+  for (int i = 0; i < KL; ++i) {
+    const int r = 4 * (wv * KL + i) + (lane >> 4);
     koff[i] = (uint32_t)(r * D + ((lane & 15) ^ (r & 15)) * 8);
-    const int d = 32 * wv + 8 * i + (lane >> 3);
-    voff[i] = (uint32_t)(d * P.spad + ((lane & 7) ^ ((d >> 1) & 7)) * 8);
   }
-  auto dma = [&](int kt_, int buf) {
+#pragma unroll
+  for (int i = 0; i < VL; ++i) {
+    const int d = RPL * (wv * VL + i) + lane / CH;
+    voff[i] = (uint32_t)(d * P.spad + ((lane % CH) ^ ((d >> 1) & (CH - 1))) * 8);
+  }
+  auto dma = [&](Tile* __restrict__ dst, int kt_) __attribute__((always_inline)) {
     const _Float16* kb_t = kbase + (int64_t)kt_ * BN * D;
     const uint16_t* vb_t = vbase + kt_ * BN;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(kb_t + koff[i], &sm.loop.k[buf][(16 * wv + 4 * i) * D]);
+    for (int i = 0; i < KL; ++i) lds_dma16(kb_t + koff[i], &dst->k[4 * (wv * KL + i) * D]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lds_dma16(vb_t + voff[i], &sm.loop.v[buf][(32 * wv + 8 * i) * BN]);
+    for (int i = 0; i < VL; ++i) lds_dma16(vb_t + voff[i], &dst->v[RPL * (wv * VL + i) * BN]);
+  };
+  // wait_tiles(n): all but this wave's last n tiles of loads have landed
+  auto wait_tiles = [&](int n) __attribute__((always_inline)) {
+    if (n <= 0) TTT_WAIT_VMCNT(0);
+    else if (n == 1) TTT_WAIT_VMCNT(TL);
+    else TTT_WAIT_VMCNT(2 * TL);
   };
 
-  dma(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
+  dma(&sm.ring[0], 0);
+#pragma unroll
+  for (int tt = 1; tt < NBUF - 1; ++tt)
+    if (tt < nkt) dma(&sm.ring[tt], tt);
+  wait_tiles(min(nkt, NBUF - 1) - 1);
   __syncthreads();
 
   f32x16 oacc[4];
@@ -202,12 +222,13 @@ __global__ void __launch_bounds__(256, 2)
   };
 
   // One key tile: S^T = K~ Q~^T, online softmax, O^T += V^T P^T.
-  auto tile = [&](const int buf, const int key0, auto masked) {
-    const _Float16* kl = sm.loop.k[buf];
-    const uint16_t* vl = sm.loop.v[buf];
-    f32x16 sacc[2];
+  auto tile = [&](const Tile* __restrict__ cur, const int key0, auto masked) __attribute__((always_inline)) {
+    constexpr int KB = BN / 32;
+    const _Float16* kl = cur->k;
+    const uint16_t* vl = cur->v;
+    f32x16 sacc[KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       const int r = kb * 32 + prow;
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
@@ -223,7 +244,7 @@ __global__ void __launch_bounds__(256, 2)
     }
     if constexpr (decltype(masked)::value) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = key0 + kb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
@@ -232,44 +253,52 @@ __global__ void __launch_bounds__(256, 2)
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * sl2;
+    mx = xhalf_max(mx) * sl2;
     raise_max(mx);
     const float neg_m = -m_run;
-    float lsum = 0.f;
-    bf16x8 pb[4];
+    bf16x8 pb[2 * KB];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float pv = fast_exp2(__builtin_fmaf(sacc[kb][v], sl2, neg_m));
-        lsum += pv;
-        pb[kb * 2 + (v >> 3)][v & 7] = (__bf16)pv;
+      for (int v = 0; v < 16; ++v) pb[kb * 2 + (v >> 3)][v & 7] = (__bf16)fast_exp2(__builtin_fmaf(sacc[kb][v], sl2, neg_m));
+    // row sum of the bf16 probabilities the PV product uses, two per v_dot2
+    const b2 one = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+    for (int c2 = 0; c2 < 2 * KB; ++c2)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const b2 pr = {pb[c2][e], pb[c2][e + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one, l_run, false);
       }
-    l_run += lsum;
     apply_scale();
 #pragma unroll
-    for (int c2 = 0; c2 < 4; ++c2) {
+    for (int c2 = 0; c2 < 2 * KB; ++c2) {
       bf16x8 a[4];
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4) {
         const int d = d4 * 32 + l32;
-        a[d4] = *(const bf16x8*)&vl[d * BN + (((2 * c2 + hf) ^ ((d >> 1) & 7)) * 8)];
+        a[d4] = *(const bf16x8*)&vl[d * BN + (((2 * c2 + hf) ^ ((d >> 1) & (CH - 1))) * 8)];
       }
 #pragma unroll
       for (int d4 = 0; d4 < 4; ++d4) oacc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4], pb[c2], oacc[d4], 0, 0, 0);
     }
   };
 
+  // Iteration j loads tile j+NBUF-1 into the buffer tile j-1 used and runs
+  // tile j.  The two buffers go through distinct restrict pointers, so the
+  // compiler knows the loads cannot alias this tile's LDS reads.
   for (int kt_ = 0; kt_ < nkt; ++kt_) {
-    const int buf = kt_ & 1;
-    if (kt_ + 1 < nkt) dma(kt_ + 1, buf ^ 1);
-    if (kt_ < n_free) tile(buf, kt_ * BN, std::false_type{});
-    else tile(buf, kt_ * BN, std::true_type{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    auto step = [&](const Tile* __restrict__ cur, Tile* __restrict__ dst) __attribute__((always_inline)) {
+      if (kt_ + NBUF - 1 < nkt) dma(dst, kt_ + NBUF - 1);
+      if (kt_ < n_free) tile(cur, kt_ * BN, std::false_type{});
+      else tile(cur, kt_ * BN, std::true_type{});
+    };
+    step(&sm.ring[kt_ % NBUF], &sm.ring[(kt_ + NBUF - 1) % NBUF]);
+    if (kt_ + 1 < nkt) wait_tiles(min(nkt, kt_ + NBUF) - (kt_ + 2));  // tile kt_+1 has landed
+    __syncthreads();                                                    // every wave is done with tile kt_
   }
 
   // ---- branch: keys/values of passes 2..p at the same row, folded into (m, l, O)
@@ -318,7 +347,7 @@ __global__ void __launch_bounds__(256, 2)
         part = __builtin_amdgcn_fdot2(a, bq, part, false);
       }
     }
-    const float s2 = (part + __shfl_xor(part, 32, 64)) * sl2;
+    const float s2 = xhalf_sum(part) * sl2;
     raise_max(s2);
     apply_scale();
     const float pe = fast_exp2(s2 - m_run);
@@ -338,7 +367,7 @@ __global__ void __launch_bounds__(256, 2)
   }
 
   // ---- epilogue: O / l, LSE
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = xhalf_sum(l_run);
   const float inv_l = 1.f / l_tot;
   const int orow = wv * 32 + l32;  // LDS row: (wave, lane row)
 #pragma unroll
