@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -224,12 +225,66 @@ void trace(const char* name, int phase, hipStream_t st) {
 }  // namespace ttt
 
 // Runs one launcher between the two trace callbacks.
-#define TTT_TRACED(name, call) \
-  do {                         \
-    ttt::trace(name, 0, st);   \
-    call;                      \
-    ttt::trace(name, 1, st);   \
+#define TTT_TRACED(name, call) TTT_TRACED_ON(name, st, call)
+#define TTT_TRACED_ON(name, stream_, call) \
+  do {                                      \
+    ttt::trace(name, 0, stream_);           \
+    call;                                   \
+    ttt::trace(name, 1, stream_);           \
   } while (0)
+
+namespace {
+// One non-blocking side stream per device (default priority), created on first
+// use and kept for the life of the process.  The bf16 backward forks the
+// HBM-bound branch-gradient kernel onto it so that it runs beside the
+// MFMA-bound dK/dV kernel, and joins it back into the caller's stream.
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+hipStream_t g_side[kMaxDevices];
+
+hipStream_t side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  if (!g_side[dev]) {
+    hipStream_t s = nullptr;
+    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_side[dev] = s;
+  }
+  return g_side[dev];
+}
+
+// Fork: `side` waits for everything enqueued on `st` so far.  Join: `st` waits
+// for everything enqueued on `side` since.  The events are released once they
+// complete.  Returns false (nothing forked) if any step fails.
+struct Fork {
+  hipStream_t side = nullptr;
+  hipEvent_t join = nullptr;
+  bool begin(hipStream_t st) {
+    side = side_stream();
+    if (!side) return false;
+    hipEvent_t fork = nullptr;
+    if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return fail();
+    const bool ok = hipEventRecord(fork, st) == hipSuccess && hipStreamWaitEvent(side, fork, 0) == hipSuccess;
+    (void)hipEventDestroy(fork);
+    if (!ok || hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) return fail();
+    return true;
+  }
+  void end(hipStream_t st) {
+    if (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(st, join, 0) != hipSuccess)
+      (void)hipStreamSynchronize(side);  // the join must hold even if the event path failed
+    (void)hipEventDestroy(join);
+  }
+  bool fail() {
+    (void)hipGetLastError();
+    side = nullptr;
+    return false;
+  }
+};
+}  // namespace
 
 extern "C" {
 
@@ -398,13 +453,21 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
                                                 sinT, kt, ktt, st));
     TTT_TRACED("prep_q", ttt::launch_prep_rot_h(P, (const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, cosT,
                                                 sinT, qt, nullptr, st));
+    // The branch gradients (HBM-bound, few registers, no LDS) go first, on the
+    // side stream when one is available, so that they run beside the dK/dV
+    // kernel (one MFMA wave per SIMD leaves room for one more wave).
+    Fork fork;
+    const bool forked = P.p > 1 && fork.begin(st);
+    const hipStream_t bst = forked ? fork.side : st;
+    if (P.p > 1)
+      TTT_TRACED_ON("branch_bwd", bst,
+                    ttt::launch_branch_bwd_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, delta, cosT,
+                                                sinT, g, bst));
     TTT_TRACED("trunk_dkdv", ttt::launch_dkdv_bf16(P, kv, lse, (const uint16_t*)dout, kt, qt, delta, tkv, cosT,
                                                    sinT, g, st));
     TTT_TRACED("trunk_dq", ttt::launch_dq_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, kt, ktt, qt,
                                                delta, tq, cosT, sinT, (uint16_t*)dq, st));
-    if (P.p > 1)
-      TTT_TRACED("branch_bwd", ttt::launch_branch_bwd_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout,
-                                                           delta, cosT, sinT, g, st));
+    if (forked) fork.end(st);
   }
   return hip_check("ttt_attn_bwd launch");
 }

@@ -199,14 +199,17 @@ def main():
     events = []
     cur_pass = [0]
 
+    cur = torch.cuda.current_stream()
+
     def hook(name, phase, stream):
+        # record on the stream the library launches this kernel on (it may be
+        # the library's side stream rather than the caller's)
+        s = cur if not stream or stream == cur.cuda_stream else torch.cuda.ExternalStream(stream)
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(s)
         if phase == 0:
-            ev = torch.cuda.Event(enable_timing=True)
-            ev.record(torch.cuda.current_stream())
             events.append([name, cur_pass[0], ev, None])
         else:
-            ev = torch.cuda.Event(enable_timing=True)
-            ev.record(torch.cuda.current_stream())
             events[-1][3] = ev
 
     if not args.no_kernel_times:
