@@ -403,46 +403,55 @@ __global__ void __launch_bounds__(256, 1)
   const int prow = perm_row(l32);
   const float sl2 = P.scale_log2;
 
-  // Steps: row block nq-1-st/r (from the sequence end downwards) of head st%r.
+  // Steps st = 0..nsteps-1: head st % r of row block nq-1-st/r (from the
+  // sequence end downwards).  The loads run three steps ahead of the compute;
+  // both sides advance (head, row block) counters instead of dividing.
   const int nq = (L - kv0 + BQ - 1) / BQ;
   const int nsteps = P.r * nq;
-  auto step_q0 = [&](int st) { return kv0 + (nq - 1 - st / P.r) * BQ; };
   // DMA lane roles (wave w issues instructions j = 2w, 2w+1 of each 8 KB tile):
-  // rows r = 4j + lane/16, slot lane%16.
-  uint32_t roff[2];
+  // rows r = 4j + lane/16, slot lane%16.  Sources at head 0 of the group, row 0.
   int rrow[2];
+  const _Float16* q_src[2];
+  const uint16_t* g_src[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int j = 2 * wv + i;
     const int r = 4 * j + (lane >> 4);
+    const int roff = ((lane & 15) ^ (r & 15)) * 8;
     rrow[i] = r;
-    roff[i] = (uint32_t)(((lane & 15) ^ (r & 15)) * 8);
+    q_src[i] = qt + ((int64_t)(b * P.Hq + g * P.r) * P.spad + slot0 + r) * D + roff;
+    g_src[i] = dout + b * P.os_b + (int64_t)(start + r) * P.os_t + (int64_t)(g * P.r) * P.os_h + roff;
   }
   // dO rows past the sequence end are read from an all-zero workspace row (the
   // last slot of the first Q~ slab never holds a token), so they add nothing.
   const uint16_t* zrow = (const uint16_t*)(qt + (int64_t)(P.spad - 1) * D);
-  // LSE / Delta: waves 0,1 load LSE rows 16w..16w+15, waves 2,3 Delta rows 16(w-2)..
-  const int mrow = (wv & 1) * 16 + (lane & 15);
-  auto issue = [&](KvBuf* __restrict__ Bd, int st) __attribute__((always_inline)) {
+  // LSE and Delta of a step's 32 rows: one dword load by wave 0, lanes 0..31
+  // LSE, lanes 32..63 Delta (they land in lse[] and the dl[] that follows it).
+  const bool m_lse = lane < 32;
+  const float* m_src = m_lse ? lse + b * P.lse_b + (int64_t)(g * P.r) * P.lse_h + start
+                             : delta + (int64_t)(b * P.Hq + g * P.r) * P.spad + slot0;
+  const int64_t m_hstride = m_lse ? P.lse_h : (int64_t)P.spad;
+  const int m_row = lane & 31, m_last = m_lse ? L - 1 : L;
+  int is_h = 0, is_q0 = kv0 + (nq - 1) * BQ;  // the next step to load
+  auto issue = [&](KvBuf* __restrict__ Bd) __attribute__((always_inline)) {
     KvBuf& B = *Bd;
-    const int hh = st % P.r, q0 = step_q0(st);
-    const int h = g * P.r + hh;
-    const _Float16* qb = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0 + q0) * D;
-    const uint16_t* gb = dout + b * P.os_b + (int64_t)start * P.os_t + h * P.os_h;
+    const int64_t qoff = ((int64_t)is_h * P.spad + is_q0) * D;
+    const int64_t goff = (int64_t)is_h * P.os_h + (int64_t)is_q0 * P.os_t;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = 2 * wv + i;
-      const int rg = q0 + rrow[i];
-      const uint16_t* gsrc = rg < L ? gb + (int64_t)rg * P.os_t : zrow;
-      lds_dma16(qb + rrow[i] * D + roff[i], &B.q[4 * j * D]);
-      lds_dma16(gsrc + roff[i], &B.g[4 * j * D]);
+      const uint16_t* gsrc = is_q0 + rrow[i] < L ? g_src[i] + goff : zrow + 8 * (lane & 15);
+      lds_dma16(q_src[i] + qoff, &B.q[4 * j * D]);
+      lds_dma16(gsrc, &B.g[4 * j * D]);
     }
-    if (lane < 16) {
-      const int rr = q0 + mrow;
-      if (wv < 2) lds_dma4(lse + b * P.lse_b + h * P.lse_h + start + min(rr, L - 1), &B.lse[(wv & 1) * 16]);
-      else lds_dma4(delta + (int64_t)(b * P.Hq + h) * P.spad + slot0 + min(rr, L), &B.dl[(wv & 1) * 16]);
+    if (wv == 0) lds_dma4(m_src + is_h * m_hstride + min(is_q0 + m_row, m_last), &B.lse[0]);
+    if (++is_h == P.r) {
+      is_h = 0;
+      is_q0 -= BQ;
     }
   };
+  // loads each wave has in flight per step (wave 0 also loads LSE/Delta)
+  const bool w0 = wv == 0;
 
   // S = Q~ K~^T and dP = dO V^T for step st (this wave's 32 keys x 32 rows).
   auto products = [&](const KvBuf* __restrict__ Bp, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
@@ -469,9 +478,13 @@ __global__ void __launch_bounds__(256, 1)
   // prologue: steps 0..2 in flight, steps 0 and 1 landed
 #pragma unroll
   for (int st = 0; st < 3; ++st)
-    if (st < nsteps) issue(&sm[st], st);
-  if (nsteps >= 3) TTT_WAIT_VMCNT(5);  // leaves only step 2's loads outstanding
-  else TTT_WAIT_VMCNT(0);
+    if (st < nsteps) issue(&sm[st]);
+  if (nsteps >= 3) {  // leaves only step 2's loads outstanding
+    if (w0) TTT_WAIT_VMCNT(5);
+    else TTT_WAIT_VMCNT(4);
+  } else {
+    TTT_WAIT_VMCNT(0);
+  }
   __syncthreads();
   f32x16 s_c, dp_c;
   products(&sm[0], s_c, dp_c);
@@ -482,12 +495,13 @@ __global__ void __launch_bounds__(256, 1)
   // The three ring buffers an iteration touches go through distinct restrict
   // pointers: the compiler then knows the loads into the step-(st+3) buffer
   // cannot alias this iteration's LDS reads and puts no wait on them.
+  int cs_h = 0, cs_q0 = kv0 + (nq - 1) * BQ;  // the step being computed
   for (int st = 0; st < nsteps; ++st) {
    auto step = [&](const KvBuf* __restrict__ Bcp, const KvBuf* __restrict__ Bnp, KvBuf* __restrict__ Bdp)
                    __attribute__((always_inline)) {
-    if (st + 3 < nsteps) issue(Bdp, st + 3);
+    if (st + 3 < nsteps) issue(Bdp);
     const KvBuf& Bc = *Bcp;
-    const int q0 = step_q0(st);
+    const int q0 = cs_q0;
     // S/dP products of step st+1 (stale data past the last step is computed and
     // ignored) interleaved with the softmax of step st (S, dP from the previous
     // iteration): the matrix pipe runs while the vector ALUs do the softmax.
@@ -542,9 +556,17 @@ __global__ void __launch_bounds__(256, 1)
     }
    };
     step(&sm[st % NBUF], &sm[(st + 1) % NBUF], &sm[(st + 3) % NBUF]);
+    if (++cs_h == P.r) {
+      cs_h = 0;
+      cs_q0 -= BQ;
+    }
     // step st+2 must have landed before the next iteration reads it
-    if (st + 3 < nsteps) TTT_WAIT_VMCNT(5);
-    else TTT_WAIT_VMCNT(0);
+    if (st + 3 < nsteps) {
+      if (w0) TTT_WAIT_VMCNT(5);
+      else TTT_WAIT_VMCNT(4);
+    } else {
+      TTT_WAIT_VMCNT(0);
+    }
     __syncthreads();
   }
   if (!key_ok) return;
