@@ -257,31 +257,39 @@ hipStream_t side_stream() {
   return g_side[dev];
 }
 
-// Fork: `side` waits for everything enqueued on `st` so far.  Join: `st` waits
-// for everything enqueued on `side` since.  The events are released once they
-// complete.  Returns false (nothing forked) if any step fails.
-struct Fork {
+// Work on the side stream, ordered against the caller's stream with events:
+// mark(s) records an event at the current end of stream s, wait(w, e) makes
+// later work on stream w wait for it.  The events are released once they
+// complete.  If an event step fails, the side stream is drained from the host
+// so that the ordering still holds.
+struct Side {
   hipStream_t side = nullptr;
-  hipEvent_t join = nullptr;
-  bool begin(hipStream_t st) {
+  hipEvent_t ev[4] = {};
+  int nev = 0;
+  bool begin(hipStream_t st) {  // the side stream starts after the work on st so far
     side = side_stream();
     if (!side) return false;
-    hipEvent_t fork = nullptr;
-    if (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess) return fail();
-    const bool ok = hipEventRecord(fork, st) == hipSuccess && hipStreamWaitEvent(side, fork, 0) == hipSuccess;
-    (void)hipEventDestroy(fork);
-    if (!ok || hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess) return fail();
+    if (!wait(side, mark(st))) {
+      side = nullptr;
+      return false;
+    }
     return true;
   }
-  void end(hipStream_t st) {
-    if (hipEventRecord(join, side) != hipSuccess || hipStreamWaitEvent(st, join, 0) != hipSuccess)
-      (void)hipStreamSynchronize(side);  // the join must hold even if the event path failed
-    (void)hipEventDestroy(join);
+  hipEvent_t mark(hipStream_t s) {
+    hipEvent_t e = nullptr;
+    if (nev == 4 || hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+    ev[nev++] = e;
+    if (hipEventRecord(e, s) != hipSuccess) return nullptr;
+    return e;
   }
-  bool fail() {
+  bool wait(hipStream_t waiter, hipEvent_t e) {
+    if (e && hipStreamWaitEvent(waiter, e, 0) == hipSuccess) return true;
     (void)hipGetLastError();
-    side = nullptr;
+    if (side) (void)hipStreamSynchronize(side);
     return false;
+  }
+  ~Side() {
+    for (int i = 0; i < nev; ++i) (void)hipEventDestroy(ev[i]);
   }
 };
 }  // namespace
@@ -367,10 +375,16 @@ int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
     }
     _Float16* kt = at<_Float16>(ws, pl.ws.kt);
     uint16_t* vt = at<uint16_t>(ws, pl.ws.vt);
+    // V^T (side stream when available) beside the rotated K~ (caller's stream)
+    Side sd;
+    const bool forked = sd.begin(st);
+    const hipStream_t vst = forked ? sd.side : st;
+    TTT_TRACED_ON("prep_vt", vst,
+                  ttt::launch_prep_transpose_bf(P, (const uint16_t*)v[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, vt, vst));
+    const hipEvent_t vt_done = forked ? sd.mark(sd.side) : nullptr;
     TTT_TRACED("prep_k", ttt::launch_prep_rot_h(P, (const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT,
                                                 sinT, kt, nullptr, st));
-    TTT_TRACED("prep_vt",
-               ttt::launch_prep_transpose_bf(P, (const uint16_t*)v[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, vt, st));
+    if (forked) sd.wait(st, vt_done);
     TTT_TRACED("trunk_fwd",
                ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st));
   }
@@ -436,7 +450,15 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
       TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, 64, 1, nullptr, 0, slots, st));
     }
   }
-  TTT_TRACED("bwd_delta", ttt::launch_delta(P, o, pl.o_f32, dout, !pl.bf16, delta, st));
+  // bf16: Delta and then the branch gradients (HBM-bound, few registers, no
+  // LDS) run on the side stream when one is available: Delta beside the
+  // Q~/K~ rotations, the branch kernel beside the dK/dV kernel (one MFMA wave
+  // per SIMD leaves room for one more wave).
+  Side sd;
+  const bool forked = pl.bf16 && sd.begin(st);
+  const hipStream_t sst = forked ? sd.side : st;
+  TTT_TRACED_ON("bwd_delta", sst, ttt::launch_delta(P, o, pl.o_f32, dout, !pl.bf16, delta, sst));
+  const hipEvent_t delta_done = forked ? sd.mark(sd.side) : nullptr;
   if (!pl.bf16) {
     float* kt = at<float>(ws, pl.ws.kt);
     float* qt = at<float>(ws, pl.ws.qt);
@@ -453,21 +475,17 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
                                                 sinT, kt, ktt, st));
     TTT_TRACED("prep_q", ttt::launch_prep_rot_h(P, (const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, cosT,
                                                 sinT, qt, nullptr, st));
-    // The branch gradients (HBM-bound, few registers, no LDS) go first, on the
-    // side stream when one is available, so that they run beside the dK/dV
-    // kernel (one MFMA wave per SIMD leaves room for one more wave).
-    Fork fork;
-    const bool forked = P.p > 1 && fork.begin(st);
-    const hipStream_t bst = forked ? fork.side : st;
+    if (forked) sd.wait(st, delta_done);
+    if (forked && P.p > 1) sd.wait(sd.side, sd.mark(st));  // start the branch kernel with dK/dV, not beside the prologue
     if (P.p > 1)
-      TTT_TRACED_ON("branch_bwd", bst,
+      TTT_TRACED_ON("branch_bwd", sst,
                     ttt::launch_branch_bwd_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, delta, cosT,
-                                                sinT, g, bst));
+                                                sinT, g, sst));
     TTT_TRACED("trunk_dkdv", ttt::launch_dkdv_bf16(P, kv, lse, (const uint16_t*)dout, kt, qt, delta, tkv, cosT,
                                                    sinT, g, st));
     TTT_TRACED("trunk_dq", ttt::launch_dq_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, kt, ktt, qt,
                                                delta, tq, cosT, sinT, (uint16_t*)dq, st));
-    if (forked) fork.end(st);
+    if (forked && P.p > 1) sd.wait(st, sd.mark(sd.side));  // the branch gradients are in
   }
   return hip_check("ttt_attn_bwd launch");
 }
