@@ -54,6 +54,18 @@ class Desc(ctypes.Structure):
     ]
 
 
+class Chunk(ctypes.Structure):
+    """One ring step: query rows at q_offset.., pass-1 keys at kv_offset.. (ttt_attn_chunk)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("with_branch", ctypes.c_int32),
+        ("q_offset", ctypes.c_int64),
+        ("kv_offset", ctypes.c_int64),
+        ("kv_len", ctypes.c_int64),
+        ("kv0_stride", ctypes.c_int64 * 3),
+    ]
+
+
 # void (*)(void* user, const char* kernel, int phase, void* stream)
 TRACE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int, ctypes.c_void_p)
 _trace_ref = None
@@ -99,6 +111,13 @@ def library() -> ctypes.CDLL:
         lib.ttt_attn_bwd.argtypes = [ctypes.POINTER(Desc), vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp,
                                      ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
         lib.ttt_attn_bwd.restype = ctypes.c_int
+        lib.ttt_attn_chunk_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Chunk)]
+        lib.ttt_attn_chunk_workspace_bytes.restype = sz
+        lib.ttt_attn_fwd_chunk.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Chunk), vp, ctypes.POINTER(vp),
+                                           ctypes.POINTER(vp), vp, vp, vp, sz, vp]
+        lib.ttt_attn_fwd_chunk.restype = ctypes.c_int
+        lib.ttt_attn_merge.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp]
+        lib.ttt_attn_merge.restype = ctypes.c_int
         lib.ttt_attn_status_string.argtypes = [ctypes.c_int]
         lib.ttt_attn_status_string.restype = ctypes.c_char_p
         lib.ttt_attn_last_error.argtypes = []
@@ -250,3 +269,79 @@ def bwd(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, cu_seqlens=None,
                                   lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), _ptrs(dks[:p]), _ptrs(dvs[:p]),
                                   wp, wn, _stream(stream)))
     return dq, dks, dvs
+
+
+def make_chunk(q_offset: int, kv_offset: int, k0, *, with_branch: bool) -> Chunk:
+    c = Chunk()
+    c.struct_size = ctypes.sizeof(Chunk)
+    c.with_branch = int(bool(with_branch))
+    c.q_offset, c.kv_offset = int(q_offset), int(kv_offset)
+    c.kv_len = k0.shape[1]
+    c.kv0_stride[:] = _strides3(k0, False)
+    return c
+
+
+def fwd_chunk(q, ks: Sequence, vs: Sequence, p: int, *, q_offset: int, kv_offset: int, with_branch: bool,
+              softmax_scale: float = 0.0, rope_base: float = 0.0, o_fp32: bool = True, out=None, lse=None,
+              workspace=None, stream=None):
+    """One ring step (BSHD, bf16): the rows of q (positions q_offset..) against the pass-1 keys ks[0], vs[0]
+    (positions kv_offset..), plus the branch keys ks[1:p], vs[1:p] of those rows when with_branch.
+    Returns (o, lse) normalised over the keys this step sees (rows that see none: o = 0, lse = -inf)."""
+    torch = _torch()
+    o_dtype = DTYPE_FP32 if o_fp32 else _dtype_code(q)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if o_dtype == DTYPE_FP32 else q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    branch_ks = list(ks[1:p]) if with_branch else []
+    d = make_desc(q, (branch_ks or [ks[0]]), p, softmax_scale=softmax_scale, rope_base=rope_base, o_dtype=o_dtype,
+                  o_like=out)
+    if branch_ks and any(t.stride() != branch_ks[0].stride() for t in branch_ks + list(vs[1:p])):
+        raise ValueError("every branch k and v must share one set of strides")
+    if vs[0].stride() != ks[0].stride():
+        raise ValueError("k[0] and v[0] must share one set of strides")
+    c = make_chunk(q_offset, kv_offset, ks[0], with_branch=with_branch)
+    nbytes = int(library().ttt_attn_chunk_workspace_bytes(ctypes.byref(d), ctypes.byref(c)))
+    if nbytes == 0:
+        raise TTTAttnError(2, library().ttt_attn_last_error().decode())
+    ws = _workspace(nbytes, q.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    n = p if with_branch else 1
+    _check(library().ttt_attn_fwd_chunk(ctypes.byref(d), ctypes.byref(c), q.data_ptr(), _ptrs(ks[:n]),
+                                        _ptrs(vs[:n]), out.data_ptr(), lse.data_ptr(), wp, wn, _stream(stream)))
+    return out, lse
+
+
+def merge(o_a, lse_a, o_b, lse_b, *, out=None, lse=None, cu_seqlens=None, stream=None):
+    """Joint-LSE merge of two partial results over disjoint key sets of the same rows.
+    out/lse may be o_a/lse_a (in-place accumulation).  Returns (o, lse)."""
+    torch = _torch()
+    if o_a.shape != o_b.shape or o_a.dtype != o_b.dtype or o_a.stride() != o_b.stride():
+        raise ValueError("o_a and o_b must match in shape, dtype and strides")
+    if out is None:
+        out = torch.empty_strided(o_a.shape, o_a.stride(), dtype=o_a.dtype, device=o_a.device)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    if out.stride() != o_a.stride():
+        raise ValueError("out must have the strides of o_a")
+    thd = cu_seqlens is not None
+    d = Desc()
+    d.struct_size = ctypes.sizeof(Desc)
+    d.layout = LAYOUT_THD if thd else LAYOUT_BSHD
+    d.dtype = DTYPE_BF16 if o_a.dtype != torch.float32 else DTYPE_FP32
+    d.o_dtype = _dtype_code(o_a)
+    if thd:
+        d.batch, d.seqlen = 1, o_a.shape[0]
+        d.num_seqs = cu_seqlens.numel() - 1
+        d.cu_seqlens = cu_seqlens.data_ptr()
+    else:
+        d.batch, d.seqlen = o_a.shape[0], o_a.shape[1]
+    d.num_q_heads = d.num_kv_heads = o_a.shape[-2]
+    d.head_dim = o_a.shape[-1]
+    d.pass_index = 1
+    d.q_stride[:] = _strides3(o_a, thd) if o_a.dtype != torch.float32 or d.dtype == DTYPE_FP32 else (0, 0, 0)
+    d.kv_stride[:] = (0, 0, 0)
+    d.o_stride[:] = _strides3(o_a, thd)
+    _check(library().ttt_attn_merge(ctypes.byref(d), o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(),
+                                    lse_b.data_ptr(), out.data_ptr(), lse.data_ptr(), _stream(stream)))
+    return out, lse

@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(256, 2)
   {
     const bool valid = my_row < L;
     const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + my_row) * P.qs_t + h * P.qs_h;
-    const int pos = my_row + P.p - 1;
+    const int pos = P.q_off + my_row + P.p - 1;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int d0 = c * 16 + hf * 8;
@@ -147,8 +147,14 @@ __global__ void __launch_bounds__(256, 2)
   }
 
   // ---- trunk main loop
+  // Pass-1 key j (position kv_off + j, j < kv_len) is visible to row i
+  // (position q_off + i) iff j <= i + dq_ and j < kv_len; for whole-sequence
+  // calls dq_ = 0 and kv_len = L.
+  const int dq_ = P.layout == 0 ? P.q_off - P.kv_off : 0;
+  const int kv_len = P.layout == 0 ? P.kv_len : L;
   const int qend = min(row0 + RT, L);
-  const int nkt = (qend + BN - 1) / BN;
+  const int kmax = min(qend - 1 + dq_, kv_len - 1);  // last key any row of the work item sees
+  const int nkt = kmax < 0 ? 0 : kmax / BN + 1;
   const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
   const uint16_t* vbase = vt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
   // DMA lane roles, loads n = w*KL + i.  K~: 1 KB = rows 4n + lane/16, slot
@@ -200,7 +206,7 @@ __global__ void __launch_bounds__(256, 2)
   const int prow = perm_row(l32);
   const float sl2 = P.scale_log2;
   // Tiles whose every key precedes every row of this wave need no mask.
-  const int n_free = (wave_row0 + 1) / BN;
+  const int n_free = max(0, min(wave_row0 + 1 + dq_, kv_len)) / BN;
 
   // Moves the running max to mx when mx exceeds it by more than 8 (log2 units).
   auto raise_max = [&](float mx) {
@@ -248,7 +254,7 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = key0 + kb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
-          if (key > my_row) sacc[kb][v] = -INFINITY;
+          if (key > my_row + dq_ || key >= kv_len) sacc[kb][v] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -258,7 +264,7 @@ __global__ void __launch_bounds__(256, 2)
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
     mx = xhalf_max(mx) * sl2;
     raise_max(mx);
-    const float neg_m = -m_run;
+    const float neg_m = m_run == -INFINITY ? 0.f : -m_run;  // no key seen yet: every P is 0
     bf16x8 pb[2 * KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -303,7 +309,7 @@ __global__ void __launch_bounds__(256, 2)
 
   // ---- branch: keys/values of passes 2..p at the same row, folded into (m, l, O)
   const int lr = rbk * 32 + l32;  // this lane's row within the tile
-  for (int qq = 2; qq <= P.p; ++qq) {
+  for (int qq = 2; qq <= (P.branch ? P.p : 1); ++qq) {
     // stage R(i+q-1) k^(q) (fp16) and v^(q) (bf16) for the tile's rows: 8 threads per row
     for (int r0 = 0; r0 < RT; r0 += 32) {
       const int rr = r0 + (tid >> 3), c8 = tid & 7;
@@ -319,7 +325,7 @@ __global__ void __launch_bounds__(256, 2)
         unpack_bf8(*(const u32x4*)(krow + dhi), x2);
         vlo = *(const u32x4*)(vrow + dlo);
         vhi = *(const u32x4*)(vrow + dhi);
-        const int pk = i + qq - 1;
+        const int pk = P.q_off + i + qq - 1;
         const float* cp = cosT + (int64_t)pk * 64 + dlo;
         const float* sp = sinT + (int64_t)pk * 64 + dlo;
 #pragma unroll
@@ -368,7 +374,7 @@ __global__ void __launch_bounds__(256, 2)
 
   // ---- epilogue: O / l, LSE
   const float l_tot = xhalf_sum(l_run);
-  const float inv_l = 1.f / l_tot;
+  const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;  // a row that sees no key: O = 0, LSE = -inf
   const int orow = wv * 32 + l32;  // LDS row: (wave, lane row)
 #pragma unroll
   for (int d4 = 0; d4 < 4; ++d4)
@@ -379,7 +385,7 @@ __global__ void __launch_bounds__(256, 2)
       for (int e = 0; e < 4; ++e) w[e] = oacc[d4][v4 * 4 + e] * inv_l;
       *(f32x4*)&sm.o[orow][d4 * 32 + v4 * 8 + hf * 4] = w;
     }
-  if (hf == 0 && my_row < L) lse[b * P.lse_b + h * P.lse_h + start + my_row] = (m_run + fast_log2(l_tot)) * kLn2;
+  if (hf == 0 && my_row < L) lse[b * P.lse_b + h * P.lse_h + start + my_row] = (l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : -INFINITY);
   __syncthreads();
   // each wave stores its own 32 rows: 8 lanes per row, 16 elements per lane
   const int c8 = lane & 7;

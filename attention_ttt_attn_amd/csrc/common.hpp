@@ -39,6 +39,10 @@ struct Prob {
   int64_t ks_b, ks_t, ks_h;
   int64_t os_b, os_t, os_h;
   int64_t lse_b, lse_h;  // LSE element (b, h, tok) = b*lse_b + h*lse_h + tok
+  // Ring steps (BSHD forward): query row i sits at position q_off + i, pass-1
+  // key j at kv_off + j for j < kv_len; branch = 0 leaves passes 2..p out.
+  // Whole-sequence calls: q_off = kv_off = 0, kv_len = stok, branch = 1.
+  int q_off, kv_off, kv_len, branch;
 };
 
 // Passes' key/value pointers (up to 16), passed by value to kernels.

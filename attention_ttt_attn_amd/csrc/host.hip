@@ -37,12 +37,14 @@ struct Plan {
   bool bf16;
   bool o_f32;
   int max_tiles_q, max_tiles_kv;
+  int64_t k0s_b, k0s_t, k0s_h;  // strides of k[0] / v[0] (ring steps; = kv strides otherwise)
 };
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Validates the descriptor and fills the kernel view and workspace plan.
-int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl) {
+// Validates the descriptor (and the ring-step chunk, if any) and fills the
+// kernel view and workspace plan.
+int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chunk* c = nullptr) {
   if (!d) return fail(TTT_ERR_NULL_ARG, "descriptor is NULL");
   if (d->struct_size != sizeof(ttt_attn_desc))
     return fail(TTT_ERR_ABI, "struct_size %u != %zu (ABI version %d)", d->struct_size, sizeof(ttt_attn_desc),
@@ -100,6 +102,29 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl) {
   P.p = p;
   P.r = Hq / Hkv;
   P.npos = stok + p - 1;
+  P.q_off = 0;
+  P.kv_off = 0;
+  P.kv_len = stok;
+  P.branch = 1;
+  if (c) {
+    if (c->struct_size != sizeof(ttt_attn_chunk))
+      return fail(TTT_ERR_ABI, "chunk struct_size %u != %zu", c->struct_size, sizeof(ttt_attn_chunk));
+    if (d->layout != TTT_LAYOUT_BSHD) return fail(TTT_ERR_UNSUPPORTED, "ring steps take the BSHD layout");
+    if (d->dtype != TTT_DTYPE_BF16) return fail(TTT_ERR_UNSUPPORTED, "ring steps are built for bf16");
+    if (c->q_offset < 0 || c->kv_offset < 0 || c->kv_len < 0)
+      return fail(TTT_ERR_BAD_SHAPE, "q_offset %lld, kv_offset %lld and kv_len %lld must be >= 0",
+                  (long long)c->q_offset, (long long)c->kv_offset, (long long)c->kv_len);
+    if (c->q_offset + stok + p > ((int64_t)1 << 30) || c->kv_offset + c->kv_len > ((int64_t)1 << 30))
+      return fail(TTT_ERR_BAD_SHAPE, "positions past 2^30");
+    P.q_off = (int)c->q_offset;
+    P.kv_off = (int)c->kv_offset;
+    P.kv_len = (int)c->kv_len;
+    P.branch = c->with_branch != 0;
+    const int rows = stok > P.kv_len ? stok : P.kv_len;
+    P.spad = ((rows + 63) / 64) * 64 + 64;
+    const int64_t qend = c->q_offset + stok + p - 1, kend = c->kv_offset + c->kv_len;
+    P.npos = (int)(qend > kend ? qend : kend);
+  }
   P.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)D);
   P.scale_log2 = P.scale * ttt::kLog2e;
   const bool thd = d->layout == TTT_LAYOUT_THD;
@@ -126,6 +151,16 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl) {
   P.qs_b = tmp[0], P.qs_t = tmp[1], P.qs_h = tmp[2];
   if (int e = strides(d->kv_stride, Hkv, tmp, "kv", ea)) return e;
   P.ks_b = tmp[0], P.ks_t = tmp[1], P.ks_h = tmp[2];
+  pl.k0s_b = P.ks_b, pl.k0s_t = P.ks_t, pl.k0s_h = P.ks_h;
+  if (c) {
+    const int64_t* s0 = c->kv0_stride;
+    if (s0[0] == 0 && s0[1] == 0 && s0[2] == 0) {
+      pl.k0s_b = (int64_t)P.kv_len * Hkv * D, pl.k0s_t = (int64_t)Hkv * D, pl.k0s_h = D;
+    } else {
+      if (int e = strides(s0, Hkv, tmp, "kv0", ea)) return e;
+      pl.k0s_b = tmp[0], pl.k0s_t = tmp[1], pl.k0s_h = tmp[2];
+    }
+  }
   const bool o_f32 = d->o_dtype == TTT_DTYPE_FP32;
   if (int e = strides(d->o_stride, Hq, tmp, "o", (o_f32 && bf16) ? 8 : ea)) return e;
   P.os_b = tmp[0], P.os_t = tmp[1], P.os_h = tmp[2];
@@ -325,11 +360,15 @@ size_t ttt_attn_workspace_bytes(const ttt_attn_desc* d, int for_bwd) {
   return pl.ws.total;
 }
 
-int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, void* o,
-                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// Forward of a whole sequence (c = NULL) or of one ring step.
+int fwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, const void* const* k,
+             const void* const* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
   Plan pl;
-  if (int e = make_plan(d, 0, pl)) return e;
+  if (int e = make_plan(d, 0, pl, c)) return e;
   ttt::Prob& P = pl.P;
   if (P.stok == 0) return TTT_OK;  // nothing to compute; pointers of empty tensors may be NULL
   if (!k || !v) return fail(TTT_ERR_NULL_ARG, "k or v pointer array is NULL");
@@ -339,7 +378,10 @@ int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
   if ((uintptr_t)lse & 3u) return fail(TTT_ERR_MISALIGNED, "lse is not 4-byte aligned");
   ttt::PassPtrs kv;
   memset(&kv, 0, sizeof kv);
-  for (int i = 0; i < P.p; ++i) {
+  const int nptr = P.branch ? P.p : 1;  // a ring step without the branch reads pass 1 only
+  for (int i = 0; i < nptr; ++i) {
+    // an empty pass-1 key block (kv_len = 0) is never read: its pointers may be NULL
+    if (i == 0 && P.kv_len == 0 && !k[0] && !v[0]) continue;
     char nm[16];
     snprintf(nm, sizeof nm, "k[%d]", i);
     if (int e = check_ptr(k[i], nm)) return e;
@@ -375,20 +417,75 @@ int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
     }
     _Float16* kt = at<_Float16>(ws, pl.ws.kt);
     uint16_t* vt = at<uint16_t>(ws, pl.ws.vt);
+    // the pass-1 keys: kv_len rows (= the sequence for whole-sequence calls) at positions kv_off + j
+    ttt::Prob Pk = P;
+    if (P.layout == TTT_LAYOUT_BSHD) Pk.stok = P.kv_len;
     // V^T (side stream when available) beside the rotated K~ (caller's stream)
     Side sd;
     const bool forked = sd.begin(st);
     const hipStream_t vst = forked ? sd.side : st;
     TTT_TRACED_ON("prep_vt", vst,
-                  ttt::launch_prep_transpose_bf(P, (const uint16_t*)v[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, vt, vst));
+                  ttt::launch_prep_transpose_bf(Pk, (const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, vt,
+                                                vst));
     const hipEvent_t vt_done = forked ? sd.mark(sd.side) : nullptr;
-    TTT_TRACED("prep_k", ttt::launch_prep_rot_h(P, (const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT,
-                                                sinT, kt, nullptr, st));
+    TTT_TRACED("prep_k", ttt::launch_prep_rot_h(Pk, (const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv,
+                                                P.kv_off, cosT, sinT, kt, nullptr, st));
     if (forked) sd.wait(st, vt_done);
     TTT_TRACED("trunk_fwd",
                ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st));
   }
   return hip_check("ttt_attn_fwd launch");
+}
+}  // namespace
+
+extern "C" {
+
+int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, void* o,
+                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return fwd_impl(d, nullptr, q, k, v, o, lse, ws, ws_bytes, stream);
+}
+
+size_t ttt_attn_chunk_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_chunk* c) {
+  g_last_error.clear();
+  if (!c) {
+    fail(TTT_ERR_NULL_ARG, "chunk is NULL");
+    return 0;
+  }
+  Plan pl;
+  if (make_plan(d, 0, pl, c) != TTT_OK) return 0;
+  return pl.ws.total;
+}
+
+int ttt_attn_fwd_chunk(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, const void* const* k,
+                       const void* const* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!c) {
+    g_last_error.clear();
+    return fail(TTT_ERR_NULL_ARG, "chunk is NULL");
+  }
+  return fwd_impl(d, c, q, k, v, o, lse, ws, ws_bytes, stream);
+}
+
+int ttt_attn_merge(const ttt_attn_desc* d, const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                   void* o, float* lse, void* stream) {
+  g_last_error.clear();
+  Plan pl;
+  if (int e = make_plan(d, 0, pl)) return e;
+  ttt::Prob& P = pl.P;
+  if (P.stok == 0) return TTT_OK;
+  if (int e = check_ptr(o_a, "o_a")) return e;
+  if (int e = check_ptr(o_b, "o_b")) return e;
+  if (int e = check_ptr(o, "o")) return e;
+  const float* ls[3] = {lse_a, lse_b, lse};
+  const char* ln[3] = {"lse_a", "lse_b", "lse"};
+  for (int i = 0; i < 3; ++i) {
+    if (!ls[i]) return fail(TTT_ERR_NULL_ARG, "%s is NULL", ln[i]);
+    if ((uintptr_t)ls[i] & 3u) return fail(TTT_ERR_MISALIGNED, "%s is not 4-byte aligned", ln[i]);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (int e = check_cu(d, st)) return e;
+  (void)hipGetLastError();
+  TTT_TRACED("lse_merge", ttt::launch_merge(P, pl.o_f32, o_a, lse_a, o_b, lse_b, o, lse, st));
+  return hip_check("ttt_attn_merge launch");
 }
 
 int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, const void* o,

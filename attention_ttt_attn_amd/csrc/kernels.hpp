@@ -42,6 +42,10 @@ void launch_branch_bwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv
                             const uint16_t* dout, const float* delta, const float* cosT, const float* sinT,
                             const PassGradPtrs& g, hipStream_t st);
 
+// joint-LSE merge of two partial (O, LSE) over disjoint key sets (prep.hip)
+void launch_merge(const Prob& P, bool o_f32, const void* o_a, const float* lse_a, const void* o_b,
+                  const float* lse_b, void* o, float* lse, hipStream_t st);
+
 // launch trace hook (host.hip)
 void trace(const char* name, int phase, hipStream_t st);
 

@@ -297,6 +297,52 @@ void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bo
 #undef TTT_DELTA
 }
 
+// Joint-LSE merge of two partial results over disjoint key sets of the same
+// rows: LSE = ln(e^LSE_a + e^LSE_b), O = e^(LSE_a-LSE) O_a + e^(LSE_b-LSE) O_b
+// (NeMo-RL issue on EAGLE-3 TTT draft co-training, "What I'm working on",
+// items 1 and 4).  One thread per 8 elements of a row (a row's threads are in
+// one wave, so in-place merges read every input before any output is written).
+template <typename OT>
+__global__ void __launch_bounds__(256) merge_kernel(Prob P, const OT* oa, const float* la,
+                                                    const OT* ob, const float* lb, OT* o, float* l) {
+  const int cpr = P.D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / cpr;
+  const int c = (int)(gid % cpr);
+  if (row >= (int64_t)P.B * P.stok * P.Hq) return;
+  const int h = (int)(row % P.Hq);
+  const int64_t bt = row / P.Hq;
+  const int t = (int)(bt % P.stok), b = (int)(bt / P.stok);
+  const int64_t li = b * P.lse_b + h * P.lse_h + t;
+  const int64_t oi = b * P.os_b + (int64_t)t * P.os_t + h * P.os_h + c * 8;
+  const float A = la[li], Bv = lb[li];
+  const float m = fmaxf(A, Bv);
+  float wa = 0.f, wb = 0.f, L = -INFINITY;
+  if (m != -INFINITY) {
+    const float ea = expf(A - m), eb = expf(Bv - m), sum = ea + eb;
+    wa = ea / sum;
+    wb = eb / sum;
+    L = m + logf(sum);
+  }
+  float x[8], y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = ld<OT>(oa + oi + e), y[e] = ld<OT>(ob + oi + e);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st<OT>(o + oi + e, wa * x[e] + wb * y[e]);
+  if (c == 0) l[li] = L;
+}
+
+void launch_merge(const Prob& P, bool o_f32, const void* o_a, const float* lse_a, const void* o_b,
+                  const float* lse_b, void* o, float* lse, hipStream_t st) {
+  const int64_t threads = (int64_t)P.B * P.stok * P.Hq * (P.D / 8);
+  const unsigned grid = (unsigned)((threads + 255) / 256);
+  if (o_f32)
+    merge_kernel<float><<<grid, 256, 0, st>>>(P, (const float*)o_a, lse_a, (const float*)o_b, lse_b, (float*)o, lse);
+  else
+    merge_kernel<uint16_t><<<grid, 256, 0, st>>>(P, (const uint16_t*)o_a, lse_a, (const uint16_t*)o_b, lse_b,
+                                                 (uint16_t*)o, lse);
+}
+
 void launch_tile_sched(const Prob& P, int tile, int descending, int4* out, int max_entries, int* slot_base,
                        hipStream_t st) {
   tile_sched_kernel<<<1, 1024, 0, st>>>(P, tile, descending, out, max_entries, slot_base);

@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--ring", type=int, default=0, metavar="CP",
+                    help="instead of the unroll, time the ring-step forward of the last pass over a zig-zag ring "
+                         "of CP ranks emulated on this GPU, per chunk shape (prints its own JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy a 256 MiB buffer 3 times (a plain copy kernel of known size "
                          "that scales the HBM byte counters of a profiler run)")
@@ -147,6 +150,83 @@ def cpu_baseline(w, seconds: float):
 
 
 # ----------------------------------------------------------------------------- main
+def ring_main(args, w, dev):
+    """Ring-step forward of pass K over a zig-zag ring of cp ranks (chunks of S/(2 cp) rows),
+    emulated on one GPU: per chunk shape (diagonal step with the branch, full off-diagonal
+    step, merge) and the whole ring against one whole-sequence call."""
+    import torch
+
+    import attention_ttt_attn_amd as tk
+    import ttt_synth as syn
+
+    cp, K = args.ring, w.K
+    if w.layout != "bshd" or w.S % (2 * cp):
+        print(f"--ring needs a BSHD workload whose length divides into {2 * cp} chunks", file=sys.stderr)
+        sys.exit(2)
+    c = w.S // (2 * cp)
+    q = syn.draw_device(w, syn.KIND_Q, K, dev)
+    ks = [syn.draw_device(w, syn.KIND_K, t, dev) for t in range(1, K + 1)]
+    vs = [syn.draw_device(w, syn.KIND_V, t, dev) for t in range(1, K + 1)]
+    ws = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    o_a = torch.empty((w.B, c, w.Hq, w.D), dtype=torch.float32, device=dev)
+    l_a = torch.empty((w.B, w.Hq, c), dtype=torch.float32, device=dev)
+    o_b, l_b = torch.empty_like(o_a), torch.empty_like(l_a)
+    kw = dict(rope_base=w.rope_base, workspace=ws)
+
+    def step(qc, kc, out, lse):
+        qa, ka = qc * c, kc * c
+        sk = [ks[0][:, ka:ka + c]] + [k[:, qa:qa + c] for k in ks[1:K]]
+        sv = [vs[0][:, ka:ka + c]] + [v[:, qa:qa + c] for v in vs[1:K]]
+        tk.fwd_chunk(q[:, qa:qa + c], sk, sv, K, q_offset=qa, kv_offset=ka, with_branch=qc == kc, out=out,
+                     lse=lse, **kw)
+
+    def ring():
+        for r in range(cp):
+            for qc in (r, 2 * cp - 1 - r):
+                step(qc, 0, o_a, l_a)
+                for kc in range(1, qc + 1):
+                    step(qc, kc, o_b, l_b)
+                    tk.merge(o_a, l_a, o_b, l_b, out=o_a, lse=l_a)
+
+    o_s = torch.empty((w.B, w.S, w.Hq, w.D), dtype=torch.float32, device=dev)
+    l_s = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
+    single = lambda: tk.fwd(q, ks, vs, K, o_fp32=True, out=o_s, lse=l_s, **kw)
+    shapes = {
+        "diag_step": lambda: step(cp, cp, o_a, l_a),
+        "full_step": lambda: step(2 * cp - 1, 0, o_a, l_a),
+        "merge": lambda: tk.merge(o_a, l_a, o_b, l_b, out=o_a, lse=l_a),
+        "ring_total": ring,
+        "single_call": single,
+    }
+    n = max(args.steps, 1)
+    res = {}
+    for name, fn in shapes.items():
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"avg_us": round(e0.elapsed_time(e1) * 1e3 / n, 2)}
+    per_head = 4.0 * w.D * w.Hq * w.B
+    flops = {"diag_step": per_head * (c * (c + 1) // 2 + (K - 1) * c), "full_step": per_head * c * c,
+             "ring_total": useful_flops(w, K)[0], "single_call": useful_flops(w, K)[0]}
+    for name, f in flops.items():
+        res[name]["tflops"] = round(f / (res[name]["avg_us"] * 1e-6) / 1e12, 1)
+    res["merge"]["gbps"] = round(w.B * c * w.Hq * (w.D * 4 * 3 + 12) / (res["merge"]["avg_us"] * 1e-6) / 1e9, 1)
+    steps_per_ring = sum(qc + 1 for r in range(cp) for qc in (r, 2 * cp - 1 - r))
+    out = {"metric": "ring-step forward time per chunk shape", "value": res["ring_total"]["avg_us"], "unit": "us",
+           "higher_is_better": False, "n_gpus": 1, "steps": n, "warmup": args.warmup, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": w.name, "pass": K, "cp": cp, "chunk_rows": c, "ring_steps": steps_per_ring,
+                      "merges": steps_per_ring - 2 * cp, "o": "fp32 partials, fp32 merge"},
+           "shapes": res, "source_digest": source_digest()}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -167,6 +247,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     w = syn.workload(args.workload)
+    if args.ring:
+        ring_main(args, w, dev)
+        return
     K = w.K
     cu = torch.from_numpy(syn.cu_seqlens_of(w.lengths())).to(dev) if w.layout == "thd" else None
 

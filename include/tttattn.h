@@ -33,8 +33,11 @@
  *
  * Ownership and state: the caller owns every buffer, including the
  * workspace.  The library allocates no device memory and keeps no state
- * between calls; calls are asynchronous on `stream` (a hipStream_t; NULL is
- * the default stream) and re-entrant.  Outputs are overwritten, never
+ * between calls except one non-blocking side stream per device, created on
+ * first use and kept for the life of the process (work forked onto it is
+ * joined back into the caller's stream before a call returns, so the calls
+ * keep the caller's stream order).  Calls are asynchronous on `stream` (a
+ * hipStream_t; NULL is the default stream) and re-entrant.  Outputs are overwritten, never
  * accumulated: gradients of a key/value tensor used by several passes are
  * summed by the caller.  Two calls that share a workspace must be ordered on
  * one stream.
@@ -124,6 +127,51 @@ int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
 int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v,
                  const void* o, const float* lse, const void* dout, void* dq, void* const* dk,
                  void* const* dv, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Ring steps: the pass-1 trunk in chunks ---------------------------------
+ * NeMo-RL issue "DFlash/DSpark and EAGLE-3 TTT draft co-training for
+ * speculative decoding (Megatron backend)", "What I'm working on", item 4:
+ * under context parallelism the pass-1 trunk K/V of a sequence travels on a
+ * (zig-zag) ring and the partial results are joined by the exact joint-LSE
+ * merge.  One ring step is the attention of a chunk of query rows against a
+ * chunk of pass-1 keys, at their positions in the sequence:
+ *   query row i of q (i < d->seqlen) sits at position q_offset + i (RoPE
+ *   position q_offset + i + p - 1); pass-1 key j of k[0]/v[0] (j < kv_len) at
+ *   position kv_offset + j; key j is visible to row i iff
+ *   kv_offset + j <= q_offset + i.
+ *   with_branch != 0 also folds in the branch keys of passes 2..p, which k[q],
+ *   v[q] (q >= 1) hold for the query rows (d->seqlen rows, positions
+ *   q_offset + i + q); a sequence's ring folds them in exactly once.
+ * Output: O normalised over the keys this step sees and its LSE; a row that
+ * sees no key gets O = 0 and LSE = -inf.  BSHD and dtype bf16 only; every
+ * batch row uses the same offsets. */
+typedef struct ttt_attn_chunk {
+  uint32_t struct_size;       /* = sizeof(ttt_attn_chunk)                                  */
+  int32_t with_branch;        /* non-zero: fold in the branch keys of passes 2..p         */
+  int64_t q_offset;           /* position of query row 0 in the sequence                  */
+  int64_t kv_offset;          /* position of pass-1 key 0 in the sequence                 */
+  int64_t kv_len;             /* rows of k[0] / v[0]                                      */
+  int64_t kv0_stride[3];      /* batch, token, head strides of k[0] / v[0] (elements); a
+                                 zero triple selects the contiguous default [B, kv_len,
+                                 Hkv, D]; kv_stride applies to k[q], v[q], q >= 1          */
+} ttt_attn_chunk;
+
+/* Bytes of workspace ttt_attn_fwd_chunk needs (0 and the last error if invalid). */
+size_t ttt_attn_chunk_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_chunk* c);
+
+/* Forward of one ring step; arguments as ttt_attn_fwd, plus the chunk. */
+int ttt_attn_fwd_chunk(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, const void* const* k,
+                       const void* const* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Joint-LSE merge of two partial results over disjoint key sets of the same
+ * rows (same issue and item as above; the operator that also joins trunk and
+ * branch):  LSE = ln(e^LSE_a + e^LSE_b),  O = e^(LSE_a-LSE) O_a + e^(LSE_b-LSE) O_b;
+ * a row with LSE_a = LSE_b = -inf gets O = 0, LSE = -inf.  Shapes, strides and
+ * o_dtype from d (BSHD or THD; o_stride for every O, lse layout as in
+ * ttt_attn_fwd).  o/lse may alias o_a/lse_a or o_b/lse_b (in-place
+ * accumulation).  An fp32 o_dtype keeps a long ring exact to fp32 rounding. */
+int ttt_attn_merge(const ttt_attn_desc* d, const void* o_a, const float* lse_a, const void* o_b,
+                   const float* lse_b, void* o, float* lse, void* stream);
 
 /* Static text of a status code. */
 const char* ttt_attn_status_string(int status);

@@ -45,6 +45,15 @@ What is computed (one call = one TTT pass p, 1-based):
   Gradients are returned per tensor (dK(q), dV(q) for q = 1..p); nothing is
   accumulated across calls.
 
+* Ring steps (issue above, item 4: context parallelism, where pass-1 K/V
+  travel around a zig-zag ring and partial results are joined by the joint-LSE
+  merge): `fwd_chunk` is the attention of a block of query rows at sequence
+  positions q_offset.. against a block of pass-1 keys at positions kv_offset..
+  (visible iff key position <= query row position), optionally with the
+  branch keys of those rows; `merge` joins two partial results over disjoint
+  key sets: LSE = ln(e^LSE_a + e^LSE_b), O = e^(LSE_a - LSE) O_a +
+  e^(LSE_b - LSE) O_b.  A row that sees no key has O = 0 and LSE = -inf.
+
 Everything is fp64; inputs are upcast from whatever float type they hold.
 No blocking, fusion or reordering beyond evaluating rows in independent
 groups.
@@ -57,7 +66,8 @@ from typing import Iterable, Optional, Sequence
 import numpy as np
 
 __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_position",
-           "ttt_mask_row", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows", "Slice"]
+           "ttt_mask_row", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows", "Slice",
+           "fwd_chunk", "merge", "ring_visible"]
 
 
 # ----------------------------------------------------------------------------- RoPE
@@ -316,3 +326,74 @@ def bwd(q, ks, vs, dout, p: int, *, layout: str = "bshd", cu_seqlens=None,
                 dK[qq][_row_index(layout, sl, rows) + (g,)] = dk[qq * sl.L:(qq + 1) * sl.L]
                 dV[qq][_row_index(layout, sl, rows) + (g,)] = dv[qq * sl.L:(qq + 1) * sl.L]
     return dQ, dK, dV
+
+
+# ----------------------------------------------------------------------------- ring steps
+def ring_visible(q_pos, k_pos) -> np.ndarray:
+    """[n, m] causal visibility of pass-1 keys at sequence positions k_pos to the
+    query rows at sequence positions q_pos (a row sees its own position)."""
+    return np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]
+
+
+def fwd_chunk(q, k0, v0, branch_ks, branch_vs, p: int, *, q_offset: int, kv_offset: int,
+              scale: Optional[float] = None, base: float = 0.0):
+    """One ring step of pass p, BSHD.  q: [B, n, Hq, D] rows at sequence positions
+    q_offset + i; k0, v0: [B, m, Hkv, D] pass-1 keys at positions kv_offset + j;
+    branch_ks, branch_vs: None, or the p-1 tensors [B, n, Hkv, D] of passes 2..p
+    at the same rows.  Query row i is rotated to position q_offset + i + p - 1,
+    trunk key j to kv_offset + j, the pass-q branch key of row i to
+    q_offset + i + q - 1.  Returns (O [B, n, Hq, D], LSE [B, Hq, n]) in fp64,
+    normalised over the keys this step sees."""
+    B, n, Hq, D = q.shape
+    m, Hkv = k0.shape[1], k0.shape[2]
+    r = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    rows = np.arange(n)
+    qpos = q_offset + rows
+    O = np.zeros((B, n, Hq, D))
+    lse = np.full((B, Hq, n), -np.inf)
+    for b in range(B):
+        for g in range(Hkv):
+            kr = rotate_half(np.asarray(k0[b, :, g], np.float64), kv_offset + np.arange(m), base)   # [m, D]
+            vv = np.asarray(v0[b, :, g], np.float64)
+            vis = ring_visible(qpos, kv_offset + np.arange(m))                                     # [n, m]
+            bk, bv = [], []
+            if branch_ks is not None:
+                for t in range(2, p + 1):
+                    bk.append(rotate_half(np.asarray(branch_ks[t - 2][b, :, g], np.float64),
+                                          key_position(t, qpos), base))                          # [n, D]
+                    bv.append(np.asarray(branch_vs[t - 2][b, :, g], np.float64))
+            for h in range(g * r, (g + 1) * r):
+                qr = rotate_half(np.asarray(q[b, :, h], np.float64), query_position(qpos, p), base)
+                for i in range(n):
+                    s = [scale * (kr[vis[i]] @ qr[i])]
+                    vals = [vv[vis[i]]]
+                    for t in range(len(bk)):
+                        s.append(np.array([scale * (bk[t][i] @ qr[i])]))
+                        vals.append(bv[t][i][None, :])
+                    s = np.concatenate(s)
+                    if s.size == 0:
+                        continue                    # no visible key: O = 0, LSE = -inf
+                    mx = s.max()
+                    w = np.exp(s - mx)
+                    lse[b, h, i] = mx + math.log(w.sum())
+                    O[b, i, h] = (w / w.sum()) @ np.concatenate(vals, axis=0)
+    return O, lse
+
+
+def merge(o_a, lse_a, o_b, lse_b):
+    """Joint-LSE merge of two partial results over disjoint key sets of the same rows.
+    o_*: [B, n, H, D]; lse_*: [B, H, n].  Rows with both LSEs -inf get O = 0, LSE = -inf."""
+    la = np.asarray(lse_a, np.float64)
+    lb = np.asarray(lse_b, np.float64)
+    mx = np.maximum(la, lb)
+    empty = mx == -np.inf
+    mx_safe = np.where(empty, 0.0, mx)
+    ea, eb = np.exp(la - mx_safe), np.exp(lb - mx_safe)
+    tot = ea + eb
+    L = np.where(empty, -np.inf, mx_safe + np.log(np.where(empty, 1.0, tot)))
+    wa = np.where(empty, 0.0, ea / np.where(empty, 1.0, tot))
+    wb = np.where(empty, 0.0, eb / np.where(empty, 1.0, tot))
+    to_rows = lambda w: np.transpose(w, (0, 2, 1))[..., None]          # [B, H, n] -> [B, n, H, 1]
+    return to_rows(wa) * np.asarray(o_a, np.float64) + to_rows(wb) * np.asarray(o_b, np.float64), L

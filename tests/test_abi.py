@@ -187,3 +187,87 @@ def test_error_text_is_thread_local():
     th.start()
     th.join()
     assert seen["text"] == "" and "q is NULL" in err()
+
+
+# ----------------------------------------------------------------------------- ring steps and merge
+def good_chunk(q_offset=256, kv_offset=0, kv_len=300, with_branch=1):
+    c = tk.Chunk()
+    c.struct_size = ctypes.sizeof(tk.Chunk)
+    c.with_branch = with_branch
+    c.q_offset, c.kv_offset, c.kv_len = q_offset, kv_offset, kv_len
+    return c
+
+
+def call_chunk(d, c, q=FAKE, k=None, v=None, o=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    lib = tk.library()
+    k = ptrs(d.pass_index) if k is None else k
+    v = ptrs(d.pass_index) if v is None else v
+    return lib.ttt_attn_fwd_chunk(ctypes.byref(d), ctypes.byref(c) if c is not None else None, q, k, v, o, lse, ws,
+                                  ws_bytes, None)
+
+
+def test_chunk_struct_matches_header():
+    assert ctypes.sizeof(tk.Chunk) == 56
+    text = open(os.path.join(ROOT, "include", "tttattn.h")).read()
+    assert "ttt_attn_chunk" in text and "kv0_stride[3]" in text
+
+
+def test_chunk_validation():
+    lib = tk.library()
+    d = good_desc()
+    assert call_chunk(d, None) == 1 and "chunk" in err()
+    c = good_chunk()
+    c.struct_size = 8
+    assert call_chunk(d, c) == 7 and "struct_size" in err()
+    assert call_chunk(good_desc(layout=tk.LAYOUT_THD), good_chunk()) == 3 and "BSHD" in err()
+    assert call_chunk(good_desc(dtype=tk.DTYPE_FP32), good_chunk()) == 3 and "bf16" in err()
+    for q_off, kv_off, kv_len in ((-1, 0, 10), (0, -64, 10), (0, 0, -1)):
+        assert call_chunk(d, good_chunk(q_off, kv_off, kv_len)) == 2 and ">= 0" in err()
+    assert call_chunk(d, good_chunk(q_offset=(1 << 30) - 50)) == 2 and "2^30" in err()
+    assert call_chunk(d, good_chunk(kv_offset=1 << 30, kv_len=1)) == 2 and "2^30" in err()
+    c = good_chunk()
+    c.kv0_stride[:] = (300 * 2 * 128, 2 * 128, 100)     # head stride of 100 elements: not 16-byte aligned
+    assert call_chunk(d, c) == 4 and "kv0" in err()
+    assert lib.ttt_attn_chunk_workspace_bytes(ctypes.byref(d), None) == 0 and "chunk" in err()
+
+
+def test_chunk_pointer_checks_follow_branch_flag():
+    d = good_desc()                                    # p = 3
+    k = ptrs(3)
+    k[2] = None
+    assert call_chunk(d, good_chunk(with_branch=1), k=k) == 1 and "k[2]" in err()
+    k0 = ptrs(3)
+    k0[0] = None
+    assert call_chunk(d, good_chunk(with_branch=0), k=k0) == 1 and "k[0]" in err()
+    # without the branch only pass 1 is read: a NULL k[2] passes the pointer checks and
+    # the call stops at the (too small) workspace instead
+    assert call_chunk(d, good_chunk(with_branch=0), k=k, ws_bytes=16) == 5
+    assert call_chunk(d, good_chunk(), q=None) == 1 and "q is NULL" in err()
+    assert call_chunk(d, good_chunk(), lse=FAKE + 2) == 4
+
+
+def test_chunk_workspace_tracks_key_block():
+    lib = tk.library()
+    d = good_desc()
+    w = lambda c: lib.ttt_attn_chunk_workspace_bytes(ctypes.byref(d), ctypes.byref(c))
+    small, big = w(good_chunk(kv_len=64)), w(good_chunk(kv_len=4096))
+    assert 0 < small < big
+    assert call_chunk(d, good_chunk(kv_len=4096), ws_bytes=big - 1) == 5 and "smaller" in err()
+    # the RoPE table covers the furthest position of either block
+    assert w(good_chunk(q_offset=0, kv_offset=100000, kv_len=64)) > w(good_chunk(q_offset=0, kv_offset=0, kv_len=64))
+
+
+def test_merge_validation():
+    lib = tk.library()
+    d = good_desc()
+    d.o_dtype = tk.DTYPE_FP32
+    call = lambda oa=FAKE, la=FAKE, ob=FAKE, lb=FAKE, o=FAKE, l=FAKE, desc=d: lib.ttt_attn_merge(
+        ctypes.byref(desc), oa, la, ob, lb, o, l, None)
+    assert call(oa=None) == 1 and "o_a" in err()
+    assert call(ob=FAKE + 4) == 4 and "o_b" in err()
+    assert call(o=None) == 1
+    assert call(lb=None) == 1 and "lse_b" in err()
+    assert call(l=FAKE + 2) == 4 and "lse" in err()
+    bad = good_desc()
+    bad.num_q_heads = 0
+    assert call(desc=bad) == 2

@@ -317,11 +317,76 @@ def check_sampled_rows_match_full():
     assert np.max(np.abs(o - of[[0, 5, 11], 3])) < 1e-14 and np.max(np.abs(l - lf[3, [0, 5, 11]])) < 1e-14
 
 
+def _dense_bshd(q, ks, vs, p, scale, base):
+    """dense_reference for a B=1 BSHD batch, returned as (O [S, Hq, D], LSE [Hq, S]) numpy."""
+    o, l = dense_reference(torch.tensor(q[0]), [torch.tensor(k[0]) for k in ks], [torch.tensor(v[0]) for v in vs],
+                           p, scale, base)
+    return o.numpy(), l.numpy()
+
+
+def check_chunk_rows_match_dense():
+    """A ring step whose key block is the whole causal prefix (with the branch) gives
+    exactly the dense masked-softmax rows; row and key offsets shift positions only."""
+    S, Hq, Hkv, D, p, base, scale = 12, 4, 2, 8, 3, 1e4, 0.4
+    q, ks, vs, _ = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=71, B=1)
+    ro, rl = _dense_bshd(q, ks, vs, p, scale, base)
+    a, n = 5, 4                                  # rows 5..8 against keys 0..8
+    o, l = O.fwd_chunk(q[:, a:a + n], ks[0][:, :a + n], vs[0][:, :a + n], [k[:, a:a + n] for k in ks[1:]],
+                       [v[:, a:a + n] for v in vs[1:]], p, q_offset=a, kv_offset=0, scale=scale, base=base)
+    assert np.max(np.abs(o[0] - ro[a:a + n])) < 1e-12
+    assert np.max(np.abs(l[0] - rl[:, a:a + n])) < 1e-12
+
+
+def check_chunk_ring_partition():
+    """Zig-zag ring: split the sequence into 2c chunks, rank r owning query chunks r and
+    2c-1-r; merging every rank's steps over all key chunks (branch folded in once, on
+    the diagonal step) gives the dense result."""
+    S, Hq, Hkv, D, p, base, scale, cp = 16, 2, 1, 8, 4, 1e6, 0.35, 2
+    q, ks, vs, _ = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=73, B=1)
+    ro, rl = _dense_bshd(q, ks, vs, p, scale, base)
+    c = S // (2 * cp)
+    for r in range(cp):
+        for qc in (r, 2 * cp - 1 - r):
+            qa = qc * c
+            acc_o = np.zeros((1, c, Hq, D)); acc_l = np.full((1, Hq, c), -np.inf)
+            for kc in range(2 * cp):
+                ka = kc * c
+                br = kc == qc
+                o, l = O.fwd_chunk(q[:, qa:qa + c], ks[0][:, ka:ka + c], vs[0][:, ka:ka + c],
+                                   [k[:, qa:qa + c] for k in ks[1:]] if br else None,
+                                   [v[:, qa:qa + c] for v in vs[1:]] if br else None,
+                                   p, q_offset=qa, kv_offset=ka, scale=scale, base=base)
+                if kc > qc:
+                    assert np.all(l == -np.inf) and np.all(o == 0)
+                acc_o, acc_l = O.merge(acc_o, acc_l, o, l)
+            assert np.max(np.abs(acc_o[0] - ro[qa:qa + c])) < 1e-12
+            assert np.max(np.abs(acc_l[0] - rl[:, qa:qa + c])) < 1e-12
+
+
+def check_merge_closed_form():
+    """Two single-key partial results: merged O is the two-way softmax average of the
+    values and LSE is log(e^s1 + e^s2); -inf partners leave the other side unchanged."""
+    rng = np.random.default_rng(75)
+    s1, s2 = rng.standard_normal((1, 3, 5)), rng.standard_normal((1, 3, 5))
+    v1, v2 = rng.standard_normal((1, 5, 3, 4)), rng.standard_normal((1, 5, 3, 4))
+    o, l = O.merge(v1, s1, v2, s2)
+    w1 = 1.0 / (1.0 + np.exp(s2 - s1))
+    w1r = np.transpose(w1, (0, 2, 1))[..., None]
+    assert np.max(np.abs(o - (w1r * v1 + (1 - w1r) * v2))) < 1e-14
+    assert np.max(np.abs(l - np.log(np.exp(s1) + np.exp(s2)))) < 1e-14
+    ninf = np.full_like(s1, -np.inf)
+    o2, l2 = O.merge(v1, s1, np.zeros_like(v2), ninf)
+    assert np.array_equal(l2, s1) and np.max(np.abs(o2 - v1)) < 1e-15
+    o3, l3 = O.merge(np.zeros_like(v1), ninf, np.zeros_like(v2), ninf)
+    assert np.all(l3 == -np.inf) and np.all(o3 == 0)
+
+
 PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check_zero_query_closed_form,
         lambda: check_zero_query_closed_form("thd"), check_sdpa_brute_force, check_p1_is_causal_sdpa,
         check_merge_invariant, check_branch_relative_position, check_grad_autograd,
         check_grad_finite_difference, check_thd_equals_bshd, check_thd_isolation, check_gqa_is_repeated_kv,
-        check_sampled_rows_match_full]
+        check_sampled_rows_match_full, check_chunk_rows_match_dense, check_chunk_ring_partition,
+        check_merge_closed_form]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
@@ -365,6 +430,7 @@ _orig_qpos = O.query_position
 _orig_kpos = O.key_position
 _orig_inv = O.inv_freq
 _orig_blk = O._row_block_fwd
+_orig_merge = O.merge
 
 
 def _rot_sign(x, pos, base):
@@ -402,6 +468,10 @@ MISTAKES = [
     ("key_position", lambda q, j: np.asarray(j) + q),
     ("inv_freq", lambda D, base: np.power(np.float64(base), -1.0 * np.arange(D // 2) / D)),
     ("_row_block_fwd", _blk_transposed_v),
+    ("ring_visible", lambda qp, kp: np.asarray(kp)[None, :] < np.asarray(qp)[:, None]),
+    ("ring_visible", lambda qp, kp: np.asarray(kp)[None, :] <= np.asarray(qp)[:, None] + 1),
+    ("merge", lambda oa, la, ob, lb: _orig_merge(ob, la, oa, lb)),
+    ("merge", lambda oa, la, ob, lb: (_orig_merge(oa, la, ob, lb)[0], np.maximum(la, lb))),
 ]
 
 

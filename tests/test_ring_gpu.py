@@ -1,0 +1,192 @@
+"""Ring steps and the joint-LSE merge on the GPU (through the C ABI).
+
+A zig-zag context-parallel ring is emulated on one GPU: the sequence is split
+into 2*cp chunks, rank r owns query chunks r and 2*cp-1-r, and each query chunk
+meets every pass-1 key chunk once (the branch keys are folded in once, on the
+diagonal step); the partial results are joined with ttt_attn_merge into fp32
+accumulators.  The joined result must match a single whole-sequence
+ttt_attn_fwd call and the fp64 oracle; single steps are checked against the
+oracle's ring step, and the merge kernel against the oracle's merge.
+"""
+import numpy as np
+import pytest
+
+import ttt_synth as syn
+from oracle import ttt_oracle as O
+from ttt_cases import TOL, Inputs, bf16_half_ulp, max_abs, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def tk():
+    import attention_ttt_attn_amd as m
+    m.library()
+    return m
+
+
+def zigzag_ring(tk, q, ks, vs, p, cp, rope_base, with_empty_steps=False):
+    """(O fp32 [B,S,Hq,D], LSE [B,Hq,S]) of pass p joined over a zig-zag ring of cp ranks."""
+    B, S, Hq, D = q.shape
+    c = S // (2 * cp)
+    assert c * 2 * cp == S
+    out_o = torch.empty((B, S, Hq, D), dtype=torch.float32, device=q.device)
+    out_l = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    for r in range(cp):
+        for qc in (r, 2 * cp - 1 - r):
+            qa = qc * c
+            acc_o = torch.zeros((B, c, Hq, D), dtype=torch.float32, device=q.device)
+            acc_l = torch.full((B, Hq, c), -float("inf"), dtype=torch.float32, device=q.device)
+            for kc in range(2 * cp if with_empty_steps else qc + 1):
+                ka = kc * c
+                diag = kc == qc
+                sk = [ks[0][:, ka:ka + c]] + [k[:, qa:qa + c] for k in ks[1:p]]
+                sv = [vs[0][:, ka:ka + c]] + [v[:, qa:qa + c] for v in vs[1:p]]
+                o, l = tk.fwd_chunk(q[:, qa:qa + c], sk, sv, p, q_offset=qa, kv_offset=ka, with_branch=diag,
+                                    rope_base=rope_base)
+                if kc > qc:
+                    torch.cuda.synchronize()
+                    assert torch.all(o == 0).item() and torch.all(l == -float("inf")).item()
+                tk.merge(acc_o, acc_l, o, l, out=acc_o, lse=acc_l)
+            out_o[:, qa:qa + c] = acc_o
+            out_l[:, :, qa:qa + c] = acc_l
+    torch.cuda.synchronize()
+    return out_o, out_l
+
+
+def check_ring(tk, inp, p, cp, label, oracle=True):
+    w = inp.w
+    ro, rl = zigzag_ring(tk, inp.gq[p], inp.gk, inp.gv, p, cp, w.rope_base, with_empty_steps=True)
+    so, sl = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, o_fp32=True, rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    d_o = (ro - so).abs().max().item()
+    d_l = (rl - sl).abs().max().item()
+    print(f"{label} p={p} cp={cp}: ring vs single call O {d_o:.3e} LSE {d_l:.3e}")
+    assert d_o <= TOL["bf16"]["o"] and d_l <= TOL["bf16"]["lse"]
+    if oracle:
+        o_ref, l_ref = O.fwd(inp.q[p], inp.k, inp.v, p, layout="bshd", base=w.rope_base)
+        eo, el = max_abs(to_np(ro), o_ref), max_abs(to_np(rl), l_ref)
+        print(f"{label} p={p} cp={cp}: ring vs oracle O {eo:.3e} LSE {el:.3e}")
+        assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
+
+
+@pytest.mark.parametrize("p,cp", [(1, 2), (3, 2), (3, 3)])
+def test_ring_ragged_chunks(dev, tk, p, cp):
+    # S = 600: chunks of 150 (cp=2) or 100 (cp=3) rows, neither a multiple of a tile; GQA 4:1
+    w = syn.Workload("ring_small", 21, "bshd", 2, 600, 8, 2, 128, 3, "bf16", 1e6, False)
+    inp = Inputs(w, dev, with_grad=False)
+    check_ring(tk, inp, p, cp, "ring_small")
+
+
+def test_ring_steps_match_oracle_step(dev, tk):
+    """Single ring steps: diagonal with branch, full off-diagonal, a partial key block,
+    a step whose keys all follow the rows (empty), and a zero-length key block."""
+    w = syn.Workload("ring_step", 22, "bshd", 1, 384, 4, 2, 128, 4, "bf16", 1e6, False)
+    inp = Inputs(w, dev, with_grad=False)
+    p = 4
+    cases = [  # (q_offset, n, kv_offset, m, with_branch)
+        (128, 128, 128, 128, True),
+        (256, 128, 0, 128, False),
+        (200, 70, 150, 90, True),
+        (0, 96, 100, 64, False),
+        (0, 96, 100, 64, True),
+        (40, 33, 40, 0, True),
+    ]
+    for qa, n, ka, m, br in cases:
+        sk = [inp.gk[0][:, ka:ka + m]] + [k[:, qa:qa + n] for k in inp.gk[1:p]]
+        sv = [inp.gv[0][:, ka:ka + m]] + [v[:, qa:qa + n] for v in inp.gv[1:p]]
+        o, l = tk.fwd_chunk(inp.gq[p][:, qa:qa + n], sk, sv, p, q_offset=qa, kv_offset=ka, with_branch=br,
+                            rope_base=w.rope_base)
+        torch.cuda.synchronize()
+        o_ref, l_ref = O.fwd_chunk(inp.q[p][:, qa:qa + n], inp.k[0][:, ka:ka + m], inp.v[0][:, ka:ka + m],
+                                   [k[:, qa:qa + n] for k in inp.k[1:p]] if br else None,
+                                   [v[:, qa:qa + n] for v in inp.v[1:p]] if br else None,
+                                   p, q_offset=qa, kv_offset=ka, base=w.rope_base)
+        og, lg = to_np(o), to_np(l)
+        empty = np.isneginf(l_ref)
+        assert np.array_equal(np.isneginf(lg), empty), (qa, n, ka, m, br)
+        eo = max_abs(og, o_ref)
+        el = max_abs(lg[~empty], l_ref[~empty])
+        print(f"step q@{qa}+{n} kv@{ka}+{m} branch={br}: O {eo:.3e} LSE {el:.3e} empty rows {int(empty.sum())}")
+        assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
+        assert np.all(og[np.transpose(empty, (0, 2, 1))] == 0)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_merge_kernel_matches_oracle(dev, tk, dtype):
+    g = torch.Generator().manual_seed(23)
+    B, n, H, D = 2, 77, 4, 128
+    tdt = torch.float32 if dtype == "fp32" else torch.bfloat16
+    oa = torch.randn((B, n, H, D), generator=g).to(tdt)
+    ob = torch.randn((B, n, H, D), generator=g).to(tdt)
+    la = torch.randn((B, H, n), generator=g) * 3
+    lb = torch.randn((B, H, n), generator=g) * 3
+    la[0, 1, :5] = -float("inf")          # one side empty
+    lb[1, 2, 10:15] = -float("inf")
+    la[1, 3, 20:24] = -float("inf")       # both sides empty
+    lb[1, 3, 20:24] = -float("inf")
+    oa[1, 20:24, 3] = 0
+    ob[1, 20:24, 3] = 0
+    ga, gb, gla, glb = oa.to(dev), ob.to(dev), la.to(dev), lb.to(dev)
+    o, l = tk.merge(ga, gla, gb, glb)
+    torch.cuda.synchronize()
+    o_ref, l_ref = O.merge(oa.double().numpy(), la.double().numpy(), ob.double().numpy(), lb.double().numpy())
+    og, lg = to_np(o), to_np(l)
+    assert np.array_equal(np.isneginf(lg), np.isneginf(l_ref))
+    fin = np.isfinite(l_ref)
+    el = max_abs(lg[fin], l_ref[fin])
+    err = np.abs(og - o_ref)
+    if dtype == "bf16":
+        err = err - bf16_half_ulp(o_ref)
+    print(f"merge {dtype}: O {err.max():.3e} LSE {el:.3e}")
+    assert el <= 1e-5 and err.max() <= 1e-5
+    # in place into o_a gives the same result
+    o2, l2 = tk.merge(ga, gla, gb, glb, out=ga, lse=gla)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(l2, l)
+
+
+def test_ring_fullsize_b4_s4k(dev, tk):
+    """The B=4, S=4096, Hq=32, Hkv=8, K=7 workload over a 4-rank zig-zag ring (chunks of
+    512 rows) at the last pass: ring vs single call on every element, and vs the oracle
+    on sampled rows."""
+    w = syn.workload("b4_s4k")
+    inp = Inputs(w, dev, passes=w.K, with_grad=False)
+    p, cp = w.K, 4
+    ro, rl = zigzag_ring(tk, inp.gq[p], inp.gk, inp.gv, p, cp, w.rope_base)
+    so, sl = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, o_fp32=True, rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    d_o = (ro - so).abs().max().item()
+    d_l = (rl - sl).abs().max().item()
+    print(f"b4_s4k p={p} cp={cp}: ring vs single call O {d_o:.3e} LSE {d_l:.3e}")
+    assert d_o <= TOL["bf16"]["o"] and d_l <= TOL["bf16"]["lse"]
+    rng = np.random.default_rng(24)
+    eo = el = 0.0
+    nrow = 0
+    r = w.Hq // w.Hkv
+    for b in range(w.B):
+        sl_ = O.Slice(b, 0, w.S)
+        for g in range(w.Hkv):
+            # chunk borders of the ring (511/512, ...) plus random rows, 2 heads of the group
+            rows = np.unique(np.concatenate([rng.integers(0, w.S, 72), [0, 511, 512, 1023, 1024, 3583, 3584, 4095]]))
+            heads = {g * r + int(h): rows for h in rng.choice(r, 2, replace=False)}
+            ref = O.fwd_group_rows(inp.q[p], inp.k, inp.v, p, sl_, g, heads, layout="bshd", Hq=w.Hq, Hkv=w.Hkv,
+                                   scale=w.scale, base=w.rope_base)
+            for h, (o_ref, l_ref) in ref.items():
+                idx = torch.as_tensor(rows, device=dev)
+                og = ro[b].index_select(0, idx)[:, h].double().cpu().numpy()
+                lg = rl[b, h].index_select(0, idx).double().cpu().numpy()
+                eo, el = max(eo, max_abs(og, o_ref)), max(el, max_abs(lg, l_ref))
+                nrow += len(rows)
+    print(f"b4_s4k ring vs oracle on {nrow} sampled rows: O {eo:.3e} LSE {el:.3e}")
+    assert nrow >= 4096
+    assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
