@@ -417,20 +417,16 @@ int fwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     }
     _Float16* kt = at<_Float16>(ws, pl.ws.kt);
     uint16_t* vt = at<uint16_t>(ws, pl.ws.vt);
-    // the pass-1 keys: kv_len rows (= the sequence for whole-sequence calls) at positions kv_off + j
+    // the pass-1 keys: kv_len rows (= the sequence for whole-sequence calls) at positions kv_off + j;
+    // rotated K~ rows and V^T in one launch
     ttt::Prob Pk = P;
     if (P.layout == TTT_LAYOUT_BSHD) Pk.stok = P.kv_len;
-    // V^T (side stream when available) beside the rotated K~ (caller's stream)
-    Side sd;
-    const bool forked = sd.begin(st);
-    const hipStream_t vst = forked ? sd.side : st;
-    TTT_TRACED_ON("prep_vt", vst,
-                  ttt::launch_prep_transpose_bf(Pk, (const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, vt,
-                                                vst));
-    const hipEvent_t vt_done = forked ? sd.mark(sd.side) : nullptr;
-    TTT_TRACED("prep_k", ttt::launch_prep_rot_h(Pk, (const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv,
-                                                P.kv_off, cosT, sinT, kt, nullptr, st));
-    if (forked) sd.wait(st, vt_done);
+    ttt::PrepJobs J;
+    memset(&J, 0, sizeof J);
+    J.n = 2;
+    J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, nullptr};
+    J.j[1] = {(const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, 0, 0, 1, nullptr, vt};
+    TTT_TRACED("prep_kv", ttt::launch_prep_bf16(Pk, J, cosT, sinT, st));
     TTT_TRACED("trunk_fwd",
                ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st));
   }
@@ -568,10 +564,13 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
     _Float16* kt = at<_Float16>(ws, pl.ws.kt);
     _Float16* ktt = at<_Float16>(ws, pl.ws.ktt);
     _Float16* qt = at<_Float16>(ws, pl.ws.qt);
-    TTT_TRACED("prep_k", ttt::launch_prep_rot_h(P, (const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, cosT,
-                                                sinT, kt, ktt, st));
-    TTT_TRACED("prep_q", ttt::launch_prep_rot_h(P, (const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, cosT,
-                                                sinT, qt, nullptr, st));
+    // rotated K~ rows, their transpose K~^T and rotated Q~ rows in one launch
+    ttt::PrepJobs J;
+    memset(&J, 0, sizeof J);
+    J.n = 2;
+    J.j[0] = {(const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, kt, (uint16_t*)ktt};
+    J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, 1, 0, qt, nullptr};
+    TTT_TRACED("prep_kq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
     if (forked) sd.wait(st, delta_done);
     if (forked && P.p > 1) sd.wait(sd.side, sd.mark(st));  // start the branch kernel with dK/dV, not beside the prologue
     if (P.p > 1)

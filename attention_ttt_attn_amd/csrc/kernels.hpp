@@ -8,10 +8,21 @@ namespace ttt {
 void launch_rope_table(const Prob& P, float* cosT, float* sinT, double base, hipStream_t st);
 void launch_prep_rot_f32(const Prob& P, const float* x, int64_t sb, int64_t st_, int64_t sh, int H, int pos_off,
                          const float* cosT, const float* sinT, float* out_row, hipStream_t st);
-void launch_prep_rot_h(const Prob& P, const uint16_t* x, int64_t sb, int64_t st_, int64_t sh, int H, int pos_off,
-                       const float* cosT, const float* sinT, _Float16* out_row, _Float16* out_col, hipStream_t st);
-void launch_prep_transpose_bf(const Prob& P, const uint16_t* x, int64_t sb, int64_t st_, int64_t sh, int H,
-                              uint16_t* out_col, hipStream_t st);
+// One staging job of the bf16 prologue (D = 128): the tensor x (element
+// strides sb, st, sh; H heads) into fp16 rows, rotated at row + pos_off when
+// rot, and/or a transposed copy (bf16 when col_bf16, else fp16).
+struct PrepJob {
+  const uint16_t* x;
+  int64_t sb, st, sh;
+  int H, pos_off, rot, col_bf16;
+  _Float16* out_row;
+  uint16_t* out_col;
+};
+struct PrepJobs {
+  PrepJob j[2];
+  int n;
+};
+void launch_prep_bf16(const Prob& P, const PrepJobs& J, const float* cosT, const float* sinT, hipStream_t st);
 void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, float* delta,
                   hipStream_t st);
 void launch_tile_sched(const Prob& P, int tile, int descending, int4* out, int max_entries, int* slot_base,

@@ -105,6 +105,74 @@ __global__ void __launch_bounds__(256) prep_rows_kernel(Prob P, const InT* __res
   }
 }
 
+// bf16 staging of up to two tensors in one launch (D = 128), 16-byte accesses:
+// job j stages X_j [b][tok][h][128] (bf16) into
+//   out_row [(b*H + h)][spad][128]  fp16, rotated at position (row + pos_off) when rot
+//   out_col [(b*H + h)][128][spad]  the same values transposed, fp16 or bf16
+// by workspace slot (slots without a token are written as 0).  Grid
+// (spad/64, H_0 + H_1, B): blockIdx.y < H_0 selects job 0.  Each thread owns
+// 8 rotation pairs (k, k + 64) of a row; 32 rows per pass, two passes.
+__global__ void __launch_bounds__(256) prep_bf16_kernel(Prob P, PrepJobs J, const float* __restrict__ cosT,
+                                                        const float* __restrict__ sinT) {
+  constexpr int D = 128, HALF = 64;
+  __shared__ uint32_t tile[64][D / 2 + 1];  // 16-bit pairs; 65-dword rows: conflict-free column reads
+  const bool second = (int)blockIdx.y >= J.j[0].H;
+  const PrepJob jb = second ? J.j[1] : J.j[0];
+  const int h = second ? (int)blockIdx.y - J.j[0].H : (int)blockIdx.y;
+  const int b = blockIdx.z, tok0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int c8 = tid & 7, rr = tid >> 3;
+  const int64_t slab = (int64_t)(b * jb.H + h) * P.spad;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int lr = pass * 32 + rr, slot = tok0 + lr;
+    float a[8], c[8];
+    int tok, row;
+    if (slot_token(P, slot, tok, row)) {
+      const uint16_t* src = jb.x + (int64_t)b * jb.sb + (int64_t)tok * jb.st + (int64_t)h * jb.sh + 8 * c8;
+      unpack_bf8(*(const u32x4*)src, a);
+      unpack_bf8(*(const u32x4*)(src + HALF), c);
+      if (jb.rot) {
+        const int64_t t = (int64_t)(row + jb.pos_off) * HALF + 8 * c8;
+        const f32x4 c0 = *(const f32x4*)(cosT + t), c1 = *(const f32x4*)(cosT + t + 4);
+        const f32x4 s0 = *(const f32x4*)(sinT + t), s1 = *(const f32x4*)(sinT + t + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float cs = e < 4 ? c0[e] : c1[e - 4], sn = e < 4 ? s0[e] : s1[e - 4];
+          const float y1 = a[e] * cs - c[e] * sn, y2 = c[e] * cs + a[e] * sn;
+          a[e] = y1;
+          c[e] = y2;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a[e] = c[e] = 0.f;
+    }
+    if (jb.out_row) {
+      _Float16* dst = jb.out_row + (slab + slot) * D + 8 * c8;
+      *(u32x4*)dst = pack_h8(a);
+      *(u32x4*)(dst + HALF) = pack_h8(c);
+    }
+    if (jb.out_col) {
+      const u32x4 wa = jb.col_bf16 ? pack_bf8(a) : pack_h8(a);
+      const u32x4 wc = jb.col_bf16 ? pack_bf8(c) : pack_h8(c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tile[lr][4 * c8 + i] = wa[i], tile[lr][HALF / 2 + 4 * c8 + i] = wc[i];
+    }
+  }
+  if (!jb.out_col) return;
+  __syncthreads();
+  // transposed write: work item (d, 8 consecutive slots) -> one 16-byte store
+#pragma unroll
+  for (int w = tid; w < D * 8; w += 256) {
+    const int d = w >> 3, t8 = (w & 7) * 8, sh = 16 * (d & 1);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      o[i] = ((tile[t8 + 2 * i][d >> 1] >> sh) & 0xffffu) | (((tile[t8 + 2 * i + 1][d >> 1] >> sh) & 0xffffu) << 16);
+    *(u32x4*)(jb.out_col + ((int64_t)(b * jb.H + h) * D + d) * P.spad + tok0 + t8) = o;
+  }
+}
+
 // Delta[(b*Hq + h)][slot] = <dO row, O row> in fp32 (0 in slots without a token).
 // Grid (spad/64, Hq, B), 256 threads, D/8 threads per row.
 template <int D, typename OT, typename GT>
@@ -267,15 +335,9 @@ void launch_prep_rot_f32(const Prob& P, const float* x, int64_t sb, int64_t st_,
   prep_rows_any<float, true, float, float>(P, x, sb, st_, sh, H, pos_off, cosT, sinT, out_row, nullptr, st);
 }
 
-void launch_prep_rot_h(const Prob& P, const uint16_t* x, int64_t sb, int64_t st_, int64_t sh, int H, int pos_off,
-                       const float* cosT, const float* sinT, _Float16* out_row, _Float16* out_col, hipStream_t st) {
-  prep_rows_any<uint16_t, true, _Float16, _Float16>(P, x, sb, st_, sh, H, pos_off, cosT, sinT, out_row, out_col, st);
-}
-
-void launch_prep_transpose_bf(const Prob& P, const uint16_t* x, int64_t sb, int64_t st_, int64_t sh, int H,
-                              uint16_t* out_col, hipStream_t st) {
-  prep_rows_any<uint16_t, false, uint16_t, uint16_t>(P, x, sb, st_, sh, H, 0, nullptr, nullptr, nullptr, out_col,
-                                                     st);
+void launch_prep_bf16(const Prob& P, const PrepJobs& J, const float* cosT, const float* sinT, hipStream_t st) {
+  dim3 grid(P.spad / 64, J.j[0].H + (J.n > 1 ? J.j[1].H : 0), P.B);
+  prep_bf16_kernel<<<grid, 256, 0, st>>>(P, J, cosT, sinT);
 }
 
 void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, float* delta,

@@ -75,12 +75,10 @@ def kernel_work(w, name: str, p: int):
         return 6.0 * w.D * w.Hq * tp, "flop"
     if name == "branch_bwd":           # read Q, dO, LSE, Delta, (p-1) K, V; write (p-1) dK, dV
         return float(T * (2 * row_q + w.Hq * 8) + (p - 1) * T * row_kv * 4), "byte"
-    if name == "prep_k":               # read K (bf16), write rotated fp16 rows (the backward's extra
-        return float(T * row_kv * 2), "byte"   # transposed copy is not counted: a lower bound there)
-    if name == "prep_vt":
-        return float(T * row_kv * 2), "byte"
-    if name == "prep_q":               # read Q, write rotated fp16 rows
-        return float(T * row_q * 2), "byte"
+    if name == "prep_kv":              # read K, V (bf16); write rotated fp16 K~ rows and V^T
+        return float(T * row_kv * 4), "byte"
+    if name == "prep_kq":              # read K, Q; write K~ rows, K~^T and Q~ rows (fp16)
+        return float(T * row_kv * 3 + T * row_q * 2), "byte"
     if name == "bwd_delta":
         return float(T * row_q * 2 + T * w.Hq * 4), "byte"
     return 0.0, "byte"
