@@ -45,6 +45,13 @@ What is computed (one call = one TTT pass p, 1-based):
   Gradients are returned per tensor (dK(q), dV(q) for q = 1..p); nothing is
   accumulated across calls.
 
+* Block drafting (issue above, item 2: anchor + mask-token blocks, attention
+  bidirectional inside a block, trunk cut at the anchor).  Reading: block n of
+  bs slots has anchor position a_n; slot t is the token at position a_n + t
+  (slot 0 is the anchor itself, slots 1.. the mask tokens); every slot of the
+  block sees the context keys at positions j < a_n and all bs keys of its own
+  block, rotated at their positions.  `block_fwd` returns O and LSE per slot.
+
 * Ring steps (issue above, item 4: context parallelism, where pass-1 K/V
   travel around a zig-zag ring and partial results are joined by the joint-LSE
   merge): `fwd_chunk` is the attention of a block of query rows at sequence
@@ -67,7 +74,7 @@ import numpy as np
 
 __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_position",
            "ttt_mask_row", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows", "Slice",
-           "fwd_chunk", "merge", "ring_visible"]
+           "fwd_chunk", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd"]
 
 
 # ----------------------------------------------------------------------------- RoPE
@@ -397,3 +404,62 @@ def merge(o_a, lse_a, o_b, lse_b):
     wb = np.where(empty, 0.0, eb / np.where(empty, 1.0, tot))
     to_rows = lambda w: np.transpose(w, (0, 2, 1))[..., None]          # [B, H, n] -> [B, n, H, 1]
     return to_rows(wa) * np.asarray(o_a, np.float64) + to_rows(wb) * np.asarray(o_b, np.float64), L
+
+
+# ----------------------------------------------------------------------------- block drafting
+def block_visible_ctx(anchor: int, ctx_len: int) -> int:
+    """Number of context keys (positions 0..n-1) a block anchored at `anchor` sees."""
+    return int(min(max(anchor, 0), ctx_len))
+
+
+def block_slot_position(anchor: int, t):
+    """Sequence position of slot t of a block anchored at `anchor`."""
+    return int(anchor) + np.asarray(t)
+
+
+def block_fwd_rows(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, b: int, h: int, rows, *,
+                   scale: Optional[float] = None, base: float = 0.0):
+    """O [n, D] and LSE [n] of block-draft rows `rows` (row = block * bs + slot) of
+    batch b, query head h.  q, k_blk, v_blk: [B, nblk*bs, H, D]; k_ctx, v_ctx:
+    [B, ctx_len, Hkv, D]; anchors: [B, nblk]."""
+    Hq, D = q.shape[-2], q.shape[-1]
+    Hkv, ctx_len = k_ctx.shape[-2], k_ctx.shape[1]
+    g = h // (Hq // Hkv)
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    rows = np.asarray(rows, dtype=np.int64)
+    O = np.zeros((len(rows), D))
+    lse = np.full(len(rows), -np.inf)
+    kc_all = rotate_half(np.asarray(k_ctx[b, :, g], np.float64), np.arange(ctx_len), base)  # key j at position j
+    for n_i, row in enumerate(rows):
+        blk, t = int(row) // bs, int(row) % bs
+        a = int(anchors[b, blk])
+        nc = block_visible_ctx(a, ctx_len)
+        qr = rotate_half(np.asarray(q[b, row, h], np.float64), block_slot_position(a, t), base)
+        kc = kc_all[:nc]
+        kb = rotate_half(np.asarray(k_blk[b, blk * bs:(blk + 1) * bs, g], np.float64),
+                         block_slot_position(a, np.arange(bs)), base)
+        keys = np.concatenate([kc, kb], axis=0)
+        vals = np.concatenate([np.asarray(v_ctx[b, :nc, g], np.float64),
+                               np.asarray(v_blk[b, blk * bs:(blk + 1) * bs, g], np.float64)], axis=0)
+        s = scale * (keys @ qr)
+        mx = s.max()
+        w = np.exp(s - mx)
+        lse[n_i] = mx + math.log(w.sum())
+        O[n_i] = (w / w.sum()) @ vals
+    return O, lse
+
+
+def block_fwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, *, scale: Optional[float] = None,
+              base: float = 0.0):
+    """Block-draft forward over every row: (O [B, nblk*bs, Hq, D], LSE [B, Hq, nblk*bs]) in fp64."""
+    B, N, Hq, D = q.shape
+    O = np.zeros((B, N, Hq, D))
+    lse = np.zeros((B, Hq, N))
+    for b in range(B):
+        for h in range(Hq):
+            o_, l_ = block_fwd_rows(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs, b, h, np.arange(N), scale=scale,
+                                    base=base)
+            O[b, :, h] = o_
+            lse[b, h] = l_
+    return O, lse

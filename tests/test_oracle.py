@@ -381,12 +381,81 @@ def check_merge_closed_form():
     assert np.all(l3 == -np.inf) and np.all(o3 == 0)
 
 
+def _block_case(B=1, ctx_len=11, bs=4, nblk=3, Hq=4, Hkv=2, D=8, seed=81):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, nblk * bs, Hq, D))
+    kb = rng.standard_normal((B, nblk * bs, Hkv, D))
+    vb = rng.standard_normal((B, nblk * bs, Hkv, D))
+    kc = rng.standard_normal((B, ctx_len, Hkv, D))
+    vc = rng.standard_normal((B, ctx_len, Hkv, D))
+    return q, kc, vc, kb, vb
+
+
+def check_block_sdpa_mask():
+    """Block drafting == torch SDPA over [context keys ; block keys] rotated at their
+    positions with an explicit mask (context j < anchor, whole own block), incl.
+    anchors 0 (no context) and ctx_len (whole context)."""
+    ctx_len, bs, nblk, Hq, Hkv, D, base, scale = 11, 4, 4, 4, 2, 8, 1e4, 0.3
+    q, kc, vc, kb, vb = _block_case(ctx_len=ctx_len, bs=bs, nblk=nblk, Hq=Hq, Hkv=Hkv, D=D)
+    anchors = np.array([[0, 3, 7, ctx_len]])
+    o, lse = O.block_fwd(q, kc, vc, kb, vb, anchors, bs, scale=scale, base=base)
+    N = nblk * bs
+    rows = torch.arange(N)
+    slot_pos = torch.tensor([int(anchors[0, r // bs]) + r % bs for r in range(N)])
+    qr = rope_complex(torch.tensor(q[0]), slot_pos[:, None].expand(N, Hq), base)
+    kcr = rope_complex(torch.tensor(kc[0]), torch.arange(ctx_len)[:, None].expand(ctx_len, Hkv), base)
+    kbr = rope_complex(torch.tensor(kb[0]), slot_pos[:, None].expand(N, Hkv), base)
+    keys = torch.cat([kcr, kbr], 0)
+    vals = torch.cat([torch.tensor(vc[0]), torch.tensor(vb[0])], 0)
+    anc = torch.tensor([int(anchors[0, r // bs]) for r in range(N)])
+    mask = torch.cat([torch.arange(ctx_len)[None, :] < anc[:, None],
+                      (rows[None, :] // bs) == (rows[:, None] // bs)], dim=1)          # [N, ctx_len + N]
+    r = Hq // Hkv
+    qh = qr.permute(1, 0, 2)
+    kh = keys.permute(1, 0, 2).repeat_interleave(r, 0)
+    vh = vals.permute(1, 0, 2).repeat_interleave(r, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask, scale=scale)
+    sc = (qh @ kh.transpose(-1, -2)) * scale
+    rl = torch.logsumexp(sc.masked_fill(~mask, -math.inf), dim=-1)
+    assert np.max(np.abs(o[0] - ref.permute(1, 0, 2).numpy())) < 1e-12
+    assert np.max(np.abs(lse[0] - rl.numpy())) < 1e-12
+
+
+def check_block_zero_query_closed_form():
+    """Zero queries: every score is 0, so LSE = ln(visible context keys + bs) and O is
+    the mean of the visible values (pins the cut at the anchor exactly)."""
+    ctx_len, bs, nblk = 9, 2, 5
+    q, kc, vc, kb, vb = _block_case(ctx_len=ctx_len, bs=bs, nblk=nblk, Hq=2, Hkv=1, D=8, seed=83)
+    q[:] = 0
+    anchors = np.array([[0, 1, 4, 8, 9]])
+    o, lse = O.block_fwd(q, kc, vc, kb, vb, anchors, bs, base=1e6)
+    for r in range(nblk * bs):
+        a = int(anchors[0, r // bs])
+        blk = r // bs
+        vis = np.concatenate([vc[0, :a, 0], vb[0, blk * bs:(blk + 1) * bs, 0]], axis=0)
+        for h in range(2):
+            assert abs(lse[0, h, r] - math.log(a + bs)) < 1e-12
+            assert np.max(np.abs(o[0, r, h] - vis.mean(axis=0))) < 1e-12
+
+
+def check_block_size1_is_causal():
+    """One slot per block anchored at its own row, with the block key/value equal to the
+    context key/value of that row: causal attention of row i over rows 0..i."""
+    S, Hq, Hkv, D, base = 10, 4, 2, 8, 1e6
+    q, ks, vs, _ = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=1, seed=85, B=1)
+    anchors = np.arange(S)[None, :]
+    o, lse = O.block_fwd(q, ks[0], vs[0], ks[0], vs[0], anchors, 1, base=base)
+    ro, rl = _dense_bshd(q, ks, vs, 1, 1 / math.sqrt(D), base)
+    assert np.max(np.abs(o[0] - ro)) < 1e-12 and np.max(np.abs(lse[0] - rl)) < 1e-12
+
+
 PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check_zero_query_closed_form,
         lambda: check_zero_query_closed_form("thd"), check_sdpa_brute_force, check_p1_is_causal_sdpa,
         check_merge_invariant, check_branch_relative_position, check_grad_autograd,
         check_grad_finite_difference, check_thd_equals_bshd, check_thd_isolation, check_gqa_is_repeated_kv,
         check_sampled_rows_match_full, check_chunk_rows_match_dense, check_chunk_ring_partition,
-        check_merge_closed_form]
+        check_merge_closed_form, check_block_sdpa_mask, check_block_zero_query_closed_form,
+        check_block_size1_is_causal]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
@@ -471,6 +540,9 @@ MISTAKES = [
     ("ring_visible", lambda qp, kp: np.asarray(kp)[None, :] < np.asarray(qp)[:, None]),
     ("ring_visible", lambda qp, kp: np.asarray(kp)[None, :] <= np.asarray(qp)[:, None] + 1),
     ("merge", lambda oa, la, ob, lb: _orig_merge(ob, la, oa, lb)),
+    ("block_visible_ctx", lambda a, L: int(min(max(a + 1, 0), L))),
+    ("block_slot_position", lambda a, t: int(a) + np.asarray(t) + 1),
+    ("block_slot_position", lambda a, t: np.asarray(t)),
     ("merge", lambda oa, la, ob, lb: (_orig_merge(oa, la, ob, lb)[0], np.maximum(la, lb))),
 ]
 

@@ -26,7 +26,8 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "workload", "thd_lengths", "cu_seqlens_of",
+__all__ = ["Workload", "WORKLOADS", "workload", "thd_lengths", "cu_seqlens_of", "BlockWorkload", "BLOCK_WORKLOADS",
+           "block_anchors",
            "draw", "draw_device", "round_bf16", "bf16_bits", "KIND_Q", "KIND_K", "KIND_V", "KIND_DO"]
 
 KIND_Q, KIND_K, KIND_V, KIND_DO = 0, 1, 2, 3
@@ -157,3 +158,56 @@ def draw(w: Workload, kind: int, pass_index: int, shape: Optional[tuple] = None)
     if w.dtype == "bf16":
         x = round_bf16(x)
     return x
+
+
+# ----------------------------------------------------------------------------- block drafting
+@dataclasses.dataclass(frozen=True)
+class BlockWorkload:
+    """Block-draft attention shape: nblk blocks of bs draft slots per batch row,
+    each anchored in a context of ctx_len tokens."""
+    name: str
+    index: int
+    B: int
+    ctx_len: int
+    bs: int
+    nblk: int
+    Hq: int
+    Hkv: int
+    D: int
+    dtype: str
+    rope_base: float
+
+    @property
+    def rows(self) -> int:
+        return self.nblk * self.bs
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def q_shape(self):
+        return (self.B, self.rows, self.Hq, self.D)
+
+    def blk_shape(self):
+        return (self.B, self.rows, self.Hkv, self.D)
+
+    def ctx_shape(self):
+        return (self.B, self.ctx_len, self.Hkv, self.D)
+
+    def as_workload(self) -> Workload:
+        """The Workload whose streams this block workload draws from (its seed and dtype)."""
+        return Workload(self.name, self.index, "bshd", self.B, self.rows, self.Hq, self.Hkv, self.D, 1,
+                        self.dtype, self.rope_base, False)
+
+
+BLOCK_WORKLOADS = {
+    # 256 blocks of 16 slots per batch row over a 4096-token context
+    "blk_b4_c4k": BlockWorkload("blk_b4_c4k", 5, 4, 4096, 16, 256, 32, 8, 128, "bf16", 1e6),
+}
+
+
+def block_anchors(B: int, nblk: int, ctx_len: int, seed: int) -> np.ndarray:
+    """int32 [B, nblk] anchor positions, i.i.d. uniform in [0, ctx_len], ascending per batch row."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 77])))
+    a = rng.integers(0, ctx_len + 1, size=(B, nblk))
+    return np.sort(a, axis=1).astype(np.int32)
