@@ -66,6 +66,17 @@ class Chunk(ctypes.Structure):
     ]
 
 
+class Block(ctypes.Structure):
+    """Block-draft shape (ttt_attn_block)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("block_size", ctypes.c_int32),
+        ("ctx_len", ctypes.c_int64),
+        ("anchors", ctypes.c_void_p),
+        ("ctx_stride", ctypes.c_int64 * 3),
+    ]
+
+
 # void (*)(void* user, const char* kernel, int phase, void* stream)
 TRACE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int, ctypes.c_void_p)
 _trace_ref = None
@@ -118,6 +129,11 @@ def library() -> ctypes.CDLL:
         lib.ttt_attn_fwd_chunk.restype = ctypes.c_int
         lib.ttt_attn_merge.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp]
         lib.ttt_attn_merge.restype = ctypes.c_int
+        lib.ttt_attn_block_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Block)]
+        lib.ttt_attn_block_workspace_bytes.restype = sz
+        lib.ttt_attn_block_fwd.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Block), vp, vp, vp, vp, vp, vp, vp,
+                                           vp, sz, vp]
+        lib.ttt_attn_block_fwd.restype = ctypes.c_int
         lib.ttt_attn_status_string.argtypes = [ctypes.c_int]
         lib.ttt_attn_status_string.restype = ctypes.c_char_p
         lib.ttt_attn_last_error.argtypes = []
@@ -344,4 +360,43 @@ def merge(o_a, lse_a, o_b, lse_b, *, out=None, lse=None, cu_seqlens=None, stream
     d.o_stride[:] = _strides3(o_a, thd)
     _check(library().ttt_attn_merge(ctypes.byref(d), o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(),
                                     lse_b.data_ptr(), out.data_ptr(), lse.data_ptr(), _stream(stream)))
+    return out, lse
+
+
+def make_block(block_size: int, k_ctx, anchors) -> Block:
+    bk = Block()
+    bk.struct_size = ctypes.sizeof(Block)
+    bk.block_size = int(block_size)
+    bk.ctx_len = k_ctx.shape[1]
+    bk.anchors = anchors.data_ptr() if anchors is not None else None
+    bk.ctx_stride[:] = _strides3(k_ctx, False) if k_ctx.numel() else (0, 0, 0)
+    return bk
+
+
+def block_fwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, *, softmax_scale: float = 0.0,
+              rope_base: float = 0.0, o_fp32: bool = False, out=None, lse=None, workspace=None, stream=None):
+    """Block-draft forward (BSHD, bf16).  q [B, N, Hq, D] with N = nblk * block_size;
+    k_ctx, v_ctx [B, ctx_len, Hkv, D]; k_blk, v_blk [B, N, Hkv, D]; anchors int32
+    [B, nblk] on the device.  Returns (o, lse [B, Hq, N])."""
+    torch = _torch()
+    o_dtype = DTYPE_FP32 if o_fp32 else _dtype_code(q)
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32 if o_dtype == DTYPE_FP32 else q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    if anchors.dtype != torch.int32:
+        raise TypeError("anchors must be int32")
+    if k_blk.stride() != v_blk.stride() or k_ctx.stride() != v_ctx.stride():
+        raise ValueError("k and v of the context (and of the blocks) must share strides")
+    d = make_desc(q, [k_blk], 1, softmax_scale=softmax_scale, rope_base=rope_base, o_dtype=o_dtype, o_like=out)
+    bk = make_block(block_size, k_ctx, anchors)
+    nbytes = int(library().ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(bk)))
+    if nbytes == 0:
+        raise TTTAttnError(2, library().ttt_attn_last_error().decode())
+    ws = _workspace(nbytes, q.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    ptr = lambda t: t.data_ptr() if t.numel() else None
+    _check(library().ttt_attn_block_fwd(ctypes.byref(d), ctypes.byref(bk), q.data_ptr(), ptr(k_ctx), ptr(v_ctx),
+                                        k_blk.data_ptr(), v_blk.data_ptr(), out.data_ptr(), lse.data_ptr(), wp, wn,
+                                        _stream(stream)))
     return out, lse

@@ -75,11 +75,15 @@ __device__ __forceinline__ int perm_row(int a) { return (a & ~0xC) | ((a & 4) <<
 // Rows of one work item, per R' (heads per workgroup).
 __host__ __device__ constexpr int tile_rows(int heads_per_wg) { return 32 * 4 / heads_per_wg; }
 
-template <int RH, bool O_F32>
+// MODE 0: TTT pass (trunk + branch).  MODE 1: block drafting -- the trunk is
+// the context prefix j < anchor of each row's block (kt/vt), then the keys of
+// the work item's own blocks (kbt/vbt) in one more masked tile pass.
+template <int RH, bool O_F32, int MODE>
 __global__ void __launch_bounds__(256, 2)
     fwd_bf16_kernel(Prob P, const uint16_t* __restrict__ q, PassPtrs kv, const _Float16* __restrict__ kt,
                     const uint16_t* __restrict__ vt, const int4* __restrict__ tiles, const float* __restrict__ cosT,
-                    const float* __restrict__ sinT, void* __restrict__ o, float* __restrict__ lse) {
+                    const float* __restrict__ sinT, void* __restrict__ o, float* __restrict__ lse,
+                    const _Float16* __restrict__ kbt, const uint16_t* __restrict__ vbt) {
   constexpr int RT = tile_rows(RH);  // rows per work item
   __shared__ __attribute__((aligned(16))) Smem sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -114,7 +118,8 @@ __global__ void __launch_bounds__(256, 2)
   {
     const bool valid = my_row < L;
     const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + my_row) * P.qs_t + h * P.qs_h;
-    const int pos = P.q_off + my_row + P.p - 1;
+    const int pos = MODE == 0 ? P.q_off + my_row + P.p - 1
+                              : (valid ? block_anchor(P, b, my_row) + (my_row & ((1 << P.bs_log2) - 1)) : 0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int d0 = c * 16 + hf * 8;
@@ -153,7 +158,21 @@ __global__ void __launch_bounds__(256, 2)
   const int dq_ = P.layout == 0 ? P.q_off - P.kv_off : 0;
   const int kv_len = P.layout == 0 ? P.kv_len : L;
   const int qend = min(row0 + RT, L);
-  const int kmax = min(qend - 1 + dq_, kv_len - 1);  // last key any row of the work item sees
+  // Block drafting: row i sees context keys j < lim (its block's anchor); the
+  // work item's extent is the largest lim of its blocks, a wave's unmasked
+  // prefix the smallest lim of the wave's blocks (loops are uniform).
+  int lim = 0, lim_hi = 0, lim_lo = 0;
+  if constexpr (MODE == 1) {
+    lim = my_row < L ? block_anchor(P, b, my_row) : 0;
+    const int wend = min(wave_row0 + 32, L);
+    lim_lo = wend > wave_row0 ? P.kv_len : 0;
+    for (int blk = row0 >> P.bs_log2; (blk << P.bs_log2) < qend; ++blk) {
+      const int a = block_anchor(P, b, blk << P.bs_log2);
+      lim_hi = max(lim_hi, a);
+      if ((blk << P.bs_log2) < wend && ((blk + 1) << P.bs_log2) > wave_row0) lim_lo = min(lim_lo, a);
+    }
+  }
+  const int kmax = MODE == 0 ? min(qend - 1 + dq_, kv_len - 1) : lim_hi - 1;  // last key any row sees
   const int nkt = kmax < 0 ? 0 : kmax / BN + 1;
   const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
   const uint16_t* vbase = vt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
@@ -175,13 +194,15 @@ __global__ void __launch_bounds__(256, 2)
     const int d = RPL * (wv * VL + i) + lane / CH;
     voff[i] = (uint32_t)(d * P.spad + ((lane % CH) ^ ((d >> 1) & (CH - 1))) * 8);
   }
-  auto dma = [&](Tile* __restrict__ dst, int kt_) __attribute__((always_inline)) {
-    const _Float16* kb_t = kbase + (int64_t)kt_ * BN * D;
-    const uint16_t* vb_t = vbase + kt_ * BN;
+  auto dma_from = [&](Tile* __restrict__ dst, const _Float16* kb_t, const uint16_t* vb_t)
+                      __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < KL; ++i) lds_dma16(kb_t + koff[i], &dst->k[4 * (wv * KL + i) * D]);
 #pragma unroll
     for (int i = 0; i < VL; ++i) lds_dma16(vb_t + voff[i], &dst->v[RPL * (wv * VL + i) * BN]);
+  };
+  auto dma = [&](Tile* __restrict__ dst, int kt_) __attribute__((always_inline)) {
+    dma_from(dst, kbase + (int64_t)kt_ * BN * D, vbase + kt_ * BN);
   };
   // wait_tiles(n): all but this wave's last n tiles of loads have landed
   auto wait_tiles = [&](int n) __attribute__((always_inline)) {
@@ -206,7 +227,7 @@ __global__ void __launch_bounds__(256, 2)
   const int prow = perm_row(l32);
   const float sl2 = P.scale_log2;
   // Tiles whose every key precedes every row of this wave need no mask.
-  const int n_free = max(0, min(wave_row0 + 1 + dq_, kv_len)) / BN;
+  const int n_free = MODE == 0 ? max(0, min(wave_row0 + 1 + dq_, kv_len)) / BN : lim_lo / BN;
 
   // Moves the running max to mx when mx exceeds it by more than 8 (log2 units).
   auto raise_max = [&](float mx) {
@@ -248,13 +269,19 @@ __global__ void __launch_bounds__(256, 2)
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], qf[c0 + c], sacc[kb], 0, 0, 0);
       }
     }
-    if constexpr (decltype(masked)::value) {
+    // masks: 1 causal trunk, 2 context prefix j < lim, 3 the row's own block
+    constexpr int M = decltype(masked)::value;
+    if constexpr (M != 0) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = key0 + kb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
-          if (key > my_row + dq_ || key >= kv_len) sacc[kb][v] = -INFINITY;
+          bool off;
+          if constexpr (M == 1) off = key > my_row + dq_ || key >= kv_len;
+          else if constexpr (M == 2) off = key >= lim;
+          else off = (key >> P.bs_log2) != (my_row >> P.bs_log2) || key >= L;
+          if (off) sacc[kb][v] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -299,17 +326,32 @@ __global__ void __launch_bounds__(256, 2)
   for (int kt_ = 0; kt_ < nkt; ++kt_) {
     auto step = [&](const Tile* __restrict__ cur, Tile* __restrict__ dst) __attribute__((always_inline)) {
       if (kt_ + NBUF - 1 < nkt) dma(dst, kt_ + NBUF - 1);
-      if (kt_ < n_free) tile(cur, kt_ * BN, std::false_type{});
-      else tile(cur, kt_ * BN, std::true_type{});
+      if (kt_ < n_free) tile(cur, kt_ * BN, std::integral_constant<int, 0>{});
+      else tile(cur, kt_ * BN, std::integral_constant<int, MODE == 0 ? 1 : 2>{});
     };
     step(&sm.ring[kt_ % NBUF], &sm.ring[(kt_ + NBUF - 1) % NBUF]);
     if (kt_ + 1 < nkt) wait_tiles(min(nkt, kt_ + NBUF) - (kt_ + 2));  // tile kt_+1 has landed
     __syncthreads();                                                    // every wave is done with tile kt_
   }
 
+  // ---- block drafting: the keys of the work item's own blocks (rows row0 ..
+  // row0+RT-1; bs divides 32, so no block straddles the work item), one
+  // 64-key tile at a time, masked to the row's block
+  if constexpr (MODE == 1) {
+    const _Float16* kbb = kbt + (int64_t)(b * P.Hkv + g) * P.spad_b * D;
+    const uint16_t* vbb = vbt + (int64_t)(b * P.Hkv + g) * D * P.spad_b;
+    for (int k0 = row0; k0 < qend; k0 += BN) {
+      dma_from(&sm.ring[0], kbb + (int64_t)k0 * D, vbb + k0);
+      TTT_WAIT_VMCNT(0);
+      __syncthreads();
+      tile(&sm.ring[0], k0, std::integral_constant<int, 3>{});
+      __syncthreads();
+    }
+  }
+
   // ---- branch: keys/values of passes 2..p at the same row, folded into (m, l, O)
   const int lr = rbk * 32 + l32;  // this lane's row within the tile
-  for (int qq = 2; qq <= (P.branch ? P.p : 1); ++qq) {
+  for (int qq = 2; qq <= (MODE == 0 && P.branch ? P.p : 1); ++qq) {
     // stage R(i+q-1) k^(q) (fp16) and v^(q) (bf16) for the tile's rows: 8 threads per row
     for (int r0 = 0; r0 < RT; r0 += 32) {
       const int rr = r0 + (tid >> 3), c8 = tid & 7;
@@ -418,19 +460,32 @@ __global__ void __launch_bounds__(256, 2)
 
 int heads_per_wg(int r) { return r % 4 == 0 ? 4 : (r % 2 == 0 ? 2 : 1); }
 
-template <int RH>
+template <int RH, int MODE>
 static void launch_rh(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const uint16_t* vt,
                       const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
-                      hipStream_t st) {
+                      const _Float16* kbt, const uint16_t* vbt, hipStream_t st) {
   constexpr int RT = tile_rows(RH);
   int ntiles;
   if (P.layout == 0) ntiles = P.B * ((P.stok + RT - 1) / RT);
   else ntiles = (P.stok + RT - 1) / RT + P.nseq;
   const int64_t grid = (int64_t)ntiles * P.Hkv * (P.r / RH);
   if (o_f32)
-    fwd_bf16_kernel<RH, true><<<(unsigned)grid, 256, 0, st>>>(P, q, kv, kt, vt, tiles, cosT, sinT, o, lse);
+    fwd_bf16_kernel<RH, true, MODE>
+        <<<(unsigned)grid, 256, 0, st>>>(P, q, kv, kt, vt, tiles, cosT, sinT, o, lse, kbt, vbt);
   else
-    fwd_bf16_kernel<RH, false><<<(unsigned)grid, 256, 0, st>>>(P, q, kv, kt, vt, tiles, cosT, sinT, o, lse);
+    fwd_bf16_kernel<RH, false, MODE>
+        <<<(unsigned)grid, 256, 0, st>>>(P, q, kv, kt, vt, tiles, cosT, sinT, o, lse, kbt, vbt);
+}
+
+template <int MODE>
+static void launch_mode(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt,
+                        const uint16_t* vt, const int4* tiles, const float* cosT, const float* sinT, void* o,
+                        bool o_f32, float* lse, const _Float16* kbt, const uint16_t* vbt, hipStream_t st) {
+  switch (heads_per_wg(P.r)) {
+    case 4: launch_rh<4, MODE>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, kbt, vbt, st); break;
+    case 2: launch_rh<2, MODE>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, kbt, vbt, st); break;
+    default: launch_rh<1, MODE>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, kbt, vbt, st); break;
+  }
 }
 
 }  // namespace fwd
@@ -440,11 +495,14 @@ int fwd_tile_rows(int r) { return fwd::tile_rows(fwd::heads_per_wg(r)); }
 void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const uint16_t* vt,
                      const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
                      hipStream_t st) {
-  switch (fwd::heads_per_wg(P.r)) {
-    case 4: fwd::launch_rh<4>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, st); break;
-    case 2: fwd::launch_rh<2>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, st); break;
-    default: fwd::launch_rh<1>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, st); break;
-  }
+  fwd::launch_mode<0>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, nullptr, nullptr, st);
+}
+
+void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const uint16_t* vt,
+                           const _Float16* kbt, const uint16_t* vbt, const float* cosT, const float* sinT, void* o,
+                           bool o_f32, float* lse, hipStream_t st) {
+  const PassPtrs none = {};
+  fwd::launch_mode<1>(P, q, none, kt, vt, nullptr, cosT, sinT, o, o_f32, lse, kbt, vbt, st);
 }
 
 }  // namespace ttt

@@ -43,7 +43,19 @@ struct Prob {
   // key j at kv_off + j for j < kv_len; branch = 0 leaves passes 2..p out.
   // Whole-sequence calls: q_off = kv_off = 0, kv_len = stok, branch = 1.
   int q_off, kv_off, kv_len, branch;
+  // Block drafting (BSHD forward): row i is slot i % bs of block i / bs, whose
+  // anchor a = anchors[b * nblk + i / bs] (clamped to [0, kv_len]) puts the
+  // slot at position a + i % bs; it sees context keys j < a (kv_len context
+  // rows) and the bs keys of its block (staged with spad_b slots per head;
+  // the forward kernel requires spad_b == spad).
+  const int* anchors;
+  int bs_log2, nblk, spad_b;
 };
+
+__device__ __forceinline__ int block_anchor(const Prob& P, int b, int row) {
+  const int a = P.anchors[(int64_t)b * P.nblk + (row >> P.bs_log2)];
+  return a < 0 ? 0 : (a > P.kv_len ? P.kv_len : a);
+}
 
 // Passes' key/value pointers (up to 16), passed by value to kernels.
 struct PassPtrs {

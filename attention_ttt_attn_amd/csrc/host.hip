@@ -424,8 +424,8 @@ int fwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     ttt::PrepJobs J;
     memset(&J, 0, sizeof J);
     J.n = 2;
-    J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, nullptr};
-    J.j[1] = {(const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, 0, 0, 1, nullptr, vt};
+    J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, nullptr, 0};
+    J.j[1] = {(const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, 0, 0, 1, nullptr, vt, 0};
     TTT_TRACED("prep_kv", ttt::launch_prep_bf16(Pk, J, cosT, sinT, st));
     TTT_TRACED("trunk_fwd",
                ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st));
@@ -459,6 +459,136 @@ int ttt_attn_fwd_chunk(const ttt_attn_desc* d, const ttt_attn_chunk* c, const vo
     return fail(TTT_ERR_NULL_ARG, "chunk is NULL");
   }
   return fwd_impl(d, c, q, k, v, o, lse, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+// Block-draft plan: the descriptor's rows are the block slots; the context
+// and the block keys each get their own staging slabs.
+struct BlockPlan {
+  Plan pl;
+  int64_t cs_b, cs_t, cs_h;  // context K/V strides
+  size_t ctx_kt, ctx_vt, blk_kt, blk_vt, total;
+};
+
+int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan& bp) {
+  if (!bk) return fail(TTT_ERR_NULL_ARG, "block descriptor is NULL");
+  if (bk->struct_size != sizeof(ttt_attn_block))
+    return fail(TTT_ERR_ABI, "block struct_size %u != %zu", bk->struct_size, sizeof(ttt_attn_block));
+  Plan& pl = bp.pl;
+  if (int e = make_plan(d, 0, pl)) return e;
+  ttt::Prob& P = pl.P;
+  if (d->layout != TTT_LAYOUT_BSHD) return fail(TTT_ERR_UNSUPPORTED, "block drafting takes the BSHD layout");
+  if (!pl.bf16) return fail(TTT_ERR_UNSUPPORTED, "block drafting is built for bf16");
+  if (d->pass_index != 1) return fail(TTT_ERR_BAD_SHAPE, "block drafting has no passes: pass_index must be 1");
+  const int bs = bk->block_size;
+  if (bs < 1 || bs > 32 || (bs & (bs - 1)))
+    return fail(TTT_ERR_UNSUPPORTED, "block_size %d: 1, 2, 4, 8, 16 or 32", bs);
+  if (P.stok % bs) return fail(TTT_ERR_BAD_SHAPE, "seqlen %d is not a whole number of blocks of %d", P.stok, bs);
+  if (bk->ctx_len < 0 || bk->ctx_len + bs > ((int64_t)1 << 30))
+    return fail(TTT_ERR_BAD_SHAPE, "ctx_len %lld outside [0, 2^30 - block_size]", (long long)bk->ctx_len);
+  const int ctx = (int)bk->ctx_len;
+  P.kv_len = ctx;
+  P.branch = 0;
+  P.bs_log2 = __builtin_ctz((unsigned)bs);
+  P.nblk = P.stok / bs;
+  P.anchors = bk->anchors;
+  P.npos = ctx + bs;                                   // slot positions a + t <= ctx + bs - 1
+  // context and block slabs share one slot count: the kernel's V^T row
+  // offsets are computed once for both
+  const int rows_max = ctx > P.stok ? ctx : P.stok;
+  P.spad = ((rows_max + 63) / 64) * 64 + 64;
+  P.spad_b = P.spad;
+  const int64_t* s0 = bk->ctx_stride;
+  const int D = P.D, Hkv = P.Hkv;
+  if (s0[0] == 0 && s0[1] == 0 && s0[2] == 0) {
+    bp.cs_b = (int64_t)ctx * Hkv * D, bp.cs_t = (int64_t)Hkv * D, bp.cs_h = D;
+  } else {
+    for (int i = 0; i < 3; ++i) {
+      if (s0[i] < 0) return fail(TTT_ERR_BAD_SHAPE, "ctx stride[%d] = %lld is negative", i, (long long)s0[i]);
+      if (s0[i] % 8) return fail(TTT_ERR_MISALIGNED, "ctx stride[%d] = %lld not a multiple of 8 elements", i,
+                                 (long long)s0[i]);
+    }
+    bp.cs_b = s0[0], bp.cs_t = s0[1], bp.cs_h = s0[2];
+  }
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at_ = off;
+    off = align256(off + bytes);
+    return at_;
+  };
+  memset(&pl.ws, 0, sizeof pl.ws);
+  pl.ws.table = take((size_t)2 * P.npos * (D / 2) * sizeof(float));
+  const size_t nc = (size_t)P.B * Hkv * P.spad * D, nb = (size_t)P.B * Hkv * P.spad_b * D;
+  bp.ctx_kt = take(nc * 2);
+  bp.ctx_vt = take(nc * 2);
+  bp.blk_kt = take(nb * 2);
+  bp.blk_vt = take(nb * 2);
+  bp.total = off;
+  pl.ws.total = off;
+  return TTT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t ttt_attn_block_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_block* bk) {
+  g_last_error.clear();
+  BlockPlan bp;
+  if (make_block_plan(d, bk, bp) != TTT_OK) return 0;
+  return bp.total;
+}
+
+int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const void* q, const void* k_ctx,
+                       const void* v_ctx, const void* k_blk, const void* v_blk, void* o, float* lse, void* ws,
+                       size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  BlockPlan bp;
+  if (int e = make_block_plan(d, bk, bp)) return e;
+  Plan& pl = bp.pl;
+  ttt::Prob& P = pl.P;
+  if (P.stok == 0) return TTT_OK;
+  if (!bk->anchors) return fail(TTT_ERR_NULL_ARG, "anchors is NULL");
+  if ((uintptr_t)bk->anchors & 3u) return fail(TTT_ERR_MISALIGNED, "anchors is not 4-byte aligned");
+  if (int e = check_ptr(q, "q")) return e;
+  if (int e = check_ptr(k_blk, "k_blk")) return e;
+  if (int e = check_ptr(v_blk, "v_blk")) return e;
+  if (int e = check_ptr(o, "o")) return e;
+  if (P.kv_len > 0) {  // an empty context is never read: its pointers may be NULL
+    if (int e = check_ptr(k_ctx, "k_ctx")) return e;
+    if (int e = check_ptr(v_ctx, "v_ctx")) return e;
+  }
+  if (!lse) return fail(TTT_ERR_NULL_ARG, "lse is NULL");
+  if ((uintptr_t)lse & 3u) return fail(TTT_ERR_MISALIGNED, "lse is not 4-byte aligned");
+  if (int e = check_ws(pl, ws, ws_bytes)) return e;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  float* cosT = at<float>(ws, pl.ws.table);
+  float* sinT = cosT + (size_t)P.npos * (P.D / 2);
+  _Float16* ckt = at<_Float16>(ws, bp.ctx_kt);
+  uint16_t* cvt = at<uint16_t>(ws, bp.ctx_vt);
+  _Float16* bkt = at<_Float16>(ws, bp.blk_kt);
+  uint16_t* bvt = at<uint16_t>(ws, bp.blk_vt);
+  TTT_TRACED("rope_table", ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st));
+  // context: K~ rows at positions j and V^T (kv_len rows)
+  ttt::Prob Pc = P;
+  Pc.stok = P.kv_len;
+  ttt::PrepJobs J;
+  memset(&J, 0, sizeof J);
+  J.n = 2;
+  J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, nullptr, 0};
+  J.j[1] = {(const uint16_t*)v_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 0, 1, nullptr, cvt, 0};
+  TTT_TRACED("prep_ctx", ttt::launch_prep_bf16(Pc, J, cosT, sinT, st));
+  // block keys: K~ rows at their slot positions and V^T (spad_b slots)
+  ttt::Prob Pb = P;
+  Pb.spad = P.spad_b;
+  J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, nullptr, 1};
+  J.j[1] = {(const uint16_t*)v_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 0, 1, nullptr, bvt, 0};
+  TTT_TRACED("prep_blk", ttt::launch_prep_bf16(Pb, J, cosT, sinT, st));
+  TTT_TRACED("block_fwd", ttt::launch_block_fwd_bf16(P, (const uint16_t*)q, ckt, cvt, bkt, bvt, cosT, sinT, o,
+                                                     pl.o_f32, lse, st));
+  return hip_check("ttt_attn_block_fwd launch");
 }
 
 int ttt_attn_merge(const ttt_attn_desc* d, const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
@@ -568,8 +698,8 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
     ttt::PrepJobs J;
     memset(&J, 0, sizeof J);
     J.n = 2;
-    J.j[0] = {(const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, kt, (uint16_t*)ktt};
-    J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, 1, 0, qt, nullptr};
+    J.j[0] = {(const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, kt, (uint16_t*)ktt, 0};
+    J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, 1, 0, qt, nullptr, 0};
     TTT_TRACED("prep_kq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
     if (forked) sd.wait(st, delta_done);
     if (forked && P.p > 1) sd.wait(sd.side, sd.mark(st));  // start the branch kernel with dK/dV, not beside the prologue

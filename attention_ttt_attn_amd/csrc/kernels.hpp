@@ -11,12 +11,15 @@ void launch_prep_rot_f32(const Prob& P, const float* x, int64_t sb, int64_t st_,
 // One staging job of the bf16 prologue (D = 128): the tensor x (element
 // strides sb, st, sh; H heads) into fp16 rows, rotated at row + pos_off when
 // rot, and/or a transposed copy (bf16 when col_bf16, else fp16).
+// pos_anchor: rotate at the block-slot position of the row (block_anchor of
+// the Prob plus the slot index) instead of row + pos_off.
 struct PrepJob {
   const uint16_t* x;
   int64_t sb, st, sh;
   int H, pos_off, rot, col_bf16;
   _Float16* out_row;
   uint16_t* out_col;
+  int pos_anchor;
 };
 struct PrepJobs {
   PrepJob j[2];
@@ -36,7 +39,13 @@ void launch_bwd_f32(const Prob& P, const PassPtrs& kv, const float* lse, const f
                     const PassGradPtrs& g, hipStream_t st);
 
 // bf16 path (MFMA trunk + shuffle-reduction branch)
-int fwd_tile_rows(int r);     // query rows per forward work item for GQA ratio r (32, 64 or 128)
+int fwd_tile_rows(int r);
+// Block-draft forward (BSHD, D = 128): context K~ / V^T in kt / vt (P.spad
+// slots), block K~ / V^T in kbt / vbt (P.spad_b slots); P.anchors, P.bs_log2,
+// P.nblk, P.kv_len (context rows) describe the blocks.
+void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const uint16_t* vt,
+                           const _Float16* kbt, const uint16_t* vbt, const float* cosT, const float* sinT, void* o,
+                           bool o_f32, float* lse, hipStream_t st);     // query rows per forward work item for GQA ratio r (32, 64 or 128)
 constexpr int kFwdMinRows = 32;
 int dq_tile_rows(int r);      // query rows per dQ work item for GQA ratio r (32, 64 or 128)
 constexpr int kBwdBKV = 128;  // key rows per dK/dV workgroup

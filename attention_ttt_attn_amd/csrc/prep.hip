@@ -132,7 +132,8 @@ __global__ void __launch_bounds__(256) prep_bf16_kernel(Prob P, PrepJobs J, cons
       unpack_bf8(*(const u32x4*)src, a);
       unpack_bf8(*(const u32x4*)(src + HALF), c);
       if (jb.rot) {
-        const int64_t t = (int64_t)(row + jb.pos_off) * HALF + 8 * c8;
+        const int pos = jb.pos_anchor ? block_anchor(P, b, row) + (row & ((1 << P.bs_log2) - 1)) : row + jb.pos_off;
+        const int64_t t = (int64_t)pos * HALF + 8 * c8;
         const f32x4 c0 = *(const f32x4*)(cosT + t), c1 = *(const f32x4*)(cosT + t + 4);
         const f32x4 s0 = *(const f32x4*)(sinT + t), s1 = *(const f32x4*)(sinT + t + 4);
 #pragma unroll

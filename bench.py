@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--ring", type=int, default=0, metavar="CP",
                     help="instead of the unroll, time the ring-step forward of the last pass over a zig-zag ring "
                          "of CP ranks emulated on this GPU, per chunk shape (prints its own JSON line)")
+    ap.add_argument("--block", action="store_true",
+                    help="instead of the unroll, time the block-draft forward on the blk_b4_c4k shape "
+                         "(prints its own JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy a 256 MiB buffer 3 times (a plain copy kernel of known size "
                          "that scales the HBM byte counters of a profiler run)")
@@ -225,6 +228,81 @@ def ring_main(args, w, dev):
     print(json.dumps(out), flush=True)
 
 
+def block_main(args, dev):
+    """Block-draft forward: 256 blocks of 16 slots per batch row over a 4096-token context
+    (B=4, Hq=32, Hkv=8, D=128).  Useful FLOPs: 4*D per (slot, head, visible key), the
+    visible keys of a slot being its block's context prefix plus the bs block keys."""
+    import numpy as np
+    import torch
+
+    import attention_ttt_attn_amd as tk
+    import ttt_synth as syn
+
+    bw = syn.BLOCK_WORKLOADS["blk_b4_c4k"]
+    w = bw.as_workload()
+    q = syn.draw_device(w, syn.KIND_Q, 1, dev, bw.q_shape())
+    kc = syn.draw_device(w, syn.KIND_K, 1, dev, bw.ctx_shape())
+    vc = syn.draw_device(w, syn.KIND_V, 1, dev, bw.ctx_shape())
+    kb = syn.draw_device(w, syn.KIND_K, 2, dev, bw.blk_shape())
+    vb = syn.draw_device(w, syn.KIND_V, 2, dev, bw.blk_shape())
+    anchors = syn.block_anchors(bw.B, bw.nblk, bw.ctx_len, bw.index)
+    ga = torch.from_numpy(anchors).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((bw.B, bw.Hq, bw.rows), dtype=torch.float32, device=dev)
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    pairs = int((np.clip(anchors, 0, bw.ctx_len).astype(np.int64) + bw.bs).sum()) * bw.bs   # per head
+    flops = 4.0 * bw.D * bw.Hq * pairs
+    run = lambda: tk.block_fwd(q, kc, vc, kb, vb, ga, bw.bs, rope_base=bw.rope_base, out=o, lse=lse, workspace=ws)
+    for _ in range(max(args.warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    events = []
+    cur = torch.cuda.current_stream()
+
+    def hook(name, phase, stream):
+        s = cur if not stream or stream == cur.cuda_stream else torch.cuda.ExternalStream(stream)
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(s)
+        if phase == 0:
+            events.append([name, ev, None])
+        else:
+            events[-1][2] = ev
+
+    n = max(args.steps, 1)
+    tk.set_trace_hook(hook)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    tk.set_trace_hook(None)
+    call_ms = e0.elapsed_time(e1) / n
+    ks = {}
+    for name, a, b in events:
+        k = ks.setdefault(name, [0, 0.0])
+        k[0] += 1
+        k[1] += a.elapsed_time(b)
+    kern = {k: {"avg_us": round(v[1] * 1e3 / v[0], 2), "launches_per_call": v[0] // n} for k, v in ks.items()}
+    fwd_us = kern["block_fwd"]["avg_us"]
+    achieved = flops / (fwd_us * 1e-6)
+    row_kv = bw.Hkv * bw.D * 2
+    kern["prep_ctx"]["gbps"] = round(bw.B * bw.ctx_len * row_kv * 4 / (kern["prep_ctx"]["avg_us"] * 1e-6) / 1e9, 1)
+    kern["prep_blk"]["gbps"] = round(bw.B * bw.rows * row_kv * 4 / (kern["prep_blk"]["avg_us"] * 1e-6) / 1e9, 1)
+    value = flops / (call_ms * 1e-3) / 1e12
+    out = {"metric": "block-draft attention fwd TFLOP/s (useful FLOPs)", "value": round(value, 2), "unit": "TFLOP/s",
+           "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(call_ms, 4), "higher_is_better": True,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": bw.name, "batch": bw.B, "ctx_len": bw.ctx_len, "block_size": bw.bs,
+                      "blocks": bw.nblk, "q_heads": bw.Hq, "kv_heads": bw.Hkv, "head_dim": bw.D,
+                      "useful_tflop_per_call": round(flops / 1e12, 4)},
+           "roofline": {"kernel": "block_fwd", "bound": "mfma", "achieved": round(achieved / 1e12, 2),
+                        "peak": 2500.0, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16, 4),
+                        "traffic": None, "work_per_launch": flops, "avg_launch_us": fwd_us},
+           "kernels": kern, "source_digest": source_digest()}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -244,6 +322,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.block:
+        block_main(args, dev)
+        return
     w = syn.workload(args.workload)
     if args.ring:
         ring_main(args, w, dev)

@@ -173,6 +173,43 @@ int ttt_attn_fwd_chunk(const ttt_attn_desc* d, const ttt_attn_chunk* c, const vo
 int ttt_attn_merge(const ttt_attn_desc* d, const void* o_a, const float* lse_a, const void* o_b,
                    const float* lse_b, void* o, float* lse, void* stream);
 
+/* ---- Block drafting: anchor + mask-token blocks ----------------------------
+ * Same issue, "What I'm working on", item 2: block drafters predict a block of
+ * tokens at once from an anchor followed by mask tokens; attention is
+ * bidirectional inside the block and the trunk (context) is cut at the
+ * anchor.  Reading taken here (the pages leave the exact mask open): block n
+ * of batch row b has bs slots and anchor a = anchors[b * nblk + n] (clamped
+ * to [0, ctx_len]); slot t is the token at position a + t (slot 0 is the
+ * anchor, 1.. the mask tokens); every slot of the block sees the context keys
+ * at positions j < a and all bs keys of its own block.  RoPE (rotate-half)
+ * at those positions, as in ttt_attn_fwd.
+ * The descriptor gives the block rows: layout BSHD, dtype BF16, seqlen =
+ * nblk * bs rows (row i = slot i % bs of block i / bs), pass_index 1,
+ * q_stride for q, kv_stride for k_blk / v_blk [B, seqlen, Hkv, D], o_stride,
+ * softmax_scale, rope_base.  Output O [B, seqlen, Hq, D] and LSE [B, Hq,
+ * seqlen] as in ttt_attn_fwd. */
+typedef struct ttt_attn_block {
+  uint32_t struct_size;       /* = sizeof(ttt_attn_block)                                 */
+  int32_t block_size;         /* bs: 1, 2, 4, 8, 16 or 32                                 */
+  int64_t ctx_len;            /* context rows of k_ctx / v_ctx                            */
+  const int32_t* anchors;     /* device int32 [B][seqlen / bs], read-only; values outside
+                                 [0, ctx_len] are clamped                                  */
+  int64_t ctx_stride[3];      /* batch, token, head strides of k_ctx / v_ctx (elements); a
+                                 zero triple selects the contiguous [B, ctx_len, Hkv, D]   */
+} ttt_attn_block;
+
+/* Bytes of workspace ttt_attn_block_fwd needs (0 and the last error if invalid). */
+size_t ttt_attn_block_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_block* blk);
+
+/* Forward of block-draft attention.  q [B, seqlen, Hq, D]; k_ctx, v_ctx the
+ * context keys/values (may be NULL when ctx_len = 0); k_blk, v_blk the block
+ * keys/values; o, lse outputs; ws, ws_bytes workspace as for ttt_attn_fwd.
+ * Checked on the host before any launch (same status codes); the anchors are
+ * not read on the host.  Returns a ttt_attn_status. */
+int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* blk, const void* q, const void* k_ctx,
+                       const void* v_ctx, const void* k_blk, const void* v_blk, void* o, float* lse, void* ws,
+                       size_t ws_bytes, void* stream);
+
 /* Static text of a status code. */
 const char* ttt_attn_status_string(int status);
 

@@ -433,7 +433,7 @@ def block_fwd_rows(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, b: int, h: i
     kc_all = rotate_half(np.asarray(k_ctx[b, :, g], np.float64), np.arange(ctx_len), base)  # key j at position j
     for n_i, row in enumerate(rows):
         blk, t = int(row) // bs, int(row) % bs
-        a = int(anchors[b, blk])
+        a = int(min(max(int(anchors[b, blk]), 0), ctx_len))      # anchors are clamped to [0, ctx_len]
         nc = block_visible_ctx(a, ctx_len)
         qr = rotate_half(np.asarray(q[b, row, h], np.float64), block_slot_position(a, t), base)
         kc = kc_all[:nc]

@@ -271,3 +271,69 @@ def test_merge_validation():
     bad = good_desc()
     bad.num_q_heads = 0
     assert call(desc=bad) == 2
+
+
+# ----------------------------------------------------------------------------- block drafting
+def good_block(bs=16, ctx_len=300, anchors=FAKE):
+    bk = tk.Block()
+    bk.struct_size = ctypes.sizeof(tk.Block)
+    bk.block_size, bk.ctx_len, bk.anchors = bs, ctx_len, anchors
+    return bk
+
+
+def block_desc(rows=128):
+    d = good_desc(p=1)
+    d.seqlen = rows
+    return d
+
+
+def call_block(d, bk, q=FAKE, kc=FAKE, vc=FAKE, kb=FAKE, vb=FAKE, o=FAKE, lse=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return tk.library().ttt_attn_block_fwd(ctypes.byref(d), ctypes.byref(bk) if bk is not None else None, q, kc, vc,
+                                           kb, vb, o, lse, ws, ws_bytes, None)
+
+
+def test_block_struct_matches_header():
+    assert ctypes.sizeof(tk.Block) == 48
+    assert "ttt_attn_block" in open(os.path.join(ROOT, "include", "tttattn.h")).read()
+
+
+def test_block_validation():
+    lib = tk.library()
+    d = block_desc()
+    assert call_block(d, None) == 1 and "block" in err()
+    bk = good_block()
+    bk.struct_size = 4
+    assert call_block(d, bk) == 7
+    for bs in (0, 3, 64):
+        assert call_block(d, good_block(bs=bs)) == 3 and "block_size" in err()
+    assert call_block(block_desc(rows=100), good_block(bs=16)) == 2 and "blocks" in err()
+    assert call_block(d, good_block(ctx_len=-1)) == 2 and "ctx_len" in err()
+    dd = block_desc()
+    dd.pass_index = 2
+    assert call_block(dd, good_block()) == 2 and "pass_index" in err()
+    assert call_block(good_desc(layout=tk.LAYOUT_THD, p=1), good_block()) == 3
+    assert call_block(good_desc(dtype=tk.DTYPE_FP32, p=1), good_block()) == 3
+    assert call_block(d, good_block(anchors=None)) == 1 and "anchors" in err()
+    assert call_block(d, good_block(anchors=FAKE + 2)) == 4
+    assert call_block(d, good_block(), kb=None) == 1 and "k_blk" in err()
+    assert call_block(d, good_block(), kc=FAKE + 8) == 4 and "k_ctx" in err()
+    assert call_block(d, good_block(), lse=None) == 1
+    bk = good_block()
+    bk.ctx_stride[:] = (300 * 256, 256, 100)
+    assert call_block(d, bk) == 4 and "ctx stride" in err()
+    need = lib.ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(good_block()))
+    assert need > 0 and call_block(d, good_block(), ws_bytes=need - 1) == 5
+
+
+def test_block_empty_context_pointers_may_be_null():
+    # ctx_len = 0: the context is never read, so NULL k_ctx / v_ctx pass the pointer checks
+    # (the call then stops at the workspace check, before any launch)
+    assert call_block(block_desc(), good_block(ctx_len=0), kc=None, vc=None, ws_bytes=16) == 5
+    assert call_block(block_desc(), good_block(ctx_len=5), kc=None, ws_bytes=16) == 1
+
+
+def test_block_workspace_grows():
+    lib = tk.library()
+    w = lambda d, bk: lib.ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(bk))
+    assert w(block_desc(128), good_block(ctx_len=4096)) > w(block_desc(128), good_block(ctx_len=64))
+    assert w(block_desc(4096), good_block()) > w(block_desc(128), good_block())
