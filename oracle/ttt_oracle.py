@@ -50,7 +50,9 @@ What is computed (one call = one TTT pass p, 1-based):
   bs slots has anchor position a_n; slot t is the token at position a_n + t
   (slot 0 is the anchor itself, slots 1.. the mask tokens); every slot of the
   block sees the context keys at positions j < a_n and all bs keys of its own
-  block, rotated at their positions.  `block_fwd` returns O and LSE per slot.
+  block, rotated at their positions.  `block_fwd` returns O and LSE per slot;
+  `block_bwd` the gradients of q, the context K/V and the block K/V by the
+  same chain rule as the TTT backward below.
 
 * Ring steps (issue above, item 4: context parallelism, where pass-1 K/V
   travel around a zig-zag ring and partial results are joined by the joint-LSE
@@ -74,7 +76,8 @@ import numpy as np
 
 __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_position",
            "ttt_mask_row", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows", "Slice",
-           "fwd_chunk", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd"]
+           "fwd_chunk", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd",
+           "block_bwd_rows", "block_bwd"]
 
 
 # ----------------------------------------------------------------------------- RoPE
@@ -463,3 +466,71 @@ def block_fwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, *, scale: Optiona
             O[b, :, h] = o_
             lse[b, h] = l_
     return O, lse
+
+
+def block_bwd_rows(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, dout, b: int, h: int, rows, *,
+                   scale: Optional[float] = None, base: float = 0.0):
+    """Backward contributions of block-draft rows `rows` of batch b, query head h.
+
+    Returns (dq [n, D], dk_ctx [ctx_len, D], dv_ctx [ctx_len, D], dk_blk [N, D],
+    dv_blk [N, D]) where the key gradients hold only these rows' contributions
+    (a key's gradient is complete once every row that sees it is included)."""
+    Hq, D = q.shape[-2], q.shape[-1]
+    Hkv, ctx_len = k_ctx.shape[-2], k_ctx.shape[1]
+    N = q.shape[1]
+    g = h // (Hq // Hkv)
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.zeros((len(rows), D))
+    dkc_rot, dvc = np.zeros((ctx_len, D)), np.zeros((ctx_len, D))
+    dkb, dvb = np.zeros((N, D)), np.zeros((N, D))
+    kc_all = rotate_half(np.asarray(k_ctx[b, :, g], np.float64), np.arange(ctx_len), base)
+    for n_i, row in enumerate(rows):
+        blk, t = int(row) // bs, int(row) % bs
+        a = int(min(max(int(anchors[b, blk]), 0), ctx_len))
+        nc = block_visible_ctx(a, ctx_len)
+        pq = block_slot_position(a, t)
+        qr = rotate_half(np.asarray(q[b, row, h], np.float64), pq, base)
+        pb = block_slot_position(a, np.arange(bs))
+        kbr = rotate_half(np.asarray(k_blk[b, blk * bs:(blk + 1) * bs, g], np.float64), pb, base)
+        keys = np.concatenate([kc_all[:nc], kbr], axis=0)
+        vals = np.concatenate([np.asarray(v_ctx[b, :nc, g], np.float64),
+                               np.asarray(v_blk[b, blk * bs:(blk + 1) * bs, g], np.float64)], axis=0)
+        s_ = scale * (keys @ qr)
+        mx = s_.max()
+        P = np.exp(s_ - mx)
+        P /= P.sum()
+        o = P @ vals
+        do = np.asarray(dout[b, row, h], np.float64)
+        dS = P * (vals @ do - do @ o)
+        dq[n_i] = unrotate_half(scale * (dS @ keys), pq, base)
+        dk_rot = scale * dS[:, None] * qr[None, :]
+        dv = P[:, None] * do[None, :]
+        dkc_rot[:nc] += dk_rot[:nc]
+        dvc[:nc] += dv[:nc]
+        dkb[blk * bs:(blk + 1) * bs] += unrotate_half(dk_rot[nc:], pb, base)
+        dvb[blk * bs:(blk + 1) * bs] += dv[nc:]
+    dkc = unrotate_half(dkc_rot, np.arange(ctx_len), base)
+    return dq, dkc, dvc, dkb, dvb
+
+
+def block_bwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, dout, *, scale: Optional[float] = None,
+              base: float = 0.0):
+    """Block-draft backward over every row: (dQ, dK_ctx, dV_ctx, dK_blk, dV_blk) in fp64,
+    shaped like q, k_ctx, v_ctx, k_blk, v_blk (GQA: key gradients summed over the group)."""
+    B, N, Hq, D = q.shape
+    dQ = np.zeros(q.shape)
+    dKc, dVc = np.zeros(k_ctx.shape), np.zeros(v_ctx.shape)
+    dKb, dVb = np.zeros(k_blk.shape), np.zeros(v_blk.shape)
+    r = Hq // k_ctx.shape[-2]
+    for b in range(B):
+        for h in range(Hq):
+            dq, dkc, dvc, dkb, dvb = block_bwd_rows(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs, dout, b, h,
+                                                    np.arange(N), scale=scale, base=base)
+            dQ[b, :, h] = dq
+            dKc[b, :, h // r] += dkc
+            dVc[b, :, h // r] += dvc
+            dKb[b, :, h // r] += dkb
+            dVb[b, :, h // r] += dvb
+    return dQ, dKc, dVc, dKb, dVb

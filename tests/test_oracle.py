@@ -449,13 +449,41 @@ def check_block_size1_is_causal():
     assert np.max(np.abs(o[0] - ro)) < 1e-12 and np.max(np.abs(lse[0] - rl)) < 1e-12
 
 
+def check_block_grad_autograd():
+    """Block-draft gradients == fp64 torch autograd through SDPA over [context ; block]
+    keys with the explicit block mask (GQA, anchors 0 .. ctx_len)."""
+    ctx_len, bs, nblk, Hq, Hkv, D, base = 9, 4, 4, 4, 2, 8, 1e4
+    q, kc, vc, kb, vb = _block_case(ctx_len=ctx_len, bs=bs, nblk=nblk, Hq=Hq, Hkv=Hkv, D=D, seed=87)
+    dout = np.random.default_rng(88).standard_normal(q.shape)
+    anchors = np.array([[0, 2, 6, ctx_len]])
+    scale = 1 / math.sqrt(D)
+    got = O.block_bwd(q, kc, vc, kb, vb, anchors, bs, dout, base=base)
+    N, r = nblk * bs, Hq // Hkv
+    T = [torch.tensor(x[0], requires_grad=True) for x in (q, kc, vc, kb, vb)]
+    tq, tkc, tvc, tkb, tvb = T
+    slot_pos = torch.tensor([int(anchors[0, i // bs]) + i % bs for i in range(N)])
+    qr = rope_complex(tq, slot_pos[:, None].expand(N, Hq), base)
+    keys = torch.cat([rope_complex(tkc, torch.arange(ctx_len)[:, None].expand(ctx_len, Hkv), base),
+                      rope_complex(tkb, slot_pos[:, None].expand(N, Hkv), base)], 0)
+    vals = torch.cat([tvc, tvb], 0)
+    anc = torch.tensor([int(anchors[0, i // bs]) for i in range(N)])
+    rows = torch.arange(N)
+    mask = torch.cat([torch.arange(ctx_len)[None, :] < anc[:, None], (rows[None, :] // bs) == (rows[:, None] // bs)], 1)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qr.permute(1, 0, 2), keys.permute(1, 0, 2).repeat_interleave(r, 0),
+        vals.permute(1, 0, 2).repeat_interleave(r, 0), attn_mask=mask, scale=scale).permute(1, 0, 2)
+    (out * torch.tensor(dout[0])).sum().backward()
+    for mine, t in zip(got, T):
+        assert np.max(np.abs(mine[0] - t.grad.numpy())) < 1e-10
+
+
 PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check_zero_query_closed_form,
         lambda: check_zero_query_closed_form("thd"), check_sdpa_brute_force, check_p1_is_causal_sdpa,
         check_merge_invariant, check_branch_relative_position, check_grad_autograd,
         check_grad_finite_difference, check_thd_equals_bshd, check_thd_isolation, check_gqa_is_repeated_kv,
         check_sampled_rows_match_full, check_chunk_rows_match_dense, check_chunk_ring_partition,
         check_merge_closed_form, check_block_sdpa_mask, check_block_zero_query_closed_form,
-        check_block_size1_is_causal]
+        check_block_size1_is_causal, check_block_grad_autograd]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
