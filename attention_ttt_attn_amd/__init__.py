@@ -129,11 +129,13 @@ def library() -> ctypes.CDLL:
         lib.ttt_attn_fwd_chunk.restype = ctypes.c_int
         lib.ttt_attn_merge.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp]
         lib.ttt_attn_merge.restype = ctypes.c_int
-        lib.ttt_attn_block_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Block)]
+        lib.ttt_attn_block_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Block), ctypes.c_int]
         lib.ttt_attn_block_workspace_bytes.restype = sz
         lib.ttt_attn_block_fwd.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Block), vp, vp, vp, vp, vp, vp, vp,
                                            vp, sz, vp]
         lib.ttt_attn_block_fwd.restype = ctypes.c_int
+        lib.ttt_attn_block_bwd.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Block)] + [vp] * 14 + [sz, vp]
+        lib.ttt_attn_block_bwd.restype = ctypes.c_int
         lib.ttt_attn_status_string.argtypes = [ctypes.c_int]
         lib.ttt_attn_status_string.restype = ctypes.c_char_p
         lib.ttt_attn_last_error.argtypes = []
@@ -390,7 +392,7 @@ def block_fwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, *, softma
         raise ValueError("k and v of the context (and of the blocks) must share strides")
     d = make_desc(q, [k_blk], 1, softmax_scale=softmax_scale, rope_base=rope_base, o_dtype=o_dtype, o_like=out)
     bk = make_block(block_size, k_ctx, anchors)
-    nbytes = int(library().ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(bk)))
+    nbytes = int(library().ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(bk), 0))
     if nbytes == 0:
         raise TTTAttnError(2, library().ttt_attn_last_error().decode())
     ws = _workspace(nbytes, q.device, workspace)
@@ -400,3 +402,37 @@ def block_fwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, *, softma
                                         k_blk.data_ptr(), v_blk.data_ptr(), out.data_ptr(), lse.data_ptr(), wp, wn,
                                         _stream(stream)))
     return out, lse
+
+
+def block_bwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, o, lse, dout, *, softmax_scale: float = 0.0,
+              rope_base: float = 0.0, dq=None, dk_ctx=None, dv_ctx=None, dk_blk=None, dv_blk=None, workspace=None,
+              stream=None):
+    """Block-draft backward.  Returns (dq, dk_ctx, dv_ctx, dk_blk, dv_blk)."""
+    torch = _torch()
+    like = lambda t: torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
+    dq = like(q) if dq is None else dq
+    dk_ctx = like(k_ctx) if dk_ctx is None else dk_ctx
+    dv_ctx = like(v_ctx) if dv_ctx is None else dv_ctx
+    dk_blk = like(k_blk) if dk_blk is None else dk_blk
+    dv_blk = like(v_blk) if dv_blk is None else dv_blk
+    if dout.stride() != o.stride():
+        raise ValueError("dout must have the strides of o")
+    if dq.stride() != q.stride() or dk_blk.stride() != k_blk.stride() or dv_blk.stride() != k_blk.stride():
+        raise ValueError("gradients take the strides of their primal")
+    if k_ctx.numel() and (dk_ctx.stride() != k_ctx.stride() or dv_ctx.stride() != k_ctx.stride()):
+        raise ValueError("gradients take the strides of their primal")
+    if k_blk.stride() != v_blk.stride() or k_ctx.stride() != v_ctx.stride():
+        raise ValueError("k and v of the context (and of the blocks) must share strides")
+    d = make_desc(q, [k_blk], 1, softmax_scale=softmax_scale, rope_base=rope_base, o_dtype=_dtype_code(o), o_like=o)
+    bk = make_block(block_size, k_ctx, anchors)
+    nbytes = int(library().ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(bk), 1))
+    if nbytes == 0:
+        raise TTTAttnError(2, library().ttt_attn_last_error().decode())
+    ws = _workspace(nbytes, q.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    ptr = lambda t: t.data_ptr() if t.numel() else None
+    _check(library().ttt_attn_block_bwd(ctypes.byref(d), ctypes.byref(bk), q.data_ptr(), ptr(k_ctx), ptr(v_ctx),
+                                        k_blk.data_ptr(), v_blk.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                        dout.data_ptr(), dq.data_ptr(), ptr(dk_ctx), ptr(dv_ctx), dk_blk.data_ptr(),
+                                        dv_blk.data_ptr(), wp, wn, _stream(stream)))
+    return dq, dk_ctx, dv_ctx, dk_blk, dv_blk

@@ -61,13 +61,16 @@ struct DqSmem {
 __host__ __device__ constexpr int dq_rows(int heads_per_wg) { return 32 * 4 / heads_per_wg; }
 static int dq_heads_per_wg(int r) { return r % 4 == 0 ? 4 : (r % 2 == 0 ? 2 : 1); }
 
-template <int RH>
+// MODE 0: TTT pass.  MODE 1: block drafting -- key tiles of the context
+// (kt/ktt, V = kv.v[0] with the P.cs strides) up to each row's block anchor,
+// then the keys of the work item's own blocks (kbt/kbtt, V = kv.v[1]).
+template <int RH, int MODE>
 __global__ void __launch_bounds__(256, 2)
     dq_bf16_kernel(Prob P, const uint16_t* __restrict__ q, PassPtrs kv, const float* __restrict__ lse,
                    const uint16_t* __restrict__ dout, const _Float16* __restrict__ kt,
                    const _Float16* __restrict__ ktt, const _Float16* __restrict__ qt, const float* __restrict__ delta,
                    const int4* __restrict__ tiles, const float* __restrict__ cosT, const float* __restrict__ sinT,
-                   uint16_t* __restrict__ dq) {
+                   uint16_t* __restrict__ dq, const _Float16* __restrict__ kbt, const _Float16* __restrict__ kbtt) {
   constexpr int RT = dq_rows(RH);  // rows per work item
   __shared__ __attribute__((aligned(16))) DqSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -110,13 +113,30 @@ __global__ void __launch_bounds__(256, 2)
   const int my_row = wave_row0 + l32;
   const bool row_ok = my_row < L;
   const int qend = min(row0 + RT, L);
-  const int nkt = (qend + QBN - 1) / QBN;  // >= 1: row0 < L
+  // Block drafting: row i sees context keys j < lim (its block's anchor); the
+  // work item spans the largest lim of its blocks, a wave's unmasked prefix
+  // is the smallest lim of the wave's blocks.
+  int lim = 0, lim_hi = 0, lim_lo = 0;
+  if constexpr (MODE == 1) {
+    lim = row_ok ? block_anchor(P, b, my_row) : 0;
+    const int wend = min(wave_row0 + 32, L);
+    lim_lo = wend > wave_row0 ? P.kv_len : 0;
+    for (int blk = row0 >> P.bs_log2; (blk << P.bs_log2) < qend; ++blk) {
+      const int a = block_anchor(P, b, blk << P.bs_log2);
+      lim_hi = max(lim_hi, a);
+      if ((blk << P.bs_log2) < wend && ((blk + 1) << P.bs_log2) > wave_row0) lim_lo = min(lim_lo, a);
+    }
+  }
+  const int nkt = MODE == 0 ? (qend + QBN - 1) / QBN : (lim_hi + QBN - 1) / QBN;  // TTT: >= 1 (row0 < L)
 
   // DMA lane roles, 6 loads per wave per tile (load n = 2w + i):
   // K~ and V rows 4n + lane/16, slot lane%16; K~^T d-rows 16n + lane/4, slot lane%4.
   const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
   const _Float16* ktbase = ktt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
-  const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * P.ks_b + (int64_t)start * P.ks_t + g * P.ks_h;
+  const int64_t vs_b = MODE == 0 ? P.ks_b : P.cs_b, vs_t = MODE == 0 ? P.ks_t : P.cs_t;
+  const int64_t vs_h = MODE == 0 ? P.ks_h : P.cs_h;
+  const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * vs_b + (int64_t)start * vs_t + g * vs_h;
+  const int vlast = (MODE == 0 ? L : P.kv_len) - 1;  // last key row of the trunk
   uint32_t roff[2], toff[2];
   int rrow[2];
 #pragma unroll
@@ -128,19 +148,22 @@ __global__ void __launch_bounds__(256, 2)
     const int d = 16 * n + (lane >> 2);
     toff[i] = (uint32_t)(d * P.spad + ((lane & 3) ^ ((d >> 2) & 3)) * 8);
   }
-  auto dma = [&](DqBuf* __restrict__ dst, int j) __attribute__((always_inline)) {
+  auto dma_from = [&](DqBuf* __restrict__ dst, const _Float16* kb, const _Float16* ktb, const uint16_t* vb,
+                      int64_t vst, int key0, int last) __attribute__((always_inline)) {
     DqBuf& B_ = *dst;
-    const int key0 = j * QBN;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int n = 2 * wv + i;
-      const int rg = min(key0 + rrow[i], L - 1);  // V rows past the end repeat the last row (masked)
-      lds_dma16(kbase + (int64_t)(key0 + rrow[i]) * D + roff[i], &B_.k[4 * n * D]);
-      lds_dma16(vbase + (int64_t)rg * P.ks_t + roff[i], &B_.v[4 * n * D]);
-      lds_dma16(ktbase + key0 + toff[i], &B_.kt[16 * n * QBN]);
+      const int rg = min(key0 + rrow[i], last);  // V rows past the end repeat the last row (masked)
+      lds_dma16(kb + (int64_t)(key0 + rrow[i]) * D + roff[i], &B_.k[4 * n * D]);
+      lds_dma16(vb + (int64_t)rg * vst + roff[i], &B_.v[4 * n * D]);
+      lds_dma16(ktb + key0 + toff[i], &B_.kt[16 * n * QBN]);
     }
   };
-  dma(&sm.buf[0], 0);
+  auto dma = [&](DqBuf* __restrict__ dst, int j) __attribute__((always_inline)) {
+    dma_from(dst, kbase, ktbase, vbase, vs_t, j * QBN, vlast);
+  };
+  if (nkt > 0) dma(&sm.buf[0], 0);
 
   // B operands of this lane's query: Q~ (fp16, pre-rotated) and dO (bf16)
   f16x8 qf[8];
@@ -171,10 +194,11 @@ __global__ void __launch_bounds__(256, 2)
     for (int v = 0; v < 16; ++v) acc[d4][v] = 0.f;
   const int prow = perm_row(l32);
   // Tiles whose every key precedes every row of this wave need no mask.
-  const int n_free = (wave_row0 + 1) / QBN;
+  const int n_free = MODE == 0 ? (wave_row0 + 1) / QBN : lim_lo / QBN;
 
   // S^T = K~ Q~^T, dP^T = V dO^T, dS = P (dP - Delta), dQ~^T += K~^T dS^T.
-  auto tile = [&](const DqBuf* __restrict__ src, const int j, auto masked) __attribute__((always_inline)) {
+  // Masks: 1 causal, 2 context prefix key < lim, 3 the row's own block.
+  auto tile = [&](const DqBuf* __restrict__ src, const int key0, auto masked) __attribute__((always_inline)) {
     const DqBuf& B_ = *src;
     f32x16 s, dp;
 #pragma unroll
@@ -195,13 +219,17 @@ __global__ void __launch_bounds__(256, 2)
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[c], dof[c0 + c], dp, 0, 0, 0);
       }
     }
-    // key of (v, hf) = j*QBN + 16*(v/8) + 8*hf + v%8
+    // key of (v, hf) = key0 + 16*(v/8) + 8*hf + v%8
     f16x8 dsb[2];
-    const int thr = my_row - (j * QBN + 8 * hf);
+    constexpr int M = decltype(masked)::value;
+    const int thr = my_row - (key0 + 8 * hf);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       float pr = fast_exp2(__builtin_fmaf(s[v], sl2, -lse2));
-      if constexpr (decltype(masked)::value) pr = (v >> 3) * 16 + (v & 7) > thr ? 0.f : pr;
+      const int key = key0 + (v >> 3) * 16 + 8 * hf + (v & 7);
+      if constexpr (M == 1) pr = (v >> 3) * 16 + (v & 7) > thr ? 0.f : pr;
+      else if constexpr (M == 2) pr = key >= lim ? 0.f : pr;
+      else if constexpr (M == 3) pr = ((key >> P.bs_log2) != (my_row >> P.bs_log2) || key >= L) ? 0.f : pr;
       dsb[v >> 3][v & 7] = (_Float16)(pr * (dp[v] - dl));
     }
 #pragma unroll
@@ -221,12 +249,26 @@ __global__ void __launch_bounds__(256, 2)
     // this tile's LDS reads, so the compiler puts no wait on them
     auto step = [&](const DqBuf* __restrict__ cur, DqBuf* __restrict__ nxt) __attribute__((always_inline)) {
       if (j + 1 < nkt) dma(nxt, j + 1);
-      if (j < n_free) tile(cur, j, std::false_type{});
-      else tile(cur, j, std::true_type{});
+      if (j < n_free) tile(cur, j * QBN, std::integral_constant<int, 0>{});
+      else tile(cur, j * QBN, std::integral_constant<int, MODE == 0 ? 1 : 2>{});
     };
     step(&sm.buf[j & 1], &sm.buf[(j + 1) & 1]);
     TTT_WAIT_VMCNT(0);  // tile j+1 has landed
     __syncthreads();    // and every wave is done with tile j
+  }
+  // block drafting: the keys of the work item's own blocks (bs divides 32, so
+  // the blocks of rows row0 .. qend-1 are exactly key rows row0 .. qend-1)
+  if constexpr (MODE == 1) {
+    const _Float16* kbb = kbt + (int64_t)(b * P.Hkv + g) * P.spad * D;
+    const _Float16* ktbb = kbtt + (int64_t)(b * P.Hkv + g) * D * P.spad;
+    const uint16_t* vbb = (const uint16_t*)kv.v[1] + b * P.ks_b + g * P.ks_h;
+    for (int k0 = row0; k0 < qend; k0 += QBN) {
+      dma_from(&sm.buf[0], kbb, ktbb, vbb, P.ks_t, k0, L - 1);
+      TTT_WAIT_VMCNT(0);
+      __syncthreads();
+      tile(&sm.buf[0], k0, std::integral_constant<int, 3>{});
+      __syncthreads();
+    }
   }
   {
     const int lr = wv * 32 + l32;
@@ -260,10 +302,10 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
       for (int e = 0; e < 4; ++e) a[e] = x0[e], a[4 + e] = x1[e], a[8 + e] = y0[e], a[12 + e] = y1[e];
     }
-    const int pos = i + P.p - 1;
+    const int pos = MODE == 0 ? i + P.p - 1 : block_anchor(P, b, i) + (i & ((1 << P.bs_log2) - 1));
     const float* cq = cosT + (int64_t)pos * 64 + dlo;
     const float* sq = sinT + (int64_t)pos * 64 + dlo;
-    if (P.p > 1) {
+    if (MODE == 0 && P.p > 1) {
       float qr[16], go[16];
       {
         const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + i) * P.qs_t + hh * P.qs_h;
@@ -344,9 +386,16 @@ struct KvBuf {
   uint16_t g[BQ * D];   // dO rows   (A of dP; columns: A of dV^T)
   float lse[BQ];        // natural-log LSE of the rows
   float dl[BQ];         // Delta of the rows
+  int anc[2 * BQ];      // block drafting, context keys: the rows' clamped block anchors (twice)
 };
 
 
+// MODE 0: TTT pass (trunk keys, rows i >= j).  Block drafting: MODE 2 the
+// context keys (P.kv_len of them; row i sees key j < its block's anchor),
+// MODE 3 the block keys (seen by the rows of their own block only).  kt, kv.v[0]
+// and gr.dk[0] / gr.dv[0] are those keys' K~ slab, V and gradients (P.ks_*
+// strides).
+template <int MODE>
 __global__ void __launch_bounds__(256, 1)
     dkdv_bf16_kernel(Prob P, PassPtrs kv, const float* __restrict__ lse, const uint16_t* __restrict__ dout,
                      const _Float16* __restrict__ kt, const _Float16* __restrict__ qt,
@@ -360,8 +409,9 @@ __global__ void __launch_bounds__(256, 1)
   // run together share that XCD's L2 for the query rows they all stream.
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   int b, t, start, L, slot0, g;
+  const int nkeys = MODE == 2 ? P.kv_len : P.stok;
   if (P.layout == 0) {
-    const int nkt = (P.stok + BKV - 1) / BKV;
+    const int nkt = (nkeys + BKV - 1) / BKV;
     const int ppx = (P.B * P.Hkv + 7) / 8;  // pairs per XCD
     t = slot / ppx;
     const int pair = (slot % ppx) * 8 + xcd;
@@ -380,7 +430,30 @@ __global__ void __launch_bounds__(256, 1)
   }
   const int kv0 = t * BKV;
   const int my_key = kv0 + wv * 32 + l32;
-  const bool key_ok = my_key < L;
+  const bool key_ok = my_key < (MODE == 2 ? nkeys : L);
+  // query rows [row_lo, row_hi) that can see this key tile
+  int row_lo = kv0, row_hi = L;
+  if constexpr (MODE == 3) row_hi = min(kv0 + BKV, L);
+  if constexpr (MODE == 2) {
+    // the first block whose anchor passes kv0 (any anchor order): rows before
+    // it see no key here.  Every wave scans all anchors itself: no shared
+    // memory or barrier before the staging ring.
+    int first = P.nblk;
+    for (int n = lane; n < P.nblk; n += 64)
+      if (block_anchor(P, b, n << P.bs_log2) > kv0) first = min(first, n);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) first = min(first, __shfl_xor(first, m, 64));
+    row_lo = min(__builtin_amdgcn_readfirstlane(first) << P.bs_log2, L) & ~(BQ - 1);
+  }
+  // position of this lane's key (block keys: the slot position in its block)
+  int kpos = my_key;
+  if constexpr (MODE == 3) kpos = key_ok ? block_anchor(P, b, my_key) + (my_key & ((1 << P.bs_log2) - 1)) : 0;
+  if constexpr (MODE != 0) {
+    // every global load above has landed before the first staging load: the
+    // compiler's load counter is then exact and no full wait lands in the loop
+    TTT_WAIT_VMCNT(0);
+    asm volatile("" ::"v"(kpos), "s"(row_lo));
+  }
 
   f16x8 kf[8];
   bf16x8 vf[8];
@@ -406,7 +479,7 @@ __global__ void __launch_bounds__(256, 1)
   // Steps st = 0..nsteps-1: head st % r of row block nq-1-st/r (from the
   // sequence end downwards).  The loads run three steps ahead of the compute;
   // both sides advance (head, row block) counters instead of dividing.
-  const int nq = (L - kv0 + BQ - 1) / BQ;
+  const int nq = max(0, (row_hi - row_lo + BQ - 1) / BQ);
   const int nsteps = P.r * nq;
   // DMA lane roles (wave w issues instructions j = 2w, 2w+1 of each 8 KB tile):
   // rows r = 4j + lane/16, slot lane%16.  Sources at head 0 of the group, row 0.
@@ -432,7 +505,11 @@ __global__ void __launch_bounds__(256, 1)
                              : delta + (int64_t)(b * P.Hq + g * P.r) * P.spad + slot0;
   const int64_t m_hstride = m_lse ? P.lse_h : (int64_t)P.spad;
   const int m_row = lane & 31, m_last = m_lse ? L - 1 : L;
-  int is_h = 0, is_q0 = kv0 + (nq - 1) * BQ;  // the next step to load
+  int is_h = 0, is_q0 = row_lo + (nq - 1) * BQ;  // the next step to load
+  // block drafting, context keys: wave 1 loads the step's rows' visible context
+  // lengths (clamped anchors, staged per slot in the workspace next to Delta)
+  const bool w1a = MODE == 2 && wv == 1;
+  const int* a_src = MODE == 2 ? (const int*)(delta + (int64_t)P.B * P.Hq * P.spad) + (int64_t)b * P.spad : nullptr;
   auto issue = [&](KvBuf* __restrict__ Bd) __attribute__((always_inline)) {
     KvBuf& B = *Bd;
     const int64_t qoff = ((int64_t)is_h * P.spad + is_q0) * D;
@@ -445,13 +522,15 @@ __global__ void __launch_bounds__(256, 1)
       lds_dma16(gsrc, &B.g[4 * j * D]);
     }
     if (wv == 0) lds_dma4(m_src + is_h * m_hstride + min(is_q0 + m_row, m_last), &B.lse[0]);
+    if (w1a) lds_dma4(a_src + is_q0 + m_row, &B.anc[0]);
     if (++is_h == P.r) {
       is_h = 0;
       is_q0 -= BQ;
     }
   };
-  // loads each wave has in flight per step (wave 0 also loads LSE/Delta)
-  const bool w0 = wv == 0;
+  // loads each wave has in flight per step (wave 0 also loads LSE/Delta, and
+  // wave 1 the anchors for the context keys of block drafting)
+  const bool w0 = wv == 0 || w1a;
 
   // S = Q~ K~^T and dP = dO V^T for step st (this wave's 32 keys x 32 rows).
   auto products = [&](const KvBuf* __restrict__ Bp, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
@@ -495,7 +574,7 @@ __global__ void __launch_bounds__(256, 1)
   // The three ring buffers an iteration touches go through distinct restrict
   // pointers: the compiler then knows the loads into the step-(st+3) buffer
   // cannot alias this iteration's LDS reads and puts no wait on them.
-  int cs_h = 0, cs_q0 = kv0 + (nq - 1) * BQ;  // the step being computed
+  int cs_h = 0, cs_q0 = row_lo + (nq - 1) * BQ;  // the step being computed
   for (int st = 0; st < nsteps; ++st) {
    auto step = [&](const KvBuf* __restrict__ Bcp, const KvBuf* __restrict__ Bnp, KvBuf* __restrict__ Bdp)
                    __attribute__((always_inline)) {
@@ -515,13 +594,23 @@ __global__ void __launch_bounds__(256, 1)
       const int thr = my_key - (q0 + m0);
       const f32x4 l0 = *(const f32x4*)&Bc.lse[m0], l1 = *(const f32x4*)&Bc.lse[m0 + 4];
       const f32x4 d0 = *(const f32x4*)&Bc.dl[m0], d1 = *(const f32x4*)&Bc.dl[m0 + 4];
+      int4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
+      if constexpr (MODE == 2) a0 = *(const int4*)&Bc.anc[m0], a1 = *(const int4*)&Bc.anc[m0 + 4];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int v = half * 8 + e;
         const float lv = (e < 4 ? l0[e] : l1[e - 4]) * kLog2e;
         const float dv_ = e < 4 ? d0[e] : d1[e - 4];
         float pr = fast_exp2(__builtin_fmaf(s_c[v], sl2, -lv));
-        pr = e >= thr ? pr : 0.f;
+        if constexpr (MODE == 0) {
+          pr = e >= thr ? pr : 0.f;
+        } else if constexpr (MODE == 2) {  // key j visible iff j < the row's (clamped) anchor
+          const int an = e == 0 ? a0.x : e == 1 ? a0.y : e == 2 ? a0.z : e == 3 ? a0.w
+                       : e == 4 ? a1.x : e == 5 ? a1.y : e == 6 ? a1.z : a1.w;
+          pr = my_key < an ? pr : 0.f;
+        } else {  // the row's own block
+          pr = ((q0 + m0 + e) >> P.bs_log2) == (my_key >> P.bs_log2) ? pr : 0.f;
+        }
         pb[half][e] = (__bf16)pr;
         dsb[half][e] = (_Float16)(pr * (dp_c[v] - dv_));
       }
@@ -574,8 +663,8 @@ __global__ void __launch_bounds__(256, 1)
   const int64_t off = b * P.ks_b + (int64_t)(start + my_key) * P.ks_t + g * P.ks_h;
   uint16_t* dkrow = (uint16_t*)gr.dk[0] + off;
   uint16_t* dvrow = (uint16_t*)gr.dv[0] + off;
-  const float* cp = cosT + (int64_t)my_key * 64;
-  const float* sp = sinT + (int64_t)my_key * 64;
+  const float* cp = cosT + (int64_t)kpos * 64;
+  const float* sp = sinT + (int64_t)kpos * 64;
 #pragma unroll
   for (int d4 = 0; d4 < 2; ++d4)
 #pragma unroll
@@ -691,13 +780,31 @@ void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const
   const int64_t grid = P.layout == 0
                            ? (int64_t)8 * ((P.B * P.Hkv + 7) / 8) * ((P.stok + bwd::BKV - 1) / bwd::BKV)
                            : (int64_t)P.Hkv * ((P.stok + bwd::BKV - 1) / bwd::BKV + P.nseq);
-  bwd::dkdv_bf16_kernel<<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);
+  bwd::dkdv_bf16_kernel<0><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);
 }
 
-template <int RH>
+void launch_block_dkdv_bf16(const Prob& P, bool ctx_keys, const uint16_t* v, const float* lse, const uint16_t* dout,
+                            const _Float16* kt, const _Float16* qt, const float* delta, const float* cosT,
+                            const float* sinT, void* dk, void* dv, hipStream_t st) {
+  PassPtrs kv = {};
+  kv.v[0] = v;
+  PassGradPtrs g = {};
+  g.dk[0] = dk;
+  g.dv[0] = dv;
+  const int nkeys = ctx_keys ? P.kv_len : P.stok;
+  const int64_t grid = (int64_t)8 * ((P.B * P.Hkv + 7) / 8) * ((nkeys + bwd::BKV - 1) / bwd::BKV);
+  if (grid == 0) return;
+  if (ctx_keys)
+    bwd::dkdv_bf16_kernel<2><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, nullptr, cosT, sinT, g);
+  else
+    bwd::dkdv_bf16_kernel<3><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, nullptr, cosT, sinT, g);
+}
+
+template <int RH, int MODE>
 static void launch_dq_rh(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
                          const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
-                         const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st) {
+                         const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq,
+                         const _Float16* kbt, const _Float16* kbtt, hipStream_t st) {
   constexpr int RT = bwd::dq_rows(RH);
   const int nsub = P.r / RH;
   int64_t grid;
@@ -707,8 +814,8 @@ static void launch_dq_rh(const Prob& P, const uint16_t* q, const PassPtrs& kv, c
   } else {
     grid = (int64_t)((P.stok + RT - 1) / RT + P.nseq) * P.Hkv * nsub;
   }
-  bwd::dq_bf16_kernel<RH><<<(unsigned)grid, 256, 0, st>>>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT,
-                                                          sinT, dq);
+  bwd::dq_bf16_kernel<RH, MODE><<<(unsigned)grid, 256, 0, st>>>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q,
+                                                                cosT, sinT, dq, kbt, kbtt);
 }
 
 int dq_tile_rows(int r) { return bwd::dq_rows(bwd::dq_heads_per_wg(r)); }
@@ -717,9 +824,23 @@ void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const 
                     const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
                     const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st) {
   switch (bwd::dq_heads_per_wg(P.r)) {
-    case 4: launch_dq_rh<4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, st); break;
-    case 2: launch_dq_rh<2>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, st); break;
-    default: launch_dq_rh<1>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, st); break;
+    case 4: launch_dq_rh<4, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st); break;
+    case 2: launch_dq_rh<2, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st); break;
+    default: launch_dq_rh<1, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st); break;
+  }
+}
+
+void launch_block_dq_bf16(const Prob& P, const uint16_t* v_ctx, const uint16_t* v_blk, const float* lse,
+                          const uint16_t* dout, const _Float16* ckt, const _Float16* cktt, const _Float16* bkt,
+                          const _Float16* bktt, const _Float16* qt, const float* delta, const float* cosT,
+                          const float* sinT, uint16_t* dq, hipStream_t st) {
+  PassPtrs kv = {};
+  kv.v[0] = v_ctx;
+  kv.v[1] = v_blk;
+  switch (bwd::dq_heads_per_wg(P.r)) {
+    case 4: launch_dq_rh<4, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, st); break;
+    case 2: launch_dq_rh<2, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, st); break;
+    default: launch_dq_rh<1, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, st); break;
   }
 }
 

@@ -50,6 +50,7 @@ struct Prob {
   // the forward kernel requires spad_b == spad).
   const int* anchors;
   int bs_log2, nblk, spad_b;
+  int64_t cs_b, cs_t, cs_h;  // block-draft backward: context K/V strides (P.ks_*: the block K/V)
 };
 
 __device__ __forceinline__ int block_anchor(const Prob& P, int b, int row) {

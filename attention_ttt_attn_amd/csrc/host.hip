@@ -424,8 +424,8 @@ int fwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     ttt::PrepJobs J;
     memset(&J, 0, sizeof J);
     J.n = 2;
-    J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, nullptr, 0};
-    J.j[1] = {(const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, 0, 0, 1, nullptr, vt, 0};
+    J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, nullptr, 0, nullptr};
+    J.j[1] = {(const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, 0, 0, 1, nullptr, vt, 0, nullptr};
     TTT_TRACED("prep_kv", ttt::launch_prep_bf16(Pk, J, cosT, sinT, st));
     TTT_TRACED("trunk_fwd",
                ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st));
@@ -469,10 +469,12 @@ namespace {
 struct BlockPlan {
   Plan pl;
   int64_t cs_b, cs_t, cs_h;  // context K/V strides
-  size_t ctx_kt, ctx_vt, blk_kt, blk_vt, total;
+  // forward: context K~ / V^T, block K~ / V^T; backward: context K~ / K~^T,
+  // block K~ / K~^T (in the same four slots), Q~ rows and Delta
+  size_t ctx_kt, ctx_vt, blk_kt, blk_vt, qt, delta, total;
 };
 
-int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan& bp) {
+int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan& bp, bool for_bwd = false) {
   if (!bk) return fail(TTT_ERR_NULL_ARG, "block descriptor is NULL");
   if (bk->struct_size != sizeof(ttt_attn_block))
     return fail(TTT_ERR_ABI, "block struct_size %u != %zu", bk->struct_size, sizeof(ttt_attn_block));
@@ -494,6 +496,7 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
   P.bs_log2 = __builtin_ctz((unsigned)bs);
   P.nblk = P.stok / bs;
   P.anchors = bk->anchors;
+  P.cs_b = 0, P.cs_t = 0, P.cs_h = 0;
   P.npos = ctx + bs;                                   // slot positions a + t <= ctx + bs - 1
   // context and block slabs share one slot count: the kernel's V^T row
   // offsets are computed once for both
@@ -512,6 +515,7 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
     }
     bp.cs_b = s0[0], bp.cs_t = s0[1], bp.cs_h = s0[2];
   }
+  P.cs_b = bp.cs_b, P.cs_t = bp.cs_t, P.cs_h = bp.cs_h;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t at_ = off;
@@ -525,6 +529,11 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
   bp.ctx_vt = take(nc * 2);
   bp.blk_kt = take(nb * 2);
   bp.blk_vt = take(nb * 2);
+  bp.qt = bp.delta = 0;
+  if (for_bwd) {
+    bp.qt = take((size_t)P.B * P.Hq * P.spad * D * 2);
+    bp.delta = take((size_t)P.B * P.Hq * P.spad * 4 + (size_t)P.B * P.spad * 4);  // Delta, then the row lims
+  }
   bp.total = off;
   pl.ws.total = off;
   return TTT_OK;
@@ -533,11 +542,79 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
 
 extern "C" {
 
-size_t ttt_attn_block_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_block* bk) {
+size_t ttt_attn_block_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_block* bk, int for_bwd) {
   g_last_error.clear();
   BlockPlan bp;
-  if (make_block_plan(d, bk, bp) != TTT_OK) return 0;
+  if (make_block_plan(d, bk, bp, for_bwd != 0) != TTT_OK) return 0;
   return bp.total;
+}
+
+int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const void* q, const void* k_ctx,
+                       const void* v_ctx, const void* k_blk, const void* v_blk, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk_ctx, void* dv_ctx, void* dk_blk, void* dv_blk, void* ws,
+                       size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  BlockPlan bp;
+  if (int e = make_block_plan(d, bk, bp, true)) return e;
+  Plan& pl = bp.pl;
+  ttt::Prob& P = pl.P;
+  if (P.stok == 0) return TTT_OK;
+  if (!bk->anchors) return fail(TTT_ERR_NULL_ARG, "anchors is NULL");
+  if ((uintptr_t)bk->anchors & 3u) return fail(TTT_ERR_MISALIGNED, "anchors is not 4-byte aligned");
+  const void* need[] = {q, k_blk, v_blk, o, dout, dq, dk_blk, dv_blk};
+  const char* names[] = {"q", "k_blk", "v_blk", "o", "dout", "dq", "dk_blk", "dv_blk"};
+  for (int i = 0; i < 8; ++i)
+    if (int e = check_ptr(need[i], names[i])) return e;
+  if (P.kv_len > 0) {  // an empty context is never read or written: its pointers may be NULL
+    const void* cneed[] = {k_ctx, v_ctx, dk_ctx, dv_ctx};
+    const char* cnames[] = {"k_ctx", "v_ctx", "dk_ctx", "dv_ctx"};
+    for (int i = 0; i < 4; ++i)
+      if (int e = check_ptr(cneed[i], cnames[i])) return e;
+  }
+  if (!lse) return fail(TTT_ERR_NULL_ARG, "lse is NULL");
+  if ((uintptr_t)lse & 3u) return fail(TTT_ERR_MISALIGNED, "lse is not 4-byte aligned");
+  if (int e = check_ws(pl, ws, ws_bytes)) return e;
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  float* cosT = at<float>(ws, pl.ws.table);
+  float* sinT = cosT + (size_t)P.npos * (P.D / 2);
+  _Float16* ckt = at<_Float16>(ws, bp.ctx_kt);
+  _Float16* cktt = at<_Float16>(ws, bp.ctx_vt);
+  _Float16* bkt = at<_Float16>(ws, bp.blk_kt);
+  _Float16* bktt = at<_Float16>(ws, bp.blk_vt);
+  _Float16* qt = at<_Float16>(ws, bp.qt);
+  float* delta = at<float>(ws, bp.delta);
+  TTT_TRACED("rope_table", ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st));
+  TTT_TRACED("bwd_delta", ttt::launch_delta(P, o, pl.o_f32, dout, false, delta, st));
+  ttt::PrepJobs J;
+  memset(&J, 0, sizeof J);
+  J.n = 1;
+  if (P.kv_len > 0) {  // context: K~ rows and K~^T
+    ttt::Prob Pc = P;
+    Pc.stok = P.kv_len;
+    J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, (uint16_t*)cktt, 0, nullptr};
+    TTT_TRACED("prep_ctx_bwd", ttt::launch_prep_bf16(Pc, J, cosT, sinT, st));
+  }
+  // block keys (K~ rows, K~^T) and queries (Q~ rows) at their slot positions
+  J.n = 2;
+  J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, (uint16_t*)bktt, 1, nullptr};
+  int* lims = (int*)(delta + (size_t)P.B * P.Hq * P.spad);  // per-slot visible context lengths
+  J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, 0, 1, 0, qt, nullptr, 1, lims};
+  TTT_TRACED("prep_blkq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
+  if (P.kv_len > 0) {
+    ttt::Prob Pc = P;  // the context keys' V / dK / dV strides
+    Pc.ks_b = bp.cs_b, Pc.ks_t = bp.cs_t, Pc.ks_h = bp.cs_h;
+    TTT_TRACED("block_dkdv_ctx", ttt::launch_block_dkdv_bf16(Pc, true, (const uint16_t*)v_ctx, lse,
+                                                             (const uint16_t*)dout, ckt, qt, delta, cosT, sinT,
+                                                             dk_ctx, dv_ctx, st));
+  }
+  TTT_TRACED("block_dkdv_blk", ttt::launch_block_dkdv_bf16(P, false, (const uint16_t*)v_blk, lse,
+                                                           (const uint16_t*)dout, bkt, qt, delta, cosT, sinT, dk_blk,
+                                                           dv_blk, st));
+  TTT_TRACED("block_dq", ttt::launch_block_dq_bf16(P, (const uint16_t*)v_ctx, (const uint16_t*)v_blk, lse,
+                                                   (const uint16_t*)dout, ckt, cktt, bkt, bktt, qt, delta, cosT,
+                                                   sinT, (uint16_t*)dq, st));
+  return hip_check("ttt_attn_block_bwd launch");
 }
 
 int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const void* q, const void* k_ctx,
@@ -577,14 +654,14 @@ int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   ttt::PrepJobs J;
   memset(&J, 0, sizeof J);
   J.n = 2;
-  J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, nullptr, 0};
-  J.j[1] = {(const uint16_t*)v_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 0, 1, nullptr, cvt, 0};
+  J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, nullptr, 0, nullptr};
+  J.j[1] = {(const uint16_t*)v_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 0, 1, nullptr, cvt, 0, nullptr};
   TTT_TRACED("prep_ctx", ttt::launch_prep_bf16(Pc, J, cosT, sinT, st));
   // block keys: K~ rows at their slot positions and V^T (spad_b slots)
   ttt::Prob Pb = P;
   Pb.spad = P.spad_b;
-  J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, nullptr, 1};
-  J.j[1] = {(const uint16_t*)v_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 0, 1, nullptr, bvt, 0};
+  J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, nullptr, 1, nullptr};
+  J.j[1] = {(const uint16_t*)v_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 0, 1, nullptr, bvt, 0, nullptr};
   TTT_TRACED("prep_blk", ttt::launch_prep_bf16(Pb, J, cosT, sinT, st));
   TTT_TRACED("block_fwd", ttt::launch_block_fwd_bf16(P, (const uint16_t*)q, ckt, cvt, bkt, bvt, cosT, sinT, o,
                                                      pl.o_f32, lse, st));
@@ -698,8 +775,8 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
     ttt::PrepJobs J;
     memset(&J, 0, sizeof J);
     J.n = 2;
-    J.j[0] = {(const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, kt, (uint16_t*)ktt, 0};
-    J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, 1, 0, qt, nullptr, 0};
+    J.j[0] = {(const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, kt, (uint16_t*)ktt, 0, nullptr};
+    J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, 1, 0, qt, nullptr, 0, nullptr};
     TTT_TRACED("prep_kq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
     if (forked) sd.wait(st, delta_done);
     if (forked && P.p > 1) sd.wait(sd.side, sd.mark(st));  // start the branch kernel with dK/dV, not beside the prologue

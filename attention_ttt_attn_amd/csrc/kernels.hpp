@@ -20,6 +20,7 @@ struct PrepJob {
   _Float16* out_row;
   uint16_t* out_col;
   int pos_anchor;
+  int* out_lim;  // pos_anchor jobs: per slot [(b)][spad] the clamped anchor of the row's block (0 past the end)
 };
 struct PrepJobs {
   PrepJob j[2];
@@ -43,6 +44,18 @@ int fwd_tile_rows(int r);
 // Block-draft forward (BSHD, D = 128): context K~ / V^T in kt / vt (P.spad
 // slots), block K~ / V^T in kbt / vbt (P.spad_b slots); P.anchors, P.bs_log2,
 // P.nblk, P.kv_len (context rows) describe the blocks.
+// Block-draft backward (BSHD, D = 128; P as for the forward, P.ks_* the
+// block K/V strides, P.cs_* the context ones).  dK/dV of the context keys
+// (ctx_keys, kt = context K~ slab, v = context V) or of the block keys (kt =
+// block K~ slab, v = block V); P.ks_* must then be the strides of v/dk/dv.
+void launch_block_dkdv_bf16(const Prob& P, bool ctx_keys, const uint16_t* v, const float* lse, const uint16_t* dout,
+                            const _Float16* kt, const _Float16* qt, const float* delta, const float* cosT,
+                            const float* sinT, void* dk, void* dv, hipStream_t st);
+// dQ: context keys (ckt, cktt, v_ctx) up to each row's anchor, then its block's keys (bkt, bktt, v_blk).
+void launch_block_dq_bf16(const Prob& P, const uint16_t* v_ctx, const uint16_t* v_blk, const float* lse,
+                          const uint16_t* dout, const _Float16* ckt, const _Float16* cktt, const _Float16* bkt,
+                          const _Float16* bktt, const _Float16* qt, const float* delta, const float* cosT,
+                          const float* sinT, uint16_t* dq, hipStream_t st);
 void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const uint16_t* vt,
                            const _Float16* kbt, const uint16_t* vbt, const float* cosT, const float* sinT, void* o,
                            bool o_f32, float* lse, hipStream_t st);     // query rows per forward work item for GQA ratio r (32, 64 or 128)

@@ -229,9 +229,10 @@ def ring_main(args, w, dev):
 
 
 def block_main(args, dev):
-    """Block-draft forward: 256 blocks of 16 slots per batch row over a 4096-token context
-    (B=4, Hq=32, Hkv=8, D=128).  Useful FLOPs: 4*D per (slot, head, visible key), the
-    visible keys of a slot being its block's context prefix plus the bs block keys."""
+    """Block-draft forward + backward: 256 blocks of 16 slots per batch row over a 4096-token
+    context (B=4, Hq=32, Hkv=8, D=128).  Useful FLOPs: forward 4*D per (slot, head, visible
+    key), the visible keys of a slot being its block's context prefix plus the bs block
+    keys; backward 2.5x that."""
     import numpy as np
     import torch
 
@@ -251,8 +252,15 @@ def block_main(args, dev):
     lse = torch.empty((bw.B, bw.Hq, bw.rows), dtype=torch.float32, device=dev)
     ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     pairs = int((np.clip(anchors, 0, bw.ctx_len).astype(np.int64) + bw.bs).sum()) * bw.bs   # per head
-    flops = 4.0 * bw.D * bw.Hq * pairs
-    run = lambda: tk.block_fwd(q, kc, vc, kb, vb, ga, bw.bs, rope_base=bw.rope_base, out=o, lse=lse, workspace=ws)
+    flops_f = 4.0 * bw.D * bw.Hq * pairs
+    flops = 3.5 * flops_f
+    do = syn.draw_device(w, syn.KIND_DO, 1, dev, bw.q_shape())
+    grads = [torch.empty_like(t) for t in (q, kc, vc, kb, vb)]
+
+    def run():
+        tk.block_fwd(q, kc, vc, kb, vb, ga, bw.bs, rope_base=bw.rope_base, out=o, lse=lse, workspace=ws)
+        tk.block_bwd(q, kc, vc, kb, vb, ga, bw.bs, o, lse, do, rope_base=bw.rope_base, dq=grads[0], dk_ctx=grads[1],
+                     dv_ctx=grads[2], dk_blk=grads[3], dv_blk=grads[4], workspace=ws)
     for _ in range(max(args.warmup, 1)):
         run()
     torch.cuda.synchronize()
@@ -285,20 +293,27 @@ def block_main(args, dev):
         k[1] += a.elapsed_time(b)
     kern = {k: {"avg_us": round(v[1] * 1e3 / v[0], 2), "launches_per_call": v[0] // n} for k, v in ks.items()}
     fwd_us = kern["block_fwd"]["avg_us"]
-    achieved = flops / (fwd_us * 1e-6)
+    achieved = flops_f / (fwd_us * 1e-6)
+    kern["block_fwd"]["tflops"] = round(achieved / 1e12, 1)
+    # dK/dV of the context keys: S, dP, dV, dK over the context pairs; dQ: S, dP, dQ over all pairs
+    ctx_pairs = int(np.clip(anchors, 0, bw.ctx_len).astype(np.int64).sum()) * bw.bs
+    for name, f in (("block_dkdv_ctx", 8.0 * bw.D * bw.Hq * ctx_pairs), ("block_dq", 6.0 * bw.D * bw.Hq * pairs)):
+        if name in kern:
+            kern[name]["tflops"] = round(f / (kern[name]["avg_us"] * 1e-6) / 1e12, 1)
     row_kv = bw.Hkv * bw.D * 2
     kern["prep_ctx"]["gbps"] = round(bw.B * bw.ctx_len * row_kv * 4 / (kern["prep_ctx"]["avg_us"] * 1e-6) / 1e9, 1)
     kern["prep_blk"]["gbps"] = round(bw.B * bw.rows * row_kv * 4 / (kern["prep_blk"]["avg_us"] * 1e-6) / 1e9, 1)
     value = flops / (call_ms * 1e-3) / 1e12
-    out = {"metric": "block-draft attention fwd TFLOP/s (useful FLOPs)", "value": round(value, 2), "unit": "TFLOP/s",
+    out = {"metric": "block-draft attention fwd+bwd TFLOP/s (useful FLOPs)", "value": round(value, 2),
+           "unit": "TFLOP/s", "frac_of_peak": round(value * 1e12 / PEAK_MFMA_BF16, 4),
            "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(call_ms, 4), "higher_is_better": True,
            "dtype": "bf16", "data": "synthetic",
            "config": {"workload": bw.name, "batch": bw.B, "ctx_len": bw.ctx_len, "block_size": bw.bs,
                       "blocks": bw.nblk, "q_heads": bw.Hq, "kv_heads": bw.Hkv, "head_dim": bw.D,
-                      "useful_tflop_per_call": round(flops / 1e12, 4)},
+                      "step": "forward then backward", "useful_tflop_per_step": round(flops / 1e12, 4)},
            "roofline": {"kernel": "block_fwd", "bound": "mfma", "achieved": round(achieved / 1e12, 2),
                         "peak": 2500.0, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16, 4),
-                        "traffic": None, "work_per_launch": flops, "avg_launch_us": fwd_us},
+                        "traffic": None, "work_per_launch": flops_f, "avg_launch_us": fwd_us},
            "kernels": kern, "source_digest": source_digest()}
     print(json.dumps(out), flush=True)
 

@@ -198,8 +198,9 @@ typedef struct ttt_attn_block {
                                  zero triple selects the contiguous [B, ctx_len, Hkv, D]   */
 } ttt_attn_block;
 
-/* Bytes of workspace ttt_attn_block_fwd needs (0 and the last error if invalid). */
-size_t ttt_attn_block_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_block* blk);
+/* Bytes of workspace ttt_attn_block_fwd (for_bwd = 0) or ttt_attn_block_bwd
+ * (for_bwd != 0) needs (0 and the last error if invalid). */
+size_t ttt_attn_block_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_block* blk, int for_bwd);
 
 /* Forward of block-draft attention.  q [B, seqlen, Hq, D]; k_ctx, v_ctx the
  * context keys/values (may be NULL when ctx_len = 0); k_blk, v_blk the block
@@ -208,6 +209,17 @@ size_t ttt_attn_block_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_blo
  * not read on the host.  Returns a ttt_attn_status. */
 int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* blk, const void* q, const void* k_ctx,
                        const void* v_ctx, const void* k_blk, const void* v_blk, void* o, float* lse, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Backward of block-draft attention, recomputing probabilities from the
+ * forward's LSE (no gradient flows into LSE).  o, lse: the forward's outputs;
+ * dout: gradient of o (o's dtype and strides).  Outputs (overwritten): dq
+ * (q's strides), dk_ctx / dv_ctx (ctx_stride; GQA: summed over the heads of
+ * a group; may be NULL when ctx_len = 0), dk_blk / dv_blk (kv_stride).
+ * Any anchor order; the workspace is ttt_attn_block_workspace_bytes(d, blk, 1). */
+int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* blk, const void* q, const void* k_ctx,
+                       const void* v_ctx, const void* k_blk, const void* v_blk, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk_ctx, void* dv_ctx, void* dk_blk, void* dv_blk, void* ws,
                        size_t ws_bytes, void* stream);
 
 /* Static text of a status code. */

@@ -321,8 +321,10 @@ def test_block_validation():
     bk = good_block()
     bk.ctx_stride[:] = (300 * 256, 256, 100)
     assert call_block(d, bk) == 4 and "ctx stride" in err()
-    need = lib.ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(good_block()))
+    need = lib.ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(good_block()), 0)
     assert need > 0 and call_block(d, good_block(), ws_bytes=need - 1) == 5
+    need_b = lib.ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(good_block()), 1)
+    assert need_b > need
 
 
 def test_block_empty_context_pointers_may_be_null():
@@ -334,6 +336,29 @@ def test_block_empty_context_pointers_may_be_null():
 
 def test_block_workspace_grows():
     lib = tk.library()
-    w = lambda d, bk: lib.ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(bk))
+    w = lambda d, bk: lib.ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(bk), 0)
     assert w(block_desc(128), good_block(ctx_len=4096)) > w(block_desc(128), good_block(ctx_len=64))
     assert w(block_desc(4096), good_block()) > w(block_desc(128), good_block())
+
+
+def call_block_bwd(d, bk, **kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, kb=FAKE, vb=FAKE, o=FAKE, lse=FAKE, dout=FAKE, dq=FAKE, dkc=FAKE, dvc=FAKE,
+             dkb=FAKE, dvb=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return tk.library().ttt_attn_block_bwd(ctypes.byref(d), ctypes.byref(bk), a["q"], a["kc"], a["vc"], a["kb"],
+                                           a["vb"], a["o"], a["lse"], a["dout"], a["dq"], a["dkc"], a["dvc"],
+                                           a["dkb"], a["dvb"], a["ws"], a["ws_bytes"], None)
+
+
+def test_block_bwd_validation():
+    d = block_desc()
+    assert call_block_bwd(d, good_block(bs=3)) == 3
+    for name in ("q", "kb", "vb", "o", "dout", "dq", "dkb", "dvb"):
+        assert call_block_bwd(d, good_block(), **{name: None}) == 1, name
+    for name in ("kc", "vc", "dkc", "dvc"):
+        assert call_block_bwd(d, good_block(), **{name: None}) == 1, name
+        # an empty context is never touched: NULL passes, and the call stops at the workspace check
+        assert call_block_bwd(d, good_block(ctx_len=0), ws_bytes=16, **{name: None}) == 5, name
+    assert call_block_bwd(d, good_block(), lse=FAKE + 2) == 4
+    assert call_block_bwd(d, good_block(anchors=None)) == 1
+    assert call_block_bwd(d, good_block(), ws_bytes=100) == 5
