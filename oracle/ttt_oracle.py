@@ -54,6 +54,16 @@ What is computed (one call = one TTT pass p, 1-based):
   `block_bwd` the gradients of q, the context K/V and the block K/V by the
   same chain rule as the TTT backward below.
 
+* Distillation loss (issue above, item 3: chunked soft cross-entropy, normalised
+  per pass over the whole batch; PR #3725 self-review: teacher_offset =
+  pass_index + 1).  Reading: pass p's student logits at row i are scored
+  against the teacher distribution softmax(teacher logits at row i + offset) of
+  the same sequence, offset = p for 1-based p; rows with no such teacher row or
+  with mask 0 are not counted; loss = (sum of counted rows' cross-entropies) /
+  (number of counted rows).  The gradient is (softmax(student) - teacher
+  distribution) / count on counted rows and 0 elsewhere.  Chunking the tokens
+  only bounds memory and does not change the value.
+
 * Ring steps (issue above, item 4: context parallelism, where pass-1 K/V
   travel around a zig-zag ring and partial results are joined by the joint-LSE
   merge): `fwd_chunk` is the attention of a block of query rows at sequence
@@ -77,7 +87,7 @@ import numpy as np
 __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_position",
            "ttt_mask_row", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows", "Slice",
            "fwd_chunk", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd",
-           "block_bwd_rows", "block_bwd"]
+           "block_bwd_rows", "block_bwd", "soft_ce_rows_counted", "soft_ce"]
 
 
 # ----------------------------------------------------------------------------- RoPE
@@ -534,3 +544,38 @@ def block_bwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, dout, *, scale: O
             dKb[b, :, h // r] += dkb
             dVb[b, :, h // r] += dvb
     return dQ, dKc, dVc, dKb, dVb
+
+
+# ----------------------------------------------------------------------------- distillation loss
+def soft_ce_rows_counted(B: int, S: int, offset: int, mask=None) -> np.ndarray:
+    """bool [B, S]: row i is counted iff row i + offset exists in its sequence and mask[b, i] != 0."""
+    i = np.arange(S)[None, :].repeat(B, axis=0)
+    ok = i + offset < S
+    if mask is not None:
+        ok = ok & (np.asarray(mask) != 0)
+    return ok
+
+
+def soft_ce(student, teacher, offset: int, mask=None):
+    """Per-pass soft cross-entropy.  student, teacher: [B, S, V] logits.  Returns
+    (loss, grad [B, S, V], row_ce [B, S]) in fp64 (row_ce is 0 on rows not counted)."""
+    s = np.asarray(student, np.float64)
+    t = np.asarray(teacher, np.float64)
+    B, S, V = s.shape
+    counted = soft_ce_rows_counted(B, S, offset, mask)
+    n = int(counted.sum())
+    row_ce = np.zeros((B, S))
+    grad = np.zeros((B, S, V))
+    for b in range(B):
+        for i in range(S):
+            if not counted[b, i]:
+                continue
+            x = s[b, i]
+            y = t[b, i + offset]
+            lx = x.max() + math.log(np.exp(x - x.max()).sum())          # log-sum-exp of the student row
+            py = np.exp(y - y.max())
+            py /= py.sum()                                               # teacher distribution
+            row_ce[b, i] = -(py * (x - lx)).sum()
+            grad[b, i] = (np.exp(x - lx) - py) / n
+    loss = row_ce.sum() / n if n else 0.0
+    return loss, grad, row_ce

@@ -477,13 +477,60 @@ def check_block_grad_autograd():
         assert np.max(np.abs(mine[0] - t.grad.numpy())) < 1e-10
 
 
+def check_soft_ce_library():
+    """Row cross-entropies == torch cross_entropy with probability targets; the gradient
+    == fp64 autograd of the mean over counted rows; offset and mask select the rows."""
+    rng = np.random.default_rng(91)
+    B, S, V, off = 2, 9, 13, 3
+    st = rng.standard_normal((B, S, V)) * 2
+    te = rng.standard_normal((B, S, V)) * 2
+    mask = np.ones((B, S), dtype=np.uint8)
+    mask[1, 2] = 0
+    loss, grad, row_ce = O.soft_ce(st, te, off, mask)
+    rows = [(b, i) for b in range(B) for i in range(S) if i + off < S and mask[b, i]]
+    x = torch.tensor(st, requires_grad=True)
+    xs = torch.stack([x[b, i] for b, i in rows])
+    tg = torch.softmax(torch.stack([torch.tensor(te[b, i + off]) for b, i in rows]), -1)
+    ce = torch.nn.functional.cross_entropy(xs, tg, reduction="none")
+    ref = ce.mean()
+    ref.backward()
+    assert abs(loss - ref.item()) < 1e-12
+    assert np.max(np.abs(grad - x.grad.numpy())) < 1e-12
+    assert np.max(np.abs(np.array([row_ce[b, i] for b, i in rows]) - ce.detach().numpy())) < 1e-12
+    assert np.all(row_ce[:, S - off:] == 0) and row_ce[1, 2] == 0
+
+
+def check_soft_ce_closed_forms():
+    """A one-hot teacher gives the hard cross-entropy lse(s) - s[label]; a constant
+    student row gives ln V; student == teacher gives the teacher's entropy."""
+    rng = np.random.default_rng(92)
+    B, S, V, off = 1, 5, 11, 1
+    st = rng.standard_normal((B, S, V))
+    te = np.full((B, S, V), -1e4)
+    labels = rng.integers(0, V, S)
+    te[0, np.arange(S), labels] = 0.0
+    _, _, row_ce = O.soft_ce(st, te, off)
+    for i in range(S - off):
+        x = st[0, i]
+        lse = math.log(np.exp(x).sum())
+        assert abs(row_ce[0, i] - (lse - x[labels[i + off]])) < 1e-9
+    const = np.zeros((B, S, V))
+    _, _, rc = O.soft_ce(const, rng.standard_normal((B, S, V)), off)
+    assert np.max(np.abs(rc[0, :S - off] - math.log(V))) < 1e-12
+    y = rng.standard_normal((B, S, V))
+    _, _, rc2 = O.soft_ce(np.roll(y, -off, axis=1), y, off)  # student row i equals teacher row i + offset
+    p = np.exp(y) / np.exp(y).sum(-1, keepdims=True)
+    ent = -(p * np.log(p)).sum(-1)
+    assert np.max(np.abs(rc2[0, :S - off] - ent[0, off:])) < 1e-12
+
+
 PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check_zero_query_closed_form,
         lambda: check_zero_query_closed_form("thd"), check_sdpa_brute_force, check_p1_is_causal_sdpa,
         check_merge_invariant, check_branch_relative_position, check_grad_autograd,
         check_grad_finite_difference, check_thd_equals_bshd, check_thd_isolation, check_gqa_is_repeated_kv,
         check_sampled_rows_match_full, check_chunk_rows_match_dense, check_chunk_ring_partition,
         check_merge_closed_form, check_block_sdpa_mask, check_block_zero_query_closed_form,
-        check_block_size1_is_causal, check_block_grad_autograd]
+        check_block_size1_is_causal, check_block_grad_autograd, check_soft_ce_library, check_soft_ce_closed_forms]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
@@ -571,6 +618,8 @@ MISTAKES = [
     ("block_visible_ctx", lambda a, L: int(min(max(a + 1, 0), L))),
     ("block_slot_position", lambda a, t: int(a) + np.asarray(t) + 1),
     ("block_slot_position", lambda a, t: np.asarray(t)),
+    ("soft_ce_rows_counted", lambda B, S, off, mask=None: np.arange(S)[None, :].repeat(B, 0) + off <= S),
+    ("soft_ce_rows_counted", lambda B, S, off, mask=None: np.ones((B, S), dtype=bool) & (np.arange(S)[None, :] + off < S)),
     ("merge", lambda oa, la, ob, lb: (_orig_merge(oa, la, ob, lb)[0], np.maximum(la, lb))),
 ]
 
