@@ -77,6 +77,21 @@ class Block(ctypes.Structure):
     ]
 
 
+class SoftCeDesc(ctypes.Structure):
+    """Per-pass soft cross-entropy shape (ttt_soft_ce_desc)."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("batch", ctypes.c_int32),
+        ("seqlen", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("teacher_offset", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("student_stride", ctypes.c_int64 * 2),
+        ("teacher_stride", ctypes.c_int64 * 2),
+        ("mask", ctypes.c_void_p),
+    ]
+
+
 # void (*)(void* user, const char* kernel, int phase, void* stream)
 TRACE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_char_p, ctypes.c_int, ctypes.c_void_p)
 _trace_ref = None
@@ -136,6 +151,12 @@ def library() -> ctypes.CDLL:
         lib.ttt_attn_block_fwd.restype = ctypes.c_int
         lib.ttt_attn_block_bwd.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Block)] + [vp] * 14 + [sz, vp]
         lib.ttt_attn_block_bwd.restype = ctypes.c_int
+        lib.ttt_soft_ce_workspace_bytes.argtypes = [ctypes.POINTER(SoftCeDesc)]
+        lib.ttt_soft_ce_workspace_bytes.restype = sz
+        lib.ttt_soft_ce_fwd.argtypes = [ctypes.POINTER(SoftCeDesc), vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.ttt_soft_ce_fwd.restype = ctypes.c_int
+        lib.ttt_soft_ce_bwd.argtypes = [ctypes.POINTER(SoftCeDesc), vp, vp, vp, vp, vp, vp, vp]
+        lib.ttt_soft_ce_bwd.restype = ctypes.c_int
         lib.ttt_attn_status_string.argtypes = [ctypes.c_int]
         lib.ttt_attn_status_string.restype = ctypes.c_char_p
         lib.ttt_attn_last_error.argtypes = []
@@ -436,3 +457,47 @@ def block_bwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, o, lse, d
                                         dout.data_ptr(), dq.data_ptr(), ptr(dk_ctx), ptr(dv_ctx), dk_blk.data_ptr(),
                                         dv_blk.data_ptr(), wp, wn, _stream(stream)))
     return dq, dk_ctx, dv_ctx, dk_blk, dv_blk
+
+
+def make_soft_ce_desc(student, teacher, teacher_offset: int, mask=None) -> SoftCeDesc:
+    d = SoftCeDesc()
+    d.struct_size = ctypes.sizeof(SoftCeDesc)
+    d.batch, d.seqlen, d.vocab = student.shape
+    if tuple(teacher.shape) != tuple(student.shape):
+        raise ValueError("student and teacher logits must have the same [B, S, V] shape")
+    if student.stride(-1) != 1 or teacher.stride(-1) != 1:
+        raise ValueError("the vocab axis must be contiguous")
+    d.teacher_offset = int(teacher_offset)
+    d.student_stride[:] = student.stride()[:2]
+    d.teacher_stride[:] = teacher.stride()[:2]
+    d.mask = mask.data_ptr() if mask is not None else None
+    return d
+
+
+def soft_ce_fwd(student, teacher, teacher_offset: int, *, mask=None, row_ce=None, stream=None):
+    """Per-pass soft cross-entropy.  student, teacher: bf16 [B, S, V]; mask: uint8 [B, S] or None.
+    Returns (stats [2] = (loss, counted rows), row_lse [B, S, 2], row_ce [B, S])."""
+    torch = _torch()
+    d = make_soft_ce_desc(student, teacher, teacher_offset, mask)
+    B, S, _ = student.shape
+    stats = torch.empty(2, dtype=torch.float32, device=student.device)
+    row_lse = torch.empty((B, S, 2), dtype=torch.float32, device=student.device)
+    if row_ce is None:
+        row_ce = torch.empty((B, S), dtype=torch.float32, device=student.device)
+    _check(library().ttt_soft_ce_fwd(ctypes.byref(d), student.data_ptr(), teacher.data_ptr(), stats.data_ptr(),
+                                     row_lse.data_ptr(), row_ce.data_ptr(), None, 0, _stream(stream)))
+    return stats, row_lse, row_ce
+
+
+def soft_ce_bwd(student, teacher, teacher_offset: int, row_lse, stats, dloss, *, mask=None, dstudent=None,
+                stream=None):
+    """Gradient of the loss with respect to the student logits (bf16, student strides)."""
+    torch = _torch()
+    d = make_soft_ce_desc(student, teacher, teacher_offset, mask)
+    if dstudent is None:
+        dstudent = torch.empty_strided(student.shape, student.stride(), dtype=student.dtype, device=student.device)
+    if dstudent.stride() != student.stride():
+        raise ValueError("dstudent must have the strides of student")
+    _check(library().ttt_soft_ce_bwd(ctypes.byref(d), student.data_ptr(), teacher.data_ptr(), row_lse.data_ptr(),
+                                     stats.data_ptr(), dloss.data_ptr(), dstudent.data_ptr(), _stream(stream)))
+    return dstudent

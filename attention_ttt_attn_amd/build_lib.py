@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtttattn.so")
-SOURCES = ["host.hip", "prep.hip", "attn_f32.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip"]
+SOURCES = ["host.hip", "prep.hip", "attn_f32.hip", "attn_fwd_bf16.hip", "attn_bwd_bf16.hip", "soft_ce.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -668,6 +668,98 @@ int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   return hip_check("ttt_attn_block_fwd launch");
 }
 
+}  // extern "C"
+
+namespace {
+int make_ce(const ttt_soft_ce_desc* d, ttt::CeProb& C) {
+  if (!d) return fail(TTT_ERR_NULL_ARG, "soft-CE descriptor is NULL");
+  if (d->struct_size != sizeof(ttt_soft_ce_desc))
+    return fail(TTT_ERR_ABI, "soft-CE struct_size %u != %zu", d->struct_size, sizeof(ttt_soft_ce_desc));
+  if (d->batch < 1 || d->seqlen < 0 || (int64_t)d->batch * d->seqlen > ((int64_t)1 << 31) - 1)
+    return fail(TTT_ERR_BAD_SHAPE, "batch %d / seqlen %d", d->batch, d->seqlen);
+  if (d->vocab < 8 || d->vocab % 8)
+    return fail(TTT_ERR_BAD_SHAPE, "vocab %d must be a positive multiple of 8", d->vocab);
+  if (d->teacher_offset < 0) return fail(TTT_ERR_BAD_SHAPE, "teacher_offset %d is negative", d->teacher_offset);
+  memset(&C, 0, sizeof C);
+  C.B = d->batch, C.S = d->seqlen, C.V = d->vocab, C.offset = d->teacher_offset, C.mask = d->mask;
+  auto st = [&](const int64_t* s, int64_t& sb, int64_t& sr, const char* name) -> int {
+    if (s[0] == 0 && s[1] == 0) {
+      sb = (int64_t)d->seqlen * d->vocab, sr = d->vocab;
+      return 0;
+    }
+    if (s[0] < 0 || s[1] < d->vocab)
+      return fail(TTT_ERR_BAD_SHAPE, "%s strides (%lld, %lld): row stride below the vocab", name, (long long)s[0],
+                  (long long)s[1]);
+    if (s[0] % 8 || s[1] % 8)
+      return fail(TTT_ERR_MISALIGNED, "%s strides (%lld, %lld) not multiples of 8 elements", name, (long long)s[0],
+                  (long long)s[1]);
+    sb = s[0], sr = s[1];
+    return 0;
+  };
+  if (int e = st(d->student_stride, C.ss_b, C.ss_t, "student")) return e;
+  if (int e = st(d->teacher_stride, C.ts_b, C.ts_t, "teacher")) return e;
+  return TTT_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t ttt_soft_ce_workspace_bytes(const ttt_soft_ce_desc* d) {
+  g_last_error.clear();
+  ttt::CeProb C;
+  if (make_ce(d, C)) return 0;
+  return align256((size_t)C.B * C.S * sizeof(float));
+}
+
+int ttt_soft_ce_fwd(const ttt_soft_ce_desc* d, const void* student, const void* teacher, float* stats,
+                    float* row_lse, float* row_ce, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  ttt::CeProb C;
+  if (int e = make_ce(d, C)) return e;
+  if (!stats || !row_lse) return fail(TTT_ERR_NULL_ARG, "stats or row_lse is NULL");
+  if (((uintptr_t)stats | (uintptr_t)row_lse | (uintptr_t)row_ce) & 3u)
+    return fail(TTT_ERR_MISALIGNED, "stats, row_lse and row_ce must be 4-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  if (C.S > 0) {
+    if (int e = check_ptr(student, "student")) return e;
+    if (int e = check_ptr(teacher, "teacher")) return e;
+    if (!row_ce) {
+      const size_t need = (size_t)C.B * C.S * sizeof(float);
+      if (!ws) return fail(TTT_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed for row_ce)", need);
+      if ((uintptr_t)ws & 255u) return fail(TTT_ERR_WORKSPACE, "workspace %p is not 256-byte aligned", ws);
+      if (ws_bytes < need) return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes is smaller than %zu", ws_bytes, need);
+      row_ce = (float*)ws;
+    }
+  }
+  (void)hipGetLastError();
+  if (C.S == 0) {
+    TTT_TRACED("soft_ce_mean", ttt::launch_soft_ce_fwd(C, nullptr, nullptr, row_lse, row_ce, stats, st));
+  } else {
+    TTT_TRACED("soft_ce_fwd", ttt::launch_soft_ce_fwd(C, (const uint16_t*)student, (const uint16_t*)teacher, row_lse,
+                                                      row_ce, stats, st));
+  }
+  return hip_check("ttt_soft_ce_fwd launch");
+}
+
+int ttt_soft_ce_bwd(const ttt_soft_ce_desc* d, const void* student, const void* teacher, const float* row_lse,
+                    const float* stats, const float* dloss, void* dstudent, void* stream) {
+  g_last_error.clear();
+  ttt::CeProb C;
+  if (int e = make_ce(d, C)) return e;
+  if (C.S == 0) return TTT_OK;
+  if (int e = check_ptr(student, "student")) return e;
+  if (int e = check_ptr(teacher, "teacher")) return e;
+  if (int e = check_ptr(dstudent, "dstudent")) return e;
+  if (!row_lse || !stats || !dloss) return fail(TTT_ERR_NULL_ARG, "row_lse, stats or dloss is NULL");
+  if (((uintptr_t)row_lse | (uintptr_t)stats | (uintptr_t)dloss) & 3u)
+    return fail(TTT_ERR_MISALIGNED, "row_lse, stats and dloss must be 4-byte aligned");
+  hipStream_t st = (hipStream_t)stream;
+  (void)hipGetLastError();
+  TTT_TRACED("soft_ce_bwd", ttt::launch_soft_ce_bwd(C, (const uint16_t*)student, (const uint16_t*)teacher, row_lse,
+                                                    stats, dloss, (uint16_t*)dstudent, st));
+  return hip_check("ttt_soft_ce_bwd launch");
+}
+
 int ttt_attn_merge(const ttt_attn_desc* d, const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                    void* o, float* lse, void* stream) {
   g_last_error.clear();

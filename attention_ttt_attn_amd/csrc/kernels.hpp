@@ -56,6 +56,17 @@ void launch_block_dq_bf16(const Prob& P, const uint16_t* v_ctx, const uint16_t* 
                           const uint16_t* dout, const _Float16* ckt, const _Float16* cktt, const _Float16* bkt,
                           const _Float16* bktt, const _Float16* qt, const float* delta, const float* cosT,
                           const float* sinT, uint16_t* dq, hipStream_t st);
+// Per-pass soft cross-entropy (bf16 logits [B][S][V], vocab contiguous, V % 8 == 0).
+struct CeProb {
+  int B, S, V, offset;
+  const uint8_t* mask;  // [B][S] or null
+  int64_t ss_b, ss_t, ts_b, ts_t;
+};
+// row_lse [B*S][2] (student, teacher), row_ce [B*S], stats [2] = (mean loss, counted rows)
+void launch_soft_ce_fwd(const CeProb& C, const uint16_t* s, const uint16_t* t, float* row_lse, float* row_ce,
+                        float* stats, hipStream_t st);
+void launch_soft_ce_bwd(const CeProb& C, const uint16_t* s, const uint16_t* t, const float* row_lse,
+                        const float* stats, const float* dloss, uint16_t* g, hipStream_t st);
 void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const uint16_t* vt,
                            const _Float16* kbt, const uint16_t* vbt, const float* cosT, const float* sinT, void* o,
                            bool o_f32, float* lse, hipStream_t st);     // query rows per forward work item for GQA ratio r (32, 64 or 128)

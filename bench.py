@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--block", action="store_true",
                     help="instead of the unroll, time the block-draft forward on the blk_b4_c4k shape "
                          "(prints its own JSON line)")
+    ap.add_argument("--soft-ce", action="store_true",
+                    help="instead of the attention unroll, time the per-pass soft cross-entropy (forward + "
+                         "backward for passes 1..7) on B=4, S=4096, V=32000 bf16 logits (prints its own JSON line)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, copy a 256 MiB buffer 3 times (a plain copy kernel of known size "
                          "that scales the HBM byte counters of a profiler run)")
@@ -318,6 +321,76 @@ def block_main(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def soft_ce_main(args, dev):
+    """Per-pass soft cross-entropy over a K=7 unroll: pass p scores its student logits against the
+    teacher rows p ahead.  HBM-bound: forward reads student + teacher once, backward reads them
+    again and writes the gradient (algorithmic bytes, counted rows only for the reads)."""
+    import torch
+
+    import attention_ttt_attn_amd as tk
+
+    B, S, V, K = 4, 4096, 32000, 7
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(60)
+    teacher = (torch.randn((B, S, V), generator=gen, device=dev) * 2).to(torch.bfloat16)
+    students = [(torch.randn((B, S, V), generator=gen, device=dev) * 2).to(torch.bfloat16) for _ in range(K)]
+    grads = [torch.empty_like(x) for x in students]
+    dloss = torch.ones(1, device=dev)
+
+    def step():
+        for p in range(1, K + 1):
+            stats, row_lse, _ = tk.soft_ce_fwd(students[p - 1], teacher, p)
+            tk.soft_ce_bwd(students[p - 1], teacher, p, row_lse, stats, dloss, dstudent=grads[p - 1])
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    events = []
+    cur = torch.cuda.current_stream()
+
+    def hook(name, phase, stream):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(cur)
+        if phase == 0:
+            events.append([name, ev, None])
+        else:
+            events[-1][2] = ev
+
+    n = max(args.steps, 1)
+    tk.set_trace_hook(hook)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    tk.set_trace_hook(None)
+    ms = e0.elapsed_time(e1) / n
+    rows = sum(B * (S - p) for p in range(1, K + 1))
+    fwd_bytes = rows * V * 2 * 2
+    bwd_bytes = rows * V * 2 * 2 + B * S * V * 2 * K
+    ks = {}
+    for name, a, b in events:
+        k = ks.setdefault(name, [0, 0.0])
+        k[0] += 1
+        k[1] += a.elapsed_time(b)
+    kern = {k: {"avg_us": round(v[1] * 1e3 / v[0], 2)} for k, v in ks.items()}
+    kern["soft_ce_fwd"]["gbps"] = round(fwd_bytes / K / (kern["soft_ce_fwd"]["avg_us"] * 1e-6) / 1e9, 1)
+    kern["soft_ce_bwd"]["gbps"] = round(bwd_bytes / K / (kern["soft_ce_bwd"]["avg_us"] * 1e-6) / 1e9, 1)
+    value = (fwd_bytes + bwd_bytes) / (ms * 1e-3) / 1e9
+    bw_dom = kern["soft_ce_bwd"]["gbps"]
+    out = {"metric": "per-pass soft cross-entropy fwd+bwd GB/s (algorithmic bytes)", "value": round(value, 1),
+           "unit": "GB/s", "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+           "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "ce_b4_s4k_v32k", "batch": B, "seq_len": S, "vocab": V, "passes": K,
+                      "teacher_offset": "p", "step": "fwd+bwd for p = 1..7"},
+           "roofline": {"kernel": "soft_ce_bwd", "bound": "hbm", "achieved": bw_dom, "peak": 8000.0,
+                        "unit": "GB/s", "frac": round(bw_dom / 8000.0, 4), "traffic": None,
+                        "work_per_launch": bwd_bytes / K, "avg_launch_us": kern["soft_ce_bwd"]["avg_us"]},
+           "kernels": kern, "source_digest": source_digest()}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -339,6 +412,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.block:
         block_main(args, dev)
+        return
+    if args.soft_ce:
+        soft_ce_main(args, dev)
         return
     w = syn.workload(args.workload)
     if args.ring:

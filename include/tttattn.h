@@ -222,6 +222,47 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* blk, const 
                        const void* dout, void* dq, void* dk_ctx, void* dv_ctx, void* dk_blk, void* dv_blk, void* ws,
                        size_t ws_bytes, void* stream);
 
+/* ---- Distillation loss after the attention ---------------------------------
+ * Same issue, "What I'm working on", item 3 (chunked soft cross-entropy,
+ * normalised per pass over the whole batch) and NeMo-RL PR #3725, self-review
+ * comment (teacher_offset = pass_index + 1).  Reading: pass p's student logits
+ * at row i are scored against softmax(teacher logits at row i + teacher_offset)
+ * of the same batch row, teacher_offset = p for 1-based p; a row is counted iff
+ * that teacher row exists (i + teacher_offset < seqlen) and mask[b][i] != 0;
+ * loss = sum over counted rows of -sum_v softmax(teacher)_v log softmax(student)_v
+ * divided by the number of counted rows (0 if none).  bf16 logits [B][S][V],
+ * vocab contiguous; V a multiple of 8; row strides multiples of 8 elements. */
+typedef struct ttt_soft_ce_desc {
+  uint32_t struct_size;       /* = sizeof(ttt_soft_ce_desc)                               */
+  int32_t batch, seqlen, vocab;
+  int32_t teacher_offset;     /* >= 0                                                     */
+  int32_t reserved;           /* 0                                                        */
+  int64_t student_stride[2];  /* batch, row strides of the student logits (elements); a
+                                 zero pair selects the contiguous [B, S, V]; the gradient
+                                 uses the same strides                                    */
+  int64_t teacher_stride[2];  /* the same for the teacher logits                          */
+  const uint8_t* mask;        /* device [B][S] (row counted iff != 0) or NULL             */
+} ttt_soft_ce_desc;
+
+/* Bytes of workspace ttt_soft_ce_fwd needs when its row_ce argument is NULL (it then
+ * keeps the rows' cross-entropies there): B * S floats, rounded up to 256.  0 and the
+ * last error if the descriptor is invalid. */
+size_t ttt_soft_ce_workspace_bytes(const ttt_soft_ce_desc* d);
+
+/* Forward: stats[0] = loss, stats[1] = number of counted rows (device float[2]);
+ * row_lse [B][S][2] (device fp32): natural-log LSE of the student and teacher rows,
+ * needed by the backward; row_ce [B][S] (device fp32, optional): each counted row's
+ * cross-entropy, 0 elsewhere (when NULL the workspace holds it).  Deterministic. */
+int ttt_soft_ce_fwd(const ttt_soft_ce_desc* d, const void* student, const void* teacher, float* stats,
+                    float* row_lse, float* row_ce, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward: dstudent = dloss[0] / stats[1] * (softmax(student) - softmax(teacher row
+ * i + offset)) on counted rows, 0 on the others (bf16, student strides).  row_lse and
+ * stats come from ttt_soft_ce_fwd; dloss is a device float (the loss's upstream
+ * gradient).  No gradient is returned for the teacher. */
+int ttt_soft_ce_bwd(const ttt_soft_ce_desc* d, const void* student, const void* teacher, const float* row_lse,
+                    const float* stats, const float* dloss, void* dstudent, void* stream);
+
 /* Static text of a status code. */
 const char* ttt_attn_status_string(int status);
 

@@ -362,3 +362,44 @@ def test_block_bwd_validation():
     assert call_block_bwd(d, good_block(), lse=FAKE + 2) == 4
     assert call_block_bwd(d, good_block(anchors=None)) == 1
     assert call_block_bwd(d, good_block(), ws_bytes=100) == 5
+
+
+# ----------------------------------------------------------------------------- soft cross-entropy
+def ce_desc(B=2, S=100, V=4096, off=1):
+    d = tk.SoftCeDesc()
+    d.struct_size = ctypes.sizeof(tk.SoftCeDesc)
+    d.batch, d.seqlen, d.vocab, d.teacher_offset = B, S, V, off
+    return d
+
+
+def test_soft_ce_struct_and_validation():
+    lib = tk.library()
+    assert ctypes.sizeof(tk.SoftCeDesc) == 64
+    fwd = lambda d, s=FAKE, t=FAKE, st=FAKE, ll=FAKE, rc=FAKE, ws=FAKE, n=1 << 40: lib.ttt_soft_ce_fwd(
+        ctypes.byref(d) if d is not None else None, s, t, st, ll, rc, ws, n, None)
+    bwd = lambda d, s=FAKE, t=FAKE, ll=FAKE, st=FAKE, dl=FAKE, g=FAKE: lib.ttt_soft_ce_bwd(
+        ctypes.byref(d), s, t, ll, st, dl, g, None)
+    assert fwd(None) == 1
+    d = ce_desc()
+    d.struct_size = 4
+    assert fwd(d) == 7
+    assert fwd(ce_desc(V=100)) == 2 and "vocab" in err()
+    assert fwd(ce_desc(V=0)) == 2
+    assert fwd(ce_desc(off=-1)) == 2 and "teacher_offset" in err()
+    assert fwd(ce_desc(B=0)) == 2
+    d = ce_desc()
+    d.student_stride[:] = (100 * 4100, 4100)
+    assert fwd(d) == 4 and "student" in err()
+    d = ce_desc()
+    d.teacher_stride[:] = (100 * 4096, 4000)
+    assert fwd(d) == 2 and "teacher" in err()
+    assert fwd(ce_desc(), s=None) == 1 and "student" in err()
+    assert fwd(ce_desc(), t=FAKE + 8) == 4 and "teacher" in err()
+    assert fwd(ce_desc(), st=None) == 1
+    assert fwd(ce_desc(), ll=FAKE + 2) == 4
+    assert fwd(ce_desc(), rc=None, ws=None) == 5 and "workspace" in err()
+    assert fwd(ce_desc(), rc=None, n=16) == 5
+    assert lib.ttt_soft_ce_workspace_bytes(ctypes.byref(ce_desc())) >= 2 * 100 * 4
+    assert bwd(ce_desc(), g=None) == 1 and "dstudent" in err()
+    assert bwd(ce_desc(), dl=None) == 1 and "dloss" in err()
+    assert bwd(ce_desc(), ll=FAKE + 2) == 4

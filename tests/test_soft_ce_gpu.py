@@ -1,0 +1,123 @@
+"""GPU parity of the per-pass soft cross-entropy (ttt_soft_ce_fwd / _bwd) against the fp64 oracle.
+
+Student row i of pass p is scored against the teacher distribution at row i + p; rows without a teacher row or
+with mask 0 are not counted; the loss is the mean over counted rows.  bf16 logits, fp32 loss/LSE, bf16 gradient
+(compared by relative Frobenius norm, which bf16 rounding bounds by about 2e-3).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import ttt_synth as syn
+from oracle import ttt_oracle as O
+from ttt_cases import rel_fro, to_np
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def tk():
+    import attention_ttt_attn_amd as m
+    m.library()
+    return m
+
+
+def logits(seed, shape, scale=2.0):
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32) * scale
+    return syn.round_bf16(x)
+
+
+def run(tk, dev, st, te, off, mask=None, dloss=1.0):
+    gs = torch.from_numpy(st).to(dev).to(torch.bfloat16)
+    gt = torch.from_numpy(te).to(dev).to(torch.bfloat16)
+    gm = torch.from_numpy(mask).to(dev) if mask is not None else None
+    stats, row_lse, row_ce = tk.soft_ce_fwd(gs, gt, off, mask=gm)
+    gd = torch.tensor([dloss], dtype=torch.float32, device=dev)
+    g = tk.soft_ce_bwd(gs, gt, off, row_lse, stats, gd, mask=gm)
+    torch.cuda.synchronize()
+    return to_np(stats), to_np(row_lse), to_np(row_ce), to_np(g)
+
+
+@pytest.mark.parametrize("off,masked", [(1, False), (3, True), (7, False)])
+def test_soft_ce_small(dev, tk, off, masked):
+    B, S, V = 2, 37, 1000
+    st, te = logits(41, (B, S, V)), logits(42, (B, S, V))
+    mask = None
+    if masked:
+        mask = (np.random.default_rng(43).random((B, S)) > 0.3).astype(np.uint8)
+    stats, row_lse, row_ce, g = run(tk, dev, st, te, off, mask, dloss=0.75)
+    loss, grad, rce = O.soft_ce(st, te, off, mask)
+    counted = O.soft_ce_rows_counted(B, S, off, mask)
+    print(f"off={off} masked={masked}: loss {stats[0]:.7f} ref {loss:.7f}, count {stats[1]:.0f}")
+    assert int(stats[1]) == int(counted.sum())
+    assert abs(stats[0] - loss) <= 1e-5 * max(1.0, abs(loss))
+    assert np.max(np.abs(row_ce - rce)) <= 2e-5
+    lse_ref = np.log(np.exp(st.astype(np.float64)).sum(-1))
+    assert np.max(np.abs(row_lse[..., 0][counted] - lse_ref[counted])) <= 2e-5
+    assert np.all(g[~counted] == 0)
+    e = rel_fro(g, 0.75 * grad)
+    print(f"  grad rel Frobenius {e:.3e}")
+    assert e <= 4e-3
+
+
+def test_soft_ce_edges(dev, tk):
+    # no counted row: loss 0, count 0, zero gradient
+    st, te = logits(44, (1, 5, 64)), logits(45, (1, 5, 64))
+    stats, _, row_ce, g = run(tk, dev, st, te, 5)
+    assert stats[0] == 0 and stats[1] == 0 and np.all(row_ce == 0) and np.all(g == 0)
+    # the smallest vocab, one row
+    st, te = logits(46, (1, 2, 8)), logits(47, (1, 2, 8))
+    stats, _, _, g = run(tk, dev, st, te, 1)
+    loss, grad, _ = O.soft_ce(st, te, 1)
+    assert stats[1] == 1 and abs(stats[0] - loss) <= 1e-5 and rel_fro(g, grad) <= 4e-3
+    # a full-size vocabulary (152064) and peaked logits
+    st, te = logits(48, (1, 3, 152064), 6.0), logits(49, (1, 3, 152064), 6.0)
+    stats, _, row_ce, g = run(tk, dev, st, te, 1)
+    loss, grad, rce = O.soft_ce(st, te, 1)
+    print(f"V=152064: loss {stats[0]:.6f} ref {loss:.6f}; grad rel Frobenius {rel_fro(g, grad):.3e}")
+    assert abs(stats[0] - loss) <= 1e-5 * max(1.0, abs(loss)) and rel_fro(g, grad) <= 4e-3
+
+
+def test_soft_ce_fullsize(dev, tk):
+    """B=4, S=4096, V=32000 at pass 7: the loss equals the fp64 mean of the kernel's own row
+    cross-entropies, and >= 512 sampled rows (row CE, LSE, gradient) match the oracle."""
+    B, S, V, off = 4, 4096, 32000, 7
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(50)
+    gs = (torch.randn((B, S, V), generator=gen, device=dev) * 2).to(torch.bfloat16)
+    gt = (torch.randn((B, S, V), generator=gen, device=dev) * 2).to(torch.bfloat16)
+    stats, row_lse, row_ce = tk.soft_ce_fwd(gs, gt, off)
+    g = tk.soft_ce_bwd(gs, gt, off, row_lse, stats, torch.ones(1, device=dev))
+    torch.cuda.synchronize()
+    st_, rl, rc = to_np(stats), to_np(row_lse), to_np(row_ce)
+    n = B * (S - off)
+    assert int(st_[1]) == n
+    mean = rc[:, :S - off].astype(np.float64).mean()
+    assert abs(st_[0] - mean) <= 1e-6 * abs(mean)
+    rng = np.random.default_rng(51)
+    rows = [(int(b), int(i)) for b, i in zip(rng.integers(0, B, 512), rng.integers(0, S - off, 512))]
+    rows += [(0, 0), (B - 1, S - off - 1)]
+    ece = el = 0.0
+    gg, gr = [], []
+    for b, i in rows:
+        s_row = to_np(gs[b, i])[None, None]
+        t_row = to_np(gt[b, i + off])[None, None]
+        _, grad1, rce1 = O.soft_ce(s_row, t_row, 0)
+        ece = max(ece, abs(rc[b, i] - rce1[0, 0]))
+        lse = math.log(np.exp(s_row.astype(np.float64)).sum())
+        el = max(el, abs(rl[b, i, 0] - lse))
+        gg.append(to_np(g[b, i]))
+        gr.append(grad1[0, 0] / n)
+    e = rel_fro(np.stack(gg), np.stack(gr))
+    print(f"full size: {len(rows)} rows, row CE max-abs {ece:.2e}, LSE max-abs {el:.2e}, grad rel Frobenius {e:.2e}")
+    assert ece <= 5e-5 and el <= 5e-5 and e <= 4e-3
