@@ -64,6 +64,11 @@ What is computed (one call = one TTT pass p, 1-based):
   distribution) / count on counted rows and 0 elsewhere.  Chunking the tokens
   only bounds memory and does not change the value.
 
+* Sliding-window trunk (issue above, item 4: sliding-window layers).  Reading:
+  with window W > 0, row i's trunk is the pass-1 keys j with i - W < j <= i
+  (the last W positions up to its own); the branch is unchanged; W = 0 is the
+  full causal trunk.
+
 * Ring steps (issue above, item 4: context parallelism, where pass-1 K/V
   travel around a zig-zag ring and partial results are joined by the joint-LSE
   merge): `fwd_chunk` is the attention of a block of query rows at sequence
@@ -85,7 +90,7 @@ from typing import Iterable, Optional, Sequence
 import numpy as np
 
 __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_position",
-           "ttt_mask_row", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows", "Slice",
+           "ttt_mask_row", "trunk_window_start", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows", "Slice",
            "fwd_chunk", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd",
            "block_bwd_rows", "block_bwd", "soft_ce_rows_counted", "soft_ce"]
 
@@ -127,11 +132,17 @@ def key_position(q: int, j):
 
 
 # ----------------------------------------------------------------------------- mask
-def ttt_mask_row(i: int, p: int, L: int) -> np.ndarray:
+def trunk_window_start(i: int, window: int) -> int:
+    """First pass-1 key row i sees: 0 without a window, else i - window + 1 (clamped at 0)."""
+    return 0 if window <= 0 else max(0, i - window + 1)
+
+
+def ttt_mask_row(i: int, p: int, L: int, window: int = 0) -> np.ndarray:
     """Explicit visibility of row i at pass p over the concatenated keys of a
-    length-L sequence, [K(1)_0..L-1 ; K(2)_0..L-1 ; ... ; K(p)_0..L-1]."""
+    length-L sequence, [K(1)_0..L-1 ; K(2)_0..L-1 ; ... ; K(p)_0..L-1].
+    window > 0 limits the trunk to the last `window` keys j <= i."""
     m = np.zeros(p * L, dtype=bool)
-    m[: i + 1] = True                      # trunk: pass-1 keys j <= i
+    m[trunk_window_start(i, window): i + 1] = True   # trunk: pass-1 keys j <= i (inside the window)
     for q in range(2, p + 1):              # branch: passes 2..p at the same row
         m[(q - 1) * L + i] = True
     return m
@@ -196,14 +207,15 @@ def _candidate_columns(rows: np.ndarray, p: int, L: int) -> np.ndarray:
     return np.unique(np.concatenate(cols))
 
 
-def _row_block_fwd(gk: _GroupKeys, q_rot: np.ndarray, rows: np.ndarray, p: int, L: int, scale: float):
+def _row_block_fwd(gk: _GroupKeys, q_rot: np.ndarray, rows: np.ndarray, p: int, L: int, scale: float,
+                   window: int = 0):
     """Scores, probabilities, LSE and O for a block of query rows (one head).
 
     The explicit mask rows are evaluated on the block's candidate columns; the
     assertion checks that no allowed key lies outside them, so the softmax over
     the candidates equals the softmax over all p*L concatenated keys."""
     cols = _candidate_columns(rows, p, L)
-    full = np.stack([ttt_mask_row(int(i), p, L) for i in rows])          # [n, p*L]
+    full = np.stack([ttt_mask_row(int(i), p, L, window) for i in rows])  # [n, p*L]
     mask = full[:, cols]
     assert np.array_equal(mask.sum(axis=1), full.sum(axis=1))
     s = scale * (q_rot @ gk.keys[cols].T)
@@ -226,7 +238,7 @@ def _block_rows(L: int, p: int) -> int:
 
 
 def fwd_group_rows(q, ks, vs, p: int, sl: Slice, g: int, rows_by_head, *, layout: str, Hq: int, Hkv: int,
-                   scale: float, base: float):
+                   scale: float, base: float, window: int = 0):
     """{h: (O [n, D], LSE [n])} for the requested rows of the query heads h of KV
     group g in sequence `sl`, at pass p (the group's rotated keys are built once)."""
     gk = _GroupKeys(sl, g, ks, vs, p, layout, base)
@@ -240,7 +252,7 @@ def fwd_group_rows(q, ks, vs, p: int, sl: Slice, g: int, rows_by_head, *, layout
         a = 0
         for blk in _blocks(rows, _block_rows(sl.L, p)):
             qr = rotate_half(qs[blk], query_position(blk, p), base)
-            _, l_, o_, _ = _row_block_fwd(gk, qr, blk, p, sl.L, scale)
+            _, l_, o_, _ = _row_block_fwd(gk, qr, blk, p, sl.L, scale, window)
             O[a: a + len(blk)] = o_
             lse[a: a + len(blk)] = l_
             a += len(blk)
@@ -249,15 +261,15 @@ def fwd_group_rows(q, ks, vs, p: int, sl: Slice, g: int, rows_by_head, *, layout
 
 
 def fwd_rows(q, ks, vs, p: int, sl: Slice, h: int, rows, *, layout: str, Hq: int, Hkv: int,
-             scale: float, base: float):
+             scale: float, base: float, window: int = 0):
     """O [n, D] and LSE [n] for rows `rows` of sequence `sl`, query head h, at pass p."""
     g = h // (Hq // Hkv)
     return fwd_group_rows(q, ks, vs, p, sl, g, {h: rows}, layout=layout, Hq=Hq, Hkv=Hkv, scale=scale,
-                          base=base)[h]
+                          base=base, window=window)[h]
 
 
 def fwd(q, ks, vs, p: int, *, layout: str = "bshd", cu_seqlens=None, scale: Optional[float] = None,
-        base: float = 0.0):
+        base: float = 0.0, window: int = 0):
     """Full forward of pass p.  q: [B,S,Hq,D] or [T,Hq,D]; ks, vs: p tensors of
     [B,S,Hkv,D] or [T,Hkv,D] (index 0 = trunk).  Returns (O fp64 like q, LSE fp64)."""
     assert len(ks) >= p and len(vs) >= p and p >= 1
@@ -275,7 +287,7 @@ def fwd(q, ks, vs, p: int, *, layout: str = "bshd", cu_seqlens=None, scale: Opti
         rows = np.arange(sl.L)
         for g in range(Hkv):
             res = fwd_group_rows(q, ks, vs, p, sl, g, {h: rows for h in range(g * r, (g + 1) * r)},
-                                 layout=layout, Hq=Hq, Hkv=Hkv, scale=scale, base=base)
+                                 layout=layout, Hq=Hq, Hkv=Hkv, scale=scale, base=base, window=window)
             for h, (o_, l_) in res.items():
                 O[_row_index(layout, sl, rows) + (h,)] = o_
                 lse[_lse_index(layout, sl, h, rows)] = l_
@@ -283,7 +295,7 @@ def fwd(q, ks, vs, p: int, *, layout: str = "bshd", cu_seqlens=None, scale: Opti
 
 
 def bwd_rows(q, ks, vs, dout, p: int, sl: Slice, g: int, rows, *, layout: str, Hq: int,
-             Hkv: int, scale: float, base: float, need_kv: bool = True):
+             Hkv: int, scale: float, base: float, need_kv: bool = True, window: int = 0):
     """Backward contributions of query rows `rows` (all r heads of KV group g).
 
     Returns (dq [r, n, D] for those rows, dk [p*L, D], dv [p*L, D]) where dk, dv
@@ -305,7 +317,7 @@ def bwd_rows(q, ks, vs, dout, p: int, sl: Slice, g: int, rows, *, layout: str, H
         a = 0
         for blk in _blocks(rows, _block_rows(sl.L, p)):
             qr = rotate_half(qs[blk], query_position(blk, p), base)
-            P, lse, O, cols = _row_block_fwd(gk, qr, blk, p, sl.L, scale)
+            P, lse, O, cols = _row_block_fwd(gk, qr, blk, p, sl.L, scale, window)
             keys, vals = gk.keys[cols], gk.vals[cols]
             do = dos[blk]
             delta = (do * O).sum(axis=1)
@@ -325,7 +337,7 @@ def bwd_rows(q, ks, vs, dout, p: int, sl: Slice, g: int, rows, *, layout: str, H
 
 
 def bwd(q, ks, vs, dout, p: int, *, layout: str = "bshd", cu_seqlens=None,
-        scale: Optional[float] = None, base: float = 0.0):
+        scale: Optional[float] = None, base: float = 0.0, window: int = 0):
     """Full backward of pass p.  Returns (dQ like q, [dK(1..p)], [dV(1..p)]) in fp64."""
     Hq, D = q.shape[-2], q.shape[-1]
     Hkv = ks[0].shape[-2]
@@ -339,7 +351,7 @@ def bwd(q, ks, vs, dout, p: int, *, layout: str = "bshd", cu_seqlens=None,
         rows = np.arange(sl.L)
         for g in range(Hkv):
             dq, dk, dv = bwd_rows(q, ks, vs, dout, p, sl, g, rows, layout=layout, Hq=Hq,
-                                  Hkv=Hkv, scale=scale, base=base)
+                                  Hkv=Hkv, scale=scale, base=base, window=window)
             for hh in range(r):
                 dQ[_row_index(layout, sl, rows) + (g * r + hh,)] = dq[hh]
             for qq in range(p):
@@ -349,14 +361,20 @@ def bwd(q, ks, vs, dout, p: int, *, layout: str = "bshd", cu_seqlens=None,
 
 
 # ----------------------------------------------------------------------------- ring steps
-def ring_visible(q_pos, k_pos) -> np.ndarray:
+def ring_visible(q_pos, k_pos, window: int = 0) -> np.ndarray:
     """[n, m] causal visibility of pass-1 keys at sequence positions k_pos to the
-    query rows at sequence positions q_pos (a row sees its own position)."""
-    return np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None]
+    query rows at sequence positions q_pos (a row sees its own position); with a
+    window, only the last `window` positions up to the row's own."""
+    k = np.asarray(k_pos)[None, :]
+    q = np.asarray(q_pos)[:, None]
+    vis = k <= q
+    if window > 0:
+        vis = vis & (k > q - window)
+    return vis
 
 
 def fwd_chunk(q, k0, v0, branch_ks, branch_vs, p: int, *, q_offset: int, kv_offset: int,
-              scale: Optional[float] = None, base: float = 0.0):
+              scale: Optional[float] = None, base: float = 0.0, window: int = 0):
     """One ring step of pass p, BSHD.  q: [B, n, Hq, D] rows at sequence positions
     q_offset + i; k0, v0: [B, m, Hkv, D] pass-1 keys at positions kv_offset + j;
     branch_ks, branch_vs: None, or the p-1 tensors [B, n, Hkv, D] of passes 2..p
@@ -377,7 +395,7 @@ def fwd_chunk(q, k0, v0, branch_ks, branch_vs, p: int, *, q_offset: int, kv_offs
         for g in range(Hkv):
             kr = rotate_half(np.asarray(k0[b, :, g], np.float64), kv_offset + np.arange(m), base)   # [m, D]
             vv = np.asarray(v0[b, :, g], np.float64)
-            vis = ring_visible(qpos, kv_offset + np.arange(m))                                     # [n, m]
+            vis = ring_visible(qpos, kv_offset + np.arange(m), window)                             # [n, m]
             bk, bv = [], []
             if branch_ks is not None:
                 for t in range(2, p + 1):

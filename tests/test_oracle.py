@@ -524,13 +524,93 @@ def check_soft_ce_closed_forms():
     assert np.max(np.abs(rc2[0, :S - off] - ent[0, off:])) < 1e-12
 
 
+def _band_mask(S, p, window):
+    """[S, p*S] visibility with a trunk band j in (i - window, i], built from tril/triu and eye blocks."""
+    ones = torch.ones(S, S, dtype=torch.bool)
+    trunk = torch.tril(ones) & torch.triu(ones, diagonal=-(window - 1))
+    return torch.cat([trunk] + [torch.eye(S, dtype=torch.bool)] * (p - 1), dim=1)
+
+
+def _window_dense(q, ks, vs, p, scale, base, window, grad=False):
+    """torch SDPA over the concatenated rotated keys of one THD sequence with the band mask."""
+    S, Hq, D = q.shape
+    Hkv = ks[0].shape[1]
+    r = Hq // Hkv
+    i = torch.arange(S)
+    T = [torch.tensor(x, requires_grad=grad) for x in [q] + list(ks[:p]) + list(vs[:p])]
+    tq, tk_, tv = T[0], T[1:1 + p], T[1 + p:]
+    qr = rope_complex(tq, (i + p - 1)[:, None].expand(S, Hq), base)
+    kc = torch.cat([rope_complex(tk_[t], (i + t)[:, None].expand(S, Hkv), base) for t in range(p)], 0)
+    vc = torch.cat(list(tv), 0)
+    mask = _band_mask(S, p, window)
+    qh, kh, vh = qr.permute(1, 0, 2), kc.permute(1, 0, 2).repeat_interleave(r, 0), vc.permute(1, 0, 2).repeat_interleave(r, 0)
+    o = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask, scale=scale).permute(1, 0, 2)
+    lse = torch.logsumexp(((qh @ kh.transpose(-1, -2)) * scale).masked_fill(~mask, -math.inf), -1)
+    return o, lse, T
+
+
+def check_window_sdpa_and_grad():
+    """Sliding-window trunk == SDPA with a band mask (window 1, 3, L-1), forward and fp64 autograd."""
+    S, Hq, Hkv, D, p, base = 12, 4, 2, 8, 3, 1e4
+    q, ks, vs, do = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=95)
+    scale = 1 / math.sqrt(D)
+    for window in (1, 3, S - 1):
+        o, lse = O.fwd(q, ks, vs, p, layout="thd", cu_seqlens=[0, S], scale=scale, base=base, window=window)
+        ro, rl, T = _window_dense(q, ks, vs, p, scale, base, window, grad=True)
+        assert np.max(np.abs(o - ro.detach().numpy())) < 1e-12
+        assert np.max(np.abs(lse - rl.detach().numpy())) < 1e-12
+        (ro * torch.tensor(do)).sum().backward()
+        dq, dk, dv = O.bwd(q, ks, vs, do, p, layout="thd", cu_seqlens=[0, S], scale=scale, base=base, window=window)
+        assert np.max(np.abs(dq - T[0].grad.numpy())) < 1e-10
+        for t in range(p):
+            assert np.max(np.abs(dk[t] - T[1 + t].grad.numpy())) < 1e-10
+            assert np.max(np.abs(dv[t] - T[1 + p + t].grad.numpy())) < 1e-10
+
+
+def check_window_closed_forms():
+    """Zero queries: LSE_i = ln(min(i+1, W) + p - 1); a window of L or more is the full trunk."""
+    S, p, W = 10, 3, 4
+    q, ks, vs, _ = make(S=S, Hq=2, Hkv=1, D=8, p=p, seed=96)
+    q[:] = 0
+    _, lse = O.fwd(q, ks, vs, p, layout="thd", cu_seqlens=[0, S], base=1e6, window=W)
+    for i in range(S):
+        assert abs(lse[0, i] - math.log(min(i + 1, W) + p - 1)) < 1e-12
+    q2, ks2, vs2, _ = make(S=S, Hq=2, Hkv=1, D=8, p=p, seed=97)
+    a = O.fwd(q2, ks2, vs2, p, layout="thd", cu_seqlens=[0, S], base=1e6, window=S)
+    b = O.fwd(q2, ks2, vs2, p, layout="thd", cu_seqlens=[0, S], base=1e6)
+    assert np.max(np.abs(a[0] - b[0])) == 0 and np.max(np.abs(a[1] - b[1])) == 0
+
+
+def check_window_ring_partition():
+    """Windowed ring steps over a zig-zag partition, merged, equal the windowed dense rows."""
+    S, Hq, Hkv, D, p, base, scale, cp, W = 16, 2, 1, 8, 3, 1e6, 0.35, 2, 5
+    q, ks, vs, _ = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=98, B=1)
+    ro, rl, _ = _window_dense(q[0], [k[0] for k in ks], [v[0] for v in vs], p, scale, base, W)
+    ro, rl = ro.numpy(), rl.numpy()
+    c = S // (2 * cp)
+    for qc in range(2 * cp):
+        qa = qc * c
+        acc_o = np.zeros((1, c, Hq, D)); acc_l = np.full((1, Hq, c), -np.inf)
+        for kc in range(2 * cp):
+            ka = kc * c
+            br = kc == qc
+            o, l = O.fwd_chunk(q[:, qa:qa + c], ks[0][:, ka:ka + c], vs[0][:, ka:ka + c],
+                               [k[:, qa:qa + c] for k in ks[1:]] if br else None,
+                               [v[:, qa:qa + c] for v in vs[1:]] if br else None,
+                               p, q_offset=qa, kv_offset=ka, scale=scale, base=base, window=W)
+            acc_o, acc_l = O.merge(acc_o, acc_l, o, l)
+        assert np.max(np.abs(acc_o[0] - ro[qa:qa + c])) < 1e-12
+        assert np.max(np.abs(acc_l[0] - rl[:, qa:qa + c])) < 1e-12
+
+
 PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check_zero_query_closed_form,
         lambda: check_zero_query_closed_form("thd"), check_sdpa_brute_force, check_p1_is_causal_sdpa,
         check_merge_invariant, check_branch_relative_position, check_grad_autograd,
         check_grad_finite_difference, check_thd_equals_bshd, check_thd_isolation, check_gqa_is_repeated_kv,
         check_sampled_rows_match_full, check_chunk_rows_match_dense, check_chunk_ring_partition,
         check_merge_closed_form, check_block_sdpa_mask, check_block_zero_query_closed_form,
-        check_block_size1_is_causal, check_block_grad_autograd, check_soft_ce_library, check_soft_ce_closed_forms]
+        check_block_size1_is_causal, check_block_grad_autograd, check_soft_ce_library, check_soft_ce_closed_forms,
+        check_window_sdpa_and_grad, check_window_closed_forms, check_window_ring_partition]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
@@ -553,16 +633,16 @@ def _orig(name):
     return getattr(O, name)
 
 
-def _mask_no_branch(i, p, L):
-    m = np.zeros(p * L, dtype=bool); m[: i + 1] = True; return m
+def _mask_no_branch(i, p, L, window=0):
+    m = np.zeros(p * L, dtype=bool); m[O.trunk_window_start(i, window): i + 1] = True; return m
 
 
-def _mask_strict_causal(i, p, L):
-    m = _orig_mask(i, p, L); m[i] = i == 0; return m
+def _mask_strict_causal(i, p, L, window=0):
+    m = _orig_mask(i, p, L, window); m[i] = i == 0; return m
 
 
-def _mask_branch_next_row(i, p, L):
-    m = np.zeros(p * L, dtype=bool); m[: i + 1] = True
+def _mask_branch_next_row(i, p, L, window=0):
+    m = np.zeros(p * L, dtype=bool); m[O.trunk_window_start(i, window): i + 1] = True
     for q in range(2, p + 1):
         m[(q - 1) * L + min(i + 1, L - 1)] = True
     return m
@@ -595,8 +675,8 @@ def _rot_pairing(x, pos, base):
     return y
 
 
-def _blk_transposed_v(gk, q_rot, rows, p, L, scale):
-    P, lse, O_, cols = _orig_blk(gk, q_rot, rows, p, L, scale)
+def _blk_transposed_v(gk, q_rot, rows, p, L, scale, window=0):
+    P, lse, O_, cols = _orig_blk(gk, q_rot, rows, p, L, scale, window)
     return P, lse, P @ gk.vals[cols][:, ::-1], cols
 
 
@@ -612,13 +692,16 @@ MISTAKES = [
     ("key_position", lambda q, j: np.asarray(j) + q),
     ("inv_freq", lambda D, base: np.power(np.float64(base), -1.0 * np.arange(D // 2) / D)),
     ("_row_block_fwd", _blk_transposed_v),
-    ("ring_visible", lambda qp, kp: np.asarray(kp)[None, :] < np.asarray(qp)[:, None]),
-    ("ring_visible", lambda qp, kp: np.asarray(kp)[None, :] <= np.asarray(qp)[:, None] + 1),
+    ("ring_visible", lambda qp, kp, w=0: np.asarray(kp)[None, :] < np.asarray(qp)[:, None]),
+    ("ring_visible", lambda qp, kp, w=0: np.asarray(kp)[None, :] <= np.asarray(qp)[:, None] + 1),
     ("merge", lambda oa, la, ob, lb: _orig_merge(ob, la, oa, lb)),
     ("block_visible_ctx", lambda a, L: int(min(max(a + 1, 0), L))),
     ("block_slot_position", lambda a, t: int(a) + np.asarray(t) + 1),
     ("block_slot_position", lambda a, t: np.asarray(t)),
     ("soft_ce_rows_counted", lambda B, S, off, mask=None: np.arange(S)[None, :].repeat(B, 0) + off <= S),
+    ("trunk_window_start", lambda i, w: 0 if w <= 0 else max(0, i - w + 2)),
+    ("trunk_window_start", lambda i, w: 0 if w <= 0 else max(0, i - w)),
+    ("ring_visible", lambda qp, kp, w=0: np.asarray(kp)[None, :] <= np.asarray(qp)[:, None]),
     ("soft_ce_rows_counted", lambda B, S, off, mask=None: np.ones((B, S), dtype=bool) & (np.arange(S)[None, :] + off < S)),
     ("merge", lambda oa, la, ob, lb: (_orig_merge(oa, la, ob, lb)[0], np.maximum(la, lb))),
 ]
