@@ -51,6 +51,8 @@ class Desc(ctypes.Structure):
         ("q_stride", ctypes.c_int64 * 3),
         ("kv_stride", ctypes.c_int64 * 3),
         ("o_stride", ctypes.c_int64 * 3),
+        ("window", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -196,7 +198,7 @@ def _strides3(t, thd: bool):
 
 
 def make_desc(q, ks, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0, rope_base: float = 0.0,
-              o_dtype: Optional[int] = None, o_like=None, check_cu_seqlens: bool = False) -> Desc:
+              o_dtype: Optional[int] = None, o_like=None, check_cu_seqlens: bool = False, window: int = 0) -> Desc:
     thd = cu_seqlens is not None
     d = Desc()
     d.struct_size = ctypes.sizeof(Desc)
@@ -218,6 +220,7 @@ def make_desc(q, ks, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0, rop
     d.q_stride[:] = _strides3(q, thd)
     d.kv_stride[:] = _strides3(ks[0], thd)
     d.o_stride[:] = _strides3(o_like if o_like is not None else q, thd)
+    d.window = int(window)
     return d
 
 
@@ -257,7 +260,7 @@ def _ws_ptr(ws):
 
 def fwd(q, ks: Sequence, vs: Sequence, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0,
         rope_base: float = 0.0, o_fp32: bool = False, out=None, lse=None, workspace=None, stream=None,
-        check_cu_seqlens: bool = False):
+        check_cu_seqlens: bool = False, window: int = 0):
     """Forward of TTT pass p.  Returns (o, lse); lse is fp32 [B,Hq,S] or [Hq,T]."""
     torch = _torch()
     thd = cu_seqlens is not None
@@ -268,7 +271,7 @@ def fwd(q, ks: Sequence, vs: Sequence, p: int, *, cu_seqlens=None, softmax_scale
         shape = (q.shape[-2], q.shape[0]) if thd else (q.shape[0], q.shape[2], q.shape[1])
         lse = torch.empty(shape, dtype=torch.float32, device=q.device)
     d = make_desc(q, ks, p, cu_seqlens=cu_seqlens, softmax_scale=softmax_scale, rope_base=rope_base,
-                  o_dtype=o_dtype, o_like=out, check_cu_seqlens=check_cu_seqlens)
+                  o_dtype=o_dtype, o_like=out, check_cu_seqlens=check_cu_seqlens, window=window)
     if any(t.stride() != ks[0].stride() for t in list(ks[:p]) + list(vs[:p])):
         raise ValueError("every k and v must share one set of strides")
     nbytes = workspace_bytes(d, False)
@@ -281,12 +284,12 @@ def fwd(q, ks: Sequence, vs: Sequence, p: int, *, cu_seqlens=None, softmax_scale
 
 def bwd(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0,
         rope_base: float = 0.0, dq=None, dks=None, dvs=None, workspace=None, stream=None,
-        check_cu_seqlens: bool = False):
+        check_cu_seqlens: bool = False, window: int = 0):
     """Backward of TTT pass p.  Returns (dq, [dk_1..dk_p], [dv_1..dv_p])."""
     torch = _torch()
     o_dtype = _dtype_code(o)
     d = make_desc(q, ks, p, cu_seqlens=cu_seqlens, softmax_scale=softmax_scale, rope_base=rope_base,
-                  o_dtype=o_dtype, o_like=o, check_cu_seqlens=check_cu_seqlens)
+                  o_dtype=o_dtype, o_like=o, check_cu_seqlens=check_cu_seqlens, window=window)
     if dout.stride() != o.stride():
         raise ValueError("dout must have the strides of o")
     like = lambda t: torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
@@ -322,7 +325,7 @@ def make_chunk(q_offset: int, kv_offset: int, k0, *, with_branch: bool) -> Chunk
 
 def fwd_chunk(q, ks: Sequence, vs: Sequence, p: int, *, q_offset: int, kv_offset: int, with_branch: bool,
               softmax_scale: float = 0.0, rope_base: float = 0.0, o_fp32: bool = True, out=None, lse=None,
-              workspace=None, stream=None):
+              workspace=None, stream=None, window: int = 0):
     """One ring step (BSHD, bf16): the rows of q (positions q_offset..) against the pass-1 keys ks[0], vs[0]
     (positions kv_offset..), plus the branch keys ks[1:p], vs[1:p] of those rows when with_branch.
     Returns (o, lse) normalised over the keys this step sees (rows that see none: o = 0, lse = -inf)."""
@@ -334,7 +337,7 @@ def fwd_chunk(q, ks: Sequence, vs: Sequence, p: int, *, q_offset: int, kv_offset
         lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
     branch_ks = list(ks[1:p]) if with_branch else []
     d = make_desc(q, (branch_ks or [ks[0]]), p, softmax_scale=softmax_scale, rope_base=rope_base, o_dtype=o_dtype,
-                  o_like=out)
+                  o_like=out, window=window)
     if branch_ks and any(t.stride() != branch_ks[0].stride() for t in branch_ks + list(vs[1:p])):
         raise ValueError("every branch k and v must share one set of strides")
     if vs[0].stride() != ks[0].stride():

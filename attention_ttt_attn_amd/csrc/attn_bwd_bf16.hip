@@ -61,7 +61,8 @@ struct DqSmem {
 __host__ __device__ constexpr int dq_rows(int heads_per_wg) { return 32 * 4 / heads_per_wg; }
 static int dq_heads_per_wg(int r) { return r % 4 == 0 ? 4 : (r % 2 == 0 ? 2 : 1); }
 
-// MODE 0: TTT pass.  MODE 1: block drafting -- key tiles of the context
+// MODE 0: TTT pass; MODE 4: the same with a sliding-window trunk (its own
+// instantiation).  MODE 1: block drafting -- key tiles of the context
 // (kt/ktt, V = kv.v[0] with the P.cs strides) up to each row's block anchor,
 // then the keys of the work item's own blocks (kbt/kbtt, V = kv.v[1]).
 template <int RH, int MODE>
@@ -73,6 +74,8 @@ __global__ void __launch_bounds__(256, 2)
                    uint16_t* __restrict__ dq, const _Float16* __restrict__ kbt, const _Float16* __restrict__ kbtt) {
   constexpr int RT = dq_rows(RH);  // rows per work item
   __shared__ __attribute__((aligned(16))) DqSmem sm;
+  constexpr bool TTT_ = MODE == 0 || MODE == 4;  // TTT pass (4: with a sliding window)
+  const int win = MODE == 4 ? P.win : 0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
 
@@ -127,16 +130,18 @@ __global__ void __launch_bounds__(256, 2)
       if ((blk << P.bs_log2) < wend && ((blk + 1) << P.bs_log2) > wave_row0) lim_lo = min(lim_lo, a);
     }
   }
-  const int nkt = MODE == 0 ? (qend + QBN - 1) / QBN : (lim_hi + QBN - 1) / QBN;  // TTT: >= 1 (row0 < L)
+  const int nkt = TTT_ ? (qend + QBN - 1) / QBN : (lim_hi + QBN - 1) / QBN;  // TTT: >= 1 (row0 < L)
+  // sliding window: the first key tile any row of the work item sees
+  const int kt_lo = (TTT_ && win > 0) ? max(0, row0 - win + 1) / QBN : 0;
 
   // DMA lane roles, 6 loads per wave per tile (load n = 2w + i):
   // K~ and V rows 4n + lane/16, slot lane%16; K~^T d-rows 16n + lane/4, slot lane%4.
   const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
   const _Float16* ktbase = ktt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
-  const int64_t vs_b = MODE == 0 ? P.ks_b : P.cs_b, vs_t = MODE == 0 ? P.ks_t : P.cs_t;
-  const int64_t vs_h = MODE == 0 ? P.ks_h : P.cs_h;
+  const int64_t vs_b = TTT_ ? P.ks_b : P.cs_b, vs_t = TTT_ ? P.ks_t : P.cs_t;
+  const int64_t vs_h = TTT_ ? P.ks_h : P.cs_h;
   const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * vs_b + (int64_t)start * vs_t + g * vs_h;
-  const int vlast = (MODE == 0 ? L : P.kv_len) - 1;  // last key row of the trunk
+  const int vlast = (TTT_ ? L : P.kv_len) - 1;  // last key row of the trunk
   uint32_t roff[2], toff[2];
   int rrow[2];
 #pragma unroll
@@ -163,7 +168,7 @@ __global__ void __launch_bounds__(256, 2)
   auto dma = [&](DqBuf* __restrict__ dst, int j) __attribute__((always_inline)) {
     dma_from(dst, kbase, ktbase, vbase, vs_t, j * QBN, vlast);
   };
-  if (nkt > 0) dma(&sm.buf[0], 0);
+  if (kt_lo < nkt) dma(&sm.buf[0], kt_lo);
 
   // B operands of this lane's query: Q~ (fp16, pre-rotated) and dO (bf16)
   f16x8 qf[8];
@@ -194,7 +199,9 @@ __global__ void __launch_bounds__(256, 2)
     for (int v = 0; v < 16; ++v) acc[d4][v] = 0.f;
   const int prow = perm_row(l32);
   // Tiles whose every key precedes every row of this wave need no mask.
-  const int n_free = MODE == 0 ? (wave_row0 + 1) / QBN : lim_lo / QBN;
+  const int n_free = TTT_ ? (wave_row0 + 1) / QBN : lim_lo / QBN;
+  // with a window, tiles from f_lo on lie inside every row's window
+  const int f_lo = (TTT_ && win > 0) ? max(0, wave_row0 + 31 - win + 1 + QBN - 1) / QBN : 0;
 
   // S^T = K~ Q~^T, dP^T = V dO^T, dS = P (dP - Delta), dQ~^T += K~^T dS^T.
   // Masks: 1 causal, 2 context prefix key < lim, 3 the row's own block.
@@ -227,7 +234,8 @@ __global__ void __launch_bounds__(256, 2)
     for (int v = 0; v < 16; ++v) {
       float pr = fast_exp2(__builtin_fmaf(s[v], sl2, -lse2));
       const int key = key0 + (v >> 3) * 16 + 8 * hf + (v & 7);
-      if constexpr (M == 1) pr = (v >> 3) * 16 + (v & 7) > thr ? 0.f : pr;
+      if constexpr (M == 1)
+        pr = ((v >> 3) * 16 + (v & 7) > thr || (MODE == 4 && key <= my_row - win)) ? 0.f : pr;
       else if constexpr (M == 2) pr = key >= lim ? 0.f : pr;
       else if constexpr (M == 3) pr = ((key >> P.bs_log2) != (my_row >> P.bs_log2) || key >= L) ? 0.f : pr;
       dsb[v >> 3][v & 7] = (_Float16)(pr * (dp[v] - dl));
@@ -244,15 +252,15 @@ __global__ void __launch_bounds__(256, 2)
       for (int d4 = 0; d4 < 4; ++d4) acc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[d4], dsb[c2], acc[d4], 0, 0, 0);
     }
   };
-  for (int j = 0; j < nkt; ++j) {
+  for (int j = kt_lo; j < nkt; ++j) {
     // distinct restrict pointers: the loads into the other buffer cannot alias
     // this tile's LDS reads, so the compiler puts no wait on them
     auto step = [&](const DqBuf* __restrict__ cur, DqBuf* __restrict__ nxt) __attribute__((always_inline)) {
       if (j + 1 < nkt) dma(nxt, j + 1);
-      if (j < n_free) tile(cur, j * QBN, std::integral_constant<int, 0>{});
-      else tile(cur, j * QBN, std::integral_constant<int, MODE == 0 ? 1 : 2>{});
+      if (j < n_free && j >= f_lo) tile(cur, j * QBN, std::integral_constant<int, 0>{});
+      else tile(cur, j * QBN, std::integral_constant<int, TTT_ ? 1 : 2>{});
     };
-    step(&sm.buf[j & 1], &sm.buf[(j + 1) & 1]);
+    step(&sm.buf[(j - kt_lo) & 1], &sm.buf[(j - kt_lo + 1) & 1]);
     TTT_WAIT_VMCNT(0);  // tile j+1 has landed
     __syncthreads();    // and every wave is done with tile j
   }
@@ -302,10 +310,10 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
       for (int e = 0; e < 4; ++e) a[e] = x0[e], a[4 + e] = x1[e], a[8 + e] = y0[e], a[12 + e] = y1[e];
     }
-    const int pos = MODE == 0 ? i + P.p - 1 : block_anchor(P, b, i) + (i & ((1 << P.bs_log2) - 1));
+    const int pos = TTT_ ? i + P.p - 1 : block_anchor(P, b, i) + (i & ((1 << P.bs_log2) - 1));
     const float* cq = cosT + (int64_t)pos * 64 + dlo;
     const float* sq = sinT + (int64_t)pos * 64 + dlo;
-    if (MODE == 0 && P.p > 1) {
+    if (TTT_ && P.p > 1) {
       float qr[16], go[16];
       {
         const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + i) * P.qs_t + hh * P.qs_h;
@@ -390,7 +398,8 @@ struct KvBuf {
 };
 
 
-// MODE 0: TTT pass (trunk keys, rows i >= j).  Block drafting: MODE 2 the
+// MODE 0: TTT pass (trunk keys, rows i >= j); MODE 4: the same with a
+// sliding window (rows j <= i < j + win).  Block drafting: MODE 2 the
 // context keys (P.kv_len of them; row i sees key j < its block's anchor),
 // MODE 3 the block keys (seen by the rows of their own block only).  kt, kv.v[0]
 // and gr.dk[0] / gr.dv[0] are those keys' K~ slab, V and gradients (P.ks_*
@@ -402,6 +411,8 @@ __global__ void __launch_bounds__(256, 1)
                      const float* __restrict__ delta, const int4* __restrict__ tiles, const float* __restrict__ cosT,
                      const float* __restrict__ sinT, PassGradPtrs gr) {
   __shared__ __attribute__((aligned(16))) KvBuf sm[NBUF];
+  constexpr bool TTT_ = MODE == 0 || MODE == 4;  // TTT pass (4: with a sliding window)
+  const int win = MODE == 4 ? P.win : 0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   // Order: key tiles heavy-first (ascending tile index), and every (batch, KV
@@ -434,6 +445,8 @@ __global__ void __launch_bounds__(256, 1)
   // query rows [row_lo, row_hi) that can see this key tile
   int row_lo = kv0, row_hi = L;
   if constexpr (MODE == 3) row_hi = min(kv0 + BKV, L);
+  if constexpr (TTT_)
+    if (win > 0) row_hi = min(L, kv0 + BKV - 1 + win);  // sliding window: rows i < j + win
   if constexpr (MODE == 2) {
     // the first block whose anchor passes kv0 (any anchor order): rows before
     // it see no key here.  Every wave scans all anchors itself: no shared
@@ -448,7 +461,7 @@ __global__ void __launch_bounds__(256, 1)
   // position of this lane's key (block keys: the slot position in its block)
   int kpos = my_key;
   if constexpr (MODE == 3) kpos = key_ok ? block_anchor(P, b, my_key) + (my_key & ((1 << P.bs_log2) - 1)) : 0;
-  if constexpr (MODE != 0) {
+  if constexpr (!TTT_) {
     // every global load above has landed before the first staging load: the
     // compiler's load counter is then exact and no full wait lands in the loop
     TTT_WAIT_VMCNT(0);
@@ -602,8 +615,9 @@ __global__ void __launch_bounds__(256, 1)
         const float lv = (e < 4 ? l0[e] : l1[e - 4]) * kLog2e;
         const float dv_ = e < 4 ? d0[e] : d1[e - 4];
         float pr = fast_exp2(__builtin_fmaf(s_c[v], sl2, -lv));
-        if constexpr (MODE == 0) {
-          pr = e >= thr ? pr : 0.f;
+        if constexpr (TTT_) {  // row - key = e - thr: visible iff 0 <= e - thr (< win)
+          if constexpr (MODE == 4) pr = (unsigned)(e - thr) < (unsigned)win ? pr : 0.f;  // win > 0 here
+          else pr = e >= thr ? pr : 0.f;
         } else if constexpr (MODE == 2) {  // key j visible iff j < the row's (clamped) anchor
           const int an = e == 0 ? a0.x : e == 1 ? a0.y : e == 2 ? a0.z : e == 3 ? a0.w
                        : e == 4 ? a1.x : e == 5 ? a1.y : e == 6 ? a1.z : a1.w;
@@ -780,7 +794,10 @@ void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const
   const int64_t grid = P.layout == 0
                            ? (int64_t)8 * ((P.B * P.Hkv + 7) / 8) * ((P.stok + bwd::BKV - 1) / bwd::BKV)
                            : (int64_t)P.Hkv * ((P.stok + bwd::BKV - 1) / bwd::BKV + P.nseq);
-  bwd::dkdv_bf16_kernel<0><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);
+  if (P.win > 0)  // sliding window: its own instantiation (MODE 4)
+    bwd::dkdv_bf16_kernel<4><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);
+  else
+    bwd::dkdv_bf16_kernel<0><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);
 }
 
 void launch_block_dkdv_bf16(const Prob& P, bool ctx_keys, const uint16_t* v, const float* lse, const uint16_t* dout,
@@ -823,10 +840,20 @@ int dq_tile_rows(int r) { return bwd::dq_rows(bwd::dq_heads_per_wg(r)); }
 void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
                     const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
                     const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st) {
+  const bool w = P.win > 0;  // sliding window: its own instantiation (MODE 4)
   switch (bwd::dq_heads_per_wg(P.r)) {
-    case 4: launch_dq_rh<4, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st); break;
-    case 2: launch_dq_rh<2, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st); break;
-    default: launch_dq_rh<1, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st); break;
+    case 4:
+      if (w) launch_dq_rh<4, 4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
+      else launch_dq_rh<4, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
+      break;
+    case 2:
+      if (w) launch_dq_rh<2, 4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
+      else launch_dq_rh<2, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
+      break;
+    default:
+      if (w) launch_dq_rh<1, 4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
+      else launch_dq_rh<1, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
+      break;
   }
 }
 

@@ -75,7 +75,9 @@ __device__ __forceinline__ int perm_row(int a) { return (a & ~0xC) | ((a & 4) <<
 // Rows of one work item, per R' (heads per workgroup).
 __host__ __device__ constexpr int tile_rows(int heads_per_wg) { return 32 * 4 / heads_per_wg; }
 
-// MODE 0: TTT pass (trunk + branch).  MODE 1: block drafting -- the trunk is
+// MODE 0: TTT pass (trunk + branch); MODE 4: the same with a sliding-window
+// trunk (a separate instantiation, so the windowless loop carries no window
+// test).  MODE 1: block drafting -- the trunk is
 // the context prefix j < anchor of each row's block (kt/vt), then the keys of
 // the work item's own blocks (kbt/vbt) in one more masked tile pass.
 template <int RH, bool O_F32, int MODE>
@@ -86,6 +88,8 @@ __global__ void __launch_bounds__(256, 2)
                     const _Float16* __restrict__ kbt, const uint16_t* __restrict__ vbt) {
   constexpr int RT = tile_rows(RH);  // rows per work item
   __shared__ __attribute__((aligned(16))) Smem sm;
+  constexpr bool TTT_ = MODE == 0 || MODE == 4;  // TTT pass (4: with a sliding window)
+  const int win = MODE == 4 ? P.win : 0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
 
@@ -118,7 +122,7 @@ __global__ void __launch_bounds__(256, 2)
   {
     const bool valid = my_row < L;
     const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + my_row) * P.qs_t + h * P.qs_h;
-    const int pos = MODE == 0 ? P.q_off + my_row + P.p - 1
+    const int pos = TTT_ ? P.q_off + my_row + P.p - 1
                               : (valid ? block_anchor(P, b, my_row) + (my_row & ((1 << P.bs_log2) - 1)) : 0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -172,8 +176,10 @@ __global__ void __launch_bounds__(256, 2)
       if ((blk << P.bs_log2) < wend && ((blk + 1) << P.bs_log2) > wave_row0) lim_lo = min(lim_lo, a);
     }
   }
-  const int kmax = MODE == 0 ? min(qend - 1 + dq_, kv_len - 1) : lim_hi - 1;  // last key any row sees
+  const int kmax = TTT_ ? min(qend - 1 + dq_, kv_len - 1) : lim_hi - 1;  // last key any row sees
   const int nkt = kmax < 0 ? 0 : kmax / BN + 1;
+  // sliding window: the first tile any row of the work item sees
+  const int kt_lo = (TTT_ && win > 0) ? max(0, row0 + dq_ - win + 1) / BN : 0;
   const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
   const uint16_t* vbase = vt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
   // DMA lane roles, loads n = w*KL + i.  K~: 1 KB = rows 4n + lane/16, slot
@@ -211,11 +217,11 @@ __global__ void __launch_bounds__(256, 2)
     else TTT_WAIT_VMCNT(2 * TL);
   };
 
-  dma(&sm.ring[0], 0);
+  if (kt_lo < nkt) dma(&sm.ring[0], kt_lo);
 #pragma unroll
   for (int tt = 1; tt < NBUF - 1; ++tt)
-    if (tt < nkt) dma(&sm.ring[tt], tt);
-  wait_tiles(min(nkt, NBUF - 1) - 1);
+    if (kt_lo + tt < nkt) dma(&sm.ring[tt], kt_lo + tt);
+  wait_tiles(min(nkt - kt_lo, NBUF - 1) - 1);
   __syncthreads();
 
   f32x16 oacc[4];
@@ -227,7 +233,9 @@ __global__ void __launch_bounds__(256, 2)
   const int prow = perm_row(l32);
   const float sl2 = P.scale_log2;
   // Tiles whose every key precedes every row of this wave need no mask.
-  const int n_free = MODE == 0 ? max(0, min(wave_row0 + 1 + dq_, kv_len)) / BN : lim_lo / BN;
+  const int n_free = TTT_ ? max(0, min(wave_row0 + 1 + dq_, kv_len)) / BN : lim_lo / BN;
+  // and, with a window, tiles from f_lo on: every key is inside every row's window
+  const int f_lo = (TTT_ && win > 0) ? max(0, wave_row0 + 31 + dq_ - win + 1 + BN - 1) / BN : 0;
 
   // Moves the running max to mx when mx exceeds it by more than 8 (log2 units).
   auto raise_max = [&](float mx) {
@@ -278,7 +286,8 @@ __global__ void __launch_bounds__(256, 2)
         for (int v = 0; v < 16; ++v) {
           const int key = key0 + kb * 32 + (v >> 3) * 16 + hf * 8 + (v & 7);
           bool off;
-          if constexpr (M == 1) off = key > my_row + dq_ || key >= kv_len;
+          if constexpr (M == 1)
+            off = key > my_row + dq_ || key >= kv_len || (MODE == 4 && key <= my_row + dq_ - win);
           else if constexpr (M == 2) off = key >= lim;
           else off = (key >> P.bs_log2) != (my_row >> P.bs_log2) || key >= L;
           if (off) sacc[kb][v] = -INFINITY;
@@ -323,13 +332,14 @@ __global__ void __launch_bounds__(256, 2)
   // Iteration j loads tile j+NBUF-1 into the buffer tile j-1 used and runs
   // tile j.  The two buffers go through distinct restrict pointers, so the
   // compiler knows the loads cannot alias this tile's LDS reads.
-  for (int kt_ = 0; kt_ < nkt; ++kt_) {
+  for (int kt_ = kt_lo; kt_ < nkt; ++kt_) {
     auto step = [&](const Tile* __restrict__ cur, Tile* __restrict__ dst) __attribute__((always_inline)) {
       if (kt_ + NBUF - 1 < nkt) dma(dst, kt_ + NBUF - 1);
-      if (kt_ < n_free) tile(cur, kt_ * BN, std::integral_constant<int, 0>{});
-      else tile(cur, kt_ * BN, std::integral_constant<int, MODE == 0 ? 1 : 2>{});
+      if (kt_ < n_free && kt_ >= f_lo) tile(cur, kt_ * BN, std::integral_constant<int, 0>{});
+      else tile(cur, kt_ * BN, std::integral_constant<int, TTT_ ? 1 : 2>{});
     };
-    step(&sm.ring[kt_ % NBUF], &sm.ring[(kt_ + NBUF - 1) % NBUF]);
+    const int rb = kt_ - kt_lo;
+    step(&sm.ring[rb % NBUF], &sm.ring[(rb + NBUF - 1) % NBUF]);
     if (kt_ + 1 < nkt) wait_tiles(min(nkt, kt_ + NBUF) - (kt_ + 2));  // tile kt_+1 has landed
     __syncthreads();                                                    // every wave is done with tile kt_
   }
@@ -351,7 +361,7 @@ __global__ void __launch_bounds__(256, 2)
 
   // ---- branch: keys/values of passes 2..p at the same row, folded into (m, l, O)
   const int lr = rbk * 32 + l32;  // this lane's row within the tile
-  for (int qq = 2; qq <= (MODE == 0 && P.branch ? P.p : 1); ++qq) {
+  for (int qq = 2; qq <= (TTT_ && P.branch ? P.p : 1); ++qq) {
     // stage R(i+q-1) k^(q) (fp16) and v^(q) (bf16) for the tile's rows: 8 threads per row
     for (int r0 = 0; r0 < RT; r0 += 32) {
       const int rr = r0 + (tid >> 3), c8 = tid & 7;
@@ -495,7 +505,10 @@ int fwd_tile_rows(int r) { return fwd::tile_rows(fwd::heads_per_wg(r)); }
 void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const uint16_t* vt,
                      const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
                      hipStream_t st) {
-  fwd::launch_mode<0>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, nullptr, nullptr, st);
+  if (P.win > 0)
+    fwd::launch_mode<4>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, nullptr, nullptr, st);
+  else
+    fwd::launch_mode<0>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, nullptr, nullptr, st);
 }
 
 void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const uint16_t* vt,

@@ -51,6 +51,9 @@ struct Prob {
   const int* anchors;
   int bs_log2, nblk, spad_b;
   int64_t cs_b, cs_t, cs_h;  // block-draft backward: context K/V strides (P.ks_*: the block K/V)
+  // Sliding-window trunk (TTT passes): win > 0 limits row i's trunk to the
+  // pass-1 keys at positions (pos_i - win, pos_i]; 0 = the full causal trunk.
+  int win;
 };
 
 __device__ __forceinline__ int block_anchor(const Prob& P, int b, int row) {

@@ -125,6 +125,9 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
     const int64_t qend = c->q_offset + stok + p - 1, kend = c->kv_offset + c->kv_len;
     P.npos = (int)(qend > kend ? qend : kend);
   }
+  if (d->window < 0) return fail(TTT_ERR_BAD_SHAPE, "window %d is negative", d->window);
+  if (d->window > 0 && !bf16) return fail(TTT_ERR_UNSUPPORTED, "a sliding window is built for bf16 only");
+  P.win = d->window;
   P.scale = d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / sqrtf((float)D);
   P.scale_log2 = P.scale * ttt::kLog2e;
   const bool thd = d->layout == TTT_LAYOUT_THD;
@@ -484,6 +487,7 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
   if (d->layout != TTT_LAYOUT_BSHD) return fail(TTT_ERR_UNSUPPORTED, "block drafting takes the BSHD layout");
   if (!pl.bf16) return fail(TTT_ERR_UNSUPPORTED, "block drafting is built for bf16");
   if (d->pass_index != 1) return fail(TTT_ERR_BAD_SHAPE, "block drafting has no passes: pass_index must be 1");
+  if (d->window != 0) return fail(TTT_ERR_UNSUPPORTED, "block drafting takes no sliding window");
   const int bs = bk->block_size;
   if (bs < 1 || bs > 32 || (bs & (bs - 1)))
     return fail(TTT_ERR_UNSUPPORTED, "block_size %d: 1, 2, 4, 8, 16 or 32", bs);

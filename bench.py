@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel event timing")
+    ap.add_argument("--window", type=int, default=0, metavar="W",
+                    help="sliding-window trunk of W keys for the unroll (0: the full causal trunk)")
     ap.add_argument("--ring", type=int, default=0, metavar="CP",
                     help="instead of the unroll, time the ring-step forward of the last pass over a zig-zag ring "
                          "of CP ranks emulated on this GPU, per chunk shape (prints its own JSON line)")
@@ -57,9 +59,16 @@ def parse():
 
 
 # ----------------------------------------------------------------------------- work accounting
+WINDOW = 0  # sliding-window trunk of the measured unroll (0: full causal trunk)
+
+
 def trunk_pairs(w) -> int:
-    """Causal (query, key) pairs of the trunk per head per pass: sum over sequences of L(L+1)/2."""
-    return sum(L * (L + 1) // 2 for L in w.lengths())
+    """Visible (query, key) pairs of the trunk per head per pass: sum over sequences of L(L+1)/2,
+    or of sum_i min(i + 1, W) with a sliding window of W keys."""
+    if WINDOW <= 0:
+        return sum(L * (L + 1) // 2 for L in w.lengths())
+    W = WINDOW
+    return sum((min(L, W) * (min(L, W) + 1)) // 2 + max(0, L - W) * W for L in w.lengths())
 
 
 def useful_flops(w, p: int) -> tuple[float, float]:
@@ -416,6 +425,8 @@ def main():
     if args.soft_ce:
         soft_ce_main(args, dev)
         return
+    global WINDOW
+    WINDOW = max(0, args.window)
     w = syn.workload(args.workload)
     if args.ring:
         ring_main(args, w, dev)
@@ -436,7 +447,7 @@ def main():
     d_f = tk.make_desc(q[K], ks, K, cu_seqlens=cu, rope_base=w.rope_base)
     ws_bytes = max(tk.workspace_bytes(d_f, False), tk.workspace_bytes(d_f, True))
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
-    kw = dict(cu_seqlens=cu, rope_base=w.rope_base, workspace=ws)
+    kw = dict(cu_seqlens=cu, rope_base=w.rope_base, workspace=ws, window=WINDOW)
 
     def step():
         for p in range(1, K + 1):
@@ -553,7 +564,7 @@ def main():
                    "step": f"fwd p=1..{K} then bwd p={K}..1", "useful_tflop_per_step": round(flops_step / 1e12, 4),
                    "fwd_useful_tflop_per_step": round(fwd_flops_step / 1e12, 4),
                    "mfma_operands": "fp16 Q~K~^T and dS, bf16 P.V, dO.V, P^T.dO; fp32 accumulate",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "window": WINDOW},
         "roofline": roofline,
         "kernels": kernels,
         "source_digest": source_digest(),

@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TTT_ATTN_ABI_VERSION 1
+#define TTT_ATTN_ABI_VERSION 2
 
 enum ttt_attn_layout { TTT_LAYOUT_BSHD = 0, TTT_LAYOUT_THD = 1 };
 enum ttt_attn_dtype { TTT_DTYPE_BF16 = 0, TTT_DTYPE_FP32 = 1 };
@@ -100,6 +100,11 @@ typedef struct ttt_attn_desc {
   int64_t q_stride[3];        /* batch, token, head strides of q / dq (elements)           */
   int64_t kv_stride[3];       /* ... of every k, v, dk, dv                                 */
   int64_t o_stride[3];        /* ... of o / dout                                           */
+  int32_t window;             /* sliding-window trunk: > 0 limits row i to the pass-1 keys
+                                 j with i - window < j <= i (positions, so ring steps too);
+                                 0 = full causal trunk; the branch is unchanged.  Same
+                                 issue, item 4 (sliding-window layers).  bf16 only      */
+  int32_t reserved;           /* 0                                                         */
 } ttt_attn_desc;
 
 /* Bytes of caller-provided device workspace a forward (for_bwd = 0) or

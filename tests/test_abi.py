@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
             "ttt_attn_last_error", "ttt_attn_abi_version", "ttt_attn_set_trace_hook"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ttt_attn_abi_version() == 1
+    assert lib.ttt_attn_abi_version() == 2
 
 
 def test_status_strings():
@@ -403,3 +403,16 @@ def test_soft_ce_struct_and_validation():
     assert bwd(ce_desc(), g=None) == 1 and "dstudent" in err()
     assert bwd(ce_desc(), dl=None) == 1 and "dloss" in err()
     assert bwd(ce_desc(), ll=FAKE + 2) == 4
+
+
+def test_window_validation():
+    d = good_desc()
+    d.window = -1
+    assert call_fwd(d) == 2 and "window" in err()
+    d = good_desc(dtype=tk.DTYPE_FP32)
+    d.window = 8
+    assert call_fwd(d) == 3 and "window" in err()
+    d = block_desc()
+    d.window = 4
+    assert call_block(d, good_block()) == 3 and "window" in err()
+    assert ctypes.sizeof(tk.Desc) == 144
