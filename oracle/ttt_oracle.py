@@ -91,7 +91,7 @@ import numpy as np
 
 __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_position",
            "ttt_mask_row", "trunk_window_start", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows", "Slice",
-           "fwd_chunk", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd",
+           "fwd_chunk", "bwd_chunk", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd",
            "block_bwd_rows", "block_bwd", "soft_ce_rows_counted", "soft_ce"]
 
 
@@ -418,6 +418,66 @@ def fwd_chunk(q, k0, v0, branch_ks, branch_vs, p: int, *, q_offset: int, kv_offs
                     lse[b, h, i] = mx + math.log(w.sum())
                     O[b, i, h] = (w / w.sum()) @ np.concatenate(vals, axis=0)
     return O, lse
+
+
+def bwd_chunk(q, k0, v0, branch_ks, branch_vs, p: int, dout, o, lse, *, q_offset: int, kv_offset: int,
+              scale: Optional[float] = None, base: float = 0.0, window: int = 0):
+    """Backward contributions of one ring step (same inputs and positions as fwd_chunk).
+
+    o and lse are the rows' final outputs over every key of the sequence (the
+    merged ring result), so that P = exp(s - lse) and Delta = <dout, o> are the
+    whole-sequence values; the step contributes the chain-rule terms of its own
+    keys.  Returns (dq [B, n, Hq, D], dk0 [B, m, Hkv, D], dv0, [dk of passes 2..p],
+    [dv of passes 2..p]) in fp64 (the branch lists are empty without branch
+    keys); summing every step's terms gives the whole-sequence gradients."""
+    B, n, Hq, D = q.shape
+    m, Hkv = k0.shape[1], k0.shape[2]
+    r = Hq // Hkv
+    if scale is None or scale <= 0:
+        scale = 1.0 / math.sqrt(D)
+    rows = np.arange(n)
+    qpos = q_offset + rows
+    kpos = kv_offset + np.arange(m)
+    nb = p - 1 if branch_ks is not None else 0
+    dq = np.zeros((B, n, Hq, D))
+    dk0, dv0 = np.zeros((B, m, Hkv, D)), np.zeros((B, m, Hkv, D))
+    dkb = [np.zeros((B, n, Hkv, D)) for _ in range(nb)]
+    dvb = [np.zeros((B, n, Hkv, D)) for _ in range(nb)]
+    for b in range(B):
+        for g in range(Hkv):
+            kr = rotate_half(np.asarray(k0[b, :, g], np.float64), kpos, base)
+            vv = np.asarray(v0[b, :, g], np.float64)
+            vis = ring_visible(qpos, kpos, window)
+            bk = [rotate_half(np.asarray(branch_ks[t][b, :, g], np.float64), key_position(t + 2, qpos), base)
+                  for t in range(nb)]
+            bv = [np.asarray(branch_vs[t][b, :, g], np.float64) for t in range(nb)]
+            dk_rot = np.zeros((m, D))
+            dkb_rot = [np.zeros((n, D)) for _ in range(nb)]
+            for h in range(g * r, (g + 1) * r):
+                qr = rotate_half(np.asarray(q[b, :, h], np.float64), query_position(qpos, p), base)
+                for i in range(n):
+                    do = np.asarray(dout[b, i, h], np.float64)
+                    delta = do @ np.asarray(o[b, i, h], np.float64)
+                    L_i = float(lse[b, h, i])
+                    dq_rot = np.zeros(D)
+                    js = np.flatnonzero(vis[i])
+                    if js.size:
+                        P = np.exp(scale * (kr[js] @ qr[i]) - L_i)
+                        dS = P * (vv[js] @ do - delta)
+                        dq_rot += scale * (dS @ kr[js])
+                        dk_rot[js] += scale * dS[:, None] * qr[i][None, :]
+                        dv0[b, js, g] += P[:, None] * do[None, :]
+                    for t in range(nb):
+                        Pb = math.exp(scale * (bk[t][i] @ qr[i]) - L_i)
+                        dSb = Pb * (bv[t][i] @ do - delta)
+                        dq_rot += scale * dSb * bk[t][i]
+                        dkb_rot[t][i] += scale * dSb * qr[i]
+                        dvb[t][b, i, g] += Pb * do
+                    dq[b, i, h] = unrotate_half(dq_rot, query_position(q_offset + i, p), base)
+            dk0[b, :, g] = unrotate_half(dk_rot, kpos, base)
+            for t in range(nb):
+                dkb[t][b, :, g] = unrotate_half(dkb_rot[t], key_position(t + 2, qpos), base)
+    return dq, dk0, dv0, dkb, dvb
 
 
 def merge(o_a, lse_a, o_b, lse_b):

@@ -603,6 +603,39 @@ def check_window_ring_partition():
         assert np.max(np.abs(acc_l[0] - rl[:, qa:qa + c])) < 1e-12
 
 
+def check_chunk_bwd_partition():
+    """Ring-step backward terms summed over a zig-zag partition (branch on the diagonal step,
+    whole-sequence O and LSE) equal the whole-sequence backward, with and without a window."""
+    S, Hq, Hkv, D, p, base, cp = 16, 4, 2, 8, 3, 1e4, 2
+    q, ks, vs, do = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=99, B=1)
+    for window in (0, 6):
+        o, lse = O.fwd(q, ks, vs, p, base=base, window=window)
+        dQ, dK, dV = O.bwd(q, ks, vs, do, p, base=base, window=window)
+        c = S // (2 * cp)
+        gq = np.zeros_like(dQ)
+        gk = [np.zeros_like(dK[0]) for _ in range(p)]
+        gv = [np.zeros_like(dV[0]) for _ in range(p)]
+        for qc in range(2 * cp):
+            qa = qc * c
+            for kc in range(2 * cp):
+                ka = kc * c
+                br = kc == qc
+                dq_, dk0, dv0, dkb, dvb = O.bwd_chunk(
+                    q[:, qa:qa + c], ks[0][:, ka:ka + c], vs[0][:, ka:ka + c],
+                    [k[:, qa:qa + c] for k in ks[1:]] if br else None, [v[:, qa:qa + c] for v in vs[1:]] if br else None,
+                    p, do[:, qa:qa + c], o[:, qa:qa + c], lse[:, :, qa:qa + c], q_offset=qa, kv_offset=ka, base=base,
+                    window=window)
+                gq[:, qa:qa + c] += dq_
+                gk[0][:, ka:ka + c] += dk0
+                gv[0][:, ka:ka + c] += dv0
+                for t in range(len(dkb)):
+                    gk[t + 1][:, qa:qa + c] += dkb[t]
+                    gv[t + 1][:, qa:qa + c] += dvb[t]
+        assert np.max(np.abs(gq - dQ)) < 1e-12
+        for t in range(p):
+            assert np.max(np.abs(gk[t] - dK[t])) < 1e-12 and np.max(np.abs(gv[t] - dV[t])) < 1e-12
+
+
 PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check_zero_query_closed_form,
         lambda: check_zero_query_closed_form("thd"), check_sdpa_brute_force, check_p1_is_causal_sdpa,
         check_merge_invariant, check_branch_relative_position, check_grad_autograd,
@@ -610,7 +643,7 @@ PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check
         check_sampled_rows_match_full, check_chunk_rows_match_dense, check_chunk_ring_partition,
         check_merge_closed_form, check_block_sdpa_mask, check_block_zero_query_closed_form,
         check_block_size1_is_causal, check_block_grad_autograd, check_soft_ce_library, check_soft_ce_closed_forms,
-        check_window_sdpa_and_grad, check_window_closed_forms, check_window_ring_partition]
+        check_window_sdpa_and_grad, check_window_closed_forms, check_window_ring_partition, check_chunk_bwd_partition]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
