@@ -144,6 +144,12 @@ def library() -> ctypes.CDLL:
         lib.ttt_attn_fwd_chunk.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Chunk), vp, ctypes.POINTER(vp),
                                            ctypes.POINTER(vp), vp, vp, vp, sz, vp]
         lib.ttt_attn_fwd_chunk.restype = ctypes.c_int
+        lib.ttt_attn_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Chunk)]
+        lib.ttt_attn_chunk_bwd_workspace_bytes.restype = sz
+        lib.ttt_attn_bwd_chunk.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Chunk), vp, ctypes.POINTER(vp),
+                                           ctypes.POINTER(vp), vp, vp, vp, vp, ctypes.POINTER(vp),
+                                           ctypes.POINTER(vp), vp, sz, vp]
+        lib.ttt_attn_bwd_chunk.restype = ctypes.c_int
         lib.ttt_attn_merge.argtypes = [ctypes.POINTER(Desc), vp, vp, vp, vp, vp, vp, vp]
         lib.ttt_attn_merge.restype = ctypes.c_int
         lib.ttt_attn_block_workspace_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Block), ctypes.c_int]
@@ -352,6 +358,46 @@ def fwd_chunk(q, ks: Sequence, vs: Sequence, p: int, *, q_offset: int, kv_offset
     _check(library().ttt_attn_fwd_chunk(ctypes.byref(d), ctypes.byref(c), q.data_ptr(), _ptrs(ks[:n]),
                                         _ptrs(vs[:n]), out.data_ptr(), lse.data_ptr(), wp, wn, _stream(stream)))
     return out, lse
+
+
+def bwd_chunk(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, q_offset: int, kv_offset: int,
+              with_branch: bool, softmax_scale: float = 0.0, rope_base: float = 0.0, window: int = 0,
+              workspace=None, stream=None):
+    """Backward terms of one ring step (BSHD, bf16 inputs): o, lse, dout are the query rows'
+    whole-sequence values.  Returns fp32 (dq, [dk0, branch dk...], [dv0, branch dv...]); the
+    branch lists hold passes 2..p only with with_branch.  Summing the steps' terms gives the
+    whole-sequence gradients."""
+    torch = _torch()
+    n_br = p - 1 if with_branch else 0
+    branch_ks = list(ks[1:p]) if with_branch else []
+    d = make_desc(q, (branch_ks or [ks[0]]), p, softmax_scale=softmax_scale, rope_base=rope_base,
+                  o_dtype=_dtype_code(o), o_like=o, window=window)
+    if dout.stride() != o.stride():
+        raise ValueError("dout must have the strides of o")
+    lse = lse.contiguous()  # the C ABI reads the step rows' LSE as a dense [B, Hq, rows] array
+    c = make_chunk(q_offset, kv_offset, ks[0], with_branch=with_branch)
+
+    def like32(t):  # fp32 output with t's element strides (dense layouts keep their strides)
+        return torch.empty_strided(t.shape, t.stride(), dtype=torch.float32, device=t.device)
+    dq = like32(q)
+    dks = [like32(ks[0])] + [like32(t) for t in branch_ks]
+    dvs = [like32(vs[0])] + [like32(t) for t in list(vs[1:p])[:n_br]]
+    nbytes = int(library().ttt_attn_chunk_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(c)))
+    if nbytes == 0:
+        raise TTTAttnError(2, library().ttt_attn_last_error().decode())
+    ws = _workspace(nbytes, q.device, workspace)
+    wp, wn = _ws_ptr(ws)
+    nptr = 1 + n_br
+    kp, vp_ = _ptrs(list(ks[:nptr])), _ptrs(list(vs[:nptr]))
+    if ks[0].numel() == 0:
+        kp[0] = vp_[0] = None
+    gk, gv = _ptrs(dks), _ptrs(dvs)
+    if ks[0].numel() == 0:
+        gk[0] = gv[0] = None
+    _check(library().ttt_attn_bwd_chunk(ctypes.byref(d), ctypes.byref(c), q.data_ptr(), kp, vp_, o.data_ptr(),
+                                        lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), gk, gv, wp, wn,
+                                        _stream(stream)))
+    return dq, dks, dvs
 
 
 def merge(o_a, lse_a, o_b, lse_b, *, out=None, lse=None, cu_seqlens=None, stream=None):

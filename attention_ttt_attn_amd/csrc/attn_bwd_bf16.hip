@@ -130,18 +130,23 @@ __global__ void __launch_bounds__(256, 2)
       if ((blk << P.bs_log2) < wend && ((blk + 1) << P.bs_log2) > wave_row0) lim_lo = min(lim_lo, a);
     }
   }
-  const int nkt = TTT_ ? (qend + QBN - 1) / QBN : (lim_hi + QBN - 1) / QBN;  // TTT: >= 1 (row0 < L)
+  // TTT ring steps (BSHD): row i sits at position q_off + i, trunk key j at
+  // kv_off + j (j < kv_len); whole-sequence calls have dq_ = 0, kvn = L.
+  const int dq_ = (TTT_ && P.layout == 0) ? P.q_off - P.kv_off : 0;
+  const int kvn = (TTT_ && P.layout == 0) ? P.kv_len : (TTT_ ? L : P.kv_len);
+  const int kmax = TTT_ ? min(qend - 1 + dq_, kvn - 1) : lim_hi - 1;  // last key any row sees
+  const int nkt = kmax < 0 ? 0 : kmax / QBN + 1;
   // sliding window: the first key tile any row of the work item sees
-  const int kt_lo = (TTT_ && win > 0) ? max(0, row0 - win + 1) / QBN : 0;
+  const int kt_lo = (TTT_ && win > 0) ? max(0, row0 + dq_ - win + 1) / QBN : 0;
 
   // DMA lane roles, 6 loads per wave per tile (load n = 2w + i):
   // K~ and V rows 4n + lane/16, slot lane%16; K~^T d-rows 16n + lane/4, slot lane%4.
   const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
   const _Float16* ktbase = ktt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
-  const int64_t vs_b = TTT_ ? P.ks_b : P.cs_b, vs_t = TTT_ ? P.ks_t : P.cs_t;
-  const int64_t vs_h = TTT_ ? P.ks_h : P.cs_h;
-  const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * vs_b + (int64_t)start * vs_t + g * vs_h;
-  const int vlast = (TTT_ ? L : P.kv_len) - 1;  // last key row of the trunk
+  // trunk V: P.cs_* strides (the pass-1 / context V; P.ks_* stay with the branch)
+  const int64_t vs_t = P.cs_t;
+  const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * P.cs_b + (int64_t)start * vs_t + g * P.cs_h;
+  const int vlast = kvn - 1;  // last key row of the trunk
   uint32_t roff[2], toff[2];
   int rrow[2];
 #pragma unroll
@@ -199,9 +204,9 @@ __global__ void __launch_bounds__(256, 2)
     for (int v = 0; v < 16; ++v) acc[d4][v] = 0.f;
   const int prow = perm_row(l32);
   // Tiles whose every key precedes every row of this wave need no mask.
-  const int n_free = TTT_ ? (wave_row0 + 1) / QBN : lim_lo / QBN;
+  const int n_free = TTT_ ? max(0, min(wave_row0 + 1 + dq_, kvn)) / QBN : lim_lo / QBN;
   // with a window, tiles from f_lo on lie inside every row's window
-  const int f_lo = (TTT_ && win > 0) ? max(0, wave_row0 + 31 - win + 1 + QBN - 1) / QBN : 0;
+  const int f_lo = (TTT_ && win > 0) ? max(0, wave_row0 + 31 + dq_ - win + 1 + QBN - 1) / QBN : 0;
 
   // S^T = K~ Q~^T, dP^T = V dO^T, dS = P (dP - Delta), dQ~^T += K~^T dS^T.
   // Masks: 1 causal, 2 context prefix key < lim, 3 the row's own block.
@@ -229,13 +234,13 @@ __global__ void __launch_bounds__(256, 2)
     // key of (v, hf) = key0 + 16*(v/8) + 8*hf + v%8
     f16x8 dsb[2];
     constexpr int M = decltype(masked)::value;
-    const int thr = my_row - (key0 + 8 * hf);
+    const int thr = my_row + dq_ - (key0 + 8 * hf);
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       float pr = fast_exp2(__builtin_fmaf(s[v], sl2, -lse2));
       const int key = key0 + (v >> 3) * 16 + 8 * hf + (v & 7);
       if constexpr (M == 1)
-        pr = ((v >> 3) * 16 + (v & 7) > thr || (MODE == 4 && key <= my_row - win)) ? 0.f : pr;
+        pr = ((v >> 3) * 16 + (v & 7) > thr || key >= kvn || (MODE == 4 && key <= my_row + dq_ - win)) ? 0.f : pr;
       else if constexpr (M == 2) pr = key >= lim ? 0.f : pr;
       else if constexpr (M == 3) pr = ((key >> P.bs_log2) != (my_row >> P.bs_log2) || key >= L) ? 0.f : pr;
       dsb[v >> 3][v & 7] = (_Float16)(pr * (dp[v] - dl));
@@ -310,10 +315,10 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
       for (int e = 0; e < 4; ++e) a[e] = x0[e], a[4 + e] = x1[e], a[8 + e] = y0[e], a[12 + e] = y1[e];
     }
-    const int pos = TTT_ ? i + P.p - 1 : block_anchor(P, b, i) + (i & ((1 << P.bs_log2) - 1));
+    const int pos = TTT_ ? P.q_off + i + P.p - 1 : block_anchor(P, b, i) + (i & ((1 << P.bs_log2) - 1));
     const float* cq = cosT + (int64_t)pos * 64 + dlo;
     const float* sq = sinT + (int64_t)pos * 64 + dlo;
-    if (TTT_ && P.p > 1) {
+    if (TTT_ && P.p > 1 && P.branch) {
       float qr[16], go[16];
       {
         const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + i) * P.qs_t + hh * P.qs_h;
@@ -340,7 +345,7 @@ __global__ void __launch_bounds__(256, 2)
         unpack_bf8(*(const u32x4*)(krow_ + dhi), x2);
         unpack_bf8(*(const u32x4*)(vrow_ + dlo), v1);
         unpack_bf8(*(const u32x4*)(vrow_ + dhi), v2);
-        const int pk = i + qq - 1;
+        const int pk = P.q_off + i + qq - 1;
         const float* ck = cosT + (int64_t)pk * 64 + dlo;
         const float* sk = sinT + (int64_t)pk * 64 + dlo;
         float kr[16];
@@ -369,9 +374,19 @@ __global__ void __launch_bounds__(256, 2)
       res[e] = a[e] * cq[e] + a[8 + e] * sq[e];
       res[8 + e] = a[8 + e] * cq[e] - a[e] * sq[e];
     }
-    uint16_t* orow = dq + b * P.qs_b + (int64_t)(start + i) * P.qs_t + hh * P.qs_h;
-    *(u32x4*)(orow + dlo) = pack_bf8(res);
-    *(u32x4*)(orow + dhi) = pack_bf8(res + 8);
+    const int64_t oi = b * P.qs_b + (int64_t)(start + i) * P.qs_t + hh * P.qs_h;
+    if (P.out_f32) {  // ring-step terms: fp32, q's element strides
+      float* orow = (float*)dq + oi;
+#pragma unroll
+      for (int e = 0; e < 8; e += 4) {
+        *(f32x4*)(orow + dlo + e) = f32x4{res[e], res[e + 1], res[e + 2], res[e + 3]};
+        *(f32x4*)(orow + dhi + e) = f32x4{res[8 + e], res[9 + e], res[10 + e], res[11 + e]};
+      }
+    } else {
+      uint16_t* orow = dq + oi;
+      *(u32x4*)(orow + dlo) = pack_bf8(res);
+      *(u32x4*)(orow + dhi) = pack_bf8(res + 8);
+    }
   }
 }
 
@@ -420,7 +435,7 @@ __global__ void __launch_bounds__(256, 1)
   // run together share that XCD's L2 for the query rows they all stream.
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   int b, t, start, L, slot0, g;
-  const int nkeys = MODE == 2 ? P.kv_len : P.stok;
+  const int nkeys = MODE == 3 ? P.stok : P.kv_len;  // TTT: kv_len = stok for whole-sequence calls
   if (P.layout == 0) {
     const int nkt = (nkeys + BKV - 1) / BKV;
     const int ppx = (P.B * P.Hkv + 7) / 8;  // pairs per XCD
@@ -441,12 +456,14 @@ __global__ void __launch_bounds__(256, 1)
   }
   const int kv0 = t * BKV;
   const int my_key = kv0 + wv * 32 + l32;
-  const bool key_ok = my_key < (MODE == 2 ? nkeys : L);
+  const bool key_ok = my_key < ((MODE == 2 || (TTT_ && P.layout == 0)) ? nkeys : L);
+  // TTT ring steps (BSHD): row i at q_off + i sees key j at kv_off + j iff i >= j - dq_
+  const int dq_ = (TTT_ && P.layout == 0) ? P.q_off - P.kv_off : 0;
   // query rows [row_lo, row_hi) that can see this key tile
-  int row_lo = kv0, row_hi = L;
+  int row_lo = TTT_ ? max(0, kv0 - dq_) & ~(BQ - 1) : kv0, row_hi = L;
   if constexpr (MODE == 3) row_hi = min(kv0 + BKV, L);
   if constexpr (TTT_)
-    if (win > 0) row_hi = min(L, kv0 + BKV - 1 + win);  // sliding window: rows i < j + win
+    if (win > 0) row_hi = min(L, max(0, kv0 + BKV - 1 - dq_ + win));  // sliding window: rows i < j - dq_ + win
   if constexpr (MODE == 2) {
     // the first block whose anchor passes kv0 (any anchor order): rows before
     // it see no key here.  Every wave scans all anchors itself: no shared
@@ -459,7 +476,7 @@ __global__ void __launch_bounds__(256, 1)
     row_lo = min(__builtin_amdgcn_readfirstlane(first) << P.bs_log2, L) & ~(BQ - 1);
   }
   // position of this lane's key (block keys: the slot position in its block)
-  int kpos = my_key;
+  int kpos = TTT_ ? P.kv_off + my_key : my_key;
   if constexpr (MODE == 3) kpos = key_ok ? block_anchor(P, b, my_key) + (my_key & ((1 << P.bs_log2) - 1)) : 0;
   if constexpr (!TTT_) {
     // every global load above has landed before the first staging load: the
@@ -604,7 +621,7 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int m0 = half * 16 + hf * 8;  // this lane's rows m = 16*(v/8) + 8*hf + v%8
-      const int thr = my_key - (q0 + m0);
+      const int thr = my_key - dq_ - (q0 + m0);
       const f32x4 l0 = *(const f32x4*)&Bc.lse[m0], l1 = *(const f32x4*)&Bc.lse[m0 + 4];
       const f32x4 d0 = *(const f32x4*)&Bc.dl[m0], d1 = *(const f32x4*)&Bc.dl[m0 + 4];
       int4 a0 = {0, 0, 0, 0}, a1 = {0, 0, 0, 0};
@@ -694,10 +711,19 @@ __global__ void __launch_bounds__(256, 1)
         vlo[e] = dv[d4][v4 * 4 + e];
         vhi[e] = dv[d4 + 2][v4 * 4 + e];
       }
-      *(u32x2*)(dkrow + d) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
-      *(u32x2*)(dkrow + d + 64) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
-      *(u32x2*)(dvrow + d) = u32x2{pack_bf2(vlo[0], vlo[1]), pack_bf2(vlo[2], vlo[3])};
-      *(u32x2*)(dvrow + d + 64) = u32x2{pack_bf2(vhi[0], vhi[1]), pack_bf2(vhi[2], vhi[3])};
+      if (P.out_f32) {  // ring-step terms: fp32, the keys' element strides
+        float* fk = (float*)gr.dk[0] + off;
+        float* fv = (float*)gr.dv[0] + off;
+        *(f32x4*)(fk + d) = f32x4{lo[0], lo[1], lo[2], lo[3]};
+        *(f32x4*)(fk + d + 64) = f32x4{hi[0], hi[1], hi[2], hi[3]};
+        *(f32x4*)(fv + d) = f32x4{vlo[0], vlo[1], vlo[2], vlo[3]};
+        *(f32x4*)(fv + d + 64) = f32x4{vhi[0], vhi[1], vhi[2], vhi[3]};
+      } else {
+        *(u32x2*)(dkrow + d) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
+        *(u32x2*)(dkrow + d + 64) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
+        *(u32x2*)(dvrow + d) = u32x2{pack_bf2(vlo[0], vlo[1]), pack_bf2(vlo[2], vlo[3])};
+        *(u32x2*)(dvrow + d + 64) = u32x2{pack_bf2(vhi[0], vhi[1]), pack_bf2(vhi[2], vhi[3])};
+      }
     }
 }
 
@@ -715,7 +741,7 @@ __global__ void __launch_bounds__(256)
   if (tok >= P.stok || !token_seq(P, tok, s, start, L)) return;
   const int i = tok - start, slot = seq_slot0(P, s) + i;
   const int dlo = c16 * 4, dhi = 64 + c16 * 4;
-  const int pq = i + P.p - 1;
+  const int pq = P.q_off + i + P.p - 1;
   const f32x4 cqa = *(const f32x4*)(cosT + (int64_t)pq * 64 + dlo);
   const f32x4 sqa = *(const f32x4*)(sinT + (int64_t)pq * 64 + dlo);
   const int64_t koff = b * P.ks_b + (int64_t)tok * P.ks_t + g * P.ks_h;
@@ -724,7 +750,7 @@ __global__ void __launch_bounds__(256)
     const uint16_t* vrow = (const uint16_t*)kv.v[qq - 1] + koff;
     const u32x2 ka = *(const u32x2*)(krow + dlo), kb2 = *(const u32x2*)(krow + dhi);
     const u32x2 va = *(const u32x2*)(vrow + dlo), vb2 = *(const u32x2*)(vrow + dhi);
-    const int pk = i + qq - 1;
+    const int pk = P.q_off + i + qq - 1;
     const f32x4 ck = *(const f32x4*)(cosT + (int64_t)pk * 64 + dlo);
     const f32x4 sk = *(const f32x4*)(sinT + (int64_t)pk * 64 + dlo);
     float kr[8], vv[8];
@@ -777,12 +803,21 @@ __global__ void __launch_bounds__(256)
       lo[e] = dk[e] * ck[e] + dk[4 + e] * sk[e];
       hi[e] = dk[4 + e] * ck[e] - dk[e] * sk[e];
     }
-    uint16_t* dkrow = (uint16_t*)gr.dk[qq - 1] + koff;
-    uint16_t* dvrow = (uint16_t*)gr.dv[qq - 1] + koff;
-    *(u32x2*)(dkrow + dlo) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
-    *(u32x2*)(dkrow + dhi) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
-    *(u32x2*)(dvrow + dlo) = u32x2{pack_bf2(dv[0], dv[1]), pack_bf2(dv[2], dv[3])};
-    *(u32x2*)(dvrow + dhi) = u32x2{pack_bf2(dv[4], dv[5]), pack_bf2(dv[6], dv[7])};
+    if (P.out_f32) {  // ring-step terms: fp32
+      float* fk = (float*)gr.dk[qq - 1] + koff;
+      float* fv = (float*)gr.dv[qq - 1] + koff;
+      *(f32x4*)(fk + dlo) = f32x4{lo[0], lo[1], lo[2], lo[3]};
+      *(f32x4*)(fk + dhi) = f32x4{hi[0], hi[1], hi[2], hi[3]};
+      *(f32x4*)(fv + dlo) = f32x4{dv[0], dv[1], dv[2], dv[3]};
+      *(f32x4*)(fv + dhi) = f32x4{dv[4], dv[5], dv[6], dv[7]};
+    } else {
+      uint16_t* dkrow = (uint16_t*)gr.dk[qq - 1] + koff;
+      uint16_t* dvrow = (uint16_t*)gr.dv[qq - 1] + koff;
+      *(u32x2*)(dkrow + dlo) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
+      *(u32x2*)(dkrow + dhi) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
+      *(u32x2*)(dvrow + dlo) = u32x2{pack_bf2(dv[0], dv[1]), pack_bf2(dv[2], dv[3])};
+      *(u32x2*)(dvrow + dhi) = u32x2{pack_bf2(dv[4], dv[5]), pack_bf2(dv[6], dv[7])};
+    }
   }
 }
 
@@ -792,8 +827,9 @@ void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const
                       const _Float16* qt, const float* delta, const int4* tiles_kv, const float* cosT,
                       const float* sinT, const PassGradPtrs& g, hipStream_t st) {
   const int64_t grid = P.layout == 0
-                           ? (int64_t)8 * ((P.B * P.Hkv + 7) / 8) * ((P.stok + bwd::BKV - 1) / bwd::BKV)
+                           ? (int64_t)8 * ((P.B * P.Hkv + 7) / 8) * ((P.kv_len + bwd::BKV - 1) / bwd::BKV)
                            : (int64_t)P.Hkv * ((P.stok + bwd::BKV - 1) / bwd::BKV + P.nseq);
+  if (grid == 0) return;
   if (P.win > 0)  // sliding window: its own instantiation (MODE 4)
     bwd::dkdv_bf16_kernel<4><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);
   else

@@ -54,6 +54,8 @@ struct Prob {
   // Sliding-window trunk (TTT passes): win > 0 limits row i's trunk to the
   // pass-1 keys at positions (pos_i - win, pos_i]; 0 = the full causal trunk.
   int win;
+  // backward outputs in fp32 (ring-step terms the caller sums) instead of the inputs' bf16
+  int out_f32;
 };
 
 __device__ __forceinline__ int block_anchor(const Prob& P, int b, int row) {

@@ -164,6 +164,8 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
       pl.k0s_b = tmp[0], pl.k0s_t = tmp[1], pl.k0s_h = tmp[2];
     }
   }
+  // the kernels read the trunk (pass-1) V with the P.cs_* strides
+  P.cs_b = pl.k0s_b, P.cs_t = pl.k0s_t, P.cs_h = pl.k0s_h;
   const bool o_f32 = d->o_dtype == TTT_DTYPE_FP32;
   if (int e = strides(d->o_stride, Hq, tmp, "o", (o_f32 && bf16) ? 8 : ea)) return e;
   P.os_b = tmp[0], P.os_t = tmp[1], P.os_h = tmp[2];
@@ -427,8 +429,8 @@ int fwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     ttt::PrepJobs J;
     memset(&J, 0, sizeof J);
     J.n = 2;
-    J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, nullptr, 0, nullptr};
-    J.j[1] = {(const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, 0, 0, 1, nullptr, vt, 0, nullptr};
+    J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, nullptr, 0, nullptr, 0};
+    J.j[1] = {(const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, 0, 0, 1, nullptr, vt, 0, nullptr, 0};
     TTT_TRACED("prep_kv", ttt::launch_prep_bf16(Pk, J, cosT, sinT, st));
     TTT_TRACED("trunk_fwd",
                ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st));
@@ -596,14 +598,14 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   if (P.kv_len > 0) {  // context: K~ rows and K~^T
     ttt::Prob Pc = P;
     Pc.stok = P.kv_len;
-    J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, (uint16_t*)cktt, 0, nullptr};
+    J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, (uint16_t*)cktt, 0, nullptr, 0};
     TTT_TRACED("prep_ctx_bwd", ttt::launch_prep_bf16(Pc, J, cosT, sinT, st));
   }
   // block keys (K~ rows, K~^T) and queries (Q~ rows) at their slot positions
   J.n = 2;
-  J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, (uint16_t*)bktt, 1, nullptr};
+  J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, (uint16_t*)bktt, 1, nullptr, 0};
   int* lims = (int*)(delta + (size_t)P.B * P.Hq * P.spad);  // per-slot visible context lengths
-  J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, 0, 1, 0, qt, nullptr, 1, lims};
+  J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, 0, 1, 0, qt, nullptr, 1, lims, 0};
   TTT_TRACED("prep_blkq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
   if (P.kv_len > 0) {
     ttt::Prob Pc = P;  // the context keys' V / dK / dV strides
@@ -658,14 +660,14 @@ int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   ttt::PrepJobs J;
   memset(&J, 0, sizeof J);
   J.n = 2;
-  J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, nullptr, 0, nullptr};
-  J.j[1] = {(const uint16_t*)v_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 0, 1, nullptr, cvt, 0, nullptr};
+  J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, nullptr, 0, nullptr, 0};
+  J.j[1] = {(const uint16_t*)v_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 0, 1, nullptr, cvt, 0, nullptr, 0};
   TTT_TRACED("prep_ctx", ttt::launch_prep_bf16(Pc, J, cosT, sinT, st));
   // block keys: K~ rows at their slot positions and V^T (spad_b slots)
   ttt::Prob Pb = P;
   Pb.spad = P.spad_b;
-  J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, nullptr, 1, nullptr};
-  J.j[1] = {(const uint16_t*)v_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 0, 1, nullptr, bvt, 0, nullptr};
+  J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, nullptr, 1, nullptr, 0};
+  J.j[1] = {(const uint16_t*)v_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 0, 1, nullptr, bvt, 0, nullptr, 0};
   TTT_TRACED("prep_blk", ttt::launch_prep_bf16(Pb, J, cosT, sinT, st));
   TTT_TRACED("block_fwd", ttt::launch_block_fwd_bf16(P, (const uint16_t*)q, ckt, cvt, bkt, bvt, cosT, sinT, o,
                                                      pl.o_f32, lse, st));
@@ -787,12 +789,15 @@ int ttt_attn_merge(const ttt_attn_desc* d, const void* o_a, const float* lse_a, 
   return hip_check("ttt_attn_merge launch");
 }
 
-int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, const void* o,
-                 const float* lse, const void* dout, void* dq, void* const* dk, void* const* dv, void* ws,
-                 size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, const void* const* k,
+             const void* const* v, const void* o, const float* lse, const void* dout, void* dq, void* const* dk,
+             void* const* dv, void* ws, size_t ws_bytes, void* stream) {
   g_last_error.clear();
   Plan pl;
-  if (int e = make_plan(d, 1, pl)) return e;
+  if (int e = make_plan(d, 1, pl, c)) return e;
   ttt::Prob& P = pl.P;
   if (P.stok == 0) return TTT_OK;  // nothing to compute; pointers of empty tensors may be NULL
   if (!k || !v || !dk || !dv) return fail(TTT_ERR_NULL_ARG, "a k/v/dk/dv pointer array is NULL");
@@ -806,7 +811,11 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
   ttt::PassGradPtrs g;
   memset(&kv, 0, sizeof kv);
   memset(&g, 0, sizeof g);
-  for (int i = 0; i < P.p; ++i) {
+  if (c) P.out_f32 = 1;                  // ring-step terms are fp32 (the caller sums them)
+  const int nptr = P.branch ? P.p : 1;  // a ring step without the branch touches pass 1 only
+  for (int i = 0; i < nptr; ++i) {
+    // an empty pass-1 key block (kv_len = 0) is never read or written: its pointers may be NULL
+    if (i == 0 && P.kv_len == 0 && !k[0] && !v[0] && !dk[0] && !dv[0]) continue;
     char nm[16];
     snprintf(nm, sizeof nm, "k[%d]", i);
     if (int e = check_ptr(k[i], nm)) return e;
@@ -871,22 +880,58 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
     ttt::PrepJobs J;
     memset(&J, 0, sizeof J);
     J.n = 2;
-    J.j[0] = {(const uint16_t*)k[0], P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, kt, (uint16_t*)ktt, 0, nullptr};
-    J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.p - 1, 1, 0, qt, nullptr, 0, nullptr};
+    // pass-1 keys: kv_len rows at positions kv_off + j; queries at q_off + i + p - 1
+    const int krows = (c && P.layout == TTT_LAYOUT_BSHD) ? (P.kv_len > 0 ? P.kv_len : -1) : 0;
+    J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, (uint16_t*)ktt, 0,
+              nullptr, krows};
+    J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.q_off + P.p - 1, 1, 0, qt, nullptr, 0, nullptr, 0};
     TTT_TRACED("prep_kq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
     if (forked) sd.wait(st, delta_done);
-    if (forked && P.p > 1) sd.wait(sd.side, sd.mark(st));  // start the branch kernel with dK/dV, not beside the prologue
-    if (P.p > 1)
+    const bool branch = P.p > 1 && P.branch;
+    if (forked && branch) sd.wait(sd.side, sd.mark(st));  // start the branch kernel with dK/dV, not beside the prologue
+    if (branch)
       TTT_TRACED_ON("branch_bwd", sst,
                     ttt::launch_branch_bwd_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, delta, cosT,
                                                 sinT, g, sst));
-    TTT_TRACED("trunk_dkdv", ttt::launch_dkdv_bf16(P, kv, lse, (const uint16_t*)dout, kt, qt, delta, tkv, cosT,
+    ttt::Prob Pk = P;  // the pass-1 keys' V / dK / dV strides
+    Pk.ks_b = pl.k0s_b, Pk.ks_t = pl.k0s_t, Pk.ks_h = pl.k0s_h;
+    TTT_TRACED("trunk_dkdv", ttt::launch_dkdv_bf16(Pk, kv, lse, (const uint16_t*)dout, kt, qt, delta, tkv, cosT,
                                                    sinT, g, st));
     TTT_TRACED("trunk_dq", ttt::launch_dq_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, kt, ktt, qt,
                                                delta, tq, cosT, sinT, (uint16_t*)dq, st));
-    if (forked && P.p > 1) sd.wait(st, sd.mark(sd.side));  // the branch gradients are in
+    if (forked && branch) sd.wait(st, sd.mark(sd.side));  // the branch gradients are in
   }
   return hip_check("ttt_attn_bwd launch");
+}
+}  // namespace
+
+extern "C" {
+
+int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, const void* o,
+                 const float* lse, const void* dout, void* dq, void* const* dk, void* const* dv, void* ws,
+                 size_t ws_bytes, void* stream) {
+  return bwd_impl(d, nullptr, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream);
+}
+
+size_t ttt_attn_chunk_bwd_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_chunk* c) {
+  g_last_error.clear();
+  if (!c) {
+    fail(TTT_ERR_NULL_ARG, "chunk is NULL");
+    return 0;
+  }
+  Plan pl;
+  if (make_plan(d, 1, pl, c) != TTT_OK) return 0;
+  return pl.ws.total;
+}
+
+int ttt_attn_bwd_chunk(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, const void* const* k,
+                       const void* const* v, const void* o, const float* lse, const void* dout, float* dq,
+                       float* const* dk, float* const* dv, void* ws, size_t ws_bytes, void* stream) {
+  if (!c) {
+    g_last_error.clear();
+    return fail(TTT_ERR_NULL_ARG, "chunk is NULL");
+  }
+  return bwd_impl(d, c, q, k, v, o, lse, dout, dq, (void* const*)dk, (void* const*)dv, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -21,6 +21,7 @@ struct PrepJob {
   uint16_t* out_col;
   int pos_anchor;
   int* out_lim;  // pos_anchor jobs: per slot [(b)][spad] the clamped anchor of the row's block (0 past the end)
+  int rows;      // BSHD: rows of this tensor when they differ from the Prob's (0: P.stok, < 0: none)
 };
 struct PrepJobs {
   PrepJob j[2];

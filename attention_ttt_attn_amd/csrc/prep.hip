@@ -127,7 +127,13 @@ __global__ void __launch_bounds__(256) prep_bf16_kernel(Prob P, PrepJobs J, cons
     const int lr = pass * 32 + rr, slot = tok0 + lr;
     float a[8], c[8];
     int tok, row;
-    const bool valid = slot_token(P, slot, tok, row);
+    bool valid;
+    if (jb.rows != 0 && P.layout == 0) {  // jb.rows < 0: an empty tensor
+      tok = row = slot;
+      valid = slot < jb.rows;
+    } else {
+      valid = slot_token(P, slot, tok, row);
+    }
     if (jb.out_lim && h == 0 && c8 == 0) jb.out_lim[(int64_t)b * P.spad + slot] = valid ? block_anchor(P, b, row) : 0;
     if (valid) {
       const uint16_t* src = jb.x + (int64_t)b * jb.sb + (int64_t)tok * jb.st + (int64_t)h * jb.sh + 8 * c8;

@@ -204,12 +204,24 @@ def ring_main(args, w, dev):
     o_s = torch.empty((w.B, w.S, w.Hq, w.D), dtype=torch.float32, device=dev)
     l_s = torch.empty((w.B, w.Hq, w.S), dtype=torch.float32, device=dev)
     single = lambda: tk.fwd(q, ks, vs, K, o_fp32=True, out=o_s, lse=l_s, **kw)
+    # backward steps: the rows' whole-sequence O / LSE, dO
+    o_b16, l_full = tk.fwd(q, ks, vs, K, rope_base=w.rope_base)
+    do = syn.draw_device(w, syn.KIND_DO, K, dev)
+
+    def bstep(qc, kc):
+        qa, ka = qc * c, kc * c
+        sk = [ks[0][:, ka:ka + c]] + [k[:, qa:qa + c] for k in ks[1:K]]
+        sv = [vs[0][:, ka:ka + c]] + [v[:, qa:qa + c] for v in vs[1:K]]
+        tk.bwd_chunk(q[:, qa:qa + c], sk, sv, o_b16[:, qa:qa + c], l_full[:, :, qa:qa + c], do[:, qa:qa + c], K,
+                     q_offset=qa, kv_offset=ka, with_branch=qc == kc, rope_base=w.rope_base, workspace=ws)
     shapes = {
         "diag_step": lambda: step(cp, cp, o_a, l_a),
         "full_step": lambda: step(2 * cp - 1, 0, o_a, l_a),
         "merge": lambda: tk.merge(o_a, l_a, o_b, l_b, out=o_a, lse=l_a),
         "ring_total": ring,
         "single_call": single,
+        "bwd_diag_step": lambda: bstep(cp, cp),
+        "bwd_full_step": lambda: bstep(2 * cp - 1, 0),
     }
     n = max(args.steps, 1)
     res = {}
@@ -226,7 +238,8 @@ def ring_main(args, w, dev):
         res[name] = {"avg_us": round(e0.elapsed_time(e1) * 1e3 / n, 2)}
     per_head = 4.0 * w.D * w.Hq * w.B
     flops = {"diag_step": per_head * (c * (c + 1) // 2 + (K - 1) * c), "full_step": per_head * c * c,
-             "ring_total": useful_flops(w, K)[0], "single_call": useful_flops(w, K)[0]}
+             "ring_total": useful_flops(w, K)[0], "single_call": useful_flops(w, K)[0],
+             "bwd_diag_step": 2.5 * per_head * (c * (c + 1) // 2 + (K - 1) * c), "bwd_full_step": 2.5 * per_head * c * c}
     for name, f in flops.items():
         res[name]["tflops"] = round(f / (res[name]["avg_us"] * 1e-6) / 1e12, 1)
     res["merge"]["gbps"] = round(w.B * c * w.Hq * (w.D * 4 * 3 + 12) / (res["merge"]["avg_us"] * 1e-6) / 1e9, 1)

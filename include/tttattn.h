@@ -168,6 +168,24 @@ size_t ttt_attn_chunk_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_chu
 int ttt_attn_fwd_chunk(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, const void* const* k,
                        const void* const* v, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* Backward of one ring step (the backward ring also carries dK/dV): the
+ * chain-rule terms of this step's keys, given the rows' FINAL outputs.
+ *   o, lse, dout : the query rows' merged O (o_dtype, o_stride), merged LSE
+ *                  (dense fp32 [B][Hq][seqlen] for these rows) and dO (o_stride)
+ *                  over the whole sequence (the ring's forward result)
+ *   dq           : fp32, q's element strides: this step's terms of dQ
+ *   dk, dv       : HOST arrays of fp32 device pointers: dk[0] / dv[0] the terms
+ *                  of the step's pass-1 keys (kv0 strides); with with_branch,
+ *                  dk[q] / dv[q] (q >= 1) the branch keys' gradients of the rows
+ *                  (kv_stride)
+ * Outputs are overwritten (not accumulated); summing every step's terms gives
+ * the whole-sequence gradients.  BSHD, bf16 inputs.  Workspace:
+ * ttt_attn_chunk_bwd_workspace_bytes. */
+size_t ttt_attn_chunk_bwd_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_chunk* c);
+int ttt_attn_bwd_chunk(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, const void* const* k,
+                       const void* const* v, const void* o, const float* lse, const void* dout, float* dq,
+                       float* const* dk, float* const* dv, void* ws, size_t ws_bytes, void* stream);
+
 /* Joint-LSE merge of two partial results over disjoint key sets of the same
  * rows (same issue and item as above; the operator that also joins trunk and
  * branch):  LSE = ln(e^LSE_a + e^LSE_b),  O = e^(LSE_a-LSE) O_a + e^(LSE_b-LSE) O_b;

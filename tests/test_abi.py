@@ -416,3 +416,24 @@ def test_window_validation():
     d.window = 4
     assert call_block(d, good_block()) == 3 and "window" in err()
     assert ctypes.sizeof(tk.Desc) == 144
+
+
+def test_chunk_bwd_validation():
+    lib = tk.library()
+    d = good_desc()
+    call = lambda c, **kw: lib.ttt_attn_bwd_chunk(
+        ctypes.byref(d), ctypes.byref(c) if c is not None else None, kw.get("q", FAKE), kw.get("k", ptrs(3)),
+        kw.get("v", ptrs(3)), kw.get("o", FAKE), kw.get("lse", FAKE), kw.get("dout", FAKE), kw.get("dq", FAKE),
+        kw.get("dk", ptrs(3)), kw.get("dv", ptrs(3)), FAKE, kw.get("ws_bytes", 1 << 40), None)
+    assert call(None) == 1 and "chunk" in err()
+    assert call(good_chunk(), dq=None) == 1 and "dq" in err()
+    dk = ptrs(3)
+    dk[2] = None
+    assert call(good_chunk(with_branch=1), dk=dk) == 1 and "dk[2]" in err()
+    # without the branch only pass 1 is touched: the call stops at the workspace check
+    assert call(good_chunk(with_branch=0), dk=dk, ws_bytes=16) == 5
+    assert lib.ttt_attn_chunk_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(good_chunk())) > \
+        lib.ttt_attn_chunk_workspace_bytes(ctypes.byref(d), ctypes.byref(good_chunk()))
+    dt = good_desc(layout=tk.LAYOUT_THD)
+    assert lib.ttt_attn_bwd_chunk(ctypes.byref(dt), ctypes.byref(good_chunk()), FAKE, ptrs(3), ptrs(3), FAKE, FAKE,
+                                  FAKE, FAKE, ptrs(3), ptrs(3), FAKE, 1 << 40, None) == 3

@@ -13,7 +13,7 @@ import pytest
 
 import ttt_synth as syn
 from oracle import ttt_oracle as O
-from ttt_cases import TOL, Inputs, bf16_half_ulp, max_abs, to_np
+from ttt_cases import TOL, Inputs, bf16_half_ulp, max_abs, rel_fro, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -190,3 +190,68 @@ def test_ring_fullsize_b4_s4k(dev, tk):
     print(f"b4_s4k ring vs oracle on {nrow} sampled rows: O {eo:.3e} LSE {el:.3e}")
     assert nrow >= 4096
     assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
+
+
+# ----------------------------------------------------------------------------- ring backward
+def zigzag_ring_bwd(tk, q, ks, vs, o, lse, dout, p, cp, rope_base, window=0):
+    """Whole-sequence gradients of pass p summed from the backward terms of every step of a zig-zag
+    ring of cp ranks (fp32 sums of fp32 terms); o/lse are the rows' whole-sequence outputs."""
+    B, S, Hq, D = q.shape
+    c = S // (2 * cp)
+    gq = torch.zeros(q.shape, dtype=torch.float32, device=q.device)
+    gk = [torch.zeros(ks[0].shape, dtype=torch.float32, device=q.device) for _ in range(p)]
+    gv = [torch.zeros(vs[0].shape, dtype=torch.float32, device=q.device) for _ in range(p)]
+    for r in range(cp):
+        for qc in (r, 2 * cp - 1 - r):
+            qa = qc * c
+            for kc in range(2 * cp):
+                ka = kc * c
+                diag = kc == qc
+                sk = [ks[0][:, ka:ka + c]] + [k[:, qa:qa + c] for k in ks[1:p]]
+                sv = [vs[0][:, ka:ka + c]] + [v[:, qa:qa + c] for v in vs[1:p]]
+                dq, dks, dvs = tk.bwd_chunk(q[:, qa:qa + c], sk, sv, o[:, qa:qa + c], lse[:, :, qa:qa + c],
+                                            dout[:, qa:qa + c], p, q_offset=qa, kv_offset=ka, with_branch=diag,
+                                            rope_base=rope_base, window=window)
+                gq[:, qa:qa + c] += dq
+                gk[0][:, ka:ka + c] += dks[0]
+                gv[0][:, ka:ka + c] += dvs[0]
+                for t in range(1, len(dks)):
+                    gk[t][:, qa:qa + c] += dks[t]
+                    gv[t][:, qa:qa + c] += dvs[t]
+    torch.cuda.synchronize()
+    return gq, gk, gv
+
+
+@pytest.mark.parametrize("cp,window", [(2, 0), (3, 0), (2, 100)])
+def test_ring_bwd_ragged(dev, tk, cp, window):
+    w = syn.Workload("ringb_small", 25, "bshd", 2, 600, 8, 2, 128, 3, "bf16", 1e6, True)
+    inp = Inputs(w, dev)
+    p = 3
+    o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, rope_base=w.rope_base, window=window)
+    gq, gk, gv = zigzag_ring_bwd(tk, inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, cp, w.rope_base, window)
+    sq, sk, sv = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, rope_base=w.rope_base, window=window)
+    torch.cuda.synchronize()
+    dq_r, dk_r, dv_r = O.bwd(inp.q[p], inp.k, inp.v, inp.do[p], p, layout="bshd", base=w.rope_base, window=window)
+    errs = {"dq": (rel_fro(to_np(gq), to_np(sq)), rel_fro(to_np(gq), dq_r))}
+    for t in range(p):
+        errs[f"dk{t + 1}"] = (rel_fro(to_np(gk[t]), to_np(sk[t])), rel_fro(to_np(gk[t]), dk_r[t]))
+        errs[f"dv{t + 1}"] = (rel_fro(to_np(gv[t]), to_np(sv[t])), rel_fro(to_np(gv[t]), dv_r[t]))
+    print(f"ring bwd cp={cp} W={window}: " + " ".join(f"{k}={a:.1e}/{b:.1e}" for k, (a, b) in errs.items()))
+    for k, (a, b) in errs.items():
+        assert a <= TOL["bf16"]["grad"] and b <= TOL["bf16"]["grad"], (k, a, b)
+
+
+def test_ring_bwd_fullsize_b4_s4k(dev, tk):
+    """B=4, S=4096, K=7 at pass 7 over a 4-rank zig-zag ring: every gradient element summed from the
+    ring's backward terms vs one whole-sequence backward (itself checked against the oracle)."""
+    w = syn.workload("b4_s4k")
+    inp = Inputs(w, dev, passes=w.K)
+    p, cp = w.K, 4
+    o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, rope_base=w.rope_base)
+    gq, gk, gv = zigzag_ring_bwd(tk, inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, cp, w.rope_base)
+    sq, sk, sv = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, rope_base=w.rope_base)
+    torch.cuda.synchronize()
+    errs = [rel_fro(to_np(gq), to_np(sq))] + [rel_fro(to_np(gk[t]), to_np(sk[t])) for t in range(p)] + \
+           [rel_fro(to_np(gv[t]), to_np(sv[t])) for t in range(p)]
+    print(f"b4_s4k ring bwd vs single call: worst rel Frobenius {max(errs):.2e}")
+    assert max(errs) <= TOL["bf16"]["grad"]
