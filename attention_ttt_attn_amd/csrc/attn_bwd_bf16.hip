@@ -393,8 +393,10 @@ __global__ void __launch_bounds__(256, 2)
 // ============================================================================= dK/dV (trunk)
 // Per 32-query step the workgroup stages Q~ rows and dO rows (8 KB each) plus
 // the rows' LSE and Delta HBM -> LDS with direct loads (global_load_lds),
-// XOR-swizzled (16-byte chunk c of row r at slot c ^ (r & 15)) so that the
-// MFMA operand reads are conflict-free.  The transposed operands of
+// XOR-swizzled (16-byte chunk c of row r at slot c ^ swz(r), swz swapping the
+// two 2-bit halves of r & 15) so that the MFMA operand reads are conflict-free:
+// a row read covers 16 distinct rows, and a transposed read's 4 consecutive
+// rows land on 4 distinct 64-byte bank groups.  The transposed operands of
 // dV^T += dO^T P and dK~^T += Q~^T dS are column reads of the same tiles
 // (ds_read_b64_tr_b16), so no transposed copy is streamed.
 // Software pipeline (one wave per SIMD): iteration i issues the loads of step
@@ -404,6 +406,7 @@ __global__ void __launch_bounds__(256, 2)
 // ALUs run the softmax.  Every wave issues the same 5 loads per step, so one
 // vmcnt threshold releases exactly the step two ahead.
 constexpr int NBUF = 4;
+__device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 struct KvBuf {
   _Float16 q[BQ * D];   // Q~ rows   (A of S; columns: A of dK^T)
   uint16_t g[BQ * D];   // dO rows   (A of dP; columns: A of dV^T)
@@ -520,7 +523,7 @@ __global__ void __launch_bounds__(256, 1)
   for (int i = 0; i < 2; ++i) {
     const int j = 2 * wv + i;
     const int r = 4 * j + (lane >> 4);
-    const int roff = ((lane & 15) ^ (r & 15)) * 8;
+    const int roff = ((lane & 15) ^ kv_swz(r)) * 8;
     rrow[i] = r;
     q_src[i] = qt + ((int64_t)(b * P.Hq + g * P.r) * P.spad + slot0 + r) * D + roff;
     g_src[i] = dout + b * P.os_b + (int64_t)(start + r) * P.os_t + (int64_t)(g * P.r) * P.os_h + roff;
@@ -573,7 +576,7 @@ __global__ void __launch_bounds__(256, 1)
       bf16x8 a2[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int off = prow * D + (((2 * (c0 + c) + hf) ^ (prow & 15)) * 8);
+        const int off = prow * D + (((2 * (c0 + c) + hf) ^ kv_swz(prow)) * 8);
         a[c] = *(const f16x8*)&B.q[off];
         a2[c] = *(const bf16x8*)&B.g[off];
       }
@@ -661,7 +664,7 @@ __global__ void __launch_bounds__(256, 1)
         for (int part = 0; part < 2; ++part) {
           const int r = c2 * 16 + hf * 8 + part * 4 + ((lane & 15) >> 2);
           const int col = d4 * 32 + (lane & 16) + 4 * (lane & 3);
-          const int off = r * D + ((((col >> 3) ^ (r & 15))) << 3) + (col & 7);
+          const int off = r * D + (((col >> 3) ^ kv_swz(r)) << 3) + (col & 7);
           x[part] = lds_read_tr16(&Bc.g[off]);
           y[part] = lds_read_tr16(&Bc.q[off]);
         }
