@@ -690,7 +690,7 @@ __global__ void __launch_bounds__(256, 1)
     } else {
       TTT_WAIT_VMCNT(0);
     }
-    __syncthreads();
+    lds_ring_barrier();
   }
   if (!key_ok) return;
   // epilogue: dK = sigma R(j)^T dK~, dV; lane owns key my_key, d = 32*d4 + 8*v4 + 4*hf + e

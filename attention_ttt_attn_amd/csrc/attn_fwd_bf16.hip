@@ -200,22 +200,29 @@ __global__ void __launch_bounds__(256, 2)
     const int d = RPL * (wv * VL + i) + lane / CH;
     voff[i] = (uint32_t)(d * P.spad + ((lane % CH) ^ ((d >> 1) & (CH - 1))) * 8);
   }
+  // a tile's K~ rows are BN*D contiguous halves; its V^T d-rows are BN keys
+  // each, spad apart
+  const uint32_t vt_bytes = (uint32_t)(((D - 1) * P.spad + BN) * 2);
   auto dma_from = [&](Tile* __restrict__ dst, const _Float16* kb_t, const uint16_t* vb_t)
                       __attribute__((always_inline)) {
+    const buf_rsrc kr = make_rsrc(kb_t, BN * D * 2), vr = make_rsrc(vb_t, vt_bytes);
 #pragma unroll
-    for (int i = 0; i < KL; ++i) lds_dma16(kb_t + koff[i], &dst->k[4 * (wv * KL + i) * D]);
+    for (int i = 0; i < KL; ++i) lds_dma16(kr, koff[i] * 2, &dst->k[4 * (wv * KL + i) * D]);
 #pragma unroll
-    for (int i = 0; i < VL; ++i) lds_dma16(vb_t + voff[i], &dst->v[RPL * (wv * VL + i) * BN]);
+    for (int i = 0; i < VL; ++i) lds_dma16(vr, voff[i] * 2, &dst->v[RPL * (wv * VL + i) * BN]);
   };
   auto dma = [&](Tile* __restrict__ dst, int kt_) __attribute__((always_inline)) {
     dma_from(dst, kbase + (int64_t)kt_ * BN * D, vbase + kt_ * BN);
   };
   // wait_tiles(n): all but this wave's last n tiles of loads have landed
+  static_assert((NBUF - 2) * TL < 64, "vmcnt threshold");
   auto wait_tiles = [&](int n) __attribute__((always_inline)) {
     if (n <= 0) TTT_WAIT_VMCNT(0);
-    else if (n == 1) TTT_WAIT_VMCNT(TL);
-    else TTT_WAIT_VMCNT(2 * TL);
+    else if (NBUF <= 2 || n == 1) TTT_WAIT_VMCNT(TL);
+    else if (NBUF <= 3 || n == 2) TTT_WAIT_VMCNT(2 * TL);
+    else TTT_WAIT_VMCNT(3 * TL);
   };
+  static_assert(NBUF <= 4, "wait_tiles covers at most 3 tiles in flight");
 
   if (kt_lo < nkt) dma(&sm.ring[0], kt_lo);
 #pragma unroll
@@ -267,15 +274,19 @@ __global__ void __launch_bounds__(256, 2)
       const int r = kb * 32 + prow;
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.f;
+      f16x8 a[8];
 #pragma unroll
-      for (int c0 = 0; c0 < 8; c0 += 4) {
-        f16x8 a[4];
+      for (int c = 0; c < 8; ++c) a[c] = *(const f16x8*)&kl[r * D + (((2 * c + hf) ^ (r & 15)) * 8)];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) a[c] = *(const f16x8*)&kl[r * D + (((2 * (c0 + c) + hf) ^ (r & 15)) * 8)];
+      for (int c = 0; c < 8; ++c) sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], qf[c], sacc[kb], 0, 0, 0);
+      // three operand reads ahead of the MFMAs, then one read per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], qf[c0 + c], sacc[kb], 0, 0, 0);
+      for (int c = 0; c < 5; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     }
     // masks: 1 causal trunk, 2 context prefix j < lim, 3 the row's own block
     constexpr int M = decltype(masked)::value;
@@ -341,7 +352,7 @@ __global__ void __launch_bounds__(256, 2)
     const int rb = kt_ - kt_lo;
     step(&sm.ring[rb % NBUF], &sm.ring[(rb + NBUF - 1) % NBUF]);
     if (kt_ + 1 < nkt) wait_tiles(min(nkt, kt_ + NBUF) - (kt_ + 2));  // tile kt_+1 has landed
-    __syncthreads();                                                    // every wave is done with tile kt_
+    lds_ring_barrier();                                                 // every wave is done with tile kt_
   }
 
   // ---- block drafting: the keys of the work item's own blocks (rows row0 ..

@@ -186,8 +186,34 @@ __device__ __forceinline__ void lds_dma4(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
                                    (void __attribute__((address_space(3)))*)l, 4, 0, 0);
 }
+// The same transfer through a buffer descriptor (buffer_load_dword* ... lds):
+// base and byte range in SGPRs, a 32-bit byte offset per lane; a lane whose
+// 16 (or 4) bytes reach past the range reads zeros.  Unlike global_load_lds,
+// which the compiler's wait insertion treats as a flat access that may count
+// on the LDS counter (forcing lgkmcnt(0) at every later LDS-read dependency
+// while any is in flight), these count on vmcnt alone, so LDS operand reads
+// keep graded waits and stay pipelined under the prefetches.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void lds_dma16(buf_rsrc r, uint32_t off, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)l, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(buf_rsrc r, uint32_t off, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)l, 4, off, 0, 0, 0);
+}
 // s_waitcnt vmcnt(n) with expcnt/lgkmcnt left open (gfx9 encoding).
 #define TTT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+
+// Workgroup barrier for LDS rings filled by direct-to-LDS loads.  The release
+// fence of __syncthreads() waits for every outstanding load of the wave (a
+// direct-to-LDS load counts as an LDS write), which would also drain the
+// prefetches issued for later steps; here the caller waits (TTT_WAIT_VMCNT) for
+// exactly the buffers the next step reads.  The wave's LDS reads complete
+// before it, and the memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void lds_ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within every 16-lane group,
 // lane 4e + a supplies the address of 4 consecutive 16-bit elements; lane
