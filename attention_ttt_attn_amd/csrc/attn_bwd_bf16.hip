@@ -158,16 +158,21 @@ __global__ void __launch_bounds__(256, 2)
     const int d = 16 * n + (lane >> 2);
     toff[i] = (uint32_t)(d * P.spad + ((lane & 3) ^ ((d >> 2) & 3)) * 8);
   }
+  // buffer descriptors at the tile's bases; the lanes add byte offsets
+  const uint32_t kt_bytes = (uint32_t)(((D - 1) * P.spad + QBN) * 2);
   auto dma_from = [&](DqBuf* __restrict__ dst, const _Float16* kb, const _Float16* ktb, const uint16_t* vb,
                       int64_t vst, int key0, int last) __attribute__((always_inline)) {
     DqBuf& B_ = *dst;
+    const buf_rsrc kr = make_rsrc(kb + (int64_t)key0 * D, QBN * D * 2);
+    const buf_rsrc vr = make_rsrc(vb + (int64_t)key0 * vst, 0xFFFFFFFFu);
+    const buf_rsrc tr = make_rsrc(ktb + key0, kt_bytes);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int n = 2 * wv + i;
-      const int rg = min(key0 + rrow[i], last);  // V rows past the end repeat the last row (masked)
-      lds_dma16(kb + (int64_t)(key0 + rrow[i]) * D + roff[i], &B_.k[4 * n * D]);
-      lds_dma16(vb + (int64_t)rg * vst + roff[i], &B_.v[4 * n * D]);
-      lds_dma16(ktb + key0 + toff[i], &B_.kt[16 * n * QBN]);
+      const int rg = min(rrow[i], last - key0);  // V rows past the end repeat the last row (masked)
+      lds_dma16(kr, (uint32_t)((rrow[i] * D + (int)roff[i]) * 2), &B_.k[4 * n * D]);
+      lds_dma16(vr, (uint32_t)((rg * vst + roff[i]) * 2), &B_.v[4 * n * D]);
+      lds_dma16(tr, toff[i] * 2, &B_.kt[16 * n * QBN]);
     }
   };
   auto dma = [&](DqBuf* __restrict__ dst, int j) __attribute__((always_inline)) {
@@ -410,7 +415,7 @@ __device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2)
 struct KvBuf {
   _Float16 q[BQ * D];   // Q~ rows   (A of S; columns: A of dK^T)
   uint16_t g[BQ * D];   // dO rows   (A of dP; columns: A of dV^T)
-  float lse[BQ];        // natural-log LSE of the rows
+  float lse[BQ];        // LSE of the rows, log2 units
   float dl[BQ];         // Delta of the rows
   int anc[2 * BQ];      // block drafting, context keys: the rows' clamped block anchors (twice)
 };
@@ -515,47 +520,47 @@ __global__ void __launch_bounds__(256, 1)
   const int nq = max(0, (row_hi - row_lo + BQ - 1) / BQ);
   const int nsteps = P.r * nq;
   // DMA lane roles (wave w issues instructions j = 2w, 2w+1 of each 8 KB tile):
-  // rows r = 4j + lane/16, slot lane%16.  Sources at head 0 of the group, row 0.
+  // rows r = 4j + lane/16, slot lane%16.  Every step builds buffer descriptors
+  // at its (head, first row) bases; the lanes add fixed byte offsets.
   int rrow[2];
-  const _Float16* q_src[2];
-  const uint16_t* g_src[2];
+  uint32_t q_lane[2], c_lane[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int j = 2 * wv + i;
     const int r = 4 * j + (lane >> 4);
     const int roff = ((lane & 15) ^ kv_swz(r)) * 8;
     rrow[i] = r;
-    q_src[i] = qt + ((int64_t)(b * P.Hq + g * P.r) * P.spad + slot0 + r) * D + roff;
-    g_src[i] = dout + b * P.os_b + (int64_t)(start + r) * P.os_t + (int64_t)(g * P.r) * P.os_h + roff;
+    q_lane[i] = (uint32_t)((r * D + roff) * 2);
+    c_lane[i] = (uint32_t)(roff * 2);
   }
-  // dO rows past the sequence end are read from an all-zero workspace row (the
-  // last slot of the first Q~ slab never holds a token), so they add nothing.
-  const uint16_t* zrow = (const uint16_t*)(qt + (int64_t)(P.spad - 1) * D);
-  // LSE and Delta of a step's 32 rows: one dword load by wave 0, lanes 0..31
-  // LSE, lanes 32..63 Delta (they land in lse[] and the dl[] that follows it).
-  const bool m_lse = lane < 32;
-  const float* m_src = m_lse ? lse + b * P.lse_b + (int64_t)(g * P.r) * P.lse_h + start
-                             : delta + (int64_t)(b * P.Hq + g * P.r) * P.spad + slot0;
-  const int64_t m_hstride = m_lse ? P.lse_h : (int64_t)P.spad;
-  const int m_row = lane & 31, m_last = m_lse ? L - 1 : L;
+  const _Float16* q_base = qt + ((int64_t)(b * P.Hq + g * P.r) * P.spad + slot0) * D;
+  const uint16_t* g_base = dout + b * P.os_b + (int64_t)start * P.os_t + (int64_t)(g * P.r) * P.os_h;
+  // LSE (log2 units, +inf past the rows' end) and Delta of a step's 32 rows:
+  // one dword load by wave 0 from the workspace, lanes 0..31 the LSE, lanes
+  // 32..63 Delta (they land in lse[] and the dl[] that follows it).
+  const float* m_base = delta + (int64_t)(b * P.Hq + g * P.r) * P.spad + slot0;
+  const uint32_t m_lane = (uint32_t)(((lane < 32 ? (int64_t)P.B * P.Hq * P.spad : 0) + (lane & 31)) * 4);
   int is_h = 0, is_q0 = row_lo + (nq - 1) * BQ;  // the next step to load
   // block drafting, context keys: wave 1 loads the step's rows' visible context
-  // lengths (clamped anchors, staged per slot in the workspace next to Delta)
+  // lengths (clamped anchors, staged per slot in the workspace after the LSE)
   const bool w1a = MODE == 2 && wv == 1;
-  const int* a_src = MODE == 2 ? (const int*)(delta + (int64_t)P.B * P.Hq * P.spad) + (int64_t)b * P.spad : nullptr;
+  const int* a_base =
+      MODE == 2 ? (const int*)(delta + (int64_t)2 * P.B * P.Hq * P.spad) + (int64_t)b * P.spad : nullptr;
   auto issue = [&](KvBuf* __restrict__ Bd) __attribute__((always_inline)) {
     KvBuf& B = *Bd;
-    const int64_t qoff = ((int64_t)is_h * P.spad + is_q0) * D;
-    const int64_t goff = (int64_t)is_h * P.os_h + (int64_t)is_q0 * P.os_t;
+    const buf_rsrc qr = make_rsrc(q_base + ((int64_t)is_h * P.spad + is_q0) * D, BQ * D * 2);
+    const buf_rsrc gr_ = make_rsrc(g_base + (int64_t)is_h * P.os_h + (int64_t)is_q0 * P.os_t, 0xFFFFFFFFu);
+    // dO rows past the sequence end repeat the last row: their probabilities
+    // are 0 (LSE +inf), so they add nothing
+    const int rmax = L - 1 - is_q0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int j = 2 * wv + i;
-      const uint16_t* gsrc = is_q0 + rrow[i] < L ? g_src[i] + goff : zrow + 8 * (lane & 15);
-      lds_dma16(q_src[i] + qoff, &B.q[4 * j * D]);
-      lds_dma16(gsrc, &B.g[4 * j * D]);
+      lds_dma16(qr, q_lane[i], &B.q[4 * j * D]);
+      lds_dma16(gr_, (uint32_t)(min(rrow[i], rmax) * P.os_t * 2) + c_lane[i], &B.g[4 * j * D]);
     }
-    if (wv == 0) lds_dma4(m_src + is_h * m_hstride + min(is_q0 + m_row, m_last), &B.lse[0]);
-    if (w1a) lds_dma4(a_src + is_q0 + m_row, &B.anc[0]);
+    if (wv == 0) lds_dma4(make_rsrc(m_base + (int64_t)is_h * P.spad + is_q0, 0xFFFFFFFFu), m_lane, &B.lse[0]);
+    if (w1a) lds_dma4(make_rsrc(a_base + is_q0, BQ * 4), (uint32_t)(lane & 31) * 4, &B.anc[0]);
     if (++is_h == P.r) {
       is_h = 0;
       is_q0 -= BQ;
@@ -632,7 +637,7 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int v = half * 8 + e;
-        const float lv = (e < 4 ? l0[e] : l1[e - 4]) * kLog2e;
+        const float lv = e < 4 ? l0[e] : l1[e - 4];  // log2 units
         const float dv_ = e < 4 ? d0[e] : d1[e - 4];
         float pr = fast_exp2(__builtin_fmaf(s_c[v], sl2, -lv));
         if constexpr (TTT_) {  // row - key = e - thr: visible iff 0 <= e - thr (< win)

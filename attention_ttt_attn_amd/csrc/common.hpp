@@ -176,23 +176,15 @@ __device__ __forceinline__ u32x4 pack_h8(const float* f) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// HBM -> LDS without VGPR staging (global_load_lds): lane l's 16 (or 4) bytes
-// land at l * 16 (or l * 4) bytes past the wave-uniform LDS address.
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)l, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)l, 4, 0, 0);
-}
-// The same transfer through a buffer descriptor (buffer_load_dword* ... lds):
-// base and byte range in SGPRs, a 32-bit byte offset per lane; a lane whose
-// 16 (or 4) bytes reach past the range reads zeros.  Unlike global_load_lds,
-// which the compiler's wait insertion treats as a flat access that may count
-// on the LDS counter (forcing lgkmcnt(0) at every later LDS-read dependency
-// while any is in flight), these count on vmcnt alone, so LDS operand reads
-// keep graded waits and stay pipelined under the prefetches.
+// HBM -> LDS without VGPR staging, through a buffer descriptor
+// (buffer_load_dword* ... lds): base and byte range in SGPRs, a 32-bit byte
+// offset per lane; lane l's 16 (or 4) bytes land at l * 16 (or l * 4) bytes
+// past the wave-uniform LDS address, and a lane whose bytes reach past the
+// range reads zeros.  The flat form (global_load_lds) is not used: the
+// compiler's wait insertion treats it as an access that may count on the LDS
+// counter and then forces lgkmcnt(0) at every later LDS-read dependency while
+// one is in flight; these count on vmcnt alone, so LDS operand reads keep
+// graded waits and stay pipelined under the prefetches.
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;
 __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);

@@ -202,7 +202,7 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
       if (thd) w.tiles_kv = take((size_t)(pl.max_tiles_kv + 1) * 16);
       w.ktt = take(nkv * 2);
       w.qt = take(nq * 2);
-      w.delta = take((size_t)B * Hq * P.spad * 4);
+      w.delta = take((size_t)2 * B * Hq * P.spad * 4);  // Delta, then the LSE in log2 units
     }
   } else {
     w.kt = take(nkv * 4);
@@ -538,7 +538,8 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
   bp.qt = bp.delta = 0;
   if (for_bwd) {
     bp.qt = take((size_t)P.B * P.Hq * P.spad * D * 2);
-    bp.delta = take((size_t)P.B * P.Hq * P.spad * 4 + (size_t)P.B * P.spad * 4);  // Delta, then the row lims
+    // Delta, the LSE in log2 units, then the row lims
+    bp.delta = take((size_t)2 * P.B * P.Hq * P.spad * 4 + (size_t)P.B * P.spad * 4);
   }
   bp.total = off;
   pl.ws.total = off;
@@ -591,7 +592,7 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   _Float16* qt = at<_Float16>(ws, bp.qt);
   float* delta = at<float>(ws, bp.delta);
   TTT_TRACED("rope_table", ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st));
-  TTT_TRACED("bwd_delta", ttt::launch_delta(P, o, pl.o_f32, dout, false, delta, st));
+  TTT_TRACED("bwd_delta", ttt::launch_delta(P, o, pl.o_f32, dout, false, lse, delta, st));
   ttt::PrepJobs J;
   memset(&J, 0, sizeof J);
   J.n = 1;
@@ -604,7 +605,7 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   // block keys (K~ rows, K~^T) and queries (Q~ rows) at their slot positions
   J.n = 2;
   J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, (uint16_t*)bktt, 1, nullptr, 0};
-  int* lims = (int*)(delta + (size_t)P.B * P.Hq * P.spad);  // per-slot visible context lengths
+  int* lims = (int*)(delta + (size_t)2 * P.B * P.Hq * P.spad);  // per-slot visible context lengths
   J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, 0, 1, 0, qt, nullptr, 1, lims, 0};
   TTT_TRACED("prep_blkq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
   if (P.kv_len > 0) {
@@ -862,7 +863,8 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
   Side sd;
   const bool forked = pl.bf16 && sd.begin(st);
   const hipStream_t sst = forked ? sd.side : st;
-  TTT_TRACED_ON("bwd_delta", sst, ttt::launch_delta(P, o, pl.o_f32, dout, !pl.bf16, delta, sst));
+  TTT_TRACED_ON("bwd_delta", sst,
+                ttt::launch_delta(P, o, pl.o_f32, dout, !pl.bf16, pl.bf16 ? lse : nullptr, delta, sst));
   const hipEvent_t delta_done = forked ? sd.mark(sd.side) : nullptr;
   if (!pl.bf16) {
     float* kt = at<float>(ws, pl.ws.kt);

@@ -28,8 +28,10 @@ struct PrepJobs {
   int n;
 };
 void launch_prep_bf16(const Prob& P, const PrepJobs& J, const float* cosT, const float* sinT, hipStream_t st);
-void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, float* delta,
-                  hipStream_t st);
+// Delta (and, with lse, the LSE in log2 units right after it, +inf past the
+// rows' ends) in the workspace slot layout.
+void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, const float* lse,
+                  float* delta, hipStream_t st);
 void launch_tile_sched(const Prob& P, int tile, int descending, int4* out, int max_entries, int* slot_base,
                        hipStream_t st);
 

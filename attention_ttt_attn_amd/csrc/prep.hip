@@ -182,28 +182,52 @@ __global__ void __launch_bounds__(256) prep_bf16_kernel(Prob P, PrepJobs J, cons
   }
 }
 
-// Delta[(b*Hq + h)][slot] = <dO row, O row> in fp32 (0 in slots without a token).
-// Grid (spad/64, Hq, B), 256 threads, D/8 threads per row.
+// 8 consecutive elements (16-byte aligned) as fp32, in 16-byte loads.
+__device__ __forceinline__ void load8(const uint16_t* p, float* x) { unpack_bf8(*(const u32x4*)p, x); }
+__device__ __forceinline__ void load8(const float* p, float* x) {
+  const f32x4 a = *(const f32x4*)p, b = *(const f32x4*)(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = a[e], x[4 + e] = b[e];
+}
+
+// Delta[(b*Hq + h)][slot] = <dO row, O row> in fp32 (0 in slots without a
+// token).  With lse given, also the rows' LSE in log2 units in the same slot
+// layout right after Delta (+inf in slots without a token, so every
+// probability recomputed for them is exactly 0).  Grid (spad/64, Hq, B), 256
+// threads, D/8 threads per row; each thread issues all its rows' loads first.
 template <int D, typename OT, typename GT>
 __global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict__ o, const GT* __restrict__ dout,
-                                                    float* __restrict__ delta) {
+                                                    const float* __restrict__ lse, float* __restrict__ delta) {
   constexpr int TPR = D / 8;
   constexpr int ROWS = 256 / TPR;
+  constexpr int NR = 64 / ROWS;  // rows per thread
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, c = tid % TPR;
-  for (int r0 = 0; r0 < 64; r0 += ROWS) {
-    int slot = blockIdx.x * 64 + r0 + tid / TPR;
-    int tok, row;
-    bool valid = slot_token(P, slot, tok, row);
-    float acc = 0.f;
-    if (valid) {
-      int64_t off = (int64_t)b * P.os_b + (int64_t)tok * P.os_t + (int64_t)h * P.os_h + 8 * c;
+  int slot[NR], tok[NR];
+  bool valid[NR];
+  float x[NR][8], y[NR][8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc += ld<OT>(o + off + e) * ld<GT>(dout + off + e);
-    }
+  for (int i = 0; i < NR; ++i) {
+    int row;
+    slot[i] = blockIdx.x * 64 + i * ROWS + tid / TPR;
+    valid[i] = slot_token(P, slot[i], tok[i], row);
+    const int64_t off = (int64_t)b * P.os_b + (int64_t)(valid[i] ? tok[i] : 0) * P.os_t + (int64_t)h * P.os_h + 8 * c;
+    load8(o + off, x[i]);
+    load8(dout + off, y[i]);
+  }
+  float* lse2 = delta + (int64_t)P.B * P.Hq * P.spad;
+#pragma unroll
+  for (int i = 0; i < NR; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += x[i][e] * y[i][e];
+    if (!valid[i]) acc = 0.f;
 #pragma unroll
     for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
-    if (c == 0) delta[(int64_t)(b * P.Hq + h) * P.spad + slot] = acc;
+    const int64_t so = (int64_t)(b * P.Hq + h) * P.spad + slot[i];
+    if (c == 0) delta[so] = acc;
+    if (lse && c == 1)
+      lse2[so] = valid[i] ? lse[(int64_t)b * P.lse_b + (int64_t)h * P.lse_h + tok[i]] * kLog2e : INFINITY;
   }
 }
 
@@ -349,17 +373,17 @@ void launch_prep_bf16(const Prob& P, const PrepJobs& J, const float* cosT, const
   prep_bf16_kernel<<<grid, 256, 0, st>>>(P, J, cosT, sinT);
 }
 
-void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, float* delta,
-                  hipStream_t st) {
+void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, const float* lse,
+                  float* delta, hipStream_t st) {
   dim3 grid(P.spad / 64, P.Hq, P.B);
 #define TTT_DELTA(DD)                                                                              \
   if (P.D == DD) {                                                                                 \
     if (o_f32 && g_f32)                                                                            \
-      delta_kernel<DD, float, float><<<grid, 256, 0, st>>>(P, (const float*)o, (const float*)dout, delta); \
+      delta_kernel<DD, float, float><<<grid, 256, 0, st>>>(P, (const float*)o, (const float*)dout, lse, delta); \
     else if (o_f32)                                                                                \
-      delta_kernel<DD, float, uint16_t><<<grid, 256, 0, st>>>(P, (const float*)o, (const uint16_t*)dout, delta); \
+      delta_kernel<DD, float, uint16_t><<<grid, 256, 0, st>>>(P, (const float*)o, (const uint16_t*)dout, lse, delta); \
     else                                                                                           \
-      delta_kernel<DD, uint16_t, uint16_t><<<grid, 256, 0, st>>>(P, (const uint16_t*)o, (const uint16_t*)dout, delta); \
+      delta_kernel<DD, uint16_t, uint16_t><<<grid, 256, 0, st>>>(P, (const uint16_t*)o, (const uint16_t*)dout, lse, delta); \
     return;                                                                                        \
   }
   TTT_DELTA(32)
