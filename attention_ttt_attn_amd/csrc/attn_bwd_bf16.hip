@@ -166,9 +166,10 @@ __global__ void __launch_bounds__(256, 2)
     const buf_rsrc kr = make_rsrc(kb + (int64_t)key0 * D, QBN * D * 2);
     const buf_rsrc vr = make_rsrc(vb + (int64_t)key0 * vst, 0xFFFFFFFFu);
     const buf_rsrc tr = make_rsrc(ktb + key0, kt_bytes);
+    const int wu = __builtin_amdgcn_readfirstlane(wv);  // the LDS bases stay scalar
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int n = 2 * wv + i;
+      const int n = 2 * wu + i;
       const int rg = min(rrow[i], last - key0);  // V rows past the end repeat the last row (masked)
       lds_dma16(kr, (uint32_t)((rrow[i] * D + (int)roff[i]) * 2), &B_.k[4 * n * D]);
       lds_dma16(vr, (uint32_t)((rg * vst + roff[i]) * 2), &B_.v[4 * n * D]);
@@ -553,9 +554,10 @@ __global__ void __launch_bounds__(256, 1)
     // dO rows past the sequence end repeat the last row: their probabilities
     // are 0 (LSE +inf), so they add nothing
     const int rmax = L - 1 - is_q0;
+    const int wu = __builtin_amdgcn_readfirstlane(wv);  // the LDS bases stay scalar
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int j = 2 * wv + i;
+      const int j = 2 * wu + i;
       lds_dma16(qr, q_lane[i], &B.q[4 * j * D]);
       lds_dma16(gr_, (uint32_t)(min(rrow[i], rmax) * P.os_t * 2) + c_lane[i], &B.g[4 * j * D]);
     }

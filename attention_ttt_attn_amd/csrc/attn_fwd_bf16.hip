@@ -206,10 +206,11 @@ __global__ void __launch_bounds__(256, 2)
   auto dma_from = [&](Tile* __restrict__ dst, const _Float16* kb_t, const uint16_t* vb_t)
                       __attribute__((always_inline)) {
     const buf_rsrc kr = make_rsrc(kb_t, BN * D * 2), vr = make_rsrc(vb_t, vt_bytes);
+    const int wu = __builtin_amdgcn_readfirstlane(wv);  // the LDS bases stay scalar
 #pragma unroll
-    for (int i = 0; i < KL; ++i) lds_dma16(kr, koff[i] * 2, &dst->k[4 * (wv * KL + i) * D]);
+    for (int i = 0; i < KL; ++i) lds_dma16(kr, koff[i] * 2, &dst->k[4 * (wu * KL + i) * D]);
 #pragma unroll
-    for (int i = 0; i < VL; ++i) lds_dma16(vr, voff[i] * 2, &dst->v[RPL * (wv * VL + i) * BN]);
+    for (int i = 0; i < VL; ++i) lds_dma16(vr, voff[i] * 2, &dst->v[RPL * (wu * VL + i) * BN]);
   };
   auto dma = [&](Tile* __restrict__ dst, int kt_) __attribute__((always_inline)) {
     dma_from(dst, kbase + (int64_t)kt_ * BN * D, vbase + kt_ * BN);
@@ -327,16 +328,27 @@ __global__ void __launch_bounds__(256, 2)
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one, l_run, false);
       }
     apply_scale();
+    {
+      bf16x8 a[2 * KB][4];
 #pragma unroll
-    for (int c2 = 0; c2 < 2 * KB; ++c2) {
-      bf16x8 a[4];
+      for (int c2 = 0; c2 < 2 * KB; ++c2)
 #pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4) {
-        const int d = d4 * 32 + l32;
-        a[d4] = *(const bf16x8*)&vl[d * BN + (((2 * c2 + hf) ^ ((d >> 1) & (CH - 1))) * 8)];
+        for (int d4 = 0; d4 < 4; ++d4) {
+          const int d = d4 * 32 + l32;
+          a[c2][d4] = *(const bf16x8*)&vl[d * BN + (((2 * c2 + hf) ^ ((d >> 1) & (CH - 1))) * 8)];
+        }
+#pragma unroll
+      for (int c2 = 0; c2 < 2 * KB; ++c2)
+#pragma unroll
+        for (int d4 = 0; d4 < 4; ++d4) oacc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c2][d4], pb[c2], oacc[d4], 0, 0, 0);
+      // three operand reads ahead of the MFMAs, then one read per MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int c = 0; c < 8 * KB - 3; ++c) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-#pragma unroll
-      for (int d4 = 0; d4 < 4; ++d4) oacc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[d4], pb[c2], oacc[d4], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
     }
   };
 
