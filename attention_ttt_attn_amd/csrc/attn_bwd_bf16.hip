@@ -41,7 +41,7 @@ __device__ __forceinline__ int perm_row(int a) { return (a & ~0xC) | ((a & 4) <<
 // (R' = 4 for GQA 4:1) times 32*4/R' rows; each wave owns 32 query rows of one
 // head, so with R' = 4 all four waves share one causal extent.  Key tiles of
 // 32 keys -- K~ rows (A of S^T), V rows (A of dP^T) and K~^T (A of dQ^T) --
-// move HBM -> LDS with direct loads (global_load_lds), XOR-swizzled, double
+// move HBM -> LDS with direct loads (buffer_load ... lds), XOR-swizzled, double
 // buffered: the next tile's loads run under this tile's products; one barrier
 // per tile.  Two workgroups per CU keep the matrix pipe busy while the other
 // one's vector ALUs form dS.
@@ -398,7 +398,7 @@ __global__ void __launch_bounds__(256, 2)
 
 // ============================================================================= dK/dV (trunk)
 // Per 32-query step the workgroup stages Q~ rows and dO rows (8 KB each) plus
-// the rows' LSE and Delta HBM -> LDS with direct loads (global_load_lds),
+// the rows' LSE and Delta HBM -> LDS with direct loads (buffer_load ... lds),
 // XOR-swizzled (16-byte chunk c of row r at slot c ^ swz(r), swz swapping the
 // two 2-bit halves of r & 15) so that the MFMA operand reads are conflict-free:
 // a row read covers 16 distinct rows, and a transposed read's 4 consecutive
@@ -409,8 +409,10 @@ __global__ void __launch_bounds__(256, 2)
 // i+3 into a 4-deep ring of LDS buffers, runs the S/dP products of step i+1,
 // the softmax of step i (whose S/dP came from iteration i-1) and step i's
 // dV/dK products, so the matrix pipe has independent work while the vector
-// ALUs run the softmax.  Every wave issues the same 5 loads per step, so one
-// vmcnt threshold releases exactly the step two ahead.
+// ALUs run the softmax.  Each wave issues 4 loads per step (wave 0 a fifth:
+// the LSE and Delta; block drafting, context keys: wave 1 a fifth, the
+// anchors), so one vmcnt threshold per wave releases exactly the step two
+// ahead.
 constexpr int NBUF = 4;
 __device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 struct KvBuf {
@@ -608,8 +610,8 @@ __global__ void __launch_bounds__(256, 1)
   f32x16 s_c, dp_c;
   products(&sm[0], s_c, dp_c);
 
-  // Rows past the sequence end need no mask: their Q~ and dO rows and their
-  // Delta are zero, so they add nothing to dK or dV.
+  // Rows past the sequence end need no mask: their staged LSE is +inf, so
+  // their probabilities are 0 and they add nothing to dK or dV.
   // The causal mask (rows before this lane's key) is one compare per score.
   // The three ring buffers an iteration touches go through distinct restrict
   // pointers: the compiler then knows the loads into the step-(st+3) buffer

@@ -27,9 +27,10 @@
 //   inputs are exact in fp16 up to 65504; the rotated values round 8x finer
 //   than in bf16).  K~ = R(j) k^(1) (fp16) and V^(1)^T (bf16) come from the
 //   prologue, so the hot loop is copies and MFMAs.
-// * K~ and V^T tiles of 64 keys move HBM -> LDS with global_load_lds_dwordx4
+// * K~ and V^T tiles of 64 keys move HBM -> LDS with buffer_load_dwordx4 ... lds
 //   (no VGPR staging), double-buffered, XOR-swizzled 16-byte chunks so that
-//   the MFMA operand reads are bank-conflict free; one barrier per tile.
+//   the MFMA operand reads are bank-conflict free; one barrier per tile; the
+//   operand reads run three ahead of their MFMAs.
 // * Softmax in the log2 domain with one FMA per score; the running max only
 //   moves when a score exceeds it by 2^8 (P <= 256), and the 64-register O
 //   rescale is skipped wave-wide otherwise.  Only diagonal tiles are masked.
