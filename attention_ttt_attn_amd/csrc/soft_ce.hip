@@ -12,9 +12,9 @@
 // intermediate exists at all.
 //
 // gfx950 design: HBM-bound.  One 256-thread workgroup per row; each thread
-// streams 16-byte chunks of the student and teacher rows with an online
-// (max, sum) in the log2 domain for both, plus the teacher-weighted student
-// sum, so the forward reads each logit once.  States merge across lanes with
+// streams 16-byte chunks of the student and teacher rows, U of each in flight,
+// with an online (max, sum) in the log2 domain for both, plus the
+// teacher-weighted student sum, so the forward reads each logit once.  States merge across lanes with
 // shuffles and across the 4 waves through LDS.  The mean over rows is a
 // fixed-order reduction (deterministic).  The backward reads both rows once
 // more and writes (softmax(student) - teacher distribution) * dloss / count.
@@ -25,6 +25,7 @@ namespace ttt {
 namespace ce {
 
 constexpr int NT = 256;
+constexpr int U = 4;  // 16-byte chunks of each row a thread has in flight
 
 // merges (m2, l2, w2) into (m, l, w); w is scaled like l
 __device__ __forceinline__ void merge(float& m, float& l, float& w, float m2, float l2, float w2) {
@@ -56,15 +57,27 @@ __global__ void __launch_bounds__(NT) soft_ce_fwd_kernel(CeProb C, const uint16_
   }
   const uint16_t* sr = s + (int64_t)b * C.ss_b + (int64_t)i * C.ss_t;
   const uint16_t* tr = t + (int64_t)b * C.ts_b + (int64_t)(i + C.offset) * C.ts_t;
-  // student: (ms, ls); teacher: (mt, lt) and wt = sum 2^(t2 - mt) * s
+  // student: (ms, ls); teacher: (mt, lt) and wt = sum 2^(t2 - mt) * s.  All
+  // U chunks' loads are issued before any of them is used.
   float ms = -INFINITY, ls = 0.f, mt = -INFINITY, lt = 0.f, wt = 0.f;
-  for (int v0 = tid * 8; v0 < C.V; v0 += NT * 8) {
-    float x[8], y[8];
-    unpack_bf8(*(const u32x4*)(sr + v0), x);
-    unpack_bf8(*(const u32x4*)(tr + v0), y);
-    float cx = x[0], cy = y[0];
+  for (int v0 = tid * 8; v0 < C.V; v0 += NT * 8 * U) {
+    u32x4 xs[U], ys[U];
 #pragma unroll
-    for (int e = 1; e < 8; ++e) cx = fmaxf(cx, x[e]), cy = fmaxf(cy, y[e]);
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * NT * 8 < C.V) {
+        xs[u] = *(const u32x4*)(sr + v0 + u * NT * 8);
+        ys[u] = *(const u32x4*)(tr + v0 + u * NT * 8);
+      }
+    float cx = -INFINITY, cy = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * NT * 8 < C.V) {
+        float x[8], y[8];
+        unpack_bf8(xs[u], x);
+        unpack_bf8(ys[u], y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cx = fmaxf(cx, x[e]), cy = fmaxf(cy, y[e]);
+      }
     cx *= kLog2e;
     cy *= kLog2e;
     if (cx > ms) {
@@ -78,12 +91,19 @@ __global__ void __launch_bounds__(NT) soft_ce_fwd_kernel(CeProb C, const uint16_
       mt = cy;
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ls += fast_exp2(__builtin_fmaf(x[e], kLog2e, -ms));
-      const float pe = fast_exp2(__builtin_fmaf(y[e], kLog2e, -mt));
-      lt += pe;
-      wt = __builtin_fmaf(pe, x[e], wt);
-    }
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * NT * 8 < C.V) {
+        float x[8], y[8];
+        unpack_bf8(xs[u], x);
+        unpack_bf8(ys[u], y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          ls += fast_exp2(__builtin_fmaf(x[e], kLog2e, -ms));
+          const float pe = fast_exp2(__builtin_fmaf(y[e], kLog2e, -mt));
+          lt += pe;
+          wt = __builtin_fmaf(pe, x[e], wt);
+        }
+      }
   }
   // lanes, then waves
 #pragma unroll
@@ -161,14 +181,25 @@ __global__ void __launch_bounds__(NT) soft_ce_bwd_kernel(CeProb C, const uint16_
   const float n = stats[1];
   const float scale = n > 0.f ? dloss[0] / n : 0.f;
   const float ls2 = row_lse[2 * (int64_t)row] * kLog2e, lt2 = row_lse[2 * (int64_t)row + 1] * kLog2e;
-  for (int v0 = tid * 8; v0 < C.V; v0 += NT * 8) {
-    float x[8], y[8], o[8];
-    unpack_bf8(*(const u32x4*)(sr + v0), x);
-    unpack_bf8(*(const u32x4*)(tr + v0), y);
+  for (int v0 = tid * 8; v0 < C.V; v0 += NT * 8 * U) {
+    u32x4 xs[U], ys[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      o[e] = scale * (fast_exp2(__builtin_fmaf(x[e], kLog2e, -ls2)) - fast_exp2(__builtin_fmaf(y[e], kLog2e, -lt2)));
-    *(u32x4*)(gr + v0) = pack_bf8(o);
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * NT * 8 < C.V) {
+        xs[u] = *(const u32x4*)(sr + v0 + u * NT * 8);
+        ys[u] = *(const u32x4*)(tr + v0 + u * NT * 8);
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (v0 + u * NT * 8 < C.V) {
+        float x[8], y[8], o[8];
+        unpack_bf8(xs[u], x);
+        unpack_bf8(ys[u], y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          o[e] = scale * (fast_exp2(__builtin_fmaf(x[e], kLog2e, -ls2)) - fast_exp2(__builtin_fmaf(y[e], kLog2e, -lt2)));
+        *(u32x4*)(gr + v0 + u * NT * 8) = pack_bf8(o);
+      }
   }
 }
 
