@@ -222,6 +222,58 @@ def zigzag_ring_bwd(tk, q, ks, vs, o, lse, dout, p, cp, rope_base, window=0):
     return gq, gk, gv
 
 
+def test_ring_bwd_steps_match_oracle_step(dev, tk):
+    """Single ring-step backward terms against the oracle's step terms, both fed the oracle's own
+    whole-sequence O (rounded to bf16) and LSE: diagonal with branch, full off-diagonal, a partial
+    key block, keys all after the rows (every term exactly 0), a zero-length key block (branch
+    terms only) and a one-row chunk."""
+    w = syn.Workload("ringb_step", 26, "bshd", 1, 192, 4, 2, 128, 3, "bf16", 1e6, True)
+    inp = Inputs(w, dev)
+    p = 3
+    o_ref, l_ref = O.fwd(inp.q[p], inp.k, inp.v, p, layout="bshd", base=w.rope_base)
+    o16 = syn.round_bf16(o_ref.astype(np.float32))
+    go = torch.from_numpy(o16).to(dev).to(torch.bfloat16)
+    gl = torch.from_numpy(np.ascontiguousarray(l_ref, dtype=np.float32)).to(dev)
+    cases = [  # (q_offset, n, kv_offset, m, with_branch)
+        (64, 64, 64, 64, True),
+        (128, 64, 0, 64, False),
+        (100, 35, 75, 45, True),
+        (0, 48, 50, 32, False),
+        (20, 17, 20, 0, True),
+        (150, 1, 100, 51, True),
+    ]
+    for qa, n, ka, m, br in cases:
+        sk = [inp.gk[0][:, ka:ka + m]] + [k[:, qa:qa + n] for k in inp.gk[1:p]]
+        sv = [inp.gv[0][:, ka:ka + m]] + [v[:, qa:qa + n] for v in inp.gv[1:p]]
+        dq, dks, dvs = tk.bwd_chunk(inp.gq[p][:, qa:qa + n], sk, sv, go[:, qa:qa + n], gl[:, :, qa:qa + n],
+                                    inp.gdo[p][:, qa:qa + n], p, q_offset=qa, kv_offset=ka, with_branch=br,
+                                    rope_base=w.rope_base)
+        torch.cuda.synchronize()
+        rq, rk0, rv0, rkb, rvb = O.bwd_chunk(
+            inp.q[p][:, qa:qa + n], inp.k[0][:, ka:ka + m], inp.v[0][:, ka:ka + m],
+            [k[:, qa:qa + n] for k in inp.k[1:p]] if br else None, [v[:, qa:qa + n] for v in inp.v[1:p]] if br else None,
+            p, inp.do[p][:, qa:qa + n], o16[:, qa:qa + n], l_ref[:, :, qa:qa + n], q_offset=qa, kv_offset=ka,
+            base=w.rope_base)
+        pairs = [("dq", dq, rq), ("dk1", dks[0], rk0), ("dv1", dvs[0], rv0)]
+        pairs += [(f"dk{t + 2}", dks[1 + t], rkb[t]) for t in range(len(rkb))]
+        pairs += [(f"dv{t + 2}", dvs[1 + t], rvb[t]) for t in range(len(rvb))]
+        assert len(dks) == 1 + len(rkb) and len(dvs) == 1 + len(rvb)
+        errs = []
+        for name, g, r in pairs:
+            g = to_np(g)
+            assert g.shape == r.shape, (name, g.shape, r.shape)
+            if r.size == 0:
+                continue
+            if not np.any(r):
+                assert not np.any(g), (qa, n, ka, m, br, name)  # a step without visible keys adds exactly 0
+                errs.append(f"{name}=0")
+                continue
+            e = rel_fro(g, r)
+            errs.append(f"{name}={e:.1e}")
+            assert e <= TOL["bf16"]["grad"], (qa, n, ka, m, br, name, e)
+        print(f"bwd step q@{qa}+{n} kv@{ka}+{m} branch={br}: " + " ".join(errs))
+
+
 @pytest.mark.parametrize("cp,window", [(2, 0), (3, 0), (2, 100)])
 def test_ring_bwd_ragged(dev, tk, cp, window):
     w = syn.Workload("ringb_small", 25, "bshd", 2, 600, 8, 2, 128, 3, "bf16", 1e6, True)
