@@ -31,6 +31,10 @@ int fail(int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Largest token stride (elements) of a caller tensor: the kernels' tile loads
+// reach 32 rows past a base with 32-bit byte offsets.
+constexpr int64_t kMaxTokenStride = (int64_t)1 << 25;
+
 struct Plan {
   ttt::Prob P;
   ttt::WsPlan ws;
@@ -143,6 +147,9 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
       if (s[i] % elem_align) return fail(TTT_ERR_MISALIGNED, "%s stride[%d] = %lld not a multiple of %d elements",
                                          name, i, (long long)s[i], elem_align);
     }
+    if (s[1] > kMaxTokenStride)  // tile loads address 32 rows with 32-bit byte offsets
+      return fail(TTT_ERR_BAD_SHAPE, "%s token stride %lld exceeds %lld elements", name, (long long)s[1],
+                  (long long)kMaxTokenStride);
     out[0] = thd ? 0 : s[0];
     out[1] = s[1];
     out[2] = s[2];
@@ -519,6 +526,9 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
       if (s0[i] % 8) return fail(TTT_ERR_MISALIGNED, "ctx stride[%d] = %lld not a multiple of 8 elements", i,
                                  (long long)s0[i]);
     }
+    if (s0[1] > kMaxTokenStride)
+      return fail(TTT_ERR_BAD_SHAPE, "ctx token stride %lld exceeds %lld elements", (long long)s0[1],
+                  (long long)kMaxTokenStride);
     bp.cs_b = s0[0], bp.cs_t = s0[1], bp.cs_h = s0[2];
   }
   P.cs_b = bp.cs_b, P.cs_t = bp.cs_t, P.cs_h = bp.cs_h;

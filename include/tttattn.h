@@ -29,7 +29,9 @@
  *                    BSHD [B, S, Hkv, D] or THD [T, Hkv, D]
  *   lse (fp32, contiguous): BSHD [B, Hq, S], THD [Hq, T]
  * q/dq use q_stride, o/dout use o_stride, every k/v/dk/dv uses kv_stride.
- * A zero stride triple selects the contiguous default.
+ * A zero stride triple selects the contiguous default.  Token strides above
+ * 2^25 elements are rejected (TTT_ERR_BAD_SHAPE): tile loads address up to 32
+ * rows past a base with 32-bit byte offsets.
  *
  * Ownership and state: the caller owns every buffer, including the
  * workspace.  The library allocates no device memory and keeps no state

@@ -437,3 +437,13 @@ def test_chunk_bwd_validation():
     dt = good_desc(layout=tk.LAYOUT_THD)
     assert lib.ttt_attn_bwd_chunk(ctypes.byref(dt), ctypes.byref(good_chunk()), FAKE, ptrs(3), ptrs(3), FAKE, FAKE,
                                   FAKE, FAKE, ptrs(3), ptrs(3), FAKE, 1 << 40, None) == 3
+
+
+def test_token_stride_limit():
+    lib = tk.library()
+    d = good_desc()
+    d.o_stride[0], d.o_stride[1], d.o_stride[2] = (1 << 26) * 64, 1 << 26, 128
+    assert lib.ttt_attn_workspace_bytes(ctypes.byref(d), 0) == 0 and "token stride" in err()
+    d = good_desc()
+    d.kv_stride[0], d.kv_stride[1], d.kv_stride[2] = (1 << 25) * 64, 1 << 25, 128
+    assert lib.ttt_attn_workspace_bytes(ctypes.byref(d), 0) > 0
