@@ -29,6 +29,8 @@ namespace ttt {
 
 namespace bwd {
 
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+typedef __bf16 b2v __attribute__((ext_vector_type(2)));
 constexpr int D = 128;
 constexpr int BKV = kBwdBKV;  // dK/dV kernel: keys per workgroup
 constexpr int BQ = 32;        // dK/dV kernel: query rows per step
@@ -71,7 +73,8 @@ __global__ void __launch_bounds__(256, 2)
                    const uint16_t* __restrict__ dout, const _Float16* __restrict__ kt,
                    const _Float16* __restrict__ ktt, const _Float16* __restrict__ qt, const float* __restrict__ delta,
                    const int4* __restrict__ tiles, const float* __restrict__ cosT, const float* __restrict__ sinT,
-                   uint16_t* __restrict__ dq, const _Float16* __restrict__ kbt, const _Float16* __restrict__ kbtt) {
+                   uint16_t* __restrict__ dq, const _Float16* __restrict__ kbt, const _Float16* __restrict__ kbtt,
+                   PassGradPtrs gr) {
   constexpr int RT = dq_rows(RH);  // rows per work item
   __shared__ __attribute__((aligned(16))) DqSmem sm;
   constexpr bool TTT_ = MODE == 0 || MODE == 4;  // TTT pass (4: with a sliding window)
@@ -303,10 +306,144 @@ __global__ void __launch_bounds__(256, 2)
   }
   __syncthreads();
 
-  // row-major epilogue: branch terms, un-rotation, store.  LDS row lr holds
-  // wave lr/32's row lr%32.
+  // Fused branch gradients (every query head of the KV group in this work
+  // item, P.dq_branch): per 16 rows, passes outer and heads inner, 16 threads
+  // per row, 8 elements (4 rotate-half pairs d, d + 64) per thread.  For
+  // branch key q of row i and head h: P = exp(s - LSE), dS = P (<dO, v> -
+  // Delta); dQ~ += sigma dS k~ (into the LDS rows), dk~^(q) += sigma dS q~ and
+  // dv^(q) += P dO summed over the heads in registers, then un-rotated and
+  // stored once: no atomics, no second pass over Q and dO.
+  if constexpr (TTT_) {
+    if (P.dq_branch && P.branch && P.p > 1) {
+      const int c16 = tid & 15;
+      const int flo = c16 * 4, fhi = 64 + c16 * 4;
+#pragma unroll 1
+      for (int r16 = 0; r16 < RT; r16 += 16) {
+        const int rr = r16 + (tid >> 4);  // row within the work item
+        const int i = row0 + rr;
+        if (i >= L) continue;
+        const int pos = P.q_off + i + P.p - 1;
+        // per head: q~ as fp16 pairs and dO as its bf16 pairs (8 values each)
+        u32x2 qh[RH][2], gh[RH][2];
+        float lse_[RH], dl_[RH];
+        {
+          const f32x4 cq = *(const f32x4*)(cosT + (int64_t)pos * 64 + flo);
+          const f32x4 sq = *(const f32x4*)(sinT + (int64_t)pos * 64 + flo);
+#pragma unroll
+          for (int hw_ = 0; hw_ < RH; ++hw_) {
+            const int hh = g * P.r + hw_;
+            const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + i) * P.qs_t + hh * P.qs_h;
+            const uint16_t* grow = dout + b * P.os_b + (int64_t)(start + i) * P.os_t + hh * P.os_h;
+            const u32x2 qa = *(const u32x2*)(qrow + flo), qb = *(const u32x2*)(qrow + fhi);
+            float y1[4], y2[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t wa = qa[e >> 1], wb = qb[e >> 1];
+              const float x1 = __uint_as_float((e & 1) ? (wa & 0xffff0000u) : (wa << 16));
+              const float x2 = __uint_as_float((e & 1) ? (wb & 0xffff0000u) : (wb << 16));
+              y1[e] = x1 * cq[e] - x2 * sq[e];
+              y2[e] = x2 * cq[e] + x1 * sq[e];
+            }
+            qh[hw_][0] = u32x2{pack_h2(y1[0], y1[1]), pack_h2(y1[2], y1[3])};
+            qh[hw_][1] = u32x2{pack_h2(y2[0], y2[1]), pack_h2(y2[2], y2[3])};
+            gh[hw_][0] = *(const u32x2*)(grow + flo);
+            gh[hw_][1] = *(const u32x2*)(grow + fhi);
+            lse_[hw_] = lse[b * P.lse_b + hh * P.lse_h + start + i];
+            dl_[hw_] = delta[(int64_t)(b * P.Hq + hh) * P.spad + slot0 + i];
+          }
+        }
+        const int64_t koff = b * P.ks_b + (int64_t)(start + i) * P.ks_t + g * P.ks_h;
+        for (int qq = 2; qq <= P.p; ++qq) {
+          const uint16_t* krow_ = (const uint16_t*)kv.k[qq - 1] + koff;
+          const uint16_t* vrow_ = (const uint16_t*)kv.v[qq - 1] + koff;
+          const u32x2 ka = *(const u32x2*)(krow_ + flo), kb = *(const u32x2*)(krow_ + fhi);
+          const u32x2 vv[2] = {*(const u32x2*)(vrow_ + flo), *(const u32x2*)(vrow_ + fhi)};
+          const int pk = P.q_off + i + qq - 1;
+          const f32x4 ck = *(const f32x4*)(cosT + (int64_t)pk * 64 + flo);
+          const f32x4 sk = *(const f32x4*)(sinT + (int64_t)pk * 64 + flo);
+          float kr[8], dk_[8], dv_[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t wa = ka[e >> 1], wb = kb[e >> 1];
+            const float x1 = __uint_as_float((e & 1) ? (wa & 0xffff0000u) : (wa << 16));
+            const float x2 = __uint_as_float((e & 1) ? (wb & 0xffff0000u) : (wb << 16));
+            kr[e] = x1 * ck[e] - x2 * sk[e];
+            kr[4 + e] = x2 * ck[e] + x1 * sk[e];
+          }
+          const uint32_t krh[4] = {pack_h2(kr[0], kr[1]), pack_h2(kr[2], kr[3]), pack_h2(kr[4], kr[5]),
+                                   pack_h2(kr[6], kr[7])};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dk_[e] = dv_[e] = 0.f;
+#pragma unroll
+          for (int hw_ = 0; hw_ < RH; ++hw_) {
+            float ps = 0.f, pd = 0.f;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int w = 0; w < 2; ++w) {
+                // vector elements go through scalars: a bit cast of an element
+                // subscript itself reads element 0
+                const uint32_t qw = qh[hw_][c][w], gw = gh[hw_][c][w], vw = vv[c][w], kw = krh[2 * c + w];
+                ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2v, qw), __builtin_bit_cast(h2v, kw), ps, false);
+                pd = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2v, gw), __builtin_bit_cast(b2v, vw), pd, false);
+              }
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) {
+              ps += __shfl_xor(ps, m, 64);
+              pd += __shfl_xor(pd, m, 64);
+            }
+            const float pr = __expf(ps * P.scale - lse_[hw_]);
+            const float dsv = pr * (pd - dl_[hw_]) * P.scale;
+            // the LDS row of (head, row): wave (rr/32)*RH + head, lane row rr%32
+            float* arow = sm.acc[((rr >> 5) * RH + hw_) * 32 + (rr & 31)];
+            f32x4 xl = *(const f32x4*)&arow[flo], xh = *(const f32x4*)&arow[fhi];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) xl[e] += dsv * kr[e], xh[e] += dsv * kr[4 + e];
+            *(f32x4*)&arow[flo] = xl;
+            *(f32x4*)&arow[fhi] = xh;
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+              for (int w = 0; w < 2; ++w) {
+                const uint32_t qw = qh[hw_][c][w], gw = gh[hw_][c][w];
+                const h2v qv = __builtin_bit_cast(h2v, qw);
+                dk_[c * 4 + 2 * w] += dsv * (float)qv[0];
+                dk_[c * 4 + 2 * w + 1] += dsv * (float)qv[1];
+                dv_[c * 4 + 2 * w] += pr * __uint_as_float(gw << 16);
+                dv_[c * 4 + 2 * w + 1] += pr * __uint_as_float(gw & 0xffff0000u);
+              }
+          }
+          float lo[4], hi[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo[e] = dk_[e] * ck[e] + dk_[4 + e] * sk[e];
+            hi[e] = dk_[4 + e] * ck[e] - dk_[e] * sk[e];
+          }
+          if (P.out_f32) {  // ring-step terms: fp32
+            float* fk = (float*)gr.dk[qq - 1] + koff;
+            float* fv = (float*)gr.dv[qq - 1] + koff;
+            *(f32x4*)(fk + flo) = f32x4{lo[0], lo[1], lo[2], lo[3]};
+            *(f32x4*)(fk + fhi) = f32x4{hi[0], hi[1], hi[2], hi[3]};
+            *(f32x4*)(fv + flo) = f32x4{dv_[0], dv_[1], dv_[2], dv_[3]};
+            *(f32x4*)(fv + fhi) = f32x4{dv_[4], dv_[5], dv_[6], dv_[7]};
+          } else {
+            uint16_t* dkrow = (uint16_t*)gr.dk[qq - 1] + koff;
+            uint16_t* dvrow = (uint16_t*)gr.dv[qq - 1] + koff;
+            *(u32x2*)(dkrow + flo) = u32x2{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3])};
+            *(u32x2*)(dkrow + fhi) = u32x2{pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
+            *(u32x2*)(dvrow + flo) = u32x2{pack_bf2(dv_[0], dv_[1]), pack_bf2(dv_[2], dv_[3])};
+            *(u32x2*)(dvrow + fhi) = u32x2{pack_bf2(dv_[4], dv_[5]), pack_bf2(dv_[6], dv_[7])};
+          }
+        }
+      }
+      __syncthreads();  // the dQ~ rows are updated across threads
+    }
+  }
+
   const int c8 = tid & 7;
   const int dlo = c8 * 8, dhi = 64 + c8 * 8;
+  // row-major epilogue: branch terms (unless fused above), un-rotation, store.
+  // LDS row lr holds wave lr/32's row lr%32.
   for (int rp = 0; rp < 128; rp += 32) {
     const int lr = rp + (tid >> 3);
     const int w_ = lr >> 5;
@@ -324,7 +461,7 @@ __global__ void __launch_bounds__(256, 2)
     const int pos = TTT_ ? P.q_off + i + P.p - 1 : block_anchor(P, b, i) + (i & ((1 << P.bs_log2) - 1));
     const float* cq = cosT + (int64_t)pos * 64 + dlo;
     const float* sq = sinT + (int64_t)pos * 64 + dlo;
-    if (TTT_ && P.p > 1 && P.branch) {
+    if (TTT_ && P.p > 1 && P.branch && !P.dq_branch) {
       float qr[16], go[16];
       {
         const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + i) * P.qs_t + hh * P.qs_h;
@@ -869,7 +1006,7 @@ template <int RH, int MODE>
 static void launch_dq_rh(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
                          const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
                          const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq,
-                         const _Float16* kbt, const _Float16* kbtt, hipStream_t st) {
+                         const _Float16* kbt, const _Float16* kbtt, const PassGradPtrs& g, hipStream_t st) {
   constexpr int RT = bwd::dq_rows(RH);
   const int nsub = P.r / RH;
   int64_t grid;
@@ -880,27 +1017,30 @@ static void launch_dq_rh(const Prob& P, const uint16_t* q, const PassPtrs& kv, c
     grid = (int64_t)((P.stok + RT - 1) / RT + P.nseq) * P.Hkv * nsub;
   }
   bwd::dq_bf16_kernel<RH, MODE><<<(unsigned)grid, 256, 0, st>>>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q,
-                                                                cosT, sinT, dq, kbt, kbtt);
+                                                                cosT, sinT, dq, kbt, kbtt, g);
 }
 
 int dq_tile_rows(int r) { return bwd::dq_rows(bwd::dq_heads_per_wg(r)); }
 
+bool dq_fuses_branch(int r) { return bwd::dq_heads_per_wg(r) == r; }
+
 void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
                     const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
-                    const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st) {
+                    const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, const PassGradPtrs& g,
+                    hipStream_t st) {
   const bool w = P.win > 0;  // sliding window: its own instantiation (MODE 4)
   switch (bwd::dq_heads_per_wg(P.r)) {
     case 4:
-      if (w) launch_dq_rh<4, 4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
-      else launch_dq_rh<4, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
+      if (w) launch_dq_rh<4, 4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, g, st);
+      else launch_dq_rh<4, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, g, st);
       break;
     case 2:
-      if (w) launch_dq_rh<2, 4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
-      else launch_dq_rh<2, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
+      if (w) launch_dq_rh<2, 4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, g, st);
+      else launch_dq_rh<2, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, g, st);
       break;
     default:
-      if (w) launch_dq_rh<1, 4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
-      else launch_dq_rh<1, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, st);
+      if (w) launch_dq_rh<1, 4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, g, st);
+      else launch_dq_rh<1, 0>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, g, st);
       break;
   }
 }
@@ -912,10 +1052,11 @@ void launch_block_dq_bf16(const Prob& P, const uint16_t* v_ctx, const uint16_t* 
   PassPtrs kv = {};
   kv.v[0] = v_ctx;
   kv.v[1] = v_blk;
+  const PassGradPtrs none = {};
   switch (bwd::dq_heads_per_wg(P.r)) {
-    case 4: launch_dq_rh<4, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, st); break;
-    case 2: launch_dq_rh<2, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, st); break;
-    default: launch_dq_rh<1, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, st); break;
+    case 4: launch_dq_rh<4, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, none, st); break;
+    case 2: launch_dq_rh<2, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, none, st); break;
+    default: launch_dq_rh<1, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, none, st); break;
   }
 }
 

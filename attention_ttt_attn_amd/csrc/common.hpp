@@ -56,6 +56,9 @@ struct Prob {
   int win;
   // backward outputs in fp32 (ring-step terms the caller sums) instead of the inputs' bf16
   int out_f32;
+  // the dQ kernel also produces the branch dK/dV of passes 2..p (its work
+  // item holds every query head of a KV group); no separate branch kernel
+  int dq_branch;
 };
 
 __device__ __forceinline__ int block_anchor(const Prob& P, int b, int row) {

@@ -899,7 +899,11 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.q_off + P.p - 1, 1, 0, qt, nullptr, 0, nullptr, 0};
     TTT_TRACED("prep_kq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
     if (forked) sd.wait(st, delta_done);
-    const bool branch = P.p > 1 && P.branch;
+    // branch dK/dV of passes 2..p: in the dQ kernel's epilogue when its work
+    // item holds every query head of a KV group, else a kernel of their own
+    // beside dK/dV on the side stream
+    P.dq_branch = ttt::dq_fuses_branch(P.r) ? 1 : 0;
+    const bool branch = P.p > 1 && P.branch && !P.dq_branch;
     if (forked && branch) sd.wait(sd.side, sd.mark(st));  // start the branch kernel with dK/dV, not beside the prologue
     if (branch)
       TTT_TRACED_ON("branch_bwd", sst,
@@ -910,7 +914,7 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     TTT_TRACED("trunk_dkdv", ttt::launch_dkdv_bf16(Pk, kv, lse, (const uint16_t*)dout, kt, qt, delta, tkv, cosT,
                                                    sinT, g, st));
     TTT_TRACED("trunk_dq", ttt::launch_dq_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, kt, ktt, qt,
-                                               delta, tq, cosT, sinT, (uint16_t*)dq, st));
+                                               delta, tq, cosT, sinT, (uint16_t*)dq, g, st));
     if (forked && branch) sd.wait(st, sd.mark(sd.side));  // the branch gradients are in
   }
   return hip_check("ttt_attn_bwd launch");

@@ -74,7 +74,10 @@ void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt,
                            const _Float16* kbt, const uint16_t* vbt, const float* cosT, const float* sinT, void* o,
                            bool o_f32, float* lse, hipStream_t st);     // query rows per forward work item for GQA ratio r (32, 64 or 128)
 constexpr int kFwdMinRows = 32;
-int dq_tile_rows(int r);      // query rows per dQ work item for GQA ratio r (32, 64 or 128)
+int dq_tile_rows(int r);
+// whether the dQ kernel's work item holds every query head of a KV group, so
+// that it can also produce the branch dK/dV (Prob::dq_branch)
+bool dq_fuses_branch(int r);      // query rows per dQ work item for GQA ratio r (32, 64 or 128)
 constexpr int kBwdBKV = 128;  // key rows per dK/dV workgroup
 void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const uint16_t* vt,
                      const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
@@ -84,7 +87,8 @@ void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const
                       const float* sinT, const PassGradPtrs& g, hipStream_t st);
 void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse, const uint16_t* dout,
                     const _Float16* kt, const _Float16* ktt, const _Float16* qt, const float* delta,
-                    const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st);
+                    const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, const PassGradPtrs& g,
+                    hipStream_t st);
 void launch_branch_bwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const float* lse,
                             const uint16_t* dout, const float* delta, const float* cosT, const float* sinT,
                             const PassGradPtrs& g, hipStream_t st);
