@@ -65,6 +65,17 @@ def test_bf16_bshd_small_backward(dev, tk, p):
     full_bwd_check(tk, Inputs(w, dev), p, "bshd_small")
 
 
+@pytest.mark.parametrize("hq,hkv,layout", [(8, 1, "bshd"), (6, 2, "bshd"), (16, 2, "thd"), (2, 1, "bshd")])
+def test_bf16_gqa_ratios_backward(dev, tk, hq, hkv, layout):
+    """GQA 8:1 and 3:1 (a KV group's query heads span several dQ work items, so the branch
+    gradients come from their own kernel), 8:1 THD, and 2:1 (the dQ epilogue produces them)."""
+    lens = [130, 1, 64, 97]
+    S = sum(lens) if layout == "thd" else 160
+    w = syn.Workload(f"gqa_{hq}_{hkv}", 27, layout, 1 if layout == "thd" else 2, S, hq, hkv, 128, 3, "bf16", 1e6, True)
+    inp = Inputs(w, dev, lengths=lens if layout == "thd" else None)
+    full_bwd_check(tk, inp, 3, f"gqa {hq}:{hkv} {layout}")
+
+
 @pytest.mark.parametrize("p", [1, 3])
 def test_bf16_thd_small_backward(dev, tk, p):
     lens = [1, 63, 64, 65, 200, 129, 3, 130]
