@@ -12,13 +12,16 @@
 // * dq_bf16_kernel (query-outer, MFMA): per 32 query rows of the heads of one
 //   KV group, loops over the causal key tiles and accumulates
 //   dQ~^T = K~^T dS^T; the epilogue adds the branch terms of passes 2..p
-//   (row-local, xor-shuffle reductions), un-rotates and writes dQ.  No
-//   atomics: deterministic.
+//   (row-local, xor-shuffle reductions), un-rotates and writes dQ.  When the
+//   work item holds every query head of the group it also sums the branch
+//   dK/dV of passes 2..p over those heads and writes them.  No atomics:
+//   deterministic.
 // * dkdv_bf16_kernel (key-outer, MFMA): per 128 trunk keys of one KV head,
 //   loops over the r query heads of the group and the query rows i >= j;
 //   dK~^T and dV^T stay in VGPRs; un-rotated in the epilogue.
 // * branch_bwd_bf16_kernel (HBM-bound, no MFMA): dK^(q), dV^(q) for q = 2..p at
-//   every row, summed over the group's heads with xor-shuffle dot products.
+//   every row, summed over the group's heads with xor-shuffle dot products,
+//   for groups wider than a dQ work item.
 // MFMA operand layouts follow the forward: transposed products so that one
 // product's accumulator is the next one's B operand (A rows read permuted).
 #include <type_traits>
