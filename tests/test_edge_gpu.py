@@ -69,6 +69,29 @@ def test_thd_with_empty_and_single_token_sequences(dev, tk):
             assert rel_fro(to_np(dvs[t]), g_ref[2][t]) <= 1e-2
 
 
+def test_thd_more_sequences_than_one_scheduler_pass(dev, tk):
+    # 1500 sequences of 0..8 tokens, two longer ones placed past the first
+    # 1024: the varlen scheduler lays out slots and lists tiles in passes of
+    # 1024 sequences, so the second pass and its carried offsets are exercised.
+    rng = np.random.default_rng(7)
+    lens = rng.integers(0, 9, 1500).tolist()
+    lens[700], lens[1200] = 300, 129
+    w = syn.Workload("thd_many", 33, "thd", 1, sum(lens), 4, 2, 128, 2, "bf16", 1e4, True)
+    inp = Inputs(w, dev, lengths=lens)
+    kw = inp.kw()
+    for p in (1, 2):
+        o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, o_fp32=True, check_cu_seqlens=True, **kw)
+        dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, **kw)
+        torch.cuda.synchronize()
+        o_ref, l_ref = O.fwd(inp.q[p], inp.k, inp.v, p, layout="thd", cu_seqlens=inp.cu_host, base=w.rope_base)
+        g_ref = O.bwd(inp.q[p], inp.k, inp.v, inp.do[p], p, layout="thd", cu_seqlens=inp.cu_host, base=w.rope_base)
+        assert max_abs(to_np(o), o_ref) <= 1e-2 and max_abs(to_np(lse), l_ref) <= 2e-3
+        assert rel_fro(to_np(dq), g_ref[0]) <= 1e-2
+        for t in range(p):
+            assert rel_fro(to_np(dks[t]), g_ref[1][t]) <= 1e-2
+            assert rel_fro(to_np(dvs[t]), g_ref[2][t]) <= 1e-2
+
+
 def test_invalid_cu_seqlens_rejected_when_checked(dev, tk):
     q = torch.zeros((10, 4, 128), dtype=torch.bfloat16, device=dev)
     k = [torch.zeros((10, 2, 128), dtype=torch.bfloat16, device=dev)]
