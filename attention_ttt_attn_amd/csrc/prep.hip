@@ -8,8 +8,13 @@ namespace ttt {
 // as fp32 [npos][D/2].  base == 0 fills the identity rotation (cos 1, sin 0).
 // Rotate-half RoPE: NeoX pairing of k and k + D/2 (NeMo-RL PR #3725,
 // self-review comment: rotate-half oracle).
-__global__ void rope_table_kernel(float* __restrict__ cosT, float* __restrict__ sinT, int npos, int half,
-                                  double base) {
+// theta_k is evaluated once per workgroup (half <= 64: D <= 128, checked by
+// the caller), then one fp64 sincos per entry.
+__global__ void __launch_bounds__(256) rope_table_kernel(float* __restrict__ cosT, float* __restrict__ sinT,
+                                                         int npos, int half, double base) {
+  __shared__ double th[64];
+  if ((int)threadIdx.x < half) th[threadIdx.x] = pow(base, -2.0 * (double)threadIdx.x / (double)(2 * half));
+  __syncthreads();
   int64_t n = (int64_t)npos * half;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
     int pos = (int)(e / half), k = (int)(e % half);
@@ -17,10 +22,10 @@ __global__ void rope_table_kernel(float* __restrict__ cosT, float* __restrict__ 
       cosT[e] = 1.f;
       sinT[e] = 0.f;
     } else {
-      double th = pow(base, -2.0 * (double)k / (double)(2 * half));
-      double a = (double)pos * th;
-      cosT[e] = (float)cos(a);
-      sinT[e] = (float)sin(a);
+      double sn, cs;
+      sincos((double)pos * th[k], &sn, &cs);
+      cosT[e] = (float)cs;
+      sinT[e] = (float)sn;
     }
   }
 }
@@ -241,11 +246,20 @@ __global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict
 // (descending == 2: the key-outer kernel's XCD-local order).  Entry = {tile
 // index, first token, length, first slot}; out[0].x = count.  One workgroup;
 // deterministic order.
+// In the heavy-first orders, sequences ascend within one tile index t, so the
+// entry of (s, t) sits at  (tiles of all sequences whose index comes before t)
+// + (sequences s' < s that have a tile t).  The first term has a closed form,
+// sum_s max(0, nt_s - t - 1) descending or sum_s min(nt_s, t) ascending
+// (nt_s = tiles of sequence s); the second is a running ballot count.  Each
+// wave lists its own tile indices t = w, w + 16, ..., so no block-wide
+// barrier is paid per tile index.
 __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int descending, int4* __restrict__ out,
                                                           int max_entries, int* __restrict__ slot_base) {
   __shared__ int s_maxt;
+  __shared__ int s_total;
   __shared__ int s_base;
   __shared__ int s_scan[1024];
+  __shared__ int4 s_seq[1024];  // listing: {first token, length, first slot, tiles} of sequences 0..1023
   const int tid = threadIdx.x;
   const int slot_cap = P.spad - 64;
   auto raw_len = [&](int s, int& a) {
@@ -266,7 +280,7 @@ __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int 
     }
     return s_scan[tid];
   };
-  if (tid == 0) s_base = 0, s_maxt = 0;
+  if (tid == 0) s_base = 0, s_maxt = 0, s_total = 0;
   __syncthreads();
   if (slot_base) {
     for (int s0 = 0; s0 < P.nseq; s0 += 1024) {
@@ -309,31 +323,51 @@ __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int 
     if (tid == 0) out[0] = make_int4(s_base < max_entries ? s_base : max_entries, 0, 0, 0);
     return;
   }
+  // sequence s's {first token, length, first slot, tiles}: from LDS for the
+  // first 1024 sequences, recomputed from cu_seqlens beyond
+  auto info = [&](int s) {
+    if (s < 1024) return s_seq[s];
+    int b, st0, L;
+    seq_info(Q, s, b, st0, L);
+    return make_int4(st0, L, Q.slot_base[s], (L + tile - 1) / tile);
+  };
+  int mine = 0;
   for (int s = tid; s < P.nseq; s += 1024) {
     int b, st0, L;
     seq_info(Q, s, b, st0, L);
-    atomicMax(&s_maxt, (L + tile - 1) / tile);
+    const int nt = (L + tile - 1) / tile;
+    if (s < 1024) s_seq[s] = make_int4(st0, L, Q.slot_base[s], nt);
+    atomicMax(&s_maxt, nt);
+    mine += nt;
   }
+  if (mine) atomicAdd(&s_total, mine);
   __syncthreads();
   const int maxt = s_maxt;
-  for (int it = 0; it < maxt; ++it) {
-    int t = descending ? maxt - 1 - it : it;
-    for (int s0 = 0; s0 < P.nseq; s0 += 1024) {
-      int s = s0 + tid;
-      int b, st0 = 0, L = 0, flag = 0;
+  const int lane = tid & 63, wv = tid >> 6;
+  for (int t = wv; t < maxt; t += 16) {
+    int before = 0;  // entries ahead of tile index t
+    for (int s0 = 0; s0 < P.nseq; s0 += 64) {
+      const int s = s0 + lane;
       if (s < P.nseq) {
-        seq_info(Q, s, b, st0, L);
-        flag = t * tile < L;
+        const int nt = info(s).w;
+        before += descending ? max(0, nt - t - 1) : min(nt, t);
       }
-      int inc = block_scan(flag);
-      int idx = s_base + inc - flag;
-      if (flag && idx < max_entries) out[1 + idx] = make_int4(t, st0, L, Q.slot_base[s]);
-      __syncthreads();
-      if (tid == 1023) s_base += s_scan[1023];
-      __syncthreads();
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) before += __shfl_xor(before, m, 64);
+    int run = 0;  // sequences before s0 that have a tile t
+    for (int s0 = 0; s0 < P.nseq; s0 += 64) {
+      const int s = s0 + lane;
+      int4 e = make_int4(0, 0, 0, 0);
+      if (s < P.nseq) e = info(s);
+      const bool flag = t < e.w;
+      const unsigned long long m = __ballot(flag);
+      const int idx = before + run + __popcll(m & ((1ull << lane) - 1ull));
+      if (flag && idx < max_entries) out[1 + idx] = make_int4(t, e.x, e.y, e.z);
+      run += __popcll(m);
     }
   }
-  if (tid == 0) out[0] = make_int4(s_base < max_entries ? s_base : max_entries, 0, 0, 0);
+  if (tid == 0) out[0] = make_int4(s_total < max_entries ? s_total : max_entries, 0, 0, 0);
 }
 
 // ----------------------------------------------------------------------------- launchers
