@@ -239,14 +239,20 @@ __global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict
 // Varlen tile scheduler (THD).  First lays out the workspace slots: sequence
 // s gets slot_base[s] .. slot_base[s+1], its length rounded up to 64 (clamped
 // so the total stays inside the workspace).  Then, when `out` is given, splits
-// every sequence into tiles of `tile` rows and lists them heavy-first:
+// every sequence into tiles of `tile` rows and lists them.  Heavy first means
 // descending tile index for the query-outer kernels (a query tile's causal
-// work grows with its index), ascending for the key-outer kernel (a key tile's
-// work shrinks with its index), or sequence-major with ascending tiles
-// (descending == 2: the key-outer kernel's XCD-local order).  Entry = {tile
-// index, first token, length, first slot}; out[0].x = count.  One workgroup;
+// work grows with its index) and ascending for the key-outer kernel (a key
+// tile's work shrinks with its index).  Orders (argument `descending`):
+//   0 / 1  all tiles by index, ascending / descending, sequences in index order
+//          within one index;
+//   2 / 3  sequence-major, longest sequence first, tiles ascending /
+//          descending within a sequence (index order of sequences past 1024).
+// The kernels map consecutive entries of one KV head to one XCD, so the
+// sequence-major orders put tiles of one sequence side by side on an XCD,
+// where they share the rows they stream through its L2.  Entry = {tile index,
+// first token, length, first slot}; out[0].x = count.  One workgroup;
 // deterministic order.
-// In the heavy-first orders, sequences ascend within one tile index t, so the
+// In orders 0 / 1, sequences ascend within one tile index t, so the
 // entry of (s, t) sits at  (tiles of all sequences whose index comes before t)
 // + (sequences s' < s that have a tile t).  The first term has a closed form,
 // sum_s max(0, nt_s - t - 1) descending or sum_s min(nt_s, t) ascending
@@ -304,7 +310,34 @@ __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int 
   if (!out) return;
   Prob Q = P;
   Q.slot_base = slot_base ? slot_base : P.slot_base;
-  if (descending == 2) {  // sequence-major, tiles ascending within a sequence
+  const bool seq_major = descending >= 2, asc = descending != 1 && descending != 3;
+  if (seq_major && P.nseq <= 1024) {
+    // sequence-major, longest sequence first (ties: lower index first), tiles
+    // heavy-first within a sequence: a sequence's entries start after the
+    // tiles of every sequence ranked before it
+    int st0 = 0, L = 0, nt = 0;
+    if (tid < P.nseq) {
+      int b;
+      seq_info(Q, tid, b, st0, L);
+      nt = (L + tile - 1) / tile;
+      s_seq[tid] = make_int4(st0, L, Q.slot_base[tid], nt);
+      atomicAdd(&s_total, nt);
+    }
+    __syncthreads();
+    if (tid < P.nseq) {
+      int base = 0;
+      for (int s2 = 0; s2 < P.nseq; ++s2) {
+        const int4 o = s_seq[s2];
+        if (o.y > L || (o.y == L && s2 < tid)) base += o.w;
+      }
+      const int slot = s_seq[tid].z;
+      for (int t = 0; t < nt; ++t)
+        if (base + t < max_entries) out[1 + base + t] = make_int4(asc ? t : nt - 1 - t, st0, L, slot);
+    }
+    if (tid == 0) out[0] = make_int4(s_total < max_entries ? s_total : max_entries, 0, 0, 0);
+    return;
+  }
+  if (seq_major) {  // more sequences: sequence-major in index order
     for (int s0 = 0; s0 < P.nseq; s0 += 1024) {
       const int s = s0 + tid;
       int b, st0 = 0, L = 0, nt = 0;
@@ -315,7 +348,7 @@ __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int 
       const int inc = block_scan(nt);
       const int base = s_base + inc - nt;
       for (int t = 0; t < nt; ++t)
-        if (base + t < max_entries) out[1 + base + t] = make_int4(t, st0, L, Q.slot_base[s]);
+        if (base + t < max_entries) out[1 + base + t] = make_int4(asc ? t : nt - 1 - t, st0, L, Q.slot_base[s]);
       __syncthreads();
       if (tid == 1023) s_base += s_scan[1023];
       __syncthreads();
