@@ -617,6 +617,7 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, (uint16_t*)bktt, 1, nullptr, 0};
   int* lims = (int*)(delta + (size_t)2 * P.B * P.Hq * P.spad);  // per-slot visible context lengths
   J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, 0, 1, 0, qt, nullptr, 1, lims, 0};
+  J.heads_fast = 1;  // mostly row-major outputs (Q~ rows)
   TTT_TRACED("prep_blkq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
   if (P.kv_len > 0) {
     ttt::Prob Pc = P;  // the context keys' V / dK / dV strides
@@ -897,6 +898,7 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, (uint16_t*)ktt, 0,
               nullptr, krows};
     J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.q_off + P.p - 1, 1, 0, qt, nullptr, 0, nullptr, 0};
+    J.heads_fast = 1;  // mostly row-major outputs (Q~ rows)
     TTT_TRACED("prep_kq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
     if (forked) sd.wait(st, delta_done);
     // branch dK/dV of passes 2..p: in the dQ kernel's epilogue when its work

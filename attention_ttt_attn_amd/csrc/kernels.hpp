@@ -26,6 +26,7 @@ struct PrepJob {
 struct PrepJobs {
   PrepJob j[2];
   int n;
+  int heads_fast;  // grid order: heads of one 64-slot tile side by side (row-major outputs) instead of tiles of one head
 };
 void launch_prep_bf16(const Prob& P, const PrepJobs& J, const float* cosT, const float* sinT, hipStream_t st);
 // Delta (and, with lse, the LSE in log2 units right after it, +inf past the

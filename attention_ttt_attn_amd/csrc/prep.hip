@@ -115,16 +115,23 @@ __global__ void __launch_bounds__(256) prep_rows_kernel(Prob P, const InT* __res
 //   out_row [(b*H + h)][spad][128]  fp16, rotated at position (row + pos_off) when rot
 //   out_col [(b*H + h)][128][spad]  the same values transposed, fp16 or bf16
 // by workspace slot (slots without a token are written as 0).  Grid
-// (spad/64, H_0 + H_1, B): blockIdx.y < H_0 selects job 0.  Each thread owns
-// 8 rotation pairs (k, k + 64) of a row; 32 rows per pass, two passes.
+// ((spad/64) * (H_0 + H_1), 1, B): head index hy = H_0 + H_1 entries, hy < H_0
+// selects job 0.  J.heads_fast puts the heads of one 64-slot tile in
+// consecutive workgroups, so that workgroups running together read whole token
+// rows (better for row-major outputs); otherwise the tiles of one head are
+// consecutive, which keeps neighbouring transposed writes adjacent.  Each
+// thread owns 8 rotation pairs (k, k + 64) of a row; 32 rows per pass, two passes.
 __global__ void __launch_bounds__(256) prep_bf16_kernel(Prob P, PrepJobs J, const float* __restrict__ cosT,
                                                         const float* __restrict__ sinT) {
   constexpr int D = 128, HALF = 64;
   __shared__ uint32_t tile[64][D / 2 + 1];  // 16-bit pairs; 65-dword rows: conflict-free column reads
-  const bool second = (int)blockIdx.y >= J.j[0].H;
+  const unsigned Ht = (unsigned)(J.j[0].H + (J.n > 1 ? J.j[1].H : 0)), ntile = (unsigned)P.spad / 64;
+  const int hy = (int)(J.heads_fast ? blockIdx.x % Ht : blockIdx.x / ntile);
+  const int tix = (int)(J.heads_fast ? blockIdx.x / Ht : blockIdx.x % ntile);
+  const bool second = hy >= J.j[0].H;
   const PrepJob jb = second ? J.j[1] : J.j[0];
-  const int h = second ? (int)blockIdx.y - J.j[0].H : (int)blockIdx.y;
-  const int b = blockIdx.z, tok0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int h = second ? hy - J.j[0].H : hy;
+  const int b = blockIdx.z, tok0 = tix * 64, tid = threadIdx.x;
   const int c8 = tid & 7, rr = tid >> 3;
   const int64_t slab = (int64_t)(b * jb.H + h) * P.spad;
 #pragma unroll
@@ -436,7 +443,7 @@ void launch_prep_rot_f32(const Prob& P, const float* x, int64_t sb, int64_t st_,
 }
 
 void launch_prep_bf16(const Prob& P, const PrepJobs& J, const float* cosT, const float* sinT, hipStream_t st) {
-  dim3 grid(P.spad / 64, J.j[0].H + (J.n > 1 ? J.j[1].H : 0), P.B);
+  dim3 grid((P.spad / 64) * (J.j[0].H + (J.n > 1 ? J.j[1].H : 0)), 1, P.B);
   prep_bf16_kernel<<<grid, 256, 0, st>>>(P, J, cosT, sinT);
 }
 
