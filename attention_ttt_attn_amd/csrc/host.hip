@@ -424,7 +424,7 @@ int fwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     if (thd) {
       int4* t = at<int4>(ws, pl.ws.tiles_q);
       TTT_TRACED("tile_sched",
-                 ttt::launch_tile_sched(P, ttt::fwd_tile_rows(P.r), 3, t, pl.max_tiles_q, slots, st));
+                 ttt::launch_tile_sched(P, ttt::fwd_tile_rows(P.r), 1, t, pl.max_tiles_q, slots, st));
       tiles = t;
     }
     _Float16* kt = at<_Float16>(ws, pl.ws.kt);
@@ -859,8 +859,8 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     if (pl.bf16) {
       int4* a = at<int4>(ws, pl.ws.tiles_q);
       int4* b = at<int4>(ws, pl.ws.tiles_kv);
-      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::dq_tile_rows(P.r), 3, a, pl.max_tiles_q, slots, st));
-      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kBwdBKV, 2, b, pl.max_tiles_kv, nullptr, st));
+      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::dq_tile_rows(P.r), 1, a, pl.max_tiles_q, slots, st));
+      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kBwdBKV, 0, b, pl.max_tiles_kv, nullptr, st));
       tq = a;
       tkv = b;
     } else {

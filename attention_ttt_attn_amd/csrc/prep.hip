@@ -246,33 +246,22 @@ __global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict
 // Varlen tile scheduler (THD).  First lays out the workspace slots: sequence
 // s gets slot_base[s] .. slot_base[s+1], its length rounded up to 64 (clamped
 // so the total stays inside the workspace).  Then, when `out` is given, splits
-// every sequence into tiles of `tile` rows and lists them.  Heavy first means
-// descending tile index for the query-outer kernels (a query tile's causal
-// work grows with its index) and ascending for the key-outer kernel (a key
-// tile's work shrinks with its index).  Orders (argument `descending`):
-//   0 / 1  all tiles by index, ascending / descending, sequences in index order
-//          within one index;
-//   2 / 3  sequence-major, longest sequence first, tiles ascending /
-//          descending within a sequence (index order of sequences past 1024).
-// The kernels map consecutive entries of one KV head to one XCD, so the
-// sequence-major orders put tiles of one sequence side by side on an XCD,
-// where they share the rows they stream through its L2.  Entry = {tile index,
-// first token, length, first slot}; out[0].x = count.  One workgroup;
-// deterministic order.
-// In orders 0 / 1, sequences ascend within one tile index t, so the
-// entry of (s, t) sits at  (tiles of all sequences whose index comes before t)
-// + (sequences s' < s that have a tile t).  The first term has a closed form,
-// sum_s max(0, nt_s - t - 1) descending or sum_s min(nt_s, t) ascending
-// (nt_s = tiles of sequence s); the second is a running ballot count.  Each
-// wave lists its own tile indices t = w, w + 16, ..., so no block-wide
-// barrier is paid per tile index.
-__global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int descending, int4* __restrict__ out,
+// every sequence into tiles of `tile` rows and lists them sequence-major:
+// longest sequence first (ties: lower index first), and within a sequence the
+// heavy tiles first -- descending tile index for the query-outer kernels
+// (`desc`: a query tile's causal work grows with its index), ascending for
+// the key-outer kernel (a key tile's work shrinks with its index).  The
+// kernels map consecutive entries of one KV head to one XCD, so tiles of one
+// sequence run side by side there and share the rows they stream through its
+// L2; ranking by length keeps the heaviest tiles early.  Past 1024 sequences
+// the sequences stay in index order.  Entry = {tile index, first token,
+// length, first slot}; out[0].x = count.  One workgroup; deterministic order.
+__global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int desc, int4* __restrict__ out,
                                                           int max_entries, int* __restrict__ slot_base) {
-  __shared__ int s_maxt;
   __shared__ int s_total;
   __shared__ int s_base;
   __shared__ int s_scan[1024];
-  __shared__ int4 s_seq[1024];  // listing: {first token, length, first slot, tiles} of sequences 0..1023
+  __shared__ int4 s_seq[1024];  // {first token, length, first slot, tiles} of each sequence
   const int tid = threadIdx.x;
   const int slot_cap = P.spad - 64;
   auto raw_len = [&](int s, int& a) {
@@ -293,7 +282,7 @@ __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int 
     }
     return s_scan[tid];
   };
-  if (tid == 0) s_base = 0, s_maxt = 0, s_total = 0;
+  if (tid == 0) s_base = 0, s_total = 0;
   __syncthreads();
   if (slot_base) {
     for (int s0 = 0; s0 < P.nseq; s0 += 1024) {
@@ -317,11 +306,8 @@ __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int 
   if (!out) return;
   Prob Q = P;
   Q.slot_base = slot_base ? slot_base : P.slot_base;
-  const bool seq_major = descending >= 2, asc = descending != 1 && descending != 3;
-  if (seq_major && P.nseq <= 1024) {
-    // sequence-major, longest sequence first (ties: lower index first), tiles
-    // heavy-first within a sequence: a sequence's entries start after the
-    // tiles of every sequence ranked before it
+  if (P.nseq <= 1024) {
+    // a sequence's entries start after the tiles of every sequence ranked before it
     int st0 = 0, L = 0, nt = 0;
     if (tid < P.nseq) {
       int b;
@@ -339,75 +325,27 @@ __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int 
       }
       const int slot = s_seq[tid].z;
       for (int t = 0; t < nt; ++t)
-        if (base + t < max_entries) out[1 + base + t] = make_int4(asc ? t : nt - 1 - t, st0, L, slot);
+        if (base + t < max_entries) out[1 + base + t] = make_int4(desc ? nt - 1 - t : t, st0, L, slot);
     }
     if (tid == 0) out[0] = make_int4(s_total < max_entries ? s_total : max_entries, 0, 0, 0);
     return;
   }
-  if (seq_major) {  // more sequences: sequence-major in index order
-    for (int s0 = 0; s0 < P.nseq; s0 += 1024) {
-      const int s = s0 + tid;
-      int b, st0 = 0, L = 0, nt = 0;
-      if (s < P.nseq) {
-        seq_info(Q, s, b, st0, L);
-        nt = (L + tile - 1) / tile;
-      }
-      const int inc = block_scan(nt);
-      const int base = s_base + inc - nt;
-      for (int t = 0; t < nt; ++t)
-        if (base + t < max_entries) out[1 + base + t] = make_int4(asc ? t : nt - 1 - t, st0, L, Q.slot_base[s]);
-      __syncthreads();
-      if (tid == 1023) s_base += s_scan[1023];
-      __syncthreads();
+  for (int s0 = 0; s0 < P.nseq; s0 += 1024) {  // more sequences: index order
+    const int s = s0 + tid;
+    int b, st0 = 0, L = 0, nt = 0;
+    if (s < P.nseq) {
+      seq_info(Q, s, b, st0, L);
+      nt = (L + tile - 1) / tile;
     }
-    if (tid == 0) out[0] = make_int4(s_base < max_entries ? s_base : max_entries, 0, 0, 0);
-    return;
+    const int inc = block_scan(nt);
+    const int base = s_base + inc - nt;
+    for (int t = 0; t < nt; ++t)
+      if (base + t < max_entries) out[1 + base + t] = make_int4(desc ? nt - 1 - t : t, st0, L, Q.slot_base[s]);
+    __syncthreads();
+    if (tid == 1023) s_base += s_scan[1023];
+    __syncthreads();
   }
-  // sequence s's {first token, length, first slot, tiles}: from LDS for the
-  // first 1024 sequences, recomputed from cu_seqlens beyond
-  auto info = [&](int s) {
-    if (s < 1024) return s_seq[s];
-    int b, st0, L;
-    seq_info(Q, s, b, st0, L);
-    return make_int4(st0, L, Q.slot_base[s], (L + tile - 1) / tile);
-  };
-  int mine = 0;
-  for (int s = tid; s < P.nseq; s += 1024) {
-    int b, st0, L;
-    seq_info(Q, s, b, st0, L);
-    const int nt = (L + tile - 1) / tile;
-    if (s < 1024) s_seq[s] = make_int4(st0, L, Q.slot_base[s], nt);
-    atomicMax(&s_maxt, nt);
-    mine += nt;
-  }
-  if (mine) atomicAdd(&s_total, mine);
-  __syncthreads();
-  const int maxt = s_maxt;
-  const int lane = tid & 63, wv = tid >> 6;
-  for (int t = wv; t < maxt; t += 16) {
-    int before = 0;  // entries ahead of tile index t
-    for (int s0 = 0; s0 < P.nseq; s0 += 64) {
-      const int s = s0 + lane;
-      if (s < P.nseq) {
-        const int nt = info(s).w;
-        before += descending ? max(0, nt - t - 1) : min(nt, t);
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) before += __shfl_xor(before, m, 64);
-    int run = 0;  // sequences before s0 that have a tile t
-    for (int s0 = 0; s0 < P.nseq; s0 += 64) {
-      const int s = s0 + lane;
-      int4 e = make_int4(0, 0, 0, 0);
-      if (s < P.nseq) e = info(s);
-      const bool flag = t < e.w;
-      const unsigned long long m = __ballot(flag);
-      const int idx = before + run + __popcll(m & ((1ull << lane) - 1ull));
-      if (flag && idx < max_entries) out[1 + idx] = make_int4(t, e.x, e.y, e.z);
-      run += __popcll(m);
-    }
-  }
-  if (tid == 0) out[0] = make_int4(s_total < max_entries ? s_total : max_entries, 0, 0, 0);
+  if (tid == 0) out[0] = make_int4(s_base < max_entries ? s_base : max_entries, 0, 0, 0);
 }
 
 // ----------------------------------------------------------------------------- launchers
@@ -512,9 +450,9 @@ void launch_merge(const Prob& P, bool o_f32, const void* o_a, const float* lse_a
                                                  (uint16_t*)o, lse);
 }
 
-void launch_tile_sched(const Prob& P, int tile, int descending, int4* out, int max_entries, int* slot_base,
+void launch_tile_sched(const Prob& P, int tile, int desc, int4* out, int max_entries, int* slot_base,
                        hipStream_t st) {
-  tile_sched_kernel<<<1, 1024, 0, st>>>(P, tile, descending, out, max_entries, slot_base);
+  tile_sched_kernel<<<1, 1024, 0, st>>>(P, tile, desc, out, max_entries, slot_base);
 }
 
 }  // namespace ttt
