@@ -385,39 +385,66 @@ __global__ void __launch_bounds__(256, 2)
 
   // ---- branch: keys/values of passes 2..p at the same row, folded into (m, l, O)
   const int lr = rbk * 32 + l32;  // this lane's row within the tile
-  for (int qq = 2; qq <= (TTT_ && P.branch ? P.p : 1); ++qq) {
-    // stage R(i+q-1) k^(q) (fp16) and v^(q) (bf16) for the tile's rows: 8 threads per row
-    for (int r0 = 0; r0 < RT; r0 += 32) {
-      const int rr = r0 + (tid >> 3), c8 = tid & 7;
-      const int i = row0 + rr;
-      const int dlo = c8 * 8, dhi = 64 + c8 * 8;
-      u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0}, vlo = {0, 0, 0, 0}, vhi = {0, 0, 0, 0};
-      if (i < L) {
-        const int64_t koff = b * P.ks_b + (int64_t)(start + i) * P.ks_t + g * P.ks_h;
-        const uint16_t* krow = (const uint16_t*)kv.k[qq - 1] + koff;
-        const uint16_t* vrow = (const uint16_t*)kv.v[qq - 1] + koff;
-        float x1[8], x2[8], y1[8], y2[8];
-        unpack_bf8(*(const u32x4*)(krow + dlo), x1);
-        unpack_bf8(*(const u32x4*)(krow + dhi), x2);
-        vlo = *(const u32x4*)(vrow + dlo);
-        vhi = *(const u32x4*)(vrow + dhi);
-        const int pk = P.q_off + i + qq - 1;
-        const float* cp = cosT + (int64_t)pk * 64 + dlo;
-        const float* sp = sinT + (int64_t)pk * 64 + dlo;
+  // Staging roles: 8 threads per row, rows 32j + tid/8.  With one 32-row set
+  // per work item the raw k^(q+1), v^(q+1) rows are loaded while pass q is
+  // computed, so a pass waits for no global load of its own (larger work
+  // items load each row set just before staging it: registers).
+  constexpr int NR = RT / 32;
+  const int bc8 = tid & 7, bdlo = bc8 * 8, bdhi = 64 + bc8 * 8;
+  auto load_rows = [&](int j, int qq, u32x4 (&kr)[2], u32x4 (&vr)[2]) __attribute__((always_inline)) {
+    const int i = row0 + j * 32 + (tid >> 3);
+    kr[0] = kr[1] = vr[0] = vr[1] = u32x4{0, 0, 0, 0};
+    if (i < L) {
+      const int64_t koff = b * P.ks_b + (int64_t)(start + i) * P.ks_t + g * P.ks_h;
+      const uint16_t* krow = (const uint16_t*)kv.k[qq - 1] + koff;
+      const uint16_t* vrow = (const uint16_t*)kv.v[qq - 1] + koff;
+      kr[0] = *(const u32x4*)(krow + bdlo);
+      kr[1] = *(const u32x4*)(krow + bdhi);
+      vr[0] = *(const u32x4*)(vrow + bdlo);
+      vr[1] = *(const u32x4*)(vrow + bdhi);
+    }
+  };
+  // R(i+q-1) k^(q) (fp16) and v^(q) (bf16) of row set j into LDS
+  auto stage_rows = [&](int j, int qq, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) __attribute__((always_inline)) {
+    const int rr = j * 32 + (tid >> 3);
+    const int i = row0 + rr;
+    u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0};
+    if (i < L) {
+      float x1[8], x2[8], y1[8], y2[8];
+      unpack_bf8(kr[0], x1);
+      unpack_bf8(kr[1], x2);
+      const int pk = P.q_off + i + qq - 1;
+      const float* cp = cosT + (int64_t)pk * 64 + bdlo;
+      const float* sp = sinT + (int64_t)pk * 64 + bdlo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          y1[e] = x1[e] * cp[e] - x2[e] * sp[e];
-          y2[e] = x2[e] * cp[e] + x1[e] * sp[e];
-        }
-        klo = pack_h8(y1);
-        khi = pack_h8(y2);
+      for (int e = 0; e < 8; ++e) {
+        y1[e] = x1[e] * cp[e] - x2[e] * sp[e];
+        y2[e] = x2[e] * cp[e] + x1[e] * sp[e];
       }
-      *(u32x4*)&sm.br.k[rr][dlo] = klo;
-      *(u32x4*)&sm.br.k[rr][dhi] = khi;
-      *(u32x4*)&sm.br.v[rr][dlo] = vlo;
-      *(u32x4*)&sm.br.v[rr][dhi] = vhi;
+      klo = pack_h8(y1);
+      khi = pack_h8(y2);
+    }
+    *(u32x4*)&sm.br.k[rr][bdlo] = klo;
+    *(u32x4*)&sm.br.k[rr][bdhi] = khi;
+    *(u32x4*)&sm.br.v[rr][bdlo] = vr[0];
+    *(u32x4*)&sm.br.v[rr][bdhi] = vr[1];
+  };
+  const int pmax = TTT_ && P.branch ? P.p : 1;
+  u32x4 kpre[2], vpre[2];  // one row set: the next pass's raw rows
+  if (NR == 1 && pmax >= 2) load_rows(0, 2, kpre, vpre);
+  for (int qq = 2; qq <= pmax; ++qq) {
+    if constexpr (NR == 1) {
+      stage_rows(0, qq, kpre, vpre);
+    } else {
+#pragma unroll 1
+      for (int j = 0; j < NR; ++j) {
+        u32x4 kr[2], vr[2];
+        load_rows(j, qq, kr, vr);
+        stage_rows(j, qq, kr, vr);
+      }
     }
     __syncthreads();
+    if (NR == 1 && qq < pmax) load_rows(0, qq + 1, kpre, vpre);
     // score: lane's Q~ fragment (d = 16c + 8hf + e) against the staged key row
     float part = 0.f;
 #pragma unroll
