@@ -356,14 +356,26 @@ __global__ void __launch_bounds__(256, 2)
           }
         }
         const int64_t koff = b * P.ks_b + (int64_t)(start + i) * P.ks_t + g * P.ks_h;
-        for (int qq = 2; qq <= P.p; ++qq) {
+        // pass q's key/value pieces and cos/sin, loaded one pass ahead
+        u32x2 nka, nkb, nva, nvb;
+        f32x4 nck, nsk;
+        auto load_pass = [&](int qq) __attribute__((always_inline)) {
           const uint16_t* krow_ = (const uint16_t*)kv.k[qq - 1] + koff;
           const uint16_t* vrow_ = (const uint16_t*)kv.v[qq - 1] + koff;
-          const u32x2 ka = *(const u32x2*)(krow_ + flo), kb = *(const u32x2*)(krow_ + fhi);
-          const u32x2 vv[2] = {*(const u32x2*)(vrow_ + flo), *(const u32x2*)(vrow_ + fhi)};
+          nka = *(const u32x2*)(krow_ + flo);
+          nkb = *(const u32x2*)(krow_ + fhi);
+          nva = *(const u32x2*)(vrow_ + flo);
+          nvb = *(const u32x2*)(vrow_ + fhi);
           const int pk = P.q_off + i + qq - 1;
-          const f32x4 ck = *(const f32x4*)(cosT + (int64_t)pk * 64 + flo);
-          const f32x4 sk = *(const f32x4*)(sinT + (int64_t)pk * 64 + flo);
+          nck = *(const f32x4*)(cosT + (int64_t)pk * 64 + flo);
+          nsk = *(const f32x4*)(sinT + (int64_t)pk * 64 + flo);
+        };
+        load_pass(2);
+        for (int qq = 2; qq <= P.p; ++qq) {
+          const u32x2 ka = nka, kb = nkb;
+          const u32x2 vv[2] = {nva, nvb};
+          const f32x4 ck = nck, sk = nsk;
+          if (qq < P.p) load_pass(qq + 1);
           float kr[8], dk_[8], dv_[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
