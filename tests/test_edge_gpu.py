@@ -72,8 +72,8 @@ def test_thd_with_empty_and_single_token_sequences(dev, tk):
 def test_thd_more_sequences_than_one_scheduler_pass(dev, tk):
     # 1500 sequences of 0..8 tokens, two longer ones placed past the first
     # 1024: the varlen scheduler lays out slots in passes of 1024 sequences
-    # (the second pass adds the first one's offset) and lists tiles from a
-    # copy of the first 1024 sequences in LDS, the rest from cu_seqlens.
+    # (the second pass adds the first one's offset), and past 1024 sequences
+    # it lists tiles sequence by sequence in index order, in the same passes.
     rng = np.random.default_rng(7)
     lens = rng.integers(0, 9, 1500).tolist()
     lens[700], lens[1200] = 300, 129
