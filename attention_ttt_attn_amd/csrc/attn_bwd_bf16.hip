@@ -41,6 +41,22 @@ constexpr int OPAD = D + 4;
 
 __device__ __forceinline__ int perm_row(int a) { return (a & ~0xC) | ((a & 4) << 1) | ((a & 8) >> 1); }
 
+// Largest of p[lo..hi) over the wave (0 for an empty range), eight loads in
+// flight per lane.
+__device__ __forceinline__ float range_max(const float* __restrict__ p, int lo, int hi, int lane) {
+  float m = 0.f;
+  for (int i = lo + lane; i < hi; i += 512) {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = i + 64 * k < hi ? p[i + 64 * k] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) m = fmaxf(m, x[k]);
+  }
+#pragma unroll
+  for (int s = 1; s < 64; s <<= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+  return m;
+}
+
 // ============================================================================= dQ
 // A workgroup is 4 wave64s: the R' query heads of one KV group that it covers
 // (R' = 4 for GQA 4:1) times 32*4/R' rows; each wave owns 32 query rows of one
@@ -203,7 +219,30 @@ __global__ void __launch_bounds__(256, 2)
   }
   // rows past the sequence end get LSE = +inf: every probability is then 0
   const float lse2 = row_ok ? lse[b * P.lse_b + h * P.lse_h + start + my_row] * kLog2e : INFINITY;
-  const float dl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row];
+  float dl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row];
+  // fp16 dS operands of this row carry the factor 2^e: |dS_ij| <= ||dO_i||_1
+  // max_j |v_jd| + |Delta_i| over the keys this work item visits (their
+  // per-32-key maxima come from the dK/dV kernel, which runs first).  The
+  // factor scales the row's dO operand (which feeds dP only) and Delta, so
+  // P (dP - Delta) 2^e is formed exactly; the epilogue takes it out again.
+  int eq;
+  {
+    const int64_t vb = (int64_t)(b * P.Hkv + g) * (P.spad / 32) + slot0 / 32;
+    float vm = TTT_ ? range_max(P.vmax + vb, kt_lo, nkt, lane) : range_max(P.vmax + vb, 0, nkt, lane);
+    if constexpr (MODE == 1) vm = fmaxf(vm, range_max(P.vmax_b + vb, row0 / 32, (qend + 31) / 32, lane));
+    const float dn = P.dnorm[(int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row];
+    eq = ds_exp(__builtin_fmaf(dn, vm, fabsf(dl)));
+    const float cq = __builtin_amdgcn_ldexpf(1.0f, eq);
+    dl *= cq;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      u32x4 x = __builtin_bit_cast(u32x4, dof[c]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        x[w] = pack_bf2(__uint_as_float(x[w] << 16) * cq, __uint_as_float(x[w] & 0xffff0000u) * cq);
+      dof[c] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
   const float sl2 = P.scale_log2;
   TTT_WAIT_VMCNT(0);
   asm volatile("" ::"v"(lse2), "v"(dl));  // their loads complete here, not inside the loop
@@ -297,13 +336,14 @@ __global__ void __launch_bounds__(256, 2)
   }
   {
     const int lr = wv * 32 + l32;
+    const float qsc = P.scale * __builtin_amdgcn_ldexpf(1.0f, -eq);  // sigma, and the dS factor undone
 #pragma unroll
     for (int d4 = 0; d4 < 4; ++d4)
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         f32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = acc[d4][v4 * 4 + e] * P.scale;
+        for (int e = 0; e < 4; ++e) w[e] = acc[d4][v4 * 4 + e] * qsc;
         *(f32x4*)&sm.acc[lr][d4 * 32 + v4 * 8 + hf * 4] = w;
       }
   }
@@ -619,7 +659,8 @@ __global__ void __launch_bounds__(256, 1)
   }
   const int kv0 = t * BKV;
   const int my_key = kv0 + wv * 32 + l32;
-  const bool key_ok = my_key < ((MODE == 2 || (TTT_ && P.layout == 0)) ? nkeys : L);
+  const int key_end = (MODE == 2 || (TTT_ && P.layout == 0)) ? nkeys : L;  // keys of this slab
+  const bool key_ok = my_key < key_end;
   // TTT ring steps (BSHD): row i at q_off + i sees key j at kv_off + j iff i >= j - dq_
   const int dq_ = (TTT_ && P.layout == 0) ? P.q_off - P.kv_off : 0;
   // query rows [row_lo, row_hi) that can see this key tile
@@ -660,6 +701,42 @@ __global__ void __launch_bounds__(256, 1)
       u32x4 x = key_ok ? *(const u32x4*)(vrow + d0) : u32x4{0, 0, 0, 0};
       vf[c] = __builtin_bit_cast(bf16x8, x);
     }
+  }
+  // fp16 dS operands carry a per-key factor 2^e: |dS_ij| <= P_ij (|<dO_i, v_j>|
+  // + |Delta_i|) <= N ||v_j||_inf + Dm, with N = max ||dO_i||_1 and Dm = max
+  // |Delta_i| over the rows of the group's heads (reduced after the Delta
+  // kernel).  Folded in exactly: V is scaled by 2^e (so dP is), Delta is
+  // scaled inside the fma that forms dP - Delta, and dK~ is unscaled in the
+  // epilogue; dV (from P) is untouched.
+  float vinf = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const u32x4 x = __builtin_bit_cast(u32x4, vf[c]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      vinf = fmaxf(vinf, fmaxf(fabsf(__uint_as_float(x[w] << 16)), fabsf(__uint_as_float(x[w] & 0xffff0000u))));
+  }
+  vinf = xhalf_max(vinf);  // the key's whole row
+  {
+    float wmax = vinf;  // the wave's 32 keys, for the dQ kernel's bound
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) wmax = fmaxf(wmax, __shfl_xor(wmax, m, 64));
+    // only waves whose keys start inside the slab: in THD the slots past a
+    // short sequence's end belong to the next sequence
+    float* vm = MODE == 3 ? P.vmax_b : P.vmax;
+    if (lane == 0 && kv0 + wv * 32 < key_end)
+      vm[(int64_t)(b * P.Hkv + g) * (P.spad / 32) + (slot0 + kv0) / 32 + wv] = wmax;
+  }
+  const float2 nd = *(const float2*)&P.dmax[(int64_t)(b * P.Hkv + g) * 2];
+  const int ek = ds_exp(__builtin_fmaf(nd.x, vinf, nd.y));
+  const float cj = __builtin_amdgcn_ldexpf(1.0f, ek);
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    u32x4 x = __builtin_bit_cast(u32x4, vf[c]);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      x[w] = pack_bf2(__uint_as_float(x[w] << 16) * cj, __uint_as_float(x[w] & 0xffff0000u) * cj);
+    vf[c] = __builtin_bit_cast(bf16x8, x);
   }
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -807,7 +884,7 @@ __global__ void __launch_bounds__(256, 1)
           pr = ((q0 + m0 + e) >> P.bs_log2) == (my_key >> P.bs_log2) ? pr : 0.f;
         }
         pb[half][e] = (__bf16)pr;
-        dsb[half][e] = (_Float16)(pr * (dp_c[v] - dv_));
+        dsb[half][e] = (_Float16)(pr * __builtin_fmaf(dv_, -cj, dp_c[v]));  // 2^e dS
       }
     }
     s_c = s_n;
@@ -860,6 +937,7 @@ __global__ void __launch_bounds__(256, 1)
   uint16_t* dvrow = (uint16_t*)gr.dv[0] + off;
   const float* cp = cosT + (int64_t)kpos * 64;
   const float* sp = sinT + (int64_t)kpos * 64;
+  const float ksc = P.scale * __builtin_amdgcn_ldexpf(1.0f, -ek);  // sigma, and the dS factor undone
 #pragma unroll
   for (int d4 = 0; d4 < 2; ++d4)
 #pragma unroll
@@ -868,7 +946,7 @@ __global__ void __launch_bounds__(256, 1)
       float lo[4], hi[4], vlo[4], vhi[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x = dk[d4][v4 * 4 + e] * P.scale, y = dk[d4 + 2][v4 * 4 + e] * P.scale;
+        const float x = dk[d4][v4 * 4 + e] * ksc, y = dk[d4 + 2][v4 * 4 + e] * ksc;
         const float c = cp[d + e], s_ = sp[d + e];
         lo[e] = x * c + y * s_;
         hi[e] = y * c - x * s_;

@@ -59,7 +59,24 @@ struct Prob {
   // the dQ kernel also produces the branch dK/dV of passes 2..p (its work
   // item holds every query head of a KV group); no separate branch kernel
   int dq_branch;
+  // bf16 backward: bounds that set the power-of-two scale of the fp16 dS
+  // operands (see ds_exp).  All in the workspace, slot-indexed.
+  float* dnorm;  // [B*Hq][spad]: ||dO_i||_1 of the row in that slot (0 past a sequence's end)
+  float* dpart;  // [B*Hq][spad/64][2]: per 64-slot block, max ||dO_i||_1 and max |Delta_i|
+  float* dmax;   // [B*Hkv][2]: the same over every row of the KV group's heads
+  float* vmax;   // [B*Hkv][spad/32]: per 32 trunk (block drafting: context) keys, max |v_jd|
+  float* vmax_b; // block drafting: the same for the block keys
 };
+
+// Exponent e of the power-of-two factor 2^e applied to fp16 dS operands whose
+// magnitude is bounded by x: |dS 2^e| <= x 2^e < 2^15 < 65504 (fp16 max), and
+// >= 2^14 at the bound, so neither small nor large dO leaves fp16's range.
+// Clamped to [-64, 64] (operands stay finite in fp32 and bf16).  Pure
+// exponent arithmetic: scaling dO by 2^k shifts e by exactly -k.
+__device__ __forceinline__ int ds_exp(float x) {
+  const int e = 15 - __builtin_amdgcn_frexp_expf(x);
+  return e < -64 ? -64 : (e > 64 ? 64 : e);
+}
 
 __device__ __forceinline__ int block_anchor(const Prob& P, int b, int row) {
   const int a = P.anchors[(int64_t)b * P.nblk + (row >> P.bs_log2)];
@@ -233,7 +250,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 // Workspace layout shared by host launchers.
 struct WsPlan {
-  size_t table, slots, tiles_q, tiles_kv, kt, vt, ktt, qt, delta, total;
+  size_t table, slots, tiles_q, tiles_kv, kt, vt, ktt, qt, delta, bnd, total;
 };
 
 }  // namespace ttt

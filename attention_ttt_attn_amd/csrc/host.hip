@@ -31,6 +31,25 @@ int fail(int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// bf16 backward: the bounds behind the fp16 dS scale (Prob::dnorm .. vmax_b),
+// one workspace region; key_sets = 2 for block drafting (context and block keys).
+size_t bound_bytes(const ttt::Prob& P, int key_sets) {
+  return align256((size_t)P.B * P.Hq * P.spad * 4) + align256((size_t)P.B * P.Hq * (P.spad / 64) * 8) +
+         align256((size_t)P.B * P.Hkv * 8) + key_sets * align256((size_t)P.B * P.Hkv * (P.spad / 32) * 4);
+}
+void set_bounds(ttt::Prob& P, void* region, int key_sets) {
+  char* c = (char*)region;
+  P.dnorm = (float*)c;
+  c += align256((size_t)P.B * P.Hq * P.spad * 4);
+  P.dpart = (float*)c;
+  c += align256((size_t)P.B * P.Hq * (P.spad / 64) * 8);
+  P.dmax = (float*)c;
+  c += align256((size_t)P.B * P.Hkv * 8);
+  P.vmax = (float*)c;
+  c += align256((size_t)P.B * P.Hkv * (P.spad / 32) * 4);
+  P.vmax_b = key_sets > 1 ? (float*)c : nullptr;
+}
+
 // Largest token stride (elements) of a caller tensor: the kernels' tile loads
 // reach 32 rows past a base with 32-bit byte offsets.
 constexpr int64_t kMaxTokenStride = (int64_t)1 << 25;
@@ -210,6 +229,7 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
       w.ktt = take(nkv * 2);
       w.qt = take(nq * 2);
       w.delta = take((size_t)2 * B * Hq * P.spad * 4);  // Delta, then the LSE in log2 units
+      w.bnd = take(bound_bytes(P, 1));
     }
   } else {
     w.kt = take(nkv * 4);
@@ -550,6 +570,7 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
     bp.qt = take((size_t)P.B * P.Hq * P.spad * D * 2);
     // Delta, the LSE in log2 units, then the row lims
     bp.delta = take((size_t)2 * P.B * P.Hq * P.spad * 4 + (size_t)P.B * P.spad * 4);
+    pl.ws.bnd = take(bound_bytes(P, 2));
   }
   bp.total = off;
   pl.ws.total = off;
@@ -601,8 +622,10 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   _Float16* bktt = at<_Float16>(ws, bp.blk_vt);
   _Float16* qt = at<_Float16>(ws, bp.qt);
   float* delta = at<float>(ws, bp.delta);
+  set_bounds(P, at<char>(ws, pl.ws.bnd), 2);
   TTT_TRACED("rope_table", ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st));
   TTT_TRACED("bwd_delta", ttt::launch_delta(P, o, pl.o_f32, dout, false, lse, delta, st));
+  TTT_TRACED("bwd_dmax", ttt::launch_dmax(P, st));
   ttt::PrepJobs J;
   memset(&J, 0, sizeof J);
   J.n = 1;
@@ -874,8 +897,10 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
   Side sd;
   const bool forked = pl.bf16 && sd.begin(st);
   const hipStream_t sst = forked ? sd.side : st;
+  if (pl.bf16) set_bounds(P, at<char>(ws, pl.ws.bnd), 1);
   TTT_TRACED_ON("bwd_delta", sst,
                 ttt::launch_delta(P, o, pl.o_f32, dout, !pl.bf16, pl.bf16 ? lse : nullptr, delta, sst));
+  if (pl.bf16) TTT_TRACED_ON("bwd_dmax", sst, ttt::launch_dmax(P, sst));
   const hipEvent_t delta_done = forked ? sd.mark(sd.side) : nullptr;
   if (!pl.bf16) {
     float* kt = at<float>(ws, pl.ws.kt);

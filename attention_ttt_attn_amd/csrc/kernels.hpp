@@ -33,6 +33,8 @@ void launch_prep_bf16(const Prob& P, const PrepJobs& J, const float* cosT, const
 // rows' ends) in the workspace slot layout.
 void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, const float* lse,
                   float* delta, hipStream_t st);
+// bf16 backward: P.dmax[B*Hkv][2] from the Delta kernel's P.dpart entries
+void launch_dmax(const Prob& P, hipStream_t st);
 // THD: workspace slots (when slot_base is given) and the sequence-major tile
 // list (when out is given); desc: tiles descending within a sequence.
 void launch_tile_sched(const Prob& P, int tile, int desc, int4* out, int max_entries, int* slot_base,

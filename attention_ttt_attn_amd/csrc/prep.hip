@@ -205,8 +205,11 @@ __device__ __forceinline__ void load8(const float* p, float* x) {
 // Delta[(b*Hq + h)][slot] = <dO row, O row> in fp32 (0 in slots without a
 // token).  With lse given, also the rows' LSE in log2 units in the same slot
 // layout right after Delta (+inf in slots without a token, so every
-// probability recomputed for them is exactly 0).  Grid (spad/64, Hq, B), 256
-// threads, D/8 threads per row; each thread issues all its rows' loads first.
+// probability recomputed for them is exactly 0).  With P.dnorm / P.dpart set
+// (bf16 backward), also every row's ||dO||_1 and, per 64-slot block, the
+// largest ||dO||_1 and |Delta| (the bounds of the dS scale).  Grid (spad/64,
+// Hq, B), 256 threads, D/8 threads per row; each thread issues all its rows'
+// loads first.
 template <int D, typename OT, typename GT>
 __global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict__ o, const GT* __restrict__ dout,
                                                     const float* __restrict__ lse, float* __restrict__ delta) {
@@ -228,18 +231,59 @@ __global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict
     load8(dout + off, y[i]);
   }
   float* lse2 = delta + (int64_t)P.B * P.Hq * P.spad;
+  float nmax = 0.f, dmax = 0.f;  // this thread's rows: max ||dO||_1, max |Delta|
 #pragma unroll
   for (int i = 0; i < NR; ++i) {
-    float acc = 0.f;
+    float acc = 0.f, n1 = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += x[i][e] * y[i][e];
-    if (!valid[i]) acc = 0.f;
+    for (int e = 0; e < 8; ++e) acc += x[i][e] * y[i][e], n1 += fabsf(y[i][e]);
+    if (!valid[i]) acc = n1 = 0.f;
 #pragma unroll
-    for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64);
+    for (int m = 1; m < TPR; m <<= 1) acc += __shfl_xor(acc, m, 64), n1 += __shfl_xor(n1, m, 64);
     const int64_t so = (int64_t)(b * P.Hq + h) * P.spad + slot[i];
     if (c == 0) delta[so] = acc;
     if (lse && c == 1)
       lse2[so] = valid[i] ? lse[(int64_t)b * P.lse_b + (int64_t)h * P.lse_h + tok[i]] * kLog2e : INFINITY;
+    if (P.dnorm && c == 2) P.dnorm[so] = n1;
+    nmax = fmaxf(nmax, n1);
+    dmax = fmaxf(dmax, fabsf(acc));
+  }
+  if (P.dpart) {  // the block's 64 slots: one (max ||dO||_1, max |Delta|) entry
+    __shared__ float red[2][4];
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, m, 64)), dmax = fmaxf(dmax, __shfl_xor(dmax, m, 64));
+    if ((tid & 63) == 0) red[0][tid >> 6] = nmax, red[1][tid >> 6] = dmax;
+    __syncthreads();
+    if (tid == 0) {
+      const int64_t bo = ((int64_t)(b * P.Hq + h) * (P.spad / 64) + blockIdx.x) * 2;
+      P.dpart[bo] = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+      P.dpart[bo + 1] = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    }
+  }
+}
+
+// Per KV group: the largest ||dO_i||_1 and |Delta_i| over every slot of the
+// group's r query heads (the Delta kernel's 64-slot block entries), the bound
+// from which the dK/dV kernel sets its fp16 dS scale.  Grid B*Hkv, 256
+// threads.
+__global__ void __launch_bounds__(256) dmax_kernel(Prob P) {
+  __shared__ float red[2][4];
+  const int bg = blockIdx.x, tid = threadIdx.x;
+  const int nb = P.spad / 64;
+  const float2* src = (const float2*)P.dpart + (int64_t)bg * P.r * nb;  // heads g*r .. g*r+r-1 are contiguous
+  float n = 0.f, d = 0.f;
+  for (int i = tid; i < P.r * nb; i += 256) {
+    const float2 x = src[i];
+    n = fmaxf(n, x.x);
+    d = fmaxf(d, x.y);
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) n = fmaxf(n, __shfl_xor(n, m, 64)), d = fmaxf(d, __shfl_xor(d, m, 64));
+  if ((tid & 63) == 0) red[0][tid >> 6] = n, red[1][tid >> 6] = d;
+  __syncthreads();
+  if (tid == 0) {
+    P.dmax[2 * bg] = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+    P.dmax[2 * bg + 1] = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
   }
 }
 
@@ -384,6 +428,8 @@ void launch_prep_bf16(const Prob& P, const PrepJobs& J, const float* cosT, const
   dim3 grid((P.spad / 64) * (J.j[0].H + (J.n > 1 ? J.j[1].H : 0)), 1, P.B);
   prep_bf16_kernel<<<grid, 256, 0, st>>>(P, J, cosT, sinT);
 }
+
+void launch_dmax(const Prob& P, hipStream_t st) { dmax_kernel<<<P.B * P.Hkv, 256, 0, st>>>(P); }
 
 void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, const float* lse,
                   float* delta, hipStream_t st) {
