@@ -19,7 +19,7 @@ import os
 from typing import Optional, Sequence
 
 __all__ = ["fwd", "bwd", "workspace_bytes", "set_trace_hook", "TTTAttnError", "library", "library_path", "Desc",
-           "LAYOUT_BSHD", "LAYOUT_THD", "DTYPE_BF16", "DTYPE_FP32", "STATUS"]
+           "LAYOUT_BSHD", "LAYOUT_THD", "DTYPE_BF16", "DTYPE_FP32", "STATUS", "fwd_noalloc"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libtttattn.so")
@@ -136,6 +136,9 @@ def library() -> ctypes.CDLL:
         lib.ttt_attn_fwd.argtypes = [ctypes.POINTER(Desc), vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp,
                                      sz, vp]
         lib.ttt_attn_fwd.restype = ctypes.c_int
+        lib.ttt_attn_fwd_noalloc.argtypes = [ctypes.POINTER(Desc), vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp,
+                                             vp, vp]
+        lib.ttt_attn_fwd_noalloc.restype = ctypes.c_int
         lib.ttt_attn_bwd.argtypes = [ctypes.POINTER(Desc), vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp, vp,
                                      ctypes.POINTER(vp), ctypes.POINTER(vp), vp, sz, vp]
         lib.ttt_attn_bwd.restype = ctypes.c_int
@@ -285,6 +288,21 @@ def fwd(q, ks: Sequence, vs: Sequence, p: int, *, cu_seqlens=None, softmax_scale
     wp, wn = _ws_ptr(ws)
     _check(library().ttt_attn_fwd(ctypes.byref(d), q.data_ptr(), _ptrs(ks[:p]), _ptrs(vs[:p]), out.data_ptr(),
                                   lse.data_ptr(), wp, wn, _stream(stream)))
+    return out, lse
+
+
+def fwd_noalloc(q, ks: Sequence, vs: Sequence, p: int, out, lse, *, cu_seqlens=None, softmax_scale: float = 0.0,
+                rope_base: float = 0.0, stream=None, window: int = 0):
+    """Forward of TTT pass p through ttt_attn_fwd_noalloc: the library's static per-GPU scratch
+    replaces the workspace, and the caller passes the outputs (nothing is allocated here)."""
+    torch = _torch()
+    o_dtype = DTYPE_FP32 if out.dtype == torch.float32 else _dtype_code(out)
+    d = make_desc(q, ks, p, cu_seqlens=cu_seqlens, softmax_scale=softmax_scale, rope_base=rope_base,
+                  o_dtype=o_dtype, o_like=out, window=window)
+    if any(t.stride() != ks[0].stride() for t in list(ks[:p]) + list(vs[:p])):
+        raise ValueError("every k and v must share one set of strides")
+    _check(library().ttt_attn_fwd_noalloc(ctypes.byref(d), q.data_ptr(), _ptrs(ks[:p]), _ptrs(vs[:p]),
+                                          out.data_ptr(), lse.data_ptr(), _stream(stream)))
     return out, lse
 
 

@@ -473,6 +473,57 @@ int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
   return fwd_impl(d, nullptr, q, k, v, o, lse, ws, ws_bytes, stream);
 }
 
+}  // extern "C"
+
+namespace {
+// Workspace of the allocation-free forward: a static device array, one copy
+// per GPU, held until the process ends.  In host code `scratch` names a host
+// stand-in, not device memory: kernels get the device address that
+// hipGetSymbolAddress returns, looked up once per device (with that device
+// current) and kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[TTT_ATTN_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TTT_ERR_HIP, "device %d is past the %d tracked", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(TTT_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
+}  // namespace
+
+extern "C" {
+
+int ttt_attn_fwd_noalloc(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v,
+                         void* o, float* lse, void* stream) {
+  g_last_error.clear();
+  Plan pl;
+  if (int e = make_plan(d, 0, pl)) return e;
+  if (d->layout == TTT_LAYOUT_THD && d->check_cu_seqlens)
+    return fail(TTT_ERR_UNSUPPORTED, "check_cu_seqlens copies to the host and synchronises: not in the "
+                                     "allocation-free forward");
+  if (pl.ws.total > (size_t)TTT_ATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(TTT_ERR_WORKSPACE, "the call needs %zu bytes of workspace; the allocation-free forward's static "
+                                   "scratch holds %zu", pl.ws.total, (size_t)TTT_ATTN_NOALLOC_SCRATCH_BYTES);
+  if (pl.P.stok == 0) return TTT_OK;
+  void* ws = nullptr;
+  if (int e = scratch_address(&ws)) return e;
+  return fwd_impl(d, nullptr, q, k, v, o, lse, ws, TTT_ATTN_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 size_t ttt_attn_chunk_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_chunk* c) {
   g_last_error.clear();
   if (!c) {

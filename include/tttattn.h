@@ -124,6 +124,23 @@ size_t ttt_attn_workspace_bytes(const ttt_attn_desc* d, int for_bwd);
 int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v,
                  void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* Forward of pass p without a workspace argument and without allocating: for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Arguments and
+ * results as ttt_attn_fwd.  The workspace is a static device array of
+ * TTT_ATTN_NOALLOC_SCRATCH_BYTES per GPU, held from this entry point's first
+ * call on that GPU until the process ends; a call whose workspace need
+ * (ttt_attn_workspace_bytes(d, 0)) exceeds it returns TTT_ERR_WORKSPACE before
+ * any launch.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other threads) race and give undefined
+ * results; calls in order on one stream are fine.  The array keeps the last
+ * call's contents, and the forward writes every byte of it that it reads, so
+ * nothing is cleared between calls.  THD's check_cu_seqlens (a host copy and
+ * a synchronisation) is rejected with TTT_ERR_UNSUPPORTED. */
+#define TTT_ATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int ttt_attn_fwd_noalloc(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v,
+                         void* o, float* lse, void* stream);
+
 /* Backward of pass p, recomputing probabilities from the forward's LSE.
  *   o, lse       : the forward's outputs for the same inputs
  *   dout         : gradient of o (dtype, o_stride)

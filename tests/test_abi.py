@@ -447,3 +447,19 @@ def test_token_stride_limit():
     d = good_desc()
     d.kv_stride[0], d.kv_stride[1], d.kv_stride[2] = (1 << 25) * 64, 1 << 25, 128
     assert lib.ttt_attn_workspace_bytes(ctypes.byref(d), 0) > 0
+
+
+def test_noalloc_forward_refusals():
+    """The allocation-free forward refuses, before touching the GPU, a problem whose workspace
+    exceeds its static scratch, and THD's host-side cu_seqlens check (a synchronisation)."""
+    lib = tk.library()
+    d = good_desc()
+    d.batch, d.seqlen, d.num_q_heads, d.num_kv_heads = 4, 4096, 32, 8
+    assert tk.workspace_bytes(d, False) > (64 << 20)
+    rc = lib.ttt_attn_fwd_noalloc(ctypes.byref(d), FAKE, ptrs(3), ptrs(3), FAKE, FAKE, None)
+    assert rc == 5 and "static" in lib.ttt_attn_last_error().decode()
+    d2 = good_desc(layout=tk.LAYOUT_THD)
+    d2.check_cu_seqlens = 1
+    assert lib.ttt_attn_fwd_noalloc(ctypes.byref(d2), FAKE, ptrs(3), ptrs(3), FAKE, FAKE, None) == 3
+    bad = good_desc(p=0)
+    assert lib.ttt_attn_fwd_noalloc(ctypes.byref(bad), FAKE, ptrs(3), ptrs(3), FAKE, FAKE, None) == 2
