@@ -15,6 +15,7 @@ tensors [T, H, D].
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Sequence
 
@@ -244,6 +245,19 @@ def _ptrs(ts):
     return arr
 
 
+def _on_stream(fn):
+    """Runs a call with its `stream` argument current, so that the outputs and the workspace it
+    allocates belong to the stream its kernels run on: the caching allocator then hands the
+    workspace to other work only after that stream's kernels."""
+    @functools.wraps(fn)
+    def wrapped(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, stream=None, **kw)
+        with _torch().cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return wrapped
+
+
 def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -267,6 +281,7 @@ def _ws_ptr(ws):
     return ctypes.c_void_p(aligned), ws.numel() - (aligned - addr)
 
 
+@_on_stream
 def fwd(q, ks: Sequence, vs: Sequence, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0,
         rope_base: float = 0.0, o_fp32: bool = False, out=None, lse=None, workspace=None, stream=None,
         check_cu_seqlens: bool = False, window: int = 0):
@@ -291,6 +306,7 @@ def fwd(q, ks: Sequence, vs: Sequence, p: int, *, cu_seqlens=None, softmax_scale
     return out, lse
 
 
+@_on_stream
 def fwd_noalloc(q, ks: Sequence, vs: Sequence, p: int, out, lse, *, cu_seqlens=None, softmax_scale: float = 0.0,
                 rope_base: float = 0.0, stream=None, window: int = 0):
     """Forward of TTT pass p through ttt_attn_fwd_noalloc: the library's static per-GPU scratch
@@ -306,6 +322,7 @@ def fwd_noalloc(q, ks: Sequence, vs: Sequence, p: int, out, lse, *, cu_seqlens=N
     return out, lse
 
 
+@_on_stream
 def bwd(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0,
         rope_base: float = 0.0, dq=None, dks=None, dvs=None, workspace=None, stream=None,
         check_cu_seqlens: bool = False, window: int = 0):
@@ -347,6 +364,7 @@ def make_chunk(q_offset: int, kv_offset: int, k0, *, with_branch: bool) -> Chunk
     return c
 
 
+@_on_stream
 def fwd_chunk(q, ks: Sequence, vs: Sequence, p: int, *, q_offset: int, kv_offset: int, with_branch: bool,
               softmax_scale: float = 0.0, rope_base: float = 0.0, o_fp32: bool = True, out=None, lse=None,
               workspace=None, stream=None, window: int = 0):
@@ -378,6 +396,7 @@ def fwd_chunk(q, ks: Sequence, vs: Sequence, p: int, *, q_offset: int, kv_offset
     return out, lse
 
 
+@_on_stream
 def bwd_chunk(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, q_offset: int, kv_offset: int,
               with_branch: bool, softmax_scale: float = 0.0, rope_base: float = 0.0, window: int = 0,
               workspace=None, stream=None):
@@ -418,6 +437,7 @@ def bwd_chunk(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, q_offset: 
     return dq, dks, dvs
 
 
+@_on_stream
 def merge(o_a, lse_a, o_b, lse_b, *, out=None, lse=None, cu_seqlens=None, stream=None):
     """Joint-LSE merge of two partial results over disjoint key sets of the same rows.
     out/lse may be o_a/lse_a (in-place accumulation).  Returns (o, lse)."""
@@ -463,6 +483,7 @@ def make_block(block_size: int, k_ctx, anchors) -> Block:
     return bk
 
 
+@_on_stream
 def block_fwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, *, softmax_scale: float = 0.0,
               rope_base: float = 0.0, o_fp32: bool = False, out=None, lse=None, workspace=None, stream=None):
     """Block-draft forward (BSHD, bf16).  q [B, N, Hq, D] with N = nblk * block_size;
@@ -492,6 +513,7 @@ def block_fwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, *, softma
     return out, lse
 
 
+@_on_stream
 def block_bwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, o, lse, dout, *, softmax_scale: float = 0.0,
               rope_base: float = 0.0, dq=None, dk_ctx=None, dv_ctx=None, dk_blk=None, dv_blk=None, workspace=None,
               stream=None):
@@ -541,6 +563,7 @@ def make_soft_ce_desc(student, teacher, teacher_offset: int, mask=None) -> SoftC
     return d
 
 
+@_on_stream
 def soft_ce_fwd(student, teacher, teacher_offset: int, *, mask=None, row_ce=None, stream=None):
     """Per-pass soft cross-entropy.  student, teacher: bf16 [B, S, V]; mask: uint8 [B, S] or None.
     Returns (stats [2] = (loss, counted rows), row_lse [B, S, 2], row_ce [B, S])."""
@@ -556,6 +579,7 @@ def soft_ce_fwd(student, teacher, teacher_offset: int, *, mask=None, row_ce=None
     return stats, row_lse, row_ce
 
 
+@_on_stream
 def soft_ce_bwd(student, teacher, teacher_offset: int, row_lse, stats, dloss, *, mask=None, dstudent=None,
                 stream=None):
     """Gradient of the loss with respect to the student logits (bf16, student strides)."""

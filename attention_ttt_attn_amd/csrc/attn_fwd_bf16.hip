@@ -22,10 +22,11 @@
 //   and the O rescale needs no broadcast.  K~ rows for the A operand are read
 //   in a permuted order (bits 2 and 3 of the row index swapped) so that the
 //   score accumulator is already the B operand of O^T = V^T P^T
-//   (v_mfma_f32_32x32x16_bf16).
+//   (v_mfma_f32_32x32x16_f16: P <= 2^8 and V in fp16, so the row sum of the
+//   rounded P that normalises O is 8x finer than with bf16 P).
 // * Q~ = R(i+p-1) q is rotated in fp32 once and kept in VGPRs as fp16 (bf16
 //   inputs are exact in fp16 up to 65504; the rotated values round 8x finer
-//   than in bf16).  K~ = R(j) k^(1) (fp16) and V^(1)^T (bf16) come from the
+//   than in bf16).  K~ = R(j) k^(1) (fp16) and V^(1)^T (fp16) come from the
 //   prologue, so the hot loop is copies and MFMAs.
 // * K~ and V^T tiles of 64 keys move HBM -> LDS with buffer_load_dwordx4 ... lds
 //   (no VGPR staging), double-buffered, XOR-swizzled 16-byte chunks so that
@@ -58,7 +59,7 @@ constexpr int NBUF = 2;          // tiles in the LDS ring (loads run NBUF-1 tile
 constexpr int CH = BN / 8;         // 16-byte chunks per V^T d-row
 struct Tile {
   _Float16 k[BN * D];  // K~ tile: row r at r*D, 16-byte chunk c at slot c ^ (r & 15)
-  uint16_t v[D * BN];  // V^T tile: d-row at d*BN, chunk c at slot c ^ ((d >> 1) & (CH - 1))
+  _Float16 v[D * BN];  // V^T tile (fp16): d-row at d*BN, chunk c at slot c ^ ((d >> 1) & (CH - 1))
 };
 struct Smem {
   union {
@@ -84,9 +85,9 @@ __host__ __device__ constexpr int tile_rows(int heads_per_wg) { return 32 * 4 / 
 template <int RH, bool O_F32, int MODE>
 __global__ void __launch_bounds__(256, 2)
     fwd_bf16_kernel(Prob P, const uint16_t* __restrict__ q, PassPtrs kv, const _Float16* __restrict__ kt,
-                    const uint16_t* __restrict__ vt, const int4* __restrict__ tiles, const float* __restrict__ cosT,
+                    const _Float16* __restrict__ vt, const int4* __restrict__ tiles, const float* __restrict__ cosT,
                     const float* __restrict__ sinT, void* __restrict__ o, float* __restrict__ lse,
-                    const _Float16* __restrict__ kbt, const uint16_t* __restrict__ vbt) {
+                    const _Float16* __restrict__ kbt, const _Float16* __restrict__ vbt) {
   constexpr int RT = tile_rows(RH);  // rows per work item
   __shared__ __attribute__((aligned(16))) Smem sm;
   constexpr bool TTT_ = MODE == 0 || MODE == 4;  // TTT pass (4: with a sliding window)
@@ -182,7 +183,7 @@ __global__ void __launch_bounds__(256, 2)
   // sliding window: the first tile any row of the work item sees
   const int kt_lo = (TTT_ && win > 0) ? max(0, row0 + dq_ - win + 1) / BN : 0;
   const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
-  const uint16_t* vbase = vt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
+  const _Float16* vbase = vt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
   // DMA lane roles, loads n = w*KL + i.  K~: 1 KB = rows 4n + lane/16, slot
   // lane%16.  V^T: 1 KB = d-rows RPL*n + lane/CH, slot lane%CH.  Per-lane 32-bit
   // offsets, tile bases are wave-uniform.
@@ -204,7 +205,7 @@ __global__ void __launch_bounds__(256, 2)
   // a tile's K~ rows are BN*D contiguous halves; its V^T d-rows are BN keys
   // each, spad apart
   const uint32_t vt_bytes = (uint32_t)(((D - 1) * P.spad + BN) * 2);
-  auto dma_from = [&](Tile* __restrict__ dst, const _Float16* kb_t, const uint16_t* vb_t)
+  auto dma_from = [&](Tile* __restrict__ dst, const _Float16* kb_t, const _Float16* vb_t)
                       __attribute__((always_inline)) {
     const buf_rsrc kr = make_rsrc(kb_t, BN * D * 2), vr = make_rsrc(vb_t, vt_bytes);
     const int wu = __builtin_amdgcn_readfirstlane(wv);  // the LDS bases stay scalar
@@ -269,7 +270,7 @@ __global__ void __launch_bounds__(256, 2)
   auto tile = [&](const Tile* __restrict__ cur, const int key0, auto masked) __attribute__((always_inline)) {
     constexpr int KB = BN / 32;
     const _Float16* kl = cur->k;
-    const uint16_t* vl = cur->v;
+    const _Float16* vl = cur->v;
     f32x16 sacc[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -314,34 +315,37 @@ __global__ void __launch_bounds__(256, 2)
     mx = xhalf_max(mx) * sl2;
     raise_max(mx);
     const float neg_m = m_run == -INFINITY ? 0.f : -m_run;  // no key seen yet: every P is 0
-    bf16x8 pb[2 * KB];
+    // P in fp16 (<= 2^8 with the lazy max; 11 significant bits, so one
+    // dominant key's rounding moves the LSE by < 5e-4) for the PV product
+    f16x8 pb[2 * KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) pb[kb * 2 + (v >> 3)][v & 7] = (__bf16)fast_exp2(__builtin_fmaf(sacc[kb][v], sl2, neg_m));
-    // row sum of the bf16 probabilities the PV product uses, two per v_dot2
-    const b2 one = {(__bf16)1.f, (__bf16)1.f};
+      for (int v = 0; v < 16; ++v) pb[kb * 2 + (v >> 3)][v & 7] = (_Float16)fast_exp2(__builtin_fmaf(sacc[kb][v], sl2, neg_m));
+    // row sum of the fp16 probabilities the PV product uses, two per v_dot2:
+    // O's weights then sum to 1 exactly
+    const h2 one = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
     for (int c2 = 0; c2 < 2 * KB; ++c2)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const b2 pr = {pb[c2][e], pb[c2][e + 1]};
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one, l_run, false);
+        const h2 pr = {pb[c2][e], pb[c2][e + 1]};
+        l_run = __builtin_amdgcn_fdot2(pr, one, l_run, false);
       }
     apply_scale();
     {
-      bf16x8 a[2 * KB][4];
+      f16x8 a[2 * KB][4];
 #pragma unroll
       for (int c2 = 0; c2 < 2 * KB; ++c2)
 #pragma unroll
         for (int d4 = 0; d4 < 4; ++d4) {
           const int d = d4 * 32 + l32;
-          a[c2][d4] = *(const bf16x8*)&vl[d * BN + (((2 * c2 + hf) ^ ((d >> 1) & (CH - 1))) * 8)];
+          a[c2][d4] = *(const f16x8*)&vl[d * BN + (((2 * c2 + hf) ^ ((d >> 1) & (CH - 1))) * 8)];
         }
 #pragma unroll
       for (int c2 = 0; c2 < 2 * KB; ++c2)
 #pragma unroll
-        for (int d4 = 0; d4 < 4; ++d4) oacc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c2][d4], pb[c2], oacc[d4], 0, 0, 0);
+        for (int d4 = 0; d4 < 4; ++d4) oacc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c2][d4], pb[c2], oacc[d4], 0, 0, 0);
       // three operand reads ahead of the MFMAs, then one read per MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
@@ -373,7 +377,7 @@ __global__ void __launch_bounds__(256, 2)
   // 64-key tile at a time, masked to the row's block
   if constexpr (MODE == 1) {
     const _Float16* kbb = kbt + (int64_t)(b * P.Hkv + g) * P.spad_b * D;
-    const uint16_t* vbb = vbt + (int64_t)(b * P.Hkv + g) * D * P.spad_b;
+    const _Float16* vbb = vbt + (int64_t)(b * P.Hkv + g) * D * P.spad_b;
     for (int k0 = row0; k0 < qend; k0 += BN) {
       dma_from(&sm.ring[0], kbb + (int64_t)k0 * D, vbb + k0);
       TTT_WAIT_VMCNT(0);
@@ -522,9 +526,9 @@ __global__ void __launch_bounds__(256, 2)
 int heads_per_wg(int r) { return r % 4 == 0 ? 4 : (r % 2 == 0 ? 2 : 1); }
 
 template <int RH, int MODE>
-static void launch_rh(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const uint16_t* vt,
+static void launch_rh(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const _Float16* vt,
                       const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
-                      const _Float16* kbt, const uint16_t* vbt, hipStream_t st) {
+                      const _Float16* kbt, const _Float16* vbt, hipStream_t st) {
   constexpr int RT = tile_rows(RH);
   int ntiles;
   if (P.layout == 0) ntiles = P.B * ((P.stok + RT - 1) / RT);
@@ -540,8 +544,8 @@ static void launch_rh(const Prob& P, const uint16_t* q, const PassPtrs& kv, cons
 
 template <int MODE>
 static void launch_mode(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt,
-                        const uint16_t* vt, const int4* tiles, const float* cosT, const float* sinT, void* o,
-                        bool o_f32, float* lse, const _Float16* kbt, const uint16_t* vbt, hipStream_t st) {
+                        const _Float16* vt, const int4* tiles, const float* cosT, const float* sinT, void* o,
+                        bool o_f32, float* lse, const _Float16* kbt, const _Float16* vbt, hipStream_t st) {
   switch (heads_per_wg(P.r)) {
     case 4: launch_rh<4, MODE>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, kbt, vbt, st); break;
     case 2: launch_rh<2, MODE>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, kbt, vbt, st); break;
@@ -553,7 +557,7 @@ static void launch_mode(const Prob& P, const uint16_t* q, const PassPtrs& kv, co
 
 int fwd_tile_rows(int r) { return fwd::tile_rows(fwd::heads_per_wg(r)); }
 
-void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const uint16_t* vt,
+void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const _Float16* vt,
                      const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
                      hipStream_t st) {
   if (P.win > 0)
@@ -562,8 +566,8 @@ void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const
     fwd::launch_mode<0>(P, q, kv, kt, vt, tiles, cosT, sinT, o, o_f32, lse, nullptr, nullptr, st);
 }
 
-void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const uint16_t* vt,
-                           const _Float16* kbt, const uint16_t* vbt, const float* cosT, const float* sinT, void* o,
+void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const _Float16* vt,
+                           const _Float16* kbt, const _Float16* vbt, const float* cosT, const float* sinT, void* o,
                            bool o_f32, float* lse, hipStream_t st) {
   const PassPtrs none = {};
   fwd::launch_mode<1>(P, q, none, kt, vt, nullptr, cosT, sinT, o, o_f32, lse, kbt, vbt, st);

@@ -65,6 +65,20 @@ struct Plan {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// The kernels address workspace slabs through buffer descriptors with 32-bit
+// byte offsets: a transposed slab spans (D-1) * spad + one tile of 2-byte
+// elements, and the log2 LSE staged after Delta starts B * Hq * spad floats
+// past it.  Larger problems would wrap (and read zeros past the range).
+int check_slab_offsets(const ttt::Prob& P) {
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)(P.D - 1) * P.spad * 2 + 1024 >= lim || (int64_t)P.B * P.Hq * P.spad * 4 >= lim)
+    return fail(TTT_ERR_BAD_SHAPE,
+                "%d workspace slots per head with %d batches x %d query heads: past the kernels' 32-bit workspace "
+                "offsets (2 (D-1) slots and 4 B Hq slots must stay below 2^31)",
+                P.spad, P.B, P.Hq);
+  return 0;
+}
+
 // Validates the descriptor (and the ring-step chunk, if any) and fills the
 // kernel view and workspace plan.
 int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chunk* c = nullptr) {
@@ -148,6 +162,7 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
     const int64_t qend = c->q_offset + stok + p - 1, kend = c->kv_offset + c->kv_len;
     P.npos = (int)(qend > kend ? qend : kend);
   }
+  if (int e = check_slab_offsets(P)) return e;
   if (d->window < 0) return fail(TTT_ERR_BAD_SHAPE, "window %d is negative", d->window);
   if (d->window > 0 && !bf16) return fail(TTT_ERR_UNSUPPORTED, "a sliding window is built for bf16 only");
   P.win = d->window;
@@ -448,7 +463,7 @@ int fwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
       tiles = t;
     }
     _Float16* kt = at<_Float16>(ws, pl.ws.kt);
-    uint16_t* vt = at<uint16_t>(ws, pl.ws.vt);
+    _Float16* vt = at<_Float16>(ws, pl.ws.vt);
     // the pass-1 keys: kv_len rows (= the sequence for whole-sequence calls) at positions kv_off + j;
     // rotated K~ rows and V^T in one launch
     ttt::Prob Pk = P;
@@ -457,7 +472,8 @@ int fwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     memset(&J, 0, sizeof J);
     J.n = 2;
     J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, nullptr, 0, nullptr, 0};
-    J.j[1] = {(const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, 0, 0, 1, nullptr, vt, 0, nullptr, 0};
+    J.j[1] = {(const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, 0, 0, 0, nullptr, (uint16_t*)vt, 0,
+              nullptr, 0};  // V^T in fp16: the PV product's operand
     TTT_TRACED("prep_kv", ttt::launch_prep_bf16(Pk, J, cosT, sinT, st));
     TTT_TRACED("trunk_fwd",
                ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st));
@@ -587,6 +603,7 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
   const int rows_max = ctx > P.stok ? ctx : P.stok;
   P.spad = ((rows_max + 63) / 64) * 64 + 64;
   P.spad_b = P.spad;
+  if (int e = check_slab_offsets(P)) return e;
   const int64_t* s0 = bk->ctx_stride;
   const int D = P.D, Hkv = P.Hkv;
   if (s0[0] == 0 && s0[1] == 0 && s0[2] == 0) {
@@ -736,9 +753,9 @@ int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   float* cosT = at<float>(ws, pl.ws.table);
   float* sinT = cosT + (size_t)P.npos * (P.D / 2);
   _Float16* ckt = at<_Float16>(ws, bp.ctx_kt);
-  uint16_t* cvt = at<uint16_t>(ws, bp.ctx_vt);
+  _Float16* cvt = at<_Float16>(ws, bp.ctx_vt);
   _Float16* bkt = at<_Float16>(ws, bp.blk_kt);
-  uint16_t* bvt = at<uint16_t>(ws, bp.blk_vt);
+  _Float16* bvt = at<_Float16>(ws, bp.blk_vt);
   TTT_TRACED("rope_table", ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st));
   // context: K~ rows at positions j and V^T (kv_len rows)
   ttt::Prob Pc = P;
@@ -747,13 +764,13 @@ int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   memset(&J, 0, sizeof J);
   J.n = 2;
   J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, nullptr, 0, nullptr, 0};
-  J.j[1] = {(const uint16_t*)v_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 0, 1, nullptr, cvt, 0, nullptr, 0};
+  J.j[1] = {(const uint16_t*)v_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 0, 0, nullptr, (uint16_t*)cvt, 0, nullptr, 0};
   TTT_TRACED("prep_ctx", ttt::launch_prep_bf16(Pc, J, cosT, sinT, st));
   // block keys: K~ rows at their slot positions and V^T (spad_b slots)
   ttt::Prob Pb = P;
   Pb.spad = P.spad_b;
   J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, nullptr, 1, nullptr, 0};
-  J.j[1] = {(const uint16_t*)v_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 0, 1, nullptr, bvt, 0, nullptr, 0};
+  J.j[1] = {(const uint16_t*)v_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 0, 0, nullptr, (uint16_t*)bvt, 0, nullptr, 0};
   TTT_TRACED("prep_blk", ttt::launch_prep_bf16(Pb, J, cosT, sinT, st));
   TTT_TRACED("block_fwd", ttt::launch_block_fwd_bf16(P, (const uint16_t*)q, ckt, cvt, bkt, bvt, cosT, sinT, o,
                                                      pl.o_f32, lse, st));

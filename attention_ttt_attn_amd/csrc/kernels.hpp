@@ -75,8 +75,8 @@ void launch_soft_ce_fwd(const CeProb& C, const uint16_t* s, const uint16_t* t, f
                         float* stats, hipStream_t st);
 void launch_soft_ce_bwd(const CeProb& C, const uint16_t* s, const uint16_t* t, const float* row_lse,
                         const float* stats, const float* dloss, uint16_t* g, hipStream_t st);
-void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const uint16_t* vt,
-                           const _Float16* kbt, const uint16_t* vbt, const float* cosT, const float* sinT, void* o,
+void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const _Float16* vt,
+                           const _Float16* kbt, const _Float16* vbt, const float* cosT, const float* sinT, void* o,
                            bool o_f32, float* lse, hipStream_t st);     // query rows per forward work item for GQA ratio r (32, 64 or 128)
 constexpr int kFwdMinRows = 32;
 int dq_tile_rows(int r);
@@ -84,7 +84,7 @@ int dq_tile_rows(int r);
 // that it can also produce the branch dK/dV (Prob::dq_branch)
 bool dq_fuses_branch(int r);      // query rows per dQ work item for GQA ratio r (32, 64 or 128)
 constexpr int kBwdBKV = 128;  // key rows per dK/dV workgroup
-void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const uint16_t* vt,
+void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const _Float16* vt,
                      const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
                      hipStream_t st);
 void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const uint16_t* dout, const _Float16* kt,

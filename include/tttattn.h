@@ -65,12 +65,24 @@ extern "C" {
 #define TTT_ATTN_ABI_VERSION 2
 
 enum ttt_attn_layout { TTT_LAYOUT_BSHD = 0, TTT_LAYOUT_THD = 1 };
+/* BF16: the score products run on fp16 operands.  q and k are rotated in fp32
+ * and rounded once to fp16, which keeps more of the rotated values' mantissa
+ * than bf16 does (an LSE error of ~4e-4 at worst instead of ~2e-3), so the
+ * rotated values must stay inside fp16's range: |R q|, |R k| < 65504 per
+ * element (|q|, |k| < 46000 suffices), else scores become inf or NaN.  The
+ * forward's P V product runs on fp16 too (P <= 256, 11-bit rounding), so
+ * |v| < 65504 as well.  The backward's fp16 dS operands are scaled by powers
+ * of two set from a bound on |dS|, so dO has no such limit.  FP32 runs in
+ * fp32 throughout. */
 enum ttt_attn_dtype { TTT_DTYPE_BF16 = 0, TTT_DTYPE_FP32 = 1 };
 
 enum ttt_attn_status {
   TTT_OK = 0,
   TTT_ERR_NULL_ARG = 1,       /* a required pointer is NULL                         */
-  TTT_ERR_BAD_SHAPE = 2,      /* sizes or strides inconsistent or out of range      */
+  TTT_ERR_BAD_SHAPE = 2,      /* sizes or strides inconsistent or out of range (also
+                                 problems past the kernels' 32-bit workspace offsets:
+                                 2 (D-1) slots < 2^31 and 4 B Hq slots < 2^31, slots
+                                 ~ tokens per batch rounded up to 64)               */
   TTT_ERR_UNSUPPORTED = 3,    /* head_dim / dtype combination not built             */
   TTT_ERR_MISALIGNED = 4,     /* base pointer or stride not 16-byte aligned         */
   TTT_ERR_WORKSPACE = 5,      /* workspace NULL, too small or not 256-byte aligned  */

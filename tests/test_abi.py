@@ -463,3 +463,20 @@ def test_noalloc_forward_refusals():
     assert lib.ttt_attn_fwd_noalloc(ctypes.byref(d2), FAKE, ptrs(3), ptrs(3), FAKE, FAKE, None) == 3
     bad = good_desc(p=0)
     assert lib.ttt_attn_fwd_noalloc(ctypes.byref(bad), FAKE, ptrs(3), ptrs(3), FAKE, FAKE, None) == 2
+
+
+def test_slab_offset_limit():
+    """Problems whose workspace slabs would overflow the kernels' 32-bit offsets are refused;
+    the largest accepted ones still plan a workspace."""
+    lib = tk.library()
+    d = good_desc()
+    d.batch, d.num_q_heads, d.num_kv_heads = 1, 8, 8
+    d.seqlen = 8_000_000                         # 2 * 127 * slots just below 2^31
+    assert tk.workspace_bytes(d, True) > 0
+    d.seqlen = 8_500_000                         # 2 * 127 * slots past 2^31
+    assert lib.ttt_attn_workspace_bytes(ctypes.byref(d), 1) == 0
+    assert "32-bit" in lib.ttt_attn_last_error().decode()
+    rc = lib.ttt_attn_fwd(ctypes.byref(d), FAKE, ptrs(3), ptrs(3), FAKE, FAKE, FAKE, 1 << 40, None)
+    assert rc == 2
+    d.batch, d.num_q_heads, d.seqlen = 2, 64, 4_500_000   # 4 B Hq slots past 2^31
+    assert lib.ttt_attn_workspace_bytes(ctypes.byref(d), 1) == 0

@@ -157,3 +157,25 @@ def test_fp32_head_dims(dev, tk):
         assert max_abs(to_np(o), o_ref) <= 1e-5 and max_abs(to_np(lse), l_ref) <= 1e-5
         assert rel_fro(to_np(dq), g_ref[0]) <= 1e-5
         assert max(rel_fro(to_np(dks[t]), g_ref[1][t]) for t in range(2)) <= 1e-5
+
+
+def test_stream_argument_not_current(dev, tk):
+    """Launch on a stream that is not torch's current one, without making it current: the
+    binding allocates outputs and workspace on that stream, so blocks the current stream
+    allocates meanwhile cannot be handed the workspace while the kernels still use it."""
+    w = syn.Workload("side_stream", 36, "bshd", 2, 400, 8, 2, 128, 3, "bf16", 1e6, True)
+    inp = Inputs(w, dev)
+    p = 3
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, o_fp32=True, rope_base=w.rope_base, stream=st)
+    dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, rope_base=w.rope_base, stream=st)
+    junk = [torch.full((1 << 22,), float("nan"), device=dev) for _ in range(16)]  # current-stream churn
+    st.synchronize()
+    del junk
+    o_ref, l_ref = O.fwd(inp.q[p], inp.k, inp.v, p, layout="bshd", base=w.rope_base)
+    g_ref = O.bwd(inp.q[p], inp.k, inp.v, inp.do[p], p, layout="bshd", base=w.rope_base)
+    assert max_abs(to_np(o), o_ref) <= 1e-2 and max_abs(to_np(lse), l_ref) <= 2e-3
+    assert rel_fro(to_np(dq), g_ref[0]) <= 1e-2
+    assert max(rel_fro(to_np(dks[t]), g_ref[1][t]) for t in range(p)) <= 1e-2
+    assert max(rel_fro(to_np(dvs[t]), g_ref[2][t]) for t in range(p)) <= 1e-2

@@ -6,7 +6,7 @@ import pytest
 
 import ttt_synth as syn
 from oracle import ttt_oracle as O
-from ttt_cases import TOL, Inputs, bf16_half_ulp, lse_at, max_abs, row_at, sample_rows, to_np
+from ttt_cases import TOL, Inputs, bf16_half_ulp, lse_at, max_abs, rel_fro, row_at, sample_rows, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -110,3 +110,32 @@ def sampled_fwd_check(tk, inp, n_rows, seed, o_fp32=True):
 def test_fwd_s2k_sampled(dev, tk):
     inp = Inputs(syn.workload("fwd_s2k"), dev, with_grad=False)
     sampled_fwd_check(tk, inp, 4096, 0)
+
+
+@pytest.mark.parametrize("qscale", [8.0, 24.0])
+def test_bf16_wide_score_range(dev, tk, qscale):
+    """Scores spanning about +-50 (q x 8) and +-150 (q x 24): the running max moves by more
+    than its lazy threshold (8 in log2 units) many times per row, and the branch keys can
+    dominate or vanish.  RoPE is off, so the fp16 score operands are the bf16 inputs
+    exactly and the comparison isolates the online softmax; forward and backward."""
+    w = syn.Workload(f"wide_{int(qscale)}", 16, "bshd", 2, 300, 8, 2, 128, 3, "bf16", 0.0, True)
+    inp = Inputs(w, dev)
+    for p in (1, 3):
+        inp.q[p] = syn.round_bf16(inp.q[p] * np.float32(qscale))
+        inp.gq[p] = torch.from_numpy(inp.q[p]).to(dev).to(torch.bfloat16)
+        o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, o_fp32=True)
+        torch.cuda.synchronize()
+        o_ref, l_ref = O.fwd(inp.q[p], inp.k, inp.v, p, layout="bshd", base=0.0)
+        eo, el = max_abs(to_np(o), o_ref), max_abs(to_np(lse), l_ref)
+        # the backward takes the fp32 O: with one dominant key dP - Delta cancels, and a bf16 O
+        # would put its 2^-9 rounding into Delta = <dO, O> (the oracle's Delta uses its exact O)
+        dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p)
+        torch.cuda.synchronize()
+        dq_r, dk_r, dv_r = O.bwd(inp.q[p], inp.k, inp.v, inp.do[p], p, layout="bshd", base=0.0)
+        eg = max([rel_fro(to_np(dq), dq_r)] + [rel_fro(to_np(dks[t]), dk_r[t]) for t in range(p)] +
+                 [rel_fro(to_np(dvs[t]), dv_r[t]) for t in range(p)])
+        lse_range = float(l_ref.max() - l_ref.min())
+        print(f"q x {qscale} p={p}: LSE spans {lse_range:.1f}; O max-abs {eo:.2e} LSE max-abs {el:.2e} "
+              f"grads {eg:.2e}")
+        assert lse_range > 40.0
+        assert eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"] and eg <= TOL["bf16"]["grad"]
