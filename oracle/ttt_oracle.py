@@ -90,7 +90,8 @@ from typing import Iterable, Optional, Sequence
 import numpy as np
 
 __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_position",
-           "ttt_mask_row", "trunk_window_start", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows", "Slice",
+           "ttt_mask_row", "trunk_window_start", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows",
+           "bwd_trunk_keys", "Slice",
            "fwd_chunk", "bwd_chunk", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd",
            "block_bwd_rows", "block_bwd", "soft_ce_rows_counted", "soft_ce"]
 
@@ -334,6 +335,43 @@ def bwd_rows(q, ks, vs, dout, p: int, sl: Slice, g: int, rows, *, layout: str, H
     idx = np.flatnonzero(touched)
     dk[idx] = unrotate_half(dk_rot[idx], gk.pos[idx], base)
     return dq, dk, dv
+
+
+def bwd_trunk_keys(q, ks, vs, dout, p: int, sl: Slice, g: int, keys, *, layout: str, Hq: int, Hkv: int,
+                   scale: float, base: float, window: int = 0):
+    """Exact dK, dV ([n, D] each) of the pass-1 (trunk) keys `keys` of KV group g in
+    sequence `sl`: the same chain rule as `bwd_rows`, summed over every row that sees
+    one of those keys (rows i >= min(keys), and i < max(keys) + window with a
+    window), each row's probabilities, O and Delta taken over its full visible key
+    set.  Only the products that reach the requested keys are formed, so a slice of
+    a long sequence costs about one forward over its rows."""
+    keys = np.asarray(keys, dtype=np.int64)
+    r = Hq // Hkv
+    gk = _GroupKeys(sl, g, ks, vs, p, layout, base)
+    D = gk.keys.shape[-1]
+    lo = int(keys.min())
+    hi = sl.L if window <= 0 else min(sl.L, int(keys.max()) + window)
+    rows = np.arange(lo, hi)
+    dk_rot = np.zeros((len(keys), D))
+    dv = np.zeros((len(keys), D))
+    for hh in range(r):
+        h = g * r + hh
+        qs = sl.take(q, layout, h)
+        dos = sl.take(dout, layout, h)
+        for blk in _blocks(rows, _block_rows(sl.L, p)):
+            qr = rotate_half(qs[blk], query_position(blk, p), base)
+            P, lse, O, cols = _row_block_fwd(gk, qr, blk, p, sl.L, scale, window)
+            do = dos[blk]
+            delta = (do * O).sum(axis=1)
+            at = np.searchsorted(cols, keys)                 # the requested keys among the block's columns
+            ok = (at < len(cols)) & (cols[np.minimum(at, len(cols) - 1)] == keys)
+            Pk = np.zeros((len(blk), len(keys)))
+            Pk[:, ok] = P[:, at[ok]]
+            dS = Pk * (do @ gk.vals[keys].T - delta[:, None])
+            dk_rot += scale * (dS.T @ qr)
+            dv += Pk.T @ do
+    dk = unrotate_half(dk_rot, gk.pos[keys], base)
+    return dk, dv
 
 
 def bwd(q, ks, vs, dout, p: int, *, layout: str = "bshd", cu_seqlens=None,

@@ -636,6 +636,24 @@ def check_chunk_bwd_partition():
             assert np.max(np.abs(gk[t] - dK[t])) < 1e-12 and np.max(np.abs(gv[t] - dV[t])) < 1e-12
 
 
+def check_trunk_keys_grad_autograd():
+    """dK/dV of a range of trunk keys, from every row that sees them with full-row
+    statistics (the form the full-size GPU tests use) == fp64 autograd through SDPA over
+    the concatenated keys, for a whole trunk, an inner key range and a windowed range."""
+    S, Hq, Hkv, D, p, base = 14, 4, 2, 8, 3, 1e4
+    q, ks, vs, do = make(S=S, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=97)
+    scale = 1 / math.sqrt(D)
+    sl = O.Slice(0, 0, S)
+    for window, keys in ((0, np.arange(S)), (0, np.arange(3, 9)), (4, np.arange(2, 11))):
+        ro, _, T = _window_dense(q, ks, vs, p, scale, base, window if window else S, grad=True)
+        (ro * torch.tensor(do)).sum().backward()
+        for g in range(Hkv):
+            dk, dv = O.bwd_trunk_keys(q, ks, vs, do, p, sl, g, keys, layout="thd", Hq=Hq, Hkv=Hkv, scale=scale,
+                                      base=base, window=window)
+            assert np.max(np.abs(dk - T[1].grad.numpy()[keys, g])) < 1e-10
+            assert np.max(np.abs(dv - T[1 + p].grad.numpy()[keys, g])) < 1e-10
+
+
 PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check_zero_query_closed_form,
         lambda: check_zero_query_closed_form("thd"), check_sdpa_brute_force, check_p1_is_causal_sdpa,
         check_merge_invariant, check_branch_relative_position, check_grad_autograd,
@@ -643,7 +661,8 @@ PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check
         check_sampled_rows_match_full, check_chunk_rows_match_dense, check_chunk_ring_partition,
         check_merge_closed_form, check_block_sdpa_mask, check_block_zero_query_closed_form,
         check_block_size1_is_causal, check_block_grad_autograd, check_soft_ce_library, check_soft_ce_closed_forms,
-        check_window_sdpa_and_grad, check_window_closed_forms, check_window_ring_partition, check_chunk_bwd_partition]
+        check_window_sdpa_and_grad, check_window_closed_forms, check_window_ring_partition, check_chunk_bwd_partition,
+        check_trunk_keys_grad_autograd]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
@@ -713,6 +732,28 @@ def _blk_transposed_v(gk, q_rot, rows, p, L, scale, window=0):
     return P, lse, P @ gk.vals[cols][:, ::-1], cols
 
 
+def _trunk_keys_late_rows(q, ks, vs, dout, p, sl, g, keys, *, layout, Hq, Hkv, scale, base, window=0):
+    """bwd_trunk_keys with its row range starting one row late (i > min(keys))."""
+    keys = np.asarray(keys, dtype=np.int64)
+    r = Hq // Hkv
+    gk = O._GroupKeys(sl, g, ks, vs, p, layout, base)
+    lo = int(keys.min()) + 1
+    hi = sl.L if window <= 0 else min(sl.L, int(keys.max()) + window)
+    dk = np.zeros((len(keys), gk.keys.shape[-1]))
+    dv = np.zeros_like(dk)
+    for hh in range(r):
+        qs, dos = sl.take(q, layout, g * r + hh), sl.take(dout, layout, g * r + hh)
+        for blk in O._blocks(np.arange(lo, hi), O._block_rows(sl.L, p)):
+            qr = O.rotate_half(qs[blk], O.query_position(blk, p), base)
+            P, _, O_, cols = O._row_block_fwd(gk, qr, blk, p, sl.L, scale, window)
+            delta = (dos[blk] * O_).sum(axis=1)
+            Pk = P[:, np.searchsorted(cols, keys)] * (keys[None, :] <= blk[:, None])
+            dS = Pk * (dos[blk] @ gk.vals[keys].T - delta[:, None])
+            dk += scale * (dS.T @ qr)
+            dv += Pk.T @ dos[blk]
+    return O.unrotate_half(dk, gk.pos[keys], base), dv
+
+
 MISTAKES = [
     ("ttt_mask_row", _mask_no_branch),
     ("ttt_mask_row", _mask_strict_causal),
@@ -737,6 +778,7 @@ MISTAKES = [
     ("ring_visible", lambda qp, kp, w=0: np.asarray(kp)[None, :] <= np.asarray(qp)[:, None]),
     ("soft_ce_rows_counted", lambda B, S, off, mask=None: np.ones((B, S), dtype=bool) & (np.arange(S)[None, :] + off < S)),
     ("merge", lambda oa, la, ob, lb: (_orig_merge(oa, la, ob, lb)[0], np.maximum(la, lb))),
+    ("bwd_trunk_keys", _trunk_keys_late_rows),
 ]
 
 

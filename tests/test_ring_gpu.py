@@ -307,3 +307,20 @@ def test_ring_bwd_fullsize_b4_s4k(dev, tk):
            [rel_fro(to_np(gv[t]), to_np(sv[t])) for t in range(p)]
     print(f"b4_s4k ring bwd vs single call: worst rel Frobenius {max(errs):.2e}")
     assert max(errs) <= TOL["bf16"]["grad"]
+    # and against the oracle: the ring-summed trunk dK/dV of one whole (batch, KV head)
+    # slice (4096 keys, every row that sees them), and 512 sampled dQ rows of its heads
+    b, g = 1, 3
+    sl = O.Slice(b, 0, w.S)
+    keys = np.arange(w.S)
+    dk_ref, dv_ref = O.bwd_trunk_keys(inp.q[p], inp.k, inp.v, inp.do[p], p, sl, g, keys, layout="bshd", Hq=w.Hq,
+                                      Hkv=w.Hkv, scale=w.scale, base=w.rope_base)
+    rows = np.sort(np.random.default_rng(27).choice(w.S, 512, replace=False))
+    dq_ref, _, _ = O.bwd_rows(inp.q[p], inp.k, inp.v, inp.do[p], p, sl, g, rows, layout="bshd", Hq=w.Hq, Hkv=w.Hkv,
+                              scale=w.scale, base=w.rope_base, need_kv=False)
+    r = w.Hq // w.Hkv
+    e_k = rel_fro(to_np(gk[0][b, :, g]), dk_ref)
+    e_v = rel_fro(to_np(gv[0][b, :, g]), dv_ref)
+    gq_b = to_np(gq[b])
+    e_q = rel_fro(np.stack([gq_b[rows, g * r + hh] for hh in range(r)]), dq_ref)
+    print(f"b4_s4k ring bwd vs oracle: trunk dK {e_k:.2e} dV {e_v:.2e} over {w.S} keys, dQ {e_q:.2e} over {len(rows)} rows x {r} heads")
+    assert max(e_k, e_v, e_q) <= TOL["bf16"]["grad"]
