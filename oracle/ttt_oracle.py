@@ -62,7 +62,12 @@ What is computed (one call = one TTT pass p, 1-based):
   with mask 0 are not counted; loss = (sum of counted rows' cross-entropies) /
   (number of counted rows).  The gradient is (softmax(student) - teacher
   distribution) / count on counted rows and 0 elsewhere.  Chunking the tokens
-  only bounds memory and does not change the value.
+  only bounds memory and does not change the value.  The same issue item names
+  per-slot normalisation for block drafting: `soft_ce_grouped` takes a table of
+  teacher rows per student row (a block slot at position a + t is scored
+  against teacher row a + t + 1, the rule above: query position + 1) and a
+  normalisation group per row (the slot index); each group's loss is the mean
+  over its own counted rows, and the loss is their (optionally weighted) sum.
 
 * Sliding-window trunk (issue above, item 4: sliding-window layers).  Reading:
   with window W > 0, row i's trunk is the pass-1 keys j with i - W < j <= i
@@ -93,7 +98,7 @@ __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_po
            "ttt_mask_row", "trunk_window_start", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows",
            "bwd_trunk_keys", "Slice",
            "fwd_chunk", "bwd_chunk", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd",
-           "block_bwd_rows", "block_bwd", "soft_ce_rows_counted", "soft_ce"]
+           "block_bwd_rows", "block_bwd", "soft_ce_rows_counted", "soft_ce_teacher_rows", "soft_ce", "soft_ce_grouped"]
 
 
 # ----------------------------------------------------------------------------- RoPE
@@ -663,23 +668,48 @@ def block_bwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, dout, *, scale: O
 
 
 # ----------------------------------------------------------------------------- distillation loss
-def soft_ce_rows_counted(B: int, S: int, offset: int, mask=None) -> np.ndarray:
-    """bool [B, S]: row i is counted iff row i + offset exists in its sequence and mask[b, i] != 0."""
-    i = np.arange(S)[None, :].repeat(B, axis=0)
-    ok = i + offset < S
+def soft_ce_teacher_rows(B: int, S: int, offset: int, teacher_rows=None) -> np.ndarray:
+    """int [B, S]: the teacher row each student row is scored against: the given table, or
+    row i + offset of the same sequence."""
+    if teacher_rows is not None:
+        return np.asarray(teacher_rows, dtype=np.int64).reshape(B, S)
+    return np.arange(S)[None, :].repeat(B, axis=0) + offset
+
+
+def soft_ce_rows_counted(B: int, S: int, offset: int, mask=None, *, teacher_rows=None, teacher_len=None,
+                         groups=None, num_groups: int = 1) -> np.ndarray:
+    """bool [B, S]: row i is counted iff its teacher row exists (0 <= row < teacher_len,
+    default S), mask[b, i] != 0 and its group is one of 0..num_groups-1."""
+    tr = soft_ce_teacher_rows(B, S, offset, teacher_rows)
+    ok = (tr >= 0) & (tr < (S if teacher_len is None else teacher_len))
     if mask is not None:
         ok = ok & (np.asarray(mask) != 0)
+    if groups is not None:
+        g = np.asarray(groups).reshape(B, S)
+        ok = ok & (g >= 0) & (g < num_groups)
     return ok
 
 
-def soft_ce(student, teacher, offset: int, mask=None):
-    """Per-pass soft cross-entropy.  student, teacher: [B, S, V] logits.  Returns
-    (loss, grad [B, S, V], row_ce [B, S]) in fp64 (row_ce is 0 on rows not counted)."""
+def soft_ce_grouped(student, teacher, offset: int, mask=None, *, teacher_rows=None, groups=None,
+                    num_groups: int = 1, weights=None):
+    """Soft cross-entropy with per-row teacher rows and per-group normalisation.
+
+    student [B, S, V], teacher [B, St, V] logits.  Row (b, i) is scored against
+    softmax(teacher[b, teacher row]) (teacher row i + offset unless a table is given);
+    counted rows per soft_ce_rows_counted.  Group g's loss is the mean of its counted
+    rows' cross-entropies (0 when it has none); loss = sum_g w_g mean_g (w_g = 1 unless
+    weights are given).  Returns (loss, grad [B, S, V] of that loss, row_ce [B, S],
+    means [G], counts [G]) in fp64."""
     s = np.asarray(student, np.float64)
     t = np.asarray(teacher, np.float64)
     B, S, V = s.shape
-    counted = soft_ce_rows_counted(B, S, offset, mask)
-    n = int(counted.sum())
+    G = num_groups
+    w = np.ones(G) if weights is None else np.asarray(weights, np.float64)
+    tr = soft_ce_teacher_rows(B, S, offset, teacher_rows)
+    counted = soft_ce_rows_counted(B, S, offset, mask, teacher_rows=teacher_rows, teacher_len=t.shape[1],
+                                   groups=groups, num_groups=G)
+    grp = np.zeros((B, S), dtype=np.int64) if groups is None else np.asarray(groups, np.int64).reshape(B, S)
+    counts = np.array([int((counted & (grp == g)).sum()) for g in range(G)])
     row_ce = np.zeros((B, S))
     grad = np.zeros((B, S, V))
     for b in range(B):
@@ -687,11 +717,20 @@ def soft_ce(student, teacher, offset: int, mask=None):
             if not counted[b, i]:
                 continue
             x = s[b, i]
-            y = t[b, i + offset]
+            y = t[b, tr[b, i]]
             lx = x.max() + math.log(np.exp(x - x.max()).sum())          # log-sum-exp of the student row
             py = np.exp(y - y.max())
             py /= py.sum()                                               # teacher distribution
             row_ce[b, i] = -(py * (x - lx)).sum()
-            grad[b, i] = (np.exp(x - lx) - py) / n
-    loss = row_ce.sum() / n if n else 0.0
+            g = grp[b, i]
+            grad[b, i] = w[g] * (np.exp(x - lx) - py) / counts[g]
+    means = np.array([row_ce[counted & (grp == g)].sum() / counts[g] if counts[g] else 0.0 for g in range(G)])
+    loss = float((w * means).sum())
+    return loss, grad, row_ce, means, counts
+
+
+def soft_ce(student, teacher, offset: int, mask=None):
+    """Per-pass soft cross-entropy.  student, teacher: [B, S, V] logits.  Returns
+    (loss, grad [B, S, V], row_ce [B, S]) in fp64 (row_ce is 0 on rows not counted)."""
+    loss, grad, row_ce, _, _ = soft_ce_grouped(student, teacher, offset, mask)
     return loss, grad, row_ce

@@ -524,6 +524,40 @@ def check_soft_ce_closed_forms():
     assert np.max(np.abs(rc2[0, :S - off] - ent[0, off:])) < 1e-12
 
 
+def check_soft_ce_grouped_library():
+    """Per-row teacher rows (a table into a teacher of another length, with rows outside it
+    uncounted) and per-group normalisation with weights == torch cross_entropy with
+    probability targets and fp64 autograd of sum_g w_g mean_g over rows chosen here."""
+    rng = np.random.default_rng(93)
+    B, S, St, V, G = 2, 9, 11, 13, 3
+    st = rng.standard_normal((B, S, V)) * 2
+    te = rng.standard_normal((B, St, V)) * 2
+    table = rng.integers(-1, St + 2, (B, S))
+    groups = rng.integers(-1, G + 1, (B, S))
+    mask = np.ones((B, S), dtype=np.uint8)
+    mask[0, 4] = 0
+    w = np.array([0.5, 1.0, 2.0])
+    loss, grad, row_ce, means, counts = O.soft_ce_grouped(st, te, 0, mask, teacher_rows=table, groups=groups,
+                                                          num_groups=G, weights=w)
+    x = torch.tensor(st, requires_grad=True)
+    total = torch.zeros((), dtype=F64)
+    for g in range(G):
+        rows = [(b, i) for b in range(B) for i in range(S)
+                if groups[b, i] == g and 0 <= table[b, i] < St and mask[b, i]]
+        assert counts[g] == len(rows)
+        if not rows:
+            continue
+        xs = torch.stack([x[b, i] for b, i in rows])
+        tg = torch.softmax(torch.stack([torch.tensor(te[b, table[b, i]]) for b, i in rows]), -1)
+        ce = torch.nn.functional.cross_entropy(xs, tg, reduction="none")
+        assert abs(means[g] - ce.mean().item()) < 1e-12
+        assert np.max(np.abs(np.array([row_ce[b, i] for b, i in rows]) - ce.detach().numpy())) < 1e-12
+        total = total + w[g] * ce.mean()
+    total.backward()
+    assert abs(loss - total.item()) < 1e-12
+    assert np.max(np.abs(grad - x.grad.numpy())) < 1e-12
+
+
 def _band_mask(S, p, window):
     """[S, p*S] visibility with a trunk band j in (i - window, i], built from tril/triu and eye blocks."""
     ones = torch.ones(S, S, dtype=torch.bool)
@@ -662,7 +696,7 @@ PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check
         check_merge_closed_form, check_block_sdpa_mask, check_block_zero_query_closed_form,
         check_block_size1_is_causal, check_block_grad_autograd, check_soft_ce_library, check_soft_ce_closed_forms,
         check_window_sdpa_and_grad, check_window_closed_forms, check_window_ring_partition, check_chunk_bwd_partition,
-        check_trunk_keys_grad_autograd]
+        check_trunk_keys_grad_autograd, check_soft_ce_grouped_library]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
@@ -754,6 +788,13 @@ def _trunk_keys_late_rows(q, ks, vs, dout, p, sl, g, keys, *, layout, Hq, Hkv, s
     return O.unrotate_half(dk, gk.pos[keys], base), dv
 
 
+_orig_counted = O.soft_ce_rows_counted
+
+
+def _ce_counted_ignores_groups(B, S, off, mask=None, *, teacher_rows=None, teacher_len=None, groups=None, num_groups=1):
+    return _orig_counted(B, S, off, mask, teacher_rows=teacher_rows, teacher_len=teacher_len)
+
+
 MISTAKES = [
     ("ttt_mask_row", _mask_no_branch),
     ("ttt_mask_row", _mask_strict_causal),
@@ -772,13 +813,15 @@ MISTAKES = [
     ("block_visible_ctx", lambda a, L: int(min(max(a + 1, 0), L))),
     ("block_slot_position", lambda a, t: int(a) + np.asarray(t) + 1),
     ("block_slot_position", lambda a, t: np.asarray(t)),
-    ("soft_ce_rows_counted", lambda B, S, off, mask=None: np.arange(S)[None, :].repeat(B, 0) + off <= S),
+    ("soft_ce_rows_counted", lambda B, S, off, mask=None, **kw: np.arange(S)[None, :].repeat(B, 0) + off <= S),
     ("trunk_window_start", lambda i, w: 0 if w <= 0 else max(0, i - w + 2)),
     ("trunk_window_start", lambda i, w: 0 if w <= 0 else max(0, i - w)),
     ("ring_visible", lambda qp, kp, w=0: np.asarray(kp)[None, :] <= np.asarray(qp)[:, None]),
-    ("soft_ce_rows_counted", lambda B, S, off, mask=None: np.ones((B, S), dtype=bool) & (np.arange(S)[None, :] + off < S)),
+    ("soft_ce_rows_counted", lambda B, S, off, mask=None, **kw: np.ones((B, S), dtype=bool) & (np.arange(S)[None, :] + off < S)),
     ("merge", lambda oa, la, ob, lb: (_orig_merge(oa, la, ob, lb)[0], np.maximum(la, lb))),
     ("bwd_trunk_keys", _trunk_keys_late_rows),
+    ("soft_ce_teacher_rows", lambda B, S, off, tr=None: np.arange(S)[None, :].repeat(B, 0) + off),
+    ("soft_ce_rows_counted", _ce_counted_ignores_groups),
 ]
 
 
