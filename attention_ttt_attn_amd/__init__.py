@@ -88,10 +88,14 @@ class SoftCeDesc(ctypes.Structure):
         ("seqlen", ctypes.c_int32),
         ("vocab", ctypes.c_int32),
         ("teacher_offset", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("teacher_seqlen", ctypes.c_int32),
         ("student_stride", ctypes.c_int64 * 2),
         ("teacher_stride", ctypes.c_int64 * 2),
         ("mask", ctypes.c_void_p),
+        ("teacher_rows", ctypes.c_void_p),
+        ("groups", ctypes.c_void_p),
+        ("num_groups", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -548,29 +552,39 @@ def block_bwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, o, lse, d
     return dq, dk_ctx, dv_ctx, dk_blk, dv_blk
 
 
-def make_soft_ce_desc(student, teacher, teacher_offset: int, mask=None) -> SoftCeDesc:
+def make_soft_ce_desc(student, teacher, teacher_offset: int, mask=None, teacher_rows=None, groups=None,
+                      num_groups: int = 1) -> SoftCeDesc:
     d = SoftCeDesc()
     d.struct_size = ctypes.sizeof(SoftCeDesc)
     d.batch, d.seqlen, d.vocab = student.shape
-    if tuple(teacher.shape) != tuple(student.shape):
-        raise ValueError("student and teacher logits must have the same [B, S, V] shape")
+    if teacher.shape[0] != student.shape[0] or teacher.shape[2] != student.shape[2]:
+        raise ValueError("student [B, S, V] and teacher [B, St, V] logits must share B and V")
+    if teacher.shape[1] != student.shape[1] and teacher_rows is None:
+        raise ValueError("a teacher of another length needs teacher_rows")
     if student.stride(-1) != 1 or teacher.stride(-1) != 1:
         raise ValueError("the vocab axis must be contiguous")
     d.teacher_offset = int(teacher_offset)
+    d.teacher_seqlen = teacher.shape[1]
     d.student_stride[:] = student.stride()[:2]
     d.teacher_stride[:] = teacher.stride()[:2]
     d.mask = mask.data_ptr() if mask is not None else None
+    d.teacher_rows = teacher_rows.data_ptr() if teacher_rows is not None else None
+    d.groups = groups.data_ptr() if groups is not None else None
+    d.num_groups = int(num_groups)
     return d
 
 
 @_on_stream
-def soft_ce_fwd(student, teacher, teacher_offset: int, *, mask=None, row_ce=None, stream=None):
-    """Per-pass soft cross-entropy.  student, teacher: bf16 [B, S, V]; mask: uint8 [B, S] or None.
-    Returns (stats [2] = (loss, counted rows), row_lse [B, S, 2], row_ce [B, S])."""
+def soft_ce_fwd(student, teacher, teacher_offset: int, *, mask=None, row_ce=None, teacher_rows=None, groups=None,
+                num_groups: int = 1, stream=None):
+    """Per-pass soft cross-entropy.  student bf16 [B, S, V], teacher bf16 [B, St, V]; mask uint8
+    [B, S]; teacher_rows / groups int32 [B, S] (per-row teacher row, normalisation group).
+    Returns (stats [2 + 2G] = (loss, counted rows, then (mean, count) per group),
+    row_lse [B, S, 2], row_ce [B, S])."""
     torch = _torch()
-    d = make_soft_ce_desc(student, teacher, teacher_offset, mask)
+    d = make_soft_ce_desc(student, teacher, teacher_offset, mask, teacher_rows, groups, num_groups)
     B, S, _ = student.shape
-    stats = torch.empty(2, dtype=torch.float32, device=student.device)
+    stats = torch.empty(2 + 2 * max(1, int(num_groups)), dtype=torch.float32, device=student.device)
     row_lse = torch.empty((B, S, 2), dtype=torch.float32, device=student.device)
     if row_ce is None:
         row_ce = torch.empty((B, S), dtype=torch.float32, device=student.device)
@@ -580,11 +594,14 @@ def soft_ce_fwd(student, teacher, teacher_offset: int, *, mask=None, row_ce=None
 
 
 @_on_stream
-def soft_ce_bwd(student, teacher, teacher_offset: int, row_lse, stats, dloss, *, mask=None, dstudent=None,
-                stream=None):
-    """Gradient of the loss with respect to the student logits (bf16, student strides)."""
+def soft_ce_bwd(student, teacher, teacher_offset: int, row_lse, stats, dloss, *, mask=None, teacher_rows=None,
+                groups=None, num_groups: int = 1, dstudent=None, stream=None):
+    """Gradient with respect to the student logits (bf16, student strides); dloss: fp32 device
+    [G], the upstream gradient of each group's mean."""
     torch = _torch()
-    d = make_soft_ce_desc(student, teacher, teacher_offset, mask)
+    d = make_soft_ce_desc(student, teacher, teacher_offset, mask, teacher_rows, groups, num_groups)
+    if dloss.numel() < max(1, int(num_groups)):
+        raise ValueError("dloss needs one value per group")
     if dstudent is None:
         dstudent = torch.empty_strided(student.shape, student.stride(), dtype=student.dtype, device=student.device)
     if dstudent.stride() != student.stride():

@@ -789,11 +789,20 @@ int make_ce(const ttt_soft_ce_desc* d, ttt::CeProb& C) {
   if (d->vocab < 8 || d->vocab % 8)
     return fail(TTT_ERR_BAD_SHAPE, "vocab %d must be a positive multiple of 8", d->vocab);
   if (d->teacher_offset < 0) return fail(TTT_ERR_BAD_SHAPE, "teacher_offset %d is negative", d->teacher_offset);
+  if (d->teacher_seqlen < 0 || (int64_t)d->batch * d->teacher_seqlen > ((int64_t)1 << 31) - 1)
+    return fail(TTT_ERR_BAD_SHAPE, "teacher_seqlen %d", d->teacher_seqlen);
+  if (d->num_groups < 0 || d->num_groups > 64)
+    return fail(TTT_ERR_BAD_SHAPE, "num_groups %d outside 0..64", d->num_groups);
+  if (((uintptr_t)d->teacher_rows | (uintptr_t)d->groups) & 3u)
+    return fail(TTT_ERR_MISALIGNED, "teacher_rows and groups must be 4-byte aligned");
   memset(&C, 0, sizeof C);
   C.B = d->batch, C.S = d->seqlen, C.V = d->vocab, C.offset = d->teacher_offset, C.mask = d->mask;
-  auto st = [&](const int64_t* s, int64_t& sb, int64_t& sr, const char* name) -> int {
+  C.T = d->teacher_seqlen > 0 ? d->teacher_seqlen : d->seqlen;
+  C.trows = d->teacher_rows, C.groups = d->groups;
+  C.G = d->num_groups > 0 ? d->num_groups : 1;
+  auto st = [&](const int64_t* s, int64_t& sb, int64_t& sr, const char* name, int rows) -> int {
     if (s[0] == 0 && s[1] == 0) {
-      sb = (int64_t)d->seqlen * d->vocab, sr = d->vocab;
+      sb = (int64_t)rows * d->vocab, sr = d->vocab;
       return 0;
     }
     if (s[0] < 0 || s[1] < d->vocab)
@@ -805,8 +814,8 @@ int make_ce(const ttt_soft_ce_desc* d, ttt::CeProb& C) {
     sb = s[0], sr = s[1];
     return 0;
   };
-  if (int e = st(d->student_stride, C.ss_b, C.ss_t, "student")) return e;
-  if (int e = st(d->teacher_stride, C.ts_b, C.ts_t, "teacher")) return e;
+  if (int e = st(d->student_stride, C.ss_b, C.ss_t, "student", C.S)) return e;
+  if (int e = st(d->teacher_stride, C.ts_b, C.ts_t, "teacher", C.T)) return e;
   return TTT_OK;
 }
 }  // namespace

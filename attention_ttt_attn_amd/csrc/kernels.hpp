@@ -67,10 +67,15 @@ void launch_block_dq_bf16(const Prob& P, const uint16_t* v_ctx, const uint16_t* 
 // Per-pass soft cross-entropy (bf16 logits [B][S][V], vocab contiguous, V % 8 == 0).
 struct CeProb {
   int B, S, V, offset;
-  const uint8_t* mask;  // [B][S] or null
+  int T;                 // teacher rows per batch
+  const uint8_t* mask;   // [B][S] or null
+  const int* trows;      // [B][S] teacher row of each student row, or null (row + offset)
+  const int* groups;     // [B][S] normalisation group, or null (group 0)
+  int G;                 // groups, 1..64
   int64_t ss_b, ss_t, ts_b, ts_t;
 };
-// row_lse [B*S][2] (student, teacher), row_ce [B*S], stats [2] = (mean loss, counted rows)
+// row_lse [B*S][2] (student, teacher), row_ce [B*S], stats [2 + 2G] = (loss, counted rows,
+// then each group's (mean, count)); dloss [G]
 void launch_soft_ce_fwd(const CeProb& C, const uint16_t* s, const uint16_t* t, float* row_lse, float* row_ce,
                         float* stats, hipStream_t st);
 void launch_soft_ce_bwd(const CeProb& C, const uint16_t* s, const uint16_t* t, const float* row_lse,

@@ -7,7 +7,11 @@
 // student logits at row i are scored against softmax(teacher logits at row
 // i + offset) of the same sequence; rows without such a teacher row, or with
 // mask 0, are not counted; loss = sum of the counted rows' cross-entropies /
-// number of counted rows.  Chunking over tokens only bounds memory in a
+// number of counted rows.  Block-draft slots (same item: per-slot
+// normalisation) pass a teacher row per student row (slot at position a + t:
+// row a + t + 1) and a group per row (the slot index); each group is then
+// normalised by its own count and the loss is the sum of the group means.
+// Chunking over tokens only bounds memory in a
 // framework implementation; these kernels stream every row once, so no [T, V]
 // intermediate exists at all.
 //
@@ -37,8 +41,12 @@ __device__ __forceinline__ void merge(float& m, float& l, float& w, float m2, fl
   m = mx;
 }
 
-__device__ __forceinline__ bool counted(const CeProb& C, int b, int i) {
-  return i + C.offset < C.S && (!C.mask || C.mask[(int64_t)b * C.S + i] != 0);
+// Row (b, i): whether it is counted, its teacher row and its group.
+__device__ __forceinline__ bool counted(const CeProb& C, int b, int i, int& trow, int& grp) {
+  const int64_t r = (int64_t)b * C.S + i;
+  trow = C.trows ? C.trows[r] : i + C.offset;
+  grp = C.groups ? C.groups[r] : 0;
+  return trow >= 0 && trow < C.T && grp >= 0 && grp < C.G && (!C.mask || C.mask[r] != 0);
 }
 
 __global__ void __launch_bounds__(NT) soft_ce_fwd_kernel(CeProb C, const uint16_t* __restrict__ s,
@@ -47,7 +55,8 @@ __global__ void __launch_bounds__(NT) soft_ce_fwd_kernel(CeProb C, const uint16_
   const int row = blockIdx.x;
   const int b = row / C.S, i = row % C.S;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  if (!counted(C, b, i)) {
+  int trow, grp;
+  if (!counted(C, b, i, trow, grp)) {
     if (tid == 0) {
       row_lse[2 * (int64_t)row] = 0.f;
       row_lse[2 * (int64_t)row + 1] = 0.f;
@@ -56,7 +65,7 @@ __global__ void __launch_bounds__(NT) soft_ce_fwd_kernel(CeProb C, const uint16_
     return;
   }
   const uint16_t* sr = s + (int64_t)b * C.ss_b + (int64_t)i * C.ss_t;
-  const uint16_t* tr = t + (int64_t)b * C.ts_b + (int64_t)(i + C.offset) * C.ts_t;
+  const uint16_t* tr = t + (int64_t)b * C.ts_b + (int64_t)trow * C.ts_t;
   // student: (ms, ls); teacher: (mt, lt) and wt = sum 2^(t2 - mt) * s.  All
   // U chunks' loads are issued before any of them is used.
   float ms = -INFINITY, ls = 0.f, mt = -INFINITY, lt = 0.f, wt = 0.f;
@@ -130,39 +139,54 @@ __global__ void __launch_bounds__(NT) soft_ce_fwd_kernel(CeProb C, const uint16_
   }
 }
 
-// Fixed-order mean over rows: thread k sums rows k, k + 1024, ... ; then a
-// fixed tree.  out[0] = loss, out[1] = number of counted rows.
+// Fixed-order means per group: for each group, thread k sums its rows k,
+// k + 1024, ...; then a fixed tree.  out = (sum of the group means, counted
+// rows, then each group's (mean, count)).
 __global__ void __launch_bounds__(1024) soft_ce_mean_kernel(CeProb C, const float* __restrict__ row_ce,
                                                             float* __restrict__ out) {
   __shared__ double sum[1024];
   __shared__ int cnt[1024];
   const int tid = threadIdx.x;
   const int rows = C.B * C.S;
-  double a = 0.0;
-  int n = 0;
-  for (int r = tid; r < rows; r += 1024) {
-    if (counted(C, r / C.S, r % C.S)) {
-      a += (double)row_ce[r];
-      ++n;
+  double loss = 0.0;
+  int total = 0;
+  for (int g = 0; g < C.G; ++g) {
+    double a = 0.0;
+    int n = 0;
+    for (int r = tid; r < rows; r += 1024) {
+      int trow, grp;
+      if (counted(C, r / C.S, r % C.S, trow, grp) && grp == g) {
+        a += (double)row_ce[r];
+        ++n;
+      }
     }
-  }
-  sum[tid] = a;
-  cnt[tid] = n;
-  __syncthreads();
-  for (int w = 512; w > 0; w >>= 1) {
-    if (tid < w) {
-      sum[tid] += sum[tid + w];
-      cnt[tid] += cnt[tid + w];
-    }
+    sum[tid] = a;
+    cnt[tid] = n;
     __syncthreads();
+    for (int w = 512; w > 0; w >>= 1) {
+      if (tid < w) {
+        sum[tid] += sum[tid + w];
+        cnt[tid] += cnt[tid + w];
+      }
+      __syncthreads();
+    }
+    const double mean = cnt[0] ? sum[0] / cnt[0] : 0.0;
+    loss += mean;
+    total += cnt[0];
+    if (tid == 0) {
+      out[2 + 2 * g] = (float)mean;
+      out[3 + 2 * g] = (float)cnt[0];
+    }
+    __syncthreads();  // sum/cnt are reused by the next group
   }
   if (tid == 0) {
-    out[0] = cnt[0] ? (float)(sum[0] / cnt[0]) : 0.f;
-    out[1] = (float)cnt[0];
+    out[0] = (float)loss;
+    out[1] = (float)total;
   }
 }
 
-// dstudent = dloss / count * (softmax(student) - teacher distribution) on counted rows, 0 elsewhere.
+// dstudent = dloss[g] / count_g * (softmax(student) - teacher distribution) on
+// counted rows of group g, 0 elsewhere.
 __global__ void __launch_bounds__(NT) soft_ce_bwd_kernel(CeProb C, const uint16_t* __restrict__ s,
                                                          const uint16_t* __restrict__ t,
                                                          const float* __restrict__ row_lse,
@@ -172,14 +196,15 @@ __global__ void __launch_bounds__(NT) soft_ce_bwd_kernel(CeProb C, const uint16_
   const int b = row / C.S, i = row % C.S;
   const int tid = threadIdx.x;
   uint16_t* gr = g + (int64_t)b * C.ss_b + (int64_t)i * C.ss_t;
-  if (!counted(C, b, i)) {
+  int trow, grp;
+  if (!counted(C, b, i, trow, grp)) {
     for (int v0 = tid * 8; v0 < C.V; v0 += NT * 8) *(u32x4*)(gr + v0) = u32x4{0, 0, 0, 0};
     return;
   }
   const uint16_t* sr = s + (int64_t)b * C.ss_b + (int64_t)i * C.ss_t;
-  const uint16_t* tr = t + (int64_t)b * C.ts_b + (int64_t)(i + C.offset) * C.ts_t;
-  const float n = stats[1];
-  const float scale = n > 0.f ? dloss[0] / n : 0.f;
+  const uint16_t* tr = t + (int64_t)b * C.ts_b + (int64_t)trow * C.ts_t;
+  const float n = stats[3 + 2 * grp];
+  const float scale = n > 0.f ? dloss[grp] / n : 0.f;
   const float ls2 = row_lse[2 * (int64_t)row] * kLog2e, lt2 = row_lse[2 * (int64_t)row + 1] * kLog2e;
   for (int v0 = tid * 8; v0 < C.V; v0 += NT * 8 * U) {
     u32x4 xs[U], ys[U];

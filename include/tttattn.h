@@ -289,13 +289,23 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* blk, const 
 typedef struct ttt_soft_ce_desc {
   uint32_t struct_size;       /* = sizeof(ttt_soft_ce_desc)                               */
   int32_t batch, seqlen, vocab;
-  int32_t teacher_offset;     /* >= 0                                                     */
-  int32_t reserved;           /* 0                                                        */
+  int32_t teacher_offset;     /* >= 0; row i is scored against teacher row i + offset
+                                 unless teacher_rows is given                             */
+  int32_t teacher_seqlen;     /* teacher rows per batch; 0 = seqlen                       */
   int64_t student_stride[2];  /* batch, row strides of the student logits (elements); a
                                  zero pair selects the contiguous [B, S, V]; the gradient
                                  uses the same strides                                    */
-  int64_t teacher_stride[2];  /* the same for the teacher logits                          */
+  int64_t teacher_stride[2];  /* the same for the teacher logits ([B, teacher_seqlen, V]) */
   const uint8_t* mask;        /* device [B][S] (row counted iff != 0) or NULL             */
+  const int32_t* teacher_rows;/* device [B][S] or NULL: the teacher row of each student
+                                 row; outside [0, teacher_seqlen) = row not counted.  A
+                                 block-draft slot at position a + t takes row a + t + 1
+                                 (same issue, item 3: per-slot normalisation)             */
+  const int32_t* groups;      /* device [B][S] or NULL: normalisation group of each row
+                                 (e.g. the block slot index); outside [0, num_groups) =
+                                 not counted; NULL = every row in group 0                 */
+  int32_t num_groups;         /* 1 .. 64 (0 = 1)                                          */
+  int32_t reserved;           /* 0                                                        */
 } ttt_soft_ce_desc;
 
 /* Bytes of workspace ttt_soft_ce_fwd needs when its row_ce argument is NULL (it then
@@ -303,17 +313,21 @@ typedef struct ttt_soft_ce_desc {
  * last error if the descriptor is invalid. */
 size_t ttt_soft_ce_workspace_bytes(const ttt_soft_ce_desc* d);
 
-/* Forward: stats[0] = loss, stats[1] = number of counted rows (device float[2]);
- * row_lse [B][S][2] (device fp32): natural-log LSE of the student and teacher rows,
- * needed by the backward; row_ce [B][S] (device fp32, optional): each counted row's
- * cross-entropy, 0 elsewhere (when NULL the workspace holds it).  Deterministic. */
+/* Forward: stats (device float[2 + 2 G], G = num_groups): stats[0] = loss = the sum
+ * over groups of each group's mean cross-entropy over its counted rows (one group:
+ * the mean over counted rows), stats[1] = counted rows, stats[2 + 2g] and
+ * stats[3 + 2g] = group g's mean and count; row_lse [B][S][2] (device fp32):
+ * natural-log LSE of the student and teacher rows, needed by the backward; row_ce
+ * [B][S] (device fp32, optional): each counted row's cross-entropy, 0 elsewhere (when
+ * NULL the workspace holds it).  Deterministic (fixed-order sums). */
 int ttt_soft_ce_fwd(const ttt_soft_ce_desc* d, const void* student, const void* teacher, float* stats,
                     float* row_lse, float* row_ce, void* ws, size_t ws_bytes, void* stream);
 
-/* Backward: dstudent = dloss[0] / stats[1] * (softmax(student) - softmax(teacher row
- * i + offset)) on counted rows, 0 on the others (bf16, student strides).  row_lse and
- * stats come from ttt_soft_ce_fwd; dloss is a device float (the loss's upstream
- * gradient).  No gradient is returned for the teacher. */
+/* Backward: dstudent = dloss[g] / count_g * (softmax(student) - softmax(the row's
+ * teacher row)) on counted rows of group g, 0 on the others (bf16, student strides).
+ * row_lse and stats come from ttt_soft_ce_fwd; dloss is device float[G], the upstream
+ * gradient of each group's mean (all equal for the gradient of stats[0]; a weighted
+ * sum of the group losses passes its weights).  No gradient for the teacher. */
 int ttt_soft_ce_bwd(const ttt_soft_ce_desc* d, const void* student, const void* teacher, const float* row_lse,
                     const float* stats, const float* dloss, void* dstudent, void* stream);
 

@@ -374,7 +374,7 @@ def ce_desc(B=2, S=100, V=4096, off=1):
 
 def test_soft_ce_struct_and_validation():
     lib = tk.library()
-    assert ctypes.sizeof(tk.SoftCeDesc) == 64
+    assert ctypes.sizeof(tk.SoftCeDesc) == 88
     fwd = lambda d, s=FAKE, t=FAKE, st=FAKE, ll=FAKE, rc=FAKE, ws=FAKE, n=1 << 40: lib.ttt_soft_ce_fwd(
         ctypes.byref(d) if d is not None else None, s, t, st, ll, rc, ws, n, None)
     bwd = lambda d, s=FAKE, t=FAKE, ll=FAKE, st=FAKE, dl=FAKE, g=FAKE: lib.ttt_soft_ce_bwd(
@@ -403,6 +403,22 @@ def test_soft_ce_struct_and_validation():
     assert bwd(ce_desc(), g=None) == 1 and "dstudent" in err()
     assert bwd(ce_desc(), dl=None) == 1 and "dloss" in err()
     assert bwd(ce_desc(), ll=FAKE + 2) == 4
+    # per-row teacher rows and normalisation groups
+    d = ce_desc()
+    d.num_groups = 65
+    assert fwd(d) == 2 and "num_groups" in err()
+    d = ce_desc()
+    d.num_groups = -1
+    assert fwd(d) == 2
+    d = ce_desc()
+    d.teacher_seqlen = -3
+    assert fwd(d) == 2 and "teacher_seqlen" in err()
+    d = ce_desc()
+    d.groups = FAKE + 2
+    assert fwd(d) == 4 and "groups" in err()
+    d = ce_desc()
+    d.teacher_rows = FAKE + 1
+    assert bwd(d) == 4
 
 
 def test_window_validation():

@@ -129,3 +129,45 @@ def test_soft_ce_fullsize(dev, tk):
     e = rel_fro(np.stack(gg), np.stack(gr))
     print(f"full size: {len(rows)} rows, row CE max-abs {ece:.2e}, LSE max-abs {el:.2e}, grad rel Frobenius {e:.2e}")
     assert ece <= 5e-5 and el <= 5e-5 and e <= 4e-3
+
+
+@pytest.mark.parametrize("bs,nblk", [(8, 9), (16, 4)])
+def test_soft_ce_block_slots(dev, tk, bs, nblk):
+    """Block-draft slots: slot t of the block anchored at a is scored against teacher row
+    a + t + 1 of a longer target sequence (rows past its end uncounted), normalised per
+    slot index (bs groups), with decaying per-slot weights as the upstream gradient."""
+    B, St, V = 2, 300, 1000
+    S = nblk * bs
+    rng = np.random.default_rng(60 + bs)
+    anchors = np.sort(rng.integers(0, St, (B, nblk)), axis=1)
+    anchors[:, -1] = St - bs // 2                         # the last block runs past the target's end
+    t_idx = np.arange(S) % bs
+    table = (np.repeat(anchors, bs, axis=1) + t_idx[None, :] + 1).astype(np.int32)
+    groups = np.broadcast_to(t_idx, (B, S)).astype(np.int32).copy()
+    mask = (rng.random((B, S)) > 0.1).astype(np.uint8)
+    st, te = logits(61, (B, S, V)), logits(62, (B, St, V))
+    w = (0.8 ** np.arange(bs)).astype(np.float32)
+    up = lambda x: torch.from_numpy(x).to(dev)
+    gs, gt = up(st).to(torch.bfloat16), up(te).to(torch.bfloat16)
+    gtab, ggrp, gm = up(table), up(groups), up(mask)
+    stats, row_lse, row_ce = tk.soft_ce_fwd(gs, gt, 0, mask=gm, teacher_rows=gtab, groups=ggrp, num_groups=bs)
+    g = tk.soft_ce_bwd(gs, gt, 0, row_lse, stats, up(w), mask=gm, teacher_rows=gtab, groups=ggrp, num_groups=bs)
+    torch.cuda.synchronize()
+    stats, row_ce, g = to_np(stats), to_np(row_ce), to_np(g)
+    loss1, _, rce, means, counts = O.soft_ce_grouped(st, te, 0, mask, teacher_rows=table, groups=groups,
+                                                     num_groups=bs)
+    _, grad_w, _, _, _ = O.soft_ce_grouped(st, te, 0, mask, teacher_rows=table, groups=groups, num_groups=bs,
+                                           weights=w)
+    counted = O.soft_ce_rows_counted(B, S, 0, mask, teacher_rows=table, teacher_len=St, groups=groups,
+                                     num_groups=bs)
+    print(f"bs={bs}: loss {stats[0]:.6f} ref {loss1:.6f}, counted {stats[1]:.0f}/{B * S}, per-slot counts "
+          f"{stats[3::2].astype(int).tolist()}")
+    assert int(stats[1]) == int(counted.sum()) < B * S
+    assert np.array_equal(stats[3::2].astype(int), counts)
+    assert np.max(np.abs(stats[2::2] - means)) <= 2e-5 * max(1.0, np.abs(means).max())
+    assert abs(stats[0] - loss1) <= 1e-5 * max(1.0, abs(loss1))
+    assert np.max(np.abs(row_ce - rce)) <= 2e-5
+    assert np.all(g[~counted] == 0)
+    e = rel_fro(g, grad_w)
+    print(f"  grad (slot weights 0.8^t) rel Frobenius {e:.3e}")
+    assert e <= 4e-3
