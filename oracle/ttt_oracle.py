@@ -82,6 +82,10 @@ What is computed (one call = one TTT pass p, 1-based):
   branch keys of those rows; `merge` joins two partial results over disjoint
   key sets: LSE = ln(e^LSE_a + e^LSE_b), O = e^(LSE_a - LSE) O_a +
   e^(LSE_b - LSE) O_b.  A row that sees no key has O = 0 and LSE = -inf.
+  Packed (THD) ring steps, `fwd_chunk_thd` / `bwd_chunk_thd`: every sequence s
+  of the batch takes its own ring step (its query rows at positions
+  q_offsets[s].., its pass-1 key rows kv_cu[s]..kv_cu[s+1] at positions
+  kv_offsets[s]..), and sequences never see each other (the THD rule above).
 
 Everything is fp64; inputs are upcast from whatever float type they hold.
 No blocking, fusion or reordering beyond evaluating rows in independent
@@ -97,7 +101,7 @@ import numpy as np
 __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_position",
            "ttt_mask_row", "trunk_window_start", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows",
            "bwd_trunk_keys", "Slice",
-           "fwd_chunk", "bwd_chunk", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd",
+           "fwd_chunk", "bwd_chunk", "fwd_chunk_thd", "bwd_chunk_thd", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd",
            "block_bwd_rows", "block_bwd", "soft_ce_rows_counted", "soft_ce_teacher_rows", "soft_ce", "soft_ce_grouped"]
 
 
@@ -520,6 +524,68 @@ def bwd_chunk(q, k0, v0, branch_ks, branch_vs, p: int, dout, o, lse, *, q_offset
             dk0[b, :, g] = unrotate_half(dk_rot, kpos, base)
             for t in range(nb):
                 dkb[t][b, :, g] = unrotate_half(dkb_rot[t], key_position(t + 2, qpos), base)
+    return dq, dk0, dv0, dkb, dvb
+
+
+def _thd_segments(cu_seqlens, kv_cu_seqlens):
+    cu = [int(x) for x in cu_seqlens]
+    kc = [int(x) for x in kv_cu_seqlens]
+    if len(cu) != len(kc):
+        raise ValueError("cu_seqlens and kv_cu_seqlens must list the same sequences")
+    return [(cu[s], cu[s + 1], kc[s], kc[s + 1]) for s in range(len(cu) - 1)]
+
+
+def fwd_chunk_thd(q, k0, v0, branch_ks, branch_vs, p: int, *, cu_seqlens, kv_cu_seqlens, q_offsets, kv_offsets,
+                  scale: Optional[float] = None, base: float = 0.0, window: int = 0):
+    """A packed (THD) ring step: q [T, Hq, D] holds the query rows of every sequence
+    (cu_seqlens), k0 / v0 [Tk, Hkv, D] their pass-1 key rows (kv_cu_seqlens), branch_ks /
+    branch_vs None or p-1 tensors [T, Hkv, D] at the query rows.  Sequence s is the ring
+    step fwd_chunk of its own rows at q_offsets[s] against its own keys at kv_offsets[s].
+    Returns (O [T, Hq, D], LSE [Hq, T])."""
+    T, Hq, D = q.shape
+    O = np.zeros((T, Hq, D))
+    lse = np.full((Hq, T), -np.inf)
+    for s, (a, e, ka, ke) in enumerate(_thd_segments(cu_seqlens, kv_cu_seqlens)):
+        if e == a:
+            continue
+        bk = None if branch_ks is None else [np.asarray(t)[None, a:e] for t in branch_ks]
+        bv = None if branch_vs is None else [np.asarray(t)[None, a:e] for t in branch_vs]
+        o, l = fwd_chunk(np.asarray(q)[None, a:e], np.asarray(k0)[None, ka:ke], np.asarray(v0)[None, ka:ke], bk, bv,
+                         p, q_offset=int(q_offsets[s]), kv_offset=int(kv_offsets[s]), scale=scale, base=base,
+                         window=window)
+        O[a:e] = o[0]
+        lse[:, a:e] = l[0]
+    return O, lse
+
+
+def bwd_chunk_thd(q, k0, v0, branch_ks, branch_vs, p: int, dout, o, lse, *, cu_seqlens, kv_cu_seqlens, q_offsets,
+                  kv_offsets, scale: Optional[float] = None, base: float = 0.0, window: int = 0):
+    """Backward terms of a packed (THD) ring step (inputs as fwd_chunk_thd; o, lse the rows'
+    whole-sequence outputs, LSE [Hq, T]): each sequence's bwd_chunk.  Returns (dq [T, Hq, D],
+    dk0 [Tk, Hkv, D], dv0, [branch dk], [branch dv]); keys of a sequence without query rows
+    get zeros."""
+    T, Hq, D = q.shape
+    Tk, Hkv = np.asarray(k0).shape[0], np.asarray(k0).shape[1]
+    nb = p - 1 if branch_ks is not None else 0
+    dq = np.zeros((T, Hq, D))
+    dk0, dv0 = np.zeros((Tk, Hkv, D)), np.zeros((Tk, Hkv, D))
+    dkb = [np.zeros((T, Hkv, D)) for _ in range(nb)]
+    dvb = [np.zeros((T, Hkv, D)) for _ in range(nb)]
+    for s, (a, e, ka, ke) in enumerate(_thd_segments(cu_seqlens, kv_cu_seqlens)):
+        if e == a:
+            continue
+        bk = None if branch_ks is None else [np.asarray(t)[None, a:e] for t in branch_ks]
+        bv = None if branch_vs is None else [np.asarray(t)[None, a:e] for t in branch_vs]
+        r = bwd_chunk(np.asarray(q)[None, a:e], np.asarray(k0)[None, ka:ke], np.asarray(v0)[None, ka:ke], bk, bv, p,
+                      np.asarray(dout)[None, a:e], np.asarray(o)[None, a:e], np.asarray(lse)[None, :, a:e],
+                      q_offset=int(q_offsets[s]), kv_offset=int(kv_offsets[s]), scale=scale, base=base,
+                      window=window)
+        dq[a:e] = r[0][0]
+        dk0[ka:ke] = r[1][0]
+        dv0[ka:ke] = r[2][0]
+        for t in range(nb):
+            dkb[t][a:e] = r[3][t][0]
+            dvb[t][a:e] = r[4][t][0]
     return dq, dk0, dv0, dkb, dvb
 
 

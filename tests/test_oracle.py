@@ -688,6 +688,59 @@ def check_trunk_keys_grad_autograd():
             assert np.max(np.abs(dv - T[1 + p].grad.numpy()[keys, g])) < 1e-10
 
 
+def check_thd_chunk_ring_partition():
+    """Packed (THD) ring steps: sequences of different lengths (one empty) each split into 4
+    zig-zag chunks; step (qc, kc) packs chunk qc's rows and chunk kc's keys of every sequence
+    at their own offsets.  Merging each row's steps gives the whole-sequence THD forward, and
+    summing the steps' backward terms its gradients."""
+    lens, Hq, Hkv, D, p, base = [8, 12, 0, 4], 4, 2, 8, 3, 1e4
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, ks, vs, do = make(S=T, Hq=Hq, Hkv=Hkv, D=D, p=p, seed=101)
+    ro, rl = O.fwd(q, ks, vs, p, layout="thd", cu_seqlens=cu, base=base)
+    dQ, dK, dV = O.bwd(q, ks, vs, do, p, layout="thd", cu_seqlens=cu, base=base)
+    nc = 4
+    rows = lambda c: np.concatenate([np.arange(cu[s] + c * (n // nc), cu[s] + (c + 1) * (n // nc))
+                                     for s, n in enumerate(lens)]).astype(np.int64)
+    ccu = lambda: np.concatenate([[0], np.cumsum([n // nc for n in lens])])
+    offs = lambda c: np.array([c * (n // nc) for n in lens])
+    acc = {}
+    gq, gk, gv = np.zeros_like(dQ), [np.zeros_like(dK[0]) for _ in range(p)], [np.zeros_like(dV[0]) for _ in range(p)]
+    for qc in range(nc):
+        qr = rows(qc)
+        acc_o, acc_l = np.zeros((1, len(qr), Hq, D)), np.full((1, Hq, len(qr)), -np.inf)
+        for kc in range(nc):
+            kr = rows(kc)
+            br = kc == qc
+            args = (q[qr], ks[0][kr], vs[0][kr], [k[qr] for k in ks[1:]] if br else None,
+                    [v[qr] for v in vs[1:]] if br else None, p)
+            geo = dict(cu_seqlens=ccu(), kv_cu_seqlens=ccu(), q_offsets=offs(qc), kv_offsets=offs(kc), base=base)
+            o, l = O.fwd_chunk_thd(*args, **geo)
+            acc_o, acc_l = O.merge(acc_o, acc_l, o[None], l[None])
+            dq_, dk0, dv0, dkb, dvb = O.bwd_chunk_thd(*args, do[qr], ro[qr], rl[:, qr], **geo)
+            gq[qr] += dq_
+            gk[0][kr] += dk0
+            gv[0][kr] += dv0
+            for t in range(len(dkb)):
+                gk[t + 1][qr] += dkb[t]
+                gv[t + 1][qr] += dvb[t]
+        assert np.max(np.abs(acc_o[0] - ro[qr])) < 1e-12
+        assert np.max(np.abs(acc_l[0] - rl[:, qr])) < 1e-12
+    assert np.max(np.abs(gq - dQ)) < 1e-12
+    for t in range(p):
+        assert np.max(np.abs(gk[t] - dK[t])) < 1e-12 and np.max(np.abs(gv[t] - dV[t])) < 1e-12
+    # one step whose keys are each sequence's whole causal prefix (more key rows than
+    # query rows): the dense rows exactly
+    qc = 2
+    qr = rows(qc)
+    kr = np.concatenate([np.arange(cu[s], cu[s] + (qc + 1) * (n // nc)) for s, n in enumerate(lens)]).astype(np.int64)
+    kcu = np.concatenate([[0], np.cumsum([(qc + 1) * (n // nc) for n in lens])])
+    o, l = O.fwd_chunk_thd(q[qr], ks[0][kr], vs[0][kr], [k[qr] for k in ks[1:]], [v[qr] for v in vs[1:]], p,
+                           cu_seqlens=ccu(), kv_cu_seqlens=kcu, q_offsets=offs(qc), kv_offsets=np.zeros(len(lens)),
+                           base=base)
+    assert np.max(np.abs(o - ro[qr])) < 1e-12 and np.max(np.abs(l - rl[:, qr])) < 1e-12
+
+
 PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check_zero_query_closed_form,
         lambda: check_zero_query_closed_form("thd"), check_sdpa_brute_force, check_p1_is_causal_sdpa,
         check_merge_invariant, check_branch_relative_position, check_grad_autograd,
@@ -696,7 +749,7 @@ PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check
         check_merge_closed_form, check_block_sdpa_mask, check_block_zero_query_closed_form,
         check_block_size1_is_causal, check_block_grad_autograd, check_soft_ce_library, check_soft_ce_closed_forms,
         check_window_sdpa_and_grad, check_window_closed_forms, check_window_ring_partition, check_chunk_bwd_partition,
-        check_trunk_keys_grad_autograd, check_soft_ce_grouped_library]
+        check_trunk_keys_grad_autograd, check_soft_ce_grouped_library, check_thd_chunk_ring_partition]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
@@ -822,6 +875,8 @@ MISTAKES = [
     ("bwd_trunk_keys", _trunk_keys_late_rows),
     ("soft_ce_teacher_rows", lambda B, S, off, tr=None: np.arange(S)[None, :].repeat(B, 0) + off),
     ("soft_ce_rows_counted", _ce_counted_ignores_groups),
+    ("_thd_segments", lambda cu, kc: [(int(cu[s]), int(cu[s + 1]), int(cu[s]), int(cu[s + 1]))
+                                      for s in range(len(cu) - 1)]),
 ]
 
 
