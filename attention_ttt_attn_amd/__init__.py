@@ -58,7 +58,8 @@ class Desc(ctypes.Structure):
 
 
 class Chunk(ctypes.Structure):
-    """One ring step: query rows at q_offset.., pass-1 keys at kv_offset.. (ttt_attn_chunk)."""
+    """One ring step: query rows at q_offset.., pass-1 keys at kv_offset.. (ttt_attn_chunk); THD:
+    per-sequence offsets and packed key rows."""
     _fields_ = [
         ("struct_size", ctypes.c_uint32),
         ("with_branch", ctypes.c_int32),
@@ -66,6 +67,10 @@ class Chunk(ctypes.Structure):
         ("kv_offset", ctypes.c_int64),
         ("kv_len", ctypes.c_int64),
         ("kv0_stride", ctypes.c_int64 * 3),
+        ("q_offsets", ctypes.c_void_p),
+        ("kv_offsets", ctypes.c_void_p),
+        ("kv_cu_seqlens", ctypes.c_void_p),
+        ("max_position", ctypes.c_int64),
     ]
 
 
@@ -358,37 +363,68 @@ def bwd(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, cu_seqlens=None,
     return dq, dks, dvs
 
 
-def make_chunk(q_offset: int, kv_offset: int, k0, *, with_branch: bool) -> Chunk:
+def make_chunk(q_offset: int, kv_offset: int, k0, *, with_branch: bool, thd=None) -> Chunk:
+    """thd: None (BSHD), or (q_offsets, kv_offsets, kv_cu_seqlens, max_position) with device int32
+    tensors for the per-sequence offsets and the packed key rows."""
     c = Chunk()
     c.struct_size = ctypes.sizeof(Chunk)
     c.with_branch = int(bool(with_branch))
     c.q_offset, c.kv_offset = int(q_offset), int(kv_offset)
-    c.kv_len = k0.shape[1]
-    c.kv0_stride[:] = _strides3(k0, False)
+    if thd is None:
+        c.kv_len = k0.shape[1]
+        c.kv0_stride[:] = _strides3(k0, False)
+    else:
+        qo, ko, kcu, max_position = thd
+        for name, t in (("q_offsets", qo), ("kv_offsets", ko), ("kv_cu_seqlens", kcu)):
+            if t.dtype != _torch().int32 or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous int32 tensor")
+        c.kv_len = k0.shape[0]
+        c.kv0_stride[:] = _strides3(k0, True)
+        c.q_offsets, c.kv_offsets, c.kv_cu_seqlens = qo.data_ptr(), ko.data_ptr(), kcu.data_ptr()
+        c.max_position = int(max_position)
     return c
 
 
+def _thd_chunk(cu_seqlens, kv_cu_seqlens, q_offsets, kv_offsets, max_position):
+    if cu_seqlens is None:
+        if any(x is not None for x in (kv_cu_seqlens, q_offsets, kv_offsets)):
+            raise ValueError("kv_cu_seqlens, q_offsets and kv_offsets belong to THD (cu_seqlens) ring steps")
+        return None
+    if any(x is None for x in (kv_cu_seqlens, q_offsets, kv_offsets)):
+        raise ValueError("a THD ring step needs kv_cu_seqlens, q_offsets and kv_offsets")
+    n = cu_seqlens.numel() - 1
+    if q_offsets.numel() != n or kv_offsets.numel() != n or kv_cu_seqlens.numel() != n + 1:
+        raise ValueError("q_offsets / kv_offsets need one entry per sequence, kv_cu_seqlens one more")
+    return (q_offsets, kv_offsets, kv_cu_seqlens, max_position)
+
+
 @_on_stream
-def fwd_chunk(q, ks: Sequence, vs: Sequence, p: int, *, q_offset: int, kv_offset: int, with_branch: bool,
+def fwd_chunk(q, ks: Sequence, vs: Sequence, p: int, *, q_offset: int = 0, kv_offset: int = 0, with_branch: bool,
               softmax_scale: float = 0.0, rope_base: float = 0.0, o_fp32: bool = True, out=None, lse=None,
-              workspace=None, stream=None, window: int = 0):
-    """One ring step (BSHD, bf16): the rows of q (positions q_offset..) against the pass-1 keys ks[0], vs[0]
+              workspace=None, stream=None, window: int = 0, cu_seqlens=None, kv_cu_seqlens=None, q_offsets=None,
+              kv_offsets=None, max_position: int = 0, check_cu_seqlens: bool = False):
+    """One ring step (bf16): the rows of q (positions q_offset..) against the pass-1 keys ks[0], vs[0]
     (positions kv_offset..), plus the branch keys ks[1:p], vs[1:p] of those rows when with_branch.
-    Returns (o, lse) normalised over the keys this step sees (rows that see none: o = 0, lse = -inf)."""
+    THD (cu_seqlens): q [T, Hq, D] packs every sequence's query rows, ks[0] / vs[0] [Tk, Hkv, D] their
+    pass-1 keys (kv_cu_seqlens); sequence s takes its step at q_offsets[s] / kv_offsets[s], and every
+    position stays below max_position.  Returns (o, lse) normalised over the keys this step sees
+    (rows that see none: o = 0, lse = -inf); lse is [B, Hq, S] or [Hq, T]."""
     torch = _torch()
+    thd = _thd_chunk(cu_seqlens, kv_cu_seqlens, q_offsets, kv_offsets, max_position)
     o_dtype = DTYPE_FP32 if o_fp32 else _dtype_code(q)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32 if o_dtype == DTYPE_FP32 else q.dtype, device=q.device)
     if lse is None:
-        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+        shape = (q.shape[1], q.shape[0]) if thd else (q.shape[0], q.shape[2], q.shape[1])
+        lse = torch.empty(shape, dtype=torch.float32, device=q.device)
     branch_ks = list(ks[1:p]) if with_branch else []
     d = make_desc(q, (branch_ks or [ks[0]]), p, softmax_scale=softmax_scale, rope_base=rope_base, o_dtype=o_dtype,
-                  o_like=out, window=window)
+                  o_like=out, window=window, cu_seqlens=cu_seqlens, check_cu_seqlens=check_cu_seqlens)
     if branch_ks and any(t.stride() != branch_ks[0].stride() for t in branch_ks + list(vs[1:p])):
         raise ValueError("every branch k and v must share one set of strides")
     if vs[0].stride() != ks[0].stride():
         raise ValueError("k[0] and v[0] must share one set of strides")
-    c = make_chunk(q_offset, kv_offset, ks[0], with_branch=with_branch)
+    c = make_chunk(q_offset, kv_offset, ks[0], with_branch=with_branch, thd=thd)
     nbytes = int(library().ttt_attn_chunk_workspace_bytes(ctypes.byref(d), ctypes.byref(c)))
     if nbytes == 0:
         raise TTTAttnError(2, library().ttt_attn_last_error().decode())
@@ -401,22 +437,25 @@ def fwd_chunk(q, ks: Sequence, vs: Sequence, p: int, *, q_offset: int, kv_offset
 
 
 @_on_stream
-def bwd_chunk(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, q_offset: int, kv_offset: int,
+def bwd_chunk(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, q_offset: int = 0, kv_offset: int = 0,
               with_branch: bool, softmax_scale: float = 0.0, rope_base: float = 0.0, window: int = 0,
-              workspace=None, stream=None):
-    """Backward terms of one ring step (BSHD, bf16 inputs): o, lse, dout are the query rows'
-    whole-sequence values.  Returns fp32 (dq, [dk0, branch dk...], [dv0, branch dv...]); the
-    branch lists hold passes 2..p only with with_branch.  Summing the steps' terms gives the
-    whole-sequence gradients."""
+              workspace=None, stream=None, cu_seqlens=None, kv_cu_seqlens=None, q_offsets=None, kv_offsets=None,
+              max_position: int = 0, check_cu_seqlens: bool = False):
+    """Backward terms of one ring step (bf16 inputs; BSHD, or THD as in fwd_chunk): o, lse, dout are
+    the query rows' whole-sequence values.  Returns fp32 (dq, [dk0, branch dk...], [dv0, branch
+    dv...]); the branch lists hold passes 2..p only with with_branch.  Summing the steps' terms
+    gives the whole-sequence gradients."""
     torch = _torch()
+    thd = _thd_chunk(cu_seqlens, kv_cu_seqlens, q_offsets, kv_offsets, max_position)
     n_br = p - 1 if with_branch else 0
     branch_ks = list(ks[1:p]) if with_branch else []
     d = make_desc(q, (branch_ks or [ks[0]]), p, softmax_scale=softmax_scale, rope_base=rope_base,
-                  o_dtype=_dtype_code(o), o_like=o, window=window)
+                  o_dtype=_dtype_code(o), o_like=o, window=window, cu_seqlens=cu_seqlens,
+                  check_cu_seqlens=check_cu_seqlens)
     if dout.stride() != o.stride():
         raise ValueError("dout must have the strides of o")
-    lse = lse.contiguous()  # the C ABI reads the step rows' LSE as a dense [B, Hq, rows] array
-    c = make_chunk(q_offset, kv_offset, ks[0], with_branch=with_branch)
+    lse = lse.contiguous()  # the C ABI reads the step rows' LSE as a dense [B, Hq, rows] / [Hq, T] array
+    c = make_chunk(q_offset, kv_offset, ks[0], with_branch=with_branch, thd=thd)
 
     def like32(t):  # fp32 output with t's element strides (dense layouts keep their strides)
         return torch.empty_strided(t.shape, t.stride(), dtype=torch.float32, device=t.device)

@@ -154,8 +154,10 @@ __global__ void __launch_bounds__(256, 2)
   }
   // TTT ring steps (BSHD): row i sits at position q_off + i, trunk key j at
   // kv_off + j (j < kv_len); whole-sequence calls have dq_ = 0, kvn = L.
-  const int dq_ = (TTT_ && P.layout == 0) ? P.q_off - P.kv_off : 0;
-  const int kvn = (TTT_ && P.layout == 0) ? P.kv_len : (TTT_ ? L : P.kv_len);
+  // (THD ring steps: the segment's own offsets and key rows kvs .. kvs + kvn.)
+  int qoff = 0, dq_ = 0, kvs = start, kvn = P.kv_len;
+  if constexpr (TTT_)
+    seq_ring(P, (P.layout == 1 && P.kv_cu) ? seq_at(P.cu, P.nseq, start) : b, start, L, qoff, dq_, kvs, kvn);
   const int kmax = TTT_ ? min(qend - 1 + dq_, kvn - 1) : lim_hi - 1;  // last key any row sees
   const int nkt = kmax < 0 ? 0 : kmax / QBN + 1;
   // sliding window: the first key tile any row of the work item sees
@@ -167,7 +169,7 @@ __global__ void __launch_bounds__(256, 2)
   const _Float16* ktbase = ktt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
   // trunk V: P.cs_* strides (the pass-1 / context V; P.ks_* stay with the branch)
   const int64_t vs_t = P.cs_t;
-  const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * P.cs_b + (int64_t)start * vs_t + g * P.cs_h;
+  const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * P.cs_b + (int64_t)kvs * vs_t + g * P.cs_h;
   const int vlast = kvn - 1;  // last key row of the trunk
   uint32_t roff[2], toff[2];
   int rrow[2];
@@ -365,13 +367,13 @@ __global__ void __launch_bounds__(256, 2)
         const int rr = r16 + (tid >> 4);  // row within the work item
         const int i = row0 + rr;
         if (i >= L) continue;
-        const int pos = P.q_off + i + P.p - 1;
+        const int pos = qoff + i + P.p - 1;
         // per head: q~ as fp16 pairs and dO as its bf16 pairs (8 values each)
         u32x2 qh[RH][2], gh[RH][2];
         float lse_[RH], dl_[RH];
         {
-          const f32x4 cq = *(const f32x4*)(cosT + (int64_t)pos * 64 + flo);
-          const f32x4 sq = *(const f32x4*)(sinT + (int64_t)pos * 64 + flo);
+          const f32x4 cq = *(const f32x4*)(cosT + rope_off(P, pos) + flo);
+          const f32x4 sq = *(const f32x4*)(sinT + rope_off(P, pos) + flo);
 #pragma unroll
           for (int hw_ = 0; hw_ < RH; ++hw_) {
             const int hh = g * P.r + hw_;
@@ -406,9 +408,9 @@ __global__ void __launch_bounds__(256, 2)
           nkb = *(const u32x2*)(krow_ + fhi);
           nva = *(const u32x2*)(vrow_ + flo);
           nvb = *(const u32x2*)(vrow_ + fhi);
-          const int pk = P.q_off + i + qq - 1;
-          nck = *(const f32x4*)(cosT + (int64_t)pk * 64 + flo);
-          nsk = *(const f32x4*)(sinT + (int64_t)pk * 64 + flo);
+          const int pk = qoff + i + qq - 1;
+          nck = *(const f32x4*)(cosT + rope_off(P, pk) + flo);
+          nsk = *(const f32x4*)(sinT + rope_off(P, pk) + flo);
         };
         load_pass(2);
         for (int qq = 2; qq <= P.p; ++qq) {
@@ -513,9 +515,9 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
       for (int e = 0; e < 4; ++e) a[e] = x0[e], a[4 + e] = x1[e], a[8 + e] = y0[e], a[12 + e] = y1[e];
     }
-    const int pos = TTT_ ? P.q_off + i + P.p - 1 : block_anchor(P, b, i) + (i & ((1 << P.bs_log2) - 1));
-    const float* cq = cosT + (int64_t)pos * 64 + dlo;
-    const float* sq = sinT + (int64_t)pos * 64 + dlo;
+    const int pos = TTT_ ? qoff + i + P.p - 1 : block_anchor(P, b, i) + (i & ((1 << P.bs_log2) - 1));
+    const float* cq = cosT + rope_off(P, pos) + dlo;
+    const float* sq = sinT + rope_off(P, pos) + dlo;
     if (TTT_ && P.p > 1 && P.branch && !P.dq_branch) {
       float qr[16], go[16];
       {
@@ -543,9 +545,9 @@ __global__ void __launch_bounds__(256, 2)
         unpack_bf8(*(const u32x4*)(krow_ + dhi), x2);
         unpack_bf8(*(const u32x4*)(vrow_ + dlo), v1);
         unpack_bf8(*(const u32x4*)(vrow_ + dhi), v2);
-        const int pk = P.q_off + i + qq - 1;
-        const float* ck = cosT + (int64_t)pk * 64 + dlo;
-        const float* sk = sinT + (int64_t)pk * 64 + dlo;
+        const int pk = qoff + i + qq - 1;
+        const float* ck = cosT + rope_off(P, pk) + dlo;
+        const float* sk = sinT + rope_off(P, pk) + dlo;
         float kr[16];
         float ps = 0.f, pd = 0.f;
 #pragma unroll
@@ -638,6 +640,8 @@ __global__ void __launch_bounds__(256, 1)
   // run together share that XCD's L2 for the query rows they all stream.
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   int b, t, start, L, slot0, g;
+  int kst = 0, kln;  // this work item's keys: token rows kst .. kst + kln of the key tensors
+  int kvoff = 0, dq_ = 0;  // TTT: key j sits at kvoff + j; row i sees it iff i >= j - dq_
   const int nkeys = MODE == 3 ? P.stok : P.kv_len;  // TTT: kv_len = stok for whole-sequence calls
   if (P.layout == 0) {
     const int nkt = (nkeys + BKV - 1) / BKV;
@@ -657,12 +661,25 @@ __global__ void __launch_bounds__(256, 1)
     const int4 e = tiles[1 + tix];
     t = e.x, start = e.y, L = e.z, slot0 = e.w, b = 0;
   }
+  kln = (MODE == 2 || (TTT_ && P.layout == 0)) ? nkeys : L;
+  if constexpr (TTT_) {
+    // THD ring steps list key segments: the rows are the same segment's query rows
+    if (P.layout == 1 && P.kv_cu) {
+      const int s = seq_at(P.kv_cu, P.nseq, start);
+      int b_;
+      kst = start;
+      seq_info(P, s, b_, start, L);
+    } else {
+      kst = P.layout == 1 ? start : 0;
+    }
+    int qoff, kvs_, kvn_;
+    seq_ring(P, P.layout == 1 && P.kv_cu ? seq_at(P.kv_cu, P.nseq, kst) : b, start, L, qoff, dq_, kvs_, kvn_);
+    kvoff = qoff - dq_;
+  }
   const int kv0 = t * BKV;
   const int my_key = kv0 + wv * 32 + l32;
-  const int key_end = (MODE == 2 || (TTT_ && P.layout == 0)) ? nkeys : L;  // keys of this slab
+  const int key_end = kln;  // keys of this slab
   const bool key_ok = my_key < key_end;
-  // TTT ring steps (BSHD): row i at q_off + i sees key j at kv_off + j iff i >= j - dq_
-  const int dq_ = (TTT_ && P.layout == 0) ? P.q_off - P.kv_off : 0;
   // query rows [row_lo, row_hi) that can see this key tile
   int row_lo = TTT_ ? max(0, kv0 - dq_) & ~(BQ - 1) : kv0, row_hi = L;
   if constexpr (MODE == 3) row_hi = min(kv0 + BKV, L);
@@ -680,7 +697,7 @@ __global__ void __launch_bounds__(256, 1)
     row_lo = min(__builtin_amdgcn_readfirstlane(first) << P.bs_log2, L) & ~(BQ - 1);
   }
   // position of this lane's key (block keys: the slot position in its block)
-  int kpos = TTT_ ? P.kv_off + my_key : my_key;
+  int kpos = TTT_ ? kvoff + my_key : my_key;
   if constexpr (MODE == 3) kpos = key_ok ? block_anchor(P, b, my_key) + (my_key & ((1 << P.bs_log2) - 1)) : 0;
   if constexpr (!TTT_) {
     // every global load above has landed before the first staging load: the
@@ -693,7 +710,7 @@ __global__ void __launch_bounds__(256, 1)
   bf16x8 vf[8];
   {
     const _Float16* krow = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0 + my_key) * D;
-    const uint16_t* vrow = (const uint16_t*)kv.v[0] + b * P.ks_b + (int64_t)(start + my_key) * P.ks_t + g * P.ks_h;
+    const uint16_t* vrow = (const uint16_t*)kv.v[0] + b * P.ks_b + (int64_t)(kst + my_key) * P.ks_t + g * P.ks_h;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int d0 = c * 16 + hf * 8;
@@ -932,11 +949,11 @@ __global__ void __launch_bounds__(256, 1)
   }
   if (!key_ok) return;
   // epilogue: dK = sigma R(j)^T dK~, dV; lane owns key my_key, d = 32*d4 + 8*v4 + 4*hf + e
-  const int64_t off = b * P.ks_b + (int64_t)(start + my_key) * P.ks_t + g * P.ks_h;
+  const int64_t off = b * P.ks_b + (int64_t)(kst + my_key) * P.ks_t + g * P.ks_h;
   uint16_t* dkrow = (uint16_t*)gr.dk[0] + off;
   uint16_t* dvrow = (uint16_t*)gr.dv[0] + off;
-  const float* cp = cosT + (int64_t)kpos * 64;
-  const float* sp = sinT + (int64_t)kpos * 64;
+  const float* cp = cosT + rope_off(P, kpos);
+  const float* sp = sinT + rope_off(P, kpos);
   const float ksc = P.scale * __builtin_amdgcn_ldexpf(1.0f, -ek);  // sigma, and the dS factor undone
 #pragma unroll
   for (int d4 = 0; d4 < 2; ++d4)
@@ -983,18 +1000,19 @@ __global__ void __launch_bounds__(256)
   if (tok >= P.stok || !token_seq(P, tok, s, start, L)) return;
   const int i = tok - start, slot = seq_slot0(P, s) + i;
   const int dlo = c16 * 4, dhi = 64 + c16 * 4;
-  const int pq = P.q_off + i + P.p - 1;
-  const f32x4 cqa = *(const f32x4*)(cosT + (int64_t)pq * 64 + dlo);
-  const f32x4 sqa = *(const f32x4*)(sinT + (int64_t)pq * 64 + dlo);
+  const int qo = (P.layout == 1 && P.kv_cu) ? P.seg_qoff[s] : P.q_off;  // the row's position offset
+  const int pq = qo + i + P.p - 1;
+  const f32x4 cqa = *(const f32x4*)(cosT + rope_off(P, pq) + dlo);
+  const f32x4 sqa = *(const f32x4*)(sinT + rope_off(P, pq) + dlo);
   const int64_t koff = b * P.ks_b + (int64_t)tok * P.ks_t + g * P.ks_h;
   for (int qq = 2; qq <= P.p; ++qq) {
     const uint16_t* krow = (const uint16_t*)kv.k[qq - 1] + koff;
     const uint16_t* vrow = (const uint16_t*)kv.v[qq - 1] + koff;
     const u32x2 ka = *(const u32x2*)(krow + dlo), kb2 = *(const u32x2*)(krow + dhi);
     const u32x2 va = *(const u32x2*)(vrow + dlo), vb2 = *(const u32x2*)(vrow + dhi);
-    const int pk = P.q_off + i + qq - 1;
-    const f32x4 ck = *(const f32x4*)(cosT + (int64_t)pk * 64 + dlo);
-    const f32x4 sk = *(const f32x4*)(sinT + (int64_t)pk * 64 + dlo);
+    const int pk = qo + i + qq - 1;
+    const f32x4 ck = *(const f32x4*)(cosT + rope_off(P, pk) + dlo);
+    const f32x4 sk = *(const f32x4*)(sinT + rope_off(P, pk) + dlo);
     float kr[8], vv[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -1070,7 +1088,7 @@ void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const
                       const float* sinT, const PassGradPtrs& g, hipStream_t st) {
   const int64_t grid = P.layout == 0
                            ? (int64_t)8 * ((P.B * P.Hkv + 7) / 8) * ((P.kv_len + bwd::BKV - 1) / bwd::BKV)
-                           : (int64_t)P.Hkv * ((P.stok + bwd::BKV - 1) / bwd::BKV + P.nseq);
+                           : (int64_t)P.Hkv * (((P.kv_cu ? P.kv_tok : P.stok) + bwd::BKV - 1) / bwd::BKV + P.nseq);
   if (grid == 0) return;
   if (P.win > 0)  // sliding window: its own instantiation (MODE 4)
     bwd::dkdv_bf16_kernel<4><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);

@@ -113,6 +113,12 @@ __global__ void __launch_bounds__(256, 2)
     const int4 e = tiles[1 + tix];
     t = e.x, start = e.y, L = e.z, slot0 = e.w, b = 0;
   }
+  // Ring geometry: row i sits at position qoff + i and sees pass-1 key j
+  // (j < kv_len, staged at the work item's slots) iff j <= i + dq_; for
+  // whole-sequence calls qoff = dq_ = 0 and kv_len = L.
+  int qoff, dq_, kvs_, kv_len;
+  seq_ring(P, (P.layout == 1 && P.kv_cu) ? seq_at(P.cu, P.nseq, start) : b, start, L, qoff, dq_, kvs_, kv_len);
+  (void)kvs_;
   const int hw = wv % RH, rbk = wv / RH;
   const int h = g * P.r + sub * RH + hw;
   const int row0 = t * RT;
@@ -124,7 +130,7 @@ __global__ void __launch_bounds__(256, 2)
   {
     const bool valid = my_row < L;
     const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + my_row) * P.qs_t + h * P.qs_h;
-    const int pos = TTT_ ? P.q_off + my_row + P.p - 1
+    const int pos = TTT_ ? qoff + my_row + P.p - 1
                               : (valid ? block_anchor(P, b, my_row) + (my_row & ((1 << P.bs_log2) - 1)) : 0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -133,8 +139,8 @@ __global__ void __launch_bounds__(256, 2)
       if (valid) {
         unpack_bf8(*(const u32x4*)(qrow + d0), x1);
         unpack_bf8(*(const u32x4*)(qrow + d0 + 64), x2);
-        const f32x4* cp = (const f32x4*)(cosT + (int64_t)pos * 64 + d0);
-        const f32x4* sp = (const f32x4*)(sinT + (int64_t)pos * 64 + d0);
+        const f32x4* cp = (const f32x4*)(cosT + rope_off(P, pos) + d0);
+        const f32x4* sp = (const f32x4*)(sinT + rope_off(P, pos) + d0);
         const f32x4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
         const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
         const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
@@ -158,11 +164,6 @@ __global__ void __launch_bounds__(256, 2)
   }
 
   // ---- trunk main loop
-  // Pass-1 key j (position kv_off + j, j < kv_len) is visible to row i
-  // (position q_off + i) iff j <= i + dq_ and j < kv_len; for whole-sequence
-  // calls dq_ = 0 and kv_len = L.
-  const int dq_ = P.layout == 0 ? P.q_off - P.kv_off : 0;
-  const int kv_len = P.layout == 0 ? P.kv_len : L;
   const int qend = min(row0 + RT, L);
   // Block drafting: row i sees context keys j < lim (its block's anchor); the
   // work item's extent is the largest lim of its blocks, a wave's unmasked
@@ -417,9 +418,9 @@ __global__ void __launch_bounds__(256, 2)
       float x1[8], x2[8], y1[8], y2[8];
       unpack_bf8(kr[0], x1);
       unpack_bf8(kr[1], x2);
-      const int pk = P.q_off + i + qq - 1;
-      const float* cp = cosT + (int64_t)pk * 64 + bdlo;
-      const float* sp = sinT + (int64_t)pk * 64 + bdlo;
+      const int pk = qoff + i + qq - 1;
+      const float* cp = cosT + rope_off(P, pk) + bdlo;
+      const float* sp = sinT + rope_off(P, pk) + bdlo;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         y1[e] = x1[e] * cp[e] - x2[e] * sp[e];

@@ -66,7 +66,57 @@ struct Prob {
   float* dmax;   // [B*Hkv][2]: the same over every row of the KV group's heads
   float* vmax;   // [B*Hkv][spad/32]: per 32 trunk (block drafting: context) keys, max |v_jd|
   float* vmax_b; // block drafting: the same for the block keys
+  // THD ring steps (kv_cu set): query segment s (rows cu[s] .. cu[s+1]) sits at
+  // positions seg_qoff[s] + i and attends to pass-1 key segment s (packed rows
+  // kv_cu[s] .. kv_cu[s+1] of k[0] / v[0], kv_tok of them) at positions
+  // seg_kvoff[s] + j.  Both segments of s share the workspace slots
+  // slot_base[s] .. slot_base[s+1] (the longer of the two, rounded up to 64).
+  const int* seg_qoff;
+  const int* seg_kvoff;
+  const int* kv_cu;
+  int kv_tok;
 };
+
+// Ring geometry of one sequence (or THD segment): its query rows' position
+// offset qoff, the query-minus-key position offset dq (query row i sees key
+// j iff j <= i + dq), and its pass-1 key rows kvs .. kvs + kvn (token indices
+// of k[0] / v[0]).  start / L: the query rows.
+__device__ __forceinline__ void seq_ring(const Prob& P, int s, int start, int L, int& qoff, int& dq, int& kvs,
+                                         int& kvn) {
+  if (P.layout == 0) {
+    qoff = P.q_off, dq = P.q_off - P.kv_off, kvs = 0, kvn = P.kv_len;
+  } else if (!P.kv_cu) {
+    qoff = 0, dq = 0, kvs = start, kvn = L;
+  } else {
+    qoff = P.seg_qoff[s];
+    dq = qoff - P.seg_kvoff[s];
+    int a = P.kv_cu[s], e = P.kv_cu[s + 1];
+    a = a < 0 ? 0 : (a > P.kv_tok ? P.kv_tok : a);
+    e = e < a ? a : (e > P.kv_tok ? P.kv_tok : e);
+    kvs = a;
+    kvn = e - a;
+    const int room = P.slot_base[s + 1] - P.slot_base[s];
+    if (kvn > room) kvn = room;
+  }
+}
+
+// Element offset of position pos's row in the D = 128 RoPE table (64 angles
+// per row), clamped into the table's npos rows: THD ring steps take their
+// position offsets from device arrays the host does not read, so an offset
+// past the declared maximum gives wrong angles, never a read outside the table.
+__device__ __forceinline__ int64_t rope_off(const Prob& P, int pos) {
+  return (int64_t)(pos < 0 ? 0 : (pos >= P.npos ? P.npos - 1 : pos)) * 64;
+}
+
+// Last s with cu[s] <= tok: the sequence whose (non-empty) rows start at tok.
+__device__ __forceinline__ int seq_at(const int* cu, int nseq, int tok) {
+  int lo = 0, hi = nseq;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= tok) lo = mid; else hi = mid;
+  }
+  return lo;
+}
 
 // Exponent e of the power-of-two factor 2^e applied to fp16 dS operands whose
 // magnitude is bounded by x: |dS 2^e| <= x 2^e < 2^15 < 65504 (fp16 max), and
@@ -133,10 +183,12 @@ __device__ __forceinline__ bool token_seq(const Prob& P, int tok, int& s, int& s
   return tok >= start && tok < start + L;
 }
 
-// Sequence owning workspace slot `slot`; tok is its token when the slot holds one.
-__device__ __forceinline__ bool slot_token(const Prob& P, int slot, int& tok, int& row) {
+// Sequence owning workspace slot `slot`; tok is its token when the slot holds
+// one, seq the sequence (THD).
+__device__ __forceinline__ bool slot_token(const Prob& P, int slot, int& tok, int& row, int* seq = nullptr) {
   if (P.layout == 0) {
     tok = row = slot;
+    if (seq) *seq = 0;
     return slot < P.stok;
   }
   int lo = 0, hi = P.nseq;  // last s with slot_base[s] <= slot
@@ -149,6 +201,7 @@ __device__ __forceinline__ bool slot_token(const Prob& P, int slot, int& tok, in
   seq_info(P, lo, b_, start, L);
   row = slot - P.slot_base[lo];
   tok = start + row;
+  if (seq) *seq = lo;
   return row < L;
 }
 

@@ -146,21 +146,40 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
   if (c) {
     if (c->struct_size != sizeof(ttt_attn_chunk))
       return fail(TTT_ERR_ABI, "chunk struct_size %u != %zu", c->struct_size, sizeof(ttt_attn_chunk));
-    if (d->layout != TTT_LAYOUT_BSHD) return fail(TTT_ERR_UNSUPPORTED, "ring steps take the BSHD layout");
     if (d->dtype != TTT_DTYPE_BF16) return fail(TTT_ERR_UNSUPPORTED, "ring steps are built for bf16");
     if (c->q_offset < 0 || c->kv_offset < 0 || c->kv_len < 0)
       return fail(TTT_ERR_BAD_SHAPE, "q_offset %lld, kv_offset %lld and kv_len %lld must be >= 0",
                   (long long)c->q_offset, (long long)c->kv_offset, (long long)c->kv_len);
-    if (c->q_offset + stok + p > ((int64_t)1 << 30) || c->kv_offset + c->kv_len > ((int64_t)1 << 30))
-      return fail(TTT_ERR_BAD_SHAPE, "positions past 2^30");
-    P.q_off = (int)c->q_offset;
-    P.kv_off = (int)c->kv_offset;
-    P.kv_len = (int)c->kv_len;
     P.branch = c->with_branch != 0;
-    const int rows = stok > P.kv_len ? stok : P.kv_len;
-    P.spad = ((rows + 63) / 64) * 64 + 64;
-    const int64_t qend = c->q_offset + stok + p - 1, kend = c->kv_offset + c->kv_len;
-    P.npos = (int)(qend > kend ? qend : kend);
+    if (d->layout == TTT_LAYOUT_BSHD) {
+      if (c->q_offsets || c->kv_offsets || c->kv_cu_seqlens || c->max_position)
+        return fail(TTT_ERR_BAD_SHAPE, "BSHD ring steps take q_offset / kv_offset; the THD fields must be NULL / 0");
+      if (c->q_offset + stok + p > ((int64_t)1 << 30) || c->kv_offset + c->kv_len > ((int64_t)1 << 30))
+        return fail(TTT_ERR_BAD_SHAPE, "positions past 2^30");
+      P.q_off = (int)c->q_offset;
+      P.kv_off = (int)c->kv_offset;
+      P.kv_len = (int)c->kv_len;
+      const int rows = stok > P.kv_len ? stok : P.kv_len;
+      P.spad = ((rows + 63) / 64) * 64 + 64;
+      const int64_t qend = c->q_offset + stok + p - 1, kend = c->kv_offset + c->kv_len;
+      P.npos = (int)(qend > kend ? qend : kend);
+    } else {
+      if (!c->q_offsets || !c->kv_offsets || !c->kv_cu_seqlens)
+        return fail(TTT_ERR_NULL_ARG, "THD ring steps need q_offsets, kv_offsets and kv_cu_seqlens");
+      if (c->q_offset != 0 || c->kv_offset != 0)
+        return fail(TTT_ERR_BAD_SHAPE, "THD ring steps take per-sequence offsets: q_offset and kv_offset must be 0");
+      if (c->max_position < 1 || c->max_position > ((int64_t)1 << 30))
+        return fail(TTT_ERR_BAD_SHAPE, "max_position %lld outside 1..2^30", (long long)c->max_position);
+      if ((int64_t)stok + c->kv_len + 128 + 64 * (int64_t)nseq > (int64_t)1 << 30)
+        return fail(TTT_ERR_BAD_SHAPE, "too many query (%d) and key (%lld) rows", stok, (long long)c->kv_len);
+      P.kv_len = P.kv_tok = (int)c->kv_len;
+      P.kv_cu = c->kv_cu_seqlens;
+      P.seg_qoff = c->q_offsets;
+      P.seg_kvoff = c->kv_offsets;
+      // a sequence's query and key rows share its slots: the longer of the two, rounded up to 64
+      P.spad = ((stok + P.kv_len + 63) / 64) * 64 + 64 + 64 * nseq;
+      P.npos = (int)c->max_position;
+    }
   }
   if (int e = check_slab_offsets(P)) return e;
   if (d->window < 0) return fail(TTT_ERR_BAD_SHAPE, "window %d is negative", d->window);
@@ -199,7 +218,7 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
   if (c) {
     const int64_t* s0 = c->kv0_stride;
     if (s0[0] == 0 && s0[1] == 0 && s0[2] == 0) {
-      pl.k0s_b = (int64_t)P.kv_len * Hkv * D, pl.k0s_t = (int64_t)Hkv * D, pl.k0s_h = D;
+      pl.k0s_b = thd ? 0 : (int64_t)P.kv_len * Hkv * D, pl.k0s_t = (int64_t)Hkv * D, pl.k0s_h = D;
     } else {
       if (int e = strides(s0, Hkv, tmp, "kv0", ea)) return e;
       pl.k0s_b = tmp[0], pl.k0s_t = tmp[1], pl.k0s_h = tmp[2];
@@ -231,7 +250,7 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
   };
   const size_t nkv = (size_t)B * Hkv * P.spad * D, nq = (size_t)B * Hq * P.spad * D;
   pl.max_tiles_q = thd ? (stok + ttt::kFwdMinRows - 1) / ttt::kFwdMinRows + nseq + 1 : 0;
-  pl.max_tiles_kv = thd ? (stok + ttt::kBwdBKV - 1) / ttt::kBwdBKV + nseq + 1 : 0;
+  pl.max_tiles_kv = thd ? (P.kv_len + ttt::kBwdBKV - 1) / ttt::kBwdBKV + nseq + 1 : 0;  // kv_len = stok unless a THD ring step
   w.table = take((size_t)2 * P.npos * (D / 2) * sizeof(float));
   if (thd) w.slots = take((size_t)(nseq + 1) * sizeof(int));
   if (bf16) {
@@ -272,18 +291,24 @@ int check_ws(const Plan& pl, const void* ws, size_t ws_bytes) {
   return 0;
 }
 
-int check_cu(const ttt_attn_desc* d, hipStream_t st) {
-  if (d->layout != TTT_LAYOUT_THD || !d->check_cu_seqlens) return 0;
-  std::vector<int32_t> cu(d->num_seqs + 1);
-  hipError_t e = hipMemcpyAsync(cu.data(), d->cu_seqlens, cu.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+int check_cu_array(const int32_t* dev, int nseq, int64_t total, const char* name, hipStream_t st) {
+  std::vector<int32_t> cu(nseq + 1);
+  hipError_t e = hipMemcpyAsync(cu.data(), dev, cu.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return fail(TTT_ERR_HIP, "reading cu_seqlens: %s", hipGetErrorString(e));
-  if (cu[0] != 0) return fail(TTT_ERR_BAD_SHAPE, "cu_seqlens[0] = %d, expected 0", cu[0]);
-  for (int s = 0; s < d->num_seqs; ++s)
-    if (cu[s + 1] < cu[s]) return fail(TTT_ERR_BAD_SHAPE, "cu_seqlens decreases at %d (%d > %d)", s, cu[s], cu[s + 1]);
-  if (cu[d->num_seqs] != d->seqlen)
-    return fail(TTT_ERR_BAD_SHAPE, "cu_seqlens[%d] = %d, expected total tokens %d", d->num_seqs, cu[d->num_seqs],
-                d->seqlen);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "reading %s: %s", name, hipGetErrorString(e));
+  if (cu[0] != 0) return fail(TTT_ERR_BAD_SHAPE, "%s[0] = %d, expected 0", name, cu[0]);
+  for (int s = 0; s < nseq; ++s)
+    if (cu[s + 1] < cu[s]) return fail(TTT_ERR_BAD_SHAPE, "%s decreases at %d (%d > %d)", name, s, cu[s], cu[s + 1]);
+  if (cu[nseq] != total)
+    return fail(TTT_ERR_BAD_SHAPE, "%s[%d] = %d, expected %lld rows", name, nseq, cu[nseq], (long long)total);
+  return 0;
+}
+
+// With check_cu_seqlens (THD): cu_seqlens, and a THD ring step's kv_cu_seqlens.
+int check_cu(const ttt_attn_desc* d, hipStream_t st, const ttt_attn_chunk* c = nullptr) {
+  if (d->layout != TTT_LAYOUT_THD || !d->check_cu_seqlens) return 0;
+  if (int e = check_cu_array(d->cu_seqlens, d->num_seqs, d->seqlen, "cu_seqlens", st)) return e;
+  if (c) return check_cu_array(c->kv_cu_seqlens, d->num_seqs, c->kv_len, "kv_cu_seqlens", st);
   return 0;
 }
 
@@ -439,7 +464,7 @@ int fwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
   }
   if (int e = check_ws(pl, ws, ws_bytes)) return e;
   hipStream_t st = (hipStream_t)stream;
-  if (int e = check_cu(d, st)) return e;
+  if (int e = check_cu(d, st, c)) return e;
   (void)hipGetLastError();
 
   float* cosT = at<float>(ws, pl.ws.table);
@@ -474,6 +499,8 @@ int fwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, nullptr, 0, nullptr, 0};
     J.j[1] = {(const uint16_t*)v[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, 0, 0, 0, nullptr, (uint16_t*)vt, 0,
               nullptr, 0};  // V^T in fp16: the PV product's operand
+    if (P.kv_cu)  // THD ring step: the packed key rows of each sequence, at its own key offset
+      for (int j = 0; j < 2; ++j) J.j[j].cu = P.kv_cu, J.j[j].ntok = P.kv_tok, J.j[j].seg_pos = j ? nullptr : P.seg_kvoff;
     TTT_TRACED("prep_kv", ttt::launch_prep_bf16(Pk, J, cosT, sinT, st));
     TTT_TRACED("trunk_fwd",
                ttt::launch_fwd_bf16(P, (const uint16_t*)q, kv, kt, vt, tiles, cosT, sinT, o, pl.o_f32, lse, st));
@@ -944,7 +971,7 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
   }
   if (int e = check_ws(pl, ws, ws_bytes)) return e;
   hipStream_t st = (hipStream_t)stream;
-  if (int e = check_cu(d, st)) return e;
+  if (int e = check_cu(d, st, c)) return e;
   (void)hipGetLastError();
 
   float* cosT = at<float>(ws, pl.ws.table);
@@ -960,7 +987,9 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
       int4* a = at<int4>(ws, pl.ws.tiles_q);
       int4* b = at<int4>(ws, pl.ws.tiles_kv);
       TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::dq_tile_rows(P.r), 1, a, pl.max_tiles_q, slots, st));
-      TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kBwdBKV, 0, b, pl.max_tiles_kv, nullptr, st));
+      ttt::Prob Pkv = P;  // key tiles: a THD ring step's packed key rows, on the slots laid out above
+      if (P.kv_cu) Pkv.cu = P.kv_cu, Pkv.stok = P.kv_tok;
+      TTT_TRACED("tile_sched", ttt::launch_tile_sched(Pkv, ttt::kBwdBKV, 0, b, pl.max_tiles_kv, nullptr, st));
       tq = a;
       tkv = b;
     } else {
@@ -1000,6 +1029,10 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, (uint16_t*)ktt, 0,
               nullptr, krows};
     J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.q_off + P.p - 1, 1, 0, qt, nullptr, 0, nullptr, 0};
+    if (P.kv_cu) {  // THD ring step: per-sequence key rows and offsets
+      J.j[0].cu = P.kv_cu, J.j[0].ntok = P.kv_tok, J.j[0].seg_pos = P.seg_kvoff;
+      J.j[1].seg_pos = P.seg_qoff;
+    }
     J.heads_fast = 1;  // mostly row-major outputs (Q~ rows)
     TTT_TRACED("prep_kq", ttt::launch_prep_bf16(P, J, cosT, sinT, st));
     if (forked) sd.wait(st, delta_done);

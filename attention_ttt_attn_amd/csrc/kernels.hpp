@@ -22,6 +22,9 @@ struct PrepJob {
   int pos_anchor;
   int* out_lim;  // pos_anchor jobs: per slot [(b)][spad] the clamped anchor of the row's block (0 past the end)
   int rows;      // BSHD: rows of this tensor when they differ from the Prob's (0: P.stok, < 0: none)
+  const int* cu; // THD: this tensor's own cu_seqlens (ntok rows) on the Prob's slots, or null (the Prob's)
+  int ntok;
+  const int* seg_pos;  // THD: per-sequence position offset added to every row's, or null
 };
 struct PrepJobs {
   PrepJob j[2];

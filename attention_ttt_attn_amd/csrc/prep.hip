@@ -138,13 +138,18 @@ __global__ void __launch_bounds__(256) prep_bf16_kernel(Prob P, PrepJobs J, cons
   for (int pass = 0; pass < 2; ++pass) {
     const int lr = pass * 32 + rr, slot = tok0 + lr;
     float a[8], c[8];
-    int tok, row;
+    int tok, row, sq = 0;
     bool valid;
     if (jb.rows != 0 && P.layout == 0) {  // jb.rows < 0: an empty tensor
       tok = row = slot;
       valid = slot < jb.rows;
+    } else if (jb.cu) {  // a THD tensor with its own sequence lengths on the shared slots
+      Prob Pj = P;
+      Pj.cu = jb.cu;
+      Pj.stok = jb.ntok;
+      valid = slot_token(Pj, slot, tok, row, &sq);
     } else {
-      valid = slot_token(P, slot, tok, row);
+      valid = slot_token(P, slot, tok, row, &sq);
     }
     if (jb.out_lim && h == 0 && c8 == 0) jb.out_lim[(int64_t)b * P.spad + slot] = valid ? block_anchor(P, b, row) : 0;
     if (valid) {
@@ -152,8 +157,9 @@ __global__ void __launch_bounds__(256) prep_bf16_kernel(Prob P, PrepJobs J, cons
       unpack_bf8(*(const u32x4*)src, a);
       unpack_bf8(*(const u32x4*)(src + HALF), c);
       if (jb.rot) {
-        const int pos = jb.pos_anchor ? block_anchor(P, b, row) + (row & ((1 << P.bs_log2) - 1)) : row + jb.pos_off;
-        const int64_t t = (int64_t)pos * HALF + 8 * c8;
+        const int pos = jb.pos_anchor ? block_anchor(P, b, row) + (row & ((1 << P.bs_log2) - 1))
+                                      : row + jb.pos_off + (jb.seg_pos ? jb.seg_pos[sq] : 0);
+        const int64_t t = rope_off(P, pos) + 8 * c8;
         const f32x4 c0 = *(const f32x4*)(cosT + t), c1 = *(const f32x4*)(cosT + t + 4);
         const f32x4 s0 = *(const f32x4*)(sinT + t), s1 = *(const f32x4*)(sinT + t + 4);
 #pragma unroll
@@ -331,7 +337,16 @@ __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int 
   if (slot_base) {
     for (int s0 = 0; s0 < P.nseq; s0 += 1024) {
       int s = s0 + tid, a, w = 0;
-      if (s < P.nseq) w = (raw_len(s, a) + 63) & ~63;
+      if (s < P.nseq) {
+        int len = raw_len(s, a);
+        if (P.kv_cu) {  // THD ring step: the segment's keys share its slots
+          int ka = P.kv_cu[s], ke = P.kv_cu[s + 1];
+          ka = ka < 0 ? 0 : (ka > P.kv_tok ? P.kv_tok : ka);
+          ke = ke < ka ? ka : (ke > P.kv_tok ? P.kv_tok : ke);
+          len = max(len, ke - ka);
+        }
+        w = (len + 63) & ~63;
+      }
       int inc = block_scan(w);
       if (s < P.nseq) {
         int lo = s_base + inc - w;

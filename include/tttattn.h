@@ -179,17 +179,35 @@ int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, co
  *   v[q] (q >= 1) hold for the query rows (d->seqlen rows, positions
  *   q_offset + i + q); a sequence's ring folds them in exactly once.
  * Output: O normalised over the keys this step sees and its LSE; a row that
- * sees no key gets O = 0 and LSE = -inf.  BSHD and dtype bf16 only; every
- * batch row uses the same offsets. */
+ * sees no key gets O = 0 and LSE = -inf.  dtype bf16 only.
+ * BSHD: every batch row uses the same offsets (q_offset, kv_offset); the
+ * THD fields below are NULL / 0.
+ * THD (packed sequences, d->cu_seqlens): every sequence s takes its own ring
+ * step.  Its query rows cu_seqlens[s] .. cu_seqlens[s+1] of q sit at
+ * positions q_offsets[s] + i, its pass-1 key rows kv_cu_seqlens[s] ..
+ * kv_cu_seqlens[s+1] of k[0] / v[0] at kv_offsets[s] + j (same visibility
+ * rule); sequences never see each other.  q_offset = kv_offset = 0, kv_len =
+ * kv_cu_seqlens[num_seqs] (the packed key rows), and every position the call
+ * touches (q_offsets[s] + rows + p - 1, kv_offsets[s] + keys) must be below
+ * max_position, which sizes the RoPE table (positions past it get the angles
+ * of max_position - 1: wrong values, never an access outside the table).
+ * The three arrays are device int32 arrays the kernels read; the host reads
+ * kv_cu_seqlens only with d->check_cu_seqlens (then it must start at 0, not
+ * decrease and end at kv_len). */
 typedef struct ttt_attn_chunk {
   uint32_t struct_size;       /* = sizeof(ttt_attn_chunk)                                  */
   int32_t with_branch;        /* non-zero: fold in the branch keys of passes 2..p         */
-  int64_t q_offset;           /* position of query row 0 in the sequence                  */
-  int64_t kv_offset;          /* position of pass-1 key 0 in the sequence                 */
-  int64_t kv_len;             /* rows of k[0] / v[0]                                      */
+  int64_t q_offset;           /* BSHD: position of query row 0 in the sequence            */
+  int64_t kv_offset;          /* BSHD: position of pass-1 key 0 in the sequence           */
+  int64_t kv_len;             /* rows of k[0] / v[0] (THD: packed rows of every sequence) */
   int64_t kv0_stride[3];      /* batch, token, head strides of k[0] / v[0] (elements); a
                                  zero triple selects the contiguous default [B, kv_len,
-                                 Hkv, D]; kv_stride applies to k[q], v[q], q >= 1          */
+                                 Hkv, D] ([kv_len, Hkv, D] in THD); kv_stride applies to
+                                 k[q], v[q], q >= 1                                        */
+  const int32_t* q_offsets;     /* THD: device [num_seqs], query row 0's position per sequence */
+  const int32_t* kv_offsets;    /* THD: device [num_seqs], pass-1 key 0's position           */
+  const int32_t* kv_cu_seqlens; /* THD: device [num_seqs + 1], packed pass-1 key rows        */
+  int64_t max_position;         /* THD: bound on every position of the call (>= 1)          */
 } ttt_attn_chunk;
 
 /* Bytes of workspace ttt_attn_fwd_chunk needs (0 and the last error if invalid). */
@@ -210,7 +228,9 @@ int ttt_attn_fwd_chunk(const ttt_attn_desc* d, const ttt_attn_chunk* c, const vo
  *                  dk[q] / dv[q] (q >= 1) the branch keys' gradients of the rows
  *                  (kv_stride)
  * Outputs are overwritten (not accumulated); summing every step's terms gives
- * the whole-sequence gradients.  BSHD, bf16 inputs.  Workspace:
+ * the whole-sequence gradients.  BSHD or THD (as for the forward), bf16
+ * inputs; in THD, pass-1 keys of a sequence without query rows get zero
+ * terms, and the LSE is [Hq][total query rows].  Workspace:
  * ttt_attn_chunk_bwd_workspace_bytes. */
 size_t ttt_attn_chunk_bwd_workspace_bytes(const ttt_attn_desc* d, const ttt_attn_chunk* c);
 int ttt_attn_bwd_chunk(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, const void* const* k,

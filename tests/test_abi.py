@@ -207,9 +207,42 @@ def call_chunk(d, c, q=FAKE, k=None, v=None, o=FAKE, lse=FAKE, ws=FAKE, ws_bytes
 
 
 def test_chunk_struct_matches_header():
-    assert ctypes.sizeof(tk.Chunk) == 56
+    assert ctypes.sizeof(tk.Chunk) == 88
     text = open(os.path.join(ROOT, "include", "tttattn.h")).read()
     assert "ttt_attn_chunk" in text and "kv0_stride[3]" in text
+    for f in ("q_offsets", "kv_offsets", "kv_cu_seqlens", "max_position"):
+        assert f in text
+
+
+def thd_chunk(kv_len=300, max_position=5000):
+    c = good_chunk(q_offset=0, kv_offset=0, kv_len=kv_len)
+    c.q_offsets, c.kv_offsets, c.kv_cu_seqlens = FAKE, FAKE + 256, FAKE + 512
+    c.max_position = max_position
+    return c
+
+
+def test_thd_chunk_validation():
+    lib = tk.library()
+    d = good_desc(layout=tk.LAYOUT_THD)
+    w = lambda c: lib.ttt_attn_chunk_workspace_bytes(ctypes.byref(d), ctypes.byref(c))
+    assert w(thd_chunk()) > 0
+    for f in ("q_offsets", "kv_offsets", "kv_cu_seqlens"):
+        c = thd_chunk()
+        setattr(c, f, None)
+        assert call_chunk(d, c) == 1 and "kv_cu_seqlens" in err()
+    c = thd_chunk()
+    c.q_offset = 5
+    assert call_chunk(d, c) == 2 and "per-sequence" in err()
+    for mp in (0, (1 << 30) + 1):
+        assert call_chunk(d, thd_chunk(max_position=mp)) == 2 and "max_position" in err()
+    assert call_chunk(d, thd_chunk(kv_len=1 << 30)) == 2 and "key" in err()
+    # BSHD ring steps refuse the THD fields
+    c = good_chunk()
+    c.kv_cu_seqlens = FAKE
+    assert call_chunk(good_desc(), c) == 2 and "THD fields" in err()
+    # the workspace holds both row sets and the RoPE table of max_position rows
+    assert w(thd_chunk(kv_len=4096)) > w(thd_chunk(kv_len=64))
+    assert w(thd_chunk(max_position=100000)) > w(thd_chunk(max_position=5000))
 
 
 def test_chunk_validation():
@@ -219,7 +252,7 @@ def test_chunk_validation():
     c = good_chunk()
     c.struct_size = 8
     assert call_chunk(d, c) == 7 and "struct_size" in err()
-    assert call_chunk(good_desc(layout=tk.LAYOUT_THD), good_chunk()) == 3 and "BSHD" in err()
+    assert call_chunk(good_desc(layout=tk.LAYOUT_THD), good_chunk(q_offset=0)) == 1 and "THD" in err()
     assert call_chunk(good_desc(dtype=tk.DTYPE_FP32), good_chunk()) == 3 and "bf16" in err()
     for q_off, kv_off, kv_len in ((-1, 0, 10), (0, -64, 10), (0, 0, -1)):
         assert call_chunk(d, good_chunk(q_off, kv_off, kv_len)) == 2 and ">= 0" in err()
@@ -451,8 +484,12 @@ def test_chunk_bwd_validation():
     assert lib.ttt_attn_chunk_bwd_workspace_bytes(ctypes.byref(d), ctypes.byref(good_chunk())) > \
         lib.ttt_attn_chunk_workspace_bytes(ctypes.byref(d), ctypes.byref(good_chunk()))
     dt = good_desc(layout=tk.LAYOUT_THD)
-    assert lib.ttt_attn_bwd_chunk(ctypes.byref(dt), ctypes.byref(good_chunk()), FAKE, ptrs(3), ptrs(3), FAKE, FAKE,
-                                  FAKE, FAKE, ptrs(3), ptrs(3), FAKE, 1 << 40, None) == 3
+    assert lib.ttt_attn_bwd_chunk(ctypes.byref(dt), ctypes.byref(good_chunk(q_offset=0)), FAKE, ptrs(3), ptrs(3),
+                                  FAKE, FAKE, FAKE, FAKE, ptrs(3), ptrs(3), FAKE, 1 << 40, None) == 1
+    assert "kv_cu_seqlens" in err()
+    # a THD ring step stops at the (too small) workspace once its arguments pass
+    assert lib.ttt_attn_bwd_chunk(ctypes.byref(dt), ctypes.byref(thd_chunk()), FAKE, ptrs(3), ptrs(3), FAKE, FAKE,
+                                  FAKE, FAKE, ptrs(3), ptrs(3), FAKE, 16, None) == 5
 
 
 def test_token_stride_limit():
