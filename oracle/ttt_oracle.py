@@ -52,7 +52,11 @@ What is computed (one call = one TTT pass p, 1-based):
   block sees the context keys at positions j < a_n and all bs keys of its own
   block, rotated at their positions.  `block_fwd` returns O and LSE per slot;
   `block_bwd` the gradients of q, the context K/V and the block K/V by the
-  same chain rule as the TTT backward below.
+  same chain rule as the TTT backward below.  Packed (THD) block drafting,
+  `block_fwd_thd` / `block_bwd_thd`: every sequence holds whole blocks and has
+  its own context (issue above, item 4: the block-draft attention on the THD
+  layout); sequences never see each other and anchors clamp to the
+  sequence's own context.
 
 * Distillation loss (issue above, item 3: chunked soft cross-entropy, normalised
   per pass over the whole batch; PR #3725 self-review: teacher_offset =
@@ -102,7 +106,7 @@ __all__ = ["inv_freq", "rotate_half", "unrotate_half", "query_position", "key_po
            "ttt_mask_row", "trunk_window_start", "sequences", "fwd", "bwd", "fwd_rows", "fwd_group_rows", "bwd_rows",
            "bwd_trunk_keys", "Slice",
            "fwd_chunk", "bwd_chunk", "fwd_chunk_thd", "bwd_chunk_thd", "merge", "ring_visible", "block_visible_ctx", "block_fwd_rows", "block_fwd",
-           "block_bwd_rows", "block_bwd", "soft_ce_rows_counted", "soft_ce_teacher_rows", "soft_ce", "soft_ce_grouped"]
+           "block_bwd_rows", "block_bwd", "block_fwd_thd", "block_bwd_thd", "soft_ce_rows_counted", "soft_ce_teacher_rows", "soft_ce", "soft_ce_grouped"]
 
 
 # ----------------------------------------------------------------------------- RoPE
@@ -730,6 +734,57 @@ def block_bwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, dout, *, scale: O
             dVc[b, :, h // r] += dvc
             dKb[b, :, h // r] += dkb
             dVb[b, :, h // r] += dvb
+    return dQ, dKc, dVc, dKb, dVb
+
+
+def _block_thd_segments(cu_seqlens, ctx_cu_seqlens, bs: int):
+    cu = [int(x) for x in cu_seqlens]
+    cc = [int(x) for x in ctx_cu_seqlens]
+    if len(cu) != len(cc):
+        raise ValueError("cu_seqlens and ctx_cu_seqlens must list the same sequences")
+    if any(x % bs for x in cu):
+        raise ValueError("every sequence holds whole blocks")
+    return [(cu[s], cu[s + 1], cc[s], cc[s + 1]) for s in range(len(cu) - 1)]
+
+
+def block_fwd_thd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, *, cu_seqlens, ctx_cu_seqlens,
+                  scale: Optional[float] = None, base: float = 0.0):
+    """Packed (THD) block drafting: q, k_blk, v_blk [T, H, D] hold every sequence's block
+    rows (cu_seqlens, whole blocks each), k_ctx, v_ctx [Tc, Hkv, D] their contexts
+    (ctx_cu_seqlens), anchors [T / bs] one per block in packed order.  Sequence s is
+    block_fwd of its own rows, context and anchors (clamped to its own context length).
+    Returns (O [T, Hq, D], LSE [Hq, T])."""
+    T, Hq, D = q.shape
+    O = np.zeros((T, Hq, D))
+    lse = np.full((Hq, T), -np.inf)
+    anchors = np.asarray(anchors)
+    for a, e, ca, ce in _block_thd_segments(cu_seqlens, ctx_cu_seqlens, bs):
+        if e == a:
+            continue
+        o, l = block_fwd(np.asarray(q)[None, a:e], np.asarray(k_ctx)[None, ca:ce], np.asarray(v_ctx)[None, ca:ce],
+                         np.asarray(k_blk)[None, a:e], np.asarray(v_blk)[None, a:e], anchors[None, a // bs:e // bs],
+                         bs, scale=scale, base=base)
+        O[a:e] = o[0]
+        lse[:, a:e] = l[0]
+    return O, lse
+
+
+def block_bwd_thd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, bs: int, dout, *, cu_seqlens, ctx_cu_seqlens,
+                  scale: Optional[float] = None, base: float = 0.0):
+    """Backward of block_fwd_thd: each sequence's block_bwd.  Returns (dQ [T, Hq, D],
+    dK_ctx, dV_ctx [Tc, Hkv, D], dK_blk, dV_blk [T, Hkv, D]); context rows of a sequence
+    without block rows get zeros."""
+    dQ = np.zeros(np.shape(q))
+    dKc, dVc = np.zeros(np.shape(k_ctx)), np.zeros(np.shape(v_ctx))
+    dKb, dVb = np.zeros(np.shape(k_blk)), np.zeros(np.shape(v_blk))
+    anchors = np.asarray(anchors)
+    for a, e, ca, ce in _block_thd_segments(cu_seqlens, ctx_cu_seqlens, bs):
+        if e == a:
+            continue
+        r = block_bwd(np.asarray(q)[None, a:e], np.asarray(k_ctx)[None, ca:ce], np.asarray(v_ctx)[None, ca:ce],
+                      np.asarray(k_blk)[None, a:e], np.asarray(v_blk)[None, a:e], anchors[None, a // bs:e // bs], bs,
+                      np.asarray(dout)[None, a:e], scale=scale, base=base)
+        dQ[a:e], dKc[ca:ce], dVc[ca:ce], dKb[a:e], dVb[a:e] = (x[0] for x in r)
     return dQ, dKc, dVc, dKb, dVb
 
 

@@ -477,6 +477,59 @@ def check_block_grad_autograd():
         assert np.max(np.abs(mine[0] - t.grad.numpy())) < 1e-10
 
 
+def _block_torch_ref(q, kc, vc, kb, vb, anchors, bs, scale, base):
+    """One sequence, torch fp64 with autograd: SDPA over [context ; block] keys rotated at
+    their positions with the explicit block mask; anchors clamped to [0, ctx_len]."""
+    N, Hq, _ = q.shape
+    ctx_len, Hkv = kc.shape[0], kc.shape[1]
+    T = [torch.tensor(x, requires_grad=True) for x in (q, kc, vc, kb, vb)]
+    tq, tkc, tvc, tkb, tvb = T
+    anc = torch.tensor([min(max(int(anchors[i // bs]), 0), ctx_len) for i in range(N)])
+    slot_pos = anc + torch.arange(N) % bs
+    keys = torch.cat([rope_complex(tkc, torch.arange(ctx_len)[:, None].expand(ctx_len, Hkv), base),
+                      rope_complex(tkb, slot_pos[:, None].expand(N, Hkv), base)], 0)
+    vals = torch.cat([tvc, tvb], 0)
+    rows = torch.arange(N)
+    mask = torch.cat([torch.arange(ctx_len)[None, :] < anc[:, None], (rows[None, :] // bs) == (rows[:, None] // bs)], 1)
+    r = Hq // Hkv
+    qh = rope_complex(tq, slot_pos[:, None].expand(N, Hq), base).permute(1, 0, 2)
+    kh = keys.permute(1, 0, 2).repeat_interleave(r, 0)
+    vh = vals.permute(1, 0, 2).repeat_interleave(r, 0)
+    out = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask, scale=scale).permute(1, 0, 2)
+    lse = torch.logsumexp(((qh @ kh.transpose(-1, -2)) * scale).masked_fill(~mask, -math.inf), dim=-1)
+    return out, lse, T
+
+
+def check_block_thd_sdpa_and_grad():
+    """Packed (THD) block drafting: three sequences with their own block counts, contexts
+    (one empty) and anchors (some past the context, one negative) == per-sequence torch SDPA
+    with the explicit block mask, forward and fp64 autograd gradients."""
+    bs, Hq, Hkv, D, base = 4, 4, 2, 8, 1e4
+    scale = 1 / math.sqrt(D)
+    nblks, ctxs = [2, 3, 1], [7, 0, 12]
+    cu = np.concatenate([[0], np.cumsum(nblks)]) * bs
+    cc = np.concatenate([[0], np.cumsum(ctxs)])
+    rng = np.random.default_rng(89)
+    T, Tc = int(cu[-1]), int(cc[-1])
+    q = rng.standard_normal((T, Hq, D))
+    kb, vb = rng.standard_normal((T, Hkv, D)), rng.standard_normal((T, Hkv, D))
+    kc, vc = rng.standard_normal((Tc, Hkv, D)), rng.standard_normal((Tc, Hkv, D))
+    dout = rng.standard_normal((T, Hq, D))
+    anchors = np.array([3, 9, 0, 2, -1, 12])               # 9 > 7 and 2 > 0 clamp; -1 -> 0
+    geo = dict(cu_seqlens=cu, ctx_cu_seqlens=cc, base=base)
+    o, lse = O.block_fwd_thd(q, kc, vc, kb, vb, anchors, bs, **geo)
+    dq, dkc, dvc, dkb, dvb = O.block_bwd_thd(q, kc, vc, kb, vb, anchors, bs, dout, **geo)
+    for s in range(3):
+        a, e, ca, ce = int(cu[s]), int(cu[s + 1]), int(cc[s]), int(cc[s + 1])
+        ro, rl, Ts = _block_torch_ref(q[a:e], kc[ca:ce], vc[ca:ce], kb[a:e], vb[a:e], anchors[a // bs:e // bs], bs,
+                                      scale, base)
+        assert np.max(np.abs(o[a:e] - ro.detach().numpy())) < 1e-12
+        assert np.max(np.abs(lse[:, a:e] - rl.detach().numpy())) < 1e-12
+        (ro * torch.tensor(dout[a:e])).sum().backward()
+        for mine, t in zip((dq[a:e], dkc[ca:ce], dvc[ca:ce], dkb[a:e], dvb[a:e]), Ts):
+            assert mine.shape == t.shape and (mine.size == 0 or np.max(np.abs(mine - t.grad.numpy())) < 1e-10)
+
+
 def check_soft_ce_library():
     """Row cross-entropies == torch cross_entropy with probability targets; the gradient
     == fp64 autograd of the mean over counted rows; offset and mask select the rows."""
@@ -749,7 +802,8 @@ PINS = [check_rope_complex_form, check_rope_single_pair, check_rope_group, check
         check_merge_closed_form, check_block_sdpa_mask, check_block_zero_query_closed_form,
         check_block_size1_is_causal, check_block_grad_autograd, check_soft_ce_library, check_soft_ce_closed_forms,
         check_window_sdpa_and_grad, check_window_closed_forms, check_window_ring_partition, check_chunk_bwd_partition,
-        check_trunk_keys_grad_autograd, check_soft_ce_grouped_library, check_thd_chunk_ring_partition]
+        check_trunk_keys_grad_autograd, check_soft_ce_grouped_library, check_thd_chunk_ring_partition,
+        check_block_thd_sdpa_and_grad]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[f"pin{i}" for i in range(len(PINS))])
@@ -877,6 +931,8 @@ MISTAKES = [
     ("soft_ce_rows_counted", _ce_counted_ignores_groups),
     ("_thd_segments", lambda cu, kc: [(int(cu[s]), int(cu[s + 1]), int(cu[s]), int(cu[s + 1]))
                                       for s in range(len(cu) - 1)]),
+    ("_block_thd_segments", lambda cu, cc, bs: [(int(cu[s]), int(cu[s + 1]), 0, int(cc[s + 1]) - int(cc[s]))
+                                                for s in range(len(cu) - 1)]),
 ]
 
 
