@@ -82,6 +82,7 @@ class Block(ctypes.Structure):
         ("ctx_len", ctypes.c_int64),
         ("anchors", ctypes.c_void_p),
         ("ctx_stride", ctypes.c_int64 * 3),
+        ("ctx_cu_seqlens", ctypes.c_void_p),
     ]
 
 
@@ -516,34 +517,54 @@ def merge(o_a, lse_a, o_b, lse_b, *, out=None, lse=None, cu_seqlens=None, stream
     return out, lse
 
 
-def make_block(block_size: int, k_ctx, anchors) -> Block:
+def make_block(block_size: int, k_ctx, anchors, ctx_cu_seqlens=None) -> Block:
+    """ctx_cu_seqlens: None (BSHD), or the device int32 cu_seqlens of the packed contexts (THD)."""
+    thd = ctx_cu_seqlens is not None
     bk = Block()
     bk.struct_size = ctypes.sizeof(Block)
     bk.block_size = int(block_size)
-    bk.ctx_len = k_ctx.shape[1]
+    bk.ctx_len = k_ctx.shape[0] if thd else k_ctx.shape[1]
     bk.anchors = anchors.data_ptr() if anchors is not None else None
-    bk.ctx_stride[:] = _strides3(k_ctx, False) if k_ctx.numel() else (0, 0, 0)
+    bk.ctx_stride[:] = _strides3(k_ctx, thd) if k_ctx.numel() else (0, 0, 0)
+    if thd:
+        if ctx_cu_seqlens.dtype != _torch().int32 or not ctx_cu_seqlens.is_contiguous():
+            raise ValueError("ctx_cu_seqlens must be a contiguous int32 tensor")
+        bk.ctx_cu_seqlens = ctx_cu_seqlens.data_ptr()
     return bk
+
+
+def _block_thd(cu_seqlens, ctx_cu_seqlens):
+    if (cu_seqlens is None) != (ctx_cu_seqlens is None):
+        raise ValueError("THD block drafting takes both cu_seqlens and ctx_cu_seqlens")
+    if cu_seqlens is not None and ctx_cu_seqlens.numel() != cu_seqlens.numel():
+        raise ValueError("cu_seqlens and ctx_cu_seqlens must list the same sequences")
+    return cu_seqlens is not None
 
 
 @_on_stream
 def block_fwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, *, softmax_scale: float = 0.0,
-              rope_base: float = 0.0, o_fp32: bool = False, out=None, lse=None, workspace=None, stream=None):
-    """Block-draft forward (BSHD, bf16).  q [B, N, Hq, D] with N = nblk * block_size;
+              rope_base: float = 0.0, o_fp32: bool = False, out=None, lse=None, workspace=None, stream=None,
+              cu_seqlens=None, ctx_cu_seqlens=None, check_cu_seqlens: bool = False):
+    """Block-draft forward (bf16).  BSHD: q [B, N, Hq, D] with N = nblk * block_size;
     k_ctx, v_ctx [B, ctx_len, Hkv, D]; k_blk, v_blk [B, N, Hkv, D]; anchors int32
-    [B, nblk] on the device.  Returns (o, lse [B, Hq, N])."""
+    [B, nblk] on the device; returns (o, lse [B, Hq, N]).  THD (cu_seqlens of the block
+    rows, whole blocks per sequence, and ctx_cu_seqlens of the contexts): q [T, Hq, D],
+    k_ctx, v_ctx [Tc, Hkv, D], anchors [T / block_size]; returns (o, lse [Hq, T])."""
     torch = _torch()
+    thd = _block_thd(cu_seqlens, ctx_cu_seqlens)
     o_dtype = DTYPE_FP32 if o_fp32 else _dtype_code(q)
     if out is None:
         out = torch.empty(q.shape, dtype=torch.float32 if o_dtype == DTYPE_FP32 else q.dtype, device=q.device)
     if lse is None:
-        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+        shape = (q.shape[1], q.shape[0]) if thd else (q.shape[0], q.shape[2], q.shape[1])
+        lse = torch.empty(shape, dtype=torch.float32, device=q.device)
     if anchors.dtype != torch.int32:
         raise TypeError("anchors must be int32")
     if k_blk.stride() != v_blk.stride() or k_ctx.stride() != v_ctx.stride():
         raise ValueError("k and v of the context (and of the blocks) must share strides")
-    d = make_desc(q, [k_blk], 1, softmax_scale=softmax_scale, rope_base=rope_base, o_dtype=o_dtype, o_like=out)
-    bk = make_block(block_size, k_ctx, anchors)
+    d = make_desc(q, [k_blk], 1, softmax_scale=softmax_scale, rope_base=rope_base, o_dtype=o_dtype, o_like=out,
+                  cu_seqlens=cu_seqlens, check_cu_seqlens=check_cu_seqlens)
+    bk = make_block(block_size, k_ctx, anchors, ctx_cu_seqlens)
     nbytes = int(library().ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(bk), 0))
     if nbytes == 0:
         raise TTTAttnError(2, library().ttt_attn_last_error().decode())
@@ -559,9 +580,10 @@ def block_fwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, *, softma
 @_on_stream
 def block_bwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, o, lse, dout, *, softmax_scale: float = 0.0,
               rope_base: float = 0.0, dq=None, dk_ctx=None, dv_ctx=None, dk_blk=None, dv_blk=None, workspace=None,
-              stream=None):
-    """Block-draft backward.  Returns (dq, dk_ctx, dv_ctx, dk_blk, dv_blk)."""
+              stream=None, cu_seqlens=None, ctx_cu_seqlens=None, check_cu_seqlens: bool = False):
+    """Block-draft backward (BSHD, or THD as in block_fwd).  Returns (dq, dk_ctx, dv_ctx, dk_blk, dv_blk)."""
     torch = _torch()
+    _block_thd(cu_seqlens, ctx_cu_seqlens)
     like = lambda t: torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
     dq = like(q) if dq is None else dq
     dk_ctx = like(k_ctx) if dk_ctx is None else dk_ctx
@@ -576,8 +598,9 @@ def block_bwd(q, k_ctx, v_ctx, k_blk, v_blk, anchors, block_size: int, o, lse, d
         raise ValueError("gradients take the strides of their primal")
     if k_blk.stride() != v_blk.stride() or k_ctx.stride() != v_ctx.stride():
         raise ValueError("k and v of the context (and of the blocks) must share strides")
-    d = make_desc(q, [k_blk], 1, softmax_scale=softmax_scale, rope_base=rope_base, o_dtype=_dtype_code(o), o_like=o)
-    bk = make_block(block_size, k_ctx, anchors)
+    d = make_desc(q, [k_blk], 1, softmax_scale=softmax_scale, rope_base=rope_base, o_dtype=_dtype_code(o), o_like=o,
+                  cu_seqlens=cu_seqlens, check_cu_seqlens=check_cu_seqlens)
+    bk = make_block(block_size, k_ctx, anchors, ctx_cu_seqlens)
     nbytes = int(library().ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(bk), 1))
     if nbytes == 0:
         raise TTTAttnError(2, library().ttt_attn_last_error().decode())

@@ -142,12 +142,14 @@ __global__ void __launch_bounds__(256, 2)
   // work item spans the largest lim of its blocks, a wave's unmasked prefix
   // is the smallest lim of the wave's blocks.
   int lim = 0, lim_hi = 0, lim_lo = 0;
+  BlkSeq bq{};  // block drafting: the sequence's anchors and context
   if constexpr (MODE == 1) {
-    lim = row_ok ? block_anchor(P, b, my_row) : 0;
+    bq = blk_seq(P, b, start);
+    lim = row_ok ? blk_anchor(P, bq, my_row) : 0;
     const int wend = min(wave_row0 + 32, L);
-    lim_lo = wend > wave_row0 ? P.kv_len : 0;
+    lim_lo = wend > wave_row0 ? bq.cn : 0;
     for (int blk = row0 >> P.bs_log2; (blk << P.bs_log2) < qend; ++blk) {
-      const int a = block_anchor(P, b, blk << P.bs_log2);
+      const int a = blk_anchor(P, bq, blk << P.bs_log2);
       lim_hi = max(lim_hi, a);
       if ((blk << P.bs_log2) < wend && ((blk + 1) << P.bs_log2) > wave_row0) lim_lo = min(lim_lo, a);
     }
@@ -155,9 +157,11 @@ __global__ void __launch_bounds__(256, 2)
   // TTT ring steps (BSHD): row i sits at position q_off + i, trunk key j at
   // kv_off + j (j < kv_len); whole-sequence calls have dq_ = 0, kvn = L.
   // (THD ring steps: the segment's own offsets and key rows kvs .. kvs + kvn.)
+  // (Block drafting: the sequence's context rows.)
   int qoff = 0, dq_ = 0, kvs = start, kvn = P.kv_len;
   if constexpr (TTT_)
     seq_ring(P, (P.layout == 1 && P.kv_cu) ? seq_at(P.cu, P.nseq, start) : b, start, L, qoff, dq_, kvs, kvn);
+  if constexpr (MODE == 1) kvs = bq.cs, kvn = bq.cn;
   const int kmax = TTT_ ? min(qend - 1 + dq_, kvn - 1) : lim_hi - 1;  // last key any row sees
   const int nkt = kmax < 0 ? 0 : kmax / QBN + 1;
   // sliding window: the first key tile any row of the work item sees
@@ -325,9 +329,9 @@ __global__ void __launch_bounds__(256, 2)
   // block drafting: the keys of the work item's own blocks (bs divides 32, so
   // the blocks of rows row0 .. qend-1 are exactly key rows row0 .. qend-1)
   if constexpr (MODE == 1) {
-    const _Float16* kbb = kbt + (int64_t)(b * P.Hkv + g) * P.spad * D;
-    const _Float16* ktbb = kbtt + (int64_t)(b * P.Hkv + g) * D * P.spad;
-    const uint16_t* vbb = (const uint16_t*)kv.v[1] + b * P.ks_b + g * P.ks_h;
+    const _Float16* kbb = kbt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
+    const _Float16* ktbb = kbtt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
+    const uint16_t* vbb = (const uint16_t*)kv.v[1] + b * P.ks_b + (int64_t)start * P.ks_t + g * P.ks_h;
     for (int k0 = row0; k0 < qend; k0 += QBN) {
       dma_from(&sm.buf[0], kbb, ktbb, vbb, P.ks_t, k0, L - 1);
       TTT_WAIT_VMCNT(0);
@@ -515,7 +519,7 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
       for (int e = 0; e < 4; ++e) a[e] = x0[e], a[4 + e] = x1[e], a[8 + e] = y0[e], a[12 + e] = y1[e];
     }
-    const int pos = TTT_ ? qoff + i + P.p - 1 : block_anchor(P, b, i) + (i & ((1 << P.bs_log2) - 1));
+    const int pos = TTT_ ? qoff + i + P.p - 1 : blk_anchor(P, bq, i) + (i & ((1 << P.bs_log2) - 1));
     const float* cq = cosT + rope_off(P, pos) + dlo;
     const float* sq = sinT + rope_off(P, pos) + dlo;
     if (TTT_ && P.p > 1 && P.branch && !P.dq_branch) {
@@ -662,6 +666,25 @@ __global__ void __launch_bounds__(256, 1)
     t = e.x, start = e.y, L = e.z, slot0 = e.w, b = 0;
   }
   kln = (MODE == 2 || (TTT_ && P.layout == 0)) ? nkeys : L;
+  BlkSeq bq{};  // block drafting: the sequence's anchors and context
+  if constexpr (MODE == 2 || MODE == 3) {
+    if (P.layout == 1) {
+      // THD lists key tiles: context keys (MODE 2) per context segment, block
+      // keys (MODE 3) per sequence; the rows are the sequence's block rows
+      kst = start;
+      kln = L;
+      if constexpr (MODE == 2) {
+        const int s = seq_at(P.kv_cu, P.nseq, start);
+        int b_;
+        seq_info(P, s, b_, start, L);
+        bq = blk_seq_of(P, s);
+      } else {
+        bq = blk_seq(P, 0, start);
+      }
+    } else {
+      bq = blk_seq(P, b, 0);
+    }
+  }
   if constexpr (TTT_) {
     // THD ring steps list key segments: the rows are the same segment's query rows
     if (P.layout == 1 && P.kv_cu) {
@@ -689,16 +712,17 @@ __global__ void __launch_bounds__(256, 1)
     // the first block whose anchor passes kv0 (any anchor order): rows before
     // it see no key here.  Every wave scans all anchors itself: no shared
     // memory or barrier before the staging ring.
-    int first = P.nblk;
-    for (int n = lane; n < P.nblk; n += 64)
-      if (block_anchor(P, b, n << P.bs_log2) > kv0) first = min(first, n);
+    const int nb = L >> P.bs_log2;  // the sequence's blocks
+    int first = nb;
+    for (int n = lane; n < nb; n += 64)
+      if (blk_anchor(P, bq, n << P.bs_log2) > kv0) first = min(first, n);
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) first = min(first, __shfl_xor(first, m, 64));
     row_lo = min(__builtin_amdgcn_readfirstlane(first) << P.bs_log2, L) & ~(BQ - 1);
   }
   // position of this lane's key (block keys: the slot position in its block)
   int kpos = TTT_ ? kvoff + my_key : my_key;
-  if constexpr (MODE == 3) kpos = key_ok ? block_anchor(P, b, my_key) + (my_key & ((1 << P.bs_log2) - 1)) : 0;
+  if constexpr (MODE == 3) kpos = key_ok ? blk_anchor(P, bq, my_key) + (my_key & ((1 << P.bs_log2) - 1)) : 0;
   if constexpr (!TTT_) {
     // every global load above has landed before the first staging load: the
     // compiler's load counter is then exact and no full wait lands in the loop
@@ -794,7 +818,7 @@ __global__ void __launch_bounds__(256, 1)
   // lengths (clamped anchors, staged per slot in the workspace after the LSE)
   const bool w1a = MODE == 2 && wv == 1;
   const int* a_base =
-      MODE == 2 ? (const int*)(delta + (int64_t)2 * P.B * P.Hq * P.spad) + (int64_t)b * P.spad : nullptr;
+      MODE == 2 ? (const int*)(delta + (int64_t)2 * P.B * P.Hq * P.spad) + (int64_t)b * P.spad + slot0 : nullptr;
   auto issue = [&](KvBuf* __restrict__ Bd) __attribute__((always_inline)) {
     KvBuf& B = *Bd;
     const buf_rsrc qr = make_rsrc(q_base + ((int64_t)is_h * P.spad + is_q0) * D, BQ * D * 2);
@@ -1097,20 +1121,21 @@ void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const
 }
 
 void launch_block_dkdv_bf16(const Prob& P, bool ctx_keys, const uint16_t* v, const float* lse, const uint16_t* dout,
-                            const _Float16* kt, const _Float16* qt, const float* delta, const float* cosT,
-                            const float* sinT, void* dk, void* dv, hipStream_t st) {
+                            const _Float16* kt, const _Float16* qt, const float* delta, const int4* tiles,
+                            const float* cosT, const float* sinT, void* dk, void* dv, hipStream_t st) {
   PassPtrs kv = {};
   kv.v[0] = v;
   PassGradPtrs g = {};
   g.dk[0] = dk;
   g.dv[0] = dv;
   const int nkeys = ctx_keys ? P.kv_len : P.stok;
-  const int64_t grid = (int64_t)8 * ((P.B * P.Hkv + 7) / 8) * ((nkeys + bwd::BKV - 1) / bwd::BKV);
+  const int64_t grid = P.layout == 0 ? (int64_t)8 * ((P.B * P.Hkv + 7) / 8) * ((nkeys + bwd::BKV - 1) / bwd::BKV)
+                                     : (int64_t)P.Hkv * ((nkeys + bwd::BKV - 1) / bwd::BKV + P.nseq);
   if (grid == 0) return;
   if (ctx_keys)
-    bwd::dkdv_bf16_kernel<2><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, nullptr, cosT, sinT, g);
+    bwd::dkdv_bf16_kernel<2><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles, cosT, sinT, g);
   else
-    bwd::dkdv_bf16_kernel<3><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, nullptr, cosT, sinT, g);
+    bwd::dkdv_bf16_kernel<3><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles, cosT, sinT, g);
 }
 
 template <int RH, int MODE>
@@ -1158,16 +1183,16 @@ void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const 
 
 void launch_block_dq_bf16(const Prob& P, const uint16_t* v_ctx, const uint16_t* v_blk, const float* lse,
                           const uint16_t* dout, const _Float16* ckt, const _Float16* cktt, const _Float16* bkt,
-                          const _Float16* bktt, const _Float16* qt, const float* delta, const float* cosT,
-                          const float* sinT, uint16_t* dq, hipStream_t st) {
+                          const _Float16* bktt, const _Float16* qt, const float* delta, const int4* tiles,
+                          const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st) {
   PassPtrs kv = {};
   kv.v[0] = v_ctx;
   kv.v[1] = v_blk;
   const PassGradPtrs none = {};
   switch (bwd::dq_heads_per_wg(P.r)) {
-    case 4: launch_dq_rh<4, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, none, st); break;
-    case 2: launch_dq_rh<2, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, none, st); break;
-    default: launch_dq_rh<1, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, nullptr, cosT, sinT, dq, bkt, bktt, none, st); break;
+    case 4: launch_dq_rh<4, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, tiles, cosT, sinT, dq, bkt, bktt, none, st); break;
+    case 2: launch_dq_rh<2, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, tiles, cosT, sinT, dq, bkt, bktt, none, st); break;
+    default: launch_dq_rh<1, 1>(P, nullptr, kv, lse, dout, ckt, cktt, qt, delta, tiles, cosT, sinT, dq, bkt, bktt, none, st); break;
   }
 }
 

@@ -116,9 +116,12 @@ __global__ void __launch_bounds__(256, 2)
   // Ring geometry: row i sits at position qoff + i and sees pass-1 key j
   // (j < kv_len, staged at the work item's slots) iff j <= i + dq_; for
   // whole-sequence calls qoff = dq_ = 0 and kv_len = L.
-  int qoff, dq_, kvs_, kv_len;
-  seq_ring(P, (P.layout == 1 && P.kv_cu) ? seq_at(P.cu, P.nseq, start) : b, start, L, qoff, dq_, kvs_, kv_len);
+  int qoff = 0, dq_ = 0, kvs_ = 0, kv_len = 0;
+  if constexpr (TTT_)
+    seq_ring(P, (P.layout == 1 && P.kv_cu) ? seq_at(P.cu, P.nseq, start) : b, start, L, qoff, dq_, kvs_, kv_len);
   (void)kvs_;
+  BlkSeq bq{};  // block drafting: the sequence's anchors and context
+  if constexpr (MODE == 1) bq = blk_seq(P, b, start);
   const int hw = wv % RH, rbk = wv / RH;
   const int h = g * P.r + sub * RH + hw;
   const int row0 = t * RT;
@@ -131,7 +134,7 @@ __global__ void __launch_bounds__(256, 2)
     const bool valid = my_row < L;
     const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + my_row) * P.qs_t + h * P.qs_h;
     const int pos = TTT_ ? qoff + my_row + P.p - 1
-                              : (valid ? block_anchor(P, b, my_row) + (my_row & ((1 << P.bs_log2) - 1)) : 0);
+                              : (valid ? blk_anchor(P, bq, my_row) + (my_row & ((1 << P.bs_log2) - 1)) : 0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int d0 = c * 16 + hf * 8;
@@ -170,11 +173,11 @@ __global__ void __launch_bounds__(256, 2)
   // prefix the smallest lim of the wave's blocks (loops are uniform).
   int lim = 0, lim_hi = 0, lim_lo = 0;
   if constexpr (MODE == 1) {
-    lim = my_row < L ? block_anchor(P, b, my_row) : 0;
+    lim = my_row < L ? blk_anchor(P, bq, my_row) : 0;
     const int wend = min(wave_row0 + 32, L);
-    lim_lo = wend > wave_row0 ? P.kv_len : 0;
+    lim_lo = wend > wave_row0 ? bq.cn : 0;
     for (int blk = row0 >> P.bs_log2; (blk << P.bs_log2) < qend; ++blk) {
-      const int a = block_anchor(P, b, blk << P.bs_log2);
+      const int a = blk_anchor(P, bq, blk << P.bs_log2);
       lim_hi = max(lim_hi, a);
       if ((blk << P.bs_log2) < wend && ((blk + 1) << P.bs_log2) > wave_row0) lim_lo = min(lim_lo, a);
     }
@@ -377,8 +380,8 @@ __global__ void __launch_bounds__(256, 2)
   // row0+RT-1; bs divides 32, so no block straddles the work item), one
   // 64-key tile at a time, masked to the row's block
   if constexpr (MODE == 1) {
-    const _Float16* kbb = kbt + (int64_t)(b * P.Hkv + g) * P.spad_b * D;
-    const _Float16* vbb = vbt + (int64_t)(b * P.Hkv + g) * D * P.spad_b;
+    const _Float16* kbb = kbt + ((int64_t)(b * P.Hkv + g) * P.spad_b + slot0) * D;
+    const _Float16* vbb = vbt + (int64_t)(b * P.Hkv + g) * D * P.spad_b + slot0;
     for (int k0 = row0; k0 < qend; k0 += BN) {
       dma_from(&sm.ring[0], kbb + (int64_t)k0 * D, vbb + k0);
       TTT_WAIT_VMCNT(0);
@@ -568,10 +571,10 @@ void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const
 }
 
 void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const _Float16* vt,
-                           const _Float16* kbt, const _Float16* vbt, const float* cosT, const float* sinT, void* o,
-                           bool o_f32, float* lse, hipStream_t st) {
+                           const _Float16* kbt, const _Float16* vbt, const int4* tiles, const float* cosT,
+                           const float* sinT, void* o, bool o_f32, float* lse, hipStream_t st) {
   const PassPtrs none = {};
-  fwd::launch_mode<1>(P, q, none, kt, vt, nullptr, cosT, sinT, o, o_f32, lse, kbt, vbt, st);
+  fwd::launch_mode<1>(P, q, none, kt, vt, tiles, cosT, sinT, o, o_f32, lse, kbt, vbt, st);
 }
 
 }  // namespace ttt

@@ -128,10 +128,6 @@ __device__ __forceinline__ int ds_exp(float x) {
   return e < -64 ? -64 : (e > 64 ? 64 : e);
 }
 
-__device__ __forceinline__ int block_anchor(const Prob& P, int b, int row) {
-  const int a = P.anchors[(int64_t)b * P.nblk + (row >> P.bs_log2)];
-  return a < 0 ? 0 : (a > P.kv_len ? P.kv_len : a);
-}
 
 // Passes' key/value pointers (up to 16), passed by value to kernels.
 struct PassPtrs {
@@ -160,6 +156,35 @@ __device__ __forceinline__ void seq_info(const Prob& P, int s, int& b, int& star
     int room = P.slot_base[s + 1] - P.slot_base[s];
     if (L > room) L = room;
   }
+}
+
+// Block drafting, the geometry of one sequence: its blocks' anchors start at
+// anchors[ab], and its context is rows cs .. cs + cn of k_ctx / v_ctx
+// (staged at the sequence's own slots in THD).  BSHD: batch row b, the whole
+// context.  THD (kv_cu = the contexts' cu_seqlens): sequence s, whose rows
+// are whole blocks, so its first block is its first row / bs.
+struct BlkSeq {
+  int64_t ab;
+  int cs, cn;
+};
+__device__ __forceinline__ BlkSeq blk_seq_of(const Prob& P, int s) {  // THD
+  int b_, start, L;
+  seq_info(P, s, b_, start, L);
+  int a = P.kv_cu[s], e = P.kv_cu[s + 1];
+  a = a < 0 ? 0 : (a > P.kv_tok ? P.kv_tok : a);
+  e = e < a ? a : (e > P.kv_tok ? P.kv_tok : e);
+  const int room = P.slot_base[s + 1] - P.slot_base[s];
+  return BlkSeq{(int64_t)(start >> P.bs_log2), a, e - a < room ? e - a : room};
+}
+// b: the batch row (BSHD); start: the first row of a THD work item.
+__device__ __forceinline__ BlkSeq blk_seq(const Prob& P, int b, int start) {
+  if (P.layout == 0) return BlkSeq{(int64_t)b * P.nblk, 0, P.kv_len};
+  return blk_seq_of(P, seq_at(P.cu, P.nseq, start));
+}
+// Anchor of the block holding row `row` (sequence-relative), clamped to [0, cn].
+__device__ __forceinline__ int blk_anchor(const Prob& P, const BlkSeq& q, int row) {
+  const int a = P.anchors[q.ab + (row >> P.bs_log2)];
+  return a < 0 ? 0 : (a > q.cn ? q.cn : a);
 }
 
 __device__ __forceinline__ int seq_slot0(const Prob& P, int s) { return P.layout == 0 ? 0 : P.slot_base[s]; }

@@ -312,6 +312,23 @@ int check_cu(const ttt_attn_desc* d, hipStream_t st, const ttt_attn_chunk* c = n
   return 0;
 }
 
+// With check_cu_seqlens (THD block drafting): cu_seqlens in whole blocks, and
+// the contexts' ctx_cu_seqlens.
+int check_block_cu(const ttt_attn_desc* d, const ttt_attn_block* bk, hipStream_t st) {
+  if (d->layout != TTT_LAYOUT_THD || !d->check_cu_seqlens) return 0;
+  if (int e = check_cu_array(d->cu_seqlens, d->num_seqs, d->seqlen, "cu_seqlens", st)) return e;
+  if (int e = check_cu_array(bk->ctx_cu_seqlens, d->num_seqs, bk->ctx_len, "ctx_cu_seqlens", st)) return e;
+  std::vector<int32_t> cu(d->num_seqs + 1);
+  hipError_t e = hipMemcpyAsync(cu.data(), d->cu_seqlens, cu.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(TTT_ERR_HIP, "reading cu_seqlens: %s", hipGetErrorString(e));
+  for (int s = 0; s <= d->num_seqs; ++s)
+    if (cu[s] % bk->block_size)
+      return fail(TTT_ERR_BAD_SHAPE, "cu_seqlens[%d] = %d: every sequence must hold whole blocks of %d", s, cu[s],
+                  bk->block_size);
+  return 0;
+}
+
 int hip_check(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(TTT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -598,6 +615,10 @@ struct BlockPlan {
   // forward: context K~ / V^T, block K~ / V^T; backward: context K~ / K~^T,
   // block K~ / K~^T (in the same four slots), Q~ rows and Delta
   size_t ctx_kt, ctx_vt, blk_kt, blk_vt, qt, delta, total;
+  // THD: workspace slots and the tile lists of the query rows, the context
+  // keys and the block keys
+  size_t slots, tiles_q, tiles_kv, tiles_kb;
+  int max_tiles_q, max_tiles_kv, max_tiles_kb;
 };
 
 int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan& bp, bool for_bwd = false) {
@@ -607,7 +628,11 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
   Plan& pl = bp.pl;
   if (int e = make_plan(d, 0, pl)) return e;
   ttt::Prob& P = pl.P;
-  if (d->layout != TTT_LAYOUT_BSHD) return fail(TTT_ERR_UNSUPPORTED, "block drafting takes the BSHD layout");
+  const bool thd = d->layout == TTT_LAYOUT_THD;
+  if (thd && !bk->ctx_cu_seqlens)
+    return fail(TTT_ERR_NULL_ARG, "THD block drafting needs ctx_cu_seqlens (the contexts' cu_seqlens)");
+  if (!thd && bk->ctx_cu_seqlens)
+    return fail(TTT_ERR_BAD_SHAPE, "ctx_cu_seqlens belongs to THD block drafting; BSHD takes it NULL");
   if (!pl.bf16) return fail(TTT_ERR_UNSUPPORTED, "block drafting is built for bf16");
   if (d->pass_index != 1) return fail(TTT_ERR_BAD_SHAPE, "block drafting has no passes: pass_index must be 1");
   if (d->window != 0) return fail(TTT_ERR_UNSUPPORTED, "block drafting takes no sliding window");
@@ -621,14 +646,23 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
   P.kv_len = ctx;
   P.branch = 0;
   P.bs_log2 = __builtin_ctz((unsigned)bs);
-  P.nblk = P.stok / bs;
+  P.nblk = P.stok / bs;  // THD: blocks of every sequence, in packed order
   P.anchors = bk->anchors;
   P.cs_b = 0, P.cs_t = 0, P.cs_h = 0;
   P.npos = ctx + bs;                                   // slot positions a + t <= ctx + bs - 1
   // context and block slabs share one slot count: the kernel's V^T row
   // offsets are computed once for both
-  const int rows_max = ctx > P.stok ? ctx : P.stok;
-  P.spad = ((rows_max + 63) / 64) * 64 + 64;
+  if (thd) {
+    // a sequence's block rows and context share its slots (the longer of the two, rounded up to 64)
+    if ((int64_t)P.stok + ctx + 128 + 64 * (int64_t)P.nseq > (int64_t)1 << 30)
+      return fail(TTT_ERR_BAD_SHAPE, "too many block (%d) and context (%d) rows", P.stok, ctx);
+    P.kv_cu = bk->ctx_cu_seqlens;
+    P.kv_tok = ctx;
+    P.spad = ((P.stok + ctx + 63) / 64) * 64 + 64 + 64 * P.nseq;
+  } else {
+    const int rows_max = ctx > P.stok ? ctx : P.stok;
+    P.spad = ((rows_max + 63) / 64) * 64 + 64;
+  }
   P.spad_b = P.spad;
   if (int e = check_slab_offsets(P)) return e;
   const int64_t* s0 = bk->ctx_stride;
@@ -655,6 +689,20 @@ int make_block_plan(const ttt_attn_desc* d, const ttt_attn_block* bk, BlockPlan&
   };
   memset(&pl.ws, 0, sizeof pl.ws);
   pl.ws.table = take((size_t)2 * P.npos * (D / 2) * sizeof(float));
+  bp.slots = bp.tiles_q = bp.tiles_kv = bp.tiles_kb = 0;
+  bp.max_tiles_q = bp.max_tiles_kv = bp.max_tiles_kb = 0;
+  if (thd) {
+    const int nseq = P.nseq;
+    bp.max_tiles_q = (P.stok + ttt::kFwdMinRows - 1) / ttt::kFwdMinRows + nseq + 1;
+    bp.max_tiles_kv = (ctx + ttt::kBwdBKV - 1) / ttt::kBwdBKV + nseq + 1;
+    bp.max_tiles_kb = (P.stok + ttt::kBwdBKV - 1) / ttt::kBwdBKV + nseq + 1;
+    bp.slots = take((size_t)(nseq + 1) * sizeof(int));
+    bp.tiles_q = take((size_t)(bp.max_tiles_q + 1) * 16);
+    if (for_bwd) {
+      bp.tiles_kv = take((size_t)(bp.max_tiles_kv + 1) * 16);
+      bp.tiles_kb = take((size_t)(bp.max_tiles_kb + 1) * 16);
+    }
+  }
   const size_t nc = (size_t)P.B * Hkv * P.spad * D, nb = (size_t)P.B * Hkv * P.spad_b * D;
   bp.ctx_kt = take(nc * 2);
   bp.ctx_vt = take(nc * 2);
@@ -708,6 +756,7 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   if ((uintptr_t)lse & 3u) return fail(TTT_ERR_MISALIGNED, "lse is not 4-byte aligned");
   if (int e = check_ws(pl, ws, ws_bytes)) return e;
   hipStream_t st = (hipStream_t)stream;
+  if (int e = check_block_cu(d, bk, st)) return e;
   (void)hipGetLastError();
   float* cosT = at<float>(ws, pl.ws.table);
   float* sinT = cosT + (size_t)P.npos * (P.D / 2);
@@ -717,8 +766,23 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   _Float16* bktt = at<_Float16>(ws, bp.blk_vt);
   _Float16* qt = at<_Float16>(ws, bp.qt);
   float* delta = at<float>(ws, bp.delta);
+  const bool thd = P.layout == TTT_LAYOUT_THD;
+  int* slots = thd ? at<int>(ws, bp.slots) : nullptr;
+  P.slot_base = slots;
   set_bounds(P, at<char>(ws, pl.ws.bnd), 2);
   TTT_TRACED("rope_table", ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st));
+  const int4 *tq = nullptr, *tkv = nullptr, *tkb = nullptr;
+  if (thd) {  // THD: slots, then the tiles of the query rows, the context keys and the block keys
+    int4* a = at<int4>(ws, bp.tiles_q);
+    int4* c = at<int4>(ws, bp.tiles_kv);
+    int4* k = at<int4>(ws, bp.tiles_kb);
+    TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::dq_tile_rows(P.r), 1, a, bp.max_tiles_q, slots, st));
+    ttt::Prob Pkv = P;
+    Pkv.cu = P.kv_cu, Pkv.stok = P.kv_tok;
+    TTT_TRACED("tile_sched", ttt::launch_tile_sched(Pkv, ttt::kBwdBKV, 0, c, bp.max_tiles_kv, nullptr, st));
+    TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kBwdBKV, 0, k, bp.max_tiles_kb, nullptr, st));
+    tq = a, tkv = c, tkb = k;
+  }
   TTT_TRACED("bwd_delta", ttt::launch_delta(P, o, pl.o_f32, dout, false, lse, delta, st));
   TTT_TRACED("bwd_dmax", ttt::launch_dmax(P, st));
   ttt::PrepJobs J;
@@ -728,6 +792,7 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
     ttt::Prob Pc = P;
     Pc.stok = P.kv_len;
     J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, (uint16_t*)cktt, 0, nullptr, 0};
+    if (thd) J.j[0].cu = P.kv_cu, J.j[0].ntok = P.kv_tok;
     TTT_TRACED("prep_ctx_bwd", ttt::launch_prep_bf16(Pc, J, cosT, sinT, st));
   }
   // block keys (K~ rows, K~^T) and queries (Q~ rows) at their slot positions
@@ -741,14 +806,14 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
     ttt::Prob Pc = P;  // the context keys' V / dK / dV strides
     Pc.ks_b = bp.cs_b, Pc.ks_t = bp.cs_t, Pc.ks_h = bp.cs_h;
     TTT_TRACED("block_dkdv_ctx", ttt::launch_block_dkdv_bf16(Pc, true, (const uint16_t*)v_ctx, lse,
-                                                             (const uint16_t*)dout, ckt, qt, delta, cosT, sinT,
+                                                             (const uint16_t*)dout, ckt, qt, delta, tkv, cosT, sinT,
                                                              dk_ctx, dv_ctx, st));
   }
   TTT_TRACED("block_dkdv_blk", ttt::launch_block_dkdv_bf16(P, false, (const uint16_t*)v_blk, lse,
-                                                           (const uint16_t*)dout, bkt, qt, delta, cosT, sinT, dk_blk,
-                                                           dv_blk, st));
+                                                           (const uint16_t*)dout, bkt, qt, delta, tkb, cosT, sinT,
+                                                           dk_blk, dv_blk, st));
   TTT_TRACED("block_dq", ttt::launch_block_dq_bf16(P, (const uint16_t*)v_ctx, (const uint16_t*)v_blk, lse,
-                                                   (const uint16_t*)dout, ckt, cktt, bkt, bktt, qt, delta, cosT,
+                                                   (const uint16_t*)dout, ckt, cktt, bkt, bktt, qt, delta, tq, cosT,
                                                    sinT, (uint16_t*)dq, st));
   return hip_check("ttt_attn_block_bwd launch");
 }
@@ -776,6 +841,7 @@ int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   if ((uintptr_t)lse & 3u) return fail(TTT_ERR_MISALIGNED, "lse is not 4-byte aligned");
   if (int e = check_ws(pl, ws, ws_bytes)) return e;
   hipStream_t st = (hipStream_t)stream;
+  if (int e = check_block_cu(d, bk, st)) return e;
   (void)hipGetLastError();
   float* cosT = at<float>(ws, pl.ws.table);
   float* sinT = cosT + (size_t)P.npos * (P.D / 2);
@@ -783,8 +849,17 @@ int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   _Float16* cvt = at<_Float16>(ws, bp.ctx_vt);
   _Float16* bkt = at<_Float16>(ws, bp.blk_kt);
   _Float16* bvt = at<_Float16>(ws, bp.blk_vt);
+  const bool thd = P.layout == TTT_LAYOUT_THD;
+  int* slots = thd ? at<int>(ws, bp.slots) : nullptr;
+  P.slot_base = slots;
   TTT_TRACED("rope_table", ttt::launch_rope_table(P, cosT, sinT, (double)d->rope_base, st));
-  // context: K~ rows at positions j and V^T (kv_len rows)
+  const int4* tiles = nullptr;
+  if (thd) {  // THD: the slots of each sequence (block rows and context), then the query tiles
+    int4* t = at<int4>(ws, bp.tiles_q);
+    TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::fwd_tile_rows(P.r), 1, t, bp.max_tiles_q, slots, st));
+    tiles = t;
+  }
+  // context: K~ rows at positions j and V^T (kv_len rows; THD: each sequence's own)
   ttt::Prob Pc = P;
   Pc.stok = P.kv_len;
   ttt::PrepJobs J;
@@ -792,6 +867,8 @@ int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   J.n = 2;
   J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, nullptr, 0, nullptr, 0};
   J.j[1] = {(const uint16_t*)v_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 0, 0, nullptr, (uint16_t*)cvt, 0, nullptr, 0};
+  if (thd)
+    for (int j = 0; j < 2; ++j) J.j[j].cu = P.kv_cu, J.j[j].ntok = P.kv_tok;
   TTT_TRACED("prep_ctx", ttt::launch_prep_bf16(Pc, J, cosT, sinT, st));
   // block keys: K~ rows at their slot positions and V^T (spad_b slots)
   ttt::Prob Pb = P;
@@ -799,8 +876,8 @@ int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, nullptr, 1, nullptr, 0};
   J.j[1] = {(const uint16_t*)v_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 0, 0, nullptr, (uint16_t*)bvt, 0, nullptr, 0};
   TTT_TRACED("prep_blk", ttt::launch_prep_bf16(Pb, J, cosT, sinT, st));
-  TTT_TRACED("block_fwd", ttt::launch_block_fwd_bf16(P, (const uint16_t*)q, ckt, cvt, bkt, bvt, cosT, sinT, o,
-                                                     pl.o_f32, lse, st));
+  TTT_TRACED("block_fwd", ttt::launch_block_fwd_bf16(P, (const uint16_t*)q, ckt, cvt, bkt, bvt, tiles, cosT, sinT,
+                                                     o, pl.o_f32, lse, st));
   return hip_check("ttt_attn_block_fwd launch");
 }
 

@@ -60,13 +60,13 @@ int fwd_tile_rows(int r);
 // (ctx_keys, kt = context K~ slab, v = context V) or of the block keys (kt =
 // block K~ slab, v = block V); P.ks_* must then be the strides of v/dk/dv.
 void launch_block_dkdv_bf16(const Prob& P, bool ctx_keys, const uint16_t* v, const float* lse, const uint16_t* dout,
-                            const _Float16* kt, const _Float16* qt, const float* delta, const float* cosT,
-                            const float* sinT, void* dk, void* dv, hipStream_t st);
+                            const _Float16* kt, const _Float16* qt, const float* delta, const int4* tiles,
+                            const float* cosT, const float* sinT, void* dk, void* dv, hipStream_t st);
 // dQ: context keys (ckt, cktt, v_ctx) up to each row's anchor, then its block's keys (bkt, bktt, v_blk).
 void launch_block_dq_bf16(const Prob& P, const uint16_t* v_ctx, const uint16_t* v_blk, const float* lse,
                           const uint16_t* dout, const _Float16* ckt, const _Float16* cktt, const _Float16* bkt,
-                          const _Float16* bktt, const _Float16* qt, const float* delta, const float* cosT,
-                          const float* sinT, uint16_t* dq, hipStream_t st);
+                          const _Float16* bktt, const _Float16* qt, const float* delta, const int4* tiles,
+                          const float* cosT, const float* sinT, uint16_t* dq, hipStream_t st);
 // Per-pass soft cross-entropy (bf16 logits [B][S][V], vocab contiguous, V % 8 == 0).
 struct CeProb {
   int B, S, V, offset;
@@ -84,8 +84,8 @@ void launch_soft_ce_fwd(const CeProb& C, const uint16_t* s, const uint16_t* t, f
 void launch_soft_ce_bwd(const CeProb& C, const uint16_t* s, const uint16_t* t, const float* row_lse,
                         const float* stats, const float* dloss, uint16_t* g, hipStream_t st);
 void launch_block_fwd_bf16(const Prob& P, const uint16_t* q, const _Float16* kt, const _Float16* vt,
-                           const _Float16* kbt, const _Float16* vbt, const float* cosT, const float* sinT, void* o,
-                           bool o_f32, float* lse, hipStream_t st);     // query rows per forward work item for GQA ratio r (32, 64 or 128)
+                           const _Float16* kbt, const _Float16* vbt, const int4* tiles, const float* cosT,
+                           const float* sinT, void* o, bool o_f32, float* lse, hipStream_t st);     // query rows per forward work item for GQA ratio r (32, 64 or 128)
 constexpr int kFwdMinRows = 32;
 int dq_tile_rows(int r);
 // whether the dQ kernel's work item holds every query head of a KV group, so

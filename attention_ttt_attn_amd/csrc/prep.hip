@@ -151,13 +151,15 @@ __global__ void __launch_bounds__(256) prep_bf16_kernel(Prob P, PrepJobs J, cons
     } else {
       valid = slot_token(P, slot, tok, row, &sq);
     }
-    if (jb.out_lim && h == 0 && c8 == 0) jb.out_lim[(int64_t)b * P.spad + slot] = valid ? block_anchor(P, b, row) : 0;
+    BlkSeq bq{};  // block drafting: the row's sequence (anchors, context)
+    if ((jb.out_lim || jb.pos_anchor) && valid) bq = P.layout == 0 ? blk_seq(P, b, 0) : blk_seq_of(P, sq);
+    if (jb.out_lim && h == 0 && c8 == 0) jb.out_lim[(int64_t)b * P.spad + slot] = valid ? blk_anchor(P, bq, row) : 0;
     if (valid) {
       const uint16_t* src = jb.x + (int64_t)b * jb.sb + (int64_t)tok * jb.st + (int64_t)h * jb.sh + 8 * c8;
       unpack_bf8(*(const u32x4*)src, a);
       unpack_bf8(*(const u32x4*)(src + HALF), c);
       if (jb.rot) {
-        const int pos = jb.pos_anchor ? block_anchor(P, b, row) + (row & ((1 << P.bs_log2) - 1))
+        const int pos = jb.pos_anchor ? blk_anchor(P, bq, row) + (row & ((1 << P.bs_log2) - 1))
                                       : row + jb.pos_off + (jb.seg_pos ? jb.seg_pos[sq] : 0);
         const int64_t t = rope_off(P, pos) + 8 * c8;
         const f32x4 c0 = *(const f32x4*)(cosT + t), c1 = *(const f32x4*)(cosT + t + 4);

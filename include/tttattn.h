@@ -257,19 +257,31 @@ int ttt_attn_merge(const ttt_attn_desc* d, const void* o_a, const float* lse_a, 
  * anchor, 1.. the mask tokens); every slot of the block sees the context keys
  * at positions j < a and all bs keys of its own block.  RoPE (rotate-half)
  * at those positions, as in ttt_attn_fwd.
- * The descriptor gives the block rows: layout BSHD, dtype BF16, seqlen =
- * nblk * bs rows (row i = slot i % bs of block i / bs), pass_index 1,
- * q_stride for q, kv_stride for k_blk / v_blk [B, seqlen, Hkv, D], o_stride,
- * softmax_scale, rope_base.  Output O [B, seqlen, Hq, D] and LSE [B, Hq,
- * seqlen] as in ttt_attn_fwd. */
+ * The descriptor gives the block rows: dtype BF16, pass_index 1, q_stride
+ * for q, kv_stride for k_blk / v_blk, o_stride, softmax_scale, rope_base.
+ * BSHD: seqlen = nblk * bs rows per batch row (row i = slot i % bs of block
+ * i / bs), k_blk / v_blk [B, seqlen, Hkv, D], output O [B, seqlen, Hq, D]
+ * and LSE [B, Hq, seqlen] as in ttt_attn_fwd; ctx_cu_seqlens is NULL.
+ * THD (same issue, item 4: the block-draft attention on the packed layout):
+ * sequence s holds block rows cu_seqlens[s] .. cu_seqlens[s+1] of q / k_blk
+ * / v_blk [T, H, D] (whole blocks: every cu_seqlens entry is a multiple of
+ * bs) and context rows ctx_cu_seqlens[s] .. ctx_cu_seqlens[s+1] of k_ctx /
+ * v_ctx [ctx_len, Hkv, D] (ctx_len = all sequences' context rows); anchors
+ * has one entry per block in packed order (T / bs) and clamps to the
+ * sequence's own context length; O [T, Hq, D], LSE [Hq, T].  Sequences
+ * never see each other.  With d->check_cu_seqlens the host checks both
+ * arrays (start 0, non-decreasing, totals T and ctx_len, whole blocks). */
 typedef struct ttt_attn_block {
   uint32_t struct_size;       /* = sizeof(ttt_attn_block)                                 */
   int32_t block_size;         /* bs: 1, 2, 4, 8, 16 or 32                                 */
-  int64_t ctx_len;            /* context rows of k_ctx / v_ctx                            */
-  const int32_t* anchors;     /* device int32 [B][seqlen / bs], read-only; values outside
-                                 [0, ctx_len] are clamped                                  */
+  int64_t ctx_len;            /* context rows of k_ctx / v_ctx (THD: of every sequence)   */
+  const int32_t* anchors;     /* device int32 [B][seqlen / bs] (THD: [T / bs]), read-only;
+                                 values outside [0, the context length] are clamped       */
   int64_t ctx_stride[3];      /* batch, token, head strides of k_ctx / v_ctx (elements); a
-                                 zero triple selects the contiguous [B, ctx_len, Hkv, D]   */
+                                 zero triple selects the contiguous [B, ctx_len, Hkv, D]
+                                 ([ctx_len, Hkv, D] in THD)                                */
+  const int32_t* ctx_cu_seqlens; /* THD: device int32 [num_seqs + 1], the contexts' rows;
+                                 BSHD: NULL                                                */
 } ttt_attn_block;
 
 /* Bytes of workspace ttt_attn_block_fwd (for_bwd = 0) or ttt_attn_block_bwd

@@ -326,8 +326,32 @@ def call_block(d, bk, q=FAKE, kc=FAKE, vc=FAKE, kb=FAKE, vb=FAKE, o=FAKE, lse=FA
 
 
 def test_block_struct_matches_header():
-    assert ctypes.sizeof(tk.Block) == 48
-    assert "ttt_attn_block" in open(os.path.join(ROOT, "include", "tttattn.h")).read()
+    assert ctypes.sizeof(tk.Block) == 56
+    text = open(os.path.join(ROOT, "include", "tttattn.h")).read()
+    assert "ttt_attn_block" in text and "ctx_cu_seqlens" in text
+
+
+def test_thd_block_validation():
+    lib = tk.library()
+    d = good_desc(layout=tk.LAYOUT_THD, p=1)         # 100 rows: not whole blocks of 16
+    d.seqlen = 128
+    bk = good_block()
+    assert call_block(d, bk) == 1 and "ctx_cu_seqlens" in err()
+    bk.ctx_cu_seqlens = FAKE
+    w = lambda dd, b: lib.ttt_attn_block_workspace_bytes(ctypes.byref(dd), ctypes.byref(b), 0)
+    assert w(d, bk) > 0
+    assert call_block(d, bk, ws_bytes=16) == 5      # the arguments pass; the workspace is too small
+    d2 = good_desc(layout=tk.LAYOUT_THD, p=1)
+    assert call_block(d2, bk) == 2 and "blocks" in err()
+    # BSHD refuses a context cu_seqlens
+    b2 = good_block()
+    b2.ctx_cu_seqlens = FAKE
+    assert call_block(block_desc(), b2) == 2 and "ctx_cu_seqlens" in err()
+    # the workspace holds both row sets per sequence
+    big = good_block(ctx_len=8192)
+    big.ctx_cu_seqlens = FAKE
+    assert w(d, big) > w(d, bk)
+    assert lib.ttt_attn_block_workspace_bytes(ctypes.byref(d), ctypes.byref(bk), 1) > w(d, bk)
 
 
 def test_block_validation():
@@ -344,7 +368,7 @@ def test_block_validation():
     dd = block_desc()
     dd.pass_index = 2
     assert call_block(dd, good_block()) == 2 and "pass_index" in err()
-    assert call_block(good_desc(layout=tk.LAYOUT_THD, p=1), good_block()) == 3
+    assert call_block(good_desc(layout=tk.LAYOUT_THD, p=1), good_block()) == 1 and "ctx_cu_seqlens" in err()
     assert call_block(good_desc(dtype=tk.DTYPE_FP32, p=1), good_block()) == 3
     assert call_block(d, good_block(anchors=None)) == 1 and "anchors" in err()
     assert call_block(d, good_block(anchors=FAKE + 2)) == 4
