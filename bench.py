@@ -129,6 +129,20 @@ def committed_traffic(kernel: str, workload: str):
     return float(m_b.group(1))
 
 
+def committed_kernel_time(kernel: str, workload: str):
+    """Average launch duration (us) of `kernel` in the rocprofv3 kernel-trace summary
+    profiles/kernels_<workload>.md, or None when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"Source digest:\s*`?([0-9a-f]+)", text)
+    m_t = re.search(r"^\|\s*" + re.escape(kernel) + r"\s*\|\s*\d+\s*\|\s*([0-9.]+)\s*\|", text, re.M)
+    if not m_src or not m_t or m_src.group(1) != source_digest():
+        return None
+    return float(m_t.group(1))
+
+
 # ----------------------------------------------------------------------------- CPU oracle baseline
 def cpu_baseline(w, seconds: float):
     import numpy as np
@@ -559,7 +573,17 @@ def main():
                     "peak": 2500.0 if mfma else 8000.0, "unit": "TFLOP/s" if mfma else "GB/s",
                     "frac": round(achieved / (PEAK_MFMA_BF16 if mfma else PEAK_HBM), 4),
                     "traffic": committed_traffic(dom, w.name),
-                    "work_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2)}
+                    "work_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2),
+                    "profile_avg_launch_us": committed_kernel_time(dom, w.name)}
+    # the trunk forward alone against the 45% of bf16 peak bar
+    gate = None
+    if "trunk_fwd" in kstats:
+        s = kstats["trunk_fwd"]
+        rate = s["work"] / (s["ms"] * 1e-3)
+        gate = {"kernel": "trunk_fwd", "achieved": round(rate / 1e12, 2), "unit": "TFLOP/s",
+                "frac": round(rate / PEAK_MFMA_BF16, 4), "bar": 0.45,
+                "avg_launch_us": round(s["ms"] / s["launches"] * 1e3, 2),
+                "profile_avg_launch_us": committed_kernel_time("trunk_fwd", w.name)}
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -584,6 +608,7 @@ def main():
                    "mfma_operands": "fp16 Q~K~^T and dS, bf16 P.V, dO.V, P^T.dO; fp32 accumulate",
                    "parallelism": "single GPU", "window": WINDOW},
         "roofline": roofline,
+        "gate": gate,
         "kernels": kernels,
         "source_digest": source_digest(),
     }
