@@ -49,6 +49,9 @@ def parse():
     ap.add_argument("--block", action="store_true",
                     help="instead of the unroll, time the block-draft forward on the blk_b4_c4k shape "
                          "(prints its own JSON line)")
+    ap.add_argument("--block-thd", action="store_true",
+                    help="instead of the unroll, time packed (THD) block drafting: the thd_32k sequences as "
+                         "contexts, 64 blocks of 16 slots per sequence (prints its own JSON line)")
     ap.add_argument("--soft-ce", action="store_true",
                     help="instead of the attention unroll, time the per-pass soft cross-entropy (forward + "
                          "backward for passes 1..7) on B=4, S=4096, V=32000 bf16 logits (prints its own JSON line)")
@@ -192,6 +195,9 @@ def ring_main(args, w, dev):
     import ttt_synth as syn
 
     cp, K = args.ring, w.K
+    if w.layout == "thd":
+        ring_thd_main(args, w, dev)
+        return
     if w.layout != "bshd" or w.S % (2 * cp):
         print(f"--ring needs a BSHD workload whose length divides into {2 * cp} chunks", file=sys.stderr)
         sys.exit(2)
@@ -269,6 +275,212 @@ def ring_main(args, w, dev):
            "config": {"workload": w.name, "pass": K, "cp": cp, "chunk_rows": c, "ring_steps": steps_per_ring,
                       "merges": steps_per_ring - 2 * cp, "o": "fp32 partials, fp32 merge"},
            "shapes": res, "source_digest": source_digest()}
+    print(json.dumps(out), flush=True)
+
+
+def ring_thd_main(args, w, dev):
+    """Packed (THD) ring steps of pass K: every sequence of the packed workload is cut into 2 cp
+    chunks ([c L / 2cp, (c+1) L / 2cp)), and step (qc, kc) packs chunk qc's rows and chunk kc's
+    keys of every sequence in one call.  The chunks' rows are gathered before the timed region
+    (a ring rank holds its chunks contiguous)."""
+    import numpy as np
+    import torch
+
+    import attention_ttt_attn_amd as tk
+    import ttt_synth as syn
+
+    cp, K = args.ring, w.K
+    nc = 2 * cp
+    lens = w.lengths()
+    cu = syn.cu_seqlens_of(lens)
+    q = syn.draw_device(w, syn.KIND_Q, K, dev)
+    ks = [syn.draw_device(w, syn.KIND_K, t, dev) for t in range(1, K + 1)]
+    vs = [syn.draw_device(w, syn.KIND_V, t, dev) for t in range(1, K + 1)]
+    do = syn.draw_device(w, syn.KIND_DO, K, dev)
+    gcu = torch.from_numpy(cu).to(dev)
+    o_full, l_full = tk.fwd(q, ks, vs, K, cu_seqlens=gcu, rope_base=w.rope_base)
+    span = lambda c: [(c * L // nc, (c + 1) * L // nc - c * L // nc) for L in lens]
+    chunks = []
+    for c in range(nc):
+        sp = span(c)
+        rows = torch.as_tensor(np.concatenate([np.arange(cu[s] + a, cu[s] + a + n) for s, (a, n) in enumerate(sp)]),
+                               device=dev)
+        i32 = lambda x: torch.as_tensor(np.asarray(x, np.int32), device=dev)
+        chunks.append(dict(
+            n=len(rows), cu=i32(np.concatenate([[0], np.cumsum([n for _, n in sp])])), off=i32([a for a, _ in sp]),
+            q=q.index_select(0, rows), k=[t.index_select(0, rows) for t in ks], v=[t.index_select(0, rows) for t in vs],
+            o=o_full.index_select(0, rows), lse=l_full.index_select(1, rows).contiguous(), do=do.index_select(0, rows),
+            pairs=[(a, n) for a, n in sp]))
+    ws = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    maxpos = max(lens) + K
+
+    def args_of(qc, kc):
+        a, b = chunks[qc], chunks[kc]
+        sk = [b["k"][0]] + a["k"][1:K]
+        sv = [b["v"][0]] + a["v"][1:K]
+        geo = dict(cu_seqlens=a["cu"], kv_cu_seqlens=b["cu"], q_offsets=a["off"], kv_offsets=b["off"],
+                   max_position=maxpos, with_branch=qc == kc, rope_base=w.rope_base, workspace=ws)
+        return a, sk, sv, geo
+
+    bufs = {}
+
+    def step(qc, kc, slot):
+        a, sk, sv, geo = args_of(qc, kc)
+        key = (qc, slot)
+        if key not in bufs:
+            bufs[key] = (torch.empty((a["n"], w.Hq, w.D), dtype=torch.float32, device=dev),
+                         torch.empty((w.Hq, a["n"]), dtype=torch.float32, device=dev))
+        o_, l_ = bufs[key]
+        tk.fwd_chunk(a["q"], sk, sv, K, out=o_, lse=l_, **geo)
+        return o_, l_
+
+    def ring():
+        for r in range(cp):
+            for qc in (r, nc - 1 - r):
+                oa, la = step(qc, 0, 0)
+                for kc in range(1, qc + 1):
+                    ob, lb = step(qc, kc, 1)
+                    tk.merge(oa, la, ob, lb, out=oa, lse=la, cu_seqlens=chunks[qc]["cu"])
+
+    def bstep(qc, kc):
+        a, sk, sv, geo = args_of(qc, kc)
+        tk.bwd_chunk(a["q"], sk, sv, a["o"], a["lse"], a["do"], K, **geo)
+
+    o_s = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    l_s = torch.empty(l_full.shape, dtype=torch.float32, device=dev)
+    m_a = step(cp, cp, 0)
+    m_b = step(cp, 0, 1)
+    shapes = {
+        "diag_step": lambda: step(cp, cp, 0),
+        "full_step": lambda: step(nc - 1, 0, 0),
+        "merge": lambda: tk.merge(m_a[0], m_a[1], m_b[0], m_b[1], out=m_a[0], lse=m_a[1], cu_seqlens=chunks[cp]["cu"]),
+        "ring_total": ring,
+        "single_call": lambda: tk.fwd(q, ks, vs, K, cu_seqlens=gcu, o_fp32=True, out=o_s, lse=l_s,
+                                      rope_base=w.rope_base, workspace=ws),
+        "bwd_diag_step": lambda: bstep(cp, cp),
+        "bwd_full_step": lambda: bstep(nc - 1, 0),
+    }
+    n = max(args.steps, 1)
+    res = {}
+    for name, fn in shapes.items():
+        for _ in range(max(args.warmup, 1)):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"avg_us": round(e0.elapsed_time(e1) * 1e3 / n, 2)}
+    per_head = 4.0 * w.D * w.Hq
+    diag = sum(nq * (nq + 1) // 2 + (K - 1) * nq for _, nq in chunks[cp]["pairs"])
+    full = sum(nq * nk for (_, nq), (_, nk) in zip(chunks[nc - 1]["pairs"], chunks[0]["pairs"]))
+    flops = {"diag_step": per_head * diag, "full_step": per_head * full, "ring_total": useful_flops(w, K)[0],
+             "single_call": useful_flops(w, K)[0], "bwd_diag_step": 2.5 * per_head * diag,
+             "bwd_full_step": 2.5 * per_head * full}
+    for name, f in flops.items():
+        res[name]["tflops"] = round(f / (res[name]["avg_us"] * 1e-6) / 1e12, 1)
+    res["merge"]["gbps"] = round(chunks[cp]["n"] * w.Hq * (w.D * 4 * 3 + 12) / (res["merge"]["avg_us"] * 1e-6) / 1e9, 1)
+    steps_per_ring = sum(qc + 1 for r in range(cp) for qc in (r, nc - 1 - r))
+    out = {"metric": "packed (THD) ring-step forward time per chunk shape", "value": res["ring_total"]["avg_us"],
+           "unit": "us", "higher_is_better": False, "n_gpus": 1, "steps": n, "warmup": args.warmup, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": w.name, "pass": K, "cp": cp, "sequences": len(lens),
+                      "chunk_rows_total": [c["n"] for c in chunks], "ring_steps": steps_per_ring,
+                      "merges": steps_per_ring - nc, "o": "fp32 partials, fp32 merge"},
+           "shapes": res, "source_digest": source_digest()}
+    print(json.dumps(out), flush=True)
+
+
+def block_thd_main(args, dev):
+    """Packed (THD) block drafting, forward + backward: the 16 thd_32k sequences (T = 32768) as
+    contexts, 64 blocks of 16 slots per sequence (16384 block rows), anchors uniform in each
+    sequence's context.  Useful FLOPs as in the BSHD block bench."""
+    import numpy as np
+    import torch
+
+    import attention_ttt_attn_amd as tk
+    import ttt_synth as syn
+
+    w = syn.workload("thd_32k")
+    bs, nb, Hq, Hkv, D = 16, 64, w.Hq, w.Hkv, w.D
+    ctx = w.lengths()
+    ns = len(ctx)
+    T, Tc = ns * nb * bs, sum(ctx)
+    rng = np.random.default_rng(w.index)
+    anchors = np.concatenate([np.sort(rng.integers(0, c + 1, nb)) for c in ctx]).astype(np.int32)
+    q = syn.draw_device(w, syn.KIND_Q, 1, dev, (T, Hq, D))
+    kb = syn.draw_device(w, syn.KIND_K, 2, dev, (T, Hkv, D))
+    vb = syn.draw_device(w, syn.KIND_V, 2, dev, (T, Hkv, D))
+    kc = syn.draw_device(w, syn.KIND_K, 1, dev, (Tc, Hkv, D))
+    vc = syn.draw_device(w, syn.KIND_V, 1, dev, (Tc, Hkv, D))
+    do = syn.draw_device(w, syn.KIND_DO, 1, dev, (T, Hq, D))
+    cu = torch.as_tensor(np.arange(ns + 1, dtype=np.int32) * nb * bs, device=dev)
+    ccu = torch.from_numpy(syn.cu_seqlens_of(ctx)).to(dev)
+    ga = torch.from_numpy(anchors).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    grads = [torch.empty_like(t) for t in (q, kc, vc, kb, vb)]
+    geo = dict(cu_seqlens=cu, ctx_cu_seqlens=ccu, rope_base=w.rope_base, workspace=ws)
+    pairs = int((anchors.astype(np.int64) + bs).sum()) * bs     # per head (anchors lie inside their contexts)
+    flops_f = 4.0 * D * Hq * pairs
+
+    def run():
+        tk.block_fwd(q, kc, vc, kb, vb, ga, bs, out=o, lse=lse, **geo)
+        tk.block_bwd(q, kc, vc, kb, vb, ga, bs, o, lse, do, dq=grads[0], dk_ctx=grads[1], dv_ctx=grads[2],
+                     dk_blk=grads[3], dv_blk=grads[4], **geo)
+    for _ in range(max(args.warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    events = []
+    cur = torch.cuda.current_stream()
+
+    def hook(name, phase, stream):
+        s_ = cur if not stream or stream == cur.cuda_stream else torch.cuda.ExternalStream(stream)
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(s_)
+        if phase == 0:
+            events.append([name, ev, None])
+        else:
+            events[-1][2] = ev
+
+    n = max(args.steps, 1)
+    tk.set_trace_hook(hook)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    tk.set_trace_hook(None)
+    call_ms = e0.elapsed_time(e1) / n
+    ks = {}
+    for name, a, b in events:
+        k = ks.setdefault(name, [0, 0.0])
+        k[0] += 1
+        k[1] += a.elapsed_time(b)
+    kern = {k: {"avg_us": round(v[1] * 1e3 / v[0], 2), "launches_per_call": v[0] // n} for k, v in ks.items()}
+    fwd_us = kern["block_fwd"]["avg_us"]
+    achieved = flops_f / (fwd_us * 1e-6)
+    kern["block_fwd"]["tflops"] = round(achieved / 1e12, 1)
+    ctx_pairs = int(anchors.astype(np.int64).sum()) * bs
+    for name, f in (("block_dkdv_ctx", 8.0 * D * Hq * ctx_pairs), ("block_dq", 6.0 * D * Hq * pairs)):
+        if name in kern:
+            kern[name]["tflops"] = round(f / (kern[name]["avg_us"] * 1e-6) / 1e12, 1)
+    value = 3.5 * flops_f / (call_ms * 1e-3) / 1e12
+    out = {"metric": "packed (THD) block-draft attention fwd+bwd TFLOP/s (useful FLOPs)", "value": round(value, 2),
+           "unit": "TFLOP/s", "frac_of_peak": round(value * 1e12 / PEAK_MFMA_BF16, 4),
+           "n_gpus": 1, "steps": n, "warmup": args.warmup, "ms_per_step": round(call_ms, 4), "higher_is_better": True,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "blk_thd_32k", "sequences": ns, "ctx_rows": Tc, "block_size": bs,
+                      "blocks_per_sequence": nb, "block_rows": T, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                      "step": "forward then backward", "useful_tflop_per_step": round(3.5 * flops_f / 1e12, 4)},
+           "roofline": {"kernel": "block_fwd", "bound": "mfma", "achieved": round(achieved / 1e12, 2),
+                        "peak": 2500.0, "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_BF16, 4),
+                        "traffic": None, "work_per_launch": flops_f, "avg_launch_us": fwd_us},
+           "kernels": kern, "source_digest": source_digest()}
     print(json.dumps(out), flush=True)
 
 
@@ -453,6 +665,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.block:
         block_main(args, dev)
+        return
+    if args.block_thd:
+        block_thd_main(args, dev)
         return
     if args.soft_ce:
         soft_ce_main(args, dev)
