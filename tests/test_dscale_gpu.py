@@ -177,3 +177,40 @@ def test_ring_backward_small_dout(dev, tk):
         errs[f"dv{t + 1}"] = rel_fro(to_np(gv[t]), dv_r[t])
     print("ring bwd cp=2 dO*1e-6: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
     assert max(errs.values()) <= TOL["bf16"]["grad"], errs
+
+
+def test_thd_ring_backward_small_dout(dev, tk):
+    """Packed (THD) ring-step backward terms at dO ~ 1e-6, summed over a zig-zag ring, against the oracle."""
+    from test_ring_thd_gpu import LENS, zigzag_thd
+    w = syn.Workload("dscale_thd_ring", 46, "thd", 1, sum(LENS), 8, 2, 128, 3, "bf16", 1e6, True)
+    inp = rescale_do(Inputs(w, dev, lengths=LENS), 1e-6)
+    p = 3
+    o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **inp.kw())
+    gq, gk, gv = zigzag_thd(tk, inp, p, 2, dev, o=o, lse=lse)
+    dq_r, dk_r, dv_r = O.bwd(inp.q[p], inp.k, inp.v, inp.do[p], p, layout="thd", cu_seqlens=inp.cu_host,
+                             base=w.rope_base)
+    errs = {"dq": rel_fro(to_np(gq), dq_r)}
+    for t in range(p):
+        errs[f"dk{t + 1}"] = rel_fro(to_np(gk[t]), dk_r[t])
+        errs[f"dv{t + 1}"] = rel_fro(to_np(gv[t]), dv_r[t])
+    print("thd ring bwd cp=2 dO*1e-6: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+    assert max(errs.values()) <= TOL["bf16"]["grad"], errs
+
+
+def test_thd_block_backward_small_dout(dev, tk):
+    """Packed (THD) block-draft backward at dO ~ 1e-6 and with a per-row mix of scales."""
+    from test_block_thd_gpu import SEQS, ThdBlock
+    inp = ThdBlock(dev, SEQS, 16, 8, 2, 47)
+    for scale in (1e-6, "mixed"):
+        do = syn.round_bf16(inp.do * do_scales(inp.do.shape, scale, 11))
+        gdo = torch.from_numpy(np.ascontiguousarray(do)).to(dev).to(torch.bfloat16)
+        o, lse = tk.block_fwd(inp.gq, inp.gkc, inp.gvc, inp.gkb, inp.gvb, inp.ga, 16, **inp.geo())
+        grads = tk.block_bwd(inp.gq, inp.gkc, inp.gvc, inp.gkb, inp.gvb, inp.ga, 16, o, lse, gdo, **inp.geo())
+        torch.cuda.synchronize()
+        ref = O.block_bwd_thd(inp.q, inp.kc, inp.vc, inp.kb, inp.vb, inp.anchors, 16, do, **inp.oracle_geo())
+        names = ["dq", "dk_ctx", "dv_ctx", "dk_blk", "dv_blk"]
+        errs = {n: rel_fro(to_np(g), r) for n, g, r in zip(names, grads, ref)}
+        print(f"thd block bwd dO*{scale}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
+        for n, g in zip(names, grads):
+            assert torch.isfinite(g.float()).all().item(), n
+        assert max(errs.values()) <= TOL["bf16"]["grad"], errs
