@@ -158,6 +158,24 @@ __device__ __forceinline__ void seq_info(const Prob& P, int s, int& b, int& star
   }
 }
 
+// THD: whether the 64 slots from slot0 (64-aligned) lie past every read of
+// the rows cu[s] .. cu[s+1] (ntok rows in all) of the sequence s owning them.
+// A sequence's readers touch at most 127 slots past its last row (128-key
+// dK/dV tiles, 128-row dQ work items; those lanes are masked), so staging
+// may skip such a tile: with block rows and a longer context sharing one
+// sequence's slots (or the other way round), most of the range is never read.
+__device__ __forceinline__ bool thd_tile_unread(const Prob& P, const int* cu, int ntok, int slot0) {
+  int lo = 0, hi = P.nseq;  // last s with slot_base[s] <= slot0 (the last sequence for the tail)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (P.slot_base[mid] <= slot0) lo = mid; else hi = mid;
+  }
+  int a = cu[lo], e = cu[lo + 1];
+  a = a < 0 ? 0 : (a > ntok ? ntok : a);
+  e = e < a ? a : (e > ntok ? ntok : e);
+  return slot0 - P.slot_base[lo] >= e - a + 128;
+}
+
 // Block drafting, the geometry of one sequence: its blocks' anchors start at
 // anchors[ab], and its context is rows cs .. cs + cn of k_ctx / v_ctx
 // (staged at the sequence's own slots in THD).  BSHD: batch row b, the whole

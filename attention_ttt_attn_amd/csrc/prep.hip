@@ -134,6 +134,7 @@ __global__ void __launch_bounds__(256) prep_bf16_kernel(Prob P, PrepJobs J, cons
   const int b = blockIdx.z, tok0 = tix * 64, tid = threadIdx.x;
   const int c8 = tid & 7, rr = tid >> 3;
   const int64_t slab = (int64_t)(b * jb.H + h) * P.spad;
+  if (P.layout == 1 && thd_tile_unread(P, jb.cu ? jb.cu : P.cu, jb.cu ? jb.ntok : P.stok, tok0)) return;
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     const int lr = pass * 32 + rr, slot = tok0 + lr;
@@ -226,6 +227,13 @@ __global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict
   constexpr int NR = 64 / ROWS;  // rows per thread
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, c = tid % TPR;
+  if (P.layout == 1 && thd_tile_unread(P, P.cu, P.stok, blockIdx.x * 64)) {
+    if (P.dpart && tid == 0) {  // the group maxima still read this block's entry
+      const int64_t bo = ((int64_t)(b * P.Hq + h) * (P.spad / 64) + blockIdx.x) * 2;
+      P.dpart[bo] = P.dpart[bo + 1] = 0.f;
+    }
+    return;
+  }
   int slot[NR], tok[NR];
   bool valid[NR];
   float x[NR][8], y[NR][8];
