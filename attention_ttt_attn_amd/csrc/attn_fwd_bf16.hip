@@ -128,44 +128,6 @@ __global__ void __launch_bounds__(256, 2)
   const int wave_row0 = row0 + rbk * 32;
   const int my_row = wave_row0 + l32;  // this lane's query row (B/C column)
 
-  // ---- Q~ = R(i+p-1) q in fp16, B operand chunks c = 0..7 (d = 16c + 8hf + e)
-  f16x8 qf[8];
-  {
-    const bool valid = my_row < L;
-    const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + my_row) * P.qs_t + h * P.qs_h;
-    const int pos = TTT_ ? qoff + my_row + P.p - 1
-                              : (valid ? blk_anchor(P, bq, my_row) + (my_row & ((1 << P.bs_log2) - 1)) : 0);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int d0 = c * 16 + hf * 8;
-      float x1[8], x2[8];
-      if (valid) {
-        unpack_bf8(*(const u32x4*)(qrow + d0), x1);
-        unpack_bf8(*(const u32x4*)(qrow + d0 + 64), x2);
-        const f32x4* cp = (const f32x4*)(cosT + rope_off(P, pos) + d0);
-        const f32x4* sp = (const f32x4*)(sinT + rope_off(P, pos) + d0);
-        const f32x4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
-        const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-        const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float y1 = x1[e] * cs[e] - x2[e] * sn[e];
-          const float y2 = x2[e] * cs[e] + x1[e] * sn[e];
-          x1[e] = y1;
-          x2[e] = y2;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x1[e] = x2[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qf[c][e] = (_Float16)x1[e];
-        qf[c + 4][e] = (_Float16)x2[e];
-      }
-    }
-  }
-
   // ---- trunk main loop
   const int qend = min(row0 + RT, L);
   // Block drafting: row i sees context keys j < lim (its block's anchor); the
@@ -235,6 +197,44 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
   for (int tt = 1; tt < NBUF - 1; ++tt)
     if (kt_lo + tt < nkt) dma(&sm.ring[tt], kt_lo + tt);
+  // ---- Q~ = R(i+p-1) q in fp16 (while the first tiles load), B operand chunks c = 0..7 (d = 16c + 8hf + e)
+  f16x8 qf[8];
+  {
+    const bool valid = my_row < L;
+    const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + my_row) * P.qs_t + h * P.qs_h;
+    const int pos = TTT_ ? qoff + my_row + P.p - 1
+                              : (valid ? blk_anchor(P, bq, my_row) + (my_row & ((1 << P.bs_log2) - 1)) : 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d0 = c * 16 + hf * 8;
+      float x1[8], x2[8];
+      if (valid) {
+        unpack_bf8(*(const u32x4*)(qrow + d0), x1);
+        unpack_bf8(*(const u32x4*)(qrow + d0 + 64), x2);
+        const f32x4* cp = (const f32x4*)(cosT + rope_off(P, pos) + d0);
+        const f32x4* sp = (const f32x4*)(sinT + rope_off(P, pos) + d0);
+        const f32x4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+        const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float y1 = x1[e] * cs[e] - x2[e] * sn[e];
+          const float y2 = x2[e] * cs[e] + x1[e] * sn[e];
+          x1[e] = y1;
+          x2[e] = y2;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x1[e] = x2[e] = 0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qf[c][e] = (_Float16)x1[e];
+        qf[c + 4][e] = (_Float16)x2[e];
+      }
+    }
+  }
+
   wait_tiles(min(nkt - kt_lo, NBUF - 1) - 1);
   __syncthreads();
 
