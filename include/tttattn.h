@@ -62,7 +62,10 @@
 extern "C" {
 #endif
 
-#define TTT_ATTN_ABI_VERSION 2
+/* 3: ttt_attn_chunk, ttt_attn_block and ttt_soft_ce_desc gained the packed
+ * (THD) and per-row / per-group fields; each struct's struct_size check
+ * refuses a caller built against an older layout. */
+#define TTT_ATTN_ABI_VERSION 3
 
 enum ttt_attn_layout { TTT_LAYOUT_BSHD = 0, TTT_LAYOUT_THD = 1 };
 /* BF16: the score products run on fp16 operands.  q and k are rotated in fp32

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
             "ttt_attn_last_error", "ttt_attn_abi_version", "ttt_attn_set_trace_hook"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ttt_attn_abi_version() == 2
+    assert lib.ttt_attn_abi_version() == 3
 
 
 def test_status_strings():
