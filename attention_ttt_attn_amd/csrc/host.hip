@@ -79,6 +79,19 @@ int check_slab_offsets(const ttt::Prob& P) {
   return 0;
 }
 
+// bf16 head_dim 32 / 64: the whole-sequence calls run the D = 128 kernels on
+// zero-padded copies of the heads (defined after the D = 128 entry points).
+bool padded_head(const ttt_attn_desc* d) {
+  return d && d->struct_size == sizeof(ttt_attn_desc) && d->dtype == TTT_DTYPE_BF16 &&
+         (d->head_dim == 32 || d->head_dim == 64);
+}
+size_t padded_ws_bytes(const ttt_attn_desc* d, int for_bwd);
+int padded_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, void* o,
+               float* lse, void* ws, size_t ws_bytes, void* stream);
+int padded_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* const* dk, void* const* dv, void* ws,
+               size_t ws_bytes, void* stream);
+
 // Validates the descriptor (and the ring-step chunk, if any) and fills the
 // kernel view and workspace plan.
 int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chunk* c = nullptr) {
@@ -99,7 +112,8 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
   if (D <= 0 || (D & 1)) return fail(TTT_ERR_BAD_SHAPE, "head_dim %d must be positive and even", D);
   const bool bf16 = d->dtype == TTT_DTYPE_BF16;
   if (bf16 ? (D != 128) : (D != 32 && D != 64 && D != 128))
-    return fail(TTT_ERR_UNSUPPORTED, "head_dim %d not built for %s (fp32: 32/64/128, bf16: 128)", D,
+    return fail(TTT_ERR_UNSUPPORTED, "head_dim %d not built for %s here (fp32: 32/64/128; bf16: 128, and 32/64 "
+                "through ttt_attn_fwd / ttt_attn_bwd only)", D,
                 bf16 ? "bf16" : "fp32");
   if (p < 1 || p > TTT_MAX_PASSES)
     return fail(TTT_ERR_BAD_SHAPE, "pass_index %d outside 1..%d", p, TTT_MAX_PASSES);
@@ -444,6 +458,7 @@ const char* ttt_attn_status_string(int status) {
 const char* ttt_attn_last_error(void) { return g_last_error.c_str(); }
 
 size_t ttt_attn_workspace_bytes(const ttt_attn_desc* d, int for_bwd) {
+  if (padded_head(d)) return padded_ws_bytes(d, for_bwd);
   Plan pl;
   if (make_plan(d, for_bwd, pl) != TTT_OK) return 0;
   return pl.ws.total;
@@ -530,6 +545,7 @@ extern "C" {
 
 int ttt_attn_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, void* o,
                  float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (padded_head(d)) return padded_fwd(d, q, k, v, o, lse, ws, ws_bytes, stream);
   return fwd_impl(d, nullptr, q, k, v, o, lse, ws, ws_bytes, stream);
 }
 
@@ -1135,11 +1151,181 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
 }
 }  // namespace
 
+namespace {
+// bf16 head_dim 32 / 64 (the pages name no head size; 32, 64 and 128 are the
+// boundary's): each head is zero-padded to 128 entries in the workspace with
+// element k < D/2 at entry (128/D) k and element D/2 + k at 64 + (128/D) k, so
+// that the D = 128 rotate-half pairs and frequencies are exactly the D-dim
+// ones and the zero entries add nothing (pad_heads_kernel); the D = 128 path
+// then runs on contiguous padded tensors with softmax scale 1/sqrt(D) unless
+// one is given, and its outputs are unpadded into the caller's tensors.  Cost:
+// the MFMA work of D = 128 plus one pass over every tensor each way.
+struct PadRoute {
+  ttt_attn_desc d;                 // D = 128, contiguous padded tensors
+  int D, S;                        // S: tokens per batch row (BSHD) or all tokens (THD)
+  int64_t rows;                    // B*S or T
+  int64_t qs[3], ks[3], os[3];     // the caller's element strides of q (and dq), k / v (and dk / dv), o (and dout)
+  size_t q, kv, o, dout, dq, dkv, inner, total;  // workspace offsets; kv / dkv: 2p padded tensors
+  size_t q_bytes, kv_bytes, o_bytes;
+};
+
+int make_pad_route(const ttt_attn_desc* d, int for_bwd, PadRoute& r) {
+  if (d->layout != TTT_LAYOUT_BSHD && d->layout != TTT_LAYOUT_THD)
+    return fail(TTT_ERR_BAD_SHAPE, "layout %d is neither BSHD (0) nor THD (1)", d->layout);
+  const bool thd = d->layout == TTT_LAYOUT_THD;
+  r.D = d->head_dim;
+  r.d = *d;
+  r.d.head_dim = 128;
+  if (!(d->softmax_scale > 0.f)) r.d.softmax_scale = 1.0f / sqrtf((float)r.D);
+  for (int i = 0; i < 3; ++i) r.d.q_stride[i] = r.d.kv_stride[i] = r.d.o_stride[i] = 0;
+  Plan pl;
+  if (int e = make_plan(&r.d, for_bwd, pl)) return e;
+  const int Hq = d->num_q_heads, Hkv = d->num_kv_heads, D = r.D;
+  r.S = d->seqlen;
+  r.rows = thd ? (int64_t)d->seqlen : (int64_t)d->batch * d->seqlen;
+  auto strides = [&](const int64_t* s, int H, int64_t* out, const char* name) -> int {
+    if (s[0] == 0 && s[1] == 0 && s[2] == 0) {
+      out[0] = thd ? 0 : (int64_t)r.S * H * D, out[1] = (int64_t)H * D, out[2] = D;
+      return 0;
+    }
+    for (int i = 0; i < 3; ++i)
+      if (s[i] < 0) return fail(TTT_ERR_BAD_SHAPE, "%s stride[%d] = %lld is negative", name, i, (long long)s[i]);
+    out[0] = thd ? 0 : s[0], out[1] = s[1], out[2] = s[2];
+    return 0;
+  };
+  if (int e = strides(d->q_stride, Hq, r.qs, "q")) return e;
+  if (int e = strides(d->kv_stride, Hkv, r.ks, "kv")) return e;
+  if (int e = strides(d->o_stride, Hq, r.os, "o")) return e;
+  const int p = d->pass_index;
+  const size_t osz = d->o_dtype == TTT_DTYPE_FP32 ? 4 : 2;
+  r.q_bytes = (size_t)r.rows * Hq * 128 * 2;
+  r.kv_bytes = (size_t)r.rows * Hkv * 128 * 2;
+  r.o_bytes = (size_t)r.rows * Hq * 128 * osz;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at_ = off;
+    off = align256(off + bytes);
+    return at_;
+  };
+  r.q = take(r.q_bytes);
+  r.kv = off;
+  for (int i = 0; i < 2 * p; ++i) take(r.kv_bytes);
+  r.o = take(r.o_bytes);
+  r.dout = r.dq = r.dkv = 0;
+  if (for_bwd) {
+    r.dout = take((size_t)r.rows * Hq * 128 * 2);
+    r.dq = take(r.q_bytes);
+    r.dkv = off;
+    for (int i = 0; i < 2 * p; ++i) take(r.kv_bytes);
+  }
+  r.inner = off;
+  r.total = off + pl.ws.total;
+  return TTT_OK;
+}
+
+char* kv_slot(void* ws, const PadRoute& r, size_t base, int i) {
+  return (char*)ws + base + (size_t)i * align256(r.kv_bytes);
+}
+
+size_t padded_ws_bytes(const ttt_attn_desc* d, int for_bwd) {
+  PadRoute r;
+  if (make_pad_route(d, for_bwd, r) != TTT_OK) return 0;
+  return r.total;
+}
+
+int padded_fwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, void* o,
+               float* lse, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  PadRoute r;
+  if (int e = make_pad_route(d, 0, r)) return e;
+  if (r.rows == 0) return TTT_OK;
+  if (!k || !v) return fail(TTT_ERR_NULL_ARG, "k or v pointer array is NULL");
+  if (!q || !o || !lse) return fail(TTT_ERR_NULL_ARG, "q, o or lse is NULL");
+  const int p = d->pass_index, Hq = d->num_q_heads, Hkv = d->num_kv_heads;
+  for (int i = 0; i < p; ++i)
+    if (!k[i] || !v[i]) return fail(TTT_ERR_NULL_ARG, "k[%d] or v[%d] is NULL", i, i);
+  if (r.total && (!ws || ((uintptr_t)ws & 255u) || ws_bytes < r.total))
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes at %p: %zu bytes, 256-byte aligned, needed", ws_bytes,
+                ws, r.total);
+  hipStream_t st = (hipStream_t)stream;
+  const bool o32 = d->o_dtype == TTT_DTYPE_FP32;
+  char* w = (char*)ws;
+  const void* kp[TTT_MAX_PASSES];
+  const void* vp[TTT_MAX_PASSES];
+  ttt::trace("pad_heads", 0, st);
+  ttt::launch_pad_heads(q, false, r.qs[0], r.qs[1], r.qs[2], r.rows, r.S, Hq, r.D, w + r.q, st);
+  for (int i = 0; i < p; ++i) {
+    kp[i] = kv_slot(ws, r, r.kv, i);
+    vp[i] = kv_slot(ws, r, r.kv, p + i);
+    ttt::launch_pad_heads(k[i], false, r.ks[0], r.ks[1], r.ks[2], r.rows, r.S, Hkv, r.D, (void*)kp[i], st);
+    ttt::launch_pad_heads(v[i], false, r.ks[0], r.ks[1], r.ks[2], r.rows, r.S, Hkv, r.D, (void*)vp[i], st);
+  }
+  ttt::trace("pad_heads", 1, st);
+  if (int e = hip_check("pad_heads launch")) return e;
+  if (int e = fwd_impl(&r.d, nullptr, w + r.q, kp, vp, w + r.o, lse, w + r.inner, ws_bytes - r.inner, stream))
+    return e;
+  ttt::trace("unpad_heads", 0, st);
+  ttt::launch_unpad_heads(w + r.o, o32, r.rows, r.S, Hq, r.D, o, r.os[0], r.os[1], r.os[2], st);
+  ttt::trace("unpad_heads", 1, st);
+  return hip_check("unpad_heads launch");
+}
+
+int padded_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* const* dk, void* const* dv, void* ws,
+               size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  PadRoute r;
+  if (int e = make_pad_route(d, 1, r)) return e;
+  if (r.rows == 0) return TTT_OK;
+  if (!k || !v || !dk || !dv) return fail(TTT_ERR_NULL_ARG, "a k/v/dk/dv pointer array is NULL");
+  if (!q || !o || !lse || !dout || !dq) return fail(TTT_ERR_NULL_ARG, "q, o, lse, dout or dq is NULL");
+  const int p = d->pass_index, Hq = d->num_q_heads, Hkv = d->num_kv_heads;
+  for (int i = 0; i < p; ++i)
+    if (!k[i] || !v[i] || !dk[i] || !dv[i]) return fail(TTT_ERR_NULL_ARG, "k/v/dk/dv[%d] is NULL", i);
+  if (r.total && (!ws || ((uintptr_t)ws & 255u) || ws_bytes < r.total))
+    return fail(TTT_ERR_WORKSPACE, "workspace of %zu bytes at %p: %zu bytes, 256-byte aligned, needed", ws_bytes,
+                ws, r.total);
+  hipStream_t st = (hipStream_t)stream;
+  const bool o32 = d->o_dtype == TTT_DTYPE_FP32;
+  char* w = (char*)ws;
+  const void* kp[TTT_MAX_PASSES];
+  const void* vp[TTT_MAX_PASSES];
+  void* dkp[TTT_MAX_PASSES];
+  void* dvp[TTT_MAX_PASSES];
+  ttt::trace("pad_heads", 0, st);
+  ttt::launch_pad_heads(q, false, r.qs[0], r.qs[1], r.qs[2], r.rows, r.S, Hq, r.D, w + r.q, st);
+  ttt::launch_pad_heads(o, o32, r.os[0], r.os[1], r.os[2], r.rows, r.S, Hq, r.D, w + r.o, st);
+  ttt::launch_pad_heads(dout, false, r.os[0], r.os[1], r.os[2], r.rows, r.S, Hq, r.D, w + r.dout, st);
+  for (int i = 0; i < p; ++i) {
+    kp[i] = kv_slot(ws, r, r.kv, i);
+    vp[i] = kv_slot(ws, r, r.kv, p + i);
+    dkp[i] = kv_slot(ws, r, r.dkv, i);
+    dvp[i] = kv_slot(ws, r, r.dkv, p + i);
+    ttt::launch_pad_heads(k[i], false, r.ks[0], r.ks[1], r.ks[2], r.rows, r.S, Hkv, r.D, (void*)kp[i], st);
+    ttt::launch_pad_heads(v[i], false, r.ks[0], r.ks[1], r.ks[2], r.rows, r.S, Hkv, r.D, (void*)vp[i], st);
+  }
+  ttt::trace("pad_heads", 1, st);
+  if (int e = hip_check("pad_heads launch")) return e;
+  if (int e = bwd_impl(&r.d, nullptr, w + r.q, kp, vp, w + r.o, lse, w + r.dout, w + r.dq, dkp, dvp, w + r.inner,
+                       ws_bytes - r.inner, stream))
+    return e;
+  ttt::trace("unpad_heads", 0, st);
+  ttt::launch_unpad_heads(w + r.dq, false, r.rows, r.S, Hq, r.D, dq, r.qs[0], r.qs[1], r.qs[2], st);
+  for (int i = 0; i < p; ++i) {
+    ttt::launch_unpad_heads(dkp[i], false, r.rows, r.S, Hkv, r.D, dk[i], r.ks[0], r.ks[1], r.ks[2], st);
+    ttt::launch_unpad_heads(dvp[i], false, r.rows, r.S, Hkv, r.D, dv[i], r.ks[0], r.ks[1], r.ks[2], st);
+  }
+  ttt::trace("unpad_heads", 1, st);
+  return hip_check("unpad_heads launch");
+}
+}  // namespace
+
 extern "C" {
 
 int ttt_attn_bwd(const ttt_attn_desc* d, const void* q, const void* const* k, const void* const* v, const void* o,
                  const float* lse, const void* dout, void* dq, void* const* dk, void* const* dv, void* ws,
                  size_t ws_bytes, void* stream) {
+  if (padded_head(d)) return padded_bwd(d, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream);
   return bwd_impl(d, nullptr, q, k, v, o, lse, dout, dq, dk, dv, ws, ws_bytes, stream);
 }
 

@@ -38,6 +38,11 @@ void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bo
                   float* delta, hipStream_t st);
 // bf16 backward: P.dmax[B*Hkv][2] from the Delta kernel's P.dpart entries
 void launch_dmax(const Prob& P, hipStream_t st);
+// bf16 head_dim 32 / 64 on the D = 128 kernels: zero-padded heads (see prep.hip)
+void launch_pad_heads(const void* src, bool f32, int64_t sb, int64_t st, int64_t sh, int64_t rows, int S, int H,
+                      int D, void* dst, hipStream_t stream);
+void launch_unpad_heads(const void* src, bool f32, int64_t rows, int S, int H, int D, void* dst, int64_t sb,
+                        int64_t st, int64_t sh, hipStream_t stream);
 // THD: workspace slots (when slot_base is given) and the sequence-major tile
 // list (when out is given); desc: tiles descending within a sequence.
 void launch_tile_sched(const Prob& P, int tile, int desc, int4* out, int max_entries, int* slot_base,

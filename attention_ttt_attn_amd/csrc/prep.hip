@@ -417,6 +417,49 @@ __global__ void __launch_bounds__(1024) tile_sched_kernel(Prob P, int tile, int 
   if (tid == 0) out[0] = make_int4(s_base < max_entries ? s_base : max_entries, 0, 0, 0);
 }
 
+// bf16 head_dim 32 / 64 run on the D = 128 kernels with each head zero-padded:
+// element k < D/2 of a head goes to entry (128/D) k, element D/2 + k to
+// 64 + (128/D) k, and every other entry is 0.  The D = 128 rotate-half pair
+// (j, j + 64) at angle pos * base^(-2j/128) is then exactly the D-dim pair
+// (k, k + D/2) at pos * base^(-2k/D), zero entries stay zero under rotation,
+// and every dot product and weighted sum over the padded head equals the one
+// over the D real entries.  rows: tokens (B*S or T); the caller's tensor has
+// element strides (sb, st, sh) with S tokens per batch row.
+template <typename T>
+__global__ void __launch_bounds__(256) pad_heads_kernel(const T* __restrict__ src, int64_t sb, int64_t st,
+                                                        int64_t sh, int S, int H, int D, int64_t n,
+                                                        T* __restrict__ dst) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const int j = (int)(idx & 127);
+  const int64_t rh = idx >> 7;
+  const int h = (int)(rh % H);
+  const int64_t r = rh / H;
+  const int sp = 128 / D, half = D / 2;
+  const int jj = j & 63;
+  T v = T(0);
+  if (jj % sp == 0) {
+    const int k = jj / sp + (j >= 64 ? half : 0);
+    v = src[(r / S) * sb + (r % S) * st + h * sh + k];
+  }
+  dst[idx] = v;
+}
+
+// The inverse: the D real entries of each padded head back to the caller's strides.
+template <typename T>
+__global__ void __launch_bounds__(256) unpad_heads_kernel(const T* __restrict__ src, int S, int H, int D, int64_t n,
+                                                          T* __restrict__ dst, int64_t sb, int64_t st, int64_t sh) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  const int k = (int)(idx % D);
+  const int64_t rh = idx / D;
+  const int h = (int)(rh % H);
+  const int64_t r = rh / H;
+  const int sp = 128 / D, half = D / 2;
+  const int j = k < half ? sp * k : 64 + sp * (k - half);
+  dst[(r / S) * sb + (r % S) * st + h * sh + k] = src[rh * 128 + j];
+}
+
 // ----------------------------------------------------------------------------- launchers
 void launch_rope_table(const Prob& P, float* cosT, float* sinT, double base, hipStream_t st) {
   int64_t n = (int64_t)P.npos * (P.D / 2);
@@ -524,6 +567,29 @@ void launch_merge(const Prob& P, bool o_f32, const void* o_a, const float* lse_a
 void launch_tile_sched(const Prob& P, int tile, int desc, int4* out, int max_entries, int* slot_base,
                        hipStream_t st) {
   tile_sched_kernel<<<1, 1024, 0, st>>>(P, tile, desc, out, max_entries, slot_base);
+}
+
+void launch_pad_heads(const void* src, bool f32, int64_t sb, int64_t st, int64_t sh, int64_t rows, int S, int H,
+                      int D, void* dst, hipStream_t st_) {
+  const int64_t n = rows * H * 128;
+  if (n == 0) return;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (f32)
+    pad_heads_kernel<float><<<blocks, 256, 0, st_>>>((const float*)src, sb, st, sh, S, H, D, n, (float*)dst);
+  else
+    pad_heads_kernel<uint16_t><<<blocks, 256, 0, st_>>>((const uint16_t*)src, sb, st, sh, S, H, D, n, (uint16_t*)dst);
+}
+
+void launch_unpad_heads(const void* src, bool f32, int64_t rows, int S, int H, int D, void* dst, int64_t sb,
+                        int64_t st, int64_t sh, hipStream_t st_) {
+  const int64_t n = rows * H * D;
+  if (n == 0) return;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (f32)
+    unpad_heads_kernel<float><<<blocks, 256, 0, st_>>>((const float*)src, S, H, D, n, (float*)dst, sb, st, sh);
+  else
+    unpad_heads_kernel<uint16_t><<<blocks, 256, 0, st_>>>((const uint16_t*)src, S, H, D, n, (uint16_t*)dst, sb, st,
+                                                          sh);
 }
 
 }  // namespace ttt

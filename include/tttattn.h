@@ -110,7 +110,12 @@ typedef struct ttt_attn_desc {
                                  non-decreasing                                            */
   int32_t num_q_heads;        /* Hq                                                        */
   int32_t num_kv_heads;       /* Hkv; Hq % Hkv == 0                                        */
-  int32_t head_dim;           /* D: 32, 64 or 128 (fp32); 128 (bf16)                       */
+  int32_t head_dim;           /* D: 32, 64 or 128.  bf16 32 / 64 (ttt_attn_fwd / _bwd /
+                                 _workspace_bytes only): the D = 128 kernels on zero-
+                                 padded copies of the heads in the workspace (entry k <
+                                 D/2 at (128/D) k, D/2 + k at 64 + (128/D) k: the same
+                                 rotate-half pairs and angles), softmax_scale <= 0 meaning
+                                 1/sqrt(D); 2x / 4x the D = 128 MFMA work                  */
   int32_t pass_index;         /* p, 1 .. TTT_MAX_PASSES                                    */
   float softmax_scale;        /* <= 0 selects 1/sqrt(D)                                    */
   float rope_base;            /* RoPE base; 0 disables the rotation                        */

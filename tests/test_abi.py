@@ -102,8 +102,25 @@ def test_bad_descriptor_fields(field, value, code):
 
 
 def test_bf16_head_dim_and_o_dtype_rules():
-    d = good_desc(D=64)
-    assert call_fwd(d) == 3 and "head_dim" in err()
+    lib = tk.library()
+    # bf16 head_dim 32 / 64 run on zero-padded heads: a workspace for the padded copies
+    # plus the D = 128 call's own; refused before any launch when it is too small
+    w128 = lib.ttt_attn_workspace_bytes(ctypes.byref(good_desc(D=128)), 0)
+    for D in (32, 64):
+        d = good_desc(D=D)
+        w = lib.ttt_attn_workspace_bytes(ctypes.byref(d), 0)
+        assert w > w128
+        assert lib.ttt_attn_workspace_bytes(ctypes.byref(d), 1) > w
+        assert call_fwd(d, ws_bytes=w - 1) == 5 and "workspace" in err()
+        assert call_fwd(d, q=None) == 1
+    for D in (48, 96):
+        assert call_fwd(good_desc(D=D)) == 3 and "head_dim" in err()
+    # the padded route serves the whole-sequence calls only
+    assert call_chunk(good_desc(D=64), good_chunk()) == 3 and "head_dim" in err()
+    assert call_block(block_desc(), good_block()) != 3
+    d64 = block_desc()
+    d64.head_dim = 64
+    assert call_block(d64, good_block()) == 3 and "head_dim" in err()
     d = good_desc(dtype=tk.DTYPE_FP32)
     d.o_dtype = tk.DTYPE_BF16
     assert call_fwd(d) == 3 and "o_dtype" in err()
