@@ -125,3 +125,57 @@ def test_thd_block_rejects_partial_blocks(dev, tk):
     with pytest.raises(tk.TTTAttnError, match="whole blocks"):
         tk.block_fwd(inp.gq, inp.gkc, inp.gvc, inp.gkb, inp.gvb, inp.ga, 16, cu_seqlens=bad,
                      ctx_cu_seqlens=inp.gccu, rope_base=inp.base, check_cu_seqlens=True)
+
+
+def test_thd_block_fullsize(dev, tk):
+    """The packed block-draft bench shape (the 16 thd_32k sequences as contexts, 64 blocks of 16 slots
+    each, 16384 block rows, 32/8 heads): O and LSE against the oracle on >= 4096 sampled rows, and the
+    context dK/dV of one whole sequence and KV head (every block row that sees it) plus dQ on the
+    sampled rows' heads against the oracle."""
+    w = syn.workload("thd_32k")
+    ctx = w.lengths()
+    inp = ThdBlock(dev, [(64, c) for c in ctx], 16, w.Hq, w.Hkv, 77)
+    o, lse = tk.block_fwd(inp.gq, inp.gkc, inp.gvc, inp.gkb, inp.gvb, inp.ga, 16, o_fp32=True, **inp.geo())
+    grads = tk.block_bwd(inp.gq, inp.gkc, inp.gvc, inp.gkb, inp.gvb, inp.ga, 16, o.to(torch.bfloat16), lse, inp.gdo,
+                         **inp.geo())
+    torch.cuda.synchronize()
+    og, lg = to_np(o), to_np(lse)
+    rng = np.random.default_rng(78)
+    eo = el = 0.0
+    n = 0
+    bs = 16
+    for s in range(len(ctx)):
+        a, e, ca, ce = int(inp.cu[s]), int(inp.cu[s + 1]), int(inp.ccu[s]), int(inp.ccu[s + 1])
+        sub = lambda x: x[None]
+        for h in rng.choice(w.Hq, 4, replace=False):
+            rows = np.unique(np.concatenate([rng.integers(0, e - a, 72), [0, bs - 1, e - a - 1]]))
+            o_ref, l_ref = O.block_fwd_rows(sub(inp.q[a:e]), sub(inp.kc[ca:ce]), sub(inp.vc[ca:ce]), sub(inp.kb[a:e]),
+                                            sub(inp.vb[a:e]), inp.anchors[None, a // bs:e // bs], bs, 0, int(h), rows,
+                                            base=inp.base)
+            eo = max(eo, max_abs(og[a + rows, h], o_ref))
+            el = max(el, max_abs(lg[h, a + rows], l_ref))
+            n += len(rows)
+    print(f"blk_thd_32k: {n} sampled rows, O max-abs {eo:.3e} LSE max-abs {el:.3e}")
+    assert n >= 4096 and eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
+    # one whole (sequence, KV head): context dK/dV from every row of its 64 blocks (4 heads), and dQ
+    s, g = int(np.argmax(ctx)), 3
+    a, e, ca, ce = int(inp.cu[s]), int(inp.cu[s + 1]), int(inp.ccu[s]), int(inp.ccu[s + 1])
+    r = w.Hq // w.Hkv
+    dkc = np.zeros((ce - ca, w.D))
+    dvc = np.zeros((ce - ca, w.D))
+    dqs, dqr = [], []
+    for hh in range(g * r, (g + 1) * r):
+        dq_, dkc_, dvc_, _, _ = O.block_bwd_rows(inp.q[None, a:e], inp.kc[None, ca:ce], inp.vc[None, ca:ce],
+                                                 inp.kb[None, a:e], inp.vb[None, a:e],
+                                                 inp.anchors[None, a // bs:e // bs], bs, inp.do[None, a:e], 0, hh,
+                                                 np.arange(e - a), base=inp.base)
+        dkc += dkc_
+        dvc += dvc_
+        dqs.append(to_np(grads[0])[a:e, hh])
+        dqr.append(dq_)
+    e_k = rel_fro(to_np(grads[1])[ca:ce, g], dkc)
+    e_v = rel_fro(to_np(grads[2])[ca:ce, g], dvc)
+    e_q = rel_fro(np.stack(dqs), np.stack(dqr))
+    print(f"blk_thd_32k bwd vs oracle, sequence {s} (context {ce - ca}) KV head {g}: dK_ctx {e_k:.2e} "
+          f"dV_ctx {e_v:.2e} dQ {e_q:.2e}")
+    assert max(e_k, e_v, e_q) <= TOL["bf16"]["grad"]

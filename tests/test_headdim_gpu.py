@@ -85,8 +85,8 @@ def test_head_dim_window_and_scale(dev, tk):
 
 
 def test_head_dim_strided_outputs_untouched(dev, tk):
-    """Heads inside a wider buffer (q and k as slices of a [.., 2D] tensor): the results equal the
-    contiguous call's bitwise and the other half of the buffer is left as it was."""
+    """O written into a slice of a wider [.., 2D] buffer: the result equals the contiguous
+    call's bitwise and the other half of the buffer is left as it was."""
     D, p = 64, 2
     w = syn.Workload("hd64_strided", 64, "bshd", 2, 100, 8, 2, D, p, "bf16", 1e6, True)
     inp = Inputs(w, dev)

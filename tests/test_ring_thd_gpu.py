@@ -240,3 +240,42 @@ def test_thd_step_rejects_bad_kv_cu(dev, tk):
         tk.fwd_chunk(inp.gq[2], [inp.gk[0]], [inp.gv[0]], 2, with_branch=False, cu_seqlens=inp.cu,
                      kv_cu_seqlens=i32(kcu, dev), q_offsets=i32(np.zeros(len(LENS)), dev),
                      kv_offsets=i32(np.zeros(len(LENS)), dev), max_position=300, check_cu_seqlens=True)
+
+
+def test_thd_ring_fullsize_thd_32k(dev, tk):
+    """thd_32k (16 packed sequences of 256..4096 tokens, T = 32768, 32/8 heads) over a zig-zag ring of
+    2 ranks (every sequence in 4 chunks) at pass 3: the ring's merged O and LSE against one
+    whole-sequence THD call on every element and against the oracle on >= 4096 sampled rows (plus
+    every sequence's first, second and last row); the backward terms summed over the ring against
+    the whole-sequence backward on every element."""
+    from ttt_cases import sample_rows
+    w = syn.workload("thd_32k")
+    inp = Inputs(w, dev, passes=w.K)
+    p, cp = w.K, 2
+    ro, rl = zigzag_thd(tk, inp, p, cp, dev)
+    so, sl = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, o_fp32=True, **inp.kw())
+    torch.cuda.synchronize()
+    d_o, d_l = (ro - so).abs().max().item(), (rl - sl).abs().max().item()
+    print(f"thd_32k ring cp={cp} p={p}: vs single THD call O {d_o:.3e} LSE {d_l:.3e}")
+    assert d_o <= TOL["bf16"]["o"] and d_l <= TOL["bf16"]["lse"]
+    slices = inp.slices()
+    eo = el = 0.0
+    n = 0
+    ro_np, rl_np = to_np(ro), to_np(rl)
+    for (pp, s, h), rows in sample_rows(inp, 4096, 31, [p]).items():
+        sl_ = slices[s]
+        o_ref, l_ref = O.fwd_rows(inp.q[p], inp.k, inp.v, p, sl_, h, rows, layout="thd", Hq=w.Hq, Hkv=w.Hkv,
+                                  scale=w.scale, base=w.rope_base)
+        eo = max(eo, max_abs(ro_np[sl_.start + rows, h], o_ref))
+        el = max(el, max_abs(rl_np[h, sl_.start + rows], l_ref))
+        n += len(rows)
+    print(f"thd_32k ring vs oracle on {n} sampled rows: O {eo:.3e} LSE {el:.3e}")
+    assert n >= 4096 and eo <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
+    o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **inp.kw())
+    gq, gk, gv = zigzag_thd(tk, inp, p, cp, dev, o=o, lse=lse)
+    sq, sk, sv = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, **inp.kw())
+    torch.cuda.synchronize()
+    errs = [rel_fro(to_np(gq), to_np(sq))] + [rel_fro(to_np(gk[t]), to_np(sk[t])) for t in range(p)] + \
+           [rel_fro(to_np(gv[t]), to_np(sv[t])) for t in range(p)]
+    print(f"thd_32k ring bwd vs single THD call: worst rel Frobenius {max(errs):.2e}")
+    assert max(errs) <= TOL["bf16"]["grad"]
