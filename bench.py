@@ -38,6 +38,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="b4_s4k")
+    ap.add_argument("--head-dim", type=int, default=0, metavar="D",
+                    help="run the unroll at head_dim D (32 or 64: bf16 on zero-padded heads) instead of the "
+                         "workload's 128; FLOPs count the D-dim work")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel event timing")
@@ -675,6 +678,9 @@ def main():
     global WINDOW
     WINDOW = max(0, args.window)
     w = syn.workload(args.workload)
+    if args.head_dim:
+        import dataclasses
+        w = dataclasses.replace(w, D=args.head_dim, name=f"{w.name}_d{args.head_dim}")
     if args.ring:
         ring_main(args, w, dev)
         return
