@@ -429,35 +429,52 @@ template <typename T>
 __global__ void __launch_bounds__(256) pad_heads_kernel(const T* __restrict__ src, int64_t sb, int64_t st,
                                                         int64_t sh, int S, int H, int D, int64_t n,
                                                         T* __restrict__ dst) {
+  // one thread per 16 bytes of a padded head (V entries)
+  constexpr int V = 16 / sizeof(T), CH = 128 / V;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= n) return;
-  const int j = (int)(idx & 127);
-  const int64_t rh = idx >> 7;
+  const int c = (int)(idx % CH);
+  const int64_t rh = idx / CH;
   const int h = (int)(rh % H);
   const int64_t r = rh / H;
+  const T* row = src + (r / S) * sb + (r % S) * st + h * sh;
   const int sp = 128 / D, half = D / 2;
-  const int jj = j & 63;
-  T v = T(0);
-  if (jj % sp == 0) {
-    const int k = jj / sp + (j >= 64 ? half : 0);
-    v = src[(r / S) * sb + (r % S) * st + h * sh + k];
+  T v[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    const int j = c * V + e, jj = j & 63;
+    v[e] = (jj % sp == 0) ? row[jj / sp + (j >= 64 ? half : 0)] : T(0);
   }
-  dst[idx] = v;
+  *(u32x4*)(dst + idx * V) = *(const u32x4*)v;
 }
 
 // The inverse: the D real entries of each padded head back to the caller's strides.
-template <typename T>
+// VEC: one thread per 16 bytes of a head (the caller's pointer and strides allow
+// it), else one thread per entry.
+template <typename T, bool VEC>
 __global__ void __launch_bounds__(256) unpad_heads_kernel(const T* __restrict__ src, int S, int H, int D, int64_t n,
                                                           T* __restrict__ dst, int64_t sb, int64_t st, int64_t sh) {
+  constexpr int V = VEC ? 16 / sizeof(T) : 1;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= n) return;
-  const int k = (int)(idx % D);
-  const int64_t rh = idx / D;
+  const int per = D / V;
+  const int c = (int)(idx % per);
+  const int64_t rh = idx / per;
   const int h = (int)(rh % H);
   const int64_t r = rh / H;
+  const T* in = src + rh * 128;
+  T* out = dst + (r / S) * sb + (r % S) * st + h * sh + c * V;
   const int sp = 128 / D, half = D / 2;
-  const int j = k < half ? sp * k : 64 + sp * (k - half);
-  dst[(r / S) * sb + (r % S) * st + h * sh + k] = src[rh * 128 + j];
+  T v[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    const int k = c * V + e;
+    v[e] = in[k < half ? sp * k : 64 + sp * (k - half)];
+  }
+  if constexpr (VEC)
+    *(u32x4*)out = *(const u32x4*)v;
+  else
+    out[0] = v[0];
 }
 
 // ----------------------------------------------------------------------------- launchers
@@ -571,7 +588,7 @@ void launch_tile_sched(const Prob& P, int tile, int desc, int4* out, int max_ent
 
 void launch_pad_heads(const void* src, bool f32, int64_t sb, int64_t st, int64_t sh, int64_t rows, int S, int H,
                       int D, void* dst, hipStream_t st_) {
-  const int64_t n = rows * H * 128;
+  const int64_t n = rows * H * (f32 ? 32 : 16);  // 16-byte pieces of the padded heads
   if (n == 0) return;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (f32)
@@ -580,16 +597,26 @@ void launch_pad_heads(const void* src, bool f32, int64_t sb, int64_t st, int64_t
     pad_heads_kernel<uint16_t><<<blocks, 256, 0, st_>>>((const uint16_t*)src, sb, st, sh, S, H, D, n, (uint16_t*)dst);
 }
 
-void launch_unpad_heads(const void* src, bool f32, int64_t rows, int S, int H, int D, void* dst, int64_t sb,
-                        int64_t st, int64_t sh, hipStream_t st_) {
-  const int64_t n = rows * H * D;
+template <typename T>
+static void unpad_as(const void* src, int64_t rows, int S, int H, int D, void* dst, int64_t sb, int64_t st,
+                     int64_t sh, hipStream_t st_) {
+  constexpr int V = 16 / sizeof(T);
+  const bool vec = ((uintptr_t)dst % 16) == 0 && sb % V == 0 && st % V == 0 && sh % V == 0;
+  const int64_t n = rows * H * (vec ? D / V : D);
   if (n == 0) return;
   const unsigned blocks = (unsigned)((n + 255) / 256);
-  if (f32)
-    unpad_heads_kernel<float><<<blocks, 256, 0, st_>>>((const float*)src, S, H, D, n, (float*)dst, sb, st, sh);
+  if (vec)
+    unpad_heads_kernel<T, true><<<blocks, 256, 0, st_>>>((const T*)src, S, H, D, n, (T*)dst, sb, st, sh);
   else
-    unpad_heads_kernel<uint16_t><<<blocks, 256, 0, st_>>>((const uint16_t*)src, S, H, D, n, (uint16_t*)dst, sb, st,
-                                                          sh);
+    unpad_heads_kernel<T, false><<<blocks, 256, 0, st_>>>((const T*)src, S, H, D, n, (T*)dst, sb, st, sh);
+}
+
+void launch_unpad_heads(const void* src, bool f32, int64_t rows, int S, int H, int D, void* dst, int64_t sb,
+                        int64_t st, int64_t sh, hipStream_t st_) {
+  if (f32)
+    unpad_as<float>(src, rows, S, H, D, dst, sb, st, sh, st_);
+  else
+    unpad_as<uint16_t>(src, rows, S, H, D, dst, sb, st, sh, st_);
 }
 
 }  // namespace ttt

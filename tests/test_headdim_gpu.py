@@ -84,16 +84,22 @@ def test_head_dim_window_and_scale(dev, tk):
     check(tk, inp, 2, "D=64 scale 0.18", scale=0.18)
 
 
-def test_head_dim_strided_outputs_untouched(dev, tk):
-    """O written into a slice of a wider [.., 2D] buffer: the result equals the contiguous
-    call's bitwise and the other half of the buffer is left as it was."""
+@pytest.mark.parametrize("o_fp32", [False, True])
+def test_head_dim_strided_outputs_untouched(dev, tk, o_fp32):
+    """O written into a slice of a wider buffer: [.., 2D] (16-byte aligned rows, the vector
+    unpadding) and [.., D+1] from entry 1 (unaligned, the per-entry unpadding).  The result equals
+    the contiguous call's bitwise and the rest of the buffer is left as it was."""
     D, p = 64, 2
     w = syn.Workload("hd64_strided", 64, "bshd", 2, 100, 8, 2, D, p, "bf16", 1e6, True)
     inp = Inputs(w, dev)
-    o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **inp.kw())
-    big = torch.full((2, 100, 8, 2 * D), 7.0, dtype=torch.bfloat16, device=dev)
-    out = big[..., :D]
-    tk.fwd(inp.gq[p], inp.gk, inp.gv, p, out=out, **inp.kw())
-    torch.cuda.synchronize()
-    assert torch.equal(out, o)
-    assert torch.all(big[..., D:] == 7.0).item()
+    dt = torch.float32 if o_fp32 else torch.bfloat16
+    o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, o_fp32=o_fp32, **inp.kw())
+    for width, lo in ((2 * D, 0), (D + 1, 1)):
+        big = torch.full((2, 100, 8, width), 7.0, dtype=dt, device=dev)
+        out = big[..., lo:lo + D]
+        tk.fwd(inp.gq[p], inp.gk, inp.gv, p, out=out, o_fp32=o_fp32, **inp.kw())
+        torch.cuda.synchronize()
+        assert torch.equal(out, o)
+        rest = torch.ones_like(big, dtype=torch.bool)
+        rest[..., lo:lo + D] = False
+        assert torch.all(big[rest] == 7.0).item()
