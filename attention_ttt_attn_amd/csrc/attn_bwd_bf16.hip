@@ -72,9 +72,19 @@ struct DqBuf {
   uint16_t v[QBN * D];   // V rows, same layout
   _Float16 kt[D * QBN];  // K~^T: d-row at d*QBN, chunk c at slot c ^ ((d >> 2) & 3)
 };
+// Stored dS (MODE 5): the tile's K~^T and every wave's 32x32 dS block, which
+// lies at [key][quarter u*2 + w][8 rows 16 u + 8 w + 0..7] (64 bytes per key):
+// a transposing read then meets each bank twice per instruction, the least
+// its 512 bytes allow.
+struct DsBuf {
+  _Float16 kt[D * QBN];    // K~^T, as in DqBuf
+  _Float16 ds[4][32 * 32]; // one block per wave
+};
+constexpr int DS_NB = 4;  // stored dS: tile buffers (loads run DS_NB - 1 tiles ahead)
 struct DqSmem {
   union {
     DqBuf buf[2];
+    DsBuf dbuf[DS_NB];
     float acc[128][OPAD];  // dQ~ rows (wave, row) for the row-major epilogue
   };
 };
@@ -83,9 +93,11 @@ __host__ __device__ constexpr int dq_rows(int heads_per_wg) { return 32 * 4 / he
 static int dq_heads_per_wg(int r) { return r % 4 == 0 ? 4 : (r % 2 == 0 ? 2 : 1); }
 
 // MODE 0: TTT pass; MODE 4: the same with a sliding-window trunk (its own
-// instantiation).  MODE 1: block drafting -- key tiles of the context
-// (kt/ktt, V = kv.v[0] with the P.cs strides) up to each row's block anchor,
-// then the keys of the work item's own blocks (kbt/kbtt, V = kv.v[1]).
+// instantiation); MODE 5: a whole-sequence BSHD TTT pass whose trunk dS the
+// dK/dV kernel stored (P.ds): dQ~^T = K~^T dS^T from those blocks, no S or dP
+// products.  MODE 1: block drafting -- key tiles of the context (kt/ktt, V =
+// kv.v[0] with the P.cs strides) up to each row's block anchor, then the keys
+// of the work item's own blocks (kbt/kbtt, V = kv.v[1]).
 template <int RH, int MODE>
 __global__ void __launch_bounds__(256, 2)
     dq_bf16_kernel(Prob P, const uint16_t* __restrict__ q, PassPtrs kv, const float* __restrict__ lse,
@@ -96,7 +108,8 @@ __global__ void __launch_bounds__(256, 2)
                    PassGradPtrs gr) {
   constexpr int RT = dq_rows(RH);  // rows per work item
   __shared__ __attribute__((aligned(16))) DqSmem sm;
-  constexpr bool TTT_ = MODE == 0 || MODE == 4;  // TTT pass (4: with a sliding window)
+  constexpr bool DSM = MODE == 5;  // trunk dS stored by the dK/dV kernel
+  constexpr bool TTT_ = MODE == 0 || MODE == 4 || DSM;  // TTT pass (4: with a sliding window)
   const int win = MODE == 4 ? P.win : 0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -207,12 +220,12 @@ __global__ void __launch_bounds__(256, 2)
   auto dma = [&](DqBuf* __restrict__ dst, int j) __attribute__((always_inline)) {
     dma_from(dst, kbase, ktbase, vbase, vs_t, j * QBN, vlast);
   };
-  if (kt_lo < nkt) dma(&sm.buf[0], kt_lo);
+  if (!DSM && kt_lo < nkt) dma(&sm.buf[0], kt_lo);
 
   // B operands of this lane's query: Q~ (fp16, pre-rotated) and dO (bf16)
   f16x8 qf[8];
   bf16x8 dof[8];
-  {
+  if constexpr (!DSM) {
     const _Float16* qrow = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row) * D;
     const uint16_t* grow = dout + b * P.os_b + (int64_t)(start + my_row) * P.os_t + h * P.os_h;
 #pragma unroll
@@ -224,15 +237,18 @@ __global__ void __launch_bounds__(256, 2)
     }
   }
   // rows past the sequence end get LSE = +inf: every probability is then 0
-  const float lse2 = row_ok ? lse[b * P.lse_b + h * P.lse_h + start + my_row] * kLog2e : INFINITY;
-  float dl = delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row];
+  const float lse2 = DSM ? 0.f : (row_ok ? lse[b * P.lse_b + h * P.lse_h + start + my_row] * kLog2e : INFINITY);
+  float dl = DSM ? 0.f : delta[(int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row];
   // fp16 dS operands of this row carry the factor 2^e: |dS_ij| <= ||dO_i||_1
   // max_j |v_jd| + |Delta_i| over the keys this work item visits (their
   // per-32-key maxima come from the dK/dV kernel, which runs first).  The
   // factor scales the row's dO operand (which feeds dP only) and Delta, so
   // P (dP - Delta) 2^e is formed exactly; the epilogue takes it out again.
   int eq;
-  {
+  if constexpr (DSM) {  // the stored blocks' exponent: the dK/dV kernel's, for the whole group
+    const float2 nd = *(const float2*)&P.dmax[(int64_t)(b * P.Hkv + g) * 2];
+    eq = ds_exp(__builtin_fmaf(nd.x, P.vgmax[b * P.Hkv + g], nd.y));
+  } else {
     const int64_t vb = (int64_t)(b * P.Hkv + g) * (P.spad / 32) + slot0 / 32;
     float vm = TTT_ ? range_max(P.vmax + vb, kt_lo, nkt, lane) : range_max(P.vmax + vb, 0, nkt, lane);
     if constexpr (MODE == 1) vm = fmaxf(vm, range_max(P.vmax_b + vb, row0 / 32, (qend + 31) / 32, lane));
@@ -314,17 +330,100 @@ __global__ void __launch_bounds__(256, 2)
       for (int d4 = 0; d4 < 4; ++d4) acc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[d4], dsb[c2], acc[d4], 0, 0, 0);
     }
   };
-  for (int j = kt_lo; j < nkt; ++j) {
-    // distinct restrict pointers: the loads into the other buffer cannot alias
-    // this tile's LDS reads, so the compiler puts no wait on them
-    auto step = [&](const DqBuf* __restrict__ cur, DqBuf* __restrict__ nxt) __attribute__((always_inline)) {
-      if (j + 1 < nkt) dma(nxt, j + 1);
-      if (j < n_free && j >= f_lo) tile(cur, j * QBN, std::integral_constant<int, 0>{});
-      else tile(cur, j * QBN, std::integral_constant<int, TTT_ ? 1 : 2>{});
+  if constexpr (!DSM) {
+    for (int j = kt_lo; j < nkt; ++j) {
+      // distinct restrict pointers: the loads into the other buffer cannot alias
+      // this tile's LDS reads, so the compiler puts no wait on them
+      auto step = [&](const DqBuf* __restrict__ cur, DqBuf* __restrict__ nxt) __attribute__((always_inline)) {
+        if (j + 1 < nkt) dma(nxt, j + 1);
+        if (j < n_free && j >= f_lo) tile(cur, j * QBN, std::integral_constant<int, 0>{});
+        else tile(cur, j * QBN, std::integral_constant<int, TTT_ ? 1 : 2>{});
+      };
+      step(&sm.buf[(j - kt_lo) & 1], &sm.buf[(j - kt_lo + 1) & 1]);
+      TTT_WAIT_VMCNT(0);  // tile j+1 has landed
+      __syncthreads();    // and every wave is done with tile j
+    }
+  } else {
+    // dQ~^T += K~^T dS^T over key groups j = 0 .. rb of this wave's row block
+    // rb.  DS_NB buffers, loads DS_NB - 1 tiles ahead; each wave loads the
+    // K~^T quarter of its lanes' roles and its own dS block (4 loads per tile).
+    // wave-uniform in scalar registers: the dS loads' buffer descriptors and
+    // the compute branch stay scalar
+    const int rbw = __builtin_amdgcn_readfirstlane(wave_row0 >> 5);
+    const int hu = __builtin_amdgcn_readfirstlane(h);
+    const bool wave_on = (rbw << 5) < L;
+    const int rbl = min(rbw, ((L + 31) >> 5) - 1);  // loads stay inside this head's blocks
+    const _Float16* dsh = P.ds + ((int64_t)(b * P.Hq + hu) * P.ds_tri + (int64_t)rbl * (rbl + 1) / 2) * 1024;
+    uint32_t dso[2];  // piece c = 64 i + lane -> LDS slot c: key c/4, quarter c%4
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = 64 * i + lane, key = c >> 2, qu = c & 3;
+      dso[i] = (uint32_t)((qu >> 1) * 1024 + ((qu & 1) * 32 + key) * 16);
+    }
+    // transposing reads of the dS^T operand (lane: row n = lane % 32, keys
+    // 8 (lane / 32) + 4 ri + 0..3 of chunk c2): 16-lane group G serves rows
+    // 16 (G % 2) + 0..15; its lane s points at key 4 ri + s/4 + (chunk base),
+    // rows 4 (s % 4) + 0..3 of that half
+    uint32_t tro[2][2];
+    {
+      const int G = lane >> 4, s16 = lane & 15;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int ri = 0; ri < 2; ++ri) {
+          const int key = 16 * c2 + 8 * (G >> 1) + 4 * ri + (s16 >> 2);
+          const int qu = (G & 1) * 2 + ((s16 & 3) >> 1);
+          tro[c2][ri] = (uint32_t)((key * 4 + qu) * 16 + (s16 & 1) * 8);
+        }
+    }
+    auto dsdma = [&](DsBuf* __restrict__ dst, int j) __attribute__((always_inline)) {
+      DsBuf& B_ = *dst;
+      const buf_rsrc tr = make_rsrc(ktbase + j * QBN, kt_bytes);
+      const buf_rsrc dr = make_rsrc(dsh + (int64_t)min(j, rbl) * 1024, 2048);
+      const int wu = __builtin_amdgcn_readfirstlane(wv);  // the LDS bases stay scalar
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma16(tr, toff[i] * 2, &B_.kt[16 * (2 * wu + i) * QBN]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma16_nt(dr, dso[i], &B_.ds[wu][512 * i]);
     };
-    step(&sm.buf[(j - kt_lo) & 1], &sm.buf[(j - kt_lo + 1) & 1]);
-    TTT_WAIT_VMCNT(0);  // tile j+1 has landed
-    __syncthreads();    // and every wave is done with tile j
+    // wait until tile t has landed, given the tiles issued after it: 4 loads each
+    auto wait_tile = [&](int t) __attribute__((always_inline)) {
+      const int later = min(nkt - 1, t + DS_NB - 2) - t;
+      static_assert(DS_NB == 4, "the waits below cover 0..2 later tiles");
+      if (later >= 2) TTT_WAIT_VMCNT(8);
+      else if (later == 1) TTT_WAIT_VMCNT(4);
+      else TTT_WAIT_VMCNT(0);
+    };
+#pragma unroll
+    for (int t = 0; t < DS_NB - 1; ++t)
+      if (t < nkt) dsdma(&sm.dbuf[t], t);
+    wait_tile(0);
+    lds_ring_barrier();
+    for (int j = 0; j < nkt; ++j) {
+      auto step = [&](const DsBuf* __restrict__ cur, DsBuf* __restrict__ ahead) __attribute__((always_inline)) {
+        if (j + DS_NB - 1 < nkt) dsdma(ahead, j + DS_NB - 1);
+        if (wave_on && j <= rbw) {
+          const DsBuf& B_ = *cur;
+          const char* dsw = (const char*)&B_.ds[wv][0];
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const s16x4 x0 = lds_read_tr16(dsw + tro[c2][0]), x1 = lds_read_tr16(dsw + tro[c2][1]);
+            const f16x8 bop = __builtin_bit_cast(f16x8, __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7));
+            f16x8 a[4];
+#pragma unroll
+            for (int d4 = 0; d4 < 4; ++d4) {
+              const int d = d4 * 32 + l32;
+              a[d4] = *(const f16x8*)&B_.kt[d * QBN + (((2 * c2 + hf) ^ ((d >> 2) & 3)) * 8)];
+            }
+#pragma unroll
+            for (int d4 = 0; d4 < 4; ++d4) acc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[d4], bop, acc[d4], 0, 0, 0);
+          }
+        }
+      };
+      step(&sm.dbuf[j % DS_NB], &sm.dbuf[(j + DS_NB - 1) % DS_NB]);
+      wait_tile(j + 1);    // tile j+1 has landed
+      lds_ring_barrier();  // and every wave is done with tile j
+    }
   }
   // block drafting: the keys of the work item's own blocks (bs divides 32, so
   // the blocks of rows row0 .. qend-1 are exactly key rows row0 .. qend-1)
@@ -635,7 +734,8 @@ __global__ void __launch_bounds__(256, 1)
                      const float* __restrict__ delta, const int4* __restrict__ tiles, const float* __restrict__ cosT,
                      const float* __restrict__ sinT, PassGradPtrs gr) {
   __shared__ __attribute__((aligned(16))) KvBuf sm[NBUF];
-  constexpr bool TTT_ = MODE == 0 || MODE == 4;  // TTT pass (4: with a sliding window)
+  // TTT pass (4: with a sliding window; 5: also storing dS for the dQ kernel)
+  constexpr bool TTT_ = MODE == 0 || MODE == 4 || MODE == 5;
   const int win = MODE == 4 ? P.win : 0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
@@ -758,7 +858,7 @@ __global__ void __launch_bounds__(256, 1)
       vinf = fmaxf(vinf, fmaxf(fabsf(__uint_as_float(x[w] << 16)), fabsf(__uint_as_float(x[w] & 0xffff0000u))));
   }
   vinf = xhalf_max(vinf);  // the key's whole row
-  {
+  if constexpr (MODE != 5) {
     float wmax = vinf;  // the wave's 32 keys, for the dQ kernel's bound
 #pragma unroll
     for (int m = 1; m < 32; m <<= 1) wmax = fmaxf(wmax, __shfl_xor(wmax, m, 64));
@@ -769,7 +869,9 @@ __global__ void __launch_bounds__(256, 1)
       vm[(int64_t)(b * P.Hkv + g) * (P.spad / 32) + (slot0 + kv0) / 32 + wv] = wmax;
   }
   const float2 nd = *(const float2*)&P.dmax[(int64_t)(b * P.Hkv + g) * 2];
-  const int ek = ds_exp(__builtin_fmaf(nd.x, vinf, nd.y));
+  // stored dS: one exponent for the whole KV group (the dQ kernel forms the
+  // same one), from the group's largest |v_jd|
+  const int ek = ds_exp(__builtin_fmaf(nd.x, MODE == 5 ? P.vgmax[b * P.Hkv + g] : vinf, nd.y));
   const float cj = __builtin_amdgcn_ldexpf(1.0f, ek);
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
@@ -887,9 +989,29 @@ __global__ void __launch_bounds__(256, 1)
   // pointers: the compiler then knows the loads into the step-(st+3) buffer
   // cannot alias this iteration's LDS reads and puts no wait on them.
   int cs_h = 0, cs_q0 = row_lo + (nq - 1) * BQ;  // the step being computed
+  // Stored dS (MODE 5): step st's block is written at the start of step st+1
+  // (before that step's loads are issued), so the stores have a whole step to
+  // drain before the step's closing vmcnt wait.  Blocks above the diagonal
+  // (row block < key group) are not part of the layout.
+  f16x8 dsp[2];
+  int sp_h = 0, sp_q0 = 0;
+  const int kgrp = (kv0 >> 5) + wv;  // this wave's key group of 32
+  auto store_ds = [&]() __attribute__((always_inline)) {
+    const int rb = sp_q0 >> 5;
+    if (rb >= kgrp) {
+      _Float16* blk =
+          P.ds + ((int64_t)(b * P.Hq + g * P.r + sp_h) * P.ds_tri + (int64_t)rb * (rb + 1) / 2 + kgrp) * 1024;
+      // read once, by the dQ kernel: non-temporal, so the Q~ / dO rows this
+      // kernel re-reads keep their cache lines
+      __builtin_nontemporal_store(dsp[0], (f16x8*)(blk + lane * 8));
+      __builtin_nontemporal_store(dsp[1], (f16x8*)(blk + 512 + lane * 8));
+    }
+  };
   for (int st = 0; st < nsteps; ++st) {
    auto step = [&](const KvBuf* __restrict__ Bcp, const KvBuf* __restrict__ Bnp, KvBuf* __restrict__ Bdp)
                    __attribute__((always_inline)) {
+    if constexpr (MODE == 5)
+      if (st > 0) store_ds();
     if (st + 3 < nsteps) issue(Bdp);
     const KvBuf& Bc = *Bcp;
     const int q0 = cs_q0;
@@ -927,6 +1049,12 @@ __global__ void __launch_bounds__(256, 1)
         pb[half][e] = (__bf16)pr;
         dsb[half][e] = (_Float16)(pr * __builtin_fmaf(dv_, -cj, dp_c[v]));  // 2^e dS
       }
+    }
+    if constexpr (MODE == 5) {
+      dsp[0] = dsb[0];
+      dsp[1] = dsb[1];
+      sp_h = cs_h;
+      sp_q0 = q0;
     }
     s_c = s_n;
     dp_c = dp_n;
@@ -971,6 +1099,8 @@ __global__ void __launch_bounds__(256, 1)
     }
     lds_ring_barrier();
   }
+  if constexpr (MODE == 5)
+    if (nsteps > 0) store_ds();
   if (!key_ok) return;
   // epilogue: dK = sigma R(j)^T dK~, dV; lane owns key my_key, d = 32*d4 + 8*v4 + 4*hf + e
   const int64_t off = b * P.ks_b + (int64_t)(kst + my_key) * P.ks_t + g * P.ks_h;
@@ -1116,6 +1246,8 @@ void launch_dkdv_bf16(const Prob& P, const PassPtrs& kv, const float* lse, const
   if (grid == 0) return;
   if (P.win > 0)  // sliding window: its own instantiation (MODE 4)
     bwd::dkdv_bf16_kernel<4><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);
+  else if (P.ds)  // also storing dS for the dQ kernel (MODE 5)
+    bwd::dkdv_bf16_kernel<5><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);
   else
     bwd::dkdv_bf16_kernel<0><<<(unsigned)grid, 256, 0, st>>>(P, kv, lse, dout, kt, qt, delta, tiles_kv, cosT, sinT, g);
 }
@@ -1165,6 +1297,14 @@ void launch_dq_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const 
                     const int4* tiles_q, const float* cosT, const float* sinT, uint16_t* dq, const PassGradPtrs& g,
                     hipStream_t st) {
   const bool w = P.win > 0;  // sliding window: its own instantiation (MODE 4)
+  if (P.ds) {  // from the dK/dV kernel's stored dS (MODE 5)
+    switch (bwd::dq_heads_per_wg(P.r)) {
+      case 4: launch_dq_rh<4, 5>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, g, st); break;
+      case 2: launch_dq_rh<2, 5>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, g, st); break;
+      default: launch_dq_rh<1, 5>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, g, st); break;
+    }
+    return;
+  }
   switch (bwd::dq_heads_per_wg(P.r)) {
     case 4:
       if (w) launch_dq_rh<4, 4>(P, q, kv, lse, dout, kt, ktt, qt, delta, tiles_q, cosT, sinT, dq, nullptr, nullptr, g, st);

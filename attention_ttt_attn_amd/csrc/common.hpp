@@ -75,6 +75,18 @@ struct Prob {
   const int* seg_kvoff;
   const int* kv_cu;
   int kv_tok;
+  // Stored dS (bf16 whole-sequence BSHD passes without a window): the dK/dV
+  // kernel writes every causal 32x32 block of 2^e dS in fp16 -- one exponent
+  // e per KV group, from dmax and vgmax -- and the dQ kernel forms dQ~ = dS K~
+  // from them instead of recomputing S and dP.  Block (rb, kg) of query head
+  // (b, h) holds rows 32 rb .. +31 and keys 32 kg .. +31 (kg <= rb) at
+  // ds + ((b Hq + h) ds_tri + rb (rb + 1) / 2 + kg) * 1024; inside it, dS of
+  // row 16 u + 8 w + e and key k sits at element 512 u + 8 (32 w + k) + e
+  // (the dK/dV kernel's register layout: one 16-byte piece per lane).
+  _Float16* ds;
+  int64_t ds_tri;  // blocks per (batch, head): n (n + 1) / 2, n = ceil(S / 32)
+  float* vpart;    // [B*Hkv][spad/64]: per 64-slot block, max |v_jd| of the trunk keys
+  float* vgmax;    // [B*Hkv]: the same over the whole group
 };
 
 // Ring geometry of one sequence (or THD segment): its query rows' position
@@ -308,6 +320,11 @@ __device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) 
 __device__ __forceinline__ void lds_dma16(buf_rsrc r, uint32_t off, void* l) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)l, 16, off, 0, 0, 0);
 }
+// The same for data read once (streamed): the non-temporal hint keeps it from
+// displacing reused lines in the caches.
+__device__ __forceinline__ void lds_dma16_nt(buf_rsrc r, uint32_t off, void* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)l, 16, off, 0, 0, 2);
+}
 __device__ __forceinline__ void lds_dma4(buf_rsrc r, uint32_t off, void* l) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (void __attribute__((address_space(3)))*)l, 4, off, 0, 0, 0);
 }
@@ -346,7 +363,7 @@ __device__ __forceinline__ float xhalf_sum(float x) {
 
 // Workspace layout shared by host launchers.
 struct WsPlan {
-  size_t table, slots, tiles_q, tiles_kv, kt, vt, ktt, qt, delta, bnd, total;
+  size_t table, slots, tiles_q, tiles_kv, kt, vt, ktt, qt, delta, bnd, ds, total;
 };
 
 }  // namespace ttt

@@ -31,13 +31,15 @@ int fail(int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// bf16 backward: the bounds behind the fp16 dS scale (Prob::dnorm .. vmax_b),
-// one workspace region; key_sets = 2 for block drafting (context and block keys).
-size_t bound_bytes(const ttt::Prob& P, int key_sets) {
+// bf16 backward: the bounds behind the fp16 dS scale (Prob::dnorm .. vmax_b,
+// and with stored dS vpart / vgmax), one workspace region; key_sets = 2 for
+// block drafting (context and block keys).
+size_t bound_bytes(const ttt::Prob& P, int key_sets, bool ds = false) {
   return align256((size_t)P.B * P.Hq * P.spad * 4) + align256((size_t)P.B * P.Hq * (P.spad / 64) * 8) +
-         align256((size_t)P.B * P.Hkv * 8) + key_sets * align256((size_t)P.B * P.Hkv * (P.spad / 32) * 4);
+         align256((size_t)P.B * P.Hkv * 8) + key_sets * align256((size_t)P.B * P.Hkv * (P.spad / 32) * 4) +
+         (ds ? align256((size_t)P.B * P.Hkv * (P.spad / 64) * 4) + align256((size_t)P.B * P.Hkv * 4) : 0);
 }
-void set_bounds(ttt::Prob& P, void* region, int key_sets) {
+void set_bounds(ttt::Prob& P, void* region, int key_sets, bool ds = false) {
   char* c = (char*)region;
   P.dnorm = (float*)c;
   c += align256((size_t)P.B * P.Hq * P.spad * 4);
@@ -48,6 +50,10 @@ void set_bounds(ttt::Prob& P, void* region, int key_sets) {
   P.vmax = (float*)c;
   c += align256((size_t)P.B * P.Hkv * (P.spad / 32) * 4);
   P.vmax_b = key_sets > 1 ? (float*)c : nullptr;
+  c += (key_sets - 1) * align256((size_t)P.B * P.Hkv * (P.spad / 32) * 4);
+  P.vpart = ds ? (float*)c : nullptr;
+  c += align256((size_t)P.B * P.Hkv * (P.spad / 64) * 4);
+  P.vgmax = ds ? (float*)c : nullptr;
 }
 
 // Largest token stride (elements) of a caller tensor: the kernels' tile loads
@@ -59,6 +65,7 @@ struct Plan {
   ttt::WsPlan ws;
   bool bf16;
   bool o_f32;
+  bool ds;  // backward with stored dS (TTT_BWD_AUTO on a BSHD pass whose blocks fit the cap)
   int max_tiles_q, max_tiles_kv;
   int64_t k0s_b, k0s_t, k0s_h;  // strides of k[0] / v[0] (ring steps; = kv strides otherwise)
 };
@@ -252,6 +259,19 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
   }
   pl.bf16 = bf16;
   pl.o_f32 = o_f32;
+  // Stored dS: ttt_attn_bwd of a bf16 BSHD pass without a window, when its
+  // causal 32x32 blocks (2 KB each per head) fit the cap.
+  if (d->bwd_mode != TTT_BWD_AUTO && d->bwd_mode != TTT_BWD_RECOMPUTE)
+    return fail(TTT_ERR_BAD_SHAPE, "bwd_mode %d is neither AUTO (0) nor RECOMPUTE (1)", d->bwd_mode);
+  pl.ds = false;
+  if (for_bwd && bf16 && !thd && !c && d->window == 0 && d->bwd_mode == TTT_BWD_AUTO) {
+    const int64_t n = (stok + 31) / 32;
+    const int64_t tri = n * (n + 1) / 2;
+    if ((double)B * Hq * tri * 2048.0 <= (double)TTT_ATTN_STORED_DS_MAX_BYTES) {
+      pl.ds = true;
+      P.ds_tri = tri;
+    }
+  }
 
   // workspace plan
   ttt::WsPlan& w = pl.ws;
@@ -277,7 +297,8 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
       w.ktt = take(nkv * 2);
       w.qt = take(nq * 2);
       w.delta = take((size_t)2 * B * Hq * P.spad * 4);  // Delta, then the LSE in log2 units
-      w.bnd = take(bound_bytes(P, 1));
+      w.bnd = take(bound_bytes(P, 1, pl.ds));
+      if (pl.ds) w.ds = take((size_t)B * Hq * P.ds_tri * 2048);
     }
   } else {
     w.kt = take(nkv * 4);
@@ -799,7 +820,7 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
     TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::kBwdBKV, 0, k, bp.max_tiles_kb, nullptr, st));
     tq = a, tkv = c, tkb = k;
   }
-  TTT_TRACED("bwd_delta", ttt::launch_delta(P, o, pl.o_f32, dout, false, lse, delta, st));
+  TTT_TRACED("bwd_delta", ttt::launch_delta(P, o, pl.o_f32, dout, false, lse, delta, nullptr, st));
   TTT_TRACED("bwd_dmax", ttt::launch_dmax(P, st));
   ttt::PrepJobs J;
   memset(&J, 0, sizeof J);
@@ -1096,9 +1117,10 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
   Side sd;
   const bool forked = pl.bf16 && sd.begin(st);
   const hipStream_t sst = forked ? sd.side : st;
-  if (pl.bf16) set_bounds(P, at<char>(ws, pl.ws.bnd), 1);
+  if (pl.bf16) set_bounds(P, at<char>(ws, pl.ws.bnd), 1, pl.ds);
+  if (pl.ds) P.ds = at<_Float16>(ws, pl.ws.ds);
   TTT_TRACED_ON("bwd_delta", sst,
-                ttt::launch_delta(P, o, pl.o_f32, dout, !pl.bf16, pl.bf16 ? lse : nullptr, delta, sst));
+                ttt::launch_delta(P, o, pl.o_f32, dout, !pl.bf16, pl.bf16 ? lse : nullptr, delta, v[0], sst));
   if (pl.bf16) TTT_TRACED_ON("bwd_dmax", sst, ttt::launch_dmax(P, sst));
   const hipEvent_t delta_done = forked ? sd.mark(sd.side) : nullptr;
   if (!pl.bf16) {
@@ -1143,8 +1165,9 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     Pk.ks_b = pl.k0s_b, Pk.ks_t = pl.k0s_t, Pk.ks_h = pl.k0s_h;
     TTT_TRACED("trunk_dkdv", ttt::launch_dkdv_bf16(Pk, kv, lse, (const uint16_t*)dout, kt, qt, delta, tkv, cosT,
                                                    sinT, g, st));
-    TTT_TRACED("trunk_dq", ttt::launch_dq_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, kt, ktt, qt,
-                                               delta, tq, cosT, sinT, (uint16_t*)dq, g, st));
+    TTT_TRACED(P.ds ? "trunk_dq_ds" : "trunk_dq",
+               ttt::launch_dq_bf16(P, (const uint16_t*)q, kv, lse, (const uint16_t*)dout, kt, ktt, qt, delta, tq, cosT,
+                                   sinT, (uint16_t*)dq, g, st));
     if (forked && branch) sd.wait(st, sd.mark(sd.side));  // the branch gradients are in
   }
   return hip_check("ttt_attn_bwd launch");

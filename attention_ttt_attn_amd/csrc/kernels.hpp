@@ -33,10 +33,12 @@ struct PrepJobs {
 };
 void launch_prep_bf16(const Prob& P, const PrepJobs& J, const float* cosT, const float* sinT, hipStream_t st);
 // Delta (and, with lse, the LSE in log2 units right after it, +inf past the
-// rows' ends) in the workspace slot layout.
+// rows' ends) in the workspace slot layout.  v: the trunk V (bf16, P.cs_*
+// strides), read only when P.vpart is set.
 void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, const float* lse,
-                  float* delta, hipStream_t st);
-// bf16 backward: P.dmax[B*Hkv][2] from the Delta kernel's P.dpart entries
+                  float* delta, const void* v, hipStream_t st);
+// bf16 backward: P.dmax[B*Hkv][2] from the Delta kernel's P.dpart entries (and
+// P.vgmax from P.vpart when set)
 void launch_dmax(const Prob& P, hipStream_t st);
 // bf16 head_dim 32 / 64 on the D = 128 kernels: zero-padded heads (see prep.hip)
 void launch_pad_heads(const void* src, bool f32, int64_t sb, int64_t st, int64_t sh, int64_t rows, int S, int H,

@@ -216,22 +216,28 @@ __device__ __forceinline__ void load8(const float* p, float* x) {
 // layout right after Delta (+inf in slots without a token, so every
 // probability recomputed for them is exactly 0).  With P.dnorm / P.dpart set
 // (bf16 backward), also every row's ||dO||_1 and, per 64-slot block, the
-// largest ||dO||_1 and |Delta| (the bounds of the dS scale).  Grid (spad/64,
-// Hq, B), 256 threads, D/8 threads per row; each thread issues all its rows'
-// loads first.
+// largest ||dO||_1 and |Delta| (the bounds of the dS scale).  With P.vpart
+// set (stored dS), the first head of every KV group also writes the block's
+// largest |v_jd| of the trunk V (key rows = the block's tokens).  Grid
+// (spad/64, Hq, B), 256 threads, D/8 threads per row; each thread issues all
+// its rows' loads first.
 template <int D, typename OT, typename GT>
 __global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict__ o, const GT* __restrict__ dout,
-                                                    const float* __restrict__ lse, float* __restrict__ delta) {
+                                                    const float* __restrict__ lse, float* __restrict__ delta,
+                                                    const uint16_t* __restrict__ vtr) {
   constexpr int TPR = D / 8;
   constexpr int ROWS = 256 / TPR;
   constexpr int NR = 64 / ROWS;  // rows per thread
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, c = tid % TPR;
+  const bool vblk = P.vpart && h % P.r == 0;  // this block also bounds its keys' |v|
+  const int64_t vo = ((int64_t)b * P.Hkv + h / P.r) * (P.spad / 64) + blockIdx.x;
   if (P.layout == 1 && thd_tile_unread(P, P.cu, P.stok, blockIdx.x * 64)) {
     if (P.dpart && tid == 0) {  // the group maxima still read this block's entry
       const int64_t bo = ((int64_t)(b * P.Hq + h) * (P.spad / 64) + blockIdx.x) * 2;
       P.dpart[bo] = P.dpart[bo + 1] = 0.f;
     }
+    if (vblk && tid == 0) P.vpart[vo] = 0.f;
     return;
   }
   int slot[NR], tok[NR];
@@ -264,16 +270,33 @@ __global__ void __launch_bounds__(256) delta_kernel(Prob P, const OT* __restrict
     nmax = fmaxf(nmax, n1);
     dmax = fmaxf(dmax, fabsf(acc));
   }
-  if (P.dpart) {  // the block's 64 slots: one (max ||dO||_1, max |Delta|) entry
-    __shared__ float red[2][4];
+  float vmax = 0.f;
+  if (vblk) {  // the same slots' rows of the group's trunk V (bf16)
+    const int g = h / P.r;
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) nmax = fmaxf(nmax, __shfl_xor(nmax, m, 64)), dmax = fmaxf(dmax, __shfl_xor(dmax, m, 64));
-    if ((tid & 63) == 0) red[0][tid >> 6] = nmax, red[1][tid >> 6] = dmax;
+    for (int i = 0; i < NR; ++i) {
+      if (!valid[i]) continue;
+      float v[8];
+      load8(vtr + (int64_t)b * P.cs_b + (int64_t)tok[i] * P.cs_t + (int64_t)g * P.cs_h + 8 * c, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vmax = fmaxf(vmax, fabsf(v[e]));
+    }
+  }
+  if (P.dpart) {  // the block's 64 slots: one (max ||dO||_1, max |Delta|) entry
+    __shared__ float red[3][4];
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      nmax = fmaxf(nmax, __shfl_xor(nmax, m, 64));
+      dmax = fmaxf(dmax, __shfl_xor(dmax, m, 64));
+      vmax = fmaxf(vmax, __shfl_xor(vmax, m, 64));
+    }
+    if ((tid & 63) == 0) red[0][tid >> 6] = nmax, red[1][tid >> 6] = dmax, red[2][tid >> 6] = vmax;
     __syncthreads();
     if (tid == 0) {
       const int64_t bo = ((int64_t)(b * P.Hq + h) * (P.spad / 64) + blockIdx.x) * 2;
       P.dpart[bo] = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
       P.dpart[bo + 1] = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+      if (vblk) P.vpart[vo] = fmaxf(fmaxf(red[2][0], red[2][1]), fmaxf(red[2][2], red[2][3]));
     }
   }
 }
@@ -300,6 +323,16 @@ __global__ void __launch_bounds__(256) dmax_kernel(Prob P) {
   if (tid == 0) {
     P.dmax[2 * bg] = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
     P.dmax[2 * bg + 1] = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+  }
+  if (P.vgmax) {  // stored dS: the group's largest |v_jd| (its trunk keys' 64-slot blocks)
+    float v = 0.f;
+    for (int i = tid; i < nb; i += 256) v = fmaxf(v, P.vpart[(int64_t)bg * nb + i]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    __syncthreads();
+    if ((tid & 63) == 0) red[0][tid >> 6] = v;
+    __syncthreads();
+    if (tid == 0) P.vgmax[bg] = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
   }
 }
 
@@ -517,16 +550,17 @@ void launch_prep_bf16(const Prob& P, const PrepJobs& J, const float* cosT, const
 void launch_dmax(const Prob& P, hipStream_t st) { dmax_kernel<<<P.B * P.Hkv, 256, 0, st>>>(P); }
 
 void launch_delta(const Prob& P, const void* o, bool o_f32, const void* dout, bool g_f32, const float* lse,
-                  float* delta, hipStream_t st) {
+                  float* delta, const void* v, hipStream_t st) {
   dim3 grid(P.spad / 64, P.Hq, P.B);
+  const uint16_t* vt = (const uint16_t*)v;
 #define TTT_DELTA(DD)                                                                              \
   if (P.D == DD) {                                                                                 \
     if (o_f32 && g_f32)                                                                            \
-      delta_kernel<DD, float, float><<<grid, 256, 0, st>>>(P, (const float*)o, (const float*)dout, lse, delta); \
+      delta_kernel<DD, float, float><<<grid, 256, 0, st>>>(P, (const float*)o, (const float*)dout, lse, delta, vt); \
     else if (o_f32)                                                                                \
-      delta_kernel<DD, float, uint16_t><<<grid, 256, 0, st>>>(P, (const float*)o, (const uint16_t*)dout, lse, delta); \
+      delta_kernel<DD, float, uint16_t><<<grid, 256, 0, st>>>(P, (const float*)o, (const uint16_t*)dout, lse, delta, vt); \
     else                                                                                           \
-      delta_kernel<DD, uint16_t, uint16_t><<<grid, 256, 0, st>>>(P, (const uint16_t*)o, (const uint16_t*)dout, lse, delta); \
+      delta_kernel<DD, uint16_t, uint16_t><<<grid, 256, 0, st>>>(P, (const uint16_t*)o, (const uint16_t*)dout, lse, delta, vt); \
     return;                                                                                        \
   }
   TTT_DELTA(32)

@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--head-dim", type=int, default=0, metavar="D",
                     help="run the unroll at head_dim D (32 or 64: bf16 on zero-padded heads) instead of the "
                          "workload's 128; FLOPs count the D-dim work")
+    ap.add_argument("--bwd-recompute", action="store_true",
+                    help="backward without stored dS: dQ recomputes S and dP (bwd_mode RECOMPUTE)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel event timing")
@@ -94,6 +96,11 @@ def kernel_work(w, name: str, p: int):
         return 8.0 * w.D * w.Hq * tp, "flop"
     if name == "trunk_dq":             # S, dP, dQ
         return 6.0 * w.D * w.Hq * tp, "flop"
+    if name == "trunk_dq_ds":          # dQ from the stored dS blocks: read them and K~^T, write dQ
+        n = (w.S + 31) // 32           # (plus, past pass 1, the branch epilogue's Q, dO and pass keys)
+        ds_bytes = w.B * w.Hq * n * (n + 1) // 2 * 2048
+        branch = T * 2 * row_q + (p - 1) * T * row_kv * 4 if p > 1 else 0
+        return float(ds_bytes + T * row_q + T * row_kv + branch), "byte"
     if name == "branch_bwd":           # read Q, dO, LSE, Delta, (p-1) K, V; write (p-1) dK, dV
         return float(T * (2 * row_q + w.Hq * 8) + (p - 1) * T * row_kv * 4), "byte"
     if name == "prep_kv":              # read K, V (bf16); write rotated fp16 K~ rows and V^T
@@ -701,12 +708,13 @@ def main():
     ws_bytes = max(tk.workspace_bytes(d_f, False), tk.workspace_bytes(d_f, True))
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     kw = dict(cu_seqlens=cu, rope_base=w.rope_base, workspace=ws, window=WINDOW)
+    kwb = dict(kw, recompute_dq=args.bwd_recompute)
 
     def step():
         for p in range(1, K + 1):
             tk.fwd(q[p], ks, vs, p, out=o[p], lse=lse[p], **kw)
         for p in range(K, 0, -1):
-            tk.bwd(q[p], ks, vs, o[p], lse[p], do[p], p, dq=dq[p], dks=dk[p], dvs=dv[p], **kw)
+            tk.bwd(q[p], ks, vs, o[p], lse[p], do[p], p, dq=dq[p], dks=dk[p], dvs=dv[p], **kwb)
 
     for _ in range(args.warmup):
         step()
@@ -740,7 +748,7 @@ def main():
             tk.fwd(q[p], ks, vs, p, out=o[p], lse=lse[p], **kw)
         for p in range(K, 0, -1):
             cur_pass[0] = p
-            tk.bwd(q[p], ks, vs, o[p], lse[p], do[p], p, dq=dq[p], dks=dk[p], dvs=dv[p], **kw)
+            tk.bwd(q[p], ks, vs, o[p], lse[p], do[p], p, dq=dq[p], dks=dk[p], dvs=dv[p], **kwb)
     end.record()
     torch.cuda.synchronize()
     tk.set_trace_hook(None)
@@ -827,7 +835,8 @@ def main():
                    "step": f"fwd p=1..{K} then bwd p={K}..1", "useful_tflop_per_step": round(flops_step / 1e12, 4),
                    "fwd_useful_tflop_per_step": round(fwd_flops_step / 1e12, 4),
                    "mfma_operands": "fp16 Q~K~^T and dS, bf16 P.V, dO.V, P^T.dO; fp32 accumulate",
-                   "parallelism": "single GPU", "window": WINDOW},
+                   "parallelism": "single GPU", "window": WINDOW,
+                   "bwd": "recompute" if args.bwd_recompute else "auto (stored dS where it fits)"},
         "roofline": roofline,
         "gate": gate,
         "kernels": kernels,

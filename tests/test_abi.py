@@ -574,3 +574,39 @@ def test_slab_offset_limit():
     assert rc == 2
     d.batch, d.num_q_heads, d.seqlen = 2, 64, 4_500_000   # 4 B Hq slots past 2^31
     assert lib.ttt_attn_workspace_bytes(ctypes.byref(d), 1) == 0
+
+
+def test_bwd_mode_stored_ds_workspace():
+    """bwd_mode: AUTO stores the trunk dS of bf16 BSHD passes without a window (B * Hq causal
+    32x32 blocks of 2 KB each, n (n + 1) / 2 with n = ceil(S / 32)) when they fit the cap;
+    RECOMPUTE, THD, a window and fp32 need none of it; any other value is refused."""
+    lib = tk.library()
+    w = lambda d, b: lib.ttt_attn_workspace_bytes(ctypes.byref(d), b)
+    auto = good_desc()
+    rec = good_desc()
+    rec.bwd_mode = tk.BWD_RECOMPUTE
+    n = (auto.seqlen + 31) // 32
+    blocks = auto.batch * auto.num_q_heads * n * (n + 1) // 2
+    assert w(auto, 1) - w(rec, 1) >= blocks * 2048
+    assert w(auto, 1) - w(rec, 1) < blocks * 2048 + 4096   # plus the V bounds
+    assert w(auto, 0) == w(rec, 0)                           # forward: unchanged
+    for mk in (lambda: good_desc(layout=tk.LAYOUT_THD), lambda: good_desc(dtype=tk.DTYPE_FP32)):
+        a, r = mk(), mk()
+        r.bwd_mode = tk.BWD_RECOMPUTE
+        assert w(a, 1) == w(r, 1)
+    a, r = good_desc(), good_desc()
+    a.window = r.window = 16
+    r.bwd_mode = tk.BWD_RECOMPUTE
+    assert w(a, 1) == w(r, 1)
+    # past the cap (one 65536-token sequence, 32 heads: 64 GiB of blocks) AUTO recomputes
+    big, big_r = good_desc(), good_desc()
+    for d in (big, big_r):
+        d.batch, d.seqlen, d.num_q_heads, d.num_kv_heads = 1, 65536, 32, 8
+    big_r.bwd_mode = tk.BWD_RECOMPUTE
+    n = 65536 // 32
+    assert 32 * n * (n + 1) // 2 * 2048 > tk.STORED_DS_MAX_BYTES
+    assert w(big, 1) == w(big_r, 1) > 0
+    d = good_desc()
+    d.bwd_mode = 2
+    assert w(d, 1) == 0 and "bwd_mode" in err()
+    assert call_bwd(d) == 2 and "bwd_mode" in err()

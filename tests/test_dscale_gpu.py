@@ -2,12 +2,14 @@
 
 A loss averaged over ~10^4 tokens gives dO elements of 1e-4 .. 1e-6, far below the
 N(0,1) draws of the other parity tests.  The trunk kernels form dS = P (dP - Delta)
-in fp32 and feed it to fp16 MFMA products; a power-of-two factor, set per query row
-(dQ) and per key (dK/dV) from a bound on |dS|, keeps those operands inside fp16's
-range at any dO scale.  Checked here against the fp64 oracle at dO scales 1e-4 and
-1e-6, with a per-row mix of scales over six decades, and with large dO and V (the
-overflow side); plus the exact property of power-of-two factors: scaling dO by 2^-20
-scales every gradient by exactly 2^-20, bit for bit.
+in fp32 and feed it to fp16 MFMA products; a power-of-two factor from a bound on |dS|
+keeps those operands inside fp16's range at any dO scale -- set per query row (dQ)
+and per key (dK/dV) in the recomputing backward, per KV group when dK/dV stores dS
+for dQ (the default for BSHD passes without a window; the BSHD cases here run both).
+Checked against the fp64 oracle at dO scales 1e-4 and 1e-6, with a per-row mix of
+scales over six decades, and with large dO and V (the overflow side); plus the exact
+property of power-of-two factors: scaling dO by 2^-20 scales every gradient by
+exactly 2^-20, bit for bit.
 """
 import numpy as np
 import pytest
@@ -52,11 +54,12 @@ def rescale_do(inp, scale, seed=5):
     return inp
 
 
-def check_grads(tk, inp, p, label, window=0):
+def check_grads(tk, inp, p, label, window=0, recompute=False):
     w = inp.w
     kw = inp.kw()
     o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, window=window, **kw)
-    dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, window=window, **kw)
+    dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, window=window, recompute_dq=recompute,
+                          **kw)
     torch.cuda.synchronize()
     dq_ref, dk_ref, dv_ref = O.bwd(inp.q[p], inp.k, inp.v, inp.do[p], p, layout=w.layout, cu_seqlens=inp.cu_host,
                                    base=w.rope_base, window=window)
@@ -88,11 +91,12 @@ THD_LENS = [1, 63, 64, 65, 200, 129, 3, 130]
 SMALL_THD = syn.Workload("dscale_thd", 42, "thd", 1, sum(THD_LENS), 8, 2, 128, 3, "bf16", 1e4, True)
 
 
+@pytest.mark.parametrize("recompute", [False, True])
 @pytest.mark.parametrize("scale", [1e-4, 1e-6, "mixed"])
-def test_bshd_backward_small_dout(dev, tk, scale):
+def test_bshd_backward_small_dout(dev, tk, scale, recompute):
     inp = rescale_do(Inputs(SMALL_BSHD, dev), scale)
     for p in (1, 4):
-        got, ref = check_grads(tk, inp, p, f"bshd dO*{scale}")
+        got, ref = check_grads(tk, inp, p, f"bshd dO*{scale} recompute={recompute}", recompute=recompute)
         if scale == "mixed":
             dq_rowwise(got, ref, inp, p, "bshd")
 
@@ -105,34 +109,38 @@ def test_thd_backward_small_dout(dev, tk, scale):
         dq_rowwise(got, ref, inp, 3, "thd")
 
 
+@pytest.mark.parametrize("recompute", [False, True])
 @pytest.mark.parametrize("hq,hkv", [(8, 1), (2, 1)])
-def test_gqa_backward_small_dout(dev, tk, hq, hkv):
+def test_gqa_backward_small_dout(dev, tk, hq, hkv, recompute):
     """GQA 8:1 (branch gradients from their own kernel) and 2:1 (64-row dQ work items)."""
     w = syn.Workload(f"dscale_gqa{hq}", 43, "bshd", 2, 160, hq, hkv, 128, 3, "bf16", 1e6, True)
-    check_grads(tk, rescale_do(Inputs(w, dev), 1e-6), 3, f"gqa {hq}:{hkv} dO*1e-6")
+    check_grads(tk, rescale_do(Inputs(w, dev), 1e-6), 3, f"gqa {hq}:{hkv} dO*1e-6 recompute={recompute}",
+                recompute=recompute)
 
 
 def test_window_backward_small_dout(dev, tk):
     check_grads(tk, rescale_do(Inputs(SMALL_BSHD, dev), 1e-6), 3, "window 50 dO*1e-6", window=50)
 
 
-def test_backward_large_dout_and_values(dev, tk):
+@pytest.mark.parametrize("recompute", [False, True])
+def test_backward_large_dout_and_values(dev, tk, recompute):
     """dO ~ 1e3 and V ~ 1e3: |dP| reaches ~1e6, past fp16's 65504 unless scaled down."""
     inp = Inputs(SMALL_BSHD, dev)
     for t in range(len(inp.v)):
         inp.v[t] = syn.round_bf16(inp.v[t] * np.float32(1e3))
         inp.gv[t] = upload(inp.v[t], inp.w, dev)
     rescale_do(inp, 1e3)
-    check_grads(tk, inp, 3, "dO*1e3 V*1e3")
+    check_grads(tk, inp, 3, f"dO*1e3 V*1e3 recompute={recompute}", recompute=recompute)
 
 
 def test_power_of_two_dout_scale_is_exact(dev, tk):
-    """grads(dO * 2^-20) == 2^-20 grads(dO), bitwise, for whole-sequence BSHD and THD calls."""
-    for w, lens in ((SMALL_BSHD, None), (SMALL_THD, THD_LENS)):
+    """grads(dO * 2^-20) == 2^-20 grads(dO), bitwise, for whole-sequence BSHD (stored dS and
+    recomputing) and THD calls."""
+    for w, lens, rec in ((SMALL_BSHD, None, False), (SMALL_BSHD, None, True), (SMALL_THD, THD_LENS, False)):
         inp = Inputs(w, dev, lengths=lens)
-        kw = inp.kw()
+        kw = dict(inp.kw(), recompute_dq=rec)
         p = 3
-        o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **kw)
+        o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **inp.kw())
         a = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, **kw)
         b = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p] * 2.0 ** -20, p, **kw)
         torch.cuda.synchronize()
