@@ -30,7 +30,7 @@ DTYPE_BF16, DTYPE_FP32 = 0, 1
 STATUS = {0: "TTT_OK", 1: "TTT_ERR_NULL_ARG", 2: "TTT_ERR_BAD_SHAPE", 3: "TTT_ERR_UNSUPPORTED",
           4: "TTT_ERR_MISALIGNED", 5: "TTT_ERR_WORKSPACE", 6: "TTT_ERR_HIP", 7: "TTT_ERR_ABI"}
 MAX_PASSES = 16
-BWD_AUTO, BWD_RECOMPUTE = 0, 1
+BWD_RECOMPUTE, BWD_STORED_DS = 0, 1
 STORED_DS_MAX_BYTES = 40 << 30
 
 
@@ -337,14 +337,14 @@ def fwd_noalloc(q, ks: Sequence, vs: Sequence, p: int, out, lse, *, cu_seqlens=N
 @_on_stream
 def bwd(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0,
         rope_base: float = 0.0, dq=None, dks=None, dvs=None, workspace=None, stream=None,
-        check_cu_seqlens: bool = False, window: int = 0, recompute_dq: bool = False):
-    """Backward of TTT pass p.  Returns (dq, [dk_1..dk_p], [dv_1..dv_p]).  recompute_dq: dQ recomputes
-    S and dP instead of reading the dS the dK/dV kernel stores (BWD_RECOMPUTE)."""
+        check_cu_seqlens: bool = False, window: int = 0, stored_ds: bool = False):
+    """Backward of TTT pass p.  Returns (dq, [dk_1..dk_p], [dv_1..dv_p]).  stored_ds: the dK/dV kernel
+    stores dS and dQ is formed from it (BWD_STORED_DS; bf16 BSHD without a window, else ignored)."""
     torch = _torch()
     o_dtype = _dtype_code(o)
     d = make_desc(q, ks, p, cu_seqlens=cu_seqlens, softmax_scale=softmax_scale, rope_base=rope_base,
                   o_dtype=o_dtype, o_like=o, check_cu_seqlens=check_cu_seqlens, window=window)
-    d.bwd_mode = BWD_RECOMPUTE if recompute_dq else BWD_AUTO
+    d.bwd_mode = BWD_STORED_DS if stored_ds else BWD_RECOMPUTE
     if dout.stride() != o.stride():
         raise ValueError("dout must have the strides of o")
     like = lambda t: torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)

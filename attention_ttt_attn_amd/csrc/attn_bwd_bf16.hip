@@ -72,19 +72,21 @@ struct DqBuf {
   uint16_t v[QBN * D];   // V rows, same layout
   _Float16 kt[D * QBN];  // K~^T: d-row at d*QBN, chunk c at slot c ^ ((d >> 2) & 3)
 };
-// Stored dS (MODE 5): the tile's K~^T and every wave's 32x32 dS block, which
-// lies at [key][quarter u*2 + w][8 rows 16 u + 8 w + 0..7] (64 bytes per key):
-// a transposing read then meets each bank twice per instruction, the least
-// its 512 bytes allow.
-struct DsBuf {
-  _Float16 kt[D * QBN];    // K~^T, as in DqBuf
-  _Float16 ds[4][32 * 32]; // one block per wave
+// Stored dS (MODE 5): two rings -- K~^T tiles (as in DqBuf), loaded DS_NK - 1
+// tiles ahead, and every wave's 32x32 dS block of a tile, loaded DS_NS - 1
+// tiles ahead (the dS stream comes from HBM, K~^T mostly from the caches).  A
+// dS block lies at [key][quarter u*2 + w][8 rows 16 u + 8 w + 0..7] (64
+// bytes per key): a transposing read then meets each bank twice per
+// instruction, the least its 512 bytes allow.
+constexpr int DS_NK = 3, DS_NS = 6;
+struct DsRing {
+  _Float16 kt[DS_NK][D * QBN];
+  _Float16 ds[DS_NS][4][32 * 32];
 };
-constexpr int DS_NB = 4;  // stored dS: tile buffers (loads run DS_NB - 1 tiles ahead)
 struct DqSmem {
   union {
     DqBuf buf[2];
-    DsBuf dbuf[DS_NB];
+    DsRing dr;
     float acc[128][OPAD];  // dQ~ rows (wave, row) for the row-major epilogue
   };
 };
@@ -183,7 +185,8 @@ __global__ void __launch_bounds__(256, 2)
   // DMA lane roles, 6 loads per wave per tile (load n = 2w + i):
   // K~ and V rows 4n + lane/16, slot lane%16; K~^T d-rows 16n + lane/4, slot lane%4.
   const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
-  const _Float16* ktbase = ktt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
+  // K~^T slabs come in 32-key tiles of D x 32 (one contiguous 8 KB piece each)
+  const _Float16* ktbase = ktt + (int64_t)(b * P.Hkv + g) * D * P.spad + (int64_t)(slot0 >> 5) * D * QBN;
   // trunk V: P.cs_* strides (the pass-1 / context V; P.ks_* stay with the branch)
   const int64_t vs_t = P.cs_t;
   const uint16_t* vbase = (const uint16_t*)kv.v[0] + b * P.cs_b + (int64_t)kvs * vs_t + g * P.cs_h;
@@ -197,16 +200,16 @@ __global__ void __launch_bounds__(256, 2)
     rrow[i] = r;
     roff[i] = (uint32_t)(((lane & 15) ^ (r & 15)) * 8);
     const int d = 16 * n + (lane >> 2);
-    toff[i] = (uint32_t)(d * P.spad + ((lane & 3) ^ ((d >> 2) & 3)) * 8);
+    toff[i] = (uint32_t)(d * QBN + ((lane & 3) ^ ((d >> 2) & 3)) * 8);
   }
   // buffer descriptors at the tile's bases; the lanes add byte offsets
-  const uint32_t kt_bytes = (uint32_t)(((D - 1) * P.spad + QBN) * 2);
+  const uint32_t kt_bytes = (uint32_t)(D * QBN * 2);  // one K~^T tile
   auto dma_from = [&](DqBuf* __restrict__ dst, const _Float16* kb, const _Float16* ktb, const uint16_t* vb,
                       int64_t vst, int key0, int last) __attribute__((always_inline)) {
     DqBuf& B_ = *dst;
     const buf_rsrc kr = make_rsrc(kb + (int64_t)key0 * D, QBN * D * 2);
     const buf_rsrc vr = make_rsrc(vb + (int64_t)key0 * vst, 0xFFFFFFFFu);
-    const buf_rsrc tr = make_rsrc(ktb + key0, kt_bytes);
+    const buf_rsrc tr = make_rsrc(ktb + (int64_t)(key0 / QBN) * D * QBN, kt_bytes);  // key0: a multiple of 32
     const int wu = __builtin_amdgcn_readfirstlane(wv);  // the LDS bases stay scalar
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -345,12 +348,14 @@ __global__ void __launch_bounds__(256, 2)
     }
   } else {
     // dQ~^T += K~^T dS^T over key groups j = 0 .. rb of this wave's row block
-    // rb.  DS_NB buffers, loads DS_NB - 1 tiles ahead; each wave loads the
-    // K~^T quarter of its lanes' roles and its own dS block (4 loads per tile).
+    // rb.  Each wave loads the K~^T quarter of its lanes' roles and its own dS
+    // block (2 + 2 loads per tile); the dS loads run DS_NS - 1 tiles ahead, the
+    // K~^T loads DS_NK - 1.
     // wave-uniform in scalar registers: the dS loads' buffer descriptors and
     // the compute branch stay scalar
     const int rbw = __builtin_amdgcn_readfirstlane(wave_row0 >> 5);
     const int hu = __builtin_amdgcn_readfirstlane(h);
+    const int wu = __builtin_amdgcn_readfirstlane(wv);  // the LDS bases stay scalar
     const bool wave_on = (rbw << 5) < L;
     const int rbl = min(rbw, ((L + 31) >> 5) - 1);  // loads stay inside this head's blocks
     const _Float16* dsh = P.ds + ((int64_t)(b * P.Hq + hu) * P.ds_tri + (int64_t)rbl * (rbl + 1) / 2) * 1024;
@@ -376,35 +381,37 @@ __global__ void __launch_bounds__(256, 2)
           tro[c2][ri] = (uint32_t)((key * 4 + qu) * 16 + (s16 & 1) * 8);
         }
     }
-    auto dsdma = [&](DsBuf* __restrict__ dst, int j) __attribute__((always_inline)) {
-      DsBuf& B_ = *dst;
-      const buf_rsrc tr = make_rsrc(ktbase + j * QBN, kt_bytes);
+    auto kdma = [&](_Float16* __restrict__ dst, int j) __attribute__((always_inline)) {
+      const buf_rsrc tr = make_rsrc(ktbase + (int64_t)j * D * QBN, kt_bytes);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) lds_dma16(tr, toff[i] * 2, dst + 16 * (2 * wu + i) * QBN);
+    };
+    auto sdma = [&](_Float16* __restrict__ dst, int j) __attribute__((always_inline)) {
       const buf_rsrc dr = make_rsrc(dsh + (int64_t)min(j, rbl) * 1024, 2048);
-      const int wu = __builtin_amdgcn_readfirstlane(wv);  // the LDS bases stay scalar
 #pragma unroll
-      for (int i = 0; i < 2; ++i) lds_dma16(tr, toff[i] * 2, &B_.kt[16 * (2 * wu + i) * QBN]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) lds_dma16_nt(dr, dso[i], &B_.ds[wu][512 * i]);
+      for (int i = 0; i < 2; ++i) lds_dma16_nt(dr, dso[i], dst + 512 * i);
     };
-    // wait until tile t has landed, given the tiles issued after it: 4 loads each
-    auto wait_tile = [&](int t) __attribute__((always_inline)) {
-      const int later = min(nkt - 1, t + DS_NB - 2) - t;
-      static_assert(DS_NB == 4, "the waits below cover 0..2 later tiles");
-      if (later >= 2) TTT_WAIT_VMCNT(8);
-      else if (later == 1) TTT_WAIT_VMCNT(4);
-      else TTT_WAIT_VMCNT(0);
-    };
+    // Issue order: the prologue's dS tiles, then its K~^T tiles; then per tile
+    // j the dS of j + DS_NS - 1 and the K~^T of j + DS_NK - 1.  Loads retire in
+    // issue order, so after tile j's loads the ones for tile j + 1 are done
+    // once at most the count issued during tile j is still in flight.
 #pragma unroll
-    for (int t = 0; t < DS_NB - 1; ++t)
-      if (t < nkt) dsdma(&sm.dbuf[t], t);
-    wait_tile(0);
+    for (int t = 0; t < DS_NS - 1; ++t)
+      if (t < nkt) sdma(&sm.dr.ds[t][wu][0], t);
+#pragma unroll
+    for (int t = 0; t < DS_NK - 1; ++t)
+      if (t < nkt) kdma(&sm.dr.kt[t][0], t);
+    if (nkt > 1) TTT_WAIT_VMCNT(2);  // tile 0 (K~^T of tile 1 may fly)
+    else TTT_WAIT_VMCNT(0);
     lds_ring_barrier();
     for (int j = 0; j < nkt; ++j) {
-      auto step = [&](const DsBuf* __restrict__ cur, DsBuf* __restrict__ ahead) __attribute__((always_inline)) {
-        if (j + DS_NB - 1 < nkt) dsdma(ahead, j + DS_NB - 1);
+      auto step = [&](const _Float16* __restrict__ ck, const _Float16* __restrict__ cs, _Float16* __restrict__ nk,
+                      _Float16* __restrict__ ns) __attribute__((always_inline)) {
+        const bool ls = j + DS_NS - 1 < nkt, lk = j + DS_NK - 1 < nkt;
+        if (ls) sdma(ns, j + DS_NS - 1);
+        if (lk) kdma(nk, j + DS_NK - 1);
         if (wave_on && j <= rbw) {
-          const DsBuf& B_ = *cur;
-          const char* dsw = (const char*)&B_.ds[wv][0];
+          const char* dsw = (const char*)cs;
 #pragma unroll
           for (int c2 = 0; c2 < 2; ++c2) {
             const s16x4 x0 = lds_read_tr16(dsw + tro[c2][0]), x1 = lds_read_tr16(dsw + tro[c2][1]);
@@ -413,15 +420,20 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
             for (int d4 = 0; d4 < 4; ++d4) {
               const int d = d4 * 32 + l32;
-              a[d4] = *(const f16x8*)&B_.kt[d * QBN + (((2 * c2 + hf) ^ ((d >> 2) & 3)) * 8)];
+              a[d4] = *(const f16x8*)&ck[d * QBN + (((2 * c2 + hf) ^ ((d >> 2) & 3)) * 8)];
             }
 #pragma unroll
             for (int d4 = 0; d4 < 4; ++d4) acc[d4] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[d4], bop, acc[d4], 0, 0, 0);
           }
         }
+        // tile j+1 has landed when only this tile's issues may still fly
+        const int fly = (ls ? 2 : 0) + (lk ? 2 : 0);
+        if (fly == 4) TTT_WAIT_VMCNT(4);
+        else if (fly == 2) TTT_WAIT_VMCNT(2);
+        else TTT_WAIT_VMCNT(0);
       };
-      step(&sm.dbuf[j % DS_NB], &sm.dbuf[(j + DS_NB - 1) % DS_NB]);
-      wait_tile(j + 1);    // tile j+1 has landed
+      step(&sm.dr.kt[j % DS_NK][0], &sm.dr.ds[j % DS_NS][wu][0], &sm.dr.kt[(j + DS_NK - 1) % DS_NK][0],
+           &sm.dr.ds[(j + DS_NS - 1) % DS_NS][wu][0]);
       lds_ring_barrier();  // and every wave is done with tile j
     }
   }
@@ -429,7 +441,7 @@ __global__ void __launch_bounds__(256, 2)
   // the blocks of rows row0 .. qend-1 are exactly key rows row0 .. qend-1)
   if constexpr (MODE == 1) {
     const _Float16* kbb = kbt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
-    const _Float16* ktbb = kbtt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
+    const _Float16* ktbb = kbtt + (int64_t)(b * P.Hkv + g) * D * P.spad + (int64_t)(slot0 >> 5) * D * QBN;
     const uint16_t* vbb = (const uint16_t*)kv.v[1] + b * P.ks_b + (int64_t)start * P.ks_t + g * P.ks_h;
     for (int k0 = row0; k0 < qend; k0 += QBN) {
       dma_from(&sm.buf[0], kbb, ktbb, vbb, P.ks_t, k0, L - 1);
@@ -711,6 +723,7 @@ __global__ void __launch_bounds__(256, 2)
 // anchors), so one vmcnt threshold per wave releases exactly the step two
 // ahead.
 constexpr int NBUF = 4;
+constexpr int kDsStoreAux = 2;  // cache policy of the stored-dS writes: non-temporal
 __device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 struct KvBuf {
   _Float16 q[BQ * D];   // Q~ rows   (A of S; columns: A of dK^T)
@@ -989,30 +1002,49 @@ __global__ void __launch_bounds__(256, 1)
   // pointers: the compiler then knows the loads into the step-(st+3) buffer
   // cannot alias this iteration's LDS reads and puts no wait on them.
   int cs_h = 0, cs_q0 = row_lo + (nq - 1) * BQ;  // the step being computed
-  // Stored dS (MODE 5): step st's block is written at the start of step st+1
-  // (before that step's loads are issued), so the stores have a whole step to
-  // drain before the step's closing vmcnt wait.  Blocks above the diagonal
-  // (row block < key group) are not part of the layout.
+  // Stored dS (MODE 5): step st's block is written in step st+1, right after
+  // that step's loads are issued.  Vector memory operations retire in issue
+  // order, so a step's closing wait -- for the loads issued one step earlier --
+  // can leave every younger operation in flight: the newest loads and the
+  // stores of this and the previous step.  Each store thus has two steps to
+  // drain.  Blocks above the diagonal (row block < key group) are not part of
+  // the layout.
   f16x8 dsp[2];
   int sp_h = 0, sp_q0 = 0;
+  int stored_prev = 0, stored_now = 0;  // stores issued in the previous / this step (0 or 2)
   const int kgrp = (kv0 >> 5) + wv;  // this wave's key group of 32
   auto store_ds = [&]() __attribute__((always_inline)) {
     const int rb = sp_q0 >> 5;
-    if (rb >= kgrp) {
-      _Float16* blk =
-          P.ds + ((int64_t)(b * P.Hq + g * P.r + sp_h) * P.ds_tri + (int64_t)rb * (rb + 1) / 2 + kgrp) * 1024;
-      // read once, by the dQ kernel: non-temporal, so the Q~ / dO rows this
-      // kernel re-reads keep their cache lines
-      __builtin_nontemporal_store(dsp[0], (f16x8*)(blk + lane * 8));
-      __builtin_nontemporal_store(dsp[1], (f16x8*)(blk + 512 + lane * 8));
+    if (rb < kgrp) return 0;
+    const _Float16* blk =
+        P.ds + ((int64_t)(b * P.Hq + g * P.r + sp_h) * P.ds_tri + (int64_t)rb * (rb + 1) / 2 + kgrp) * 1024;
+    // read once, by the dQ kernel: non-temporal, so the Q~ / dO rows this
+    // kernel re-reads keep their cache lines
+    const buf_rsrc r = make_rsrc(blk, 2048);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dsp[0]), r, lane * 16, 0, kDsStoreAux);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, dsp[1]), r, 1024 + lane * 16, 0, kDsStoreAux);
+    return 2;
+  };
+  auto wait_vm = [&](int n) __attribute__((always_inline)) {
+    switch (n) {
+      case 2: TTT_WAIT_VMCNT(2); break;
+      case 4: TTT_WAIT_VMCNT(4); break;
+      case 5: TTT_WAIT_VMCNT(5); break;
+      case 6: TTT_WAIT_VMCNT(6); break;
+      case 7: TTT_WAIT_VMCNT(7); break;
+      case 8: TTT_WAIT_VMCNT(8); break;
+      case 9: TTT_WAIT_VMCNT(9); break;
+      default: TTT_WAIT_VMCNT(0); break;
     }
   };
   for (int st = 0; st < nsteps; ++st) {
    auto step = [&](const KvBuf* __restrict__ Bcp, const KvBuf* __restrict__ Bnp, KvBuf* __restrict__ Bdp)
                    __attribute__((always_inline)) {
-    if constexpr (MODE == 5)
-      if (st > 0) store_ds();
     if (st + 3 < nsteps) issue(Bdp);
+    if constexpr (MODE == 5) {
+      stored_prev = stored_now;
+      stored_now = st > 0 ? store_ds() : 0;
+    }
     const KvBuf& Bc = *Bcp;
     const int q0 = cs_q0;
     // S/dP products of step st+1 (stale data past the last step is computed and
@@ -1091,7 +1123,9 @@ __global__ void __launch_bounds__(256, 1)
       cs_q0 -= BQ;
     }
     // step st+2 must have landed before the next iteration reads it
-    if (st + 3 < nsteps) {
+    if constexpr (MODE == 5) {
+      wait_vm((st + 3 < nsteps ? (w0 ? 5 : 4) : 0) + stored_prev + stored_now);
+    } else if (st + 3 < nsteps) {
       if (w0) TTT_WAIT_VMCNT(5);
       else TTT_WAIT_VMCNT(4);
     } else {

@@ -75,7 +75,7 @@ struct Prob {
   const int* seg_kvoff;
   const int* kv_cu;
   int kv_tok;
-  // Stored dS (bf16 whole-sequence BSHD passes without a window): the dK/dV
+  // Stored dS (asked for; bf16 whole-sequence BSHD passes without a window): the dK/dV
   // kernel writes every causal 32x32 block of 2^e dS in fp16 -- one exponent
   // e per KV group, from dmax and vgmax -- and the dQ kernel forms dQ~ = dS K~
   // from them instead of recomputing S and dP.  Block (rb, kg) of query head

@@ -65,7 +65,7 @@ struct Plan {
   ttt::WsPlan ws;
   bool bf16;
   bool o_f32;
-  bool ds;  // backward with stored dS (TTT_BWD_AUTO on a BSHD pass whose blocks fit the cap)
+  bool ds;  // backward with stored dS (TTT_BWD_STORED_DS on a BSHD pass whose blocks fit the cap)
   int max_tiles_q, max_tiles_kv;
   int64_t k0s_b, k0s_t, k0s_h;  // strides of k[0] / v[0] (ring steps; = kv strides otherwise)
 };
@@ -259,12 +259,12 @@ int make_plan(const ttt_attn_desc* d, int for_bwd, Plan& pl, const ttt_attn_chun
   }
   pl.bf16 = bf16;
   pl.o_f32 = o_f32;
-  // Stored dS: ttt_attn_bwd of a bf16 BSHD pass without a window, when its
-  // causal 32x32 blocks (2 KB each per head) fit the cap.
-  if (d->bwd_mode != TTT_BWD_AUTO && d->bwd_mode != TTT_BWD_RECOMPUTE)
-    return fail(TTT_ERR_BAD_SHAPE, "bwd_mode %d is neither AUTO (0) nor RECOMPUTE (1)", d->bwd_mode);
+  // Stored dS (asked for): ttt_attn_bwd of a bf16 BSHD pass without a window,
+  // when its causal 32x32 blocks (2 KB each per head) fit the cap.
+  if (d->bwd_mode != TTT_BWD_RECOMPUTE && d->bwd_mode != TTT_BWD_STORED_DS)
+    return fail(TTT_ERR_BAD_SHAPE, "bwd_mode %d is neither RECOMPUTE (0) nor STORED_DS (1)", d->bwd_mode);
   pl.ds = false;
-  if (for_bwd && bf16 && !thd && !c && d->window == 0 && d->bwd_mode == TTT_BWD_AUTO) {
+  if (for_bwd && bf16 && !thd && !c && d->window == 0 && d->bwd_mode == TTT_BWD_STORED_DS) {
     const int64_t n = (stok + 31) / 32;
     const int64_t tri = n * (n + 1) / 2;
     if ((double)B * Hq * tri * 2048.0 <= (double)TTT_ATTN_STORED_DS_MAX_BYTES) {
@@ -830,11 +830,13 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
     Pc.stok = P.kv_len;
     J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, (uint16_t*)cktt, 0, nullptr, 0};
     if (thd) J.j[0].cu = P.kv_cu, J.j[0].ntok = P.kv_tok;
+    J.j[0].col_tiled = 1;  // K~^T in the dQ kernel's 32-key tiles
     TTT_TRACED("prep_ctx_bwd", ttt::launch_prep_bf16(Pc, J, cosT, sinT, st));
   }
   // block keys (K~ rows, K~^T) and queries (Q~ rows) at their slot positions
   J.n = 2;
   J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, (uint16_t*)bktt, 1, nullptr, 0};
+  J.j[0].col_tiled = 1;  // K~^T in the dQ kernel's 32-key tiles
   int* lims = (int*)(delta + (size_t)2 * P.B * P.Hq * P.spad);  // per-slot visible context lengths
   J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, 0, 1, 0, qt, nullptr, 1, lims, 0};
   J.heads_fast = 1;  // mostly row-major outputs (Q~ rows)
@@ -1143,6 +1145,7 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     const int krows = (c && P.layout == TTT_LAYOUT_BSHD) ? (P.kv_len > 0 ? P.kv_len : -1) : 0;
     J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, (uint16_t*)ktt, 0,
               nullptr, krows};
+    J.j[0].col_tiled = 1;  // K~^T in the dQ kernel's 32-key tiles
     J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.q_off + P.p - 1, 1, 0, qt, nullptr, 0, nullptr, 0};
     if (P.kv_cu) {  // THD ring step: per-sequence key rows and offsets
       J.j[0].cu = P.kv_cu, J.j[0].ntok = P.kv_tok, J.j[0].seg_pos = P.seg_kvoff;

@@ -41,8 +41,8 @@ def parse():
     ap.add_argument("--head-dim", type=int, default=0, metavar="D",
                     help="run the unroll at head_dim D (32 or 64: bf16 on zero-padded heads) instead of the "
                          "workload's 128; FLOPs count the D-dim work")
-    ap.add_argument("--bwd-recompute", action="store_true",
-                    help="backward without stored dS: dQ recomputes S and dP (bwd_mode RECOMPUTE)")
+    ap.add_argument("--bwd-stored-ds", action="store_true",
+                    help="backward with stored dS: dK/dV writes dS, dQ = dS K~ (bwd_mode STORED_DS)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="bound on the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel event timing")
@@ -708,7 +708,7 @@ def main():
     ws_bytes = max(tk.workspace_bytes(d_f, False), tk.workspace_bytes(d_f, True))
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     kw = dict(cu_seqlens=cu, rope_base=w.rope_base, workspace=ws, window=WINDOW)
-    kwb = dict(kw, recompute_dq=args.bwd_recompute)
+    kwb = dict(kw, stored_ds=args.bwd_stored_ds)
 
     def step():
         for p in range(1, K + 1):
@@ -836,7 +836,7 @@ def main():
                    "fwd_useful_tflop_per_step": round(fwd_flops_step / 1e12, 4),
                    "mfma_operands": "fp16 Q~K~^T and dS, bf16 P.V, dO.V, P^T.dO; fp32 accumulate",
                    "parallelism": "single GPU", "window": WINDOW,
-                   "bwd": "recompute" if args.bwd_recompute else "auto (stored dS where it fits)"},
+                   "bwd": "stored dS" if args.bwd_stored_ds else "recompute"},
         "roofline": roofline,
         "gate": gate,
         "kernels": kernels,

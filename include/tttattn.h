@@ -127,19 +127,20 @@ typedef struct ttt_attn_desc {
                                  0 = full causal trunk; the branch is unchanged.  Same
                                  issue, item 4 (sliding-window layers).  bf16 only      */
   int32_t bwd_mode;           /* ttt_attn_bwd only (0 elsewhere):
-                                 TTT_BWD_AUTO (0): bf16 BSHD without a window stores the
-                                   trunk dS (fp16, one power-of-two scale per KV group)
-                                   in the workspace while dK/dV are formed and forms dQ
-                                   from it, instead of recomputing S and dP for dQ, when
-                                   those blocks take at most TTT_ATTN_STORED_DS_MAX_BYTES
-                                   (B * Hq * n (n + 1) / 2 * 2048 bytes, n = ceil(S / 32));
-                                   otherwise as TTT_BWD_RECOMPUTE.
-                                 TTT_BWD_RECOMPUTE (1): dQ recomputes S and dP; the
-                                   smallest workspace.
+                                 TTT_BWD_RECOMPUTE (0): dQ recomputes S and dP (the
+                                   smallest workspace; the default).
+                                 TTT_BWD_STORED_DS (1): for bf16 BSHD passes without a
+                                   window, the dK/dV kernel also stores the trunk dS
+                                   (fp16, one power-of-two scale per KV group) in the
+                                   workspace and dQ is formed from it, when those blocks
+                                   take at most TTT_ATTN_STORED_DS_MAX_BYTES (B * Hq *
+                                   n (n + 1) / 2 * 2048 bytes, n = ceil(S / 32));
+                                   otherwise as RECOMPUTE.  Fewer matrix products, more
+                                   HBM traffic: see the measurements in the docs.
                                  Both are deterministic.                                  */
 } ttt_attn_desc;
 
-enum ttt_attn_bwd_mode { TTT_BWD_AUTO = 0, TTT_BWD_RECOMPUTE = 1 };
+enum ttt_attn_bwd_mode { TTT_BWD_RECOMPUTE = 0, TTT_BWD_STORED_DS = 1 };
 #define TTT_ATTN_STORED_DS_MAX_BYTES ((size_t)40 << 30)
 
 /* Bytes of caller-provided device workspace a forward (for_bwd = 0) or

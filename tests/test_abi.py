@@ -577,32 +577,34 @@ def test_slab_offset_limit():
 
 
 def test_bwd_mode_stored_ds_workspace():
-    """bwd_mode: AUTO stores the trunk dS of bf16 BSHD passes without a window (B * Hq causal
-    32x32 blocks of 2 KB each, n (n + 1) / 2 with n = ceil(S / 32)) when they fit the cap;
-    RECOMPUTE, THD, a window and fp32 need none of it; any other value is refused."""
+    """bwd_mode: STORED_DS keeps the trunk dS of bf16 BSHD passes without a window (B * Hq
+    causal 32x32 blocks of 2 KB each, n (n + 1) / 2 with n = ceil(S / 32)) when they fit the
+    cap; RECOMPUTE (the default), THD, a window and fp32 need none of it; any other value is
+    refused."""
     lib = tk.library()
     w = lambda d, b: lib.ttt_attn_workspace_bytes(ctypes.byref(d), b)
-    auto = good_desc()
     rec = good_desc()
-    rec.bwd_mode = tk.BWD_RECOMPUTE
-    n = (auto.seqlen + 31) // 32
-    blocks = auto.batch * auto.num_q_heads * n * (n + 1) // 2
-    assert w(auto, 1) - w(rec, 1) >= blocks * 2048
-    assert w(auto, 1) - w(rec, 1) < blocks * 2048 + 4096   # plus the V bounds
-    assert w(auto, 0) == w(rec, 0)                           # forward: unchanged
+    sto = good_desc()
+    sto.bwd_mode = tk.BWD_STORED_DS
+    assert rec.bwd_mode == tk.BWD_RECOMPUTE == 0
+    n = (rec.seqlen + 31) // 32
+    blocks = rec.batch * rec.num_q_heads * n * (n + 1) // 2
+    assert w(sto, 1) - w(rec, 1) >= blocks * 2048
+    assert w(sto, 1) - w(rec, 1) < blocks * 2048 + 4096   # plus the V bounds
+    assert w(sto, 0) == w(rec, 0)                           # forward: unchanged
     for mk in (lambda: good_desc(layout=tk.LAYOUT_THD), lambda: good_desc(dtype=tk.DTYPE_FP32)):
-        a, r = mk(), mk()
-        r.bwd_mode = tk.BWD_RECOMPUTE
+        r, a = mk(), mk()
+        a.bwd_mode = tk.BWD_STORED_DS
         assert w(a, 1) == w(r, 1)
-    a, r = good_desc(), good_desc()
+    r, a = good_desc(), good_desc()
     a.window = r.window = 16
-    r.bwd_mode = tk.BWD_RECOMPUTE
+    a.bwd_mode = tk.BWD_STORED_DS
     assert w(a, 1) == w(r, 1)
-    # past the cap (one 65536-token sequence, 32 heads: 64 GiB of blocks) AUTO recomputes
+    # past the cap (one 65536-token sequence, 32 heads: 64 GiB of blocks) it recomputes
     big, big_r = good_desc(), good_desc()
     for d in (big, big_r):
         d.batch, d.seqlen, d.num_q_heads, d.num_kv_heads = 1, 65536, 32, 8
-    big_r.bwd_mode = tk.BWD_RECOMPUTE
+    big.bwd_mode = tk.BWD_STORED_DS
     n = 65536 // 32
     assert 32 * n * (n + 1) // 2 * 2048 > tk.STORED_DS_MAX_BYTES
     assert w(big, 1) == w(big_r, 1) > 0

@@ -4,8 +4,8 @@ A loss averaged over ~10^4 tokens gives dO elements of 1e-4 .. 1e-6, far below t
 N(0,1) draws of the other parity tests.  The trunk kernels form dS = P (dP - Delta)
 in fp32 and feed it to fp16 MFMA products; a power-of-two factor from a bound on |dS|
 keeps those operands inside fp16's range at any dO scale -- set per query row (dQ)
-and per key (dK/dV) in the recomputing backward, per KV group when dK/dV stores dS
-for dQ (the default for BSHD passes without a window; the BSHD cases here run both).
+and per key (dK/dV) in the recomputing backward (the default), per KV group when
+dK/dV stores dS for dQ (bwd_mode STORED_DS; the BSHD cases here run both).
 Checked against the fp64 oracle at dO scales 1e-4 and 1e-6, with a per-row mix of
 scales over six decades, and with large dO and V (the overflow side); plus the exact
 property of power-of-two factors: scaling dO by 2^-20 scales every gradient by
@@ -54,12 +54,11 @@ def rescale_do(inp, scale, seed=5):
     return inp
 
 
-def check_grads(tk, inp, p, label, window=0, recompute=False):
+def check_grads(tk, inp, p, label, window=0, stored=False):
     w = inp.w
     kw = inp.kw()
     o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, window=window, **kw)
-    dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, window=window, recompute_dq=recompute,
-                          **kw)
+    dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, window=window, stored_ds=stored, **kw)
     torch.cuda.synchronize()
     dq_ref, dk_ref, dv_ref = O.bwd(inp.q[p], inp.k, inp.v, inp.do[p], p, layout=w.layout, cu_seqlens=inp.cu_host,
                                    base=w.rope_base, window=window)
@@ -91,12 +90,12 @@ THD_LENS = [1, 63, 64, 65, 200, 129, 3, 130]
 SMALL_THD = syn.Workload("dscale_thd", 42, "thd", 1, sum(THD_LENS), 8, 2, 128, 3, "bf16", 1e4, True)
 
 
-@pytest.mark.parametrize("recompute", [False, True])
+@pytest.mark.parametrize("stored", [False, True])
 @pytest.mark.parametrize("scale", [1e-4, 1e-6, "mixed"])
-def test_bshd_backward_small_dout(dev, tk, scale, recompute):
+def test_bshd_backward_small_dout(dev, tk, scale, stored):
     inp = rescale_do(Inputs(SMALL_BSHD, dev), scale)
     for p in (1, 4):
-        got, ref = check_grads(tk, inp, p, f"bshd dO*{scale} recompute={recompute}", recompute=recompute)
+        got, ref = check_grads(tk, inp, p, f"bshd dO*{scale} stored_ds={stored}", stored=stored)
         if scale == "mixed":
             dq_rowwise(got, ref, inp, p, "bshd")
 
@@ -109,36 +108,35 @@ def test_thd_backward_small_dout(dev, tk, scale):
         dq_rowwise(got, ref, inp, 3, "thd")
 
 
-@pytest.mark.parametrize("recompute", [False, True])
+@pytest.mark.parametrize("stored", [False, True])
 @pytest.mark.parametrize("hq,hkv", [(8, 1), (2, 1)])
-def test_gqa_backward_small_dout(dev, tk, hq, hkv, recompute):
+def test_gqa_backward_small_dout(dev, tk, hq, hkv, stored):
     """GQA 8:1 (branch gradients from their own kernel) and 2:1 (64-row dQ work items)."""
     w = syn.Workload(f"dscale_gqa{hq}", 43, "bshd", 2, 160, hq, hkv, 128, 3, "bf16", 1e6, True)
-    check_grads(tk, rescale_do(Inputs(w, dev), 1e-6), 3, f"gqa {hq}:{hkv} dO*1e-6 recompute={recompute}",
-                recompute=recompute)
+    check_grads(tk, rescale_do(Inputs(w, dev), 1e-6), 3, f"gqa {hq}:{hkv} dO*1e-6 stored_ds={stored}", stored=stored)
 
 
 def test_window_backward_small_dout(dev, tk):
     check_grads(tk, rescale_do(Inputs(SMALL_BSHD, dev), 1e-6), 3, "window 50 dO*1e-6", window=50)
 
 
-@pytest.mark.parametrize("recompute", [False, True])
-def test_backward_large_dout_and_values(dev, tk, recompute):
+@pytest.mark.parametrize("stored", [False, True])
+def test_backward_large_dout_and_values(dev, tk, stored):
     """dO ~ 1e3 and V ~ 1e3: |dP| reaches ~1e6, past fp16's 65504 unless scaled down."""
     inp = Inputs(SMALL_BSHD, dev)
     for t in range(len(inp.v)):
         inp.v[t] = syn.round_bf16(inp.v[t] * np.float32(1e3))
         inp.gv[t] = upload(inp.v[t], inp.w, dev)
     rescale_do(inp, 1e3)
-    check_grads(tk, inp, 3, f"dO*1e3 V*1e3 recompute={recompute}", recompute=recompute)
+    check_grads(tk, inp, 3, f"dO*1e3 V*1e3 stored_ds={stored}", stored=stored)
 
 
 def test_power_of_two_dout_scale_is_exact(dev, tk):
-    """grads(dO * 2^-20) == 2^-20 grads(dO), bitwise, for whole-sequence BSHD (stored dS and
-    recomputing) and THD calls."""
-    for w, lens, rec in ((SMALL_BSHD, None, False), (SMALL_BSHD, None, True), (SMALL_THD, THD_LENS, False)):
+    """grads(dO * 2^-20) == 2^-20 grads(dO), bitwise, for whole-sequence BSHD (recomputing and
+    stored dS) and THD calls."""
+    for w, lens, sto in ((SMALL_BSHD, None, False), (SMALL_BSHD, None, True), (SMALL_THD, THD_LENS, False)):
         inp = Inputs(w, dev, lengths=lens)
-        kw = dict(inp.kw(), recompute_dq=rec)
+        kw = dict(inp.kw(), stored_ds=sto)
         p = 3
         o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **inp.kw())
         a = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, **kw)

@@ -13,7 +13,7 @@ check compares sampled outputs it computes one by one:
     by the oracle over every query row that sees it with that row's full-row
     softmax (oracle.bwd_trunk_keys): b4_s4k a whole slice at passes 1 and 7,
     thd_32k the longest sequence at passes 1 and 3, s32k keys 0..4095 of one
-    slice at pass 7 (all 32768 rows of that slice enter: about 60-90 s of oracle
+    slice at pass 7 (all 32768 rows of that slice enter: about 90-120 s of oracle
     time on 16 host cores, the largest share of this file's budget).  Relative
     Frobenius over the keys, and the per-key relative error at the edge keys
     (first, second, tile borders, last).
@@ -180,6 +180,7 @@ def test_thd_32k_fullsize(dev, tk):
     run_fullsize(tk, "thd_32k", dev)
 
 
+@pytest.mark.timeout(480)  # the oracle's share (all 32768 rows of one slice) runs 1.5-2 minutes on the host
 def test_s32k_fullsize(dev, tk):
     run_fullsize(tk, "s32k", dev)
 

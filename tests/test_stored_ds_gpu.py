@@ -1,4 +1,4 @@
-"""Backward with stored dS (the default for bf16 BSHD passes without a window).
+"""Backward with stored dS (bwd_mode STORED_DS: bf16 BSHD passes without a window).
 
 The dK/dV kernel writes every causal 32x32 block of the fp16 dS (one power-of-two
 scale per KV group) into the workspace, and dQ~ = dS K~ is formed from those blocks
@@ -6,7 +6,7 @@ instead of recomputing S and dP.  Checked against the fp64 oracle for the shape
 classes the blocks and the dQ work items meet -- S = 1, S a multiple of 32 and not,
 GQA 4:1 (four heads per work item), 2:1 (two row blocks per work item), 1:1 and 3:1
 (four row blocks of one head), 8:1 (two work items per group; branch gradients from
-their own kernel) -- and for the recomputing backward (bwd_mode RECOMPUTE) on the same
+their own kernel) -- and for the recomputing backward (the default) on the same
 inputs; plus bitwise determinism of the stored-dS backward.
 """
 import numpy as np
@@ -46,11 +46,11 @@ CASES = [
 ]
 
 
-def grads_vs_oracle(tk, inp, p, recompute):
+def grads_vs_oracle(tk, inp, p, stored):
     w = inp.w
     kw = inp.kw()
     o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **kw)
-    dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, recompute_dq=recompute, **kw)
+    dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, stored_ds=stored, **kw)
     torch.cuda.synchronize()
     dq_r, dk_r, dv_r = O.bwd(inp.q[p], inp.k, inp.v, inp.do[p], p, layout=w.layout, base=w.rope_base)
     errs = {"dq": rel_fro(to_np(dq), dq_r)}
@@ -66,9 +66,9 @@ def test_stored_ds_backward_matches_oracle(dev, tk, B, S, Hq, Hkv, passes):
                      True)
     inp = Inputs(w, dev)
     for p in passes:
-        for recompute in (False, True):
-            (dq, _, _), errs = grads_vs_oracle(tk, inp, p, recompute)
-            tag = "recompute" if recompute else "stored dS"
+        for stored in (True, False):
+            (dq, _, _), errs = grads_vs_oracle(tk, inp, p, stored)
+            tag = "stored dS" if stored else "recompute"
             print(f"B{B} S{S} {Hq}/{Hkv} p={p} {tag}: " + " ".join(f"{k}={v:.1e}" for k, v in errs.items()))
             assert torch.isfinite(dq.float()).all().item()
             assert max(errs.values()) <= TOL["bf16"]["grad"], errs
@@ -79,8 +79,8 @@ def test_stored_ds_backward_is_deterministic(dev, tk):
     inp = Inputs(w, dev)
     p = 3
     o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **inp.kw())
-    a = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, **inp.kw())
-    b = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, **inp.kw())
+    a = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, stored_ds=True, **inp.kw())
+    b = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, stored_ds=True, **inp.kw())
     torch.cuda.synchronize()
     for x, y in [(a[0], b[0])] + list(zip(a[1], b[1])) + list(zip(a[2], b[2])):
         assert torch.equal(x, y)
