@@ -149,7 +149,8 @@ __global__ void __launch_bounds__(256, 2)
   // sliding window: the first tile any row of the work item sees
   const int kt_lo = (TTT_ && win > 0) ? max(0, row0 + dq_ - win + 1) / BN : 0;
   const _Float16* kbase = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0) * D;
-  const _Float16* vbase = vt + (int64_t)(b * P.Hkv + g) * D * P.spad + slot0;
+  // V^T slabs come in 32-key tiles of D x 32 (a 64-key tile: two adjacent ones, 16 KB)
+  const _Float16* vbase = vt + (int64_t)(b * P.Hkv + g) * D * P.spad + (int64_t)(slot0 >> 5) * D * 32;
   // DMA lane roles, loads n = w*KL + i.  K~: 1 KB = rows 4n + lane/16, slot
   // lane%16.  V^T: 1 KB = d-rows RPL*n + lane/CH, slot lane%CH.  Per-lane 32-bit
   // offsets, tile bases are wave-uniform.
@@ -166,11 +167,11 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
   for (int i = 0; i < VL; ++i) {
     const int d = RPL * (wv * VL + i) + lane / CH;
-    voff[i] = (uint32_t)(d * P.spad + ((lane % CH) ^ ((d >> 1) & (CH - 1))) * 8);
+    const int c = (lane % CH) ^ ((d >> 1) & (CH - 1));  // the 8-key chunk landing in this lane's LDS slot
+    voff[i] = (uint32_t)((((c >> 2) * D) + d) * 32 + (c & 3) * 8);
   }
-  // a tile's K~ rows are BN*D contiguous halves; its V^T d-rows are BN keys
-  // each, spad apart
-  const uint32_t vt_bytes = (uint32_t)(((D - 1) * P.spad + BN) * 2);
+  // a tile's K~ rows are BN*D contiguous halves, and so is its V^T (two 32-key pieces)
+  const uint32_t vt_bytes = (uint32_t)(BN * D * 2);
   auto dma_from = [&](Tile* __restrict__ dst, const _Float16* kb_t, const _Float16* vb_t)
                       __attribute__((always_inline)) {
     const buf_rsrc kr = make_rsrc(kb_t, BN * D * 2), vr = make_rsrc(vb_t, vt_bytes);
@@ -181,7 +182,7 @@ __global__ void __launch_bounds__(256, 2)
     for (int i = 0; i < VL; ++i) lds_dma16(vr, voff[i] * 2, &dst->v[RPL * (wu * VL + i) * BN]);
   };
   auto dma = [&](Tile* __restrict__ dst, int kt_) __attribute__((always_inline)) {
-    dma_from(dst, kbase + (int64_t)kt_ * BN * D, vbase + kt_ * BN);
+    dma_from(dst, kbase + (int64_t)kt_ * BN * D, vbase + (int64_t)kt_ * BN * D);
   };
   // wait_tiles(n): all but this wave's last n tiles of loads have landed
   static_assert((NBUF - 2) * TL < 64, "vmcnt threshold");
@@ -381,9 +382,9 @@ __global__ void __launch_bounds__(256, 2)
   // 64-key tile at a time, masked to the row's block
   if constexpr (MODE == 1) {
     const _Float16* kbb = kbt + ((int64_t)(b * P.Hkv + g) * P.spad_b + slot0) * D;
-    const _Float16* vbb = vbt + (int64_t)(b * P.Hkv + g) * D * P.spad_b + slot0;
-    for (int k0 = row0; k0 < qend; k0 += BN) {
-      dma_from(&sm.ring[0], kbb + (int64_t)k0 * D, vbb + k0);
+    const _Float16* vbb = vbt + (int64_t)(b * P.Hkv + g) * D * P.spad_b + (int64_t)(slot0 >> 5) * D * 32;
+    for (int k0 = row0; k0 < qend; k0 += BN) {  // k0: a multiple of 32
+      dma_from(&sm.ring[0], kbb + (int64_t)k0 * D, vbb + (int64_t)(k0 >> 5) * D * 32);
       TTT_WAIT_VMCNT(0);
       __syncthreads();
       tile(&sm.ring[0], k0, std::integral_constant<int, 3>{});

@@ -830,13 +830,11 @@ int ttt_attn_block_bwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
     Pc.stok = P.kv_len;
     J.j[0] = {(const uint16_t*)k_ctx, bp.cs_b, bp.cs_t, bp.cs_h, P.Hkv, 0, 1, 0, ckt, (uint16_t*)cktt, 0, nullptr, 0};
     if (thd) J.j[0].cu = P.kv_cu, J.j[0].ntok = P.kv_tok;
-    J.j[0].col_tiled = 1;  // K~^T in the dQ kernel's 32-key tiles
     TTT_TRACED("prep_ctx_bwd", ttt::launch_prep_bf16(Pc, J, cosT, sinT, st));
   }
   // block keys (K~ rows, K~^T) and queries (Q~ rows) at their slot positions
   J.n = 2;
   J.j[0] = {(const uint16_t*)k_blk, P.ks_b, P.ks_t, P.ks_h, P.Hkv, 0, 1, 0, bkt, (uint16_t*)bktt, 1, nullptr, 0};
-  J.j[0].col_tiled = 1;  // K~^T in the dQ kernel's 32-key tiles
   int* lims = (int*)(delta + (size_t)2 * P.B * P.Hq * P.spad);  // per-slot visible context lengths
   J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, 0, 1, 0, qt, nullptr, 1, lims, 0};
   J.heads_fast = 1;  // mostly row-major outputs (Q~ rows)
@@ -1145,7 +1143,6 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     const int krows = (c && P.layout == TTT_LAYOUT_BSHD) ? (P.kv_len > 0 ? P.kv_len : -1) : 0;
     J.j[0] = {(const uint16_t*)k[0], pl.k0s_b, pl.k0s_t, pl.k0s_h, P.Hkv, P.kv_off, 1, 0, kt, (uint16_t*)ktt, 0,
               nullptr, krows};
-    J.j[0].col_tiled = 1;  // K~^T in the dQ kernel's 32-key tiles
     J.j[1] = {(const uint16_t*)q, P.qs_b, P.qs_t, P.qs_h, P.Hq, P.q_off + P.p - 1, 1, 0, qt, nullptr, 0, nullptr, 0};
     if (P.kv_cu) {  // THD ring step: per-sequence key rows and offsets
       J.j[0].cu = P.kv_cu, J.j[0].ntok = P.kv_tok, J.j[0].seg_pos = P.seg_kvoff;

@@ -25,9 +25,6 @@ struct PrepJob {
   const int* cu; // THD: this tensor's own cu_seqlens (ntok rows) on the Prob's slots, or null (the Prob's)
   int ntok;
   const int* seg_pos;  // THD: per-sequence position offset added to every row's, or null
-  // out_col in 32-slot tiles: element (d, slot) of a head at ((slot / 32) * D + d) * 32 + slot % 32, so one
-  // 32-key tile of the transpose is one contiguous 8 KB piece (the dQ kernels' K~^T); else d * spad + slot
-  int col_tiled;
 };
 struct PrepJobs {
   PrepJob j[2];

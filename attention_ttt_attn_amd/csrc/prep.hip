@@ -200,8 +200,7 @@ __global__ void __launch_bounds__(256) prep_bf16_kernel(Prob P, PrepJobs J, cons
     for (int i = 0; i < 4; ++i)
       o[i] = ((tile[t8 + 2 * i][d >> 1] >> sh) & 0xffffu) | (((tile[t8 + 2 * i + 1][d >> 1] >> sh) & 0xffffu) << 16);
     const int sl = tok0 + t8;
-    const int64_t at = jb.col_tiled ? ((int64_t)(sl >> 5) * D + d) * 32 + (sl & 31) : (int64_t)d * P.spad + sl;
-    *(u32x4*)(jb.out_col + (int64_t)(b * jb.H + h) * D * P.spad + at) = o;
+    *(u32x4*)(jb.out_col + (int64_t)(b * jb.H + h) * D * P.spad + ((int64_t)(sl >> 5) * D + d) * 32 + (sl & 31)) = o;
   }
 }
 
