@@ -75,7 +75,7 @@ def edge_keys(keys, L):
     return np.array(sorted(set(keys.tolist()) & want))
 
 
-def run_fullsize(tk, name, dev, n_rows=4096, check_bwd=True, do_scale=None, check_fwd=True):
+def run_fullsize(tk, name, dev, n_rows=4096, check_bwd=True, do_scale=None, check_fwd=True, stored_ds=False):
     w = syn.workload(name)
     inp = Inputs(w, dev, with_grad=check_bwd)
     if do_scale is not None:
@@ -114,7 +114,7 @@ def run_fullsize(tk, name, dev, n_rows=4096, check_bwd=True, do_scale=None, chec
         if not check_bwd:
             continue
         ob, lb = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **kw)
-        dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, ob, lb, inp.gdo[p], p, **kw)
+        dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, ob, lb, inp.gdo[p], p, stored_ds=stored_ds, **kw)
         torch.cuda.synchronize()
         # dQ rows and branch dK/dV at the same rows (all heads of the group)
         for (s, g), heads in by_group.items():
@@ -163,7 +163,7 @@ def run_fullsize(tk, name, dev, n_rows=4096, check_bwd=True, do_scale=None, chec
                 "dv_trunk": rel_fro(np.concatenate(tv_g), np.concatenate(tv_r))}
         n_dq = sum(len(x) for x in dq_g)
         n_keys = sum(len(x) for x in tk_g)
-        tag = "" if do_scale is None else f" (dO x {do_scale})"
+        tag = ("" if do_scale is None else f" (dO x {do_scale})") + (" (stored dS)" if stored_ds else "")
         print(f"{name}{tag}: backward {n_dq} sampled dQ rows, {n_keys} trunk key rows: " +
               " ".join(f"{k}={v:.2e}" for k, v in errs.items()) +
               f"; edge keys: worst per-key rel error {max(edge_err):.2e} over {len(edge_err)}")
@@ -188,3 +188,9 @@ def test_s32k_fullsize(dev, tk):
 def test_b4_s4k_fullsize_small_dout(dev, tk):
     """The bench workload's backward with dO x 1e-6 (a loss averaged over many tokens)."""
     run_fullsize(tk, "b4_s4k", dev, do_scale=1e-6, check_fwd=False)
+
+
+def test_b4_s4k_fullsize_stored_ds(dev, tk):
+    """The bench workload's backward with stored dS (bwd_mode STORED_DS), at dO x 1 and x 1e-6."""
+    run_fullsize(tk, "b4_s4k", dev, check_fwd=False, stored_ds=True)
+    run_fullsize(tk, "b4_s4k", dev, check_fwd=False, stored_ds=True, do_scale=1e-6)

@@ -4,8 +4,9 @@ These head sizes run the D = 128 kernels on zero-padded copies of the heads: eac
 D-dim head is spread over 128 entries so that the rotate-half pairs and angles
 are the D-dim ones, and every padded entry stays zero.  Checked here: forward O
 (bf16 and fp32 output) and LSE, and every gradient, for BSHD and THD (ragged
-lengths), GQA 4:1, passes 1 and 3, a sliding window, and an explicit softmax
-scale; and that the padding changes nothing outside the caller's tensors.
+lengths), GQA 4:1, passes 1 and 3, a sliding window, an explicit softmax scale and
+the stored-dS backward; and that the padding changes nothing outside the caller's
+tensors.
 """
 import numpy as np
 import pytest
@@ -36,7 +37,7 @@ def tk():
 THD_LENS = [1, 63, 64, 65, 200, 129, 3]
 
 
-def check(tk, inp, p, label, window=0, scale=0.0):
+def check(tk, inp, p, label, window=0, scale=0.0, stored_ds=False):
     w = inp.w
     kw = inp.kw()
     for o_fp32 in (True, False):
@@ -51,7 +52,7 @@ def check(tk, inp, p, label, window=0, scale=0.0):
         print(f"{label} p={p} o_fp32={o_fp32}: O {eo.max():.3e} LSE {el:.3e}")
         assert eo.max() <= TOL["bf16"]["o"] and el <= TOL["bf16"]["lse"]
     dq, dks, dvs = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, inp.gdo[p], p, window=window, softmax_scale=scale,
-                          **kw)
+                          stored_ds=stored_ds, **kw)
     torch.cuda.synchronize()
     dq_r, dk_r, dv_r = O.bwd(inp.q[p], inp.k, inp.v, inp.do[p], p, layout=w.layout, cu_seqlens=inp.cu_host,
                              scale=scale if scale > 0 else None, base=w.rope_base, window=window)
@@ -69,6 +70,7 @@ def test_bshd_head_dim(dev, tk, D):
     inp = Inputs(w, dev)
     for p in (1, 3):
         check(tk, inp, p, f"bshd D={D}")
+    check(tk, inp, 3, f"bshd D={D} stored dS", stored_ds=True)
 
 
 @pytest.mark.parametrize("D", [32, 64])
