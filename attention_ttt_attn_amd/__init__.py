@@ -56,6 +56,7 @@ class Desc(ctypes.Structure):
         ("o_stride", ctypes.c_int64 * 3),
         ("window", ctypes.c_int32),
         ("bwd_mode", ctypes.c_int32),
+        ("aux_stream", ctypes.c_void_p),
     ]
 
 
@@ -270,6 +271,26 @@ def _on_stream(fn):
     return wrapped
 
 
+_AUX_STREAMS = {}
+
+
+def _aux_stream(aux, device) -> int:
+    """Handle of a backward call's second stream: "auto" = one per device, created on first use at
+    the default priority and kept by this module; None = none (the whole call on its stream); or a
+    torch.cuda.Stream of the caller's."""
+    if aux is None:
+        return 0
+    if isinstance(aux, str):
+        if aux != "auto":
+            raise ValueError(f"aux_stream: 'auto', None or a torch.cuda.Stream, not {aux!r}")
+        torch = _torch()
+        key = torch.device(device).index
+        if key not in _AUX_STREAMS:
+            _AUX_STREAMS[key] = torch.cuda.Stream(device=device)
+        aux = _AUX_STREAMS[key]
+    return int(aux.cuda_stream)
+
+
 def _stream(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -337,14 +358,16 @@ def fwd_noalloc(q, ks: Sequence, vs: Sequence, p: int, out, lse, *, cu_seqlens=N
 @_on_stream
 def bwd(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, cu_seqlens=None, softmax_scale: float = 0.0,
         rope_base: float = 0.0, dq=None, dks=None, dvs=None, workspace=None, stream=None,
-        check_cu_seqlens: bool = False, window: int = 0, stored_ds: bool = False):
+        check_cu_seqlens: bool = False, window: int = 0, stored_ds: bool = False, aux_stream="auto"):
     """Backward of TTT pass p.  Returns (dq, [dk_1..dk_p], [dv_1..dv_p]).  stored_ds: the dK/dV kernel
-    stores dS and dQ is formed from it (BWD_STORED_DS; bf16 BSHD without a window, else ignored)."""
+    stores dS and dQ is formed from it (BWD_STORED_DS; bf16 BSHD without a window, else ignored).
+    aux_stream: the second stream the HBM-bound kernels may run on ("auto", None or a stream)."""
     torch = _torch()
     o_dtype = _dtype_code(o)
     d = make_desc(q, ks, p, cu_seqlens=cu_seqlens, softmax_scale=softmax_scale, rope_base=rope_base,
                   o_dtype=o_dtype, o_like=o, check_cu_seqlens=check_cu_seqlens, window=window)
     d.bwd_mode = BWD_STORED_DS if stored_ds else BWD_RECOMPUTE
+    d.aux_stream = _aux_stream(aux_stream, q.device)
     if dout.stride() != o.stride():
         raise ValueError("dout must have the strides of o")
     like = lambda t: torch.empty_strided(t.shape, t.stride(), dtype=t.dtype, device=t.device)
@@ -445,7 +468,7 @@ def fwd_chunk(q, ks: Sequence, vs: Sequence, p: int, *, q_offset: int = 0, kv_of
 def bwd_chunk(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, q_offset: int = 0, kv_offset: int = 0,
               with_branch: bool, softmax_scale: float = 0.0, rope_base: float = 0.0, window: int = 0,
               workspace=None, stream=None, cu_seqlens=None, kv_cu_seqlens=None, q_offsets=None, kv_offsets=None,
-              max_position: int = 0, check_cu_seqlens: bool = False):
+              max_position: int = 0, check_cu_seqlens: bool = False, aux_stream="auto"):
     """Backward terms of one ring step (bf16 inputs; BSHD, or THD as in fwd_chunk): o, lse, dout are
     the query rows' whole-sequence values.  Returns fp32 (dq, [dk0, branch dk...], [dv0, branch
     dv...]); the branch lists hold passes 2..p only with with_branch.  Summing the steps' terms
@@ -457,6 +480,7 @@ def bwd_chunk(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, q_offset: 
     d = make_desc(q, (branch_ks or [ks[0]]), p, softmax_scale=softmax_scale, rope_base=rope_base,
                   o_dtype=_dtype_code(o), o_like=o, window=window, cu_seqlens=cu_seqlens,
                   check_cu_seqlens=check_cu_seqlens)
+    d.aux_stream = _aux_stream(aux_stream, q.device)
     if dout.stride() != o.stride():
         raise ValueError("dout must have the strides of o")
     lse = lse.contiguous()  # the C ABI reads the step rows' LSE as a dense [B, Hq, rows] / [Hq, T] array

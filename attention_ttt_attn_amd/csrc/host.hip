@@ -393,41 +393,18 @@ void trace(const char* name, int phase, hipStream_t st) {
   } while (0)
 
 namespace {
-// One non-blocking side stream per device (default priority), created on first
-// use and kept for the life of the process.  The bf16 backward forks the
-// HBM-bound branch-gradient kernel onto it so that it runs beside the
-// MFMA-bound dK/dV kernel, and joins it back into the caller's stream.
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-hipStream_t g_side[kMaxDevices];
-
-hipStream_t side_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lock(g_side_mu);
-  if (!g_side[dev]) {
-    hipStream_t s = nullptr;
-    if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
-      (void)hipGetLastError();
-      return nullptr;
-    }
-    g_side[dev] = s;
-  }
-  return g_side[dev];
-}
-
-// Work on the side stream, ordered against the caller's stream with events:
-// mark(s) records an event at the current end of stream s, wait(w, e) makes
-// later work on stream w wait for it.  The events are released once they
-// complete.  If an event step fails, the side stream is drained from the host
-// so that the ordering still holds.
+// Work on the caller's second stream (the descriptor's aux_stream), ordered
+// against the call's stream with events: mark(s) records an event at the
+// current end of stream s, wait(w, e) makes later work on stream w wait for
+// it.  The events are released once they complete.  If an event step fails,
+// the side stream is drained from the host so that the ordering still holds.
 struct Side {
   hipStream_t side = nullptr;
   hipEvent_t ev[4] = {};
   int nev = 0;
-  bool begin(hipStream_t st) {  // the side stream starts after the work on st so far
-    side = side_stream();
-    if (!side) return false;
+  bool begin(hipStream_t st, hipStream_t aux) {  // the side stream starts after the work on st so far
+    if (!aux || aux == st) return false;
+    side = aux;
     if (!wait(side, mark(st))) {
       side = nullptr;
       return false;
@@ -579,6 +556,7 @@ namespace {
 // hipGetSymbolAddress returns, looked up once per device (with that device
 // current) and kept in g_scratch_ptr.
 static __device__ __align__(256) unsigned char scratch[TTT_ATTN_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];
 
@@ -1115,7 +1093,7 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
   // Q~/K~ rotations, the branch kernel beside the dK/dV kernel (one MFMA wave
   // per SIMD leaves room for one more wave).
   Side sd;
-  const bool forked = pl.bf16 && sd.begin(st);
+  const bool forked = pl.bf16 && sd.begin(st, (hipStream_t)d->aux_stream);
   const hipStream_t sst = forked ? sd.side : st;
   if (pl.bf16) set_bounds(P, at<char>(ws, pl.ws.bnd), 1, pl.ds);
   if (pl.ds) P.ds = at<_Float16>(ws, pl.ws.ds);

@@ -34,15 +34,13 @@
  * rows past a base with 32-bit byte offsets.
  *
  * Ownership and state: the caller owns every buffer, including the
- * workspace.  The library allocates no device memory and keeps no state
- * between calls except one non-blocking side stream per device, created on
- * first use and kept for the life of the process (work forked onto it is
- * joined back into the caller's stream before a call returns, so the calls
- * keep the caller's stream order).  Calls are asynchronous on `stream` (a
- * hipStream_t; NULL is the default stream) and re-entrant.  Outputs are overwritten, never
- * accumulated: gradients of a key/value tensor used by several passes are
- * summed by the caller.  Two calls that share a workspace must be ordered on
- * one stream.
+ * workspace, and the optional second stream of the backward (aux_stream).
+ * The library allocates no device memory and keeps no state between calls
+ * (ttt_attn_fwd_noalloc's static scratch array aside).  Calls are
+ * asynchronous on `stream` (a hipStream_t; NULL is the default stream) and
+ * re-entrant.  Outputs are overwritten, never accumulated: gradients of a
+ * key/value tensor used by several passes are summed by the caller.  Two
+ * calls that share a workspace must be ordered on one stream.
  *
  * Empty problems (zero tokens) return TTT_OK at once, after the descriptor is
  * checked; their tensor pointers are not examined.
@@ -64,8 +62,9 @@ extern "C" {
 
 /* 3: ttt_attn_chunk, ttt_attn_block and ttt_soft_ce_desc gained the packed
  * (THD) and per-row / per-group fields; each struct's struct_size check
- * refuses a caller built against an older layout. */
-#define TTT_ATTN_ABI_VERSION 3
+ * refuses a caller built against an older layout.  4: ttt_attn_desc gained
+ * aux_stream (the library keeps no stream of its own). */
+#define TTT_ATTN_ABI_VERSION 4
 
 enum ttt_attn_layout { TTT_LAYOUT_BSHD = 0, TTT_LAYOUT_THD = 1 };
 /* BF16: the score products run on fp16 operands.  q and k are rotated in fp32
@@ -138,6 +137,15 @@ typedef struct ttt_attn_desc {
                                    otherwise as RECOMPUTE.  Fewer matrix products, more
                                    HBM traffic: see the measurements in the docs.
                                  Both are deterministic.                                  */
+  void* aux_stream;           /* ttt_attn_bwd / ttt_attn_bwd_chunk, bf16 (ignored elsewhere):
+                                 an optional second stream of the caller's (a
+                                 hipStream_t, NULL = none, different from `stream`).
+                                 When given, the HBM-bound Delta and branch-gradient
+                                 kernels run on it beside the staging and dK/dV kernels,
+                                 ordered against `stream` with events and joined back
+                                 into `stream` before the call returns; results are the
+                                 same either way.  Two calls in flight at once must not
+                                 share an aux stream.                                     */
 } ttt_attn_desc;
 
 enum ttt_attn_bwd_mode { TTT_BWD_RECOMPUTE = 0, TTT_BWD_STORED_DS = 1 };

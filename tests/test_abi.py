@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
             "ttt_attn_last_error", "ttt_attn_abi_version", "ttt_attn_set_trace_hook"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ttt_attn_abi_version() == 3
+    assert lib.ttt_attn_abi_version() == 4
 
 
 def test_status_strings():
@@ -505,7 +505,7 @@ def test_window_validation():
     d = block_desc()
     d.window = 4
     assert call_block(d, good_block()) == 3 and "window" in err()
-    assert ctypes.sizeof(tk.Desc) == 144
+    assert ctypes.sizeof(tk.Desc) == 152
 
 
 def test_chunk_bwd_validation():

@@ -81,3 +81,30 @@ def test_bf16_thd_small_backward(dev, tk, p):
     lens = [1, 63, 64, 65, 200, 129, 3, 130]
     w = syn.Workload("thd_small_bwd", 15, "thd", 1, sum(lens), 4, 1, 128, 3, "bf16", 1e4, True)
     full_bwd_check(tk, Inputs(w, dev, lengths=lens), p, "thd_small")
+
+
+@pytest.mark.parametrize("hq,hkv,layout", [(8, 1, "bshd"), (8, 2, "bshd"), (16, 2, "thd")])
+def test_bf16_backward_aux_stream(dev, tk, hq, hkv, layout):
+    """The backward's optional second stream (desc.aux_stream): none, the binding's own and one of
+    the caller's give bitwise the same gradients (GQA 8:1: the branch kernel on it; 4:1: Delta), and
+    the call stays ordered on its stream (the inputs are rewritten right after the call)."""
+    lens = [130, 1, 64, 97]
+    S = sum(lens) if layout == "thd" else 160
+    w = syn.Workload(f"aux_{hq}_{hkv}", 28, layout, 1 if layout == "thd" else 2, S, hq, hkv, 128, 3, "bf16", 1e6, True)
+    inp = Inputs(w, dev, lengths=lens if layout == "thd" else None)
+    kw = inp.kw()
+    p = 3
+    o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **kw)
+    mine = torch.cuda.Stream()
+    res = []
+    for aux in (None, "auto", mine):
+        dout = inp.gdo[p].clone()
+        g = tk.bwd(inp.gq[p], inp.gk, inp.gv, o, lse, dout, p, aux_stream=aux, **kw)
+        dout.fill_(float("nan"))  # ordered after the call's kernels on the current stream
+        torch.cuda.synchronize()
+        res.append([g[0]] + list(g[1]) + list(g[2]))
+    for other in res[1:]:
+        for x, y in zip(res[0], other):
+            assert torch.equal(x, y)
+    assert all(torch.isfinite(x.float()).all() for x in res[0])
+    print(f"aux stream {hq}:{hkv} {layout}: none, binding-owned and caller-owned aux streams bitwise equal")
