@@ -472,7 +472,7 @@ def bwd_chunk(q, ks: Sequence, vs: Sequence, o, lse, dout, p: int, *, q_offset: 
     """Backward terms of one ring step (bf16 inputs; BSHD, or THD as in fwd_chunk): o, lse, dout are
     the query rows' whole-sequence values.  Returns fp32 (dq, [dk0, branch dk...], [dv0, branch
     dv...]); the branch lists hold passes 2..p only with with_branch.  Summing the steps' terms
-    gives the whole-sequence gradients."""
+    gives the whole-sequence gradients.  aux_stream: as for bwd."""
     torch = _torch()
     thd = _thd_chunk(cu_seqlens, kv_cu_seqlens, q_offsets, kv_offsets, max_position)
     n_br = p - 1 if with_branch else 0
