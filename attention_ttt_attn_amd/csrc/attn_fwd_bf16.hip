@@ -12,10 +12,11 @@
 // LSE = logaddexp(LSE_trunk, LSE_branch), O = sum_x e^(LSE_x - LSE) O_x.
 //
 // gfx950 design
-// * A workgroup is 4 wave64s: the R' query heads of one KV head that it
-//   covers (R' = 4 for GQA 4:1) times 32*4/R' rows.  With R' = 4 all four
-//   waves share one causal diagonal and every K/V tile in LDS serves the whole
-//   GQA group.
+// * A workgroup is NW wave64s: the R' query heads of one KV head that it
+//   covers (R' = 4 for GQA 4:1) times 32*NW/R' rows.  With R' = 4 the TTT
+//   passes run NW = 8 (4 heads x 64 rows, one workgroup of two waves per SIMD
+//   per CU: every K~/V^T tile staged in LDS serves twice the rows of the
+//   4-wave shape, which the other modes and head ratios keep).
 // * Scores are computed transposed, S^T = K~ Q~^T, with
 //   v_mfma_f32_32x32x16_f16: each lane then holds 16 keys of ONE query, so the
 //   running max/sum are per-lane scalars (one cross-half exchange per tile)
@@ -61,6 +62,7 @@ struct Tile {
   _Float16 k[BN * D];  // K~ tile: row r at r*D, 16-byte chunk c at slot c ^ (r & 15)
   _Float16 v[D * BN];  // V^T tile (fp16): d-row at d*BN, chunk c at slot c ^ ((d >> 1) & (CH - 1))
 };
+template <int NW>
 struct Smem {
   union {
     Tile ring[NBUF];
@@ -68,28 +70,29 @@ struct Smem {
       _Float16 k[128][D + 8];  // branch keys R(i+q-1) k^(q), fp16, per row of the tile
       uint16_t v[128][D + 8];  // branch values, bf16
     } br;
-    float o[128][OPAD];        // normalised O rows for the stores
+    float o[32 * NW][OPAD];    // normalised O rows for the stores (32 per wave)
   };
 };
+constexpr int kFwdWaves = 8;  // TTT passes at GQA 4:1: waves per work item (4 or 8)
 
 __device__ __forceinline__ int perm_row(int a) { return (a & ~0xC) | ((a & 4) << 1) | ((a & 8) >> 1); }
 
 // Rows of one work item, per R' (heads per workgroup).
-__host__ __device__ constexpr int tile_rows(int heads_per_wg) { return 32 * 4 / heads_per_wg; }
+__host__ __device__ constexpr int tile_rows(int heads_per_wg, int nw = 4) { return 32 * nw / heads_per_wg; }
 
 // MODE 0: TTT pass (trunk + branch); MODE 4: the same with a sliding-window
 // trunk (a separate instantiation, so the windowless loop carries no window
 // test).  MODE 1: block drafting -- the trunk is
 // the context prefix j < anchor of each row's block (kt/vt), then the keys of
 // the work item's own blocks (kbt/vbt) in one more masked tile pass.
-template <int RH, bool O_F32, int MODE>
-__global__ void __launch_bounds__(256, 2)
+template <int RH, bool O_F32, int MODE, int NW = 4>
+__global__ void __launch_bounds__(64 * NW, 8 / NW)
     fwd_bf16_kernel(Prob P, const uint16_t* __restrict__ q, PassPtrs kv, const _Float16* __restrict__ kt,
                     const _Float16* __restrict__ vt, const int4* __restrict__ tiles, const float* __restrict__ cosT,
                     const float* __restrict__ sinT, void* __restrict__ o, float* __restrict__ lse,
                     const _Float16* __restrict__ kbt, const _Float16* __restrict__ vbt) {
-  constexpr int RT = tile_rows(RH);  // rows per work item
-  __shared__ __attribute__((aligned(16))) Smem sm;
+  constexpr int RT = tile_rows(RH, NW);  // rows per work item
+  __shared__ __attribute__((aligned(16))) Smem<NW> sm;
   constexpr bool TTT_ = MODE == 0 || MODE == 4;  // TTT pass (4: with a sliding window)
   const int win = MODE == 4 ? P.win : 0;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -154,9 +157,9 @@ __global__ void __launch_bounds__(256, 2)
   // DMA lane roles, loads n = w*KL + i.  K~: 1 KB = rows 4n + lane/16, slot
   // lane%16.  V^T: 1 KB = d-rows RPL*n + lane/CH, slot lane%CH.  Per-lane 32-bit
   // offsets, tile bases are wave-uniform.
-  constexpr int KL = BN / 16;        // K~ loads per wave per tile
+  constexpr int KL = BN / 4 / NW;    // K~ loads per wave per tile
   constexpr int RPL = 64 / CH;       // V^T d-rows per load
-  constexpr int VL = D / RPL / 4;    // V^T loads per wave per tile
+  constexpr int VL = D / RPL / NW;   // V^T loads per wave per tile
   constexpr int TL = KL + VL;        // loads per wave per tile
   uint32_t koff[KL], voff[VL];
 #pragma unroll
@@ -394,14 +397,15 @@ __global__ void __launch_bounds__(256, 2)
 
   // ---- branch: keys/values of passes 2..p at the same row, folded into (m, l, O)
   const int lr = rbk * 32 + l32;  // this lane's row within the tile
-  // Staging roles: 8 threads per row, rows 32j + tid/8.  With one 32-row set
+  // Staging roles: 8 threads per row, rows RPS*j + tid/8.  With one row set
   // per work item the raw k^(q+1), v^(q+1) rows are loaded while pass q is
   // computed, so a pass waits for no global load of its own (larger work
   // items load each row set just before staging it: registers).
-  constexpr int NR = RT / 32;
+  constexpr int RPS = 8 * NW;  // rows per staged set
+  constexpr int NR = RT / RPS;
   const int bc8 = tid & 7, bdlo = bc8 * 8, bdhi = 64 + bc8 * 8;
   auto load_rows = [&](int j, int qq, u32x4 (&kr)[2], u32x4 (&vr)[2]) __attribute__((always_inline)) {
-    const int i = row0 + j * 32 + (tid >> 3);
+    const int i = row0 + j * RPS + (tid >> 3);
     kr[0] = kr[1] = vr[0] = vr[1] = u32x4{0, 0, 0, 0};
     if (i < L) {
       const int64_t koff = b * P.ks_b + (int64_t)(start + i) * P.ks_t + g * P.ks_h;
@@ -415,7 +419,7 @@ __global__ void __launch_bounds__(256, 2)
   };
   // R(i+q-1) k^(q) (fp16) and v^(q) (bf16) of row set j into LDS
   auto stage_rows = [&](int j, int qq, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) __attribute__((always_inline)) {
-    const int rr = j * 32 + (tid >> 3);
+    const int rr = j * RPS + (tid >> 3);
     const int i = row0 + rr;
     u32x4 klo = {0, 0, 0, 0}, khi = {0, 0, 0, 0};
     if (i < L) {
@@ -534,6 +538,18 @@ template <int RH, int MODE>
 static void launch_rh(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const _Float16* vt,
                       const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,
                       const _Float16* kbt, const _Float16* vbt, hipStream_t st) {
+  if constexpr (RH == 4 && MODE != 1 && kFwdWaves == 8) {  // TTT passes: 4 heads x 64 rows per work item
+    constexpr int RT8 = tile_rows(4, 8);
+    const int ntiles8 = P.layout == 0 ? P.B * ((P.stok + RT8 - 1) / RT8) : (P.stok + RT8 - 1) / RT8 + P.nseq;
+    const int64_t grid8 = (int64_t)ntiles8 * P.Hkv * (P.r / 4);
+    if (o_f32)
+      fwd_bf16_kernel<4, true, MODE, 8>
+          <<<(unsigned)grid8, 512, 0, st>>>(P, q, kv, kt, vt, tiles, cosT, sinT, o, lse, kbt, vbt);
+    else
+      fwd_bf16_kernel<4, false, MODE, 8>
+          <<<(unsigned)grid8, 512, 0, st>>>(P, q, kv, kt, vt, tiles, cosT, sinT, o, lse, kbt, vbt);
+    return;
+  }
   constexpr int RT = tile_rows(RH);
   int ntiles;
   if (P.layout == 0) ntiles = P.B * ((P.stok + RT - 1) / RT);
@@ -560,7 +576,11 @@ static void launch_mode(const Prob& P, const uint16_t* q, const PassPtrs& kv, co
 
 }  // namespace fwd
 
-int fwd_tile_rows(int r) { return fwd::tile_rows(fwd::heads_per_wg(r)); }
+int fwd_tile_rows(int r) {
+  const int rh = fwd::heads_per_wg(r);
+  return fwd::tile_rows(rh, rh == 4 ? fwd::kFwdWaves : 4);
+}
+int block_fwd_tile_rows(int r) { return fwd::tile_rows(fwd::heads_per_wg(r)); }
 
 void launch_fwd_bf16(const Prob& P, const uint16_t* q, const PassPtrs& kv, const _Float16* kt, const _Float16* vt,
                      const int4* tiles, const float* cosT, const float* sinT, void* o, bool o_f32, float* lse,

@@ -871,7 +871,8 @@ int ttt_attn_block_fwd(const ttt_attn_desc* d, const ttt_attn_block* bk, const v
   const int4* tiles = nullptr;
   if (thd) {  // THD: the slots of each sequence (block rows and context), then the query tiles
     int4* t = at<int4>(ws, bp.tiles_q);
-    TTT_TRACED("tile_sched", ttt::launch_tile_sched(P, ttt::fwd_tile_rows(P.r), 1, t, bp.max_tiles_q, slots, st));
+    TTT_TRACED("tile_sched",
+               ttt::launch_tile_sched(P, ttt::block_fwd_tile_rows(P.r), 1, t, bp.max_tiles_q, slots, st));
     tiles = t;
   }
   // context: K~ rows at positions j and V^T (kv_len rows; THD: each sequence's own)

@@ -58,7 +58,8 @@ void launch_bwd_f32(const Prob& P, const PassPtrs& kv, const float* lse, const f
                     const PassGradPtrs& g, hipStream_t st);
 
 // bf16 path (MFMA trunk + shuffle-reduction branch)
-int fwd_tile_rows(int r);
+int fwd_tile_rows(int r);        // rows per forward work item (TTT passes; THD tile lists)
+int block_fwd_tile_rows(int r);  // the same for block drafting
 // Block-draft forward (BSHD, D = 128): context K~ / V^T in kt / vt (P.spad
 // slots), block K~ / V^T in kbt / vbt (P.spad_b slots); P.anchors, P.bs_log2,
 // P.nblk, P.kv_len (context rows) describe the blocks.
