@@ -1090,7 +1090,7 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     }
   }
   // bf16: Delta and then the branch gradients (HBM-bound, few registers, no
-  // LDS) run on the side stream when one is available: Delta beside the
+  // LDS) run on the caller's aux stream when one is given: Delta beside the
   // Q~/K~ rotations, the branch kernel beside the dK/dV kernel (one MFMA wave
   // per SIMD leaves room for one more wave).
   Side sd;
@@ -1132,7 +1132,7 @@ int bwd_impl(const ttt_attn_desc* d, const ttt_attn_chunk* c, const void* q, con
     if (forked) sd.wait(st, delta_done);
     // branch dK/dV of passes 2..p: in the dQ kernel's epilogue when its work
     // item holds every query head of a KV group, else a kernel of their own
-    // beside dK/dV on the side stream
+    // beside dK/dV on the aux stream
     P.dq_branch = ttt::dq_fuses_branch(P.r) ? 1 : 0;
     const bool branch = P.p > 1 && P.branch && !P.dq_branch;
     if (forked && branch) sd.wait(sd.side, sd.mark(st));  // start the branch kernel with dK/dV, not beside the prologue
