@@ -108,3 +108,26 @@ def test_bf16_backward_aux_stream(dev, tk, hq, hkv, layout):
             assert torch.equal(x, y)
     assert all(torch.isfinite(x.float()).all() for x in res[0])
     print(f"aux stream {hq}:{hkv} {layout}: none, binding-owned and caller-owned aux streams bitwise equal")
+
+
+def test_bf16_bwd_chunk_aux_stream(dev, tk):
+    """A ring step's backward terms (GQA 8:1: the branch kernel runs on the aux stream) are bitwise
+    the same with and without the second stream."""
+    w = syn.Workload("aux_chunk", 29, "bshd", 1, 192, 8, 1, 128, 3, "bf16", 1e6, True)
+    inp = Inputs(w, dev)
+    p, qa, n, ka, m = 3, 64, 96, 32, 100
+    o, lse = tk.fwd(inp.gq[p], inp.gk, inp.gv, p, **inp.kw())
+    sk = [inp.gk[0][:, ka:ka + m]] + [k[:, qa:qa + n] for k in inp.gk[1:p]]
+    sv = [inp.gv[0][:, ka:ka + m]] + [v[:, qa:qa + n] for v in inp.gv[1:p]]
+    res = []
+    for aux in (None, "auto"):
+        g = tk.bwd_chunk(inp.gq[p][:, qa:qa + n], sk, sv, o[:, qa:qa + n], lse[:, :, qa:qa + n],
+                         inp.gdo[p][:, qa:qa + n], p, q_offset=qa, kv_offset=ka, with_branch=True,
+                         rope_base=w.rope_base, aux_stream=aux)
+        torch.cuda.synchronize()
+        res.append([g[0]] + list(g[1]) + list(g[2]))
+    assert len(res[0]) == 1 + 2 * p
+    for x, y in zip(*res):
+        assert torch.equal(x, y)
+    assert all(torch.isfinite(x).all() for x in res[0]) and any(x.abs().max() > 0 for x in res[0][1 + p:])
+    print("bwd_chunk GQA 8:1 with branch: no aux stream and the binding's aux stream bitwise equal")
