@@ -62,6 +62,7 @@ struct Tile {
   _Float16 k[BN * D];  // K~ tile: row r at r*D, 16-byte chunk c at slot c ^ (r & 15)
   _Float16 v[D * BN];  // V^T tile (fp16): d-row at d*BN, chunk c at slot c ^ ((d >> 1) & (CH - 1))
 };
+constexpr int QST_ROWS = 64, QST_PITCH = 1024 + 16;
 template <int NW>
 struct Smem {
   union {
@@ -71,6 +72,12 @@ struct Smem {
       uint16_t v[128][D + 8];  // branch values, bf16
     } br;
     float o[32 * NW][OPAD];    // normalised O rows for the stores (32 per wave)
+    struct {  // 8-wave work items: Q rows and angles staged beside the first tile (4 waves: unused)
+      unsigned char first_tile[NW == 8 ? sizeof(Tile) : 16];
+      unsigned char q[NW == 8 ? QST_ROWS * QST_PITCH : 16];      // token rows: 4 heads' 1 KB, 16-byte pad
+      unsigned char c[NW == 8 ? QST_ROWS / 4 * QST_PITCH : 16];  // cos rows, 4 positions per padded 1 KB
+      unsigned char s[NW == 8 ? QST_ROWS / 4 * QST_PITCH : 16];  // sin rows
+    } qst;
   };
 };
 constexpr int kFwdWaves = 8;  // TTT passes at GQA 4:1: waves per work item (4 or 8)
@@ -203,7 +210,59 @@ __global__ void __launch_bounds__(64 * NW, 8 / NW)
     if (kt_lo + tt < nkt) dma(&sm.ring[tt], kt_lo + tt);
   // ---- Q~ = R(i+p-1) q in fp16 (while the first tiles load), B operand chunks c = 0..7 (d = 16c + 8hf + e)
   f16x8 qf[8];
-  {
+  // 64-row work items over the 4 heads of a group (contiguous in a token
+  // row): the rows and their angles come in through LDS as whole 1 KB token
+  // rows and table rows (each lane reading 32-byte pieces of 32 rows from
+  // memory would move several times the bytes through the load path), then
+  // each lane reads its own pieces back.
+  constexpr bool QSTAGE = TTT_ && NW == 8 && RH == 4 && RT == QST_ROWS;
+  if (QSTAGE && P.qs_h == D) {
+    static_assert(!QSTAGE || NBUF == 2, "the staging shares the LDS of ring slot 1");
+    const int wu = __builtin_amdgcn_readfirstlane(wv);
+    const int nrows = min(RT, L - row0);  // >= 1
+    const uint16_t* qb = q + b * P.qs_b + (int64_t)(start + row0) * P.qs_t + (int64_t)(g * P.r + sub * RH) * P.qs_h;
+    const buf_rsrc qr = make_rsrc(qb, (uint32_t)((nrows - 1) * P.qs_t * 2 + RH * D * 2));
+#pragma unroll
+    for (int j = 0; j < RT / NW; ++j) {
+      const int r = wu * (RT / NW) + j;
+      lds_dma16(qr, (uint32_t)(r * P.qs_t * 2) + lane * 16, &sm.qst.q[r * QST_PITCH]);
+    }
+    const int pos0 = min(max(qoff + row0 + P.p - 1, 0), P.npos - 1);
+    const uint32_t tab_bytes = (uint32_t)(P.npos - pos0) * 64 * 4;  // rows past the table read zeros
+    const buf_rsrc cr = make_rsrc(cosT + (int64_t)pos0 * 64, tab_bytes), sr = make_rsrc(sinT + (int64_t)pos0 * 64, tab_bytes);
+#pragma unroll
+    for (int j = 0; j < RT / 4 / NW; ++j) {
+      const int k4 = wu * (RT / 4 / NW) + j;
+      lds_dma16(cr, (uint32_t)(k4 * 1024) + lane * 16, &sm.qst.c[k4 * QST_PITCH]);
+      lds_dma16(sr, (uint32_t)(k4 * 1024) + lane * 16, &sm.qst.s[k4 * QST_PITCH]);
+    }
+    TTT_WAIT_VMCNT(0);
+    __syncthreads();
+    const bool valid = my_row < L;
+    const int rr = rbk * 32 + l32;
+    const unsigned char* ql = &sm.qst.q[rr * QST_PITCH + hw * D * 2];
+    const unsigned char* cl = &sm.qst.c[(rr >> 2) * QST_PITCH + (rr & 3) * 256];
+    const unsigned char* sl = &sm.qst.s[(rr >> 2) * QST_PITCH + (rr & 3) * 256];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int d0 = c * 16 + hf * 8;
+      float x1[8], x2[8];
+      unpack_bf8(*(const u32x4*)(ql + d0 * 2), x1);
+      unpack_bf8(*(const u32x4*)(ql + (d0 + 64) * 2), x2);
+      const f32x4 c0 = *(const f32x4*)(cl + d0 * 4), c1 = *(const f32x4*)(cl + d0 * 4 + 16);
+      const f32x4 s0 = *(const f32x4*)(sl + d0 * 4), s1 = *(const f32x4*)(sl + d0 * 4 + 16);
+      const float cs[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+      const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float y1 = x1[e] * cs[e] - x2[e] * sn[e];
+        const float y2 = x2[e] * cs[e] + x1[e] * sn[e];
+        qf[c][e] = (_Float16)(valid ? y1 : 0.f);
+        qf[c + 4][e] = (_Float16)(valid ? y2 : 0.f);
+      }
+    }
+    lds_ring_barrier();  // every wave has its rows before ring slot 1 is refilled
+  } else {
     const bool valid = my_row < L;
     const uint16_t* qrow = q + b * P.qs_b + (int64_t)(start + my_row) * P.qs_t + h * P.qs_h;
     const int pos = TTT_ ? qoff + my_row + P.p - 1
