@@ -83,11 +83,16 @@ struct DsRing {
   _Float16 kt[DS_NK][D * QBN];
   _Float16 ds[DS_NS][4][32 * 32];
 };
+constexpr int GST_PITCH = 1024 + 16;  // one token row of 4 heads' dO, padded
 struct DqSmem {
   union {
     DqBuf buf[2];
     DsRing dr;
     float acc[128][OPAD];  // dQ~ rows (wave, row) for the row-major epilogue
+    struct {               // 4-head work items: dO rows staged beside the first key tile
+      unsigned char first_tile[sizeof(DqBuf)];
+      unsigned char g[32 * GST_PITCH];
+    } gst;
   };
 };
 
@@ -225,18 +230,35 @@ __global__ void __launch_bounds__(256, 2)
   };
   if (!DSM && kt_lo < nkt) dma(&sm.buf[0], kt_lo);
 
-  // B operands of this lane's query: Q~ (fp16, pre-rotated) and dO (bf16)
+  // B operands of this lane's query: Q~ (fp16, pre-rotated) and dO (bf16).
+  // With the 4 heads of a group in one work item (adjacent in a token row),
+  // the dO rows come in through LDS as whole 1 KB token rows (per-lane
+  // 32-byte pieces of 32 rows would move several times the bytes through the
+  // load path); the pre-rotated Q~ rows are contiguous per head already.
   f16x8 qf[8];
   bf16x8 dof[8];
+  const bool gstage = !DSM && RH == 4 && P.os_h == D;
   if constexpr (!DSM) {
     const _Float16* qrow = qt + ((int64_t)(b * P.Hq + h) * P.spad + slot0 + my_row) * D;
-    const uint16_t* grow = dout + b * P.os_b + (int64_t)(start + my_row) * P.os_t + h * P.os_h;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int d0 = c * 16 + hf * 8;
-      qf[c] = *(const f16x8*)(qrow + d0);
-      u32x4 gv = row_ok ? *(const u32x4*)(grow + d0) : u32x4{0, 0, 0, 0};
-      dof[c] = __builtin_bit_cast(bf16x8, gv);
+    for (int c = 0; c < 8; ++c) qf[c] = *(const f16x8*)(qrow + c * 16 + hf * 8);
+    if (gstage) {
+      const int wu = __builtin_amdgcn_readfirstlane(wv);
+      const int nrows = min(32, L - row0);  // >= 1
+      const uint16_t* gb = dout + b * P.os_b + (int64_t)(start + row0) * P.os_t + (int64_t)(g * P.r + sub * RH) * P.os_h;
+      const buf_rsrc gr_ = make_rsrc(gb, (uint32_t)((nrows - 1) * P.os_t * 2 + RH * D * 2));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = wu * 8 + j;
+        lds_dma16(gr_, (uint32_t)(r * P.os_t * 2) + lane * 16, &sm.gst.g[r * GST_PITCH]);
+      }
+    } else {
+      const uint16_t* grow = dout + b * P.os_b + (int64_t)(start + my_row) * P.os_t + h * P.os_h;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        u32x4 gv = row_ok ? *(const u32x4*)(grow + c * 16 + hf * 8) : u32x4{0, 0, 0, 0};
+        dof[c] = __builtin_bit_cast(bf16x8, gv);
+      }
     }
   }
   // rows past the sequence end get LSE = +inf: every probability is then 0
@@ -259,6 +281,17 @@ __global__ void __launch_bounds__(256, 2)
     eq = ds_exp(__builtin_fmaf(dn, vm, fabsf(dl)));
     const float cq = __builtin_amdgcn_ldexpf(1.0f, eq);
     dl *= cq;
+    if (gstage) {  // the staged dO rows (rows past the end: zero)
+      TTT_WAIT_VMCNT(0);
+      __syncthreads();
+      const unsigned char* gl = &sm.gst.g[(rbk * 32 + l32) * GST_PITCH + hw * D * 2];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        u32x4 gv = *(const u32x4*)(gl + (c * 16 + hf * 8) * 2);
+        if (!row_ok) gv = u32x4{0, 0, 0, 0};
+        dof[c] = __builtin_bit_cast(bf16x8, gv);
+      }
+    }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       u32x4 x = __builtin_bit_cast(u32x4, dof[c]);
