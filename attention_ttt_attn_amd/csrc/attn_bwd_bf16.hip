@@ -756,6 +756,7 @@ __global__ void __launch_bounds__(256, 2)
 // anchors), so one vmcnt threshold per wave releases exactly the step two
 // ahead.
 constexpr int NBUF = 4;
+constexpr int KST_PITCH = 1024 + 16;  // dK/dV key staging: 4 rows of 256 bytes, padded
 constexpr int kDsStoreAux = 2;  // cache policy of the stored-dS writes: non-temporal
 __device__ __forceinline__ int kv_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 struct KvBuf {
@@ -780,6 +781,11 @@ __global__ void __launch_bounds__(256, 1)
                      const float* __restrict__ delta, const int4* __restrict__ tiles, const float* __restrict__ cosT,
                      const float* __restrict__ sinT, PassGradPtrs gr) {
   __shared__ __attribute__((aligned(16))) KvBuf sm[NBUF];
+  // the work item's K~ and V rows, staged once (4 rows per padded 1 KB) in
+  // the step ring before its first loads: no LDS beyond the ring
+  static_assert(2 * BKV / 4 * KST_PITCH <= NBUF * sizeof(KvBuf), "key staging fits the ring");
+  typedef unsigned char KvStage[BKV / 4 * KST_PITCH];
+  KvStage* kvst = reinterpret_cast<KvStage*>(&sm[0]);
   // TTT pass (4: with a sliding window; 5: also storing dS for the dQ kernel)
   constexpr bool TTT_ = MODE == 0 || MODE == 4 || MODE == 5;
   const int win = MODE == 4 ? P.win : 0;
@@ -876,18 +882,38 @@ __global__ void __launch_bounds__(256, 1)
     asm volatile("" ::"v"(kpos), "s"(row_lo));
   }
 
+  // This lane's key fragments: the work item's K~ rows (contiguous) and V rows
+  // come in through LDS as whole 256-byte rows, 16 lanes per row (per-lane
+  // 32-byte pieces of 32 rows would move several times the bytes through the
+  // load path), and each lane reads its pieces back.
   f16x8 kf[8];
   bf16x8 vf[8];
   {
-    const _Float16* krow = kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0 + my_key) * D;
-    const uint16_t* vrow = (const uint16_t*)kv.v[0] + b * P.ks_b + (int64_t)(kst + my_key) * P.ks_t + g * P.ks_h;
+    const int wu = __builtin_amdgcn_readfirstlane(wv);
+    const int nk = min(BKV, kln - kv0);  // keys of the slab in this work item (may be <= 0)
+    const buf_rsrc kr = make_rsrc(kt + ((int64_t)(b * P.Hkv + g) * P.spad + slot0 + kv0) * D, BKV * D * 2);
+    const buf_rsrc vr = make_rsrc((const uint16_t*)kv.v[0] + b * P.ks_b + (int64_t)(kst + kv0) * P.ks_t + g * P.ks_h,
+                                  nk > 0 ? (uint32_t)((nk - 1) * P.ks_t * 2 + D * 2) : 0u);
+#pragma unroll
+    for (int j = 0; j < BKV / 4 / 4; ++j) {  // each wave stages 32 rows, 4 per instruction
+      const int n = wu * (BKV / 4) + 4 * j;   // first row of this instruction's four
+      const int r = n + (lane >> 4);
+      lds_dma16(kr, (uint32_t)((r * D + (lane & 15) * 8) * 2), &kvst[0][(n >> 2) * KST_PITCH]);
+      lds_dma16(vr, (uint32_t)(r * P.ks_t * 2 + (lane & 15) * 16), &kvst[1][(n >> 2) * KST_PITCH]);
+    }
+    TTT_WAIT_VMCNT(0);
+    __syncthreads();
+    const int rr = wv * 32 + l32;
+    const int lo = (rr >> 2) * KST_PITCH + (rr & 3) * D * 2;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const int d0 = c * 16 + hf * 8;
-      kf[c] = *(const f16x8*)(krow + d0);
-      u32x4 x = key_ok ? *(const u32x4*)(vrow + d0) : u32x4{0, 0, 0, 0};
+      kf[c] = *(const f16x8*)&kvst[0][lo + d0 * 2];
+      u32x4 x = *(const u32x4*)&kvst[1][lo + d0 * 2];
+      if (!key_ok) x = u32x4{0, 0, 0, 0};
       vf[c] = __builtin_bit_cast(bf16x8, x);
     }
+    lds_ring_barrier();  // every wave has its fragments before the ring is refilled
   }
   // fp16 dS operands carry a per-key factor 2^e: |dS_ij| <= P_ij (|<dO_i, v_j>|
   // + |Delta_i|) <= N ||v_j||_inf + Dm, with N = max ||dO_i||_1 and Dm = max
